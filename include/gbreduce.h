@@ -1,0 +1,228 @@
+/*
+ * gbreduce.h — C ABI of libgbreduce, the leader-side arithmetic of a
+ * reduce-bridge-broadcast all-reduce on one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the gpubridge README ("How it works"; "Collective
+ * policies" and its "Bridge compression" paragraph; "API").  In
+ * reduce-bridge-broadcast each island reduces onto its leader, the leaders
+ * combine the island sums over a CPU bridge, and each leader broadcasts the
+ * total to its island.  The leader's share of that work is what this library
+ * computes, with every contribution already resident in device memory:
+ *
+ *   - the elementwise fp32 SUM of k contributions in fixed rank order;
+ *   - the opt-in bf16 bridge compression (encode; decode and add in fp32);
+ *   - the opt-in fp8 bridge compression: OCP E4M3 codes with one fp32 scale
+ *     per 256 values (encode; decode and add in fp32).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Element arrays (fp32 inputs and outputs, bf16 and fp8 code arrays) are
+ *    DEVICE pointers, 16-byte aligned; scale arrays are device pointers,
+ *    4-byte aligned.  Pointer ARRAYS (srcs, codes, scales) are HOST arrays of
+ *    k device pointers; they are copied into the launch, so the caller may
+ *    reuse them as soon as the call returns.
+ *  - The caller owns every buffer.  Calls allocate no device memory.
+ *  - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *    NULL is the null stream) and the call returns.  Buffers must stay alive
+ *    and untouched until the stream has passed the work (the duty the
+ *    README's "Async collectives" section places on tensors in flight).
+ *  - Validation happens before anything is enqueued: a call that returns an
+ *    error enqueued nothing and wrote nothing.  n == 0 is GB_OK and enqueues
+ *    nothing.  The calls never abort or exit the process.
+ *  - Failures return a gb_status; gb_last_error() then holds a one-line
+ *    detail for the calling thread.
+ *  - Arithmetic is IEEE binary32 with round-to-nearest-even, subnormals kept
+ *    and no fused multiply-add: every sum is a left fold over ranks
+ *    0, 1, ..., k-1 starting from rank 0's value, so a result does not depend
+ *    on the launch configuration and is bit-reproducible.
+ *  - Only fp32 SUM is supported, as the README's compression applies to
+ *    floating-point SUM; the codecs never apply to other reductions.
+ */
+#ifndef GBREDUCE_H
+#define GBREDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GB_VERSION 1
+/* Values per fp8 scale block (README "Bridge compression": one scale per
+ * 256 values). */
+#define GB_BLOCK 256
+/* Largest number of contributions (ranks or islands) one call sums. */
+#define GB_MAX_K 8
+/* Required byte alignment of element arrays. */
+#define GB_ALIGN 16
+
+typedef enum gb_status {
+  GB_OK = 0,
+  GB_ERR_INVALID_ARG = 1, /* null pointer with n > 0, k out of range, bad flag, bad bucket size */
+  GB_ERR_MISALIGNED = 2,  /* an element array is not 16-byte aligned, or a scale array not 4-byte */
+  GB_ERR_UNSUPPORTED = 3, /* unknown codec or scale mode */
+  GB_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than required */
+  GB_ERR_HIP = 5          /* the HIP runtime refused a launch; detail in gb_last_error() */
+} gb_status;
+
+/* Bridge payload codecs ("Bridge compression": off, bf16 or fp8). */
+typedef enum gb_codec {
+  GB_CODEC_NONE = 0,        /* payload is the fp32 values themselves          */
+  GB_CODEC_BF16 = 1,        /* n uint16 codes                                 */
+  GB_CODEC_FP8_E4M3_B256 = 2 /* n uint8 OCP E4M3 codes + ceil(n/256) fp32 scales */
+} gb_codec;
+
+/* How the fp8 scale s of a block is derived from the block's largest
+ * magnitude a (NaN elements ignored; a = +0 for an all-zero block).
+ * Every element of the block is encoded as E4M3(RN(x / s)), saturating to
+ * +-448, and decodes as RN(E4M3value * s). */
+typedef enum gb_scale_mode {
+  /* s = RN(a / 448): the block's largest element encodes to +-448.
+   * A zero block stores s = 0 and encodes each element as +-0. */
+  GB_SCALE_ABSMAX_DIV_448 = 0,
+  /* s = 2^e with e the smallest integer >= -149 such that a <= 448 * 2^e,
+   * i.e. the README's scale that is a power of two.
+   * A zero block stores s = 1. */
+  GB_SCALE_POW2 = 1
+} gb_scale_mode;
+
+/*
+ * gb_reduce_sum — the leader's sum of island sums (README "How it works":
+ * leaders all-reduce the island sums, each leader then holds the total).
+ *   dst[i] = RN(...RN(RN(srcs[0][i] + srcs[1][i]) + srcs[2][i]) ... + srcs[k-1][i])
+ * for i in [0, n).  k = 1 copies srcs[0].
+ *   dst   device fp32[n], written; may equal srcs[0] (in place), must not
+ *         otherwise overlap any source.
+ *   srcs  host array of k device fp32[n] pointers, read only.
+ *   k     1 .. GB_MAX_K.
+ * The sum is written once, straight into dst: this is also the leader's copy
+ * of the total into the buffer its island broadcast reads.
+ */
+gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n,
+                        void* stream);
+
+/*
+ * gb_encode_bf16 — bf16 bridge compression of one fp32 payload
+ * (README "Bridge compression": half the bytes of float32).
+ *   codes[i] = nearest bf16 to src[i], ties to the even code; values beyond
+ *              the bf16 range round to +-Inf as IEEE rounding does;
+ *              subnormals are kept; a NaN keeps its sign and top 7 payload
+ *              bits with the quiet bit forced on: (bits >> 16) | 0x0040.
+ *   codes device uint16[n], written.   src device fp32[n], read only.
+ */
+gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n,
+                         void* stream);
+
+/*
+ * gb_encode_fp8_e4m3_blockscaled — fp8 bridge compression of one fp32
+ * payload (README "Bridge compression": OCP E4M3 with one scale per 256
+ * values, about 3.9x fewer bytes than fp32).
+ * Block b covers elements [256b, min(256b + 256, n)); the last block may be
+ * partial and its scale covers only the elements present.
+ *   scales[b] = s_b, from the block's largest non-NaN magnitude per scale_mode.
+ *   codes[i]  = E4M3(v) with v = RN(src[i] / s_b) (v = src[i] when s_b == 0):
+ *               nearest OCP E4M3 value (bias 7, largest finite 448, no Inf),
+ *               ties to the even code, |v| > 448 saturating to 448 (0x7E);
+ *               the sign bit is src[i]'s sign (so -0 encodes as 0x80); a NaN
+ *               src[i], or a NaN quotient (an Inf element in a block whose
+ *               scale is Inf), encodes as 0x7F | sign.
+ *   codes  device uint8[n], written (16-byte aligned).
+ *   scales device fp32[ceil(n/256)], written (4-byte aligned).
+ *   src    device fp32[n], read only.
+ * The payload on the bridge is codes followed by scales: gb_payload_bytes().
+ */
+gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales,
+                                         const float* src, size_t n,
+                                         int scale_mode, void* stream);
+
+/*
+ * gb_decode_accumulate — decode every leader's payload and add in float32
+ * after the bridge step (README "Bridge compression": dequantize and add in
+ * float32, so every rank ends with the same bits).
+ *   v_r[i]  = codes[r][i] as fp32                        (GB_CODEC_NONE)
+ *           = bf16 codes[r][i] widened to fp32 (exact)   (GB_CODEC_BF16)
+ *           = RN(E4M3value(codes[r][i]) * scales[r][i/256]) (GB_CODEC_FP8_E4M3_B256)
+ *   accumulate == 0:  acc[i] = RN(...RN(v_0[i] + v_1[i]) ... + v_{k-1}[i])
+ *   accumulate == 1:  acc[i] = RN(...RN(acc[i] + v_0[i]) ... + v_{k-1}[i])
+ * The product and the sum are rounded separately (never fused).
+ *   acc    device fp32[n], written (and read when accumulate == 1); must not
+ *          overlap any payload.
+ *   codes  host array of k device pointers: fp32[n], uint16[n] or uint8[n].
+ *   scales host array of k device fp32[ceil(n/256)] pointers for fp8;
+ *          ignored (may be NULL) for the other codecs.
+ *   k      1 .. GB_MAX_K.   accumulate 0 or 1.
+ */
+gb_status gb_decode_accumulate(float* acc, const void* const* codes,
+                               const float* const* scales, int k, size_t n,
+                               int codec, int accumulate, void* stream);
+
+/*
+ * gb_bucket_allreduce_local — the leader arithmetic of one DDP-style bucket
+ * stream (README "DistributedDataParallel": each gradient bucket is one
+ * all_reduce), with all k contributions resident on this GPU.
+ * The n-element buffers are cut into consecutive buckets of bucket_elems
+ * elements (the last one partial).  For each bucket, in order, on `stream`:
+ *   codec NONE : out = fixed-order sum of the k buckets (as gb_reduce_sum);
+ *   codec BF16 : each rank's bucket is bf16-encoded into the workspace, then
+ *                out = decode-and-accumulate of the k payloads (accumulate 0);
+ *   codec FP8  : each rank's bucket is E4M3-encoded with per-256 scales into
+ *                the workspace, then out = decode-and-accumulate.
+ * Each value is read from srcs once: encode and decode of a bucket are one
+ * pass, and the decoded values are the ones stored payloads decode to.
+ *   out          device fp32[n], written; may equal srcs[0].
+ *   srcs         host array of k device fp32[n] pointers, read only.
+ *   bucket_elems a positive multiple of 256 (so fp8 blocks never straddle a
+ *                bucket and each bucket starts 16-byte aligned).
+ *   workspace    device buffer of at least gb_bucket_workspace_bytes(); it
+ *                receives every rank's payload for the whole buffer, laid out
+ *                as gb_bucket_workspace_layout() reports (unused for NONE,
+ *                may then be NULL with workspace_bytes 0).
+ * Because every bucket starts on a 256-element boundary, rank r's payload in
+ * the workspace equals what gb_encode_bf16 / gb_encode_fp8_e4m3_blockscaled
+ * writes for the whole of srcs[r].
+ */
+gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
+                                    int k, size_t n, size_t bucket_elems,
+                                    int codec, int scale_mode,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Bytes one rank's n-value payload occupies on the bridge:
+ * 4n (NONE), 2n (BF16), n + 4*ceil(n/256) (FP8).  0 for an unknown codec. */
+size_t gb_payload_bytes(int codec, size_t n);
+
+/* Workspace layout of gb_bucket_allreduce_local, all offsets in bytes from
+ * the workspace start:
+ *   rank r's codes  at r * codes_stride             (codes_stride = the code
+ *                   bytes of n values rounded up to 256);
+ *   rank r's scales at scales_offset + r * scales_stride (fp8 only;
+ *                   scales_stride = 4*ceil(n/256) rounded up to 256).
+ * *total receives gb_bucket_workspace_bytes().  Returns GB_ERR_INVALID_ARG
+ * or GB_ERR_UNSUPPORTED for arguments gb_bucket_allreduce_local would refuse
+ * (null output pointers included).  Host only; touches no device. */
+gb_status gb_bucket_workspace_layout(int codec, int k, size_t n,
+                                     size_t bucket_elems, size_t* codes_stride,
+                                     size_t* scales_offset,
+                                     size_t* scales_stride, size_t* total);
+
+/* Workspace bytes gb_bucket_allreduce_local needs; 0 for codec NONE or for
+ * arguments it would refuse. */
+size_t gb_bucket_workspace_bytes(int codec, int k, size_t n,
+                                 size_t bucket_elems);
+
+/* Static English name of a status ("GB_OK", ...); "unknown status" else. */
+const char* gb_status_string(int status);
+
+/* Detail of the calling thread's last failed call ("" if none yet).  Valid
+ * until that thread's next libgbreduce call. */
+const char* gb_last_error(void);
+
+/* GB_VERSION of the library that is loaded. */
+int gb_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* GBREDUCE_H */

@@ -1,0 +1,311 @@
+/*
+ * gb_oracle.c — the CPU oracle (test infrastructure; see gb_oracle.h).
+ *
+ * Written from the definitions, one element at a time, for a reader to check
+ * by eye.  Rounding decisions are made by comparing the exact value with the
+ * exact midpoint of its two neighbouring codes (both held exactly in double);
+ * nothing here is a fast bit trick.
+ *
+ * How each function is pinned to something other than itself (the CPU tests
+ * named in brackets):
+ *   or_reduce_sum         k copies of 1.0 give k; the README's four-rank
+ *                         simulation example gives 10.0; exact integer sums;
+ *                         a rank-order case where the left fold differs from
+ *                         any other order; exact rational brute force
+ *                         [test_oracle_sum.py, test_golden.py].
+ *   or_bf16_encode_one    torch's float32->bfloat16 cast on every non-NaN
+ *                         float32 (all 2^32 bit patterns); round trip of all
+ *                         2^16 codes; even code at every midpoint
+ *                         [test_oracle_bf16.py].  The NaN rule is this
+ *                         library's convention: parity unpinned for NaN.
+ *   or_e4m3_*             torch's float8_e4m3fn decode of all 256 codes;
+ *                         torch's saturating cast (clamp to +-448, then cast)
+ *                         on every non-NaN float32; exact brute force over
+ *                         the 253 finite codes [test_oracle_fp8.py].
+ *   or_block_absmax,      brute force over permutations; the block's largest
+ *   or_block_scale        element encodes to 448; the power-of-two scale is
+ *                         the smallest that fits (checked against exact
+ *                         powers) [test_oracle_fp8.py].
+ *   or_fp8_quantize_one   exact rational division then exact nearest-code
+ *                         search [test_oracle_fp8.py]; half-ulp bound.
+ *   or_decode_accumulate  equals the plain sum on exactly representable
+ *                         data; error bound; k=1 equals the decode
+ *                         [test_oracle_decode.py].
+ *   or_bucket_allreduce   equals the whole-buffer encode + decode when
+ *                         buckets are multiples of 256 [test_oracle_decode.py].
+ * The pages fix none of the NaN and Inf conventions (NaN sign and payload,
+ * Inf scale); they are readings taken here, stated at each function: parity
+ * unpinned for non-finite inputs.
+ */
+#include "gb_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+/* No contraction into fused multiply-add: the build passes -ffp-contract=off. */
+
+static uint32_t float_bits(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  return u;
+}
+
+static float bits_float(uint32_t u) {
+  float x;
+  memcpy(&x, &u, sizeof x);
+  return x;
+}
+
+/* ------------------------------------------------------------------------
+ * Fixed-order sum.  README "How it works": the leaders all-reduce the island
+ * sums, so the leader holds the SUM of the k contributions; "API": all_reduce
+ * with SUM.  The pages leave the order open (the Rust bridges add in ring
+ * order, Gloo in its own); reading taken: a left fold over ranks 0..k-1
+ * starting from rank 0's value (not from +0, so a sum of -0 values stays -0).
+ * --------------------------------------------------------------------- */
+void or_reduce_sum(float* out, const float* const* x, int k, size_t n) {
+  for (size_t i = 0; i < n; i++) {
+    float acc = x[0][i];
+    for (int r = 1; r < k; r++) {
+      acc = acc + x[r][i];
+    }
+    out[i] = acc;
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * bf16.  README "Bridge compression": the bf16 payload is half the size of
+ * float32.  bf16 is binary32
+ * with the low 16 bits of the encoding dropped: 1 sign, 8 exponent and 7
+ * fraction bits.  Encoding takes the nearest bf16 value, the even code at a
+ * midpoint; values beyond the largest finite bf16 round to Inf exactly as
+ * IEEE rounding with an unbounded exponent would (the code after the largest
+ * finite one, 0x7F80, stands for 2^128 in that comparison).
+ * --------------------------------------------------------------------- */
+float or_bf16_decode_one(uint16_t c) { return bits_float((uint32_t)c << 16); }
+
+/* Magnitude value of a non-negative bf16 code, exact in double. */
+static double bf16_magnitude(uint32_t code) {
+  if (code == 0x7F80u) return ldexp(1.0, 128); /* rounding boundary of Inf */
+  return (double)bits_float(code << 16);
+}
+
+uint16_t or_bf16_encode_one(float x) {
+  uint32_t u = float_bits(x);
+  if (isnan(x)) {
+    /* Reading taken: keep sign and top payload bits, force the quiet bit. */
+    return (uint16_t)((u >> 16) | 0x0040u);
+  }
+  uint32_t sign = (u >> 16) & 0x8000u;
+  uint32_t mag = u & 0x7FFFFFFFu;
+  uint32_t below = mag >> 16; /* largest bf16 magnitude code <= |x| */
+  if ((mag & 0xFFFFu) == 0) return (uint16_t)(sign | below); /* exact */
+  uint32_t above = below + 1; /* smallest bf16 magnitude code > |x| */
+  double m = fabs((double)x);
+  double mid = (bf16_magnitude(below) + bf16_magnitude(above)) / 2.0;
+  uint32_t code;
+  if (m < mid) {
+    code = below;
+  } else if (m > mid) {
+    code = above;
+  } else {
+    code = (below % 2 == 0) ? below : above;
+  }
+  return (uint16_t)(sign | code);
+}
+
+void or_encode_bf16(uint16_t* codes, const float* x, size_t n) {
+  for (size_t i = 0; i < n; i++) codes[i] = or_bf16_encode_one(x[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * OCP E4M3.  README "Bridge compression": fp8 is OCP E4M3.  Per the OCP 8-bit
+ * floating point format: 1 sign bit, 4 exponent bits with bias 7, 3 fraction
+ * bits; exponent field 0 holds subnormals f * 2^-9; no infinities; the codes
+ * S.1111.111 are NaN, so the largest finite magnitude is 0x7E = 1.75 * 2^8 =
+ * 448.  Magnitude codes 0..0x7E are increasing in value.
+ * --------------------------------------------------------------------- */
+static double e4m3_magnitude(unsigned code) { /* code in 0..0x7E */
+  unsigned e = code >> 3;
+  unsigned f = code & 7u;
+  if (e == 0) return ldexp((double)f, -9);
+  return ldexp(1.0 + (double)f / 8.0, (int)e - 7);
+}
+
+float or_e4m3_decode_one(uint8_t c) {
+  unsigned mag = c & 0x7Fu;
+  int negative = (c & 0x80u) != 0;
+  if (mag == 0x7Fu) return negative ? -NAN : NAN;
+  float v = (float)e4m3_magnitude(mag); /* exact: 4 significant bits */
+  return negative ? -v : v;
+}
+
+uint8_t or_e4m3_encode_one(float v, int negative) {
+  unsigned sign = negative ? 0x80u : 0u;
+  if (isnan(v)) return (uint8_t)(0x7Fu | sign);
+  double m = fabs((double)v);
+  /* Saturate (reading taken): every magnitude at or above 448, Inf included,
+   * gives 448, so a finite input never becomes NaN. */
+  if (m >= 448.0) return (uint8_t)(0x7Eu | sign);
+  /* Binary search for the largest code `below` with value <= m. */
+  unsigned lo = 0, hi = 0x7E; /* value(lo) <= m < value(hi) */
+  while (hi - lo > 1) {
+    unsigned mid = (lo + hi) / 2;
+    if (e4m3_magnitude(mid) <= m) {
+      lo = mid;
+    } else {
+      hi = mid;
+    }
+  }
+  unsigned below = lo, above = lo + 1;
+  double midpoint = (e4m3_magnitude(below) + e4m3_magnitude(above)) / 2.0;
+  unsigned code;
+  if (m < midpoint) {
+    code = below;
+  } else if (m > midpoint) {
+    code = above;
+  } else {
+    code = (below % 2 == 0) ? below : above;
+  }
+  return (uint8_t)(code | sign);
+}
+
+void or_e4m3_encode_array(uint8_t* codes, const float* v, size_t n) {
+  for (size_t i = 0; i < n; i++) {
+    codes[i] = or_e4m3_encode_one(v[i], signbit(v[i]) != 0);
+  }
+}
+
+void or_e4m3_decode_array(float* v, const uint8_t* codes, size_t n) {
+  for (size_t i = 0; i < n; i++) v[i] = or_e4m3_decode_one(codes[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * Block scale.  README "Bridge compression": one scale per 256 values, with
+ * the precision stated relative to the largest value of the block, so the
+ * scale comes from the block's largest magnitude a.  NaN elements are skipped (reading taken);
+ * an Inf element makes a = Inf.
+ *   ABSMAX_DIV_448: s = RN(a / 448), so the largest element lands on 448.
+ *   POW2 (the README's scale that is a power of two): the smallest 2^e, e >= -149 so
+ *   that 2^e is a float, with a <= 448 * 2^e: nothing saturates.
+ * Zero block: s = 0 (ABSMAX_DIV_448; the quotient step is then skipped) and
+ * s = 1 (POW2).  Inf block: s = Inf in both modes.
+ * --------------------------------------------------------------------- */
+float or_block_absmax(const float* x, size_t len) {
+  float a = 0.0f;
+  for (size_t i = 0; i < len; i++) {
+    float m = fabsf(x[i]);
+    if (!isnan(m) && m > a) a = m;
+  }
+  return a;
+}
+
+float or_block_scale(float a, int mode) {
+  if (mode == OR_SCALE_ABSMAX_DIV_448) return a / 448.0f;
+  /* OR_SCALE_POW2 */
+  if (a == 0.0f) return 1.0f;
+  if (isinf(a)) return INFINITY;
+  for (int e = -149;; e++) {
+    if ((double)a <= 448.0 * ldexp(1.0, e)) return ldexpf(1.0f, e);
+  }
+}
+
+uint8_t or_fp8_quantize_one(float x, float s) {
+  int negative = signbit(x) != 0;
+  if (isnan(x)) return or_e4m3_encode_one(x, negative);
+  float v = (s == 0.0f) ? x : x / s; /* correctly rounded binary32 divide */
+  return or_e4m3_encode_one(v, negative);
+}
+
+void or_encode_fp8(uint8_t* codes, float* scales, const float* x, size_t n,
+                   int mode) {
+  size_t nblocks = (n + 255) / 256;
+  for (size_t b = 0; b < nblocks; b++) {
+    size_t start = b * 256;
+    size_t len = (n - start < 256) ? n - start : 256;
+    float s = or_block_scale(or_block_absmax(x + start, len), mode);
+    scales[b] = s;
+    for (size_t i = 0; i < len; i++) {
+      codes[start + i] = or_fp8_quantize_one(x[start + i], s);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Decode and accumulate.  README "Bridge compression": after the bridge step
+ * the leaders dequantize the payloads and add them in float32, and every rank
+ * ends with the same bits.  Reading taken: every rank's payload is decoded
+ * (the leader's own included) and added in rank order; an fp8 value is
+ * RN(code value * scale), rounded before the add (no fused multiply-add).
+ * --------------------------------------------------------------------- */
+static float decoded_value(const void* codes, const float* scales, size_t i,
+                           int codec) {
+  if (codec == OR_CODEC_NONE) return ((const float*)codes)[i];
+  if (codec == OR_CODEC_BF16) {
+    return or_bf16_decode_one(((const uint16_t*)codes)[i]);
+  }
+  float q = or_e4m3_decode_one(((const uint8_t*)codes)[i]);
+  float s = scales[i / 256];
+  return q * s;
+}
+
+void or_decode_accumulate(float* acc, const void* const* codes,
+                          const float* const* scales, int k, size_t n,
+                          int codec, int accumulate) {
+  for (size_t i = 0; i < n; i++) {
+    const float* sc0 = scales ? scales[0] : NULL;
+    float a;
+    int r0;
+    if (accumulate) {
+      a = acc[i];
+      r0 = 0;
+    } else {
+      a = decoded_value(codes[0], sc0, i, codec);
+      r0 = 1;
+    }
+    for (int r = r0; r < k; r++) {
+      const float* sc = scales ? scales[r] : NULL;
+      float v = decoded_value(codes[r], sc, i, codec);
+      a = a + v;
+    }
+    acc[i] = a;
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Bucket stream.  README "DistributedDataParallel": each gradient bucket is
+ * one all_reduce.  Per bucket: encode each rank's slice (blocks restart at
+ * the bucket start), then decode and accumulate the k payloads into out.
+ * --------------------------------------------------------------------- */
+void or_bucket_allreduce(float* out, void* const* codes, float* const* scales,
+                         const float* const* x, int k, size_t n,
+                         size_t bucket_elems, int codec, int mode) {
+  const float* xs[64];
+  const void* cs[64];
+  const float* ss[64];
+  size_t scale_base = 0;
+  for (size_t start = 0; start < n; start += bucket_elems) {
+    size_t len = (n - start < bucket_elems) ? n - start : bucket_elems;
+    for (int r = 0; r < k; r++) xs[r] = x[r] + start;
+    if (codec == OR_CODEC_NONE) {
+      or_reduce_sum(out + start, xs, k, len);
+      continue;
+    }
+    for (int r = 0; r < k; r++) {
+      if (codec == OR_CODEC_BF16) {
+        uint16_t* c = (uint16_t*)codes[r] + start;
+        or_encode_bf16(c, xs[r], len);
+        cs[r] = c;
+        ss[r] = NULL;
+      } else {
+        uint8_t* c = (uint8_t*)codes[r] + start;
+        or_encode_fp8(c, scales[r] + scale_base, xs[r], len, mode);
+        cs[r] = c;
+        ss[r] = scales[r] + scale_base;
+      }
+    }
+    or_decode_accumulate(out + start, cs, codec == OR_CODEC_FP8 ? ss : NULL, k,
+                         len, codec, 0);
+    scale_base += (len + 255) / 256;
+  }
+}

@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an AMD Instinct GPU (gfx950) and the built libgbreduce")
+    config.addinivalue_line(
+        "markers", "exhaustive: sweeps all 2^32 float32 bit patterns (opt-in: GB_EXHAUSTIVE=1)")
+
+
+def pytest_collection_modifyitems(config, items):
+    if os.environ.get("GB_EXHAUSTIVE") == "1":
+        return
+    skip = pytest.mark.skip(reason="full 2^32 sweep is opt-in: set GB_EXHAUSTIVE=1")
+    for item in items:
+        if "exhaustive" in item.keywords:
+            item.add_marker(skip)
