@@ -1,0 +1,422 @@
+"""Benchmark of libgbreduce on one GPU: effective HBM GB/s of the leader-side
+arithmetic of reduce-bridge-broadcast (fixed-order fp32 sum, bf16 / fp8
+bridge codecs).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  A step is one pass of the workload's path over its
+synthetic inputs, which are resident in device memory before timing starts.
+`value` is algorithmic bytes per step / measured time per step (GB/s, 1e9).
+Algorithmic bytes are the least reads and writes the step needs: every input
+value read once, every payload byte and every output value written once
+(and, where a call reads a payload back, read once).
+
+Workloads (inputs from workloads.py):
+  ddp_1b_buckets   (default) k=4 ranks x 1.0e9 fp32 gradients in 153 buckets
+                   of 25 MiB; per bucket: fp8 E4M3 encode of every rank with
+                   one absmax/448 scale per 256 values, decode and add in rank
+                   order, fp32 sum written out.  One gb_bucket_allreduce_local
+                   call per step (one launch per bucket).
+  gradients_256mib k=4 x 2^26 fp32; 4 x gb_encode_fp8_e4m3_blockscaled +
+                   gb_decode_accumulate(fp8).
+  gradients_64mib  k=4 x 2^24 fp32; 4 x gb_encode_bf16 + gb_decode_accumulate(bf16).
+  two_island_sweep k=2, 19 sizes 2^8..2^26 fp32; gb_reduce_sum into a
+                   separate output at every size.
+  two_rank_4mib    k=2 x 2^20 fp32; gb_reduce_sum, gb_encode_bf16 of the sum,
+                   gb_decode_accumulate(bf16, k=1).
+
+The roofline object reports the step's dominant kernel: its algorithmic bytes
+per launch over its average launch time, timed with HIP events on the stream
+the library launches on, against MI355X's 8 TB/s HBM peak.  The CPU baseline
+is the oracle (oracle/, single-threaded C) on a bounded sample of the same
+workload, on this host; the sample's GPU outputs are also checked against it.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (and % of peak) for k-way reduce + bf16/fp8 encode/decode"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="ddp_1b_buckets",
+                   choices=["ddp_1b_buckets", "gradients_256mib", "gradients_64mib",
+                            "two_island_sweep", "two_rank_4mib"])
+    p.add_argument("--scale-mode", type=int, default=0, choices=[0, 1],
+                   help="fp8 scale: 0 absmax/448, 1 power of two")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="rough budget of oracle CPU time for the baseline sample")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Inputs resident on the device, a step, and the step's byte count."""
+    name = ""
+    config = {}
+
+    def __init__(self, gb, torch, args):
+        self.gb, self.torch, self.args = gb, torch, args
+        self.dev = "cuda:0"
+        self.stream = torch.cuda.current_stream()
+
+    def timed_kernel(self):
+        """(name, bytes per launch, callable doing `launches` launches)."""
+        raise NotImplementedError
+
+
+def nblocks(n):
+    return (n + 255) // 256
+
+
+class DdpBuckets(Workload):
+    name = "ddp_1b_buckets"
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        import workloads as W
+        self.W = W
+        self.k, self.n, self.bucket = 4, W.DDP_N, W.DDP_BUCKET
+        self.mode = args.scale_mode
+        self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n,
+                       "bucket_elems": self.bucket, "buckets": len(W.ddp_buckets()),
+                       "codec": "fp8_e4m3_b256",
+                       "scale_mode": ["absmax_div_448", "pow2"][self.mode],
+                       "distribution": "N(0, sigma=1e-3)"}
+
+    def setup(self):
+        torch, gb = self.torch, self.gb
+        self.x = [self.W.device_gradients(self.n, self.W.BASE_SEED + r, self.dev) for r in range(self.k)]
+        self.out = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+        self.lay = gb.gb_bucket_workspace_layout(gb.GB_CODEC_FP8_E4M3_B256, self.k, self.n, self.bucket)
+        self.ws = torch.empty(self.lay["total"], dtype=torch.uint8, device=self.dev)
+
+    def step(self):
+        self.gb.gb_bucket_allreduce_local(self.out, self.x, self.bucket, self.gb.GB_CODEC_FP8_E4M3_B256,
+                                          self.mode, self.ws)
+
+    def bytes_for(self, n):
+        return self.k * 4 * n + self.k * (n + 4 * nblocks(n)) + 4 * n
+
+    def step_bytes(self):
+        return sum(self.bytes_for(l) for _, l in self.W.ddp_buckets())
+
+    def timed_kernel(self):
+        nb = len(self.W.ddp_buckets())
+        return ("fused_fp8_kernel<4>", self.step_bytes() / nb, nb, self.step)
+
+    def cpu_sample(self, budget):
+        """Run the oracle on the first buckets; compare with the GPU's."""
+        from oracle import oracle as O
+        import numpy as np
+        torch = self.torch
+        torch.cuda.synchronize()
+        done_bytes, t_oracle, nb, ok = 0, 0.0, 0, True
+        for start, length in self.W.ddp_buckets():
+            xs = [t[start:start + length].cpu().numpy() for t in self.x]
+            t0 = time.perf_counter()
+            want, codes, scales = O.bucket_allreduce(xs, self.bucket, O.CODEC_FP8, self.mode)
+            t_oracle += time.perf_counter() - t0
+            done_bytes += self.bytes_for(length)
+            nb += 1
+            got = self.out[start:start + length].cpu().numpy()
+            ok &= bool((got.view(np.uint32) == want.view(np.uint32)).all())
+            for r in range(self.k):
+                c0 = r * self.lay["codes_stride"] + start
+                s0 = self.lay["scales_offset"] + r * self.lay["scales_stride"] + 4 * (start // 256)
+                gc = self.ws[c0:c0 + length].cpu().numpy()
+                gs = self.ws[s0:s0 + 4 * nblocks(length)].cpu().numpy().view(np.uint32)
+                ok &= bool((gc == codes[r]).all()) and bool((gs == scales[r].view(np.uint32)).all())
+            if t_oracle >= budget:
+                break
+        sample = f"first {nb} of {len(self.W.ddp_buckets())} buckets ({nb * self.bucket:,} values x {self.k} ranks)"
+        return done_bytes, t_oracle, sample, ok
+
+
+class Gradients256(Workload):
+    name = "gradients_256mib"
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        import workloads as W
+        self.W = W
+        self.k, self.n = 4, W.GRAD256_N
+        self.mode = args.scale_mode
+        self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n,
+                       "codec": "fp8_e4m3_b256", "scale_mode": ["absmax_div_448", "pow2"][self.mode],
+                       "distribution": "N(0, sigma=1e-3), 1% outliers x100",
+                       "path": "4 x encode_fp8 + decode_accumulate"}
+
+    def setup(self):
+        torch = self.torch
+        self.xh = self.W.gradient_ranks(self.k, self.n)
+        self.x = [torch.from_numpy(a).to(self.dev) for a in self.xh]
+        self.codes = [torch.empty(self.n, dtype=torch.uint8, device=self.dev) for _ in range(self.k)]
+        self.scales = [torch.empty(nblocks(self.n), dtype=torch.float32, device=self.dev) for _ in range(self.k)]
+        self.out = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+
+    def encode(self, r):
+        self.gb.gb_encode_fp8_e4m3_blockscaled(self.codes[r], self.scales[r], self.x[r], self.mode)
+
+    def step(self):
+        for r in range(self.k):
+            self.encode(r)
+        self.gb.gb_decode_accumulate(self.out, self.codes, self.scales, self.gb.GB_CODEC_FP8_E4M3_B256)
+
+    def step_bytes(self):
+        p = self.n + 4 * nblocks(self.n)
+        return self.k * (4 * self.n + p) + self.k * p + 4 * self.n
+
+    def timed_kernel(self):
+        per = 4 * self.n + self.n + 4 * nblocks(self.n)
+        return ("encode_fp8_kernel<2>", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
+
+    def cpu_sample(self, budget):
+        from oracle import oracle as O
+        import numpy as np
+        m = 1 << 22  # a prefix of every rank (4 Mi values = 16 MiB each)
+        self.torch.cuda.synchronize()
+        xs = [a[:m] for a in self.xh]
+        t0 = time.perf_counter()
+        enc = [O.encode_fp8(a, self.mode) for a in xs]
+        want = O.decode_accumulate([c for c, _ in enc], [s for _, s in enc], O.CODEC_FP8)
+        t = time.perf_counter() - t0
+        ok = bool((self.out[:m].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
+        for r in range(self.k):
+            ok &= bool((self.codes[r][:m].cpu().numpy() == enc[r][0]).all())
+            ok &= bool((self.scales[r][:m // 256].cpu().numpy().view(np.uint32) == enc[r][1].view(np.uint32)).all())
+        p = m + 4 * nblocks(m)
+        return self.k * (4 * m + p) + self.k * p + 4 * m, t, f"first {m:,} values of each of the {self.k} ranks", ok
+
+
+class Gradients64(Workload):
+    name = "gradients_64mib"
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        import workloads as W
+        self.W = W
+        self.k, self.n = 4, W.GRAD64_N
+        self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n, "codec": "bf16",
+                       "distribution": "N(0, sigma=1e-3), 1% outliers x100",
+                       "path": "4 x encode_bf16 + decode_accumulate"}
+
+    def setup(self):
+        torch = self.torch
+        self.xh = self.W.gradient_ranks(self.k, self.n)
+        self.x = [torch.from_numpy(a).to(self.dev) for a in self.xh]
+        self.codes = [torch.empty(self.n, dtype=torch.uint16, device=self.dev) for _ in range(self.k)]
+        self.out = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+
+    def encode(self, r):
+        self.gb.gb_encode_bf16(self.codes[r], self.x[r])
+
+    def step(self):
+        for r in range(self.k):
+            self.encode(r)
+        self.gb.gb_decode_accumulate(self.out, self.codes, None, self.gb.GB_CODEC_BF16)
+
+    def step_bytes(self):
+        return self.k * 6 * self.n + self.k * 2 * self.n + 4 * self.n
+
+    def timed_kernel(self):
+        return ("encode_bf16_kernel<2>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
+
+    def cpu_sample(self, budget):
+        from oracle import oracle as O
+        import numpy as np
+        m = 1 << 22
+        self.torch.cuda.synchronize()
+        xs = [a[:m] for a in self.xh]
+        t0 = time.perf_counter()
+        codes = [O.encode_bf16(a) for a in xs]
+        want = O.decode_accumulate(codes, None, O.CODEC_BF16)
+        t = time.perf_counter() - t0
+        ok = bool((self.out[:m].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
+        for r in range(self.k):
+            got = self.codes[r][:m].view(self.torch.int16).cpu().numpy().view(np.uint16)
+            ok &= bool((got == codes[r]).all())
+        return self.k * 8 * m + 4 * m, t, f"first {m:,} values of each of the {self.k} ranks", ok
+
+
+class Sweep(Workload):
+    name = "two_island_sweep"
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        import workloads as W
+        self.W = W
+        self.sizes = W.SWEEP_SIZES
+        self.config = {"workload": self.name, "k": 2, "sizes": f"2^8..2^26 values ({len(self.sizes)} sizes)",
+                       "distribution": "N(0,1)", "path": "reduce_sum into a separate output"}
+
+    def setup(self):
+        torch = self.torch
+        self.xh = {n: self.W.normal_ranks(2, n) for n in self.sizes}
+        self.x = {n: [torch.from_numpy(a).to(self.dev) for a in xs] for n, xs in self.xh.items()}
+        self.out = {n: torch.empty(n, dtype=torch.float32, device=self.dev) for n in self.sizes}
+
+    def step(self):
+        for n in self.sizes:
+            self.gb.gb_reduce_sum(self.out[n], self.x[n])
+
+    def step_bytes(self):
+        return sum(12 * n for n in self.sizes)
+
+    def timed_kernel(self):
+        n = self.sizes[-1]
+        return ("reduce_sum_kernel<2,4>", 12 * n, 1, lambda: self.gb.gb_reduce_sum(self.out[n], self.x[n]))
+
+    def cpu_sample(self, budget):
+        from oracle import oracle as O
+        import numpy as np
+        self.torch.cuda.synchronize()
+        t, ok = 0.0, True
+        for n in self.sizes:
+            t0 = time.perf_counter()
+            want = O.reduce_sum(self.xh[n])
+            t += time.perf_counter() - t0
+            ok &= bool((self.out[n].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
+        return self.step_bytes(), t, "the whole sweep", ok
+
+
+class TwoRank(Workload):
+    name = "two_rank_4mib"
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        import workloads as W
+        self.W = W
+        self.n = W.TWO_RANK_N
+        self.config = {"workload": self.name, "k": 2, "n_per_rank": self.n, "distribution": "N(0,1)",
+                       "path": "reduce_sum, encode_bf16 of the sum, decode (k=1)",
+                       "note": "24 MiB per step stays in the 256 MB last-level cache"}
+
+    def setup(self):
+        torch = self.torch
+        self.xh = self.W.normal_ranks(2, self.n)
+        self.x = [torch.from_numpy(a).to(self.dev) for a in self.xh]
+        self.sum = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+        self.codes = torch.empty(self.n, dtype=torch.uint16, device=self.dev)
+        self.dec = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+
+    def step(self):
+        gb = self.gb
+        gb.gb_reduce_sum(self.sum, self.x)
+        gb.gb_encode_bf16(self.codes, self.sum)
+        gb.gb_decode_accumulate(self.dec, [self.codes], None, gb.GB_CODEC_BF16)
+
+    def step_bytes(self):
+        return 12 * self.n + 6 * self.n + 6 * self.n
+
+    def timed_kernel(self):
+        return ("reduce_sum_kernel<2,4>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
+
+    def cpu_sample(self, budget):
+        from oracle import oracle as O
+        import numpy as np
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        s = O.reduce_sum(self.xh)
+        c = O.encode_bf16(s)
+        d = O.decode_accumulate([c], None, O.CODEC_BF16)
+        t = time.perf_counter() - t0
+        ok = bool((self.dec.cpu().numpy().view(np.uint32) == d.view(np.uint32)).all())
+        return self.step_bytes(), t, "the whole workload", ok
+
+
+WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank)}
+
+
+def time_region(torch, stream, fn, reps):
+    """Milliseconds for `reps` calls of fn, HIP events on `stream`."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the leader arithmetic runs on a single device "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); run it with --gpus 1",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import gradient_all_reduce_amd as gb
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload](gb, torch, args)
+    log(f"[bench] workload {wl.name}: allocating and drawing inputs")
+    wl.setup()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ms = time_region(torch, wl.stream, wl.step, args.steps)
+    ms_per_step = ms / args.steps
+    step_bytes = wl.step_bytes()
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    kname, kbytes, klaunches, kfn = wl.timed_kernel()
+    reps = max(3, args.steps)
+    kms = time_region(torch, wl.stream, kfn, reps) / (reps * klaunches)
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} GB/s; {kname}: {kms * 1e3:.2f} us/launch, "
+        f"{achieved:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: oracle on a sample")
+        sb, st, sample, ok = wl.cpu_sample(args.cpu_seconds)
+        cpu = {"value": round(sb / st / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": sample, "seconds": round(st, 2), "gpu_matches_oracle_on_sample": ok}
+        log(f"[bench] oracle {sb / st / 1e9:.3f} GB/s over {sample}; GPU output matches: {ok}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": wl.config,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

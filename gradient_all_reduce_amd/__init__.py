@@ -1,0 +1,208 @@
+"""Python binding of libgbreduce (include/gbreduce.h).
+
+Argument marshalling only: each function takes torch tensors that live in
+device memory, passes their data pointers, sizes and the current HIP stream
+to the C function of the same name, and raises GbError on a failed status.
+Every step of the arithmetic runs in the library's HIP kernels; there is no
+other implementation to fall back to.  If the library was not built this
+module raises ImportError on import.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (one runtime, one device context).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GB_OK", "GB_ERR_INVALID_ARG", "GB_ERR_MISALIGNED", "GB_ERR_UNSUPPORTED",
+    "GB_ERR_WORKSPACE", "GB_ERR_HIP", "GB_CODEC_NONE", "GB_CODEC_BF16",
+    "GB_CODEC_FP8_E4M3_B256", "GB_SCALE_ABSMAX_DIV_448", "GB_SCALE_POW2",
+    "GB_BLOCK", "GB_MAX_K", "GbError", "library_path", "gb_reduce_sum",
+    "gb_encode_bf16", "gb_encode_fp8_e4m3_blockscaled", "gb_decode_accumulate",
+    "gb_bucket_allreduce_local", "gb_payload_bytes", "gb_bucket_workspace_layout",
+    "gb_bucket_workspace_bytes", "gb_status_string", "gb_last_error", "gb_version",
+]
+
+GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
+GB_ERR_UNSUPPORTED, GB_ERR_WORKSPACE, GB_ERR_HIP = 3, 4, 5
+GB_CODEC_NONE, GB_CODEC_BF16, GB_CODEC_FP8_E4M3_B256 = 0, 1, 2
+GB_SCALE_ABSMAX_DIV_448, GB_SCALE_POW2 = 0, 1
+GB_BLOCK = 256
+GB_MAX_K = 8
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgbreduce.so")
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"libgbreduce is not built ({library_path} is missing); build it with "
+        "`python -m gradient_all_reduce_amd.build` or __graft_entry__.build()")
+
+_lib = ctypes.CDLL(library_path)
+
+_P, _S, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_SP = ctypes.POINTER(ctypes.c_size_t)
+_SIGNATURES = {
+    "gb_reduce_sum": (_I, [_P, _PP, _I, _S, _P]),
+    "gb_encode_bf16": (_I, [_P, _P, _S, _P]),
+    "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
+    "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
+    "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
+    "gb_payload_bytes": (_S, [_I, _S]),
+    "gb_bucket_workspace_layout": (_I, [_I, _I, _S, _S, _SP, _SP, _SP, _SP]),
+    "gb_bucket_workspace_bytes": (_S, [_I, _I, _S, _S]),
+    "gb_status_string": (ctypes.c_char_p, [_I]),
+    "gb_last_error": (ctypes.c_char_p, []),
+    "gb_version": (_I, []),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class GbError(RuntimeError):
+    """A libgbreduce call returned a failed gb_status."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{gb_status_string(status)}: {detail}")
+
+
+def _check(status):
+    if status != GB_OK:
+        raise GbError(status, gb_last_error())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr() if t is not None else None
+    return ctypes.cast(arr, _PP)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _device_tensor(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in device memory, not on {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_numel(ts, n, name):
+    for i, t in enumerate(ts):
+        if t.numel() != n:
+            raise ValueError(f"{name}[{i}] has {t.numel()} elements, expected {n}")
+
+
+_CODE_DTYPE = {GB_CODEC_NONE: torch.float32, GB_CODEC_BF16: torch.uint16,
+               GB_CODEC_FP8_E4M3_B256: torch.uint8}
+
+
+def gb_reduce_sum(dst, srcs, stream=None):
+    """dst = srcs[0] + srcs[1] + ... in rank order (fp32, in place if dst is srcs[0])."""
+    _device_tensor(dst, torch.float32, "dst")
+    for i, s in enumerate(srcs):
+        _device_tensor(s, torch.float32, f"srcs[{i}]")
+    _same_numel(srcs, dst.numel(), "srcs")
+    _check(_lib.gb_reduce_sum(_ptr(dst), _ptr_array(srcs), len(srcs), dst.numel(),
+                              _stream(stream, dst.device)))
+
+
+def gb_encode_bf16(codes, src, stream=None):
+    """codes (uint16) = bf16 round-to-nearest-even of src (fp32)."""
+    _device_tensor(codes, torch.uint16, "codes")
+    _device_tensor(src, torch.float32, "src")
+    _same_numel([codes], src.numel(), "codes")
+    _check(_lib.gb_encode_bf16(_ptr(codes), _ptr(src), src.numel(), _stream(stream, src.device)))
+
+
+def gb_encode_fp8_e4m3_blockscaled(codes, scales, src, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                   stream=None):
+    """codes (uint8, E4M3) and scales (fp32, one per 256 values) of src (fp32)."""
+    _device_tensor(codes, torch.uint8, "codes")
+    _device_tensor(scales, torch.float32, "scales")
+    _device_tensor(src, torch.float32, "src")
+    n = src.numel()
+    _same_numel([codes], n, "codes")
+    _same_numel([scales], (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    _check(_lib.gb_encode_fp8_e4m3_blockscaled(_ptr(codes), _ptr(scales), _ptr(src), n,
+                                               int(scale_mode), _stream(stream, src.device)))
+
+
+def gb_decode_accumulate(acc, codes, scales, codec, accumulate=False, stream=None):
+    """acc (fp32) = [acc +] decoded codes[0] + decoded codes[1] + ... in rank order."""
+    _device_tensor(acc, torch.float32, "acc")
+    n = acc.numel()
+    dt = _CODE_DTYPE.get(int(codec))
+    if dt is not None:
+        for i, c in enumerate(codes):
+            _device_tensor(c, dt, f"codes[{i}]")
+        _same_numel(codes, n, "codes")
+    if scales is not None:
+        for i, s in enumerate(scales):
+            _device_tensor(s, torch.float32, f"scales[{i}]")
+        _same_numel(scales, (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    scale_ptrs = _ptr_array(scales) if scales is not None else None
+    _check(_lib.gb_decode_accumulate(_ptr(acc), _ptr_array(codes), scale_ptrs, len(codes), n,
+                                     int(codec), int(bool(accumulate)), _stream(stream, acc.device)))
+
+
+def gb_bucket_allreduce_local(out, srcs, bucket_elems, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                              workspace=None, stream=None):
+    """Bucket stream: per bucket, encode each rank, decode and add in rank order into out."""
+    _device_tensor(out, torch.float32, "out")
+    for i, s in enumerate(srcs):
+        _device_tensor(s, torch.float32, f"srcs[{i}]")
+    n = out.numel()
+    _same_numel(srcs, n, "srcs")
+    ws_bytes = 0
+    if workspace is not None:
+        _device_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(_lib.gb_bucket_allreduce_local(_ptr(out), _ptr_array(srcs), len(srcs), n,
+                                          int(bucket_elems), int(codec), int(scale_mode),
+                                          _ptr(workspace), ws_bytes, _stream(stream, out.device)))
+
+
+def gb_payload_bytes(codec, n):
+    return int(_lib.gb_payload_bytes(int(codec), int(n)))
+
+
+def gb_bucket_workspace_layout(codec, k, n, bucket_elems):
+    """Return dict(codes_stride, scales_offset, scales_stride, total) in bytes."""
+    out = [ctypes.c_size_t(0) for _ in range(4)]
+    _check(_lib.gb_bucket_workspace_layout(int(codec), int(k), int(n), int(bucket_elems),
+                                           *[ctypes.byref(o) for o in out]))
+    return dict(zip(("codes_stride", "scales_offset", "scales_stride", "total"),
+                    (o.value for o in out)))
+
+
+def gb_bucket_workspace_bytes(codec, k, n, bucket_elems):
+    return int(_lib.gb_bucket_workspace_bytes(int(codec), int(k), int(n), int(bucket_elems)))
+
+
+def gb_status_string(status):
+    return _lib.gb_status_string(int(status)).decode()
+
+
+def gb_last_error():
+    return _lib.gb_last_error().decode()
+
+
+def gb_version():
+    return int(_lib.gb_version())

@@ -1,0 +1,263 @@
+// gb_api.cpp — the C ABI of libgbreduce (include/gbreduce.h): argument
+// validation, workspace layout and kernel launch.  Nothing is enqueued unless
+// every argument is valid; no call allocates device memory.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gb_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gb_status fail(gb_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gb_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GB_OK;
+  return fail(GB_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t nblocks(size_t n) { return (n + GB_BLOCK - 1) / GB_BLOCK; }
+
+size_t code_bytes(int codec, size_t n) {
+  switch (codec) {
+    case GB_CODEC_NONE: return 4 * n;
+    case GB_CODEC_BF16: return 2 * n;
+    case GB_CODEC_FP8_E4M3_B256: return n;
+    default: return 0;
+  }
+}
+
+bool known_codec(int codec) {
+  return codec == GB_CODEC_NONE || codec == GB_CODEC_BF16 || codec == GB_CODEC_FP8_E4M3_B256;
+}
+bool known_mode(int mode) { return mode == GB_SCALE_ABSMAX_DIV_448 || mode == GB_SCALE_POW2; }
+
+gb_status check_k(int k, const char* fn) {
+  if (k < 1 || k > GB_MAX_K) {
+    return fail(GB_ERR_INVALID_ARG, "%s: k = %d is outside 1..%d", fn, k, GB_MAX_K);
+  }
+  return GB_OK;
+}
+
+gb_status check_array(const void* p, size_t align, const char* fn, const char* name) {
+  if (p == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+  if (!aligned(p, align)) {
+    return fail(GB_ERR_MISALIGNED, "%s: %s = %p is not %zu-byte aligned", fn, name, p, align);
+  }
+  return GB_OK;
+}
+
+gb_status check_table(const void* const* table, int k, size_t align, const char* fn, const char* name,
+                      gb::PtrTable* out) {
+  if (table == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: %s array is NULL", fn, name);
+  for (int r = 0; r < k; r++) {
+    char label[64];
+    std::snprintf(label, sizeof label, "%s[%d]", name, r);
+    gb_status s = check_array(table[r], align, fn, label);
+    if (s != GB_OK) return s;
+    out->p[r] = table[r];
+  }
+  return GB_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int gb_version(void) { return GB_VERSION; }
+
+const char* gb_status_string(int status) {
+  switch (status) {
+    case GB_OK: return "GB_OK";
+    case GB_ERR_INVALID_ARG: return "GB_ERR_INVALID_ARG";
+    case GB_ERR_MISALIGNED: return "GB_ERR_MISALIGNED";
+    case GB_ERR_UNSUPPORTED: return "GB_ERR_UNSUPPORTED";
+    case GB_ERR_WORKSPACE: return "GB_ERR_WORKSPACE";
+    case GB_ERR_HIP: return "GB_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* gb_last_error(void) { return g_last_error; }
+
+size_t gb_payload_bytes(int codec, size_t n) {
+  if (!known_codec(codec)) return 0;
+  return code_bytes(codec, n) + (codec == GB_CODEC_FP8_E4M3_B256 ? 4 * nblocks(n) : 0);
+}
+
+gb_status gb_bucket_workspace_layout(int codec, int k, size_t n, size_t bucket_elems,
+                                     size_t* codes_stride, size_t* scales_offset,
+                                     size_t* scales_stride, size_t* total) {
+  const char* fn = "gb_bucket_workspace_layout";
+  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (bucket_elems == 0 || bucket_elems % GB_BLOCK != 0) {
+    return fail(GB_ERR_INVALID_ARG, "%s: bucket_elems = %zu is not a positive multiple of %d", fn,
+                bucket_elems, GB_BLOCK);
+  }
+  if (!codes_stride || !scales_offset || !scales_stride || !total) {
+    return fail(GB_ERR_INVALID_ARG, "%s: an output pointer is NULL", fn);
+  }
+  if (codec == GB_CODEC_NONE) {
+    *codes_stride = *scales_offset = *scales_stride = *total = 0;
+    return GB_OK;
+  }
+  const size_t cs = round_up(code_bytes(codec, n), 256);
+  const size_t ss = codec == GB_CODEC_FP8_E4M3_B256 ? round_up(4 * nblocks(n), 256) : 0;
+  *codes_stride = cs;
+  *scales_offset = (size_t)k * cs;
+  *scales_stride = ss;
+  *total = (size_t)k * (cs + ss);
+  return GB_OK;
+}
+
+size_t gb_bucket_workspace_bytes(int codec, int k, size_t n, size_t bucket_elems) {
+  size_t cs, so, ss, total;
+  char saved[sizeof g_last_error];
+  std::memcpy(saved, g_last_error, sizeof saved);
+  gb_status s = gb_bucket_workspace_layout(codec, k, n, bucket_elems, &cs, &so, &ss, &total);
+  std::memcpy(g_last_error, saved, sizeof saved);  // a size query reports no failure
+  return s == GB_OK ? total : 0;
+}
+
+gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n, void* stream) {
+  const char* fn = "gb_reduce_sum";
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (n == 0) return GB_OK;
+  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+  gb::PtrTable t = {};
+  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) {
+    return s;
+  }
+  return from_hip(gb::launch_reduce_sum(dst, t, k, n, false, as_stream(stream)), fn);
+}
+
+gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stream) {
+  const char* fn = "gb_encode_bf16";
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  return from_hip(gb::launch_encode_bf16(codes, src, n, as_stream(stream)), fn);
+}
+
+gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales, const float* src, size_t n,
+                                         int scale_mode, void* stream) {
+  const char* fn = "gb_encode_fp8_e4m3_blockscaled";
+  if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  return from_hip(gb::launch_encode_fp8(codes, scales, src, n, scale_mode, as_stream(stream)), fn);
+}
+
+gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float* const* scales, int k,
+                               size_t n, int codec, int accumulate, void* stream) {
+  const char* fn = "gb_decode_accumulate";
+  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (accumulate != 0 && accumulate != 1) {
+    return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
+  }
+  if (n == 0) return GB_OK;
+  if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
+  gb::PtrTable c = {};
+  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes", &c)) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  switch (codec) {
+    case GB_CODEC_NONE:
+      return from_hip(gb::launch_reduce_sum(acc, c, k, n, accumulate != 0, st), fn);
+    case GB_CODEC_BF16:
+      return from_hip(gb::launch_decode_bf16(acc, c, k, n, accumulate != 0, st), fn);
+    default: {
+      gb::PtrTable sc = {};
+      if ((s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales", &sc)) != GB_OK) {
+        return s;
+      }
+      return from_hip(gb::launch_decode_fp8(acc, c, sc, k, n, accumulate != 0, st), fn);
+    }
+  }
+}
+
+gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k, size_t n,
+                                    size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const char* fn = "gb_bucket_allreduce_local";
+  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  }
+  size_t cs, so, ss, need;
+  gb_status s = gb_bucket_workspace_layout(codec, k, n, bucket_elems, &cs, &so, &ss, &need);
+  if (s != GB_OK) {
+    // re-label the failure with this function's name
+    return fail(s, "%s: %s", fn, g_last_error + std::strlen("gb_bucket_workspace_layout: "));
+  }
+  if (n == 0) return GB_OK;
+  if ((s = check_array(out, GB_ALIGN, fn, "out")) != GB_OK) return s;
+  gb::PtrTable t = {};
+  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) {
+    return s;
+  }
+  if (codec != GB_CODEC_NONE) {
+    if (workspace == nullptr || workspace_bytes < need) {
+      return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes,
+                  need);
+    }
+    if (!aligned(workspace, 256)) {
+      return fail(GB_ERR_MISALIGNED, "%s: workspace = %p is not 256-byte aligned", fn, workspace);
+    }
+  }
+  hipStream_t st = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  // One launch per bucket, in order, on the caller's stream.  Each bucket
+  // starts on a 256-value boundary, so its blocks are the whole buffer's
+  // blocks and rank r's payload lands where a whole-buffer encode puts it.
+  for (size_t start = 0; start < n;) {
+    const size_t len = n - start < bucket_elems ? n - start : bucket_elems;
+    gb::PtrTable src = {};
+    for (int r = 0; r < k; r++) src.p[r] = srcs[r] + start;
+    hipError_t e;
+    if (codec == GB_CODEC_NONE) {
+      e = gb::launch_reduce_sum(out + start, src, k, len, false, st);
+    } else if (codec == GB_CODEC_BF16) {
+      uint16_t* c[GB_MAX_K];
+      for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs) + start;
+      e = gb::launch_fused_bf16(out + start, src, c, k, len, st);
+    } else {
+      uint8_t* c[GB_MAX_K];
+      float* sc[GB_MAX_K];
+      for (int r = 0; r < k; r++) {
+        c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs) + start;
+        sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss) + start / GB_BLOCK;
+      }
+      e = gb::launch_fused_fp8(out + start, src, c, sc, k, len, scale_mode, st);
+    }
+    if (e != hipSuccess) return from_hip(e, fn);
+    start += len;
+  }
+  return GB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// gb_internal.h — launchers shared by the C-ABI layer (gb_api.cpp) and the
+// HIP kernels (gb_kernels.hip).  Not installed; the public ABI is
+// include/gbreduce.h.
+//
+// Every launcher assumes its arguments were validated by gb_api.cpp: pointers
+// non-null and aligned as the ABI requires, 1 <= k <= GB_MAX_K, n > 0.  Each
+// returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gbreduce.h"
+
+namespace gb {
+
+// Up to GB_MAX_K device pointers, passed to kernels by value.
+struct PtrTable {
+  const void* p[GB_MAX_K];
+};
+
+// Values per fp8 scale block, and blocks per workgroup in the block kernels
+// (a 256-lane workgroup = 4 wavefronts x 4 rows of 16 lanes, one row per
+// block).
+constexpr size_t kBlock = GB_BLOCK;
+
+hipError_t launch_reduce_sum(float* dst, const PtrTable& srcs, int k, size_t n,
+                             bool accumulate, hipStream_t stream);
+hipError_t launch_encode_bf16(uint16_t* codes, const float* src, size_t n,
+                              hipStream_t stream);
+hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const float* src,
+                             size_t n, int scale_mode, hipStream_t stream);
+hipError_t launch_decode_bf16(float* acc, const PtrTable& codes, int k,
+                              size_t n, bool accumulate, hipStream_t stream);
+hipError_t launch_decode_fp8(float* acc, const PtrTable& codes,
+                             const PtrTable& scales, int k, size_t n,
+                             bool accumulate, hipStream_t stream);
+// One pass over [0, n) of k sources: encode each source into its payload
+// (codes[r], scales[r]) and write the decoded rank-order sum to out.
+hipError_t launch_fused_bf16(float* out, const PtrTable& srcs,
+                             uint16_t* const* codes, int k, size_t n,
+                             hipStream_t stream);
+hipError_t launch_fused_fp8(float* out, const PtrTable& srcs,
+                            uint8_t* const* codes, float* const* scales, int k,
+                            size_t n, int scale_mode, hipStream_t stream);
+
+}  // namespace gb

@@ -1,0 +1,133 @@
+"""The C-ABI library loads without a GPU, exports every symbol its header
+declares, and its host-side logic (argument validation, sizes, workspace
+layout, status strings) behaves as documented.  No call here reaches a
+kernel: each one fails validation, or is a host-only query."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gbreduce.h")
+
+
+@pytest.fixture(scope="module")
+def gb():
+    import gradient_all_reduce_amd as lib
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for f in ["gb_reduce_sum", "gb_encode_bf16", "gb_encode_fp8_e4m3_blockscaled",
+              "gb_decode_accumulate", "gb_bucket_allreduce_local"]:
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(gb):
+    lib = ctypes.CDLL(gb.library_path)
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing
+
+
+def test_single_hip_runtime_in_process(gb):
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) <= 1, paths
+
+
+def test_constants_match_header(gb):
+    text = open(HEADER).read()
+    for name in ["GB_BLOCK", "GB_MAX_K", "GB_VERSION"]:
+        v = int(re.search(rf"#define {name} (\d+)", text).group(1))
+        if name == "GB_VERSION":
+            assert gb.gb_version() == v
+        else:
+            assert getattr(gb, name) == v
+    for name in ["GB_OK", "GB_ERR_INVALID_ARG", "GB_ERR_MISALIGNED", "GB_ERR_UNSUPPORTED",
+                 "GB_ERR_WORKSPACE", "GB_ERR_HIP", "GB_CODEC_NONE", "GB_CODEC_BF16",
+                 "GB_CODEC_FP8_E4M3_B256", "GB_SCALE_ABSMAX_DIV_448", "GB_SCALE_POW2"]:
+        v = int(re.search(rf"\b{name} = (\d+)", text).group(1))
+        assert getattr(gb, name) == v, name
+
+
+def test_status_strings(gb):
+    assert gb.gb_status_string(0) == "GB_OK"
+    assert gb.gb_status_string(4) == "GB_ERR_WORKSPACE"
+    assert gb.gb_status_string(99) == "unknown status"
+
+
+def test_payload_bytes(gb):
+    n = 67_108_864
+    assert gb.gb_payload_bytes(gb.GB_CODEC_NONE, n) == 4 * n
+    assert gb.gb_payload_bytes(gb.GB_CODEC_BF16, n) == 2 * n
+    assert gb.gb_payload_bytes(gb.GB_CODEC_FP8_E4M3_B256, n) == n + 4 * (n // 256)
+    assert gb.gb_payload_bytes(gb.GB_CODEC_FP8_E4M3_B256, 257) == 257 + 8
+    assert gb.gb_payload_bytes(7, 10) == 0
+
+
+def test_workspace_layout(gb):
+    lay = gb.gb_bucket_workspace_layout(gb.GB_CODEC_FP8_E4M3_B256, 4, 1000, 256)
+    assert lay == {"codes_stride": 1024, "scales_offset": 4096, "scales_stride": 256, "total": 5120}
+    lay = gb.gb_bucket_workspace_layout(gb.GB_CODEC_BF16, 2, 1000, 512)
+    assert lay == {"codes_stride": 2048, "scales_offset": 4096, "scales_stride": 0, "total": 4096}
+    n, b = 1_000_000_000, 6_553_600
+    total = gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, 4, n, b)
+    assert total == 4 * (n + 4 * 3_906_250 + (256 - 4 * 3_906_250 % 256) % 256)
+    assert gb.gb_bucket_workspace_bytes(gb.GB_CODEC_NONE, 4, n, b) == 0
+    assert gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, 4, n, 100) == 0
+    assert gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, 0, n, b) == 0
+    with pytest.raises(gb.GbError):
+        gb.gb_bucket_workspace_layout(9, 4, n, b)
+
+
+# Raw calls with fake (never dereferenced) addresses: validation must reject
+# them before any HIP call.
+def _arr(*addrs):
+    a = (ctypes.c_void_p * len(addrs))(*addrs)
+    return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+
+
+@pytest.mark.parametrize("call,status,msg", [
+    (lambda L: L.gb_reduce_sum(None, _arr(256), 0, 10, None), 1, "k = 0"),
+    (lambda L: L.gb_reduce_sum(None, _arr(256), 9, 10, None), 1, "k = 9"),
+    (lambda L: L.gb_reduce_sum(None, _arr(256), 1, 10, None), 1, "dst is NULL"),
+    (lambda L: L.gb_reduce_sum(ctypes.c_void_p(260), _arr(256), 1, 10, None), 2, "dst"),
+    (lambda L: L.gb_reduce_sum(ctypes.c_void_p(256), _arr(256, 0), 2, 10, None), 1, "srcs[1] is NULL"),
+    (lambda L: L.gb_reduce_sum(ctypes.c_void_p(256), _arr(256, 264), 2, 10, None), 2, "srcs[1]"),
+    (lambda L: L.gb_reduce_sum(ctypes.c_void_p(256), None, 2, 10, None), 1, "srcs array is NULL"),
+    (lambda L: L.gb_encode_bf16(ctypes.c_void_p(258), ctypes.c_void_p(256), 10, None), 2, "codes"),
+    (lambda L: L.gb_encode_fp8_e4m3_blockscaled(ctypes.c_void_p(256), ctypes.c_void_p(258),
+                                                ctypes.c_void_p(256), 10, 0, None), 2, "scales"),
+    (lambda L: L.gb_encode_fp8_e4m3_blockscaled(None, None, None, 10, 2, None), 3, "scale mode"),
+    (lambda L: L.gb_decode_accumulate(ctypes.c_void_p(256), _arr(256), None, 1, 10, 5, 0, None), 3, "codec"),
+    (lambda L: L.gb_decode_accumulate(ctypes.c_void_p(256), _arr(256), None, 1, 10, 1, 2, None), 1, "accumulate"),
+    (lambda L: L.gb_decode_accumulate(ctypes.c_void_p(256), _arr(256), None, 1, 10, 2, 0, None), 1, "scales array"),
+    (lambda L: L.gb_bucket_allreduce_local(ctypes.c_void_p(256), _arr(256), 1, 1000, 300, 0, 0,
+                                           None, 0, None), 1, "bucket_elems"),
+    (lambda L: L.gb_bucket_allreduce_local(ctypes.c_void_p(256), _arr(256), 1, 1000, 256, 2, 0,
+                                           ctypes.c_void_p(512), 100, None), 4, "needed"),
+    (lambda L: L.gb_bucket_allreduce_local(ctypes.c_void_p(256), _arr(256), 1, 1000, 256, 2, 0,
+                                           ctypes.c_void_p(272), 1 << 20, None), 2, "workspace"),
+    (lambda L: L.gb_bucket_allreduce_local(ctypes.c_void_p(256), _arr(256), 1, 1000, 256, 2, 5,
+                                           ctypes.c_void_p(512), 1 << 20, None), 3, "scale mode"),
+])
+def test_validation_rejects_before_launch(gb, call, status, msg):
+    assert call(gb._lib) == status
+    assert msg in gb.gb_last_error()
+
+
+def test_zero_length_returns_ok_without_pointers(gb):
+    L = gb._lib
+    assert L.gb_reduce_sum(None, None, 2, 0, None) == 0
+    assert L.gb_encode_bf16(None, None, 0, None) == 0
+    assert L.gb_encode_fp8_e4m3_blockscaled(None, None, None, 0, 0, None) == 0
+    assert L.gb_decode_accumulate(None, None, None, 3, 0, 2, 0, None) == 0
+    assert L.gb_bucket_allreduce_local(None, None, 2, 0, 256, 2, 0, None, 0, None) == 0
