@@ -16,7 +16,9 @@ Workloads (inputs from workloads.py):
                    of 25 MiB; per bucket: fp8 E4M3 encode of every rank with
                    one absmax/448 scale per 256 values, decode and add in rank
                    order, fp32 sum written out.  One gb_bucket_allreduce_local
-                   call per step (one launch per bucket).
+                   call over the whole stream per step (one launch; buckets
+                   start on block boundaries).  The same pass made as one call
+                   per bucket, as a DDP hook would issue it, is reported too.
   gradients_256mib k=4 x 2^26 fp32; 4 x gb_encode_fp8_e4m3_blockscaled +
                    gb_decode_accumulate(fp8).
   gradients_64mib  k=4 x 2^24 fp32; 4 x gb_encode_bf16 + gb_decode_accumulate(bf16).
@@ -113,8 +115,28 @@ class DdpBuckets(Workload):
         return sum(self.bytes_for(l) for _, l in self.W.ddp_buckets())
 
     def timed_kernel(self):
-        nb = len(self.W.ddp_buckets())
-        return ("fused_fp8_kernel<4>", self.step_bytes() / nb, nb, self.step)
+        return ("fused_fp8_kernel<4>", self.step_bytes(), 1, self.step)
+
+    def per_bucket_step(self):
+        gb = self.gb
+        for start, length in self.W.ddp_buckets():
+            gb.gb_bucket_allreduce_local(self.out[start:start + length],
+                                         [t[start:start + length] for t in self.x], self.bucket,
+                                         gb.GB_CODEC_FP8_E4M3_B256, self.mode,
+                                         self.ws_views[start])
+
+    def extra(self, time_region, reps):
+        """Throughput of the same pass issued as one call per bucket."""
+        torch, gb = self.torch, self.gb
+        # per-bucket workspaces: each bucket's payloads in its own slice
+        self.ws_views = {}
+        for start, length in self.W.ddp_buckets():
+            need = gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, self.k, length, self.bucket)
+            self.ws_views[start] = self.ws[self.k * start + 4 * self.k * (start // 256):][:need]
+        self.per_bucket_step()
+        ms = time_region(self.per_bucket_step, reps) / reps
+        return {"per_bucket_calls_gbs": round(self.step_bytes() / (ms * 1e-3) / 1e9, 2),
+                "per_bucket_calls_ms": round(ms, 4)}
 
     def cpu_sample(self, budget):
         """Run the oracle on the first buckets; compare with the GPU's."""
@@ -180,7 +202,7 @@ class Gradients256(Workload):
 
     def timed_kernel(self):
         per = 4 * self.n + self.n + 4 * nblocks(self.n)
-        return ("encode_fp8_kernel<2>", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
+        return ("encode_fp8_kernel", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -231,7 +253,7 @@ class Gradients64(Workload):
         return self.k * 6 * self.n + self.k * 2 * self.n + 4 * self.n
 
     def timed_kernel(self):
-        return ("encode_bf16_kernel<2>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
+        return ("encode_bf16_kernel", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -276,7 +298,7 @@ class Sweep(Workload):
 
     def timed_kernel(self):
         n = self.sizes[-1]
-        return ("reduce_sum_kernel<2,4>", 12 * n, 1, lambda: self.gb.gb_reduce_sum(self.out[n], self.x[n]))
+        return ("reduce_sum_kernel<2>", 12 * n, 1, lambda: self.gb.gb_reduce_sum(self.out[n], self.x[n]))
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -321,7 +343,7 @@ class TwoRank(Workload):
         return 12 * self.n + 6 * self.n + 6 * self.n
 
     def timed_kernel(self):
-        return ("reduce_sum_kernel<2,4>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
+        return ("reduce_sum_kernel<2>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -388,6 +410,11 @@ def main():
     log(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} GB/s; {kname}: {kms * 1e3:.2f} us/launch, "
         f"{achieved:.1f} GB/s")
 
+    extra = {}
+    if hasattr(wl, "extra"):
+        extra = wl.extra(lambda fn, reps: time_region(torch, wl.stream, fn, reps), max(3, args.steps // 2))
+        log(f"[bench] extra: {extra}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on a sample")
@@ -409,7 +436,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": wl.config,
+        "config": dict(wl.config, **extra),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3)},

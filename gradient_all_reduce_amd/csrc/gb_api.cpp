@@ -231,32 +231,29 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
   }
   hipStream_t st = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
-  // One launch per bucket, in order, on the caller's stream.  Each bucket
-  // starts on a 256-value boundary, so its blocks are the whole buffer's
-  // blocks and rank r's payload lands where a whole-buffer encode puts it.
-  for (size_t start = 0; start < n;) {
-    const size_t len = n - start < bucket_elems ? n - start : bucket_elems;
-    gb::PtrTable src = {};
-    for (int r = 0; r < k; r++) src.p[r] = srcs[r] + start;
-    hipError_t e;
-    if (codec == GB_CODEC_NONE) {
-      e = gb::launch_reduce_sum(out + start, src, k, len, false, st);
-    } else if (codec == GB_CODEC_BF16) {
-      uint16_t* c[GB_MAX_K];
-      for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs) + start;
-      e = gb::launch_fused_bf16(out + start, src, c, k, len, st);
-    } else {
-      uint8_t* c[GB_MAX_K];
-      float* sc[GB_MAX_K];
-      for (int r = 0; r < k; r++) {
-        c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs) + start;
-        sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss) + start / GB_BLOCK;
-      }
-      e = gb::launch_fused_fp8(out + start, src, c, sc, k, len, scale_mode, st);
+  // Every bucket starts on a 256-value boundary, so the blocks of a bucket
+  // are blocks of the whole buffer and the buckets together are exactly one
+  // pass over [0, n): a single launch covers all of them, its workgroups
+  // taking blocks (hence buckets) in order.  The result equals one launch per
+  // bucket bit for bit, without a partly idle GPU at the end of every bucket.
+  // Rank r's payload lands where a whole-buffer encode would put it.
+  hipError_t e;
+  if (codec == GB_CODEC_NONE) {
+    e = gb::launch_reduce_sum(out, t, k, n, false, st);
+  } else if (codec == GB_CODEC_BF16) {
+    uint16_t* c[GB_MAX_K];
+    for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
+    e = gb::launch_fused_bf16(out, t, c, k, n, st);
+  } else {
+    uint8_t* c[GB_MAX_K];
+    float* sc[GB_MAX_K];
+    for (int r = 0; r < k; r++) {
+      c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
+      sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
     }
-    if (e != hipSuccess) return from_hip(e, fn);
-    start += len;
+    e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, st);
   }
+  if (e != hipSuccess) return from_hip(e, fn);
   return GB_OK;
 }
 

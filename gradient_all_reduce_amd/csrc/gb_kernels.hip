@@ -4,24 +4,27 @@
 // All of this work streams HBM: a few integer and float operations per 4-byte
 // element, no reuse, no contraction (so no MFMA).  The kernels are shaped for
 // that:
-//   * every lane moves 16-byte vectors, and each load instruction of a 64-lane
-//     wavefront covers whole 256-byte runs, so requests coalesce;
-//   * a lane issues all of its loads (every rank, several vectors) before it
-//     computes, keeping many bytes in flight per compute unit;
-//   * the k contributions of an element are read once and combined in
-//     registers (reduce, encode and decode-accumulate are fused where the
-//     call allows it);
-//   * the fp8 block maximum is reduced across the 16 lanes of one DPP row
-//     (four row-local DPP steps, no LDS and no barrier): a 256-value block is
-//     one row of 16 lanes holding 16 values each, so a wavefront works on 4
-//     blocks and a 256-lane workgroup on 16.
+//   * every lane moves 16-byte vectors (4-byte words for fp8 codes), and each
+//     load or store instruction of a 16-lane row covers 256 contiguous bytes,
+//     so requests coalesce into whole cache lines;
+//   * loads and stores carry the non-temporal hint: each byte is touched once,
+//     so nothing is worth keeping in L2 or the last-level cache;
+//   * a lane issues all of its loads (every rank) before it computes, and the
+//     k contributions of an element are combined in registers: reduce, encode
+//     and decode-accumulate are fused where the call allows it;
+//   * the fp8 block maximum is reduced across the 16 lanes of one DPP row (four
+//     row-local DPP steps, no LDS, no barrier): a 256-value block is one row of
+//     16 lanes holding 16 values each, a wavefront works on 4 blocks and a
+//     256-lane workgroup on 16;
+//   * E4M3 conversion uses gfx950's packed converters (v_cvt_pk_fp8_f32 to
+//     encode two values per instruction, v_cvt_pk_f32_fp8 to decode two).
 //
 // Arithmetic follows the gpubridge README, "How it works" (sum of island sums)
 // and "Bridge compression" (bf16; OCP E4M3 with one scale per 256 values;
 // decode and add in float32).  Every rounding is IEEE binary32
-// round-to-nearest-even with subnormals kept, and nothing is contracted into
-// a fused multiply-add (built with -ffp-contract=off), so results are
-// independent of the launch shape.
+// round-to-nearest-even with subnormals kept, and nothing is contracted into a
+// fused multiply-add (built with -ffp-contract=off), so results do not depend
+// on the launch shape.
 #include <hip/hip_runtime.h>
 
 #include "gb_internal.h"
@@ -30,6 +33,7 @@ namespace gb {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 struct OutTable {
@@ -41,27 +45,27 @@ constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
 
+// ---------------------------------------------------------------------------
+// Streaming memory access (non-temporal) with guarded variants for the ragged
+// end of a buffer.
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ f4 load4(const float* p) {
-  return *reinterpret_cast<const f4*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
 }
 __device__ __forceinline__ void store4(float* p, f4 v) {
-  *reinterpret_cast<f4*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
 }
 
-// Elements [i, min(i + 4, n)) of p, zero beyond n.  Requires i < n.
-__device__ __forceinline__ f4 load4_tail(const float* p, size_t i, size_t n) {
-  f4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-  v.x = p[i];
-  if (i + 1 < n) v.y = p[i + 1];
-  if (i + 2 < n) v.z = p[i + 2];
-  if (i + 3 < n) v.w = p[i + 3];
-  return v;
-}
+// Elements [i, i + 4) of p, zero at and beyond n.
 __device__ __forceinline__ f4 load4_any(const float* p, size_t i, size_t n) {
   if (i + 4 <= n) return load4(p + i);
-  if (i < n) return load4_tail(p, i, n);
-  return f4{0.0f, 0.0f, 0.0f, 0.0f};
+  f4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (i < n) v.x = p[i];
+  if (i + 1 < n) v.y = p[i + 1];
+  if (i + 2 < n) v.z = p[i + 2];
+  return v;
 }
+// Stores the elements of [i, i + 4) that lie below n.
 __device__ __forceinline__ void store4_any(float* p, size_t i, size_t n, f4 v) {
   if (i + 4 <= n) {
     store4(p + i, v);
@@ -72,26 +76,95 @@ __device__ __forceinline__ void store4_any(float* p, size_t i, size_t n, f4 v) {
   if (i + 2 < n) p[i + 2] = v.z;
 }
 
+// 4 fp8 codes of elements [i, i + 4) as one little-endian word, clipped to n.
+__device__ __forceinline__ uint32_t load_codes4(const uint8_t* codes, size_t i, size_t n) {
+  if (i + 4 <= n) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + i));
+  uint32_t w = 0;
+  for (int e = 0; e < 3; e++) {
+    if (i + e < n) w |= (uint32_t)codes[i + e] << (8 * e);
+  }
+  return w;
+}
+__device__ __forceinline__ void store_codes4(uint8_t* codes, size_t i, size_t n, uint32_t w) {
+  if (i + 4 <= n) {
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + i));
+    return;
+  }
+  for (int e = 0; e < 3; e++) {
+    if (i + e < n) codes[i + e] = (uint8_t)(w >> (8 * e));
+  }
+}
+
+// 8 bf16 codes of elements [i, i + 8) as 4 words, clipped to n.
+__device__ __forceinline__ u4 load_bf16_8(const uint16_t* codes, size_t i, size_t n) {
+  if (i + 8 <= n) return __builtin_nontemporal_load(reinterpret_cast<const u4*>(codes + i));
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; e++) {
+    if (i + e < n) w[e >> 1] |= (uint32_t)codes[i + e] << (16 * (e & 1));
+  }
+  return u4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ void store_bf16_8(uint16_t* codes, size_t i, size_t n, u4 w) {
+  if (i + 8 <= n) {
+    __builtin_nontemporal_store(w, reinterpret_cast<u4*>(codes + i));
+    return;
+  }
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int e = 0; e < 8; e++) {
+    if (i + e < n) codes[i + e] = (uint16_t)(ws[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
 // ---------------------------------------------------------------------------
-// bf16: nearest value, ties to the even code (carry into the exponent gives
-// the IEEE overflow to Inf); NaN keeps sign and top payload, quiet bit set.
+// bf16: nearest value, ties to the even code (the carry of the rounding add
+// runs into the exponent, which gives IEEE overflow to Inf); a NaN keeps its
+// sign and top payload bits with the quiet bit set.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t bf16_code(float x) {
   const uint32_t u = fbits(x);
   const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
 }
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return bitsf(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return bitsf(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ u4 bf16_pack8(f4 lo, f4 hi) {
+  return u4{bf16_code(lo.x) | (bf16_code(lo.y) << 16), bf16_code(lo.z) | (bf16_code(lo.w) << 16),
+            bf16_code(hi.x) | (bf16_code(hi.y) << 16), bf16_code(hi.z) | (bf16_code(hi.w) << 16)};
+}
+// bf16 -> fp32 is exact: the code is the top half of the binary32 pattern.
+__device__ __forceinline__ f4 bf16_unpack_lo(u4 w) {
+  return f4{bitsf(w.x << 16), bitsf(w.x & 0xFFFF0000u), bitsf(w.y << 16), bitsf(w.y & 0xFFFF0000u)};
+}
+__device__ __forceinline__ f4 bf16_unpack_hi(u4 w) {
+  return f4{bitsf(w.z << 16), bitsf(w.z & 0xFFFF0000u), bitsf(w.w << 16), bitsf(w.w & 0xFFFF0000u)};
+}
 
 // ---------------------------------------------------------------------------
-// fp8 (OCP E4M3, bias 7, largest finite 448 = 0x7E, S.1111.111 = NaN).
+// fp8: OCP E4M3 (bias 7, largest finite 448 = 0x7E, S.1111.111 = NaN), one
+// fp32 scale per 256-value block.
 // ---------------------------------------------------------------------------
-// |x| as an unsigned integer, NaN counted as 0: the integer maximum of these
-// is the bit pattern of the largest non-NaN magnitude, in any order.
-__device__ __forceinline__ uint32_t magnitude_bits(float x) {
-  const uint32_t m = fbits(x) & 0x7FFFFFFFu;
-  return m > 0x7F800000u ? 0u : m;
+// Largest non-NaN magnitude of a lane's 16 values, as a bit pattern: the
+// unsigned maximum of |x| bit patterns orders like the magnitudes, in any
+// order of evaluation.  A NaN among the 16 shows as a pattern above Inf's;
+// only then are the values scanned again with the NaNs counted as 0.
+__device__ __forceinline__ uint32_t lane_absmax16(const f4 (&x)[4]) {
+  uint32_t a = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    a = max(a, max(fbits(x[j].x) & 0x7FFFFFFFu, fbits(x[j].y) & 0x7FFFFFFFu));
+    a = max(a, max(fbits(x[j].z) & 0x7FFFFFFFu, fbits(x[j].w) & 0x7FFFFFFFu));
+  }
+  if (a > 0x7F800000u) {
+    a = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t m = fbits(x[j][e]) & 0x7FFFFFFFu;
+        a = max(a, m > 0x7F800000u ? 0u : m);
+      }
+    }
+  }
+  return a;
 }
 
 // Maximum over the 16 lanes of this lane's DPP row; every lane of the row
@@ -140,40 +213,46 @@ __device__ __forceinline__ double scale_reciprocal(float s) {
 // both round to the same binary32 value; below 2^-126 both give values that
 // encode to E4M3 zero.  An s of 0 gives rinv = 1 (v = x); s = Inf gives
 // rinv = 0, i.e. x / Inf = +-0 and Inf / Inf = NaN, as IEEE division does.
-__device__ __forceinline__ float quotient(float x, double rinv) {
-  return (float)((double)x * rinv);
+__device__ __forceinline__ f4 quotient4(f4 x, double rinv) {
+  return f4{(float)((double)x.x * rinv), (float)((double)x.y * rinv), (float)((double)x.z * rinv),
+            (float)((double)x.w * rinv)};
 }
 
-// E4M3 code of v (already divided by the scale), the sign bit taken from x.
-// |v| >= 2^-6: round the binary32 fraction to 3 bits (ties to even, the carry
-// runs into the exponent), re-bias the exponent from 127 to 7 (120 << 3 =
-// 960), saturate at 0x7E.  |v| < 2^-6: the subnormal code is rint(|v| * 2^9),
-// the integer rounding done by adding 2^23.  NaN gives 0x7F.
-__device__ __forceinline__ uint32_t e4m3_code(float v, float x) {
-  const uint32_t m = fbits(v) & 0x7FFFFFFFu;
-  uint32_t c;
-  if (m >= 0x3C800000u) {
-    const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
-    c = min(r - 960u, 0x7Eu);
-  } else {
-    const float t = bitsf(m) * 512.0f;
-    c = fbits(t + 8388608.0f) - 0x4B000000u;
+// E4M3 codes of 4 quotients v, packed little-endian, sign bits from the
+// inputs x.  The hardware converter rounds to nearest even and agrees with the
+// E4M3 definition for every |v| <= 448 * (1 + 2^-23) (checked over all such
+// binary32 values); above that it does not saturate, so callers bring larger
+// quotients back to +-448 first (see clamp448).  It returns 0xFF for any NaN,
+// so the sign bit is replaced by x's: NaN codes become 0x7F | sign.
+__device__ __forceinline__ uint32_t e4m3_pack4(f4 v, f4 x) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x, v.y, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z, v.w, w, true);
+  const uint32_t s01 = __builtin_amdgcn_perm(fbits(x.y), fbits(x.x), 0x0C0C0703u);  // x.x, x.y top bytes -> bytes 0, 1
+  const uint32_t s23 = __builtin_amdgcn_perm(fbits(x.w), fbits(x.z), 0x07030C0Cu);  // x.z, x.w top bytes -> bytes 2, 3
+  return ((uint32_t)w & 0x7F7F7F7Fu) | ((s01 | s23) & 0x80808080u);
+}
+
+// Saturation of quotients to +-448, NaN kept.  Only a block whose scale is
+// subnormal needs it: a normal s = RN(a / 448) is within 2^-24 of a / 448, so
+// |x / s| <= a / s rounds to at most 448 * (1 + 2^-23), and a power-of-two
+// scale is at least a / 448.  A subnormal s carries an absolute rounding
+// error that can put a / s anywhere above 448.
+__device__ __forceinline__ f4 clamp448(f4 v) {
+  f4 c;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const float t = fminf(fmaxf(v[e], -448.0f), 448.0f);
+    c[e] = v[e] != v[e] ? v[e] : t;
   }
-  c = m > 0x7F800000u ? 0x7Fu : c;
-  return c | ((fbits(x) >> 24) & 0x80u);
+  return c;
 }
 
-// Value of an E4M3 code: the 7 magnitude bits placed at binary32 bits 26..20
-// read as a binary32 number and scaled by 2^120 (exact, subnormal codes
-// included), NaN for 0x7F, sign from bit 7.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t m = c & 0x7Fu;
-  float v = bitsf(m << 20) * 0x1p120f;
-  v = m == 0x7Fu ? __builtin_nanf("") : v;
-  return bitsf(fbits(v) | ((c & 0x80u) << 24));
+// Values of 4 packed E4M3 codes (exact; NaN codes give NaN).
+__device__ __forceinline__ f4 e4m3_unpack4(uint32_t w) {
+  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return f4{lo.x, lo.y, hi.x, hi.y};
 }
-
-__device__ __forceinline__ uint32_t byte_of(uint32_t w, int e) { return (w >> (8 * e)) & 0xFFu; }
 
 // Elements of a 256-value block owned by a lane: 4 vectors, vector j at
 // element offset (16 j + col) * 4 of the block, so every load or store
@@ -182,124 +261,63 @@ __device__ __forceinline__ size_t lane_elem(size_t block, int j, uint32_t col) {
   return block * kBlock + (size_t)(16 * j + col) * 4;
 }
 
-// Stores 4 codes of elements [i, i+4), clipped to n.
-__device__ __forceinline__ void store_codes4(uint8_t* codes, size_t i, size_t n, uint32_t w) {
-  if (i + 4 <= n) {
-    *reinterpret_cast<uint32_t*>(codes + i) = w;
-    return;
+// Encodes a lane's 16 values of one block (all 64 lanes must be active):
+// returns the block scale and writes the 4 packed code words to w.
+__device__ __forceinline__ float encode_block16(const f4 (&x)[4], int mode, uint32_t (&w)[4]) {
+  const float s = block_scale(row_max16(lane_absmax16(x)), mode);
+  const double rinv = scale_reciprocal(s);
+  const bool subnormal_scale = s > 0.0f && s < 0x1p-126f;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f4 v = quotient4(x[j], rinv);
+    if (subnormal_scale) v = clamp448(v);
+    w[j] = e4m3_pack4(v, x[j]);
   }
-  for (int e = 0; e < 3; e++) {
-    if (i + e < n) codes[i + e] = (uint8_t)byte_of(w, e);
-  }
-}
-__device__ __forceinline__ uint32_t load_codes4(const uint8_t* codes, size_t i, size_t n) {
-  if (i + 4 <= n) return *reinterpret_cast<const uint32_t*>(codes + i);
-  uint32_t w = 0;
-  for (int e = 0; e < 3; e++) {
-    if (i + e < n) w |= (uint32_t)codes[i + e] << (8 * e);
-  }
-  return w;
+  return s;
 }
 
 // ===========================================================================
-// Fixed-order sum: dst = (ACC ? dst : 0-term-free) + src0 + src1 + ...
-// Each lane owns U 4-element vectors, 256 vectors apart.
+// Fixed-order sum: dst = [dst +] src0 + src1 + ... + src(K-1), one 4-value
+// vector per lane.
 // ===========================================================================
-template <int K, int U, bool ACC>
+template <int K, bool ACC>
 __global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTable src, size_t n) {
-  const size_t v0 = (size_t)blockIdx.x * (kThreads * U) + threadIdx.x;
-  f4 x[U][K];
-  f4 a[U];
-  const bool full = (v0 + (size_t)(U - 1) * kThreads + 1) * 4 <= n;
-  if (full) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  f4 x[K];
+  f4 a;
+  if (i + 4 <= n) {
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const size_t i = (v0 + (size_t)u * kThreads) * 4;
+    for (int r = 0; r < K; r++) x[r] = load4(static_cast<const float*>(src.p[r]) + i);
+    if (ACC) a = load4(dst + i);
+  } else {
+    if (i >= n) return;
 #pragma unroll
-      for (int r = 0; r < K; r++) x[u][r] = load4(static_cast<const float*>(src.p[r]) + i);
-      if (ACC) a[u] = load4(dst + i);
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      f4 s = ACC ? a[u] + x[u][0] : x[u][0];
-#pragma unroll
-      for (int r = 1; r < K; r++) s = s + x[u][r];
-      store4(dst + (v0 + (size_t)u * kThreads) * 4, s);
-    }
-    return;
+    for (int r = 0; r < K; r++) x[r] = load4_any(static_cast<const float*>(src.p[r]), i, n);
+    if (ACC) a = load4_any(dst, i, n);
   }
+  f4 s = ACC ? a + x[0] : x[0];
 #pragma unroll
-  for (int u = 0; u < U; u++) {
-    const size_t i = (v0 + (size_t)u * kThreads) * 4;
-#pragma unroll
-    for (int r = 0; r < K; r++) x[u][r] = load4_any(static_cast<const float*>(src.p[r]), i, n);
-    if (ACC) a[u] = load4_any(dst, i, n);
-  }
-#pragma unroll
-  for (int u = 0; u < U; u++) {
-    f4 s = ACC ? a[u] + x[u][0] : x[u][0];
-#pragma unroll
-    for (int r = 1; r < K; r++) s = s + x[u][r];
-    store4_any(dst, (v0 + (size_t)u * kThreads) * 4, n, s);
-  }
+  for (int r = 1; r < K; r++) s = s + x[r];
+  store4_any(dst, i, n, s);
 }
 
 // ===========================================================================
-// bf16 encode: each lane owns U groups of 8 values (two 16-byte loads, one
-// 16-byte store of codes), groups 256 apart.
+// bf16 encode: 8 values per lane (two 16-byte loads, one 16-byte store).
 // ===========================================================================
-__device__ __forceinline__ u4 bf16_pack8(f4 lo, f4 hi) {
-  u4 w;
-  w.x = bf16_code(lo.x) | (bf16_code(lo.y) << 16);
-  w.y = bf16_code(lo.z) | (bf16_code(lo.w) << 16);
-  w.z = bf16_code(hi.x) | (bf16_code(hi.y) << 16);
-  w.w = bf16_code(hi.z) | (bf16_code(hi.w) << 16);
-  return w;
-}
-
-__device__ __forceinline__ void store_bf16_8(uint16_t* codes, size_t i, size_t n, u4 w) {
-  if (i + 8 <= n) {
-    *reinterpret_cast<u4*>(codes + i) = w;
-    return;
-  }
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  for (int e = 0; e < 8; e++) {
-    if (i + e < n) codes[i + e] = (uint16_t)(ws[e >> 1] >> (16 * (e & 1)));
-  }
-}
-__device__ __forceinline__ u4 load_bf16_8(const uint16_t* codes, size_t i, size_t n) {
-  if (i + 8 <= n) return *reinterpret_cast<const u4*>(codes + i);
-  uint32_t ws[4] = {0u, 0u, 0u, 0u};
-  for (int e = 0; e < 8; e++) {
-    if (i + e < n) ws[e >> 1] |= (uint32_t)codes[i + e] << (16 * (e & 1));
-  }
-  return u4{ws[0], ws[1], ws[2], ws[3]};
-}
-
-template <int U>
 __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const float* src, size_t n) {
-  const size_t g0 = (size_t)blockIdx.x * (kThreads * U) + threadIdx.x;
-  f4 lo[U], hi[U];
-#pragma unroll
-  for (int u = 0; u < U; u++) {
-    const size_t i = (g0 + (size_t)u * kThreads) * 8;
-    lo[u] = load4_any(src, i, n);
-    hi[u] = load4_any(src, i + 4, n);
-  }
-#pragma unroll
-  for (int u = 0; u < U; u++) {
-    const size_t i = (g0 + (size_t)u * kThreads) * 8;
-    if (i < n) store_bf16_8(codes, i, n, bf16_pack8(lo[u], hi[u]));
-  }
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (i >= n) return;
+  const f4 lo = load4_any(src, i, n);
+  const f4 hi = load4_any(src, i + 4, n);
+  store_bf16_8(codes, i, n, bf16_pack8(lo, hi));
 }
 
 // ===========================================================================
-// bf16 decode-accumulate over K payloads, groups of 8 values per lane.
+// bf16 decode-accumulate over K payloads, 8 values per lane.
 // ===========================================================================
 template <int K, bool ACC>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(float* acc, PtrTable codes, size_t n) {
-  const size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t i = g * 8;
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 8;
   if (i >= n) return;
   u4 w[K];
 #pragma unroll
@@ -311,80 +329,45 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(float* acc, PtrTa
   }
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    const f4 vlo = {bf16_lo(w[r].x), bf16_hi(w[r].x), bf16_lo(w[r].y), bf16_hi(w[r].y)};
-    const f4 vhi = {bf16_lo(w[r].z), bf16_hi(w[r].z), bf16_lo(w[r].w), bf16_hi(w[r].w)};
-    if (!ACC && r == 0) {
-      lo = vlo;
-      hi = vhi;
-    } else {
-      lo = lo + vlo;
-      hi = hi + vhi;
-    }
+    const f4 vlo = bf16_unpack_lo(w[r]);
+    const f4 vhi = bf16_unpack_hi(w[r]);
+    lo = (!ACC && r == 0) ? vlo : lo + vlo;
+    hi = (!ACC && r == 0) ? vhi : hi + vhi;
   }
   store4_any(acc, i, n, lo);
   store4_any(acc, i + 4, n, hi);
 }
 
 // ===========================================================================
-// fp8 encode: one DPP row per 256-value block, G groups of 4 blocks per
-// wavefront, all loads issued first.
+// fp8 encode: one DPP row per 256-value block.
 // ===========================================================================
-template <int G>
-__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales,
-                                                               const float* src, size_t n,
-                                                               int mode) {
+__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const float* src,
+                                                               size_t n, int mode) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
-  const uint32_t row = lane >> 4;
-  const size_t wave = (size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
   const size_t nblocks = (n + kBlock - 1) / kBlock;
-  f4 x[G][4];
+  f4 x[4];
 #pragma unroll
-  for (int g = 0; g < G; g++) {
-    const size_t block = (wave * G + g) * 4 + row;
+  for (int j = 0; j < 4; j++) x[j] = load4_any(src, lane_elem(block, j, col), n);
+  uint32_t w[4];
+  const float s = encode_block16(x, mode, w);
+  if (block >= nblocks) return;
+  if (col == 0u) scales[block] = s;
 #pragma unroll
-    for (int j = 0; j < 4; j++) x[g][j] = load4_any(src, lane_elem(block, j, col), n);
-  }
-#pragma unroll
-  for (int g = 0; g < G; g++) {
-    const size_t block = (wave * G + g) * 4 + row;
-    uint32_t am = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      am = max(am, magnitude_bits(x[g][j].x));
-      am = max(am, magnitude_bits(x[g][j].y));
-      am = max(am, magnitude_bits(x[g][j].z));
-      am = max(am, magnitude_bits(x[g][j].w));
-    }
-    am = row_max16(am);
-    const float s = block_scale(am, mode);
-    const double rinv = scale_reciprocal(s);
-    if (block < nblocks) {
-      if (col == 0u) scales[block] = s;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const f4 v = x[g][j];
-        const uint32_t w = e4m3_code(quotient(v.x, rinv), v.x) |
-                           (e4m3_code(quotient(v.y, rinv), v.y) << 8) |
-                           (e4m3_code(quotient(v.z, rinv), v.z) << 16) |
-                           (e4m3_code(quotient(v.w, rinv), v.w) << 24);
-        store_codes4(codes, lane_elem(block, j, col), n, w);
-      }
-    }
-  }
+  for (int j = 0; j < 4; j++) store_codes4(codes, lane_elem(block, j, col), n, w[j]);
 }
 
 // ===========================================================================
-// fp8 decode-accumulate over K payloads: one DPP row per block, the scale of
-// a rank's block read once per row.
+// fp8 decode-accumulate over K payloads: one DPP row per block, each rank's
+// block scale read once per lane.
 // ===========================================================================
 template <int K, bool ACC>
-__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTable codes,
-                                                               PtrTable scales, size_t n) {
+__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTable codes, PtrTable scales,
+                                                               size_t n) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
-  const uint32_t row = lane >> 4;
-  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + row;
+  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
   const size_t nblocks = (n + kBlock - 1) / kBlock;
   if (block >= nblocks) return;
   uint32_t w[K][4];
@@ -405,8 +388,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTab
   for (int r = 0; r < K; r++) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const f4 v = {e4m3_value(byte_of(w[r][j], 0)) * s[r], e4m3_value(byte_of(w[r][j], 1)) * s[r],
-                    e4m3_value(byte_of(w[r][j], 2)) * s[r], e4m3_value(byte_of(w[r][j], 3)) * s[r]};
+      const f4 v = e4m3_unpack4(w[r][j]) * s[r];
       a[j] = (!ACC && r == 0) ? v : a[j] + v;
     }
   }
@@ -423,58 +405,43 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(float* out, PtrTabl
                                                               OutTable scales, size_t n, int mode) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
-  const uint32_t row = lane >> 4;
-  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + row;
+  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
   const size_t nblocks = (n + kBlock - 1) / kBlock;
   f4 x[K][4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      x[r][j] = load4_any(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n);
-    }
+    for (int j = 0; j < 4; j++) x[r][j] = load4_any(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n);
   }
+  const bool live = block < nblocks;
   f4 a[4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    uint32_t am = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      am = max(am, magnitude_bits(x[r][j].x));
-      am = max(am, magnitude_bits(x[r][j].y));
-      am = max(am, magnitude_bits(x[r][j].z));
-      am = max(am, magnitude_bits(x[r][j].w));
-    }
-    am = row_max16(am);
-    const float s = block_scale(am, mode);
-    const double rinv = scale_reciprocal(s);
+    uint32_t w[4];
+    const float s = encode_block16(x[r], mode, w);
     uint8_t* c = static_cast<uint8_t*>(codes.p[r]);
-    if (block < nblocks && col == 0u) static_cast<float*>(scales.p[r])[block] = s;
+    if (live) {
+      if (col == 0u) static_cast<float*>(scales.p[r])[block] = s;
+#pragma unroll
+      for (int j = 0; j < 4; j++) store_codes4(c, lane_elem(block, j, col), n, w[j]);
+    }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const f4 xv = x[r][j];
-      const uint32_t c0 = e4m3_code(quotient(xv.x, rinv), xv.x);
-      const uint32_t c1 = e4m3_code(quotient(xv.y, rinv), xv.y);
-      const uint32_t c2 = e4m3_code(quotient(xv.z, rinv), xv.z);
-      const uint32_t c3 = e4m3_code(quotient(xv.w, rinv), xv.w);
-      if (block < nblocks) store_codes4(c, lane_elem(block, j, col), n, c0 | (c1 << 8) | (c2 << 16) | (c3 << 24));
-      const f4 v = {e4m3_value(c0) * s, e4m3_value(c1) * s, e4m3_value(c2) * s, e4m3_value(c3) * s};
+      const f4 v = e4m3_unpack4(w[j]) * s;
       a[j] = r == 0 ? v : a[j] + v;
     }
   }
-  if (block >= nblocks) return;
+  if (!live) return;
 #pragma unroll
   for (int j = 0; j < 4; j++) store4_any(out, lane_elem(block, j, col), n, a[j]);
 }
 
 // ===========================================================================
-// Fused bf16 bucket pass, groups of 8 values per lane.
+// Fused bf16 bucket pass, 8 values per lane.
 // ===========================================================================
 template <int K>
-__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTable src, OutTable codes,
-                                                               size_t n) {
-  const size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t i = g * 8;
+__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTable src, OutTable codes, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 8;
   if (i >= n) return;
   f4 lo[K], hi[K];
 #pragma unroll
@@ -487,8 +454,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTab
   for (int r = 0; r < K; r++) {
     const u4 w = bf16_pack8(lo[r], hi[r]);
     store_bf16_8(static_cast<uint16_t*>(codes.p[r]), i, n, w);
-    const f4 vlo = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-    const f4 vhi = {bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    const f4 vlo = bf16_unpack_lo(w);
+    const f4 vhi = bf16_unpack_hi(w);
     alo = r == 0 ? vlo : alo + vlo;
     ahi = r == 0 ? vhi : ahi + vhi;
   }
@@ -499,11 +466,15 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTab
 // ---------------------------------------------------------------------------
 // Launch helpers.
 // ---------------------------------------------------------------------------
-constexpr size_t kMaxGrid = (size_t)1 << 31;
+constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 
-hipError_t finish_launch() { return hipGetLastError(); }
+// Workgroups for one lane per `per_lane` values, or 0 if too many.
+size_t grid_for(size_t n, size_t per_lane) {
+  const size_t g = ceil_div(ceil_div(n, per_lane), (size_t)kThreads);
+  return g > kMaxGrid ? 0 : g;
+}
 
 #define GB_DISPATCH_K(k, CALL) \
   switch (k) {                 \
@@ -522,84 +493,71 @@ hipError_t finish_launch() { return hipGetLastError(); }
 
 hipError_t launch_reduce_sum(float* dst, const PtrTable& srcs, int k, size_t n, bool accumulate,
                              hipStream_t stream) {
-  // Vectors per lane: enough 16-byte loads in flight per lane without
-  // running out of registers.
-  const int u = k <= 2 ? 4 : (k <= 4 ? 2 : 1);
-  const size_t grid = ceil_div(ceil_div(n, 4), (size_t)kThreads * u);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-#define GB_CALL(K)                                                                                     \
-  if (u == 4) {                                                                                        \
-    if (accumulate) reduce_sum_kernel<K, 4, true><<<grid, kThreads, 0, stream>>>(dst, srcs, n);        \
-    else reduce_sum_kernel<K, 4, false><<<grid, kThreads, 0, stream>>>(dst, srcs, n);                  \
-  } else if (u == 2) {                                                                                 \
-    if (accumulate) reduce_sum_kernel<K, 2, true><<<grid, kThreads, 0, stream>>>(dst, srcs, n);        \
-    else reduce_sum_kernel<K, 2, false><<<grid, kThreads, 0, stream>>>(dst, srcs, n);                  \
-  } else {                                                                                             \
-    if (accumulate) reduce_sum_kernel<K, 1, true><<<grid, kThreads, 0, stream>>>(dst, srcs, n);        \
-    else reduce_sum_kernel<K, 1, false><<<grid, kThreads, 0, stream>>>(dst, srcs, n);                  \
-  }
+#define GB_CALL(K)                                                                     \
+  if (accumulate) reduce_sum_kernel<K, true><<<grid, kThreads, 0, stream>>>(dst, srcs, n); \
+  else reduce_sum_kernel<K, false><<<grid, kThreads, 0, stream>>>(dst, srcs, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-  return finish_launch();
+  return hipGetLastError();
 }
 
 hipError_t launch_encode_bf16(uint16_t* codes, const float* src, size_t n, hipStream_t stream) {
-  constexpr int U = 2;
-  const size_t grid = ceil_div(ceil_div(n, 8), (size_t)kThreads * U);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 8);
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-  encode_bf16_kernel<U><<<grid, kThreads, 0, stream>>>(codes, src, n);
-  return finish_launch();
+  encode_bf16_kernel<<<grid, kThreads, 0, stream>>>(codes, src, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const float* src, size_t n, int scale_mode,
                              hipStream_t stream) {
-  constexpr int G = 2;
-  const size_t grid = ceil_div(ceil_div(n, kBlock), (size_t)16 * G);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 16);  // 16 values per lane: a 256-lane group does 16 blocks
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-  encode_fp8_kernel<G><<<grid, kThreads, 0, stream>>>(codes, scales, src, n, scale_mode);
-  return finish_launch();
+  encode_fp8_kernel<<<grid, kThreads, 0, stream>>>(codes, scales, src, n, scale_mode);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_bf16(float* acc, const PtrTable& codes, int k, size_t n, bool accumulate,
                               hipStream_t stream) {
-  const size_t grid = ceil_div(ceil_div(n, 8), (size_t)kThreads);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 8);
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K)                                                                          \
   if (accumulate) decode_bf16_kernel<K, true><<<grid, kThreads, 0, stream>>>(acc, codes, n); \
   else decode_bf16_kernel<K, false><<<grid, kThreads, 0, stream>>>(acc, codes, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-  return finish_launch();
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fp8(float* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
                              bool accumulate, hipStream_t stream) {
-  const size_t grid = ceil_div(ceil_div(n, kBlock), (size_t)16);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K)                                                                                   \
   if (accumulate) decode_fp8_kernel<K, true><<<grid, kThreads, 0, stream>>>(acc, codes, scales, n);   \
   else decode_fp8_kernel<K, false><<<grid, kThreads, 0, stream>>>(acc, codes, scales, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-  return finish_launch();
+  return hipGetLastError();
 }
 
 hipError_t launch_fused_bf16(float* out, const PtrTable& srcs, uint16_t* const* codes, int k, size_t n,
                              hipStream_t stream) {
   OutTable c = {};
   for (int r = 0; r < k; r++) c.p[r] = codes[r];
-  const size_t grid = ceil_div(ceil_div(n, 8), (size_t)kThreads);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 8);
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K) fused_bf16_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, c, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-  return finish_launch();
+  return hipGetLastError();
 }
 
 hipError_t launch_fused_fp8(float* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales,
@@ -609,13 +567,13 @@ hipError_t launch_fused_fp8(float* out, const PtrTable& srcs, uint8_t* const* co
     c.p[r] = codes[r];
     s.p[r] = scales[r];
   }
-  const size_t grid = ceil_div(ceil_div(n, kBlock), (size_t)16);
-  if (grid >= kMaxGrid) return hipErrorInvalidValue;
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K) fused_fp8_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, c, s, n, scale_mode);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-  return finish_launch();
+  return hipGetLastError();
 }
 
 }  // namespace gb

@@ -170,6 +170,10 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes,
  *                the workspace, then out = decode-and-accumulate.
  * Each value is read from srcs once: encode and decode of a bucket are one
  * pass, and the decoded values are the ones stored payloads decode to.
+ * Buckets start on 256-value boundaries, so they are processed together in
+ * one launch whose workgroups take them in order; the result equals one call
+ * per bucket bit for bit.  A caller that holds only some buckets (a DDP hook
+ * as buckets become ready) calls once per bucket with n = that bucket.
  *   out          device fp32[n], written; may equal srcs[0].
  *   srcs         host array of k device fp32[n] pointers, read only.
  *   bucket_elems a positive multiple of 256 (so fp8 blocks never straddle a

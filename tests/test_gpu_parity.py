@@ -130,6 +130,8 @@ def special_blocks():
     blocks.append(np.full(256, -0.0, np.float32))
     blocks.append((rng.standard_normal(256) * 2.0 ** -140).astype(np.float32))  # subnormal block
     blocks.append((rng.standard_normal(256) * 2.0 ** -128).astype(np.float32))  # subnormal scale
+    for e in range(-152, -115):  # every binade where a / 448 is subnormal or nearly so
+        blocks.append((rng.standard_normal(256) * 2.0 ** e).astype(np.float32))
     b = rng.standard_normal(256).astype(np.float32)
     b[17] = 448.0
     blocks.append(b)  # scale 1 in both modes
