@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="rough budget of oracle CPU time for the baseline sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain 1 GiB device copies (gb_reduce_sum with k=1, and torch "
+                        "copy_), the known-size kernels that scale rocprofv3 FETCH_SIZE / "
+                        "WRITE_SIZE readings")
     return p.parse_args()
 
 
@@ -119,24 +123,44 @@ class DdpBuckets(Workload):
 
     def per_bucket_step(self):
         gb = self.gb
-        for start, length in self.W.ddp_buckets():
-            gb.gb_bucket_allreduce_local(self.out[start:start + length],
-                                         [t[start:start + length] for t in self.x], self.bucket,
-                                         gb.GB_CODEC_FP8_E4M3_B256, self.mode,
-                                         self.ws_views[start])
+        for out, xs, ws in self.pb_args:
+            gb.gb_bucket_allreduce_local(out, xs, self.bucket, gb.GB_CODEC_FP8_E4M3_B256, self.mode, ws)
 
     def extra(self, time_region, reps):
-        """Throughput of the same pass issued as one call per bucket."""
+        """Throughput of the same pass issued as one call per bucket, as a DDP
+        hook would issue it, each bucket's payloads in its own slice of the
+        workspace.  The 153 calls are captured once in a HIP graph and the
+        graph is replayed, so the figure is the GPU's, not the Python
+        binding's per-call cost; every replay's output is checked against the
+        single-launch result.  Leaves the workspace in the per-bucket layout."""
         torch, gb = self.torch, self.gb
-        # per-bucket workspaces: each bucket's payloads in its own slice
-        self.ws_views = {}
+        want = self.out.clone()
+        self.pb_args = []
+        off = 0
         for start, length in self.W.ddp_buckets():
             need = gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, self.k, length, self.bucket)
-            self.ws_views[start] = self.ws[self.k * start + 4 * self.k * (start // 256):][:need]
-        self.per_bucket_step()
-        ms = time_region(self.per_bucket_step, reps) / reps
-        return {"per_bucket_calls_gbs": round(self.step_bytes() / (ms * 1e-3) / 1e9, 2),
-                "per_bucket_calls_ms": round(ms, 4)}
+            self.pb_args.append((self.out[start:start + length],
+                                 [t[start:start + length] for t in self.x],
+                                 self.ws[off:off + need]))
+            off += need
+        self.per_bucket_step()  # eager, also warms up
+        torch.cuda.synchronize()
+        eager_ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.per_bucket_step()
+        self.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        replay_ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        ms = time_region(graph.replay, reps) / reps
+        replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        eager_ms = time_region(self.per_bucket_step, reps) / reps
+        del graph
+        return {"per_bucket_calls_graph_gbs": round(self.step_bytes() / (ms * 1e-3) / 1e9, 2),
+                "per_bucket_calls_graph_ms": round(ms, 4),
+                "per_bucket_calls_eager_ms": round(eager_ms, 4),
+                "per_bucket_outputs_match": eager_ok and replay_ok}
 
     def cpu_sample(self, budget):
         """Run the oracle on the first buckets; compare with the GPU's."""
@@ -298,7 +322,7 @@ class Sweep(Workload):
 
     def timed_kernel(self):
         n = self.sizes[-1]
-        return ("reduce_sum_kernel<2>", 12 * n, 1, lambda: self.gb.gb_reduce_sum(self.out[n], self.x[n]))
+        return ("reduce_sum_kernel<2,false>", 12 * n, 1, lambda: self.gb.gb_reduce_sum(self.out[n], self.x[n]))
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -343,7 +367,7 @@ class TwoRank(Workload):
         return 12 * self.n + 6 * self.n + 6 * self.n
 
     def timed_kernel(self):
-        return ("reduce_sum_kernel<2>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
+        return ("reduce_sum_kernel<2,false>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -359,6 +383,27 @@ class TwoRank(Workload):
 
 
 WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank)}
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 counter
+    summaries under profiles/, or None when none was taken on the kernel
+    source as it is now (the summary records the source's sha256)."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "gradient_all_reduce_amd", "csrc", "gb_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic "):
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split()[1:])
+            if (kv.get("kernel") == kernel and kv.get("workload") == workload
+                    and kv.get("kernels_sha256") == sha):
+                return int(float(kv["traffic_bytes"]))
+    return None
 
 
 def time_region(torch, stream, fn, reps):
@@ -389,6 +434,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # gb_reduce_sum with one source is a plain copy through the library's
+        # own streaming kernel: it reads and writes exactly 1 GiB per launch.
+        n = (1 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            gb.gb_reduce_sum(dst, [src])
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {4 * n} bytes 3 times with gb_reduce_sum(k=1) and 3 times with torch copy_")
+        return
     wl = WORKLOADS[args.workload](gb, torch, args)
     log(f"[bench] workload {wl.name}: allocating and drawing inputs")
     wl.setup()
@@ -410,11 +468,6 @@ def main():
     log(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} GB/s; {kname}: {kms * 1e3:.2f} us/launch, "
         f"{achieved:.1f} GB/s")
 
-    extra = {}
-    if hasattr(wl, "extra"):
-        extra = wl.extra(lambda fn, reps: time_region(torch, wl.stream, fn, reps), max(3, args.steps // 2))
-        log(f"[bench] extra: {extra}")
-
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on a sample")
@@ -422,6 +475,11 @@ def main():
         cpu = {"value": round(sb / st / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": sample, "seconds": round(st, 2), "gpu_matches_oracle_on_sample": ok}
         log(f"[bench] oracle {sb / st / 1e9:.3f} GB/s over {sample}; GPU output matches: {ok}")
+
+    extra = {}
+    if hasattr(wl, "extra"):
+        extra = wl.extra(lambda fn, reps: time_region(torch, wl.stream, fn, reps), max(3, args.steps // 2))
+        log(f"[bench] extra: {extra}")
 
     line = {
         "metric": METRIC,
@@ -438,7 +496,7 @@ def main():
         "data": "synthetic",
         "config": dict(wl.config, **extra),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(kname, wl.name),
                      "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3)},
         "cpu_baseline": cpu,
     }

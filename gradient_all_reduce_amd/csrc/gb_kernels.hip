@@ -34,7 +34,7 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 struct OutTable {
   void* p[GB_MAX_K];
@@ -95,22 +95,22 @@ __device__ __forceinline__ void store_codes4(uint8_t* codes, size_t i, size_t n,
   }
 }
 
-// 8 bf16 codes of elements [i, i + 8) as 4 words, clipped to n.
-__device__ __forceinline__ u4 load_bf16_8(const uint16_t* codes, size_t i, size_t n) {
-  if (i + 8 <= n) return __builtin_nontemporal_load(reinterpret_cast<const u4*>(codes + i));
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  for (int e = 0; e < 8; e++) {
+// 4 bf16 codes of elements [i, i + 4) as 2 words, clipped to n.
+__device__ __forceinline__ u2 load_bf16_4(const uint16_t* codes, size_t i, size_t n) {
+  if (i + 4 <= n) return __builtin_nontemporal_load(reinterpret_cast<const u2*>(codes + i));
+  uint32_t w[2] = {0u, 0u};
+  for (int e = 0; e < 3; e++) {
     if (i + e < n) w[e >> 1] |= (uint32_t)codes[i + e] << (16 * (e & 1));
   }
-  return u4{w[0], w[1], w[2], w[3]};
+  return u2{w[0], w[1]};
 }
-__device__ __forceinline__ void store_bf16_8(uint16_t* codes, size_t i, size_t n, u4 w) {
-  if (i + 8 <= n) {
-    __builtin_nontemporal_store(w, reinterpret_cast<u4*>(codes + i));
+__device__ __forceinline__ void store_bf16_4(uint16_t* codes, size_t i, size_t n, u2 w) {
+  if (i + 4 <= n) {
+    __builtin_nontemporal_store(w, reinterpret_cast<u2*>(codes + i));
     return;
   }
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  for (int e = 0; e < 8; e++) {
+  const uint32_t ws[2] = {w.x, w.y};
+  for (int e = 0; e < 3; e++) {
     if (i + e < n) codes[i + e] = (uint16_t)(ws[e >> 1] >> (16 * (e & 1)));
   }
 }
@@ -126,16 +126,12 @@ __device__ __forceinline__ uint32_t bf16_code(float x) {
   return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
 }
 
-__device__ __forceinline__ u4 bf16_pack8(f4 lo, f4 hi) {
-  return u4{bf16_code(lo.x) | (bf16_code(lo.y) << 16), bf16_code(lo.z) | (bf16_code(lo.w) << 16),
-            bf16_code(hi.x) | (bf16_code(hi.y) << 16), bf16_code(hi.z) | (bf16_code(hi.w) << 16)};
+__device__ __forceinline__ u2 bf16_pack4(f4 x) {
+  return u2{bf16_code(x.x) | (bf16_code(x.y) << 16), bf16_code(x.z) | (bf16_code(x.w) << 16)};
 }
 // bf16 -> fp32 is exact: the code is the top half of the binary32 pattern.
-__device__ __forceinline__ f4 bf16_unpack_lo(u4 w) {
+__device__ __forceinline__ f4 bf16_unpack4(u2 w) {
   return f4{bitsf(w.x << 16), bitsf(w.x & 0xFFFF0000u), bitsf(w.y << 16), bitsf(w.y & 0xFFFF0000u)};
-}
-__device__ __forceinline__ f4 bf16_unpack_hi(u4 w) {
-  return f4{bitsf(w.z << 16), bitsf(w.z & 0xFFFF0000u), bitsf(w.w << 16), bitsf(w.w & 0xFFFF0000u)};
 }
 
 // ---------------------------------------------------------------------------
@@ -302,40 +298,31 @@ __global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTab
 }
 
 // ===========================================================================
-// bf16 encode: 8 values per lane (two 16-byte loads, one 16-byte store).
+// bf16 encode and decode-accumulate: one 4-value vector per lane, so each
+// instruction of a wavefront loads 1 KiB of fp32 and stores 512 bytes of
+// codes (or the reverse), contiguously.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const float* src, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (i >= n) return;
-  const f4 lo = load4_any(src, i, n);
-  const f4 hi = load4_any(src, i + 4, n);
-  store_bf16_8(codes, i, n, bf16_pack8(lo, hi));
+  store_bf16_4(codes, i, n, bf16_pack4(load4_any(src, i, n)));
 }
 
-// ===========================================================================
-// bf16 decode-accumulate over K payloads, 8 values per lane.
-// ===========================================================================
 template <int K, bool ACC>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(float* acc, PtrTable codes, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (i >= n) return;
-  u4 w[K];
+  u2 w[K];
 #pragma unroll
-  for (int r = 0; r < K; r++) w[r] = load_bf16_8(static_cast<const uint16_t*>(codes.p[r]), i, n);
-  f4 lo, hi;
-  if (ACC) {
-    lo = load4_any(acc, i, n);
-    hi = load4_any(acc, i + 4, n);
-  }
+  for (int r = 0; r < K; r++) w[r] = load_bf16_4(static_cast<const uint16_t*>(codes.p[r]), i, n);
+  f4 a;
+  if (ACC) a = load4_any(acc, i, n);
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    const f4 vlo = bf16_unpack_lo(w[r]);
-    const f4 vhi = bf16_unpack_hi(w[r]);
-    lo = (!ACC && r == 0) ? vlo : lo + vlo;
-    hi = (!ACC && r == 0) ? vhi : hi + vhi;
+    const f4 v = bf16_unpack4(w[r]);
+    a = (!ACC && r == 0) ? v : a + v;
   }
-  store4_any(acc, i, n, lo);
-  store4_any(acc, i + 4, n, hi);
+  store4_any(acc, i, n, a);
 }
 
 // ===========================================================================
@@ -437,30 +424,24 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(float* out, PtrTabl
 }
 
 // ===========================================================================
-// Fused bf16 bucket pass, 8 values per lane.
+// Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
 template <int K>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTable src, OutTable codes, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (i >= n) return;
-  f4 lo[K], hi[K];
+  f4 x[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) x[r] = load4_any(static_cast<const float*>(src.p[r]), i, n);
+  f4 a;
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    lo[r] = load4_any(static_cast<const float*>(src.p[r]), i, n);
-    hi[r] = load4_any(static_cast<const float*>(src.p[r]), i + 4, n);
+    const u2 w = bf16_pack4(x[r]);
+    store_bf16_4(static_cast<uint16_t*>(codes.p[r]), i, n, w);
+    const f4 v = bf16_unpack4(w);
+    a = r == 0 ? v : a + v;
   }
-  f4 alo, ahi;
-#pragma unroll
-  for (int r = 0; r < K; r++) {
-    const u4 w = bf16_pack8(lo[r], hi[r]);
-    store_bf16_8(static_cast<uint16_t*>(codes.p[r]), i, n, w);
-    const f4 vlo = bf16_unpack_lo(w);
-    const f4 vhi = bf16_unpack_hi(w);
-    alo = r == 0 ? vlo : alo + vlo;
-    ahi = r == 0 ? vhi : ahi + vhi;
-  }
-  store4_any(out, i, n, alo);
-  store4_any(out, i + 4, n, ahi);
+  store4_any(out, i, n, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,7 +486,7 @@ hipError_t launch_reduce_sum(float* dst, const PtrTable& srcs, int k, size_t n, 
 }
 
 hipError_t launch_encode_bf16(uint16_t* codes, const float* src, size_t n, hipStream_t stream) {
-  const size_t grid = grid_for(n, 8);
+  const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
   encode_bf16_kernel<<<grid, kThreads, 0, stream>>>(codes, src, n);
@@ -523,7 +504,7 @@ hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const float* src, si
 
 hipError_t launch_decode_bf16(float* acc, const PtrTable& codes, int k, size_t n, bool accumulate,
                               hipStream_t stream) {
-  const size_t grid = grid_for(n, 8);
+  const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K)                                                                          \
@@ -551,7 +532,7 @@ hipError_t launch_fused_bf16(float* out, const PtrTable& srcs, uint16_t* const* 
                              hipStream_t stream) {
   OutTable c = {};
   for (int r = 0; r < k; r++) c.p[r] = codes[r];
-  const size_t grid = grid_for(n, 8);
+  const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K) fused_bf16_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, c, n);
