@@ -115,6 +115,37 @@ __device__ __forceinline__ void store_bf16_4(uint16_t* codes, size_t i, size_t n
   }
 }
 
+// The same accesses with the bounds test resolved at compile time: FULL means
+// the caller knows the whole workgroup's range lies below n, so no access is
+// guarded (one straight run of loads, no divergent branches).
+template <bool FULL>
+__device__ __forceinline__ f4 load4_at(const float* p, size_t i, size_t n) {
+  return FULL ? load4(p + i) : load4_any(p, i, n);
+}
+template <bool FULL>
+__device__ __forceinline__ void store4_at(float* p, size_t i, size_t n, f4 v) {
+  if (FULL) store4(p + i, v);
+  else store4_any(p, i, n, v);
+}
+template <bool FULL>
+__device__ __forceinline__ uint32_t load_codes4_at(const uint8_t* codes, size_t i, size_t n) {
+  return FULL ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + i)) : load_codes4(codes, i, n);
+}
+template <bool FULL>
+__device__ __forceinline__ void store_codes4_at(uint8_t* codes, size_t i, size_t n, uint32_t w) {
+  if (FULL) __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + i));
+  else store_codes4(codes, i, n, w);
+}
+template <bool FULL>
+__device__ __forceinline__ u2 load_bf16_4_at(const uint16_t* codes, size_t i, size_t n) {
+  return FULL ? __builtin_nontemporal_load(reinterpret_cast<const u2*>(codes + i)) : load_bf16_4(codes, i, n);
+}
+template <bool FULL>
+__device__ __forceinline__ void store_bf16_4_at(uint16_t* codes, size_t i, size_t n, u2 w) {
+  if (FULL) __builtin_nontemporal_store(w, reinterpret_cast<u2*>(codes + i));
+  else store_bf16_4(codes, i, n, w);
+}
+
 // ---------------------------------------------------------------------------
 // bf16: nearest value, ties to the even code (the carry of the rounding add
 // runs into the exponent, which gives IEEE overflow to Inf); a NaN keeps its
@@ -272,29 +303,40 @@ __device__ __forceinline__ float encode_block16(const f4 (&x)[4], int mode, uint
   return s;
 }
 
+// Every kernel below runs one of two instantiations of its body per
+// workgroup: FULL when the workgroup's whole range lies below n (all but the
+// last workgroup of a launch), with no bounds test on any access, and the
+// guarded one otherwise.  The choice is uniform across the workgroup.
+constexpr size_t kVecPerGroup = (size_t)kThreads * 4;       // 1024 values: one 4-vector per lane
+constexpr size_t kBlocksPerGroup = kThreads / 16;          // 16 fp8 blocks: one per 16-lane row
+
+__device__ __forceinline__ bool group_full(size_t per_group, size_t n) {
+  return ((size_t)blockIdx.x + 1) * per_group <= n;
+}
+
 // ===========================================================================
 // Fixed-order sum: dst = [dst +] src0 + src1 + ... + src(K-1), one 4-value
 // vector per lane.
 // ===========================================================================
-template <int K, bool ACC>
-__global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTable src, size_t n) {
+template <int K, bool ACC, bool FULL>
+__device__ __forceinline__ void reduce_sum_body(float* dst, const PtrTable& src, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (!FULL && i >= n) return;
   f4 x[K];
   f4 a;
-  if (i + 4 <= n) {
 #pragma unroll
-    for (int r = 0; r < K; r++) x[r] = load4(static_cast<const float*>(src.p[r]) + i);
-    if (ACC) a = load4(dst + i);
-  } else {
-    if (i >= n) return;
-#pragma unroll
-    for (int r = 0; r < K; r++) x[r] = load4_any(static_cast<const float*>(src.p[r]), i, n);
-    if (ACC) a = load4_any(dst, i, n);
-  }
+  for (int r = 0; r < K; r++) x[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), i, n);
+  if (ACC) a = load4_at<FULL>(dst, i, n);
   f4 s = ACC ? a + x[0] : x[0];
 #pragma unroll
   for (int r = 1; r < K; r++) s = s + x[r];
-  store4_any(dst, i, n, s);
+  store4_at<FULL>(dst, i, n, s);
+}
+
+template <int K, bool ACC>
+__global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTable src, size_t n) {
+  if (group_full(kVecPerGroup, n)) reduce_sum_body<K, ACC, true>(dst, src, n);
+  else reduce_sum_body<K, ACC, false>(dst, src, n);
 }
 
 // ===========================================================================
@@ -302,74 +344,90 @@ __global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTab
 // instruction of a wavefront loads 1 KiB of fp32 and stores 512 bytes of
 // codes (or the reverse), contiguously.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const float* src, size_t n) {
+template <bool FULL>
+__device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const float* src, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
-  if (i >= n) return;
-  store_bf16_4(codes, i, n, bf16_pack4(load4_any(src, i, n)));
+  if (!FULL && i >= n) return;
+  store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(load4_at<FULL>(src, i, n)));
 }
 
-template <int K, bool ACC>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(float* acc, PtrTable codes, size_t n) {
+__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const float* src, size_t n) {
+  if (group_full(kVecPerGroup, n)) encode_bf16_body<true>(codes, src, n);
+  else encode_bf16_body<false>(codes, src, n);
+}
+
+template <int K, bool ACC, bool FULL>
+__device__ __forceinline__ void decode_bf16_body(float* acc, const PtrTable& codes, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
-  if (i >= n) return;
+  if (!FULL && i >= n) return;
   u2 w[K];
 #pragma unroll
-  for (int r = 0; r < K; r++) w[r] = load_bf16_4(static_cast<const uint16_t*>(codes.p[r]), i, n);
+  for (int r = 0; r < K; r++) w[r] = load_bf16_4_at<FULL>(static_cast<const uint16_t*>(codes.p[r]), i, n);
   f4 a;
-  if (ACC) a = load4_any(acc, i, n);
+  if (ACC) a = load4_at<FULL>(acc, i, n);
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const f4 v = bf16_unpack4(w[r]);
     a = (!ACC && r == 0) ? v : a + v;
   }
-  store4_any(acc, i, n, a);
+  store4_at<FULL>(acc, i, n, a);
+}
+
+template <int K, bool ACC>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(float* acc, PtrTable codes, size_t n) {
+  if (group_full(kVecPerGroup, n)) decode_bf16_body<K, ACC, true>(acc, codes, n);
+  else decode_bf16_body<K, ACC, false>(acc, codes, n);
 }
 
 // ===========================================================================
 // fp8 encode: one DPP row per 256-value block.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const float* src,
-                                                               size_t n, int mode) {
+template <bool FULL>
+__device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, const float* src, size_t n,
+                                                int mode) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
-  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  const size_t nblocks = (n + kBlock - 1) / kBlock;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++) x[j] = load4_any(src, lane_elem(block, j, col), n);
+  for (int j = 0; j < 4; j++) x[j] = load4_at<FULL>(src, lane_elem(block, j, col), n);
   uint32_t w[4];
-  const float s = encode_block16(x, mode, w);
-  if (block >= nblocks) return;
+  const float s = encode_block16(x, mode, w);  // all 64 lanes take part
+  if (!FULL && block * kBlock >= n) return;
   if (col == 0u) scales[block] = s;
 #pragma unroll
-  for (int j = 0; j < 4; j++) store_codes4(codes, lane_elem(block, j, col), n, w[j]);
+  for (int j = 0; j < 4; j++) store_codes4_at<FULL>(codes, lane_elem(block, j, col), n, w[j]);
+}
+
+__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const float* src,
+                                                               size_t n, int mode) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) encode_fp8_body<true>(codes, scales, src, n, mode);
+  else encode_fp8_body<false>(codes, scales, src, n, mode);
 }
 
 // ===========================================================================
 // fp8 decode-accumulate over K payloads: one DPP row per block, each rank's
 // block scale read once per lane.
 // ===========================================================================
-template <int K, bool ACC>
-__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTable codes, PtrTable scales,
-                                                               size_t n) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t col = lane & 15u;
-  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  const size_t nblocks = (n + kBlock - 1) / kBlock;
-  if (block >= nblocks) return;
+template <int K, bool ACC, bool FULL>
+__device__ __forceinline__ void decode_fp8_body(float* acc, const PtrTable& codes, const PtrTable& scales,
+                                                size_t n) {
+  const uint32_t col = threadIdx.x & 15u;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  if (!FULL && block * kBlock >= n) return;
   uint32_t w[K][4];
   float s[K];
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const uint8_t* c = static_cast<const uint8_t*>(codes.p[r]);
 #pragma unroll
-    for (int j = 0; j < 4; j++) w[r][j] = load_codes4(c, lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) w[r][j] = load_codes4_at<FULL>(c, lane_elem(block, j, col), n);
     s[r] = static_cast<const float*>(scales.p[r])[block];
   }
   f4 a[4];
   if (ACC) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) a[j] = load4_any(acc, lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) a[j] = load4_at<FULL>(acc, lane_elem(block, j, col), n);
   }
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -380,37 +438,42 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTab
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; j++) store4_any(acc, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store4_at<FULL>(acc, lane_elem(block, j, col), n, a[j]);
+}
+
+template <int K, bool ACC>
+__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTable codes, PtrTable scales,
+                                                               size_t n) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) decode_fp8_body<K, ACC, true>(acc, codes, scales, n);
+  else decode_fp8_body<K, ACC, false>(acc, codes, scales, n);
 }
 
 // ===========================================================================
 // Fused fp8 bucket pass: read each rank's block once, write its payload
 // (codes, scale), decode those codes and add them in rank order.
 // ===========================================================================
-template <int K>
-__global__ __launch_bounds__(kThreads) void fused_fp8_kernel(float* out, PtrTable src, OutTable codes,
-                                                              OutTable scales, size_t n, int mode) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t col = lane & 15u;
-  const size_t block = ((size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  const size_t nblocks = (n + kBlock - 1) / kBlock;
+template <int K, bool FULL>
+__device__ __forceinline__ void fused_fp8_body(float* out, const PtrTable& src, const OutTable& codes,
+                                               const OutTable& scales, size_t n, int mode) {
+  const uint32_t col = threadIdx.x & 15u;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[K][4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) x[r][j] = load4_any(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) x[r][j] = load4_at<FULL>(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n);
   }
-  const bool live = block < nblocks;
+  const bool live = FULL || block * kBlock < n;
   f4 a[4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
     uint32_t w[4];
-    const float s = encode_block16(x[r], mode, w);
+    const float s = encode_block16(x[r], mode, w);  // all 64 lanes take part
     uint8_t* c = static_cast<uint8_t*>(codes.p[r]);
     if (live) {
       if (col == 0u) static_cast<float*>(scales.p[r])[block] = s;
 #pragma unroll
-      for (int j = 0; j < 4; j++) store_codes4(c, lane_elem(block, j, col), n, w[j]);
+      for (int j = 0; j < 4; j++) store_codes4_at<FULL>(c, lane_elem(block, j, col), n, w[j]);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -420,28 +483,41 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(float* out, PtrTabl
   }
   if (!live) return;
 #pragma unroll
-  for (int j = 0; j < 4; j++) store4_any(out, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store4_at<FULL>(out, lane_elem(block, j, col), n, a[j]);
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void fused_fp8_kernel(float* out, PtrTable src, OutTable codes,
+                                                              OutTable scales, size_t n, int mode) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, true>(out, src, codes, scales, n, mode);
+  else fused_fp8_body<K, false>(out, src, codes, scales, n, mode);
 }
 
 // ===========================================================================
 // Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
-template <int K>
-__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTable src, OutTable codes, size_t n) {
+template <int K, bool FULL>
+__device__ __forceinline__ void fused_bf16_body(float* out, const PtrTable& src, const OutTable& codes, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
-  if (i >= n) return;
+  if (!FULL && i >= n) return;
   f4 x[K];
 #pragma unroll
-  for (int r = 0; r < K; r++) x[r] = load4_any(static_cast<const float*>(src.p[r]), i, n);
+  for (int r = 0; r < K; r++) x[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), i, n);
   f4 a;
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const u2 w = bf16_pack4(x[r]);
-    store_bf16_4(static_cast<uint16_t*>(codes.p[r]), i, n, w);
+    store_bf16_4_at<FULL>(static_cast<uint16_t*>(codes.p[r]), i, n, w);
     const f4 v = bf16_unpack4(w);
     a = r == 0 ? v : a + v;
   }
-  store4_any(out, i, n, a);
+  store4_at<FULL>(out, i, n, a);
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTable src, OutTable codes, size_t n) {
+  if (group_full(kVecPerGroup, n)) fused_bf16_body<K, true>(out, src, codes, n);
+  else fused_bf16_body<K, false>(out, src, codes, n);
 }
 
 // ---------------------------------------------------------------------------
