@@ -33,6 +33,13 @@
  *                         [test_oracle_decode.py].
  *   or_bucket_allreduce   equals the whole-buffer encode + decode when
  *                         buckets are multiples of 256 [test_oracle_decode.py].
+ *   or_encode_*_ef        with a zero residual the payload is the plain
+ *                         encode; the bf16 residual is exact and within half
+ *                         an ulp; exact rational step-by-step simulation with
+ *                         brute-force rounding; over repeated steps the
+ *                         running mean of the decoded values converges to the
+ *                         input, which fails for a wrong sign or a dropped
+ *                         feedback term [test_oracle_ef.py].
  * The pages fix none of the NaN and Inf conventions (NaN sign and payload,
  * Inf scale); they are readings taken here, stated at each function: parity
  * unpinned for non-finite inputs.
@@ -300,6 +307,70 @@ void or_bucket_allreduce(float* out, void* const* codes, float* const* scales,
       } else {
         uint8_t* c = (uint8_t*)codes[r] + start;
         or_encode_fp8(c, scales[r] + scale_base, xs[r], len, mode);
+        cs[r] = c;
+        ss[r] = scales[r] + scale_base;
+      }
+    }
+    or_decode_accumulate(out + start, cs, codec == OR_CODEC_FP8 ? ss : NULL, k,
+                         len, codec, 0);
+    scale_base += (len + 255) / 256;
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Error feedback.  README "Bridge compression": each bridge member keeps an
+ * error-feedback residual per buffer, so the rounding error of one step is
+ * carried into the next instead of accumulating.  Reading taken (the usual
+ * error-feedback step, in binary32): y = x + residual; the payload encodes y
+ * exactly as the plain encoders do (for fp8 the block scale comes from y);
+ * the new residual is y minus the value the payload decodes to.
+ * --------------------------------------------------------------------- */
+void or_encode_bf16_ef(uint16_t* codes, float* residual, const float* x, size_t n) {
+  for (size_t i = 0; i < n; i++) {
+    float y = x[i] + residual[i];
+    codes[i] = or_bf16_encode_one(y);
+    residual[i] = y - or_bf16_decode_one(codes[i]);
+  }
+}
+
+void or_encode_fp8_ef(uint8_t* codes, float* scales, float* residual,
+                      const float* x, size_t n, int mode) {
+  size_t nblocks = (n + 255) / 256;
+  float y[256];
+  for (size_t b = 0; b < nblocks; b++) {
+    size_t start = b * 256;
+    size_t len = (n - start < 256) ? n - start : 256;
+    for (size_t i = 0; i < len; i++) y[i] = x[start + i] + residual[start + i];
+    float s = or_block_scale(or_block_absmax(y, len), mode);
+    scales[b] = s;
+    for (size_t i = 0; i < len; i++) {
+      uint8_t c = or_fp8_quantize_one(y[i], s);
+      codes[start + i] = c;
+      float decoded = or_e4m3_decode_one(c) * s;
+      residual[start + i] = y[i] - decoded;
+    }
+  }
+}
+
+void or_bucket_allreduce_ef(float* out, void* const* codes,
+                            float* const* scales, float* const* residuals,
+                            const float* const* x, int k, size_t n,
+                            size_t bucket_elems, int codec, int mode) {
+  const void* cs[64];
+  const float* ss[64];
+  size_t scale_base = 0;
+  for (size_t start = 0; start < n; start += bucket_elems) {
+    size_t len = (n - start < bucket_elems) ? n - start : bucket_elems;
+    for (int r = 0; r < k; r++) {
+      if (codec == OR_CODEC_BF16) {
+        uint16_t* c = (uint16_t*)codes[r] + start;
+        or_encode_bf16_ef(c, residuals[r] + start, x[r] + start, len);
+        cs[r] = c;
+        ss[r] = NULL;
+      } else {
+        uint8_t* c = (uint8_t*)codes[r] + start;
+        or_encode_fp8_ef(c, scales[r] + scale_base, residuals[r] + start,
+                         x[r] + start, len, mode);
         cs[r] = c;
         ss[r] = scales[r] + scale_base;
       }

@@ -74,6 +74,18 @@ void or_bucket_allreduce(float* out, void* const* codes, float* const* scales,
                          const float* const* x, int k, size_t n,
                          size_t bucket_elems, int codec, int mode);
 
+/* Error feedback: y = x + residual is encoded, and residual becomes
+ * y - decode(payload).  residual is read and written (caller-owned). */
+void or_encode_bf16_ef(uint16_t* codes, float* residual, const float* x, size_t n);
+void or_encode_fp8_ef(uint8_t* codes, float* scales, float* residual,
+                      const float* x, size_t n, int mode);
+/* The bucket stream with error feedback (bf16 or fp8): each rank's residual
+ * residuals[r][n] is updated as its buckets are encoded. */
+void or_bucket_allreduce_ef(float* out, void* const* codes,
+                            float* const* scales, float* const* residuals,
+                            const float* const* x, int k, size_t n,
+                            size_t bucket_elems, int codec, int mode);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,9 @@ def _load():
         "or_encode_fp8": (None, [_P, _P, _P, _S, _I]),
         "or_decode_accumulate": (None, [_P, _P, _P, _I, _S, _I, _I]),
         "or_bucket_allreduce": (None, [_P, _P, _P, _P, _I, _S, _S, _I, _I]),
+        "or_encode_bf16_ef": (None, [_P, _P, _P, _S]),
+        "or_encode_fp8_ef": (None, [_P, _P, _P, _P, _S, _I]),
+        "or_bucket_allreduce_ef": (None, [_P, _P, _P, _P, _P, _I, _S, _S, _I, _I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,3 +187,42 @@ def bucket_allreduce(xs, bucket_elems, codec, mode=SCALE_ABSMAX_DIV_448):
         _ptr(out), _ptr_array(codes), _ptr_array(scales) if scales else None,
         _ptr_array(xs), k, n, int(bucket_elems), int(codec), int(mode))
     return out, codes, scales
+
+
+def encode_bf16_ef(x, residual):
+    """Error-feedback bf16 encode: returns (codes, new residual)."""
+    x = _f32(x)
+    res = _f32(residual).copy()
+    codes = np.empty(x.size, dtype=np.uint16)
+    _load().or_encode_bf16_ef(_ptr(codes), _ptr(res), _ptr(x), x.size)
+    return codes, res
+
+
+def encode_fp8_ef(x, residual, mode):
+    """Error-feedback fp8 encode: returns (codes, scales, new residual)."""
+    x = _f32(x)
+    res = _f32(residual).copy()
+    codes = np.empty(x.size, dtype=np.uint8)
+    scales = np.empty(nblocks(x.size), dtype=np.float32)
+    _load().or_encode_fp8_ef(_ptr(codes), _ptr(scales), _ptr(res), _ptr(x), x.size, int(mode))
+    return codes, scales, res
+
+
+def bucket_allreduce_ef(xs, residuals, bucket_elems, codec, mode=SCALE_ABSMAX_DIV_448):
+    """Bucket stream with error feedback.  Returns (out, codes, scales or None,
+    new residuals)."""
+    xs = [_f32(x) for x in xs]
+    res = [_f32(r).copy() for r in residuals]
+    k, n = len(xs), xs[0].size
+    out = np.empty(n, dtype=np.float32)
+    if codec == CODEC_BF16:
+        codes = [np.empty(n, dtype=np.uint16) for _ in range(k)]
+        scales = None
+    else:
+        codes = [np.empty(n, dtype=np.uint8) for _ in range(k)]
+        nb = sum(nblocks(min(bucket_elems, n - s)) for s in range(0, n, bucket_elems))
+        scales = [np.empty(nb, dtype=np.float32) for _ in range(k)]
+    _load().or_bucket_allreduce_ef(
+        _ptr(out), _ptr_array(codes), _ptr_array(scales) if scales else None, _ptr_array(res),
+        _ptr_array(xs), k, n, int(bucket_elems), int(codec), int(mode))
+    return out, codes, scales, res
