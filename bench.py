@@ -26,6 +26,9 @@ Workloads (inputs from workloads.py):
                    separate output at every size.
   two_rank_4mib    k=2 x 2^20 fp32; gb_reduce_sum, gb_encode_bf16 of the sum,
                    gb_decode_accumulate(bf16, k=1).
+  ddp_1b_buckets_ef the ddp_1b_buckets stream with error feedback: each rank
+                   keeps an fp32 residual, encodes gradient + residual and
+                   writes the new residual (gb_bucket_allreduce_local_ef).
 
 The roofline object reports the step's dominant kernel: its algorithmic bytes
 per launch over its average launch time, timed with HIP events on the stream
@@ -50,7 +53,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="ddp_1b_buckets",
                    choices=["ddp_1b_buckets", "gradients_256mib", "gradients_64mib",
-                            "two_island_sweep", "two_rank_4mib"])
+                            "two_island_sweep", "two_rank_4mib", "ddp_1b_buckets_ef"])
     p.add_argument("--scale-mode", type=int, default=0, choices=[0, 1],
                    help="fp8 scale: 0 absmax/448, 1 power of two")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -187,6 +190,65 @@ class DdpBuckets(Workload):
             if t_oracle >= budget:
                 break
         sample = f"first {nb} of {len(self.W.ddp_buckets())} buckets ({nb * self.bucket:,} values x {self.k} ranks)"
+        return done_bytes, t_oracle, sample, ok
+
+
+class DdpBucketsEF(DdpBuckets):
+    name = "ddp_1b_buckets_ef"
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        self.config = dict(self.config, workload=self.name, error_feedback="fp32 residual per rank")
+
+    def setup(self):
+        super().setup()
+        self.res = [self.torch.zeros(self.n, dtype=self.torch.float32, device=self.dev) for _ in range(self.k)]
+
+    def step(self):
+        self.gb.gb_bucket_allreduce_local_ef(self.out, self.x, self.res, self.bucket,
+                                             self.gb.GB_CODEC_FP8_E4M3_B256, self.mode, self.ws)
+
+    def bytes_for(self, n):
+        # sources and residuals read; payload, residuals and sum written
+        return self.k * 8 * n + self.k * (n + 4 * nblocks(n)) + self.k * 4 * n + 4 * n
+
+    def timed_kernel(self):
+        return ("fused_fp8_ef_kernel<4>", self.step_bytes(), 1, self.step)
+
+    def extra(self, time_region, reps):
+        return {}
+
+    def cpu_sample(self, budget):
+        """One more step checked against the oracle from the residuals it starts
+        from, on the first buckets."""
+        from oracle import oracle as O
+        import numpy as np
+        torch = self.torch
+        torch.cuda.synchronize()
+        buckets = []
+        t_est = 0.0
+        for start, length in self.W.ddp_buckets():
+            buckets.append((start, length))
+            t_est += 2.2  # about 2.2 s of oracle work per 25 MiB bucket of 4 ranks
+            if t_est >= budget:
+                break
+        before = [[r[s:s + l].cpu().numpy() for r in self.res] for s, l in buckets]
+        self.step()
+        torch.cuda.synchronize()
+        done_bytes, t_oracle, ok = 0, 0.0, True
+        for (start, length), res0 in zip(buckets, before):
+            xs = [t[start:start + length].cpu().numpy() for t in self.x]
+            t0 = time.perf_counter()
+            want, codes, scales, res1 = O.bucket_allreduce_ef(xs, res0, self.bucket, O.CODEC_FP8, self.mode)
+            t_oracle += time.perf_counter() - t0
+            done_bytes += self.bytes_for(length)
+            ok &= bool((self.out[start:start + length].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
+            for r in range(self.k):
+                got = self.res[r][start:start + length].cpu().numpy().view(np.uint32)
+                ok &= bool((got == res1[r].view(np.uint32)).all())
+                c0 = r * self.lay["codes_stride"] + start
+                ok &= bool((self.ws[c0:c0 + length].cpu().numpy() == codes[r]).all())
+        sample = f"one step of the first {len(buckets)} of {len(self.W.ddp_buckets())} buckets"
         return done_bytes, t_oracle, sample, ok
 
 
@@ -382,7 +444,7 @@ class TwoRank(Workload):
         return self.step_bytes(), t, "the whole workload", ok
 
 
-WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank)}
+WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank, DdpBucketsEF)}
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 

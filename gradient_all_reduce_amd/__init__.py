@@ -23,6 +23,7 @@ __all__ = [
     "gb_encode_bf16", "gb_encode_fp8_e4m3_blockscaled", "gb_decode_accumulate",
     "gb_bucket_allreduce_local", "gb_payload_bytes", "gb_bucket_workspace_layout",
     "gb_bucket_workspace_bytes", "gb_status_string", "gb_last_error", "gb_version",
+    "gb_encode_bf16_ef", "gb_encode_fp8_e4m3_blockscaled_ef", "gb_bucket_allreduce_local_ef",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -49,6 +50,9 @@ _SIGNATURES = {
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
+    "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
+    "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
+    "gb_bucket_allreduce_local_ef": (_I, [_P, _PP, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
     "gb_payload_bytes": (_S, [_I, _S]),
     "gb_bucket_workspace_layout": (_I, [_I, _I, _S, _S, _SP, _SP, _SP, _SP]),
     "gb_bucket_workspace_bytes": (_S, [_I, _I, _S, _S]),
@@ -177,6 +181,50 @@ def gb_bucket_allreduce_local(out, srcs, bucket_elems, codec, scale_mode=GB_SCAL
     _check(_lib.gb_bucket_allreduce_local(_ptr(out), _ptr_array(srcs), len(srcs), n,
                                           int(bucket_elems), int(codec), int(scale_mode),
                                           _ptr(workspace), ws_bytes, _stream(stream, out.device)))
+
+
+def gb_encode_bf16_ef(codes, residual, src, stream=None):
+    """Error-feedback bf16 encode: encodes src + residual, updates residual."""
+    _device_tensor(codes, torch.uint16, "codes")
+    _device_tensor(residual, torch.float32, "residual")
+    _device_tensor(src, torch.float32, "src")
+    _same_numel([codes, residual], src.numel(), "codes/residual")
+    _check(_lib.gb_encode_bf16_ef(_ptr(codes), _ptr(residual), _ptr(src), src.numel(),
+                                  _stream(stream, src.device)))
+
+
+def gb_encode_fp8_e4m3_blockscaled_ef(codes, scales, residual, src, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                      stream=None):
+    """Error-feedback fp8 encode: encodes src + residual, updates residual."""
+    _device_tensor(codes, torch.uint8, "codes")
+    _device_tensor(scales, torch.float32, "scales")
+    _device_tensor(residual, torch.float32, "residual")
+    _device_tensor(src, torch.float32, "src")
+    n = src.numel()
+    _same_numel([codes, residual], n, "codes/residual")
+    _same_numel([scales], (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    _check(_lib.gb_encode_fp8_e4m3_blockscaled_ef(_ptr(codes), _ptr(scales), _ptr(residual), _ptr(src), n,
+                                                  int(scale_mode), _stream(stream, src.device)))
+
+
+def gb_bucket_allreduce_local_ef(out, srcs, residuals, bucket_elems, codec,
+                                 scale_mode=GB_SCALE_ABSMAX_DIV_448, workspace=None, stream=None):
+    """Bucket stream with error feedback: residuals[r] is updated for rank r."""
+    _device_tensor(out, torch.float32, "out")
+    n = out.numel()
+    for name, ts in (("srcs", srcs), ("residuals", residuals)):
+        for i, t in enumerate(ts):
+            _device_tensor(t, torch.float32, f"{name}[{i}]")
+        _same_numel(ts, n, name)
+    if len(residuals) != len(srcs):
+        raise ValueError("one residual per source is needed")
+    ws_bytes = 0
+    if workspace is not None:
+        _device_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(_lib.gb_bucket_allreduce_local_ef(_ptr(out), _ptr_array(srcs), _ptr_array(residuals), len(srcs), n,
+                                             int(bucket_elems), int(codec), int(scale_mode), _ptr(workspace),
+                                             ws_bytes, _stream(stream, out.device)))
 
 
 def gb_payload_bytes(codec, n):

@@ -200,24 +200,28 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float
   }
 }
 
-gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k, size_t n,
-                                    size_t bucket_elems, int codec, int scale_mode, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local";
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two bucket-stream calls; on success fills the
+// workspace layout and the source table.
+gb_status check_bucket(const char* fn, float* out, const float* const* srcs, int k, size_t n,
+                       size_t bucket_elems, int codec, int scale_mode, void* workspace, size_t workspace_bytes,
+                       size_t* cs, size_t* so, size_t* ss, gb::PtrTable* t) {
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
   if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
     return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
   }
-  size_t cs, so, ss, need;
-  gb_status s = gb_bucket_workspace_layout(codec, k, n, bucket_elems, &cs, &so, &ss, &need);
+  size_t need;
+  gb_status s = gb_bucket_workspace_layout(codec, k, n, bucket_elems, cs, so, ss, &need);
   if (s != GB_OK) {
     // re-label the failure with this function's name
     return fail(s, "%s: %s", fn, g_last_error + std::strlen("gb_bucket_workspace_layout: "));
   }
   if (n == 0) return GB_OK;
   if ((s = check_array(out, GB_ALIGN, fn, "out")) != GB_OK) return s;
-  gb::PtrTable t = {};
-  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) {
+  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", t)) != GB_OK) {
     return s;
   }
   if (codec != GB_CODEC_NONE) {
@@ -229,6 +233,22 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
       return fail(GB_ERR_MISALIGNED, "%s: workspace = %p is not 256-byte aligned", fn, workspace);
     }
   }
+  return GB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k, size_t n,
+                                    size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const char* fn = "gb_bucket_allreduce_local";
+  size_t cs, so, ss;
+  gb::PtrTable t = {};
+  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes,
+                             &cs, &so, &ss, &t);
+  if (s != GB_OK || n == 0) return s;
   hipStream_t st = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   // Every bucket starts on a 256-value boundary, so the blocks of a bucket
@@ -253,8 +273,68 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
     }
     e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, st);
   }
-  if (e != hipSuccess) return from_hip(e, fn);
-  return GB_OK;
+  return from_hip(e, fn);
+}
+
+gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n, void* stream) {
+  const char* fn = "gb_encode_bf16_ef";
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  return from_hip(gb::launch_encode_bf16_ef(codes, residual, src, n, as_stream(stream)), fn);
+}
+
+gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales, float* residual, const float* src,
+                                            size_t n, int scale_mode, void* stream) {
+  const char* fn = "gb_encode_fp8_e4m3_blockscaled_ef";
+  if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+  if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  return from_hip(gb::launch_encode_fp8_ef(codes, scales, residual, src, n, scale_mode, as_stream(stream)), fn);
+}
+
+gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, float* const* residuals, int k,
+                                       size_t n, size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "gb_bucket_allreduce_local_ef";
+  if (codec == GB_CODEC_NONE) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
+  }
+  size_t cs, so, ss;
+  gb::PtrTable t = {};
+  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes,
+                             &cs, &so, &ss, &t);
+  if (s != GB_OK || n == 0) return s;
+  gb::PtrTable rt = {};
+  if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals", &rt)) !=
+      GB_OK) {
+    return s;
+  }
+  float* res[GB_MAX_K];
+  for (int r = 0; r < k; r++) res[r] = residuals[r];
+  hipStream_t st = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  if (codec == GB_CODEC_BF16) {
+    uint16_t* c[GB_MAX_K];
+    for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
+    e = gb::launch_fused_bf16_ef(out, t, res, c, k, n, st);
+  } else {
+    uint8_t* c[GB_MAX_K];
+    float* sc[GB_MAX_K];
+    for (int r = 0; r < k; r++) {
+      c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
+      sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
+    }
+    e = gb::launch_fused_fp8_ef(out, t, res, c, sc, k, n, scale_mode, st);
+  }
+  return from_hip(e, fn);
 }
 
 }  // extern "C"

@@ -192,6 +192,40 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/*
+ * Error feedback (README "Bridge compression": each bridge member keeps an
+ * error-feedback residual per buffer, so the rounding error of one step is
+ * carried into the next instead of accumulating).  The residual is a
+ * caller-owned device fp32[n] per buffer, 16-byte aligned, zero before the
+ * first step; each call reads it and writes it back:
+ *   y[i]        = RN(src[i] + residual[i])
+ *   payload     = the plain encoder's payload of y (for fp8 the block scales
+ *                 come from y)
+ *   residual[i] = RN(y[i] - decoded payload value[i])   (exact for bf16)
+ * The residual must not overlap src or the payload.  Non-finite values follow
+ * the formulas (an Inf y gives a NaN residual).
+ */
+gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src,
+                            size_t n, void* stream);
+gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales,
+                                            float* residual, const float* src,
+                                            size_t n, int scale_mode,
+                                            void* stream);
+
+/*
+ * gb_bucket_allreduce_local_ef — gb_bucket_allreduce_local with error
+ * feedback: rank r's buckets are encoded from y = srcs[r] + residuals[r] and
+ * residuals[r] is updated as above; out receives the rank-order sum of the
+ * decoded payloads.  residuals: host array of k device fp32[n] pointers.
+ * codec must be BF16 or FP8 (GB_ERR_UNSUPPORTED for NONE: there is no
+ * rounding to feed back).
+ */
+gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs,
+                                       float* const* residuals, int k, size_t n,
+                                       size_t bucket_elems, int codec,
+                                       int scale_mode, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Bytes one rank's n-value payload occupies on the bridge:
  * 4n (NONE), 2n (BF16), n + 4*ceil(n/256) (FP8).  0 for an unknown codec. */
 size_t gb_payload_bytes(int codec, size_t n);
