@@ -33,6 +33,11 @@
  *                         [test_oracle_decode.py].
  *   or_bucket_allreduce   equals the whole-buffer encode + decode when
  *                         buckets are multiples of 256 [test_oracle_decode.py].
+ *   or_reduce (AVG, MAX,  AVG: exact rational RN(sum / d) on exact sums; k
+ *   MIN)                  copies of x averaged over k give x.  MAX/MIN:
+ *                         brute force against an exact order with the
+ *                         IEEE 754-2019 zero and NaN rules; rank-permutation
+ *                         invariance [test_oracle_ops.py].
  *   or_encode_*_ef        with a zero residual the payload is the plain
  *                         encode; the bf16 residual is exact and within half
  *                         an ulp; exact rational step-by-step simulation with
@@ -378,5 +383,50 @@ void or_bucket_allreduce_ef(float* out, void* const* codes,
     or_decode_accumulate(out + start, cs, codec == OR_CODEC_FP8 ? ss : NULL, k,
                          len, codec, 0);
     scale_base += (len + 255) / 256;
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Other reductions.  README "API": all_reduce takes SUM, AVG, MAX or MIN;
+ * AVG is a SUM divided by the world size, identically on every rank.  The
+ * world size is the number of ranks in the job, not the number k of island
+ * sums the leader adds, so it is an explicit divisor d (reading taken).
+ *   AVG:  out = RN(sum / RN(d)), sum the fixed-order SUM.
+ *   MAX:  IEEE 754-2019 maximum over ranks (reading taken: the README leaves
+ *         NaN to the backends): NaN if any value is NaN, otherwise the
+ *         largest, with +0 above -0.
+ *   MIN:  likewise the smallest, with -0 below +0.
+ * --------------------------------------------------------------------- */
+static float max2019(float a, float b) {
+  if (isnan(a) || isnan(b)) return NAN;
+  if (a > b) return a;
+  if (b > a) return b;
+  /* equal: they differ only if one is +0 and the other -0 */
+  return signbit(a) ? b : a;
+}
+
+static float min2019(float a, float b) {
+  if (isnan(a) || isnan(b)) return NAN;
+  if (a < b) return a;
+  if (b < a) return b;
+  return signbit(a) ? a : b;
+}
+
+void or_reduce(float* out, const float* const* x, int k, size_t n, int op,
+               int divisor) {
+  if (op == OR_OP_SUM || op == OR_OP_AVG) {
+    or_reduce_sum(out, x, k, n);
+    if (op == OR_OP_AVG) {
+      float d = (float)divisor;
+      for (size_t i = 0; i < n; i++) out[i] = out[i] / d;
+    }
+    return;
+  }
+  for (size_t i = 0; i < n; i++) {
+    float acc = x[0][i];
+    for (int r = 1; r < k; r++) {
+      acc = (op == OR_OP_MAX) ? max2019(acc, x[r][i]) : min2019(acc, x[r][i]);
+    }
+    out[i] = acc;
   }
 }

@@ -32,6 +32,7 @@ extern "C" {
 /* Codec numbers and scale-mode numbers of this oracle. */
 enum { OR_CODEC_NONE = 0, OR_CODEC_BF16 = 1, OR_CODEC_FP8 = 2 };
 enum { OR_SCALE_ABSMAX_DIV_448 = 0, OR_SCALE_POW2 = 1 };
+enum { OR_OP_SUM = 0, OR_OP_AVG = 1, OR_OP_MAX = 2, OR_OP_MIN = 3 };
 
 /* out[i] = left fold over ranks 0..k-1 of x[r][i], starting from x[0][i]. */
 void or_reduce_sum(float* out, const float* const* x, int k, size_t n);
@@ -73,6 +74,10 @@ void or_decode_accumulate(float* acc, const void* const* codes,
 void or_bucket_allreduce(float* out, void* const* codes, float* const* scales,
                          const float* const* x, int k, size_t n,
                          size_t bucket_elems, int codec, int mode);
+
+/* SUM, AVG (SUM / divisor, the world size), MAX or MIN over k ranks. */
+void or_reduce(float* out, const float* const* x, int k, size_t n, int op,
+               int divisor);
 
 /* Error feedback: y = x + residual is encoded, and residual becomes
  * y - decode(payload).  residual is read and written (caller-owned). */

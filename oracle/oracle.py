@@ -17,6 +17,7 @@ import numpy as np
 from . import build as _build
 
 CODEC_NONE, CODEC_BF16, CODEC_FP8 = 0, 1, 2
+OP_SUM, OP_AVG, OP_MAX, OP_MIN = 0, 1, 2, 3
 SCALE_ABSMAX_DIV_448, SCALE_POW2 = 0, 1
 BLOCK = 256
 
@@ -48,6 +49,7 @@ def _load():
         "or_encode_fp8": (None, [_P, _P, _P, _S, _I]),
         "or_decode_accumulate": (None, [_P, _P, _P, _I, _S, _I, _I]),
         "or_bucket_allreduce": (None, [_P, _P, _P, _P, _I, _S, _S, _I, _I]),
+        "or_reduce": (None, [_P, _P, _I, _S, _I, _I]),
         "or_encode_bf16_ef": (None, [_P, _P, _P, _S]),
         "or_encode_fp8_ef": (None, [_P, _P, _P, _P, _S, _I]),
         "or_bucket_allreduce_ef": (None, [_P, _P, _P, _P, _P, _I, _S, _S, _I, _I]),
@@ -86,6 +88,15 @@ def reduce_sum(xs):
     n = xs[0].size
     out = np.empty(n, dtype=np.float32)
     _load().or_reduce_sum(_ptr(out), _ptr_array(xs), len(xs), n)
+    return out
+
+
+def reduce(xs, op, divisor=1):
+    """SUM, AVG (divided by `divisor`), MAX or MIN over ranks."""
+    xs = [_f32(x) for x in xs]
+    n = xs[0].size
+    out = np.empty(n, dtype=np.float32)
+    _load().or_reduce(_ptr(out), _ptr_array(xs), len(xs), n, int(op), int(divisor))
     return out
 
 
