@@ -56,6 +56,9 @@ def parse():
                             "two_island_sweep", "two_rank_4mib", "ddp_1b_buckets_ef"])
     p.add_argument("--scale-mode", type=int, default=0, choices=[0, 1],
                    help="fp8 scale: 0 absmax/448, 1 power of two")
+    p.add_argument("--op", default="sum", choices=["sum", "avg", "max", "min"],
+                   help="reduction of the two_island_sweep workload (avg divides by the "
+                        "world size, 2 here)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="rough budget of oracle CPU time for the baseline sample")
@@ -360,14 +363,17 @@ class Gradients64(Workload):
 
 class Sweep(Workload):
     name = "two_island_sweep"
+    OPS = {"sum": 0, "avg": 1, "max": 2, "min": 3}
 
     def __init__(self, gb, torch, args):
         super().__init__(gb, torch, args)
         import workloads as W
         self.W = W
         self.sizes = W.SWEEP_SIZES
+        self.op = self.OPS[args.op]
         self.config = {"workload": self.name, "k": 2, "sizes": f"2^8..2^26 values ({len(self.sizes)} sizes)",
-                       "distribution": "N(0,1)", "path": "reduce_sum into a separate output"}
+                       "distribution": "N(0,1)", "op": args.op,
+                       "path": f"{args.op} of the two island results into a separate output"}
 
     def setup(self):
         torch = self.torch
@@ -375,16 +381,23 @@ class Sweep(Workload):
         self.x = {n: [torch.from_numpy(a).to(self.dev) for a in xs] for n, xs in self.xh.items()}
         self.out = {n: torch.empty(n, dtype=torch.float32, device=self.dev) for n in self.sizes}
 
+    def reduce(self, n):
+        if self.op == 0:
+            self.gb.gb_reduce_sum(self.out[n], self.x[n])
+        else:
+            self.gb.gb_reduce(self.out[n], self.x[n], self.op, 2)
+
     def step(self):
         for n in self.sizes:
-            self.gb.gb_reduce_sum(self.out[n], self.x[n])
+            self.reduce(n)
 
     def step_bytes(self):
         return sum(12 * n for n in self.sizes)
 
     def timed_kernel(self):
         n = self.sizes[-1]
-        return ("reduce_sum_kernel<2,false>", 12 * n, 1, lambda: self.gb.gb_reduce_sum(self.out[n], self.x[n]))
+        name = "reduce_sum_kernel<2,false>" if self.op == 0 else f"reduce_op_kernel<2,{self.op}>"
+        return (name, 12 * n, 1, lambda: self.reduce(n))
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -393,9 +406,11 @@ class Sweep(Workload):
         t, ok = 0.0, True
         for n in self.sizes:
             t0 = time.perf_counter()
-            want = O.reduce_sum(self.xh[n])
+            want = O.reduce(self.xh[n], self.op, 2)
             t += time.perf_counter() - t0
-            ok &= bool((self.out[n].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
+            got = self.out[n].cpu().numpy()
+            ok &= bool((np.isnan(got) == np.isnan(want)).all())
+            ok &= bool((got.view(np.uint32)[~np.isnan(got)] == want.view(np.uint32)[~np.isnan(want)]).all())
         return self.step_bytes(), t, "the whole sweep", ok
 
 

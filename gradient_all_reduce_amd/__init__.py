@@ -24,12 +24,14 @@ __all__ = [
     "gb_bucket_allreduce_local", "gb_payload_bytes", "gb_bucket_workspace_layout",
     "gb_bucket_workspace_bytes", "gb_status_string", "gb_last_error", "gb_version",
     "gb_encode_bf16_ef", "gb_encode_fp8_e4m3_blockscaled_ef", "gb_bucket_allreduce_local_ef",
+    "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
 GB_ERR_UNSUPPORTED, GB_ERR_WORKSPACE, GB_ERR_HIP = 3, 4, 5
 GB_CODEC_NONE, GB_CODEC_BF16, GB_CODEC_FP8_E4M3_B256 = 0, 1, 2
 GB_SCALE_ABSMAX_DIV_448, GB_SCALE_POW2 = 0, 1
+GB_OP_SUM, GB_OP_AVG, GB_OP_MAX, GB_OP_MIN = 0, 1, 2, 3
 GB_BLOCK = 256
 GB_MAX_K = 8
 
@@ -46,6 +48,7 @@ _PP = ctypes.POINTER(ctypes.c_void_p)
 _SP = ctypes.POINTER(ctypes.c_size_t)
 _SIGNATURES = {
     "gb_reduce_sum": (_I, [_P, _PP, _I, _S, _P]),
+    "gb_reduce": (_I, [_P, _PP, _I, _S, _I, _I, _P]),
     "gb_encode_bf16": (_I, [_P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
@@ -125,6 +128,16 @@ def gb_reduce_sum(dst, srcs, stream=None):
     _same_numel(srcs, dst.numel(), "srcs")
     _check(_lib.gb_reduce_sum(_ptr(dst), _ptr_array(srcs), len(srcs), dst.numel(),
                               _stream(stream, dst.device)))
+
+
+def gb_reduce(dst, srcs, op, divisor=1, stream=None):
+    """dst = SUM, AVG (sum / divisor, the world size), MAX or MIN of srcs."""
+    _device_tensor(dst, torch.float32, "dst")
+    for i, s in enumerate(srcs):
+        _device_tensor(s, torch.float32, f"srcs[{i}]")
+    _same_numel(srcs, dst.numel(), "srcs")
+    _check(_lib.gb_reduce(_ptr(dst), _ptr_array(srcs), len(srcs), dst.numel(), int(op), int(divisor),
+                          _stream(stream, dst.device)))
 
 
 def gb_encode_bf16(codes, src, stream=None):

@@ -340,6 +340,37 @@ __global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTab
 }
 
 // ===========================================================================
+// AVG, MAX and MIN over K sources (README "API": all_reduce takes SUM, AVG,
+// MAX or MIN; AVG is the SUM divided by the world size).  AVG divides the
+// fixed-order sum by d with a correctly rounded binary32 divide; MAX and MIN
+// are the IEEE 754-2019 maximum and minimum (NaN propagates, -0 < +0), which
+// gfx950 executes as v_maximum3_f32 / v_minimum3_f32.
+// ===========================================================================
+template <int K, int OP, bool FULL>
+__device__ __forceinline__ void reduce_op_body(float* dst, const PtrTable& src, size_t n, float d) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (!FULL && i >= n) return;
+  f4 x[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) x[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), i, n);
+  f4 s = x[0];
+#pragma unroll
+  for (int r = 1; r < K; r++) {
+    if (OP == GB_OP_AVG) s = s + x[r];
+    if (OP == GB_OP_MAX) s = __builtin_elementwise_maximum(s, x[r]);
+    if (OP == GB_OP_MIN) s = __builtin_elementwise_minimum(s, x[r]);
+  }
+  if (OP == GB_OP_AVG) s = s / d;
+  store4_at<FULL>(dst, i, n, s);
+}
+
+template <int K, int OP>
+__global__ __launch_bounds__(kThreads) void reduce_op_kernel(float* dst, PtrTable src, size_t n, float d) {
+  if (group_full(kVecPerGroup, n)) reduce_op_body<K, OP, true>(dst, src, n, d);
+  else reduce_op_body<K, OP, false>(dst, src, n, d);
+}
+
+// ===========================================================================
 // bf16 encode and decode-accumulate: one 4-value vector per lane, so each
 // instruction of a wavefront loads 1 KiB of fp32 and stores 512 bytes of
 // codes (or the reverse), contiguously.
@@ -685,6 +716,22 @@ hipError_t launch_reduce_sum(float* dst, const PtrTable& srcs, int k, size_t n, 
   (void)hipGetLastError();
 #define GB_CALL(K)                                                                     \
   if (accumulate) reduce_sum_kernel<K, true><<<grid, kThreads, 0, stream>>>(dst, srcs, n); \
+  else reduce_sum_kernel<K, false><<<grid, kThreads, 0, stream>>>(dst, srcs, n);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_op(float* dst, const PtrTable& srcs, int k, size_t n, int op, int divisor,
+                            hipStream_t stream) {
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
+  const float d = (float)divisor;
+  (void)hipGetLastError();
+#define GB_CALL(K)                                                                                \
+  if (op == GB_OP_AVG) reduce_op_kernel<K, GB_OP_AVG><<<grid, kThreads, 0, stream>>>(dst, srcs, n, d);      \
+  else if (op == GB_OP_MAX) reduce_op_kernel<K, GB_OP_MAX><<<grid, kThreads, 0, stream>>>(dst, srcs, n, d); \
+  else if (op == GB_OP_MIN) reduce_op_kernel<K, GB_OP_MIN><<<grid, kThreads, 0, stream>>>(dst, srcs, n, d); \
   else reduce_sum_kernel<K, false><<<grid, kThreads, 0, stream>>>(dst, srcs, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL

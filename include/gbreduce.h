@@ -87,6 +87,15 @@ typedef enum gb_scale_mode {
   GB_SCALE_POW2 = 1
 } gb_scale_mode;
 
+/* Reductions of gb_reduce (README "API": all_reduce with SUM, AVG, MAX or
+ * MIN).  The bridge codecs apply to SUM and AVG only. */
+typedef enum gb_op {
+  GB_OP_SUM = 0,
+  GB_OP_AVG = 1, /* the SUM divided by the world size (an explicit divisor) */
+  GB_OP_MAX = 2, /* IEEE 754-2019 maximum: NaN if any value is NaN; +0 > -0 */
+  GB_OP_MIN = 3  /* IEEE 754-2019 minimum: NaN if any value is NaN; -0 < +0 */
+} gb_op;
+
 /*
  * gb_reduce_sum — the leader's sum of island sums (README "How it works":
  * leaders all-reduce the island sums, each leader then holds the total).
@@ -101,6 +110,23 @@ typedef enum gb_scale_mode {
  */
 gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n,
                         void* stream);
+
+/*
+ * gb_reduce — the leader's uncompressed all_reduce of the island results with
+ * any of the README's reductions:
+ *   SUM  dst[i] = the fixed-order sum (exactly gb_reduce_sum);
+ *   AVG  dst[i] = RN(sum[i] / RN(divisor)): divisor is the job's world size
+ *        (the number of ranks, not k), 1 .. 2^24; identical on every rank;
+ *   MAX  dst[i] = IEEE 754-2019 maximum over the k values (rank order does not
+ *        matter; a NaN anywhere gives NaN);
+ *   MIN  dst[i] = IEEE 754-2019 minimum.
+ * divisor is ignored except for AVG.  A compressed AVG is
+ * gb_decode_accumulate followed by gb_reduce(acc, {acc}, 1, n, GB_OP_AVG, d).
+ * Arguments, aliasing and errors as gb_reduce_sum; GB_ERR_UNSUPPORTED for an
+ * unknown op, GB_ERR_INVALID_ARG for an AVG divisor outside 1 .. 2^24.
+ */
+gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n,
+                    int op, int divisor, void* stream);
 
 /*
  * gb_encode_bf16 — bf16 bridge compression of one fp32 payload

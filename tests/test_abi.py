@@ -53,7 +53,8 @@ def test_constants_match_header(gb):
             assert getattr(gb, name) == v
     for name in ["GB_OK", "GB_ERR_INVALID_ARG", "GB_ERR_MISALIGNED", "GB_ERR_UNSUPPORTED",
                  "GB_ERR_WORKSPACE", "GB_ERR_HIP", "GB_CODEC_NONE", "GB_CODEC_BF16",
-                 "GB_CODEC_FP8_E4M3_B256", "GB_SCALE_ABSMAX_DIV_448", "GB_SCALE_POW2"]:
+                 "GB_CODEC_FP8_E4M3_B256", "GB_SCALE_ABSMAX_DIV_448", "GB_SCALE_POW2",
+                 "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN"]:
         v = int(re.search(rf"\b{name} = (\d+)", text).group(1))
         assert getattr(gb, name) == v, name
 
@@ -120,6 +121,23 @@ def _arr(*addrs):
                                            ctypes.c_void_p(512), 1 << 20, None), 3, "scale mode"),
 ])
 def test_validation_rejects_before_launch(gb, call, status, msg):
+    assert call(gb._lib) == status
+    assert msg in gb.gb_last_error()
+
+
+@pytest.mark.parametrize("call,status,msg", [
+    (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 1, 10, 7, 1, None), 3, "unknown op"),
+    (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 1, 10, 1, 0, None), 1, "divisor"),
+    (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 1, 10, 1, (1 << 24) + 1, None), 1, "divisor"),
+    (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 0, 10, 2, 1, None), 1, "k = 0"),
+    (lambda L: L.gb_bucket_allreduce_local_ef(ctypes.c_void_p(256), _arr(256), _arr(512), 1, 1000, 256, 0, 0,
+                                              None, 0, None), 3, "lossy codec"),
+    (lambda L: L.gb_bucket_allreduce_local_ef(ctypes.c_void_p(256), _arr(256), _arr(520), 1, 1000, 256, 2, 0,
+                                              ctypes.c_void_p(512), 1 << 20, None), 2, "residuals[0]"),
+    (lambda L: L.gb_encode_bf16_ef(ctypes.c_void_p(256), ctypes.c_void_p(264), ctypes.c_void_p(256), 10, None),
+     2, "residual"),
+])
+def test_validation_of_the_wider_calls(gb, call, status, msg):
     assert call(gb._lib) == status
     assert msg in gb.gb_last_error()
 
