@@ -26,6 +26,13 @@ Workloads (inputs from workloads.py):
                    separate output at every size.
   two_rank_4mib    k=2 x 2^20 fp32; gb_reduce_sum, gb_encode_bf16 of the sum,
                    gb_decode_accumulate(bf16, k=1).
+  staged_fp8_256mib the leader's staged (pipelined) bridge step on one GPU:
+                   its 2^26-value fp32 island sum encoded to fp8 and copied to
+                   pinned host memory in 4 MiB chunks (gb_encode_staged), then
+                   the 4 leaders' payloads copied back from pinned host memory
+                   in chunks and decoded-and-accumulated
+                   (gb_decode_accumulate_staged).  Bound by the host link;
+                   the same work done serially is reported too.
   ddp_1b_buckets_ef the ddp_1b_buckets stream with error feedback: each rank
                    keeps an fp32 residual, encodes gradient + residual and
                    writes the new residual (gb_bucket_allreduce_local_ef).
@@ -53,7 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="ddp_1b_buckets",
                    choices=["ddp_1b_buckets", "gradients_256mib", "gradients_64mib",
-                            "two_island_sweep", "two_rank_4mib", "ddp_1b_buckets_ef"])
+                            "two_island_sweep", "two_rank_4mib", "ddp_1b_buckets_ef",
+                            "staged_fp8_256mib"])
     p.add_argument("--scale-mode", type=int, default=0, choices=[0, 1],
                    help="fp8 scale: 0 absmax/448, 1 power of two")
     p.add_argument("--op", default="sum", choices=["sum", "avg", "max", "min"],
@@ -253,6 +261,110 @@ class DdpBucketsEF(DdpBuckets):
                 ok &= bool((self.ws[c0:c0 + length].cpu().numpy() == codes[r]).all())
         sample = f"one step of the first {len(buckets)} of {len(self.W.ddp_buckets())} buckets"
         return done_bytes, t_oracle, sample, ok
+
+
+class Staged(Workload):
+    name = "staged_fp8_256mib"
+    CHUNK = (4 << 20) // 4  # 4 MiB of fp32 per chunk
+
+    def __init__(self, gb, torch, args):
+        super().__init__(gb, torch, args)
+        import workloads as W
+        self.W = W
+        self.k, self.n = 4, W.GRAD256_N
+        self.mode = args.scale_mode
+        self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n, "chunk_elems": self.CHUNK,
+                       "codec": "fp8_e4m3_b256", "scale_mode": ["absmax_div_448", "pow2"][self.mode],
+                       "distribution": "N(0, sigma=1e-3), 1% outliers x100",
+                       "path": "encode_staged (device -> pinned host) + decode_accumulate_staged "
+                               "(pinned host -> device, k=4)"}
+
+    def setup(self):
+        torch, gb, n, k = self.torch, self.gb, self.n, self.k
+        nb = nblocks(n)
+        self.xh = self.W.gradient_ranks(k, n)
+        self.x = [torch.from_numpy(a).to(self.dev) for a in self.xh]
+        self.cd = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.sd = torch.empty(nb, dtype=torch.float32, device=self.dev)
+        self.ch = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+        self.sh = torch.empty(nb, dtype=torch.float32, pin_memory=True)
+        # the payloads of the k leaders as the bridge delivers them: pinned host memory
+        self.rh, self.rsh = [], []
+        for r in range(k):
+            gb.gb_encode_fp8_e4m3_blockscaled(self.cd, self.sd, self.x[r], self.mode)
+            self.rh.append(self.cd.cpu().pin_memory())
+            self.rsh.append(self.sd.cpu().pin_memory())
+        self.rd = [torch.empty(n, dtype=torch.uint8, device=self.dev) for _ in range(k)]
+        self.rsd = [torch.empty(nb, dtype=torch.float32, device=self.dev) for _ in range(k)]
+        self.acc = torch.empty(n, dtype=torch.float32, device=self.dev)
+
+    def step(self):
+        gb = self.gb
+        gb.gb_encode_staged(gb.GB_CODEC_FP8_E4M3_B256, self.cd, self.sd, self.ch, self.sh, self.x[0], self.CHUNK,
+                            self.mode)
+        gb.gb_decode_accumulate_staged(self.acc, self.rh, self.rsh, self.rd, self.rsd,
+                                       gb.GB_CODEC_FP8_E4M3_B256, self.CHUNK)
+
+    def serial_step(self):
+        gb = self.gb
+        gb.gb_encode_fp8_e4m3_blockscaled(self.cd, self.sd, self.x[0], self.mode)
+        self.ch.copy_(self.cd, non_blocking=True)
+        self.sh.copy_(self.sd, non_blocking=True)
+        for r in range(self.k):
+            self.rd[r].copy_(self.rh[r], non_blocking=True)
+            self.rsd[r].copy_(self.rsh[r], non_blocking=True)
+        gb.gb_decode_accumulate(self.acc, self.rd, self.rsd, gb.GB_CODEC_FP8_E4M3_B256)
+
+    def payload(self):
+        return self.n + 4 * nblocks(self.n)
+
+    def step_bytes(self):
+        # HBM: encode (4n read, payload written), the D2H copy (payload read),
+        # the H2D copies (k payloads written), decode (k payloads read, 4n written)
+        return 4 * self.n + 2 * self.payload() + 2 * self.k * self.payload() + 4 * self.n
+
+    def timed_kernel(self):
+        n = self.n
+        per = self.k * self.payload() + 4 * n
+        return ("decode_fp8_kernel<4,false>", per, 1,
+                lambda: self.gb.gb_decode_accumulate(self.acc, self.rd, self.rsd, self.gb.GB_CODEC_FP8_E4M3_B256))
+
+    def extra(self, time_region, reps):
+        self.serial_step()
+        serial_ms = time_region(self.serial_step, reps) / reps
+        staged_ms = time_region(self.step, reps) / reps
+        sweep = {}
+        default_chunk = self.CHUNK
+        for chunk in (1 << 18, 1 << 20, 1 << 22, 1 << 24):
+            self.CHUNK = chunk
+            sweep[str(chunk)] = round(time_region(self.step, reps) / reps, 4)
+        self.CHUNK = default_chunk
+        link = (1 + self.k) * self.payload()
+        d2h = self.torch.empty(self.payload(), dtype=self.torch.uint8, pin_memory=True)
+        src = self.torch.empty(self.payload(), dtype=self.torch.uint8, device=self.dev)
+        copy_ms = time_region(lambda: d2h.copy_(src, non_blocking=True), reps) / reps
+        return {"link_payload_bytes_per_step": link,
+                "link_gbs_staged": round(link / (staged_ms * 1e-3) / 1e9, 2),
+                "staged_ms": round(staged_ms, 4), "serial_ms": round(serial_ms, 4),
+                "overlap_speedup": round(serial_ms / staged_ms, 4),
+                "staged_ms_by_chunk_elems": sweep,
+                "d2h_copy_gbs_one_payload": round(self.payload() / (copy_ms * 1e-3) / 1e9, 2)}
+
+    def cpu_sample(self, budget):
+        from oracle import oracle as O
+        import numpy as np
+        self.step()
+        self.torch.cuda.synchronize()
+        m = 1 << 22
+        t0 = time.perf_counter()
+        wc, ws = O.encode_fp8(self.xh[0][:m], self.mode)
+        enc = [O.encode_fp8(a[:m], self.mode) for a in self.xh]
+        want = O.decode_accumulate([c for c, _ in enc], [s for _, s in enc], O.CODEC_FP8)
+        t = time.perf_counter() - t0
+        ok = bool((self.ch[:m].numpy() == wc).all()) and bool((self.sh[:m // 256].numpy() == ws).all())
+        ok &= bool((self.acc[:m].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
+        p = m + 4 * nblocks(m)
+        return 4 * m + 2 * p + 2 * self.k * p + 4 * m, t, f"first {m:,} values of each rank", ok
 
 
 class Gradients256(Workload):
@@ -459,7 +571,7 @@ class TwoRank(Workload):
         return self.step_bytes(), t, "the whole workload", ok
 
 
-WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank, DdpBucketsEF)}
+WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank, DdpBucketsEF, Staged)}
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 

@@ -25,6 +25,7 @@ __all__ = [
     "gb_bucket_workspace_bytes", "gb_status_string", "gb_last_error", "gb_version",
     "gb_encode_bf16_ef", "gb_encode_fp8_e4m3_blockscaled_ef", "gb_bucket_allreduce_local_ef",
     "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
+    "gb_encode_staged", "gb_decode_accumulate_staged",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -56,6 +57,8 @@ _SIGNATURES = {
     "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
     "gb_bucket_allreduce_local_ef": (_I, [_P, _PP, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
+    "gb_encode_staged": (_I, [_I, _I, _P, _P, _P, _P, _P, _S, _S, _P]),
+    "gb_decode_accumulate_staged": (_I, [_P, _PP, _PP, _PP, _PP, _I, _S, _S, _I, _I, _P]),
     "gb_payload_bytes": (_S, [_I, _S]),
     "gb_bucket_workspace_layout": (_I, [_I, _I, _S, _S, _SP, _SP, _SP, _SP]),
     "gb_bucket_workspace_bytes": (_S, [_I, _I, _S, _S]),
@@ -238,6 +241,59 @@ def gb_bucket_allreduce_local_ef(out, srcs, residuals, bucket_elems, codec,
     _check(_lib.gb_bucket_allreduce_local_ef(_ptr(out), _ptr_array(srcs), _ptr_array(residuals), len(srcs), n,
                                              int(bucket_elems), int(codec), int(scale_mode), _ptr(workspace),
                                              ws_bytes, _stream(stream, out.device)))
+
+
+def _host_pinned(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor (pin_memory=True)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gb_encode_staged(codec, codes_dev, scales_dev, codes_host, scales_host, src, chunk_elems,
+                     scale_mode=GB_SCALE_ABSMAX_DIV_448, stream=None):
+    """Encode src chunk by chunk, copying each chunk's payload to pinned host
+    tensors while the next chunk is encoded."""
+    _device_tensor(src, torch.float32, "src")
+    dt = _CODE_DTYPE[int(codec)]
+    _device_tensor(codes_dev, dt, "codes_dev")
+    _host_pinned(codes_host, "codes_host")
+    n = src.numel()
+    _same_numel([codes_dev, codes_host], n, "codes")
+    if scales_dev is not None:
+        _device_tensor(scales_dev, torch.float32, "scales_dev")
+        _host_pinned(scales_host, "scales_host")
+        _same_numel([scales_dev, scales_host], (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    _check(_lib.gb_encode_staged(int(codec), int(scale_mode), _ptr(codes_dev), _ptr(scales_dev),
+                                 _ptr(codes_host), _ptr(scales_host), _ptr(src), n, int(chunk_elems),
+                                 _stream(stream, src.device)))
+
+
+def gb_decode_accumulate_staged(acc, codes_host, scales_host, codes_dev, scales_dev, codec, chunk_elems,
+                                accumulate=False, stream=None):
+    """Copy k host payloads to device staging chunk by chunk while the
+    previous chunk is decoded and accumulated into acc."""
+    _device_tensor(acc, torch.float32, "acc")
+    n = acc.numel()
+    dt = _CODE_DTYPE[int(codec)]
+    for i, (h, d) in enumerate(zip(codes_host, codes_dev)):
+        _host_pinned(h, f"codes_host[{i}]")
+        _device_tensor(d, dt, f"codes_dev[{i}]")
+    _same_numel(list(codes_host) + list(codes_dev), n, "codes")
+    if len(codes_host) != len(codes_dev):
+        raise ValueError("one device staging buffer per host payload is needed")
+    sh = sd = None
+    if scales_host is not None:
+        for i, (h, d) in enumerate(zip(scales_host, scales_dev)):
+            _host_pinned(h, f"scales_host[{i}]")
+            _device_tensor(d, torch.float32, f"scales_dev[{i}]")
+        _same_numel(list(scales_host) + list(scales_dev), (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+        sh, sd = _ptr_array(scales_host), _ptr_array(scales_dev)
+    _check(_lib.gb_decode_accumulate_staged(_ptr(acc), _ptr_array(codes_host), sh, _ptr_array(codes_dev), sd,
+                                            len(codes_host), n, int(chunk_elems), int(codec),
+                                            int(bool(accumulate)), _stream(stream, acc.device)))
 
 
 def gb_payload_bytes(codec, n):

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "gb_internal.h"
 
@@ -75,6 +76,64 @@ gb_status check_table(const void* const* table, int k, size_t align, const char*
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------------------
+// Per-device state of the staged (pipelined) calls: two copy streams, at the
+// default priority, so that consecutive chunks' copies go to two DMA queues
+// and the fixed cost of one copy overlaps the transfer of the other, and the
+// events that order them against the caller's stream.  Created on a device's
+// first staged call and kept until the process ends.  A staged call holds
+// the device's lock while it enqueues, so calls from several host threads
+// interleave whole, never chunk by chunk.
+// ---------------------------------------------------------------------------
+constexpr int kCopyStreams = 2;
+struct StagingContext {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t copy[kCopyStreams] = {};
+  hipEvent_t ev_copy[kCopyStreams] = {};  // copy stream -> compute stream
+  hipEvent_t ev_compute = nullptr;        // compute stream -> copy stream
+};
+constexpr int kMaxDevices = 64;
+StagingContext g_staging[kMaxDevices];
+
+gb_status staging_context(const char* fn, StagingContext** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GB_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GB_ERR_HIP, "%s: device %d out of range", fn, dev);
+  *out = &g_staging[dev];
+  return GB_OK;
+}
+
+// Creates the context's streams and events; call with c->mu held.
+gb_status staging_ready(const char* fn, StagingContext* c) {
+  if (c->ready) return GB_OK;
+  hipError_t e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming);
+  for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) {
+    e = hipStreamCreateWithFlags(&c->copy[i], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy[i], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) return fail(GB_ERR_HIP, "%s: creating the copy streams: %s", fn, hipGetErrorString(e));
+  c->ready = true;
+  return GB_OK;
+}
+
+// Host buffers of the staged calls must be pinned (page-locked and mapped
+// for the device), so the copies are asynchronous DMA.
+gb_status check_pinned(const void* p, size_t align, const char* fn, const char* name) {
+  gb_status s = check_array(p, align, fn, name);
+  if (s != GB_OK) return s;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) (void)hipGetLastError();  // an unknown host pointer leaves an error behind
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    return fail(GB_ERR_INVALID_ARG, "%s: %s = %p is not pinned host memory", fn, name, p);
+  }
+  return GB_OK;
+}
+
+size_t code_size(int codec) { return codec == GB_CODEC_BF16 ? 2 : (codec == GB_CODEC_FP8_E4M3_B256 ? 1 : 4); }
 
 }  // namespace
 
@@ -217,6 +276,131 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float
       return from_hip(gb::launch_decode_fp8(acc, c, sc, k, n, accumulate != 0, st), fn);
     }
   }
+}
+
+gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* scales_dev, void* codes_host,
+                           float* scales_host, const float* src, size_t n, size_t chunk_elems, void* stream) {
+  const char* fn = "gb_encode_staged";
+  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+  }
+  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (chunk_elems == 0 || chunk_elems % GB_BLOCK != 0) {
+    return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
+                GB_BLOCK);
+  }
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_array(codes_dev, GB_ALIGN, fn, "codes_dev")) != GB_OK) return s;
+  if ((s = check_pinned(codes_host, 4, fn, "codes_host")) != GB_OK) return s;
+  if (fp8) {
+    if ((s = check_array(scales_dev, 4, fn, "scales_dev")) != GB_OK) return s;
+    if ((s = check_pinned(scales_host, 4, fn, "scales_host")) != GB_OK) return s;
+  }
+  StagingContext* c;
+  if ((s = staging_context(fn, &c)) != GB_OK) return s;
+  std::lock_guard<std::mutex> lock(c->mu);
+  if ((s = staging_ready(fn, c)) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  const size_t cb = code_size(codec);
+  char* cd = static_cast<char*>(codes_dev);
+  char* ch = static_cast<char*>(codes_host);
+  hipError_t e = hipSuccess;
+  size_t chunk = 0;
+  for (size_t o = 0; o < n && e == hipSuccess; o += chunk_elems, chunk++) {
+    const size_t l = n - o < chunk_elems ? n - o : chunk_elems;
+    hipStream_t cs = c->copy[chunk % kCopyStreams];
+    e = fp8 ? gb::launch_encode_fp8(reinterpret_cast<uint8_t*>(cd + o), scales_dev + o / GB_BLOCK, src + o, l,
+                                    scale_mode, st)
+            : gb::launch_encode_bf16(reinterpret_cast<uint16_t*>(cd + 2 * o), src + o, l, st);
+    if (e == hipSuccess) e = hipEventRecord(c->ev_compute, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, c->ev_compute, 0);
+    if (e == hipSuccess) e = hipMemcpyAsync(ch + cb * o, cd + cb * o, cb * l, hipMemcpyDeviceToHost, cs);
+  }
+  // the scales (4 bytes per 256 values) go in one copy once all are written
+  if (e == hipSuccess && fp8) {
+    const size_t cs_last = (chunk - 1) % kCopyStreams;
+    e = hipMemcpyAsync(scales_host, scales_dev, 4 * ((n + GB_BLOCK - 1) / GB_BLOCK), hipMemcpyDeviceToHost,
+                       c->copy[cs_last]);
+  }
+  for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) {
+    e = hipEventRecord(c->ev_copy[i], c->copy[i]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[i], 0);
+  }
+  return from_hip(e, fn);
+}
+
+gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host, const float* const* scales_host,
+                                      void* const* codes_dev, float* const* scales_dev, int k, size_t n,
+                                      size_t chunk_elems, int codec, int accumulate, void* stream) {
+  const char* fn = "gb_decode_accumulate_staged";
+  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (accumulate != 0 && accumulate != 1) {
+    return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
+  }
+  if (chunk_elems == 0 || chunk_elems % GB_BLOCK != 0) {
+    return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
+                GB_BLOCK);
+  }
+  if (n == 0) return GB_OK;
+  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+  if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
+  if (codes_host == nullptr || codes_dev == nullptr || (fp8 && (scales_host == nullptr || scales_dev == nullptr))) {
+    return fail(GB_ERR_INVALID_ARG, "%s: a pointer array is NULL", fn);
+  }
+  for (int r = 0; r < k; r++) {
+    char name[32];
+    std::snprintf(name, sizeof name, "codes_host[%d]", r);
+    if ((s = check_pinned(codes_host[r], 4, fn, name)) != GB_OK) return s;
+    std::snprintf(name, sizeof name, "codes_dev[%d]", r);
+    if ((s = check_array(codes_dev[r], GB_ALIGN, fn, name)) != GB_OK) return s;
+    if (fp8) {
+      std::snprintf(name, sizeof name, "scales_host[%d]", r);
+      if ((s = check_pinned(scales_host[r], 4, fn, name)) != GB_OK) return s;
+      std::snprintf(name, sizeof name, "scales_dev[%d]", r);
+      if ((s = check_array(scales_dev[r], 4, fn, name)) != GB_OK) return s;
+    }
+  }
+  StagingContext* c;
+  if ((s = staging_context(fn, &c)) != GB_OK) return s;
+  std::lock_guard<std::mutex> lock(c->mu);
+  if ((s = staging_ready(fn, c)) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  const size_t cb = code_size(codec);
+  // copies into the device staging buffers start after the caller's earlier
+  // work on `stream`, which may still read them
+  hipError_t e = hipEventRecord(c->ev_compute, st);
+  for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) e = hipStreamWaitEvent(c->copy[i], c->ev_compute, 0);
+  // every rank's scales (4 bytes per 256 values) first, in one copy each on
+  // the first copy stream, ahead of chunk 0, which the compute stream waits for
+  for (int r = 0; r < k && e == hipSuccess && fp8; r++) {
+    e = hipMemcpyAsync(scales_dev[r], scales_host[r], 4 * ((n + GB_BLOCK - 1) / GB_BLOCK), hipMemcpyHostToDevice,
+                       c->copy[0]);
+  }
+  size_t chunk = 0;
+  for (size_t o = 0; o < n && e == hipSuccess; o += chunk_elems, chunk++) {
+    const size_t l = n - o < chunk_elems ? n - o : chunk_elems;
+    const int ci = (int)(chunk % kCopyStreams);
+    gb::PtrTable cp = {}, sp = {};
+    for (int r = 0; r < k && e == hipSuccess; r++) {
+      char* dst = static_cast<char*>(codes_dev[r]) + cb * o;
+      e = hipMemcpyAsync(dst, static_cast<const char*>(codes_host[r]) + cb * o, cb * l, hipMemcpyHostToDevice,
+                         c->copy[ci]);
+      cp.p[r] = dst;
+      if (fp8) sp.p[r] = scales_dev[r] + o / GB_BLOCK;
+    }
+    if (e == hipSuccess) e = hipEventRecord(c->ev_copy[ci], c->copy[ci]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[ci], 0);
+    if (e != hipSuccess) break;
+    if (codec == GB_CODEC_NONE) e = gb::launch_reduce_sum(acc + o, cp, k, l, accumulate != 0, st);
+    else if (codec == GB_CODEC_BF16) e = gb::launch_decode_bf16(acc + o, cp, k, l, accumulate != 0, st);
+    else e = gb::launch_decode_fp8(acc + o, cp, sp, k, l, accumulate != 0, st);
+  }
+  return from_hip(e, fn);
 }
 
 }  // extern "C"

@@ -252,6 +252,53 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs,
                                        int scale_mode, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/*
+ * Staged (pipelined) leader steps: the README's pipelined policy cuts the
+ * bridge step into chunks so that the copy of one chunk to pinned host memory
+ * overlaps the work on the next ("Collective policies": pipelined
+ * reduce-bridge-broadcast, and the pinned staging paragraph).  These two calls
+ * do the device side of it for one GPU:
+ *
+ * gb_encode_staged — encode src (fp32[n]) into the device payload
+ *   (codes_dev, scales_dev) chunk by chunk on `stream`, and copy each chunk's
+ *   codes to the pinned host payload (codes_host) on the library's copy
+ *   streams as soon as that chunk is encoded, so the copy of chunk c overlaps
+ *   the encode of chunk c+1; the scales (4 bytes per 256 values) follow in
+ *   one copy.  codec BF16 or FP8 (scale_mode
+ *   as gb_encode_fp8_e4m3_blockscaled; scales unused and may be NULL for
+ *   BF16).  The payload is exactly the one-shot encoder's.  When `stream`
+ *   reaches the end of the call's work, every copy has finished.
+ *
+ * gb_decode_accumulate_staged — the reverse: copy each of the k payloads
+ *   received in pinned host memory (codes_host[r], scales_host[r]) into the
+ *   device staging payloads (codes_dev[r], scales_dev[r]) chunk by chunk on
+ *   the copy streams (every rank's scales first, in one copy each), and
+ *   decode-and-accumulate each chunk on `stream` as soon as its copies are
+ *   done (the result is exactly gb_decode_accumulate's).
+ *   The copies start only after the work already queued on `stream`.
+ *
+ * chunk_elems: a positive multiple of 256 (the README's default chunk is
+ * 4 MiB, i.e. 1,048,576 fp32 values; a copy has a fixed cost of some
+ * microseconds, so chunks of a few MiB of payload or more pay off).  Host
+ * buffers must be pinned
+ * (hipHostMalloc, or torch's pin_memory): GB_ERR_INVALID_ARG otherwise.
+ * Device arrays are 16-byte aligned, scale arrays 4-byte; host code arrays
+ * 4-byte.  The library's two copy streams and their events are created on a
+ * device's
+ * first staged call and kept for the life of the process; calls on one
+ * device from several host threads are serialised while they enqueue.
+ */
+gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev,
+                           float* scales_dev, void* codes_host,
+                           float* scales_host, const float* src, size_t n,
+                           size_t chunk_elems, void* stream);
+gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
+                                      const float* const* scales_host,
+                                      void* const* codes_dev,
+                                      float* const* scales_dev, int k, size_t n,
+                                      size_t chunk_elems, int codec,
+                                      int accumulate, void* stream);
+
 /* Bytes one rank's n-value payload occupies on the bridge:
  * 4n (NONE), 2n (BF16), n + 4*ceil(n/256) (FP8).  0 for an unknown codec. */
 size_t gb_payload_bytes(int codec, size_t n);

@@ -136,6 +136,17 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
                                               ctypes.c_void_p(512), 1 << 20, None), 2, "residuals[0]"),
     (lambda L: L.gb_encode_bf16_ef(ctypes.c_void_p(256), ctypes.c_void_p(264), ctypes.c_void_p(256), 10, None),
      2, "residual"),
+    (lambda L: L.gb_encode_staged(0, 0, None, None, None, None, None, 10, 256, None), 3, "not bf16 or fp8"),
+    (lambda L: L.gb_encode_staged(2, 0, None, None, None, None, None, 10, 100, None), 1, "chunk_elems"),
+    (lambda L: L.gb_encode_staged(2, 9, None, None, None, None, None, 10, 256, None), 3, "scale mode"),
+    (lambda L: L.gb_encode_staged(2, 0, ctypes.c_void_p(264), None, None, None, ctypes.c_void_p(256), 10, 256,
+                                  None), 2, "codes_dev"),
+    (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 1, 10, 256, 1, 0, None),
+     1, "pointer array"),
+    (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 1, 10, 0, 1, 0, None),
+     1, "chunk_elems"),
+    (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 9, 10, 256, 1, 0, None),
+     1, "k = 9"),
 ])
 def test_validation_of_the_wider_calls(gb, call, status, msg):
     assert call(gb._lib) == status
