@@ -686,6 +686,17 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(float* out, Ptr
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 
+// Dynamic LDS reserved per workgroup by the kernels that keep the most bytes
+// in flight.  No kernel uses LDS: reserving 64 KiB of the 160 KiB a compute
+// unit has caps it at 2 such workgroups.  A fused fp8 pass over k >= 4 ranks
+// keeps 16k bytes of loads in flight per lane; measured on MI355X at 1e9
+// values per rank, 2 workgroups per compute unit move about 4% more bytes
+// per second than the 5 its registers allow (fewer concurrent streams of
+// requests at the memory), while 1 per unit is worse.  Kernels with fewer
+// bytes per lane lose heavily under any cap and get none.
+constexpr unsigned kHeavyLds = 64u << 10;
+__host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kHeavyLds : 0u; }
+
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 
 // Workgroups for one lane per `per_lane` values, or 0 if too many.
@@ -774,8 +785,8 @@ hipError_t launch_decode_fp8(float* acc, const PtrTable& codes, const PtrTable& 
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
 #define GB_CALL(K)                                                                                   \
-  if (accumulate) decode_fp8_kernel<K, true><<<grid, kThreads, 0, stream>>>(acc, codes, scales, n);   \
-  else decode_fp8_kernel<K, false><<<grid, kThreads, 0, stream>>>(acc, codes, scales, n);
+  if (accumulate) decode_fp8_kernel<K, true><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n); \
+  else decode_fp8_kernel<K, false><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
@@ -804,7 +815,7 @@ hipError_t launch_fused_fp8(float* out, const PtrTable& srcs, uint8_t* const* co
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-#define GB_CALL(K) fused_fp8_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, c, s, n, scale_mode);
+#define GB_CALL(K) fused_fp8_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, c, s, n, scale_mode);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
@@ -855,7 +866,7 @@ hipError_t launch_fused_fp8_ef(float* out, const PtrTable& srcs, float* const* r
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-#define GB_CALL(K) fused_fp8_ef_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, rs, c, s, n, scale_mode);
+#define GB_CALL(K) fused_fp8_ef_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, rs, c, s, n, scale_mode);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
