@@ -38,6 +38,11 @@
  *                         brute force against an exact order with the
  *                         IEEE 754-2019 zero and NaN rules; rank-permutation
  *                         invariance [test_oracle_ops.py].
+ *   or_reduce_typed       f16 / bf16 sums and averages against torch's CPU
+ *                         half and bfloat16 arithmetic and exact rational
+ *                         rounding; f64 against exact rationals; integer
+ *                         sums against numpy's wrapping arithmetic; MAX/MIN
+ *                         by brute force [test_oracle_dtypes.py].
  *   or_encode_*_ef        with a zero residual the payload is the plain
  *                         encode; the bf16 residual is exact and within half
  *                         an ulp; exact rational step-by-step simulation with
@@ -428,5 +433,171 @@ void or_reduce(float* out, const float* const* x, int k, size_t n, int op,
       acc = (op == OR_OP_MAX) ? max2019(acc, x[r][i]) : min2019(acc, x[r][i]);
     }
     out[i] = acc;
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Other element types.  README "API": tensors may be float16, bfloat16,
+ * float32, float64, int8, uint8, int32 or int64, and all_reduce takes SUM,
+ * AVG, MAX or MIN, with AVG only for floating-point types.  Readings taken:
+ *   floating-point SUM is a left fold over ranks, each addition rounded to
+ *   the element type (nearest, ties to even, IEEE overflow to Inf); AVG is
+ *   RN_type(sum / d); MAX / MIN are the IEEE 754-2019 maximum / minimum;
+ *   integer SUM wraps modulo 2^bits (two's complement); integer MAX / MIN are
+ *   the ordinary order.
+ * Each half-precision result is computed in binary64 and rounded once to the
+ * type: the exact sum or quotient of two half-precision values, rounded to
+ * binary64 (53 bits >= 2p + 2 with p = 11 or 8), rounds to the same value as
+ * the exact result would (Figueroa, "When is double rounding innocuous?").
+ * --------------------------------------------------------------------- */
+enum { OR_T_F32 = 0, OR_T_F16 = 1, OR_T_BF16 = 2, OR_T_F64 = 3,
+       OR_T_I8 = 4, OR_T_U8 = 5, OR_T_I32 = 6, OR_T_I64 = 7 };
+
+/* Value of an IEEE half (1-5-10) code. */
+static double f16_value(uint16_t c) {
+  int e = (c >> 10) & 31;
+  int f = c & 1023;
+  double sign = (c & 0x8000) ? -1.0 : 1.0;
+  if (e == 31) return f ? NAN : sign * INFINITY;
+  if (e == 0) return sign * ldexp((double)f, -24);
+  return sign * ldexp(1024.0 + f, e - 25);
+}
+
+/* Nearest value with p significant bits and least normal exponent emin
+ * (subnormals below), ties to the even significand, rounding as if the
+ * exponent were unbounded and giving Inf when that reaches 2^(emax+1).  v is
+ * finite. */
+static double round_format(double v, int p, int emin, int emax) {
+  if (v == 0.0) return v;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1) */
+  e = e - 1;             /* 2^e <= a < 2^(e+1) */
+  if (e < emin) e = emin;
+  double quantum = ldexp(1.0, e - (p - 1));
+  double m = a / quantum; /* exact: a power-of-two scaling */
+  double lo = floor(m);
+  double rem = m - lo;
+  double q = lo;
+  if (rem > 0.5 || (rem == 0.5 && fmod(lo, 2.0) == 1.0)) q = lo + 1.0;
+  double r = q * quantum;
+  if (r >= ldexp(1.0, emax + 1)) return copysign(INFINITY, v);  /* IEEE overflow */
+  return copysign(r, v);
+}
+
+static uint16_t f16_code(double v) {  /* v is an f16 value, NaN or +-Inf */
+  if (isnan(v)) return 0x7E00;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isinf(a)) return sign | 0x7C00;
+  if (a < ldexp(1.0, -14)) return sign | (uint16_t)(a / ldexp(1.0, -24));
+  int e;
+  double m = frexp(a, &e);  /* a = m * 2^e, m in [0.5, 1) */
+  return sign | (uint16_t)((e - 1 + 15) << 10) | (uint16_t)((m * 2.0 - 1.0) * 1024.0);
+}
+
+/* Value of element i of an array of the given type, as binary64 (exact for
+ * every type here except int64 beyond 2^53, which the integer path avoids). */
+static double value_at(const void* a, size_t i, int t) {
+  switch (t) {
+    case OR_T_F32: return ((const float*)a)[i];
+    case OR_T_F16: return f16_value(((const uint16_t*)a)[i]);
+    case OR_T_BF16: return or_bf16_decode_one(((const uint16_t*)a)[i]);
+    case OR_T_F64: return ((const double*)a)[i];
+    default: return 0.0;
+  }
+}
+
+static double round_to_type(double v, int t) {
+  if (isnan(v) || isinf(v)) return v;
+  switch (t) {
+    case OR_T_F32: return (double)(float)v;  /* one binary32 rounding */
+    case OR_T_F16: return round_format(v, 11, -14, 15);
+    case OR_T_BF16: return round_format(v, 8, -126, 127);
+    default: return v;
+  }
+}
+
+static void store_at(void* a, size_t i, int t, double v) {
+  switch (t) {
+    case OR_T_F32: ((float*)a)[i] = (float)v; break;
+    case OR_T_F16: ((uint16_t*)a)[i] = f16_code(v); break;
+    case OR_T_BF16: ((uint16_t*)a)[i] = or_bf16_encode_one((float)v); break;
+    case OR_T_F64: ((double*)a)[i] = v; break;
+    default: break;
+  }
+}
+
+static double max2019d(double a, double b) {
+  if (isnan(a) || isnan(b)) return NAN;
+  if (a > b) return a;
+  if (b > a) return b;
+  return signbit(a) ? b : a;
+}
+
+static double min2019d(double a, double b) {
+  if (isnan(a) || isnan(b)) return NAN;
+  if (a < b) return a;
+  if (b < a) return b;
+  return signbit(a) ? a : b;
+}
+
+static void reduce_float(void* out, const void* const* x, int k, size_t n, int t,
+                         int op, int divisor) {
+  for (size_t i = 0; i < n; i++) {
+    double acc = value_at(x[0], i, t);
+    for (int r = 1; r < k; r++) {
+      double v = value_at(x[r], i, t);
+      if (op == OR_OP_SUM || op == OR_OP_AVG) {
+        acc = round_to_type(acc + v, t);  /* binary64 add (or binary32 for f32 below) */
+      } else if (op == OR_OP_MAX) {
+        acc = max2019d(acc, v);
+      } else {
+        acc = min2019d(acc, v);
+      }
+    }
+    if (op == OR_OP_AVG) acc = round_to_type(acc / (double)divisor, t);
+    store_at(out, i, t, acc);
+  }
+}
+
+static void reduce_int(void* out, const void* const* x, int k, size_t n, int t,
+                       int op) {
+  for (size_t i = 0; i < n; i++) {
+    int64_t v[64] = {0};
+    for (int r = 0; r < k; r++) {
+      switch (t) {
+        case OR_T_I8: v[r] = ((const int8_t*)x[r])[i]; break;
+        case OR_T_U8: v[r] = ((const uint8_t*)x[r])[i]; break;
+        case OR_T_I32: v[r] = ((const int32_t*)x[r])[i]; break;
+        default: v[r] = ((const int64_t*)x[r])[i]; break;
+      }
+    }
+    uint64_t sum = (uint64_t)v[0];  /* unsigned: wraps modulo 2^64 */
+    int64_t best = v[0];
+    for (int r = 1; r < k; r++) {
+      sum += (uint64_t)v[r];
+      if (op == OR_OP_MAX && v[r] > best) best = v[r];
+      if (op == OR_OP_MIN && v[r] < best) best = v[r];
+    }
+    uint64_t res = (op == OR_OP_SUM) ? sum : (uint64_t)best;
+    switch (t) {  /* keep the low bits: wraps modulo 2^bits */
+      case OR_T_I8: ((uint8_t*)out)[i] = (uint8_t)res; break;
+      case OR_T_U8: ((uint8_t*)out)[i] = (uint8_t)res; break;
+      case OR_T_I32: ((uint32_t*)out)[i] = (uint32_t)res; break;
+      default: ((uint64_t*)out)[i] = res; break;
+    }
+  }
+}
+
+void or_reduce_typed(void* out, const void* const* x, int k, size_t n, int dtype,
+                     int op, int divisor) {
+  if (dtype == OR_T_F32) {
+    /* binary32 adds, exactly as or_reduce */
+    or_reduce((float*)out, (const float* const*)x, k, n, op, divisor);
+  } else if (dtype == OR_T_F16 || dtype == OR_T_BF16 || dtype == OR_T_F64) {
+    reduce_float(out, x, k, n, dtype, op, divisor);
+  } else {
+    reduce_int(out, x, k, n, dtype, op);
   }
 }

@@ -79,6 +79,14 @@ void or_bucket_allreduce(float* out, void* const* codes, float* const* scales,
 void or_reduce(float* out, const float* const* x, int k, size_t n, int op,
                int divisor);
 
+/* Element types of or_reduce_typed. */
+enum { OR_DTYPE_F32 = 0, OR_DTYPE_F16 = 1, OR_DTYPE_BF16 = 2, OR_DTYPE_F64 = 3,
+       OR_DTYPE_I8 = 4, OR_DTYPE_U8 = 5, OR_DTYPE_I32 = 6, OR_DTYPE_I64 = 7 };
+/* SUM / AVG / MAX / MIN over k arrays of one element type (AVG: floating
+ * types only). */
+void or_reduce_typed(void* out, const void* const* x, int k, size_t n, int dtype,
+                     int op, int divisor);
+
 /* Error feedback: y = x + residual is encoded, and residual becomes
  * y - decode(payload).  residual is read and written (caller-owned). */
 void or_encode_bf16_ef(uint16_t* codes, float* residual, const float* x, size_t n);

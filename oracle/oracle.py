@@ -18,6 +18,9 @@ from . import build as _build
 
 CODEC_NONE, CODEC_BF16, CODEC_FP8 = 0, 1, 2
 OP_SUM, OP_AVG, OP_MAX, OP_MIN = 0, 1, 2, 3
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3, "i8": 4, "u8": 5, "i32": 6, "i64": 7}
+NP_DTYPES = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64,
+             "i8": np.int8, "u8": np.uint8, "i32": np.int32, "i64": np.int64}
 SCALE_ABSMAX_DIV_448, SCALE_POW2 = 0, 1
 BLOCK = 256
 
@@ -50,6 +53,7 @@ def _load():
         "or_decode_accumulate": (None, [_P, _P, _P, _I, _S, _I, _I]),
         "or_bucket_allreduce": (None, [_P, _P, _P, _P, _I, _S, _S, _I, _I]),
         "or_reduce": (None, [_P, _P, _I, _S, _I, _I]),
+        "or_reduce_typed": (None, [_P, _P, _I, _S, _I, _I, _I]),
         "or_encode_bf16_ef": (None, [_P, _P, _P, _S]),
         "or_encode_fp8_ef": (None, [_P, _P, _P, _P, _S, _I]),
         "or_bucket_allreduce_ef": (None, [_P, _P, _P, _P, _P, _I, _S, _S, _I, _I]),
@@ -97,6 +101,17 @@ def reduce(xs, op, divisor=1):
     n = xs[0].size
     out = np.empty(n, dtype=np.float32)
     _load().or_reduce(_ptr(out), _ptr_array(xs), len(xs), n, int(op), int(divisor))
+    return out
+
+
+def reduce_typed(xs, dtype, op, divisor=1):
+    """Reduce k arrays of element type `dtype` ("f32", "f16", "bf16", "f64",
+    "i8", "u8", "i32", "i64"); f16 and bf16 arrays hold raw 16-bit codes."""
+    nt = NP_DTYPES[dtype]
+    xs = [np.ascontiguousarray(x, dtype=nt) for x in xs]
+    n = xs[0].size
+    out = np.empty(n, dtype=nt)
+    _load().or_reduce_typed(_ptr(out), _ptr_array(xs), len(xs), n, DTYPES[dtype], int(op), int(divisor))
     return out
 
 
