@@ -23,7 +23,9 @@ Workloads (inputs from workloads.py):
                    gb_decode_accumulate(fp8).
   gradients_64mib  k=4 x 2^24 fp32; 4 x gb_encode_bf16 + gb_decode_accumulate(bf16).
   two_island_sweep k=2, 19 sizes 2^8..2^26 fp32; gb_reduce_sum into a
-                   separate output at every size.
+                   separate output at every size.  --op avg|max|min uses
+                   gb_reduce; --dtype f16|bf16|f64|i8|u8|i32|i64 runs the
+                   sweep in that element type through gb_reduce_typed.
   two_rank_4mib    k=2 x 2^20 fp32; gb_reduce_sum, gb_encode_bf16 of the sum,
                    gb_decode_accumulate(bf16, k=1).
   staged_fp8_256mib the leader's staged (pipelined) bridge step on one GPU:
@@ -67,6 +69,8 @@ def parse():
     p.add_argument("--op", default="sum", choices=["sum", "avg", "max", "min"],
                    help="reduction of the two_island_sweep workload (avg divides by the "
                         "world size, 2 here)")
+    p.add_argument("--dtype", default="f32", choices=["f32", "f16", "bf16", "f64", "i8", "u8", "i32", "i64"],
+                   help="element type of the two_island_sweep workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="rough budget of oracle CPU time for the baseline sample")
@@ -476,6 +480,7 @@ class Gradients64(Workload):
 class Sweep(Workload):
     name = "two_island_sweep"
     OPS = {"sum": 0, "avg": 1, "max": 2, "min": 3}
+    ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8, "i8": 1, "u8": 1, "i32": 4, "i64": 8}
 
     def __init__(self, gb, torch, args):
         super().__init__(gb, torch, args)
@@ -483,18 +488,37 @@ class Sweep(Workload):
         self.W = W
         self.sizes = W.SWEEP_SIZES
         self.op = self.OPS[args.op]
+        self.dt = args.dtype
+        self.esize = self.ESIZE[self.dt]
+        if self.dt in ("i8", "u8", "i32", "i64") and self.op == 1:
+            raise SystemExit("AVG is defined for floating-point element types only")
+        dist = "N(0,1)" if self.dt in ("f32", "f16", "bf16", "f64") else "uniform over the type"
         self.config = {"workload": self.name, "k": 2, "sizes": f"2^8..2^26 values ({len(self.sizes)} sizes)",
-                       "distribution": "N(0,1)", "op": args.op,
+                       "distribution": dist, "op": args.op, "element_type": self.dt,
                        "path": f"{args.op} of the two island results into a separate output"}
 
     def setup(self):
         torch = self.torch
-        self.xh = {n: self.W.normal_ranks(2, n) for n in self.sizes}
-        self.x = {n: [torch.from_numpy(a).to(self.dev) for a in xs] for n, xs in self.xh.items()}
-        self.out = {n: torch.empty(n, dtype=torch.float32, device=self.dev) for n in self.sizes}
+        if self.dt == "f32":
+            self.xh = {n: self.W.normal_ranks(2, n) for n in self.sizes}
+            self.x = {n: [torch.from_numpy(a).to(self.dev) for a in xs] for n, xs in self.xh.items()}
+            self.out = {n: torch.empty(n, dtype=torch.float32, device=self.dev) for n in self.sizes}
+            return
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64, "i8": torch.int8,
+               "u8": torch.uint8, "i32": torch.int32, "i64": torch.int64}[self.dt]
+        self.xh = {n: self.W.typed_ranks(2, n, self.dt) for n in self.sizes}
+
+        def dev(a):
+            if a.dtype == __import__("numpy").uint16:  # 16-bit float codes
+                return torch.from_numpy(a.view("int16")).to(self.dev).view(tdt)
+            return torch.from_numpy(a).to(self.dev)
+        self.x = {n: [dev(a) for a in xs] for n, xs in self.xh.items()}
+        self.out = {n: torch.empty(n, dtype=tdt, device=self.dev) for n in self.sizes}
 
     def reduce(self, n):
-        if self.op == 0:
+        if self.dt != "f32":
+            self.gb.gb_reduce_typed(self.out[n], self.x[n], self.op, 2)
+        elif self.op == 0:
             self.gb.gb_reduce_sum(self.out[n], self.x[n])
         else:
             self.gb.gb_reduce(self.out[n], self.x[n], self.op, 2)
@@ -504,12 +528,17 @@ class Sweep(Workload):
             self.reduce(n)
 
     def step_bytes(self):
-        return sum(12 * n for n in self.sizes)
+        return sum(3 * self.esize * n for n in self.sizes)
 
     def timed_kernel(self):
         n = self.sizes[-1]
-        name = "reduce_sum_kernel<2,false>" if self.op == 0 else f"reduce_op_kernel<2,{self.op}>"
-        return (name, 12 * n, 1, lambda: self.reduce(n))
+        if self.dt != "f32":
+            name = f"reduce_typed_kernel<{self.gb.GB_DTYPE_OF[self.dt]},{self.op}>"
+        elif self.op == 0:
+            name = "reduce_sum_kernel<2,false>"
+        else:
+            name = f"reduce_op_kernel<2,{self.op}>"
+        return (name, 3 * self.esize * n, 1, lambda: self.reduce(n))
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -518,11 +547,27 @@ class Sweep(Workload):
         t, ok = 0.0, True
         for n in self.sizes:
             t0 = time.perf_counter()
-            want = O.reduce(self.xh[n], self.op, 2)
+            if self.dt == "f32":
+                want = O.reduce(self.xh[n], self.op, 2)
+            else:
+                want = O.reduce_typed(self.xh[n], self.dt, self.op, 2)
             t += time.perf_counter() - t0
-            got = self.out[n].cpu().numpy()
-            ok &= bool((np.isnan(got) == np.isnan(want)).all())
-            ok &= bool((got.view(np.uint32)[~np.isnan(got)] == want.view(np.uint32)[~np.isnan(want)]).all())
+            out = self.out[n]
+            if self.dt in ("f16", "bf16"):
+                got = out.view(self.torch.int16).cpu().numpy().view(np.uint16)
+                vals = out.float().cpu().numpy()
+                nan_g = np.isnan(vals)
+                wt = self.torch.from_numpy(want.view(np.int16)).view(out.dtype).float().numpy()
+                nan_w = np.isnan(wt)
+            else:
+                got = out.cpu().numpy()
+                nan_g = np.isnan(got) if got.dtype.kind == "f" else np.zeros(got.size, bool)
+                nan_w = np.isnan(want) if want.dtype.kind == "f" else np.zeros(want.size, bool)
+            ok &= bool((nan_g == nan_w).all())
+            if got.dtype.kind == "f":
+                got, want = got.view(np.uint32 if got.itemsize == 4 else np.uint64), \
+                    want.view(np.uint32 if want.itemsize == 4 else np.uint64)
+            ok &= bool((got[~nan_g] == want[~nan_w]).all())
         return self.step_bytes(), t, "the whole sweep", ok
 
 
@@ -681,7 +726,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": getattr(wl, "dt", "f32"),
         "data": "synthetic",
         "config": dict(wl.config, **extra),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -25,7 +25,7 @@ __all__ = [
     "gb_bucket_workspace_bytes", "gb_status_string", "gb_last_error", "gb_version",
     "gb_encode_bf16_ef", "gb_encode_fp8_e4m3_blockscaled_ef", "gb_bucket_allreduce_local_ef",
     "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
-    "gb_encode_staged", "gb_decode_accumulate_staged",
+    "gb_encode_staged", "gb_decode_accumulate_staged", "gb_reduce_typed", "GB_DTYPE", "GB_DTYPE_OF",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -35,6 +35,11 @@ GB_SCALE_ABSMAX_DIV_448, GB_SCALE_POW2 = 0, 1
 GB_OP_SUM, GB_OP_AVG, GB_OP_MAX, GB_OP_MIN = 0, 1, 2, 3
 GB_BLOCK = 256
 GB_MAX_K = 8
+# gb_dtype of each torch element type gb_reduce_typed takes
+GB_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3,
+            torch.int8: 4, torch.uint8: 5, torch.int32: 6, torch.int64: 7}
+# the same numbers by short name
+GB_DTYPE_OF = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3, "i8": 4, "u8": 5, "i32": 6, "i64": 7}
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgbreduce.so")
 if not os.path.exists(library_path):
@@ -50,6 +55,7 @@ _SP = ctypes.POINTER(ctypes.c_size_t)
 _SIGNATURES = {
     "gb_reduce_sum": (_I, [_P, _PP, _I, _S, _P]),
     "gb_reduce": (_I, [_P, _PP, _I, _S, _I, _I, _P]),
+    "gb_reduce_typed": (_I, [_P, _PP, _I, _S, _I, _I, _I, _P]),
     "gb_encode_bf16": (_I, [_P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
@@ -141,6 +147,18 @@ def gb_reduce(dst, srcs, op, divisor=1, stream=None):
     _same_numel(srcs, dst.numel(), "srcs")
     _check(_lib.gb_reduce(_ptr(dst), _ptr_array(srcs), len(srcs), dst.numel(), int(op), int(divisor),
                           _stream(stream, dst.device)))
+
+
+def gb_reduce_typed(dst, srcs, op, divisor=1, stream=None):
+    """gb_reduce over dst's element type (any key of GB_DTYPE); srcs share it."""
+    if not isinstance(dst, torch.Tensor) or dst.dtype not in GB_DTYPE:
+        raise TypeError(f"dst must be a tensor of one of {list(GB_DTYPE)}")
+    _device_tensor(dst, dst.dtype, "dst")
+    for i, s in enumerate(srcs):
+        _device_tensor(s, dst.dtype, f"srcs[{i}]")
+    _same_numel(srcs, dst.numel(), "srcs")
+    _check(_lib.gb_reduce_typed(_ptr(dst), _ptr_array(srcs), len(srcs), dst.numel(), GB_DTYPE[dst.dtype],
+                                int(op), int(divisor), _stream(stream, dst.device)))
 
 
 def gb_encode_bf16(codes, src, stream=None):

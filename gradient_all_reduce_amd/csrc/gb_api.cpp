@@ -228,6 +228,32 @@ gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n, int o
   return from_hip(gb::launch_reduce_op(dst, t, k, n, op, divisor, as_stream(stream)), fn);
 }
 
+gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, int dtype, int op, int divisor,
+                          void* stream) {
+  const char* fn = "gb_reduce_typed";
+  if (dtype < GB_DTYPE_F32 || dtype > GB_DTYPE_I64) return fail(GB_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (op != GB_OP_SUM && op != GB_OP_AVG && op != GB_OP_MAX && op != GB_OP_MIN) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: unknown op %d", fn, op);
+  }
+  if (op == GB_OP_AVG && dtype >= GB_DTYPE_I8) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: AVG needs a floating-point dtype", fn);
+  }
+  if (op == GB_OP_AVG && (divisor < 1 || divisor > (1 << 24))) {
+    return fail(GB_ERR_INVALID_ARG, "%s: AVG divisor %d is outside 1..2^24", fn, divisor);
+  }
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (n == 0) return GB_OK;
+  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+  gb::PtrTable t = {};
+  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  if (dtype == GB_DTYPE_F32) {
+    return from_hip(gb::launch_reduce_op(static_cast<float*>(dst), t, k, n, op, divisor, st), fn);
+  }
+  return from_hip(gb::launch_reduce_typed(dst, t, k, n, dtype, op, divisor, st), fn);
+}
+
 gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stream) {
   const char* fn = "gb_encode_bf16";
   if (n == 0) return GB_OK;

@@ -30,6 +30,9 @@ hipError_t launch_reduce_sum(float* dst, const PtrTable& srcs, int k, size_t n,
 // op = GB_OP_SUM, GB_OP_AVG (sum / divisor), GB_OP_MAX or GB_OP_MIN.
 hipError_t launch_reduce_op(float* dst, const PtrTable& srcs, int k, size_t n, int op, int divisor,
                             hipStream_t stream);
+// Any element type but fp32 (GB_DTYPE_*); integer types with SUM, MAX, MIN.
+hipError_t launch_reduce_typed(void* dst, const PtrTable& srcs, int k, size_t n, int dtype, int op, int divisor,
+                               hipStream_t stream);
 hipError_t launch_encode_bf16(uint16_t* codes, const float* src, size_t n,
                               hipStream_t stream);
 hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const float* src,

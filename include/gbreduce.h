@@ -96,6 +96,19 @@ typedef enum gb_op {
   GB_OP_MIN = 3  /* IEEE 754-2019 minimum: NaN if any value is NaN; -0 < +0 */
 } gb_op;
 
+/* Element types of gb_reduce_typed (README "API": the dtypes every backend
+ * supports).  The bridge codecs apply to float32 only. */
+typedef enum gb_dtype {
+  GB_DTYPE_F32 = 0,
+  GB_DTYPE_F16 = 1,  /* IEEE binary16 */
+  GB_DTYPE_BF16 = 2, /* bfloat16: top half of binary32 */
+  GB_DTYPE_F64 = 3,
+  GB_DTYPE_I8 = 4,
+  GB_DTYPE_U8 = 5,
+  GB_DTYPE_I32 = 6,
+  GB_DTYPE_I64 = 7
+} gb_dtype;
+
 /*
  * gb_reduce_sum — the leader's sum of island sums (README "How it works":
  * leaders all-reduce the island sums, each leader then holds the total).
@@ -127,6 +140,22 @@ gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n,
  */
 gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n,
                     int op, int divisor, void* stream);
+
+/*
+ * gb_reduce_typed — gb_reduce over any of the README's element types, on
+ * arrays of n elements of `dtype` (void pointers, 16-byte aligned):
+ *   SUM  floating types: left fold over ranks, every add rounded to the type
+ *        (nearest, ties to even, IEEE overflow to Inf); integer types: wraps
+ *        modulo 2^bits;
+ *   AVG  floating types only (GB_ERR_UNSUPPORTED for integers):
+ *        RN_type(sum / divisor), divisor 1 .. 2^24;
+ *   MAX, MIN  IEEE 754-2019 for floating types, the ordinary order for
+ *        integers (uint8 unsigned).
+ * GB_DTYPE_F32 is exactly gb_reduce.  Arguments, aliasing and errors as
+ * gb_reduce; GB_ERR_UNSUPPORTED for an unknown dtype.
+ */
+gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n,
+                          int dtype, int op, int divisor, void* stream);
 
 /*
  * gb_encode_bf16 — bf16 bridge compression of one fp32 payload

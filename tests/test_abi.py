@@ -57,6 +57,14 @@ def test_constants_match_header(gb):
                  "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN"]:
         v = int(re.search(rf"\b{name} = (\d+)", text).group(1))
         assert getattr(gb, name) == v, name
+    # element types: the header's gb_dtype, the binding's map and the oracle's numbering agree
+    from oracle import oracle as O
+    import torch
+    names = {"F32": torch.float32, "F16": torch.float16, "BF16": torch.bfloat16, "F64": torch.float64,
+             "I8": torch.int8, "U8": torch.uint8, "I32": torch.int32, "I64": torch.int64}
+    for name, dt in names.items():
+        v = int(re.search(rf"\bGB_DTYPE_{name} = (\d+)", text).group(1))
+        assert gb.GB_DTYPE[dt] == v == O.DTYPES[name.lower()], name
 
 
 def test_status_strings(gb):
@@ -130,6 +138,14 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
     (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 1, 10, 1, 0, None), 1, "divisor"),
     (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 1, 10, 1, (1 << 24) + 1, None), 1, "divisor"),
     (lambda L: L.gb_reduce(ctypes.c_void_p(256), _arr(256), 0, 10, 2, 1, None), 1, "k = 0"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 1, 10, 8, 0, 1, None), 3, "unknown dtype"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 1, 10, -1, 0, 1, None), 3, "unknown dtype"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 1, 10, 6, 1, 2, None), 3, "floating-point"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 1, 10, 1, 4, 1, None), 3, "unknown op"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 1, 10, 2, 1, 0, None), 1, "divisor"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(264), _arr(256), 1, 10, 4, 0, 1, None), 2, "dst"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256, 257), 2, 10, 5, 2, 1, None), 2, "srcs[1]"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 9, 10, 3, 0, 1, None), 1, "k = 9"),
     (lambda L: L.gb_bucket_allreduce_local_ef(ctypes.c_void_p(256), _arr(256), _arr(512), 1, 1000, 256, 0, 0,
                                               None, 0, None), 3, "lossy codec"),
     (lambda L: L.gb_bucket_allreduce_local_ef(ctypes.c_void_p(256), _arr(256), _arr(520), 1, 1000, 256, 2, 0,
@@ -156,6 +172,7 @@ def test_validation_of_the_wider_calls(gb, call, status, msg):
 def test_zero_length_returns_ok_without_pointers(gb):
     L = gb._lib
     assert L.gb_reduce_sum(None, None, 2, 0, None) == 0
+    assert L.gb_reduce_typed(None, None, 2, 0, 7, 2, 1, None) == 0
     assert L.gb_encode_bf16(None, None, 0, None) == 0
     assert L.gb_encode_fp8_e4m3_blockscaled(None, None, None, 0, 0, None) == 0
     assert L.gb_decode_accumulate(None, None, None, 3, 0, 2, 0, None) == 0

@@ -83,3 +83,17 @@ def test_compressed_avg_is_decode_then_divide(gb, codec):
     torch.cuda.synchronize()
     summed = O.decode_accumulate(codes, scales, codec)
     same(acc.cpu().numpy(), O.reduce([summed], O.OP_AVG, world), "compressed avg")
+
+
+@pytest.mark.parametrize("divisor", [2, 1024, 1 << 24, 3, (1 << 24) - 1])
+def test_avg_over_every_binade(gb, divisor):
+    """AVG of one rank over random bit patterns spanning every binade,
+    subnormals included: a power-of-two divisor (taken as a multiply by its
+    exact reciprocal) and any other divisor both give the once-rounded
+    quotient, also where it underflows."""
+    rng = np.random.default_rng(1100 + divisor % 1000)
+    x = rng.integers(0, 1 << 32, 300007, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    out = torch.empty(x.size, device=DEV)
+    gb.gb_reduce(out, [dev(x)], gb.GB_OP_AVG, divisor)
+    torch.cuda.synchronize()
+    same(out.cpu().numpy(), O.reduce([x], O.OP_AVG, divisor), f"avg d={divisor}")

@@ -2,12 +2,15 @@
 
 This module draws random numbers and nothing else: it holds none of the
 arithmetic under test, and it is the only code the GPU path's callers and the
-oracle's callers share.  Every input is float32.
+oracle's callers share.  Every input is float32 unless typed_ranks draws it
+in another element type.
 
 Workloads (all seeds start at BASE_SEED; rank r uses BASE_SEED + r):
   two_rank_4mib      k=2, n=1,048,576, N(0,1).
   two_island_sweep   k=2, n=2^8 .. 2^26 (1 KiB .. 256 MiB per rank), N(0,1),
-                     the same per-rank seeds at every size.
+                     the same per-rank seeds at every size.  With another element
+                     type: the same N(0,1) draws carried into that type
+                     (typed_ranks).
   gradients_64mib    k=4, n=16,777,216, N(0, sigma=1e-3), then floor(n/100)
                      distinct positions drawn without replacement scaled by
                      100 (outliers).
@@ -69,6 +72,28 @@ def device_gradients(n, seed, device):
     x = torch.randn(n, generator=g, device=device, dtype=torch.float32)
     x.mul_(float(SIGMA))
     return x
+
+
+def typed(n, dtype, seed):
+    """n values of element type `dtype` ("f16", "bf16", "f64", "i8", "u8",
+    "i32", "i64") from the given seed.  Floating types carry the N(0,1) draw:
+    float16 by numpy's conversion, bfloat16 as the top 16 bits of the float32
+    draw (uint16 codes, truncated: a draw, not a rounding under test), float64
+    by widening.  Integer types are uniform over the type's whole range."""
+    if dtype in ("f16", "bf16", "f64"):
+        x = normal(n, seed)
+        if dtype == "f16":
+            return x.astype(np.float16).view(np.uint16)
+        if dtype == "bf16":
+            return (x.view(np.uint32) >> 16).astype(np.uint16)
+        return x.astype(np.float64)
+    t = {"i8": np.int8, "u8": np.uint8, "i32": np.int32, "i64": np.int64}[dtype]
+    info = np.iinfo(t)
+    return np.random.default_rng(seed).integers(info.min, info.max, n, endpoint=True, dtype=t)
+
+
+def typed_ranks(k, n, dtype, base_seed=BASE_SEED):
+    return [typed(n, dtype, base_seed + r) for r in range(k)]
 
 
 def special_values():
