@@ -43,6 +43,12 @@
  *                         rounding; f64 against exact rationals; integer
  *                         sums against numpy's wrapping arithmetic; MAX/MIN
  *                         by brute force [test_oracle_dtypes.py].
+ *   or_encode_typed,      bfloat16 input through the bf16 codec is the
+ *   or_decode_sum_typed,  identity; every other input equals the binary32
+ *   or_bucket_allreduce_  path fed by torch's / numpy's own conversions, and
+ *   typed                 the typed total equals torch's rounding of the
+ *                         binary32 total; no codec is the typed SUM
+ *                         [test_oracle_typed_codec.py].
  *   or_encode_*_ef        with a zero residual the payload is the plain
  *                         encode; the bf16 residual is exact and within half
  *                         an ulp; exact rational step-by-step simulation with
@@ -57,6 +63,7 @@
 #include "gb_oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* No contraction into fused multiply-add: the build passes -ffp-contract=off. */
@@ -600,4 +607,71 @@ void or_reduce_typed(void* out, const void* const* x, int k, size_t n, int dtype
   } else {
     reduce_int(out, x, k, n, dtype, op);
   }
+}
+
+/* ------------------------------------------------------------------------
+ * Bridge compression of float16, bfloat16 and float64 tensors.  README
+ * "Bridge compression": the bridged policies compress floating-point SUM and
+ * AVG; leaders quantize their island's sum, and the payloads are dequantized
+ * and added in float32.  Readings taken: an island sum of another floating
+ * type is first taken to binary32 (exact from float16 and bfloat16; one
+ * rounding to nearest-even from float64) and then encoded exactly as a
+ * binary32 array; the float32 total is rounded once to the tensor's type
+ * (nearest, ties to even, IEEE overflow to Inf).  Without a codec the stream
+ * is the exact SUM of that type (or_reduce_typed).
+ * --------------------------------------------------------------------- */
+static float typed_to_f32(const void* a, size_t i, int t) {
+  switch (t) {
+    case OR_T_F32: return ((const float*)a)[i];
+    case OR_T_F16: return (float)f16_value(((const uint16_t*)a)[i]);  /* exact */
+    case OR_T_BF16: return or_bf16_decode_one(((const uint16_t*)a)[i]);
+    default: return (float)((const double*)a)[i];  /* one binary32 rounding */
+  }
+}
+
+static void f32_to_typed(void* a, size_t i, int t, float v) {
+  switch (t) {
+    case OR_T_F32: ((float*)a)[i] = v; break;
+    case OR_T_F16: ((uint16_t*)a)[i] = f16_code(round_to_type((double)v, OR_T_F16)); break;
+    case OR_T_BF16: ((uint16_t*)a)[i] = or_bf16_encode_one(v); break;
+    default: ((double*)a)[i] = (double)v; break;  /* exact */
+  }
+}
+
+static float* typed_array_to_f32(const void* x, size_t n, int t) {
+  float* f = (float*)malloc((n ? n : 1) * sizeof(float));
+  for (size_t i = 0; i < n; i++) f[i] = typed_to_f32(x, i, t);
+  return f;
+}
+
+void or_encode_typed(int codec, int dtype, void* codes, float* scales, const void* x,
+                     size_t n, int mode) {
+  float* f = typed_array_to_f32(x, n, dtype);
+  if (codec == OR_CODEC_BF16) or_encode_bf16((uint16_t*)codes, f, n);
+  else or_encode_fp8((uint8_t*)codes, scales, f, n, mode);
+  free(f);
+}
+
+void or_decode_sum_typed(void* out, int dtype, const void* const* codes,
+                         const float* const* scales, int k, size_t n, int codec) {
+  float* f = (float*)malloc((n ? n : 1) * sizeof(float));
+  or_decode_accumulate(f, codes, scales, k, n, codec, 0);
+  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, f[i]);
+  free(f);
+}
+
+void or_bucket_allreduce_typed(void* out, void* const* codes, float* const* scales,
+                               const void* const* x, int k, size_t n, size_t bucket_elems,
+                               int codec, int mode, int dtype) {
+  if (codec == OR_CODEC_NONE) {
+    or_reduce_typed(out, x, k, n, dtype, OR_OP_SUM, 1);
+    return;
+  }
+  float* f[64];
+  for (int r = 0; r < k; r++) f[r] = typed_array_to_f32(x[r], n, dtype);
+  float* sum = (float*)malloc((n ? n : 1) * sizeof(float));
+  or_bucket_allreduce(sum, codes, scales, (const float* const*)f, k, n, bucket_elems, codec, mode);
+  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, sum[i]);
+  free(sum);
+  for (int r = 0; r < k; r++) free(f[r]);
 }

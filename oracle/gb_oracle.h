@@ -99,6 +99,17 @@ void or_bucket_allreduce_ef(float* out, void* const* codes,
                             const float* const* x, int k, size_t n,
                             size_t bucket_elems, int codec, int mode);
 
+/* Bridge codecs over float16 / bfloat16 / float64 arrays (f16 and bf16 as raw
+ * 16-bit codes): the values go to binary32 first, then through the binary32
+ * encoders; the decoded binary32 total is rounded once to the type. */
+void or_encode_typed(int codec, int dtype, void* codes, float* scales, const void* x,
+                     size_t n, int mode);
+void or_decode_sum_typed(void* out, int dtype, const void* const* codes,
+                         const float* const* scales, int k, size_t n, int codec);
+void or_bucket_allreduce_typed(void* out, void* const* codes, float* const* scales,
+                               const void* const* x, int k, size_t n, size_t bucket_elems,
+                               int codec, int mode, int dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,9 @@ def _load():
         "or_encode_bf16_ef": (None, [_P, _P, _P, _S]),
         "or_encode_fp8_ef": (None, [_P, _P, _P, _P, _S, _I]),
         "or_bucket_allreduce_ef": (None, [_P, _P, _P, _P, _P, _I, _S, _S, _I, _I]),
+        "or_encode_typed": (None, [_I, _I, _P, _P, _P, _S, _I]),
+        "or_decode_sum_typed": (None, [_P, _I, _P, _P, _I, _S, _I]),
+        "or_bucket_allreduce_typed": (None, [_P, _P, _P, _P, _I, _S, _S, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -252,3 +255,51 @@ def bucket_allreduce_ef(xs, residuals, bucket_elems, codec, mode=SCALE_ABSMAX_DI
         _ptr(out), _ptr_array(codes), _ptr_array(scales) if scales else None, _ptr_array(res),
         _ptr_array(xs), k, n, int(bucket_elems), int(codec), int(mode))
     return out, codes, scales, res
+
+
+def _typed(x, dtype):
+    return np.ascontiguousarray(x, dtype=NP_DTYPES[dtype])
+
+
+def encode_typed(x, dtype, codec, mode=SCALE_ABSMAX_DIV_448):
+    """Bridge encode of a float16 / bfloat16 / float64 (or float32) array:
+    returns (codes, scales or None)."""
+    x = _typed(x, dtype)
+    n = x.size
+    if codec == CODEC_BF16:
+        codes, scales = np.empty(n, dtype=np.uint16), None
+    else:
+        codes, scales = np.empty(n, dtype=np.uint8), np.empty(nblocks(n), dtype=np.float32)
+    _load().or_encode_typed(int(codec), DTYPES[dtype], _ptr(codes),
+                            _ptr(scales) if scales is not None else None, _ptr(x), n, int(mode))
+    return codes, scales
+
+
+def decode_sum_typed(codes, scales, codec, dtype):
+    """Rank-order binary32 sum of the decoded payloads, rounded once to dtype."""
+    dt = {CODEC_BF16: np.uint16, CODEC_FP8: np.uint8}[codec]
+    codes = [np.ascontiguousarray(c, dtype=dt) for c in codes]
+    n = codes[0].size
+    sp = _ptr_array([_f32(s) for s in scales]) if codec == CODEC_FP8 else None
+    out = np.empty(n, dtype=NP_DTYPES[dtype])
+    _load().or_decode_sum_typed(_ptr(out), DTYPES[dtype], _ptr_array(codes), sp, len(codes), n, int(codec))
+    return out
+
+
+def bucket_allreduce_typed(xs, dtype, bucket_elems, codec, mode=SCALE_ABSMAX_DIV_448):
+    """Bucket stream over arrays of dtype.  Returns (out, codes, scales or None)."""
+    xs = [_typed(x, dtype) for x in xs]
+    k, n = len(xs), xs[0].size
+    out = np.empty(n, dtype=NP_DTYPES[dtype])
+    if codec == CODEC_NONE:
+        codes, scales = [np.empty(0, dtype=np.float32) for _ in range(k)], None
+    elif codec == CODEC_BF16:
+        codes, scales = [np.empty(n, dtype=np.uint16) for _ in range(k)], None
+    else:
+        codes = [np.empty(n, dtype=np.uint8) for _ in range(k)]
+        nb = sum(nblocks(min(bucket_elems, n - s)) for s in range(0, n, bucket_elems))
+        scales = [np.empty(nb, dtype=np.float32) for _ in range(k)]
+    _load().or_bucket_allreduce_typed(
+        _ptr(out), _ptr_array(codes), _ptr_array(scales) if scales else None, _ptr_array(xs), k, n,
+        int(bucket_elems), int(codec), int(mode), DTYPES[dtype])
+    return out, codes, scales
