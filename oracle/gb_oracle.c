@@ -620,12 +620,33 @@ void or_reduce_typed(void* out, const void* const* x, int k, size_t n, int dtype
  * (nearest, ties to even, IEEE overflow to Inf).  Without a codec the stream
  * is the exact SUM of that type (or_reduce_typed).
  * --------------------------------------------------------------------- */
+/* A NaN keeps its sign and the top bits of its payload and comes out quiet
+ * (IEEE 754-2019, 6.2.3, the preferred NaN propagation of a format
+ * conversion); bfloat16 widens bit for bit, as the bf16 codec decodes. */
+static float quiet_nan_f32(uint32_t sign, uint32_t payload23) {
+  return bits_float(sign | 0x7FC00000u | (payload23 & 0x3FFFFFu));
+}
+
 static float typed_to_f32(const void* a, size_t i, int t) {
   switch (t) {
     case OR_T_F32: return ((const float*)a)[i];
-    case OR_T_F16: return (float)f16_value(((const uint16_t*)a)[i]);  /* exact */
+    case OR_T_F16: {
+      uint16_t c = ((const uint16_t*)a)[i];
+      if ((c & 0x7C00) == 0x7C00 && (c & 0x03FF)) {  /* NaN: 10 payload bits */
+        return quiet_nan_f32((uint32_t)(c & 0x8000) << 16, (uint32_t)(c & 0x03FF) << 13);
+      }
+      return (float)f16_value(c);  /* exact */
+    }
     case OR_T_BF16: return or_bf16_decode_one(((const uint16_t*)a)[i]);
-    default: return (float)((const double*)a)[i];  /* one binary32 rounding */
+    default: {
+      double d = ((const double*)a)[i];
+      if (isnan(d)) {  /* top 23 of the 52 payload bits */
+        uint64_t u;
+        memcpy(&u, &d, sizeof u);
+        return quiet_nan_f32((uint32_t)(u >> 32) & 0x80000000u, (uint32_t)((u >> 29) & 0x7FFFFFu));
+      }
+      return (float)d;  /* one binary32 rounding */
+    }
   }
 }
 

@@ -134,3 +134,30 @@ def test_bucket_stream(dt, codec):
         assert (codes[r] == wc[r]).all()
         if codec == O.CODEC_FP8:
             assert (scales[r].view(np.uint32) == ws[r].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("codec", [O.CODEC_BF16, O.CODEC_FP8])
+def test_every_f16_code_including_nan_payloads(codec):
+    """All 2^16 half codes: the encode equals the binary32 encode of torch's
+    own half -> float cast, which keeps a NaN's sign and payload (so the bf16
+    code of a NaN carries the top payload bits and the fp8 code its sign)."""
+    x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    codes, scales = O.encode_typed(x, "f16", codec, 0)
+    if codec == O.CODEC_BF16:
+        assert (codes == O.encode_bf16(as_f32(x, "f16"))).all()
+    else:
+        wc, ws = O.encode_fp8(as_f32(x, "f16"), 0)
+        assert (codes == wc).all() and (scales.view(np.uint32) == ws.view(np.uint32)).all()
+
+
+def test_f64_nan_payload_and_sign():
+    """float64 NaNs with payloads and both signs: numpy's float64 -> float32
+    cast keeps the sign and the top payload bits, quiet."""
+    u = np.array([0x7FF8000000000000, 0xFFF8000000000000, 0x7FF0000000000001, 0x7FF4000000000000,
+                  0xFFFABCDEF0123456, 0x7FF0000020000000, 0x7FFFFFFFFFFFFFFF], dtype=np.uint64)
+    x = np.concatenate([u.view(np.float64), np.ones(256 - u.size)])
+    codes, _ = O.encode_typed(x, "f64", O.CODEC_BF16)
+    with np.errstate(invalid="ignore"):  # signalling NaNs raise "invalid" as they are quieted
+        want = O.encode_bf16(x.astype(np.float32))
+    assert (codes == want).all()
+    assert codes[4] & 0x8000 and codes[4] != 0xFFC0  # sign and payload survive
