@@ -19,6 +19,10 @@ Workloads (inputs from workloads.py):
                    call over the whole stream per step (one launch; buckets
                    start on block boundaries).  The same pass made as one call
                    per bucket, as a DDP hook would issue it, is reported too.
+                   --dtype f16|bf16|f64 runs the same stream over gradients
+                   of that type (gb_bucket_allreduce_local_typed): values
+                   taken to float32, encoded, the float32 total rounded once
+                   to the type.
   gradients_256mib k=4 x 2^26 fp32; 4 x gb_encode_fp8_e4m3_blockscaled +
                    gb_decode_accumulate(fp8).
   gradients_64mib  k=4 x 2^24 fp32; 4 x gb_encode_bf16 + gb_decode_accumulate(bf16).
@@ -113,31 +117,41 @@ class DdpBuckets(Workload):
         self.W = W
         self.k, self.n, self.bucket = 4, W.DDP_N, W.DDP_BUCKET
         self.mode = args.scale_mode
+        self.dt = args.dtype
+        if self.dt not in ("f32", "f16", "bf16", "f64"):
+            raise SystemExit("the bucket stream compresses floating-point gradients only")
+        self.esize = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}[self.dt]
         self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n,
                        "bucket_elems": self.bucket, "buckets": len(W.ddp_buckets()),
                        "codec": "fp8_e4m3_b256",
                        "scale_mode": ["absmax_div_448", "pow2"][self.mode],
-                       "distribution": "N(0, sigma=1e-3)"}
+                       "distribution": "N(0, sigma=1e-3)", "element_type": self.dt}
 
     def setup(self):
         torch, gb = self.torch, self.gb
-        self.x = [self.W.device_gradients(self.n, self.W.BASE_SEED + r, self.dev) for r in range(self.k)]
-        self.out = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+        self.x = [self.W.device_gradients_typed(self.n, self.W.BASE_SEED + r, self.dev, self.dt)
+                  for r in range(self.k)]
+        self.out = torch.empty(self.n, dtype=self.x[0].dtype, device=self.dev)
         self.lay = gb.gb_bucket_workspace_layout(gb.GB_CODEC_FP8_E4M3_B256, self.k, self.n, self.bucket)
         self.ws = torch.empty(self.lay["total"], dtype=torch.uint8, device=self.dev)
 
     def step(self):
-        self.gb.gb_bucket_allreduce_local(self.out, self.x, self.bucket, self.gb.GB_CODEC_FP8_E4M3_B256,
-                                          self.mode, self.ws)
+        if self.dt == "f32":
+            self.gb.gb_bucket_allreduce_local(self.out, self.x, self.bucket, self.gb.GB_CODEC_FP8_E4M3_B256,
+                                              self.mode, self.ws)
+        else:
+            self.gb.gb_bucket_allreduce_local_typed(self.out, self.x, self.bucket, self.gb.GB_CODEC_FP8_E4M3_B256,
+                                                    self.mode, self.ws)
 
     def bytes_for(self, n):
-        return self.k * 4 * n + self.k * (n + 4 * nblocks(n)) + 4 * n
+        # every rank's gradients read, every payload written, the sum written
+        return self.k * self.esize * n + self.k * (n + 4 * nblocks(n)) + self.esize * n
 
     def step_bytes(self):
         return sum(self.bytes_for(l) for _, l in self.W.ddp_buckets())
 
     def timed_kernel(self):
-        return ("fused_fp8_kernel<4>", self.step_bytes(), 1, self.step)
+        return (f"fused_fp8_kernel<4,{self.gb.GB_DTYPE_OF[self.dt]}>", self.step_bytes(), 1, self.step)
 
     def per_bucket_step(self):
         gb = self.gb
@@ -150,8 +164,11 @@ class DdpBuckets(Workload):
         workspace.  The 153 calls are captured once in a HIP graph and the
         graph is replayed, so the figure is the GPU's, not the Python
         binding's per-call cost; every replay's output is checked against the
-        single-launch result.  Leaves the workspace in the per-bucket layout."""
+        single-launch result.  Leaves the workspace in the per-bucket layout.
+        Measured on float32 gradients only."""
         torch, gb = self.torch, self.gb
+        if self.dt != "f32":
+            return {}
         want = self.out.clone()
         self.pb_args = []
         off = 0
@@ -187,15 +204,23 @@ class DdpBuckets(Workload):
         torch = self.torch
         torch.cuda.synchronize()
         done_bytes, t_oracle, nb, ok = 0, 0.0, 0, True
+
+        def host(t):  # 16-bit floats as their raw codes
+            return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.element_size() == 2 else t.cpu().numpy()
         for start, length in self.W.ddp_buckets():
-            xs = [t[start:start + length].cpu().numpy() for t in self.x]
+            xs = [host(t[start:start + length]) for t in self.x]
             t0 = time.perf_counter()
-            want, codes, scales = O.bucket_allreduce(xs, self.bucket, O.CODEC_FP8, self.mode)
+            if self.dt == "f32":
+                want, codes, scales = O.bucket_allreduce(xs, self.bucket, O.CODEC_FP8, self.mode)
+            else:
+                want, codes, scales = O.bucket_allreduce_typed(xs, self.dt, self.bucket, O.CODEC_FP8, self.mode)
             t_oracle += time.perf_counter() - t0
             done_bytes += self.bytes_for(length)
             nb += 1
-            got = self.out[start:start + length].cpu().numpy()
-            ok &= bool((got.view(np.uint32) == want.view(np.uint32)).all())
+            got = host(self.out[start:start + length])
+            gn = np.isnan(got) if got.dtype.kind == "f" else np.zeros(got.size, bool)
+            wn = np.isnan(want) if want.dtype.kind == "f" else np.zeros(want.size, bool)
+            ok &= bool((gn == wn).all()) and bool((got[~gn].tobytes() == want[~wn].tobytes()))
             for r in range(self.k):
                 c0 = r * self.lay["codes_stride"] + start
                 s0 = self.lay["scales_offset"] + r * self.lay["scales_stride"] + 4 * (start // 256)
@@ -330,7 +355,7 @@ class Staged(Workload):
     def timed_kernel(self):
         n = self.n
         per = self.k * self.payload() + 4 * n
-        return ("decode_fp8_kernel<4,false>", per, 1,
+        return ("decode_fp8_kernel<4,false,0>", per, 1,
                 lambda: self.gb.gb_decode_accumulate(self.acc, self.rd, self.rsd, self.gb.GB_CODEC_FP8_E4M3_B256))
 
     def extra(self, time_region, reps):
@@ -407,7 +432,7 @@ class Gradients256(Workload):
 
     def timed_kernel(self):
         per = 4 * self.n + self.n + 4 * nblocks(self.n)
-        return ("encode_fp8_kernel", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
+        return ("encode_fp8_kernel<0>", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
     def cpu_sample(self, budget):
         from oracle import oracle as O
@@ -458,7 +483,7 @@ class Gradients64(Workload):
         return self.k * 6 * self.n + self.k * 2 * self.n + 4 * self.n
 
     def timed_kernel(self):
-        return ("encode_bf16_kernel", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
+        return ("encode_bf16_kernel<0>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
     def cpu_sample(self, budget):
         from oracle import oracle as O

@@ -26,6 +26,7 @@ __all__ = [
     "gb_encode_bf16_ef", "gb_encode_fp8_e4m3_blockscaled_ef", "gb_bucket_allreduce_local_ef",
     "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
     "gb_encode_staged", "gb_decode_accumulate_staged", "gb_reduce_typed", "GB_DTYPE", "GB_DTYPE_OF",
+    "gb_encode", "gb_decode_sum", "gb_bucket_allreduce_local_typed",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -56,6 +57,9 @@ _SIGNATURES = {
     "gb_reduce_sum": (_I, [_P, _PP, _I, _S, _P]),
     "gb_reduce": (_I, [_P, _PP, _I, _S, _I, _I, _P]),
     "gb_reduce_typed": (_I, [_P, _PP, _I, _S, _I, _I, _I, _P]),
+    "gb_encode": (_I, [_I, _I, _P, _P, _P, _S, _I, _P]),
+    "gb_decode_sum": (_I, [_I, _P, _PP, _PP, _I, _S, _I, _P]),
+    "gb_bucket_allreduce_local_typed": (_I, [_I, _P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
     "gb_encode_bf16": (_I, [_P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
@@ -215,6 +219,65 @@ def gb_bucket_allreduce_local(out, srcs, bucket_elems, codec, scale_mode=GB_SCAL
     _check(_lib.gb_bucket_allreduce_local(_ptr(out), _ptr_array(srcs), len(srcs), n,
                                           int(bucket_elems), int(codec), int(scale_mode),
                                           _ptr(workspace), ws_bytes, _stream(stream, out.device)))
+
+
+_CODEC_TYPES = (torch.float32, torch.float16, torch.bfloat16, torch.float64)
+
+
+def _float_tensor(t, name):
+    if not isinstance(t, torch.Tensor) or t.dtype not in _CODEC_TYPES:
+        raise TypeError(f"{name} must be a tensor of one of {list(_CODEC_TYPES)}")
+    _device_tensor(t, t.dtype, name)
+
+
+def gb_encode(codec, codes, scales, src, scale_mode=GB_SCALE_ABSMAX_DIV_448, stream=None):
+    """Bridge encode of src (float32, float16, bfloat16 or float64): codes
+    (uint16 for bf16, uint8 for fp8) and, for fp8, scales (fp32)."""
+    _float_tensor(src, "src")
+    n = src.numel()
+    _device_tensor(codes, _CODE_DTYPE[int(codec)] if int(codec) in _CODE_DTYPE else torch.uint8, "codes")
+    _same_numel([codes], n, "codes")
+    if scales is not None:
+        _device_tensor(scales, torch.float32, "scales")
+        _same_numel([scales], (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    _check(_lib.gb_encode(int(codec), GB_DTYPE[src.dtype], _ptr(codes), _ptr(scales), _ptr(src), n,
+                          int(scale_mode), _stream(stream, src.device)))
+
+
+def gb_decode_sum(dst, codes, scales, codec, stream=None):
+    """dst (float32, float16, bfloat16 or float64) = the float32 rank-order sum
+    of the decoded payloads, rounded once to dst's type."""
+    _float_tensor(dst, "dst")
+    n = dst.numel()
+    dt = _CODE_DTYPE.get(int(codec))
+    if dt is not None:
+        for i, c in enumerate(codes):
+            _device_tensor(c, dt, f"codes[{i}]")
+        _same_numel(codes, n, "codes")
+    if scales is not None:
+        for i, sc in enumerate(scales):
+            _device_tensor(sc, torch.float32, f"scales[{i}]")
+    _check(_lib.gb_decode_sum(GB_DTYPE[dst.dtype], _ptr(dst), _ptr_array(codes),
+                              _ptr_array(scales) if scales is not None else None, len(codes), n, int(codec),
+                              _stream(stream, dst.device)))
+
+
+def gb_bucket_allreduce_local_typed(out, srcs, bucket_elems, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                    workspace=None, stream=None):
+    """gb_bucket_allreduce_local over float32, float16, bfloat16 or float64
+    buffers (out's type; srcs share it)."""
+    _float_tensor(out, "out")
+    for i, s in enumerate(srcs):
+        _device_tensor(s, out.dtype, f"srcs[{i}]")
+    n = out.numel()
+    _same_numel(srcs, n, "srcs")
+    ws_bytes = 0
+    if workspace is not None:
+        _device_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(_lib.gb_bucket_allreduce_local_typed(GB_DTYPE[out.dtype], _ptr(out), _ptr_array(srcs), len(srcs), n,
+                                                int(bucket_elems), int(codec), int(scale_mode), _ptr(workspace),
+                                                ws_bytes, _stream(stream, out.device)))
 
 
 def gb_encode_bf16_ef(codes, residual, src, stream=None):

@@ -133,6 +133,12 @@ gb_status check_pinned(const void* p, size_t align, const char* fn, const char* 
   return GB_OK;
 }
 
+// Element types the codec calls read and write (README "Bridge compression"
+// applies to floating-point tensors).
+bool codec_dtype(int dtype) {
+  return dtype == GB_DTYPE_F32 || dtype == GB_DTYPE_F16 || dtype == GB_DTYPE_BF16 || dtype == GB_DTYPE_F64;
+}
+
 size_t code_size(int codec) { return codec == GB_CODEC_BF16 ? 2 : (codec == GB_CODEC_FP8_E4M3_B256 ? 1 : 4); }
 
 }  // namespace
@@ -260,7 +266,7 @@ gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stre
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  return from_hip(gb::launch_encode_bf16(codes, src, n, as_stream(stream)), fn);
+  return from_hip(gb::launch_encode_bf16(codes, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
 }
 
 gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales, const float* src, size_t n,
@@ -272,7 +278,7 @@ gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales, const fl
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  return from_hip(gb::launch_encode_fp8(codes, scales, src, n, scale_mode, as_stream(stream)), fn);
+  return from_hip(gb::launch_encode_fp8(codes, scales, src, n, scale_mode, GB_DTYPE_F32, as_stream(stream)), fn);
 }
 
 gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float* const* scales, int k,
@@ -293,13 +299,65 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float
     case GB_CODEC_NONE:
       return from_hip(gb::launch_reduce_sum(acc, c, k, n, accumulate != 0, st), fn);
     case GB_CODEC_BF16:
-      return from_hip(gb::launch_decode_bf16(acc, c, k, n, accumulate != 0, st), fn);
+      return from_hip(gb::launch_decode_bf16(acc, c, k, n, accumulate != 0, GB_DTYPE_F32, st), fn);
     default: {
       gb::PtrTable sc = {};
       if ((s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales", &sc)) != GB_OK) {
         return s;
       }
-      return from_hip(gb::launch_decode_fp8(acc, c, sc, k, n, accumulate != 0, st), fn);
+      return from_hip(gb::launch_decode_fp8(acc, c, sc, k, n, accumulate != 0, GB_DTYPE_F32, st), fn);
+    }
+  }
+}
+
+gb_status gb_encode(int codec, int dtype, void* codes, float* scales, const void* src, size_t n, int scale_mode,
+                    void* stream) {
+  const char* fn = "gb_encode";
+  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+  }
+  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  if (fp8) {
+    return from_hip(gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, src, n, scale_mode, dtype, st), fn);
+  }
+  return from_hip(gb::launch_encode_bf16(static_cast<uint16_t*>(codes), src, n, dtype, st), fn);
+}
+
+gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes, const float* const* scales, int k,
+                        size_t n, int codec, void* stream) {
+  const char* fn = "gb_decode_sum";
+  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+  if (codec == GB_CODEC_NONE && dtype != GB_DTYPE_F32) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: uncompressed payloads are float32; reduce other types exactly with "
+                "gb_reduce_typed", fn);
+  }
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (n == 0) return GB_OK;
+  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+  gb::PtrTable c = {};
+  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes", &c)) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  switch (codec) {
+    case GB_CODEC_NONE:
+      return from_hip(gb::launch_reduce_sum(static_cast<float*>(dst), c, k, n, false, st), fn);
+    case GB_CODEC_BF16:
+      return from_hip(gb::launch_decode_bf16(dst, c, k, n, false, dtype, st), fn);
+    default: {
+      gb::PtrTable sc = {};
+      if ((s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales", &sc)) != GB_OK) {
+        return s;
+      }
+      return from_hip(gb::launch_decode_fp8(dst, c, sc, k, n, false, dtype, st), fn);
     }
   }
 }
@@ -339,8 +397,8 @@ gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* sc
     const size_t l = n - o < chunk_elems ? n - o : chunk_elems;
     hipStream_t cs = c->copy[chunk % kCopyStreams];
     e = fp8 ? gb::launch_encode_fp8(reinterpret_cast<uint8_t*>(cd + o), scales_dev + o / GB_BLOCK, src + o, l,
-                                    scale_mode, st)
-            : gb::launch_encode_bf16(reinterpret_cast<uint16_t*>(cd + 2 * o), src + o, l, st);
+                                    scale_mode, GB_DTYPE_F32, st)
+            : gb::launch_encode_bf16(reinterpret_cast<uint16_t*>(cd + 2 * o), src + o, l, GB_DTYPE_F32, st);
     if (e == hipSuccess) e = hipEventRecord(c->ev_compute, st);
     if (e == hipSuccess) e = hipStreamWaitEvent(cs, c->ev_compute, 0);
     if (e == hipSuccess) e = hipMemcpyAsync(ch + cb * o, cd + cb * o, cb * l, hipMemcpyDeviceToHost, cs);
@@ -423,8 +481,8 @@ gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
     if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[ci], 0);
     if (e != hipSuccess) break;
     if (codec == GB_CODEC_NONE) e = gb::launch_reduce_sum(acc + o, cp, k, l, accumulate != 0, st);
-    else if (codec == GB_CODEC_BF16) e = gb::launch_decode_bf16(acc + o, cp, k, l, accumulate != 0, st);
-    else e = gb::launch_decode_fp8(acc + o, cp, sp, k, l, accumulate != 0, st);
+    else if (codec == GB_CODEC_BF16) e = gb::launch_decode_bf16(acc + o, cp, k, l, accumulate != 0, GB_DTYPE_F32, st);
+    else e = gb::launch_decode_fp8(acc + o, cp, sp, k, l, accumulate != 0, GB_DTYPE_F32, st);
   }
   return from_hip(e, fn);
 }
@@ -435,7 +493,7 @@ namespace {
 
 // Validation shared by the two bucket-stream calls; on success fills the
 // workspace layout and the source table.
-gb_status check_bucket(const char* fn, float* out, const float* const* srcs, int k, size_t n,
+gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k, size_t n,
                        size_t bucket_elems, int codec, int scale_mode, void* workspace, size_t workspace_bytes,
                        size_t* cs, size_t* so, size_t* ss, gb::PtrTable* t) {
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
@@ -445,14 +503,15 @@ gb_status check_bucket(const char* fn, float* out, const float* const* srcs, int
   size_t need;
   gb_status s = gb_bucket_workspace_layout(codec, k, n, bucket_elems, cs, so, ss, &need);
   if (s != GB_OK) {
-    // re-label the failure with this function's name
-    return fail(s, "%s: %s", fn, g_last_error + std::strlen("gb_bucket_workspace_layout: "));
+    // re-label the failure with this function's name (from a copy: fail()
+    // writes the buffer the message is read from)
+    char msg[sizeof g_last_error];
+    std::snprintf(msg, sizeof msg, "%s", g_last_error + std::strlen("gb_bucket_workspace_layout: "));
+    return fail(s, "%s: %s", fn, msg);
   }
   if (n == 0) return GB_OK;
   if ((s = check_array(out, GB_ALIGN, fn, "out")) != GB_OK) return s;
-  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", t)) != GB_OK) {
-    return s;
-  }
+  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs", t)) != GB_OK) return s;
   if (codec != GB_CODEC_NONE) {
     if (workspace == nullptr || workspace_bytes < need) {
       return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes,
@@ -475,8 +534,8 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
   const char* fn = "gb_bucket_allreduce_local";
   size_t cs, so, ss;
   gb::PtrTable t = {};
-  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes,
-                             &cs, &so, &ss, &t);
+  gb_status s = check_bucket(fn, out, reinterpret_cast<const void* const*>(srcs), k, n, bucket_elems, codec,
+                             scale_mode, workspace, workspace_bytes, &cs, &so, &ss, &t);
   if (s != GB_OK || n == 0) return s;
   hipStream_t st = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
@@ -492,7 +551,7 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
   } else if (codec == GB_CODEC_BF16) {
     uint16_t* c[GB_MAX_K];
     for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
-    e = gb::launch_fused_bf16(out, t, c, k, n, st);
+    e = gb::launch_fused_bf16(out, t, c, k, n, GB_DTYPE_F32, st);
   } else {
     uint8_t* c[GB_MAX_K];
     float* sc[GB_MAX_K];
@@ -500,7 +559,41 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
       c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
       sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
     }
-    e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, st);
+    e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, GB_DTYPE_F32, st);
+  }
+  return from_hip(e, fn);
+}
+
+gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* const* srcs, int k, size_t n,
+                                          size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  const char* fn = "gb_bucket_allreduce_local_typed";
+  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+  size_t cs, so, ss;
+  gb::PtrTable t = {};
+  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                             &so, &ss, &t);
+  if (s != GB_OK || n == 0) return s;
+  hipStream_t st = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  // One launch over all buckets, as gb_bucket_allreduce_local; without a
+  // codec the exact SUM of the type.
+  hipError_t e;
+  if (codec == GB_CODEC_NONE) {
+    e = dtype == GB_DTYPE_F32 ? gb::launch_reduce_sum(static_cast<float*>(out), t, k, n, false, st)
+                              : gb::launch_reduce_typed(out, t, k, n, dtype, GB_OP_SUM, 1, st);
+  } else if (codec == GB_CODEC_BF16) {
+    uint16_t* c[GB_MAX_K];
+    for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
+    e = gb::launch_fused_bf16(out, t, c, k, n, dtype, st);
+  } else {
+    uint8_t* c[GB_MAX_K];
+    float* sc[GB_MAX_K];
+    for (int r = 0; r < k; r++) {
+      c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
+      sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
+    }
+    e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, dtype, st);
   }
   return from_hip(e, fn);
 }
@@ -537,8 +630,8 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, flo
   }
   size_t cs, so, ss;
   gb::PtrTable t = {};
-  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes,
-                             &cs, &so, &ss, &t);
+  gb_status s = check_bucket(fn, out, reinterpret_cast<const void* const*>(srcs), k, n, bucket_elems, codec,
+                             scale_mode, workspace, workspace_bytes, &cs, &so, &ss, &t);
   if (s != GB_OK || n == 0) return s;
   gb::PtrTable rt = {};
   if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals", &rt)) !=

@@ -33,23 +33,21 @@ hipError_t launch_reduce_op(float* dst, const PtrTable& srcs, int k, size_t n, i
 // Any element type but fp32 (GB_DTYPE_*); integer types with SUM, MAX, MIN.
 hipError_t launch_reduce_typed(void* dst, const PtrTable& srcs, int k, size_t n, int dtype, int op, int divisor,
                                hipStream_t stream);
-hipError_t launch_encode_bf16(uint16_t* codes, const float* src, size_t n,
+// The codec launchers take the element type of the values they read or
+// write (dtype: GB_DTYPE_F32, F16, BF16 or F64); accumulate needs F32.
+hipError_t launch_encode_bf16(uint16_t* codes, const void* src, size_t n, int dtype, hipStream_t stream);
+hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const void* src, size_t n, int scale_mode, int dtype,
+                             hipStream_t stream);
+hipError_t launch_decode_bf16(void* acc, const PtrTable& codes, int k, size_t n, bool accumulate, int dtype,
                               hipStream_t stream);
-hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const float* src,
-                             size_t n, int scale_mode, hipStream_t stream);
-hipError_t launch_decode_bf16(float* acc, const PtrTable& codes, int k,
-                              size_t n, bool accumulate, hipStream_t stream);
-hipError_t launch_decode_fp8(float* acc, const PtrTable& codes,
-                             const PtrTable& scales, int k, size_t n,
-                             bool accumulate, hipStream_t stream);
+hipError_t launch_decode_fp8(void* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
+                             bool accumulate, int dtype, hipStream_t stream);
 // One pass over [0, n) of k sources: encode each source into its payload
 // (codes[r], scales[r]) and write the decoded rank-order sum to out.
-hipError_t launch_fused_bf16(float* out, const PtrTable& srcs,
-                             uint16_t* const* codes, int k, size_t n,
+hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* codes, int k, size_t n, int dtype,
                              hipStream_t stream);
-hipError_t launch_fused_fp8(float* out, const PtrTable& srcs,
-                            uint8_t* const* codes, float* const* scales, int k,
-                            size_t n, int scale_mode, hipStream_t stream);
+hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales, int k,
+                            size_t n, int scale_mode, int dtype, hipStream_t stream);
 
 // Error-feedback variants: residual (or residuals[r]) is read and rewritten.
 hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n,

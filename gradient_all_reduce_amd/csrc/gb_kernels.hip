@@ -166,6 +166,69 @@ __device__ __forceinline__ f4 bf16_unpack4(u2 w) {
 }
 
 // ---------------------------------------------------------------------------
+// Element types of the codec kernels' inputs and outputs (README "Bridge
+// compression": floating-point tensors; their payloads are added in
+// float32).  ET is GB_DTYPE_F32, F16, BF16 or F64.  A load gives elements
+// [i, i + 4) as binary32 (exact from the halves, rounded once to nearest-even
+// from float64; zero at and beyond n); a store rounds binary32 once to the
+// type (nearest-even, IEEE overflow; exact to float64).
+// ---------------------------------------------------------------------------
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef double d2v __attribute__((ext_vector_type(2)));
+
+template <int ET, bool FULL>
+__device__ __forceinline__ f4 load_vals4_at(const void* p, size_t i, size_t n) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    return load4_at<FULL>(static_cast<const float*>(p), i, n);
+  } else if constexpr (ET == GB_DTYPE_BF16) {
+    return bf16_unpack4(load_bf16_4_at<FULL>(static_cast<const uint16_t*>(p), i, n));
+  } else if constexpr (ET == GB_DTYPE_F16) {
+    const h4 h = __builtin_bit_cast(h4, load_bf16_4_at<FULL>(static_cast<const uint16_t*>(p), i, n));
+    return f4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+  } else {
+    const double* d = static_cast<const double*>(p) + i;
+    d2v lo, hi;
+    if (FULL || i + 4 <= n) {
+      lo = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(d));
+      hi = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(d + 2));
+    } else {
+      lo = d2v{i < n ? d[0] : 0.0, i + 1 < n ? d[1] : 0.0};
+      hi = d2v{i + 2 < n ? d[2] : 0.0, 0.0};
+    }
+    return f4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+  }
+}
+
+template <int ET, bool FULL>
+__device__ __forceinline__ void store_vals4_at(void* p, size_t i, size_t n, f4 v) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    store4_at<FULL>(static_cast<float*>(p), i, n, v);
+  } else if constexpr (ET == GB_DTYPE_BF16) {
+    store_bf16_4_at<FULL>(static_cast<uint16_t*>(p), i, n, bf16_pack4(v));
+  } else if constexpr (ET == GB_DTYPE_F16) {
+    // The binary32 values must exist before they are rounded to float16: left
+    // alone, the compiler may fold the product or sum that made them into one
+    // mixed-precision fma rounding straight to float16 (one rounding instead
+    // of the two the definition has, and +0 for a -0 product).  The empty asm
+    // pins them in registers and emits nothing.
+    asm volatile("" : "+v"(v));
+    const h4 h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    store_bf16_4_at<FULL>(static_cast<uint16_t*>(p), i, n, __builtin_bit_cast(u2, h));
+  } else {
+    double* d = static_cast<double*>(p) + i;
+    const d2v lo = {(double)v.x, (double)v.y}, hi = {(double)v.z, (double)v.w};
+    if (FULL || i + 4 <= n) {
+      __builtin_nontemporal_store(lo, reinterpret_cast<d2v*>(d));
+      __builtin_nontemporal_store(hi, reinterpret_cast<d2v*>(d + 2));
+    } else {
+      if (i < n) d[0] = lo.x;
+      if (i + 1 < n) d[1] = lo.y;
+      if (i + 2 < n) d[2] = hi.x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp8: OCP E4M3 (bias 7, largest finite 448 = 0x7E, S.1111.111 = NaN), one
 // fp32 scale per 256-value block.
 // ---------------------------------------------------------------------------
@@ -626,53 +689,54 @@ __global__ __launch_bounds__(kThreads) void reduce_typed_kernel(void* dst, PtrTa
 // instruction of a wavefront loads 1 KiB of fp32 and stores 512 bytes of
 // codes (or the reverse), contiguously.
 // ===========================================================================
-template <bool FULL>
-__device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const float* src, size_t n) {
+template <int ET, bool FULL>
+__device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const void* src, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
-  store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(load4_at<FULL>(src, i, n)));
+  store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(load_vals4_at<ET, FULL>(src, i, n)));
 }
 
-__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const float* src, size_t n) {
-  if (group_full(kVecPerGroup, n)) encode_bf16_body<true>(codes, src, n);
-  else encode_bf16_body<false>(codes, src, n);
+template <int ET>
+__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const void* src, size_t n) {
+  if (group_full(kVecPerGroup, n)) encode_bf16_body<ET, true>(codes, src, n);
+  else encode_bf16_body<ET, false>(codes, src, n);
 }
 
-template <int K, bool ACC, bool FULL>
-__device__ __forceinline__ void decode_bf16_body(float* acc, const PtrTable& codes, size_t n) {
+template <int K, bool ACC, int ET, bool FULL>
+__device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   u2 w[K];
 #pragma unroll
   for (int r = 0; r < K; r++) w[r] = load_bf16_4_at<FULL>(static_cast<const uint16_t*>(codes.p[r]), i, n);
   f4 a;
-  if (ACC) a = load4_at<FULL>(acc, i, n);
+  if (ACC) a = load_vals4_at<ET, FULL>(acc, i, n);
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const f4 v = bf16_unpack4(w[r]);
     a = (!ACC && r == 0) ? v : a + v;
   }
-  store4_at<FULL>(acc, i, n, a);
+  store_vals4_at<ET, FULL>(acc, i, n, a);
 }
 
-template <int K, bool ACC>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(float* acc, PtrTable codes, size_t n) {
-  if (group_full(kVecPerGroup, n)) decode_bf16_body<K, ACC, true>(acc, codes, n);
-  else decode_bf16_body<K, ACC, false>(acc, codes, n);
+template <int K, bool ACC, int ET>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTable codes, size_t n) {
+  if (group_full(kVecPerGroup, n)) decode_bf16_body<K, ACC, ET, true>(acc, codes, n);
+  else decode_bf16_body<K, ACC, ET, false>(acc, codes, n);
 }
 
 // ===========================================================================
 // fp8 encode: one DPP row per 256-value block.
 // ===========================================================================
-template <bool FULL>
-__device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, const float* src, size_t n,
+template <int ET, bool FULL>
+__device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, const void* src, size_t n,
                                                 int mode) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
   const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++) x[j] = load4_at<FULL>(src, lane_elem(block, j, col), n);
+  for (int j = 0; j < 4; j++) x[j] = load_vals4_at<ET, FULL>(src, lane_elem(block, j, col), n);
   uint32_t w[4];
   const float s = encode_block16(x, mode, w);  // all 64 lanes take part
   if (!FULL && block * kBlock >= n) return;
@@ -681,18 +745,19 @@ __device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, c
   for (int j = 0; j < 4; j++) store_codes4_at<FULL>(codes, lane_elem(block, j, col), n, w[j]);
 }
 
-__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const float* src,
+template <int ET>
+__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const void* src,
                                                                size_t n, int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) encode_fp8_body<true>(codes, scales, src, n, mode);
-  else encode_fp8_body<false>(codes, scales, src, n, mode);
+  if (group_full(kBlocksPerGroup * kBlock, n)) encode_fp8_body<ET, true>(codes, scales, src, n, mode);
+  else encode_fp8_body<ET, false>(codes, scales, src, n, mode);
 }
 
 // ===========================================================================
 // fp8 decode-accumulate over K payloads: one DPP row per block, each rank's
 // block scale read once per lane.
 // ===========================================================================
-template <int K, bool ACC, bool FULL>
-__device__ __forceinline__ void decode_fp8_body(float* acc, const PtrTable& codes, const PtrTable& scales,
+template <int K, bool ACC, int ET, bool FULL>
+__device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes, const PtrTable& scales,
                                                 size_t n) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
@@ -709,7 +774,7 @@ __device__ __forceinline__ void decode_fp8_body(float* acc, const PtrTable& code
   f4 a[4];
   if (ACC) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) a[j] = load4_at<FULL>(acc, lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) a[j] = load_vals4_at<ET, FULL>(acc, lane_elem(block, j, col), n);
   }
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -720,22 +785,22 @@ __device__ __forceinline__ void decode_fp8_body(float* acc, const PtrTable& code
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; j++) store4_at<FULL>(acc, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(acc, lane_elem(block, j, col), n, a[j]);
 }
 
-template <int K, bool ACC>
-__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(float* acc, PtrTable codes, PtrTable scales,
+template <int K, bool ACC, int ET>
+__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTable codes, PtrTable scales,
                                                                size_t n) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) decode_fp8_body<K, ACC, true>(acc, codes, scales, n);
-  else decode_fp8_body<K, ACC, false>(acc, codes, scales, n);
+  if (group_full(kBlocksPerGroup * kBlock, n)) decode_fp8_body<K, ACC, ET, true>(acc, codes, scales, n);
+  else decode_fp8_body<K, ACC, ET, false>(acc, codes, scales, n);
 }
 
 // ===========================================================================
 // Fused fp8 bucket pass: read each rank's block once, write its payload
 // (codes, scale), decode those codes and add them in rank order.
 // ===========================================================================
-template <int K, bool FULL>
-__device__ __forceinline__ void fused_fp8_body(float* out, const PtrTable& src, const OutTable& codes,
+template <int K, int ET, bool FULL>
+__device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, const OutTable& codes,
                                                const OutTable& scales, size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
@@ -743,7 +808,7 @@ __device__ __forceinline__ void fused_fp8_body(float* out, const PtrTable& src, 
 #pragma unroll
   for (int r = 0; r < K; r++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) x[r][j] = load4_at<FULL>(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) x[r][j] = load_vals4_at<ET, FULL>(src.p[r], lane_elem(block, j, col), n);
   }
   const bool live = FULL || block * kBlock < n;
   f4 a[4];
@@ -765,26 +830,26 @@ __device__ __forceinline__ void fused_fp8_body(float* out, const PtrTable& src, 
   }
   if (!live) return;
 #pragma unroll
-  for (int j = 0; j < 4; j++) store4_at<FULL>(out, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(out, lane_elem(block, j, col), n, a[j]);
 }
 
-template <int K>
-__global__ __launch_bounds__(kThreads) void fused_fp8_kernel(float* out, PtrTable src, OutTable codes,
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable src, OutTable codes,
                                                               OutTable scales, size_t n, int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, true>(out, src, codes, scales, n, mode);
-  else fused_fp8_body<K, false>(out, src, codes, scales, n, mode);
+  if (group_full(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode);
+  else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode);
 }
 
 // ===========================================================================
 // Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
-template <int K, bool FULL>
-__device__ __forceinline__ void fused_bf16_body(float* out, const PtrTable& src, const OutTable& codes, size_t n) {
+template <int K, int ET, bool FULL>
+__device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   f4 x[K];
 #pragma unroll
-  for (int r = 0; r < K; r++) x[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), i, n);
+  for (int r = 0; r < K; r++) x[r] = load_vals4_at<ET, FULL>(src.p[r], i, n);
   f4 a;
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -793,13 +858,13 @@ __device__ __forceinline__ void fused_bf16_body(float* out, const PtrTable& src,
     const f4 v = bf16_unpack4(w);
     a = r == 0 ? v : a + v;
   }
-  store4_at<FULL>(out, i, n, a);
+  store_vals4_at<ET, FULL>(out, i, n, a);
 }
 
-template <int K>
-__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(float* out, PtrTable src, OutTable codes, size_t n) {
-  if (group_full(kVecPerGroup, n)) fused_bf16_body<K, true>(out, src, codes, n);
-  else fused_bf16_body<K, false>(out, src, codes, n);
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTable src, OutTable codes, size_t n) {
+  if (group_full(kVecPerGroup, n)) fused_bf16_body<K, ET, true>(out, src, codes, n);
+  else fused_bf16_body<K, ET, false>(out, src, codes, n);
 }
 
 // ===========================================================================
@@ -1042,76 +1107,139 @@ hipError_t launch_reduce_typed(void* dst, const PtrTable& srcs, int k, size_t n,
   }
 }
 
-hipError_t launch_encode_bf16(uint16_t* codes, const float* src, size_t n, hipStream_t stream) {
+namespace {
+// One launcher body per element type ET; the exported launchers switch on
+// the type.  Accumulation into the output is offered for float32 only.
+template <int ET>
+hipError_t encode_bf16_t(uint16_t* codes, const void* src, size_t n, hipStream_t stream) {
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-  encode_bf16_kernel<<<grid, kThreads, 0, stream>>>(codes, src, n);
+  encode_bf16_kernel<ET><<<grid, kThreads, 0, stream>>>(codes, src, n);
   return hipGetLastError();
 }
 
-hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const float* src, size_t n, int scale_mode,
-                             hipStream_t stream) {
+template <int ET>
+hipError_t encode_fp8_t(uint8_t* codes, float* scales, const void* src, size_t n, int scale_mode,
+                        hipStream_t stream) {
   const size_t grid = grid_for(n, 16);  // 16 values per lane: a 256-lane group does 16 blocks
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-  encode_fp8_kernel<<<grid, kThreads, 0, stream>>>(codes, scales, src, n, scale_mode);
+  encode_fp8_kernel<ET><<<grid, kThreads, 0, stream>>>(codes, scales, src, n, scale_mode);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_bf16(float* acc, const PtrTable& codes, int k, size_t n, bool accumulate,
-                              hipStream_t stream) {
+template <int ET>
+hipError_t decode_bf16_t(void* acc, const PtrTable& codes, int k, size_t n, bool accumulate, hipStream_t stream) {
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-#define GB_CALL(K)                                                                          \
-  if (accumulate) decode_bf16_kernel<K, true><<<grid, kThreads, 0, stream>>>(acc, codes, n); \
-  else decode_bf16_kernel<K, false><<<grid, kThreads, 0, stream>>>(acc, codes, n);
+  if (accumulate && ET != GB_DTYPE_F32) return hipErrorInvalidValue;
+#define GB_CALL(K)                                                                                      \
+  if constexpr (ET == GB_DTYPE_F32) {                                                                   \
+    if (accumulate) decode_bf16_kernel<K, true, ET><<<grid, kThreads, 0, stream>>>(acc, codes, n);        \
+    else decode_bf16_kernel<K, false, ET><<<grid, kThreads, 0, stream>>>(acc, codes, n);                  \
+  } else {                                                                                              \
+    decode_bf16_kernel<K, false, ET><<<grid, kThreads, 0, stream>>>(acc, codes, n);                       \
+  }
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
 }
 
-hipError_t launch_decode_fp8(float* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
-                             bool accumulate, hipStream_t stream) {
+template <int ET>
+hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
+                        bool accumulate, hipStream_t stream) {
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-#define GB_CALL(K)                                                                                   \
-  if (accumulate) decode_fp8_kernel<K, true><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n); \
-  else decode_fp8_kernel<K, false><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);
+  if (accumulate && ET != GB_DTYPE_F32) return hipErrorInvalidValue;
+#define GB_CALL(K)                                                                                               \
+  if constexpr (ET == GB_DTYPE_F32) {                                                                            \
+    if (accumulate) decode_fp8_kernel<K, true, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n); \
+    else decode_fp8_kernel<K, false, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);          \
+  } else {                                                                                                       \
+    decode_fp8_kernel<K, false, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);             \
+  }
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
 }
 
-hipError_t launch_fused_bf16(float* out, const PtrTable& srcs, uint16_t* const* codes, int k, size_t n,
+template <int ET>
+hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_bf16_kernel<K, ET><<<grid, kThreads, 0, stream>>>(out, srcs, c, n);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const OutTable& s, int k, size_t n,
+                       int scale_mode, hipStream_t stream) {
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_fp8_kernel<K, ET><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, c, s, n, scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+#define GB_DISPATCH_ET(et, CALL)                      \
+  (void)hipGetLastError();                             \
+  switch (et) {                                        \
+    case GB_DTYPE_F32: return CALL(GB_DTYPE_F32);      \
+    case GB_DTYPE_F16: return CALL(GB_DTYPE_F16);      \
+    case GB_DTYPE_BF16: return CALL(GB_DTYPE_BF16);    \
+    case GB_DTYPE_F64: return CALL(GB_DTYPE_F64);      \
+    default: return hipErrorInvalidValue;              \
+  }
+}  // namespace
+
+hipError_t launch_encode_bf16(uint16_t* codes, const void* src, size_t n, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) encode_bf16_t<ET>(codes, src, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const void* src, size_t n, int scale_mode, int dtype,
+                             hipStream_t stream) {
+#define GB_CALL(ET) encode_fp8_t<ET>(codes, scales, src, n, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_decode_bf16(void* acc, const PtrTable& codes, int k, size_t n, bool accumulate, int dtype,
+                              hipStream_t stream) {
+#define GB_CALL(ET) decode_bf16_t<ET>(acc, codes, k, n, accumulate, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_decode_fp8(void* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
+                             bool accumulate, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) decode_fp8_t<ET>(acc, codes, scales, k, n, accumulate, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* codes, int k, size_t n, int dtype,
                              hipStream_t stream) {
   OutTable c = {};
   for (int r = 0; r < k; r++) c.p[r] = codes[r];
-  const size_t grid = grid_for(n, 4);
-  if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-#define GB_CALL(K) fused_bf16_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, c, n);
-  GB_DISPATCH_K(k, GB_CALL)
+#define GB_CALL(ET) fused_bf16_t<ET>(out, srcs, c, k, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
-  return hipGetLastError();
 }
 
-hipError_t launch_fused_fp8(float* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales,
-                            int k, size_t n, int scale_mode, hipStream_t stream) {
+hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales, int k,
+                            size_t n, int scale_mode, int dtype, hipStream_t stream) {
   OutTable c = {}, s = {};
   for (int r = 0; r < k; r++) {
     c.p[r] = codes[r];
     s.p[r] = scales[r];
   }
-  const size_t grid = grid_for(n, 16);
-  if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-#define GB_CALL(K) fused_fp8_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, c, s, n, scale_mode);
-  GB_DISPATCH_K(k, GB_CALL)
+#define GB_CALL(ET) fused_fp8_t<ET>(out, srcs, c, s, k, n, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
-  return hipGetLastError();
 }
 
 hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n,

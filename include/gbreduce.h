@@ -248,6 +248,51 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
                                     void* stream);
 
 /*
+ * Bridge compression of float16, bfloat16 and float64 tensors (README
+ * "Bridge compression": the bridged policies compress floating-point SUM and
+ * AVG, and the dequantized payloads are added in float32).  The island sum,
+ * of the tensor's type, is first taken to binary32 (exactly from float16 and
+ * bfloat16; rounded once to nearest-even from float64) and encoded exactly
+ * as a binary32 array is; the float32 total of the decoded payloads is
+ * rounded once to the tensor's type (nearest, ties to even, IEEE overflow to
+ * Inf; exact to float64).  dtype is GB_DTYPE_F32, F16, BF16 or F64
+ * (GB_ERR_UNSUPPORTED otherwise); arrays of dtype are 16-byte aligned.
+ *
+ * gb_encode — codes (and, for fp8, scales) of src (dtype[n]), as
+ *   gb_encode_bf16 (codec GB_CODEC_BF16; scales unused, may be NULL) or
+ *   gb_encode_fp8_e4m3_blockscaled (codec GB_CODEC_FP8_E4M3_B256) would
+ *   write for the binary32 values.  GB_ERR_UNSUPPORTED for codec NONE.
+ */
+gb_status gb_encode(int codec, int dtype, void* codes, float* scales,
+                    const void* src, size_t n, int scale_mode, void* stream);
+
+/*
+ * gb_decode_sum — dst (dtype[n]) = the rank-order float32 sum of the k
+ *   decoded payloads (as gb_decode_accumulate with accumulate 0), rounded once
+ *   to dtype.  codes, scales, k and codec as gb_decode_accumulate; codec NONE
+ *   (float32 payloads) only with dtype F32 (other types reduce exactly with
+ *   gb_reduce_typed).  dst must not overlap any payload.
+ */
+gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes,
+                        const float* const* scales, int k, size_t n, int codec,
+                        void* stream);
+
+/*
+ * gb_bucket_allreduce_local_typed — gb_bucket_allreduce_local over arrays of
+ *   dtype: out and srcs[r] hold dtype[n].  With a codec each rank's bucket is
+ *   encoded as gb_encode does (into the same workspace, of the same size, as
+ *   for float32) and out = the float32 total rounded once to dtype; without
+ *   one (GB_CODEC_NONE) out is the exact SUM of the type (gb_reduce_typed).
+ *   out may equal srcs[0].  Everything else as gb_bucket_allreduce_local.
+ */
+gb_status gb_bucket_allreduce_local_typed(int dtype, void* out,
+                                          const void* const* srcs, int k,
+                                          size_t n, size_t bucket_elems,
+                                          int codec, int scale_mode,
+                                          void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * Error feedback (README "Bridge compression": each bridge member keeps an
  * error-feedback residual per buffer, so the rounding error of one step is
  * carried into the next instead of accumulating).  The residual is a

@@ -146,6 +146,22 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
     (lambda L: L.gb_reduce_typed(ctypes.c_void_p(264), _arr(256), 1, 10, 4, 0, 1, None), 2, "dst"),
     (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256, 257), 2, 10, 5, 2, 1, None), 2, "srcs[1]"),
     (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 9, 10, 3, 0, 1, None), 1, "k = 9"),
+    (lambda L: L.gb_encode(0, 1, None, None, None, 10, 0, None), 3, "not bf16 or fp8"),
+    (lambda L: L.gb_encode(1, 6, None, None, None, 10, 0, None), 3, "not a floating-point type"),
+    (lambda L: L.gb_encode(2, 2, None, None, None, 10, 3, None), 3, "scale mode"),
+    (lambda L: L.gb_encode(2, 2, ctypes.c_void_p(256), ctypes.c_void_p(258), ctypes.c_void_p(256), 10, 0, None),
+     2, "scales"),
+    (lambda L: L.gb_encode(1, 3, ctypes.c_void_p(256), None, ctypes.c_void_p(264), 10, 0, None), 2, "src"),
+    (lambda L: L.gb_decode_sum(1, ctypes.c_void_p(256), _arr(256), None, 1, 10, 0, None), 3, "uncompressed"),
+    (lambda L: L.gb_decode_sum(4, ctypes.c_void_p(256), _arr(256), None, 1, 10, 1, None), 3, "floating-point"),
+    (lambda L: L.gb_decode_sum(2, ctypes.c_void_p(256), _arr(256), None, 1, 10, 2, None), 1, "scales array"),
+    (lambda L: L.gb_decode_sum(2, ctypes.c_void_p(256), _arr(256), None, 0, 10, 1, None), 1, "k = 0"),
+    (lambda L: L.gb_bucket_allreduce_local_typed(7, ctypes.c_void_p(256), _arr(256), 1, 1000, 256, 2, 0,
+                                                 ctypes.c_void_p(512), 1 << 20, None), 3, "floating-point"),
+    (lambda L: L.gb_bucket_allreduce_local_typed(1, ctypes.c_void_p(256), _arr(256), 1, 1000, 300, 2, 0,
+                                                 ctypes.c_void_p(512), 1 << 20, None), 1, "bucket_elems"),
+    (lambda L: L.gb_bucket_allreduce_local_typed(2, ctypes.c_void_p(256), _arr(256), 1, 1000, 256, 2, 0,
+                                                 ctypes.c_void_p(512), 100, None), 4, "needed"),
     (lambda L: L.gb_bucket_allreduce_local_ef(ctypes.c_void_p(256), _arr(256), _arr(512), 1, 1000, 256, 0, 0,
                                               None, 0, None), 3, "lossy codec"),
     (lambda L: L.gb_bucket_allreduce_local_ef(ctypes.c_void_p(256), _arr(256), _arr(520), 1, 1000, 256, 2, 0,
@@ -173,6 +189,9 @@ def test_zero_length_returns_ok_without_pointers(gb):
     L = gb._lib
     assert L.gb_reduce_sum(None, None, 2, 0, None) == 0
     assert L.gb_reduce_typed(None, None, 2, 0, 7, 2, 1, None) == 0
+    assert L.gb_encode(2, 1, None, None, None, 0, 0, None) == 0
+    assert L.gb_decode_sum(3, None, None, None, 2, 0, 2, None) == 0
+    assert L.gb_bucket_allreduce_local_typed(2, None, None, 2, 0, 256, 2, 0, None, 0, None) == 0
     assert L.gb_encode_bf16(None, None, 0, None) == 0
     assert L.gb_encode_fp8_e4m3_blockscaled(None, None, None, 0, 0, None) == 0
     assert L.gb_decode_accumulate(None, None, None, 3, 0, 2, 0, None) == 0

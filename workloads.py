@@ -96,6 +96,22 @@ def typed_ranks(k, n, dtype, base_seed=BASE_SEED):
     return [typed(n, dtype, base_seed + r) for r in range(k)]
 
 
+def device_gradients_typed(n, seed, device, dtype):
+    """device_gradients carried into float16 (torch's conversion), bfloat16
+    (the top 16 bits of each float32 draw: truncated, a draw and not a
+    rounding under test) or float64 (widened)."""
+    import torch
+
+    x = device_gradients(n, seed, device)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.half()
+    if dtype == "f64":
+        return x.double()
+    return (x.view(torch.int32) >> 16).to(torch.int16).view(torch.bfloat16)
+
+
 def special_values():
     """float32 values where rounding and the format edges are decided."""
     u = np.array([
