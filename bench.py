@@ -558,7 +558,7 @@ class Sweep(Workload):
     def timed_kernel(self):
         n = self.sizes[-1]
         if self.dt != "f32":
-            name = f"reduce_typed_kernel<{self.gb.GB_DTYPE_OF[self.dt]},{self.op}>"
+            name = f"reduce_typed_kernel<{self.gb.GB_DTYPE_OF[self.dt]},2,{self.op}>"
         elif self.op == 0:
             name = "reduce_sum_kernel<2,false>"
         else:
