@@ -108,6 +108,36 @@ def nblocks(n):
     return (n + 255) // 256
 
 
+class Unit:
+    """One independent piece of the CPU baseline: `compute` runs the oracle on
+    inputs already copied to the host (the timed part), `check` compares its
+    result with the GPU's output (untimed); `nbytes` counts the piece's
+    algorithmic bytes by the workload's own formula."""
+
+    def __init__(self, nbytes, compute, check):
+        self.nbytes, self.compute, self.check = nbytes, compute, check
+        self.result = None
+
+
+def host_values(torch, t):
+    """A device tensor's values on the host; 16-bit floats as raw codes."""
+    import numpy as np
+    if t.element_size() == 2 and t.is_floating_point():
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def same_bits(got, want):
+    """Bit-identical arrays, NaN compared as NaN."""
+    import numpy as np
+    if got.dtype.kind == "f" or want.dtype.kind == "f":
+        gn, wn = np.isnan(got), np.isnan(want)
+        if not (gn == wn).all():
+            return False
+        got, want = got[~gn], want[~wn]
+    return got.tobytes() == want.tobytes()
+
+
 class DdpBuckets(Workload):
     name = "ddp_1b_buckets"
 
@@ -197,40 +227,39 @@ class DdpBuckets(Workload):
                 "per_bucket_calls_eager_ms": round(eager_ms, 4),
                 "per_bucket_outputs_match": eager_ok and replay_ok}
 
-    def cpu_sample(self, budget):
-        """Run the oracle on the first buckets; compare with the GPU's."""
-        from oracle import oracle as O
-        import numpy as np
-        torch = self.torch
-        torch.cuda.synchronize()
-        done_bytes, t_oracle, nb, ok = 0, 0.0, 0, True
+    CPU_CHUNK = 1_638_400  # a quarter of a bucket (6,400 blocks)
 
-        def host(t):  # 16-bit floats as their raw codes
-            return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.element_size() == 2 else t.cpu().numpy()
-        for start, length in self.W.ddp_buckets():
-            xs = [host(t[start:start + length]) for t in self.x]
-            t0 = time.perf_counter()
-            if self.dt == "f32":
-                want, codes, scales = O.bucket_allreduce(xs, self.bucket, O.CODEC_FP8, self.mode)
-            else:
-                want, codes, scales = O.bucket_allreduce_typed(xs, self.dt, self.bucket, O.CODEC_FP8, self.mode)
-            t_oracle += time.perf_counter() - t0
-            done_bytes += self.bytes_for(length)
-            nb += 1
-            got = host(self.out[start:start + length])
-            gn = np.isnan(got) if got.dtype.kind == "f" else np.zeros(got.size, bool)
-            wn = np.isnan(want) if want.dtype.kind == "f" else np.zeros(want.size, bool)
-            ok &= bool((gn == wn).all()) and bool((got[~gn].tobytes() == want[~wn].tobytes()))
-            for r in range(self.k):
-                c0 = r * self.lay["codes_stride"] + start
-                s0 = self.lay["scales_offset"] + r * self.lay["scales_stride"] + 4 * (start // 256)
-                gc = self.ws[c0:c0 + length].cpu().numpy()
-                gs = self.ws[s0:s0 + 4 * nblocks(length)].cpu().numpy().view(np.uint32)
-                ok &= bool((gc == codes[r]).all()) and bool((gs == scales[r].view(np.uint32)).all())
-            if t_oracle >= budget:
-                break
-        sample = f"first {nb} of {len(self.W.ddp_buckets())} buckets ({nb * self.bucket:,} values x {self.k} ranks)"
-        return done_bytes, t_oracle, sample, ok
+    def cpu_units(self):
+        """Quarter-bucket pieces of the stream, in order; each is the oracle's
+        bucket stream over that piece (pieces start on block boundaries, so
+        their blocks are the whole stream's)."""
+        from oracle import oracle as O
+        torch = self.torch
+
+        def make(start, length):
+            def factory():
+                xs = [host_values(torch, t[start:start + length]) for t in self.x]
+                if self.dt == "f32":
+                    compute = lambda: O.bucket_allreduce(xs, self.bucket, O.CODEC_FP8, self.mode)
+                else:
+                    compute = lambda: O.bucket_allreduce_typed(xs, self.dt, self.bucket, O.CODEC_FP8, self.mode)
+
+                def check(res):
+                    want, codes, scales = res
+                    ok = same_bits(host_values(torch, self.out[start:start + length]), want)
+                    for r in range(self.k):
+                        c0 = r * self.lay["codes_stride"] + start
+                        s0 = self.lay["scales_offset"] + r * self.lay["scales_stride"] + 4 * (start // 256)
+                        ok &= same_bits(self.ws[c0:c0 + length].cpu().numpy(), codes[r])
+                        ok &= same_bits(self.ws[s0:s0 + 4 * nblocks(length)].cpu().numpy(), scales[r].view("uint8"))
+                    return ok
+                return Unit(self.bytes_for(length), compute, check)
+            return factory
+
+        factories = [make(s + o, min(self.CPU_CHUNK, l - o))
+                     for s, l in self.W.ddp_buckets() for o in range(0, l, self.CPU_CHUNK)]
+        return factories, lambda m: (f"first {m} quarter-buckets ({m * self.CPU_CHUNK:,} values x {self.k} ranks) "
+                                     f"of {len(factories)}")
 
 
 class DdpBucketsEF(DdpBuckets):
@@ -258,38 +287,39 @@ class DdpBucketsEF(DdpBuckets):
     def extra(self, time_region, reps):
         return {}
 
-    def cpu_sample(self, budget):
-        """One more step checked against the oracle from the residuals it starts
-        from, on the first buckets."""
+    def cpu_units(self):
+        """One more step of the stream, checked against the oracle from the
+        residuals it starts from, on the first quarter-buckets (their
+        residuals are captured before that step)."""
         from oracle import oracle as O
-        import numpy as np
         torch = self.torch
-        torch.cuda.synchronize()
-        buckets = []
-        t_est = 0.0
-        for start, length in self.W.ddp_buckets():
-            buckets.append((start, length))
-            t_est += 2.2  # about 2.2 s of oracle work per 25 MiB bucket of 4 ranks
-            if t_est >= budget:
-                break
-        before = [[r[s:s + l].cpu().numpy() for r in self.res] for s, l in buckets]
+        pieces = []
+        for s, l in self.W.ddp_buckets():
+            for o in range(0, l, self.CPU_CHUNK):
+                pieces.append((s + o, min(self.CPU_CHUNK, l - o)))
+        pieces = pieces[:24]  # about 0.55 s of oracle work each
+        before = [[r[s:s + l].cpu().numpy() for r in self.res] for s, l in pieces]
         self.step()
         torch.cuda.synchronize()
-        done_bytes, t_oracle, ok = 0, 0.0, True
-        for (start, length), res0 in zip(buckets, before):
-            xs = [t[start:start + length].cpu().numpy() for t in self.x]
-            t0 = time.perf_counter()
-            want, codes, scales, res1 = O.bucket_allreduce_ef(xs, res0, self.bucket, O.CODEC_FP8, self.mode)
-            t_oracle += time.perf_counter() - t0
-            done_bytes += self.bytes_for(length)
-            ok &= bool((self.out[start:start + length].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
-            for r in range(self.k):
-                got = self.res[r][start:start + length].cpu().numpy().view(np.uint32)
-                ok &= bool((got == res1[r].view(np.uint32)).all())
-                c0 = r * self.lay["codes_stride"] + start
-                ok &= bool((self.ws[c0:c0 + length].cpu().numpy() == codes[r]).all())
-        sample = f"one step of the first {len(buckets)} of {len(self.W.ddp_buckets())} buckets"
-        return done_bytes, t_oracle, sample, ok
+
+        def make(i):
+            start, length = pieces[i]
+
+            def factory():
+                xs = [t[start:start + length].cpu().numpy() for t in self.x]
+                compute = lambda: O.bucket_allreduce_ef(xs, before[i], self.bucket, O.CODEC_FP8, self.mode)
+
+                def check(res):
+                    want, codes, scales, res1 = res
+                    ok = same_bits(self.out[start:start + length].cpu().numpy(), want)
+                    for r in range(self.k):
+                        ok &= same_bits(self.res[r][start:start + length].cpu().numpy(), res1[r])
+                        c0 = r * self.lay["codes_stride"] + start
+                        ok &= same_bits(self.ws[c0:c0 + length].cpu().numpy(), codes[r])
+                    return ok
+                return Unit(self.bytes_for(length), compute, check)
+            return factory
+        return [make(i) for i in range(len(pieces))], lambda m: f"one step of the first {m} quarter-buckets"
 
 
 class Staged(Workload):
@@ -379,21 +409,31 @@ class Staged(Workload):
                 "staged_ms_by_chunk_elems": sweep,
                 "d2h_copy_gbs_one_payload": round(self.payload() / (copy_ms * 1e-3) / 1e9, 2)}
 
-    def cpu_sample(self, budget):
+    def cpu_units(self):
+        """The staged step's arithmetic (rank 0's fp8 encode; decode-and-add of
+        the four payloads) on 2^18-value pieces of the first 2^22 values."""
         from oracle import oracle as O
-        import numpy as np
         self.step()
         self.torch.cuda.synchronize()
-        m = 1 << 22
-        t0 = time.perf_counter()
-        wc, ws = O.encode_fp8(self.xh[0][:m], self.mode)
-        enc = [O.encode_fp8(a[:m], self.mode) for a in self.xh]
-        want = O.decode_accumulate([c for c, _ in enc], [s for _, s in enc], O.CODEC_FP8)
-        t = time.perf_counter() - t0
-        ok = bool((self.ch[:m].numpy() == wc).all()) and bool((self.sh[:m // 256].numpy() == ws).all())
-        ok &= bool((self.acc[:m].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
-        p = m + 4 * nblocks(m)
-        return 4 * m + 2 * p + 2 * self.k * p + 4 * m, t, f"first {m:,} values of each rank", ok
+        piece = 1 << 18
+
+        def make(start):
+            def factory():
+                xs = [a[start:start + piece] for a in self.xh]
+
+                def compute():
+                    enc = [O.encode_fp8(a, self.mode) for a in xs]
+                    return enc, O.decode_accumulate([c for c, _ in enc], [s for _, s in enc], O.CODEC_FP8)
+
+                def check(res):
+                    enc, want = res
+                    ok = same_bits(self.ch[start:start + piece].numpy(), enc[0][0])
+                    ok &= same_bits(self.sh[start // 256:(start + piece) // 256].numpy(), enc[0][1])
+                    return ok and same_bits(self.acc[start:start + piece].cpu().numpy(), want)
+                p = piece + 4 * nblocks(piece)
+                return Unit(4 * piece + 2 * p + 2 * self.k * p + 4 * piece, compute, check)
+            return factory
+        return [make(o) for o in range(0, 1 << 22, piece)], lambda m: f"first {m * piece:,} values of each rank"
 
 
 class Gradients256(Workload):
@@ -434,22 +474,32 @@ class Gradients256(Workload):
         per = 4 * self.n + self.n + 4 * nblocks(self.n)
         return ("encode_fp8_kernel<0>", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
-    def cpu_sample(self, budget):
+    def cpu_units(self):
+        """4 fp8 encodes and the decode-and-add on 2^18-value pieces of every
+        rank, in order."""
         from oracle import oracle as O
-        import numpy as np
-        m = 1 << 22  # a prefix of every rank (4 Mi values = 16 MiB each)
-        self.torch.cuda.synchronize()
-        xs = [a[:m] for a in self.xh]
-        t0 = time.perf_counter()
-        enc = [O.encode_fp8(a, self.mode) for a in xs]
-        want = O.decode_accumulate([c for c, _ in enc], [s for _, s in enc], O.CODEC_FP8)
-        t = time.perf_counter() - t0
-        ok = bool((self.out[:m].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
-        for r in range(self.k):
-            ok &= bool((self.codes[r][:m].cpu().numpy() == enc[r][0]).all())
-            ok &= bool((self.scales[r][:m // 256].cpu().numpy().view(np.uint32) == enc[r][1].view(np.uint32)).all())
-        p = m + 4 * nblocks(m)
-        return self.k * (4 * m + p) + self.k * p + 4 * m, t, f"first {m:,} values of each of the {self.k} ranks", ok
+        piece = 1 << 18
+
+        def make(start):
+            def factory():
+                xs = [a[start:start + piece] for a in self.xh]
+
+                def compute():
+                    enc = [O.encode_fp8(a, self.mode) for a in xs]
+                    return enc, O.decode_accumulate([c for c, _ in enc], [s for _, s in enc], O.CODEC_FP8)
+
+                def check(res):
+                    enc, want = res
+                    ok = same_bits(self.out[start:start + piece].cpu().numpy(), want)
+                    for r in range(self.k):
+                        ok &= same_bits(self.codes[r][start:start + piece].cpu().numpy(), enc[r][0])
+                        ok &= same_bits(self.scales[r][start // 256:(start + piece) // 256].cpu().numpy(), enc[r][1])
+                    return ok
+                p = piece + 4 * nblocks(piece)
+                return Unit(self.k * (4 * piece + p) + self.k * p + 4 * piece, compute, check)
+            return factory
+        return ([make(o) for o in range(0, self.n, piece)],
+                lambda m: f"first {m * piece:,} values of each of the {self.k} ranks")
 
 
 class Gradients64(Workload):
@@ -485,21 +535,31 @@ class Gradients64(Workload):
     def timed_kernel(self):
         return ("encode_bf16_kernel<0>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
-    def cpu_sample(self, budget):
+    def cpu_units(self):
+        """4 bf16 encodes and the decode-and-add on 2^18-value pieces."""
         from oracle import oracle as O
-        import numpy as np
-        m = 1 << 22
-        self.torch.cuda.synchronize()
-        xs = [a[:m] for a in self.xh]
-        t0 = time.perf_counter()
-        codes = [O.encode_bf16(a) for a in xs]
-        want = O.decode_accumulate(codes, None, O.CODEC_BF16)
-        t = time.perf_counter() - t0
-        ok = bool((self.out[:m].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all())
-        for r in range(self.k):
-            got = self.codes[r][:m].view(self.torch.int16).cpu().numpy().view(np.uint16)
-            ok &= bool((got == codes[r]).all())
-        return self.k * 8 * m + 4 * m, t, f"first {m:,} values of each of the {self.k} ranks", ok
+        torch = self.torch
+        piece = 1 << 18
+
+        def make(start):
+            def factory():
+                xs = [a[start:start + piece] for a in self.xh]
+
+                def compute():
+                    codes = [O.encode_bf16(a) for a in xs]
+                    return codes, O.decode_accumulate(codes, None, O.CODEC_BF16)
+
+                def check(res):
+                    codes, want = res
+                    ok = same_bits(self.out[start:start + piece].cpu().numpy(), want)
+                    for r in range(self.k):
+                        ok &= same_bits(host_values(torch, self.codes[r][start:start + piece].view(torch.int16))
+                                        .view("uint16"), codes[r])
+                    return ok
+                return Unit(self.k * 8 * piece + 4 * piece, compute, check)
+            return factory
+        return ([make(o) for o in range(0, self.n, piece)],
+                lambda m: f"first {m * piece:,} values of each of the {self.k} ranks")
 
 
 class Sweep(Workload):
@@ -565,35 +625,44 @@ class Sweep(Workload):
             name = f"reduce_op_kernel<2,{self.op}>"
         return (name, 3 * self.esize * n, 1, lambda: self.reduce(n))
 
-    def cpu_sample(self, budget):
-        from oracle import oracle as O
-        import numpy as np
-        self.torch.cuda.synchronize()
-        t, ok = 0.0, True
+    def extra(self, time_region, reps):
+        """Every size of the sweep timed alone: the median of `reps` calls, a
+        1 GiB buffer rewritten (untimed) before each so that no call finds its
+        inputs in the 256 MB last-level cache; microseconds and GB/s.  Small
+        sizes are latency, the large ones bandwidth."""
+        torch = self.torch
+        scratch = torch.empty((1 << 30) // 4, dtype=torch.float32, device=self.dev)
+        us, gbs = {}, {}
         for n in self.sizes:
-            t0 = time.perf_counter()
-            if self.dt == "f32":
-                want = O.reduce(self.xh[n], self.op, 2)
-            else:
-                want = O.reduce_typed(self.xh[n], self.dt, self.op, 2)
-            t += time.perf_counter() - t0
-            out = self.out[n]
-            if self.dt in ("f16", "bf16"):
-                got = out.view(self.torch.int16).cpu().numpy().view(np.uint16)
-                vals = out.float().cpu().numpy()
-                nan_g = np.isnan(vals)
-                wt = self.torch.from_numpy(want.view(np.int16)).view(out.dtype).float().numpy()
-                nan_w = np.isnan(wt)
-            else:
-                got = out.cpu().numpy()
-                nan_g = np.isnan(got) if got.dtype.kind == "f" else np.zeros(got.size, bool)
-                nan_w = np.isnan(want) if want.dtype.kind == "f" else np.zeros(want.size, bool)
-            ok &= bool((nan_g == nan_w).all())
-            if got.dtype.kind == "f":
-                got, want = got.view(np.uint32 if got.itemsize == 4 else np.uint64), \
-                    want.view(np.uint32 if want.itemsize == 4 else np.uint64)
-            ok &= bool((got[~nan_g] == want[~nan_w]).all())
-        return self.step_bytes(), t, "the whole sweep", ok
+            t = []
+            for i in range(max(5, reps)):
+                scratch.fill_(float(i))
+                t.append(time_region(lambda: self.reduce(n), 1))
+            t.sort()
+            med = t[len(t) // 2]
+            us[str(n)] = round(med * 1e3, 2)
+            gbs[str(n)] = round(3 * self.esize * n / (med * 1e-3) / 1e9, 1)
+        del scratch
+        return {"per_size_us_cache_flushed": us, "per_size_gbs_cache_flushed": gbs}
+
+    def cpu_units(self):
+        """Every size of the sweep, the larger ones in 2^20-value pieces."""
+        from oracle import oracle as O
+        torch = self.torch
+        piece = 1 << 20
+
+        def make(n, start, length):
+            def factory():
+                xs = [a[start:start + length] for a in self.xh[n]]
+                if self.dt == "f32":
+                    compute = lambda: O.reduce(xs, self.op, 2)
+                else:
+                    compute = lambda: O.reduce_typed(xs, self.dt, self.op, 2)
+                check = lambda want: same_bits(host_values(torch, self.out[n][start:start + length]), want)
+                return Unit(3 * self.esize * length, compute, check)
+            return factory
+        factories = [make(n, o, min(piece, n - o)) for n in self.sizes for o in range(0, n, piece)]
+        return factories, lambda m: "the whole sweep" if m == len(factories) else f"{m} of {len(factories)} pieces"
 
 
 class TwoRank(Workload):
@@ -628,17 +697,22 @@ class TwoRank(Workload):
     def timed_kernel(self):
         return ("reduce_sum_kernel<2,false>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
 
-    def cpu_sample(self, budget):
+    def cpu_units(self):
+        """Sum, bf16 encode of the sum and its decode, on 2^18-value pieces."""
         from oracle import oracle as O
-        import numpy as np
-        self.torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        s = O.reduce_sum(self.xh)
-        c = O.encode_bf16(s)
-        d = O.decode_accumulate([c], None, O.CODEC_BF16)
-        t = time.perf_counter() - t0
-        ok = bool((self.dec.cpu().numpy().view(np.uint32) == d.view(np.uint32)).all())
-        return self.step_bytes(), t, "the whole workload", ok
+        piece = 1 << 18
+
+        def make(start):
+            def factory():
+                xs = [a[start:start + piece] for a in self.xh]
+
+                def compute():
+                    s = O.reduce_sum(xs)
+                    return O.decode_accumulate([O.encode_bf16(s)], None, O.CODEC_BF16)
+                check = lambda want: same_bits(self.dec[start:start + piece].cpu().numpy(), want)
+                return Unit(24 * piece, compute, check)
+            return factory
+        return [make(o) for o in range(0, self.n, piece)], lambda m: f"first {m * piece:,} values of both ranks"
 
 
 WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, TwoRank, DdpBucketsEF, Staged)}
@@ -676,6 +750,79 @@ def time_region(torch, stream, fn, reps):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget):
+    """The oracle on a bounded sample of the workload: units are taken in order
+    (their inputs copied to the host untimed) until about `budget` seconds of
+    single-threaded oracle work, then the same units are run again across the
+    host's cores (the oracle is C; ctypes releases the GIL), and every unit's
+    result is compared with the GPU's output."""
+    import concurrent.futures as cf
+    wl.torch.cuda.synchronize()
+    factories, describe = wl.cpu_units()
+    units, t_one = [], 0.0
+    for factory in factories:
+        u = factory()
+        t0 = time.perf_counter()
+        u.result = u.compute()
+        t_one += time.perf_counter() - t0
+        units.append(u)
+        if t_one >= budget:
+            break
+    ok = all(bool(u.check(u.result)) for u in units)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    with cf.ThreadPoolExecutor(cores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda u: u.compute(), units))
+        t_all = time.perf_counter() - t0
+    nbytes = sum(u.nbytes for u in units)
+    return {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": describe(len(units)), "seconds": round(t_all, 3),
+            "single_core": {"value": round(nbytes / t_one / 1e9, 4), "seconds": round(t_one, 3)},
+            "cpu_model": cpu_model(), "gpu_matches_oracle_on_sample": ok}
+
+
+def copy_ceiling(torch, gb, stream, reps=5):
+    """GB/s of plain 1 GiB device copies: the library's own streaming copy
+    (gb_reduce_sum with one source) and the runtime's device-to-device copy
+    (torch copy_, a hipMemcpyDtoD), each reading and writing 1 GiB."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    gb.gb_reduce_sum(dst, [src])
+    dst.copy_(src)
+    lib_ms = time_region(torch, stream, lambda: gb.gb_reduce_sum(dst, [src]), reps) / reps
+    rt_ms = time_region(torch, stream, lambda: dst.copy_(src), reps) / reps
+    del src, dst
+    return {"library_copy_gbs": round(2 * 4 * n / (lib_ms * 1e-3) / 1e9, 1),
+            "hipMemcpyDtoD_gbs": round(2 * 4 * n / (rt_ms * 1e-3) / 1e9, 1), "bytes_each_way": 4 * n}
+
+
+def step_distribution(torch, stream, fn, reps):
+    """Per-step milliseconds, each step timed alone with HIP events, a 1 GiB
+    buffer rewritten (untimed) before each so no step starts from a warm
+    last-level cache; p10 / p50 / p90."""
+    scratch = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda:0")
+    times = []
+    for i in range(reps):
+        scratch.fill_(float(i))
+        times.append(time_region(torch, stream, fn, 1))
+    del scratch
+    times.sort()
+    q = lambda f: times[min(len(times) - 1, int(f * (len(times) - 1) + 0.5))]
+    return {"reps": reps, "p10_ms": round(q(0.1), 4), "p50_ms": round(q(0.5), 4), "p90_ms": round(q(0.9), 4),
+            "cache_flushed": True}
 
 
 def main():
@@ -727,13 +874,18 @@ def main():
     log(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} GB/s; {kname}: {kms * 1e3:.2f} us/launch, "
         f"{achieved:.1f} GB/s")
 
+    dist = step_distribution(torch, wl.stream, wl.step, max(5, min(args.steps, 50)))
+    log(f"[bench] per step (cache flushed): p10 {dist['p10_ms']} p50 {dist['p50_ms']} p90 {dist['p90_ms']} ms")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on a sample")
-        sb, st, sample, ok = wl.cpu_sample(args.cpu_seconds)
-        cpu = {"value": round(sb / st / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": sample, "seconds": round(st, 2), "gpu_matches_oracle_on_sample": ok}
-        log(f"[bench] oracle {sb / st / 1e9:.3f} GB/s over {sample}; GPU output matches: {ok}")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']} GB/s on {cpu['cores']} cores ({cpu['single_core']['value']} on one) "
+            f"over {cpu['sample']}; GPU output matches: {cpu['gpu_matches_oracle_on_sample']}")
+
+    ceiling = copy_ceiling(torch, gb, wl.stream)
+    log(f"[bench] copy ceiling: {ceiling}")
 
     extra = {}
     if hasattr(wl, "extra"):
@@ -756,7 +908,11 @@ def main():
         "config": dict(wl.config, **extra),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(kname, wl.name),
-                     "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3)},
+                     "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3),
+                     "frac_of_copy_ceiling": round(achieved / max(ceiling["library_copy_gbs"],
+                                                                  ceiling["hipMemcpyDtoD_gbs"]), 4)},
+        "copy_ceiling": ceiling,
+        "step_distribution": dist,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
