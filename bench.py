@@ -720,14 +720,24 @@ WORKLOADS = {c.name: c for c in (DdpBuckets, Gradients256, Gradients64, Sweep, T
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+def kernel_sources_sha256():
+    """sha256 over the kernel sources (gb_device.h and every .hip file, by name
+    in sorted order: each name, a NUL, its bytes, a NUL)."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "gradient_all_reduce_amd", "csrc")
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + [os.path.join(csrc, "gb_device.h")]):
+        h.update(os.path.basename(path).encode() + b"\0" + open(path, "rb").read() + b"\0")
+    return h.hexdigest()
+
+
 def profiled_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 counter
     summaries under profiles/, or None when none was taken on the kernel
     source as it is now (the summary records the source's sha256)."""
     import glob
-    import hashlib
-    src = os.path.join(ROOT, "gradient_all_reduce_amd", "csrc", "gb_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = kernel_sources_sha256()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(path):
             if not line.startswith("traffic "):

@@ -4,6 +4,7 @@ The library links the HIP runtime by its soname (libamdhip64.so.7); in a
 process that has imported torch first, the dynamic loader reuses the runtime
 torch already loaded, so both share one HIP runtime and one device context.
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -13,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgbreduce.so")
-SOURCES = ["gb_kernels.hip", "gb_api.cpp"]
+# The kernels are split over several sources so that they compile in parallel.
+SOURCES = ["gb_reduce.hip", "gb_codec_fp8.hip", "gb_codec_bf16.hip", "gb_ef.hip", "gb_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: no multiply-add fusion, so decode (multiply) and add
@@ -30,16 +32,20 @@ FLAGS = [
 
 
 def build(verbose=False):
-    """Compile every source and link the shared library; return its path."""
-    objs = []
-    for src in SOURCES:
+    """Compile every source (in parallel) and link the shared library; return
+    its path."""
+    def compile_one(src):
         obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+        return obj
+
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

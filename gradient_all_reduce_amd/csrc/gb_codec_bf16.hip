@@ -1,0 +1,136 @@
+// gb_codec_bf16.hip — the bf16 bridge codec of libgbreduce: encode,
+// decode-and-accumulate and the fused bucket pass, over every codec element type.
+#include "gb_device.h"
+
+namespace gb {
+namespace {
+
+// ===========================================================================
+// bf16 encode and decode-accumulate: one 4-value vector per lane, so each
+// instruction of a wavefront loads 1 KiB of fp32 and stores 512 bytes of
+// codes (or the reverse), contiguously.
+// ===========================================================================
+template <int ET, bool FULL>
+__device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const void* src, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (!FULL && i >= n) return;
+  store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(load_vals4_at<ET, FULL>(src, i, n)));
+}
+
+template <int ET>
+__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const void* src, size_t n) {
+  if (group_full(kVecPerGroup, n)) encode_bf16_body<ET, true>(codes, src, n);
+  else encode_bf16_body<ET, false>(codes, src, n);
+}
+
+template <int K, bool ACC, int ET, bool FULL>
+__device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (!FULL && i >= n) return;
+  u2 w[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) w[r] = load_bf16_4_at<FULL>(static_cast<const uint16_t*>(codes.p[r]), i, n);
+  f4 a;
+  if (ACC) a = load_vals4_at<ET, FULL>(acc, i, n);
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    const f4 v = bf16_unpack4(w[r]);
+    a = (!ACC && r == 0) ? v : a + v;
+  }
+  store_vals4_at<ET, FULL>(acc, i, n, a);
+}
+
+template <int K, bool ACC, int ET>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTable codes, size_t n) {
+  if (group_full(kVecPerGroup, n)) decode_bf16_body<K, ACC, ET, true>(acc, codes, n);
+  else decode_bf16_body<K, ACC, ET, false>(acc, codes, n);
+}
+
+// ===========================================================================
+// Fused bf16 bucket pass, one 4-value vector per lane.
+// ===========================================================================
+template <int K, int ET, bool FULL>
+__device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (!FULL && i >= n) return;
+  f4 x[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) x[r] = load_vals4_at<ET, FULL>(src.p[r], i, n);
+  f4 a;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    const u2 w = bf16_pack4(x[r]);
+    store_bf16_4_at<FULL>(static_cast<uint16_t*>(codes.p[r]), i, n, w);
+    const f4 v = bf16_unpack4(w);
+    a = r == 0 ? v : a + v;
+  }
+  store_vals4_at<ET, FULL>(out, i, n, a);
+}
+
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTable src, OutTable codes, size_t n) {
+  if (group_full(kVecPerGroup, n)) fused_bf16_body<K, ET, true>(out, src, codes, n);
+  else fused_bf16_body<K, ET, false>(out, src, codes, n);
+}
+
+// Launcher bodies, one per element type ET.
+template <int ET>
+hipError_t encode_bf16_t(uint16_t* codes, const void* src, size_t n, hipStream_t stream) {
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
+  encode_bf16_kernel<ET><<<grid, kThreads, 0, stream>>>(codes, src, n);
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t decode_bf16_t(void* acc, const PtrTable& codes, int k, size_t n, bool accumulate, hipStream_t stream) {
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
+  if (accumulate && ET != GB_DTYPE_F32) return hipErrorInvalidValue;
+#define GB_CALL(K)                                                                                      \
+  if constexpr (ET == GB_DTYPE_F32) {                                                                   \
+    if (accumulate) decode_bf16_kernel<K, true, ET><<<grid, kThreads, 0, stream>>>(acc, codes, n);        \
+    else decode_bf16_kernel<K, false, ET><<<grid, kThreads, 0, stream>>>(acc, codes, n);                  \
+  } else {                                                                                              \
+    decode_bf16_kernel<K, false, ET><<<grid, kThreads, 0, stream>>>(acc, codes, n);                       \
+  }
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_bf16_kernel<K, ET><<<grid, kThreads, 0, stream>>>(out, srcs, c, n);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_bf16(uint16_t* codes, const void* src, size_t n, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) encode_bf16_t<ET>(codes, src, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_decode_bf16(void* acc, const PtrTable& codes, int k, size_t n, bool accumulate, int dtype,
+                              hipStream_t stream) {
+#define GB_CALL(ET) decode_bf16_t<ET>(acc, codes, k, n, accumulate, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* codes, int k, size_t n, int dtype,
+                             hipStream_t stream) {
+  OutTable c = {};
+  for (int r = 0; r < k; r++) c.p[r] = codes[r];
+#define GB_CALL(ET) fused_bf16_t<ET>(out, srcs, c, k, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+}  // namespace gb

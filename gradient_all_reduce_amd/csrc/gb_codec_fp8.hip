@@ -1,0 +1,192 @@
+// gb_codec_fp8.hip — the fp8 (OCP E4M3, one scale per 256 values) bridge
+// codec of libgbreduce: encode, decode-and-accumulate and the fused bucket
+// pass, over every codec element type.
+#include "gb_device.h"
+
+namespace gb {
+namespace {
+
+// ===========================================================================
+// fp8 encode: one DPP row per 256-value block.
+// ===========================================================================
+template <int ET, bool FULL>
+__device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, const void* src, size_t n,
+                                                int mode) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t col = lane & 15u;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  f4 x[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) x[j] = load_vals4_at<ET, FULL>(src, lane_elem(block, j, col), n);
+  uint32_t w[4];
+  const float s = encode_block16(x, mode, w);  // all 64 lanes take part
+  if (!FULL && block * kBlock >= n) return;
+  if (col == 0u) scales[block] = s;
+#pragma unroll
+  for (int j = 0; j < 4; j++) store_codes4_at<FULL>(codes, lane_elem(block, j, col), n, w[j]);
+}
+
+template <int ET>
+__global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const void* src,
+                                                               size_t n, int mode) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) encode_fp8_body<ET, true>(codes, scales, src, n, mode);
+  else encode_fp8_body<ET, false>(codes, scales, src, n, mode);
+}
+
+// ===========================================================================
+// fp8 decode-accumulate over K payloads: one DPP row per block, each rank's
+// block scale read once per lane.
+// ===========================================================================
+template <int K, bool ACC, int ET, bool FULL>
+__device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes, const PtrTable& scales,
+                                                size_t n) {
+  const uint32_t col = threadIdx.x & 15u;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  if (!FULL && block * kBlock >= n) return;
+  uint32_t w[K][4];
+  float s[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    const uint8_t* c = static_cast<const uint8_t*>(codes.p[r]);
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[r][j] = load_codes4_at<FULL>(c, lane_elem(block, j, col), n);
+    s[r] = static_cast<const float*>(scales.p[r])[block];
+  }
+  f4 a[4];
+  if (ACC) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) a[j] = load_vals4_at<ET, FULL>(acc, lane_elem(block, j, col), n);
+  }
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f4 v = e4m3_unpack4(w[r][j]) * s[r];
+      a[j] = (!ACC && r == 0) ? v : a[j] + v;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(acc, lane_elem(block, j, col), n, a[j]);
+}
+
+template <int K, bool ACC, int ET>
+__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTable codes, PtrTable scales,
+                                                               size_t n) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) decode_fp8_body<K, ACC, ET, true>(acc, codes, scales, n);
+  else decode_fp8_body<K, ACC, ET, false>(acc, codes, scales, n);
+}
+
+// ===========================================================================
+// Fused fp8 bucket pass: read each rank's block once, write its payload
+// (codes, scale), decode those codes and add them in rank order.
+// ===========================================================================
+template <int K, int ET, bool FULL>
+__device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, const OutTable& codes,
+                                               const OutTable& scales, size_t n, int mode) {
+  const uint32_t col = threadIdx.x & 15u;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  f4 x[K][4];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) x[r][j] = load_vals4_at<ET, FULL>(src.p[r], lane_elem(block, j, col), n);
+  }
+  const bool live = FULL || block * kBlock < n;
+  f4 a[4];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    uint32_t w[4];
+    const float s = encode_block16(x[r], mode, w);  // all 64 lanes take part
+    uint8_t* c = static_cast<uint8_t*>(codes.p[r]);
+    if (live) {
+      if (col == 0u) static_cast<float*>(scales.p[r])[block] = s;
+#pragma unroll
+      for (int j = 0; j < 4; j++) store_codes4_at<FULL>(c, lane_elem(block, j, col), n, w[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f4 v = e4m3_unpack4(w[j]) * s;
+      a[j] = r == 0 ? v : a[j] + v;
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(out, lane_elem(block, j, col), n, a[j]);
+}
+
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable src, OutTable codes,
+                                                              OutTable scales, size_t n, int mode) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode);
+  else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode);
+}
+
+// Launcher bodies, one per element type ET.  Accumulation into the output
+// is offered for float32 only.
+template <int ET>
+hipError_t encode_fp8_t(uint8_t* codes, float* scales, const void* src, size_t n, int scale_mode,
+                        hipStream_t stream) {
+  const size_t grid = grid_for(n, 16);  // 16 values per lane: a 256-lane group does 16 blocks
+  if (grid == 0) return hipErrorInvalidValue;
+  encode_fp8_kernel<ET><<<grid, kThreads, 0, stream>>>(codes, scales, src, n, scale_mode);
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
+                        bool accumulate, hipStream_t stream) {
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
+  if (accumulate && ET != GB_DTYPE_F32) return hipErrorInvalidValue;
+#define GB_CALL(K)                                                                                               \
+  if constexpr (ET == GB_DTYPE_F32) {                                                                            \
+    if (accumulate) decode_fp8_kernel<K, true, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n); \
+    else decode_fp8_kernel<K, false, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);          \
+  } else {                                                                                                       \
+    decode_fp8_kernel<K, false, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);             \
+  }
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const OutTable& s, int k, size_t n,
+                       int scale_mode, hipStream_t stream) {
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_fp8_kernel<K, ET><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, c, s, n, scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_fp8(uint8_t* codes, float* scales, const void* src, size_t n, int scale_mode, int dtype,
+                             hipStream_t stream) {
+#define GB_CALL(ET) encode_fp8_t<ET>(codes, scales, src, n, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_decode_fp8(void* acc, const PtrTable& codes, const PtrTable& scales, int k, size_t n,
+                             bool accumulate, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) decode_fp8_t<ET>(acc, codes, scales, k, n, accumulate, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales, int k,
+                            size_t n, int scale_mode, int dtype, hipStream_t stream) {
+  OutTable c = {}, s = {};
+  for (int r = 0; r < k; r++) {
+    c.p[r] = codes[r];
+    s.p[r] = scales[r];
+  }
+#define GB_CALL(ET) fused_fp8_t<ET>(out, srcs, c, s, k, n, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+}  // namespace gb

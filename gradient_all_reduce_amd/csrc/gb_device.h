@@ -1,0 +1,434 @@
+// gb_device.h — device helpers shared by the kernel sources of libgbreduce
+// (gb_reduce.hip, gb_codec_bf16.hip, gb_codec_fp8.hip, gb_ef.hip), for
+// gfx950 (AMD Instinct MI355X, CDNA4).  Everything here has internal linkage:
+// each kernel source compiles its own copy, and the sources build in
+// parallel.
+//
+// All of this work streams HBM: a few integer and float operations per 4-byte
+// element, no reuse, no contraction (so no MFMA).  The kernels are shaped for
+// that:
+//   * every lane moves 16-byte vectors (4-byte words for fp8 codes), and each
+//     load or store instruction of a 16-lane row covers 256 contiguous bytes,
+//     so requests coalesce into whole cache lines;
+//   * loads and stores carry the non-temporal hint: each byte is touched once,
+//     so nothing is worth keeping in L2 or the last-level cache;
+//   * a lane issues all of its loads (every rank) before it computes, and the
+//     k contributions of an element are combined in registers: reduce, encode
+//     and decode-accumulate are fused where the call allows it;
+//   * the fp8 block maximum is reduced across the 16 lanes of one DPP row (four
+//     row-local DPP steps, no LDS, no barrier): a 256-value block is one row of
+//     16 lanes holding 16 values each, a wavefront works on 4 blocks and a
+//     256-lane workgroup on 16;
+//   * E4M3 conversion uses gfx950's packed converters (v_cvt_pk_fp8_f32 to
+//     encode two values per instruction, v_cvt_pk_f32_fp8 to decode two).
+//
+// Arithmetic follows the gpubridge README, "How it works" (sum of island sums)
+// and "Bridge compression" (bf16; OCP E4M3 with one scale per 256 values;
+// decode and add in float32).  Every rounding is IEEE binary32
+// round-to-nearest-even with subnormals kept, and nothing is contracted into a
+// fused multiply-add (built with -ffp-contract=off), so results do not depend
+// on the launch shape.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gb_internal.h"
+
+namespace gb {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+struct OutTable {
+  void* p[GB_MAX_K];
+};
+
+constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
+
+// ---------------------------------------------------------------------------
+// Streaming memory access (non-temporal) with guarded variants for the ragged
+// end of a buffer.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f4 load4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+}
+__device__ __forceinline__ void store4(float* p, f4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+}
+
+// Elements [i, i + 4) of p, zero at and beyond n.
+__device__ __forceinline__ f4 load4_any(const float* p, size_t i, size_t n) {
+  if (i + 4 <= n) return load4(p + i);
+  f4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (i < n) v.x = p[i];
+  if (i + 1 < n) v.y = p[i + 1];
+  if (i + 2 < n) v.z = p[i + 2];
+  return v;
+}
+// Stores the elements of [i, i + 4) that lie below n.
+__device__ __forceinline__ void store4_any(float* p, size_t i, size_t n, f4 v) {
+  if (i + 4 <= n) {
+    store4(p + i, v);
+    return;
+  }
+  if (i < n) p[i] = v.x;
+  if (i + 1 < n) p[i + 1] = v.y;
+  if (i + 2 < n) p[i + 2] = v.z;
+}
+
+// 4 fp8 codes of elements [i, i + 4) as one little-endian word, clipped to n.
+__device__ __forceinline__ uint32_t load_codes4(const uint8_t* codes, size_t i, size_t n) {
+  if (i + 4 <= n) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + i));
+  uint32_t w = 0;
+  for (int e = 0; e < 3; e++) {
+    if (i + e < n) w |= (uint32_t)codes[i + e] << (8 * e);
+  }
+  return w;
+}
+__device__ __forceinline__ void store_codes4(uint8_t* codes, size_t i, size_t n, uint32_t w) {
+  if (i + 4 <= n) {
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + i));
+    return;
+  }
+  for (int e = 0; e < 3; e++) {
+    if (i + e < n) codes[i + e] = (uint8_t)(w >> (8 * e));
+  }
+}
+
+// 4 bf16 codes of elements [i, i + 4) as 2 words, clipped to n.
+__device__ __forceinline__ u2 load_bf16_4(const uint16_t* codes, size_t i, size_t n) {
+  if (i + 4 <= n) return __builtin_nontemporal_load(reinterpret_cast<const u2*>(codes + i));
+  uint32_t w[2] = {0u, 0u};
+  for (int e = 0; e < 3; e++) {
+    if (i + e < n) w[e >> 1] |= (uint32_t)codes[i + e] << (16 * (e & 1));
+  }
+  return u2{w[0], w[1]};
+}
+__device__ __forceinline__ void store_bf16_4(uint16_t* codes, size_t i, size_t n, u2 w) {
+  if (i + 4 <= n) {
+    __builtin_nontemporal_store(w, reinterpret_cast<u2*>(codes + i));
+    return;
+  }
+  const uint32_t ws[2] = {w.x, w.y};
+  for (int e = 0; e < 3; e++) {
+    if (i + e < n) codes[i + e] = (uint16_t)(ws[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+// The same accesses with the bounds test resolved at compile time: FULL means
+// the caller knows the whole workgroup's range lies below n, so no access is
+// guarded (one straight run of loads, no divergent branches).
+template <bool FULL>
+__device__ __forceinline__ f4 load4_at(const float* p, size_t i, size_t n) {
+  return FULL ? load4(p + i) : load4_any(p, i, n);
+}
+template <bool FULL>
+__device__ __forceinline__ void store4_at(float* p, size_t i, size_t n, f4 v) {
+  if (FULL) store4(p + i, v);
+  else store4_any(p, i, n, v);
+}
+template <bool FULL>
+__device__ __forceinline__ uint32_t load_codes4_at(const uint8_t* codes, size_t i, size_t n) {
+  return FULL ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + i)) : load_codes4(codes, i, n);
+}
+template <bool FULL>
+__device__ __forceinline__ void store_codes4_at(uint8_t* codes, size_t i, size_t n, uint32_t w) {
+  if (FULL) __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(codes + i));
+  else store_codes4(codes, i, n, w);
+}
+template <bool FULL>
+__device__ __forceinline__ u2 load_bf16_4_at(const uint16_t* codes, size_t i, size_t n) {
+  return FULL ? __builtin_nontemporal_load(reinterpret_cast<const u2*>(codes + i)) : load_bf16_4(codes, i, n);
+}
+template <bool FULL>
+__device__ __forceinline__ void store_bf16_4_at(uint16_t* codes, size_t i, size_t n, u2 w) {
+  if (FULL) __builtin_nontemporal_store(w, reinterpret_cast<u2*>(codes + i));
+  else store_bf16_4(codes, i, n, w);
+}
+
+// ---------------------------------------------------------------------------
+// bf16: nearest value, ties to the even code (the carry of the rounding add
+// runs into the exponent, which gives IEEE overflow to Inf); a NaN keeps its
+// sign and top payload bits with the quiet bit set.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_code(float x) {
+  const uint32_t u = fbits(x);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+__device__ __forceinline__ u2 bf16_pack4(f4 x) {
+  return u2{bf16_code(x.x) | (bf16_code(x.y) << 16), bf16_code(x.z) | (bf16_code(x.w) << 16)};
+}
+// bf16 -> fp32 is exact: the code is the top half of the binary32 pattern.
+__device__ __forceinline__ f4 bf16_unpack4(u2 w) {
+  return f4{bitsf(w.x << 16), bitsf(w.x & 0xFFFF0000u), bitsf(w.y << 16), bitsf(w.y & 0xFFFF0000u)};
+}
+
+// ---------------------------------------------------------------------------
+// Element types of the codec kernels' inputs and outputs (README "Bridge
+// compression": floating-point tensors; their payloads are added in
+// float32).  ET is GB_DTYPE_F32, F16, BF16 or F64.  A load gives elements
+// [i, i + 4) as binary32 (exact from the halves, rounded once to nearest-even
+// from float64; zero at and beyond n); a store rounds binary32 once to the
+// type (nearest-even, IEEE overflow; exact to float64).
+// ---------------------------------------------------------------------------
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef double d2v __attribute__((ext_vector_type(2)));
+
+template <int ET, bool FULL>
+__device__ __forceinline__ f4 load_vals4_at(const void* p, size_t i, size_t n) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    return load4_at<FULL>(static_cast<const float*>(p), i, n);
+  } else if constexpr (ET == GB_DTYPE_BF16) {
+    return bf16_unpack4(load_bf16_4_at<FULL>(static_cast<const uint16_t*>(p), i, n));
+  } else if constexpr (ET == GB_DTYPE_F16) {
+    const h4 h = __builtin_bit_cast(h4, load_bf16_4_at<FULL>(static_cast<const uint16_t*>(p), i, n));
+    return f4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+  } else {
+    const double* d = static_cast<const double*>(p) + i;
+    d2v lo, hi;
+    if (FULL || i + 4 <= n) {
+      lo = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(d));
+      hi = __builtin_nontemporal_load(reinterpret_cast<const d2v*>(d + 2));
+    } else {
+      lo = d2v{i < n ? d[0] : 0.0, i + 1 < n ? d[1] : 0.0};
+      hi = d2v{i + 2 < n ? d[2] : 0.0, 0.0};
+    }
+    return f4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+  }
+}
+
+template <int ET, bool FULL>
+__device__ __forceinline__ void store_vals4_at(void* p, size_t i, size_t n, f4 v) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    store4_at<FULL>(static_cast<float*>(p), i, n, v);
+  } else if constexpr (ET == GB_DTYPE_BF16) {
+    store_bf16_4_at<FULL>(static_cast<uint16_t*>(p), i, n, bf16_pack4(v));
+  } else if constexpr (ET == GB_DTYPE_F16) {
+    // The binary32 values must exist before they are rounded to float16: left
+    // alone, the compiler may fold the product or sum that made them into one
+    // mixed-precision fma rounding straight to float16 (one rounding instead
+    // of the two the definition has, and +0 for a -0 product).  The empty asm
+    // pins them in registers and emits nothing.
+    asm volatile("" : "+v"(v));
+    const h4 h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    store_bf16_4_at<FULL>(static_cast<uint16_t*>(p), i, n, __builtin_bit_cast(u2, h));
+  } else {
+    double* d = static_cast<double*>(p) + i;
+    const d2v lo = {(double)v.x, (double)v.y}, hi = {(double)v.z, (double)v.w};
+    if (FULL || i + 4 <= n) {
+      __builtin_nontemporal_store(lo, reinterpret_cast<d2v*>(d));
+      __builtin_nontemporal_store(hi, reinterpret_cast<d2v*>(d + 2));
+    } else {
+      if (i < n) d[0] = lo.x;
+      if (i + 1 < n) d[1] = lo.y;
+      if (i + 2 < n) d[2] = hi.x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp8: OCP E4M3 (bias 7, largest finite 448 = 0x7E, S.1111.111 = NaN), one
+// fp32 scale per 256-value block.
+// ---------------------------------------------------------------------------
+// Largest non-NaN magnitude of a lane's 16 values, as a bit pattern: the
+// unsigned maximum of |x| bit patterns orders like the magnitudes, in any
+// order of evaluation.  A NaN among the 16 shows as a pattern above Inf's;
+// only then are the values scanned again with the NaNs counted as 0.
+__device__ __forceinline__ uint32_t lane_absmax16(const f4 (&x)[4]) {
+  uint32_t a = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    a = max(a, max(fbits(x[j].x) & 0x7FFFFFFFu, fbits(x[j].y) & 0x7FFFFFFFu));
+    a = max(a, max(fbits(x[j].z) & 0x7FFFFFFFu, fbits(x[j].w) & 0x7FFFFFFFu));
+  }
+  if (a > 0x7F800000u) {
+    a = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t m = fbits(x[j][e]) & 0x7FFFFFFFu;
+        a = max(a, m > 0x7F800000u ? 0u : m);
+      }
+    }
+  }
+  return a;
+}
+
+// Maximum over the 16 lanes of this lane's DPP row; every lane of the row
+// receives it.  Requires all 64 lanes active.
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
+// Scale of a block whose largest non-NaN magnitude has bit pattern `abits`.
+//   ABSMAX_DIV_448: RN(a / 448) (correctly rounded divide; 0 for a = 0).
+//   POW2: the smallest 2^e, e >= -149, with a <= 448 * 2^e.  Writing
+//   a = m * 2^q with m in [1, 2): e = q - 8 when m <= 1.75 (448 = 1.75 * 2^8),
+//   else q - 7.  1 for a = 0, Inf for a = Inf.
+__device__ __forceinline__ float block_scale(uint32_t abits, int mode) {
+  if (mode == GB_SCALE_ABSMAX_DIV_448) return bitsf(abits) / 448.0f;
+  if (abits == 0u) return 1.0f;
+  if (abits >= 0x7F800000u) return bitsf(0x7F800000u);
+  int q;
+  uint32_t frac;
+  const uint32_t ef = abits >> 23;
+  if (ef != 0u) {
+    q = (int)ef - 127;
+    frac = abits & 0x7FFFFFu;
+  } else {  // subnormal a: normalise on its leading one
+    const int p = 31 - __clz(abits);
+    q = p - 149;
+    frac = (abits << (23 - p)) & 0x7FFFFFu;
+  }
+  int e = q - 8 + (frac > 0x600000u ? 1 : 0);
+  e = e < -149 ? -149 : e;
+  return e >= -126 ? bitsf((uint32_t)(e + 127) << 23) : bitsf(1u << (e + 149));
+}
+
+// 1/s in binary64, and 1 for s = 0 (a zero block skips the division).
+__device__ __forceinline__ double scale_reciprocal(float s) {
+  return s == 0.0f ? 1.0 : 1.0 / (double)s;
+}
+
+// RN32(x / s) computed as RN32(RN64(x * RN64(1/s))).  Exact: for binary32 x
+// and s the quotient is never closer than 2^-48 (relative) to a binary32
+// rounding midpoint, while the binary64 route is within about 2^-52 of it, so
+// both round to the same binary32 value; below 2^-126 both give values that
+// encode to E4M3 zero.  An s of 0 gives rinv = 1 (v = x); s = Inf gives
+// rinv = 0, i.e. x / Inf = +-0 and Inf / Inf = NaN, as IEEE division does.
+__device__ __forceinline__ f4 quotient4(f4 x, double rinv) {
+  return f4{(float)((double)x.x * rinv), (float)((double)x.y * rinv), (float)((double)x.z * rinv),
+            (float)((double)x.w * rinv)};
+}
+
+// E4M3 codes of 4 quotients v, packed little-endian, sign bits from the
+// inputs x.  The hardware converter rounds to nearest even and agrees with the
+// E4M3 definition for every |v| <= 448 * (1 + 2^-23) (checked over all such
+// binary32 values); above that it does not saturate, so callers bring larger
+// quotients back to +-448 first (see clamp448).  It returns 0xFF for any NaN,
+// so the sign bit is replaced by x's: NaN codes become 0x7F | sign.
+__device__ __forceinline__ uint32_t e4m3_pack4(f4 v, f4 x) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x, v.y, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z, v.w, w, true);
+  const uint32_t s01 = __builtin_amdgcn_perm(fbits(x.y), fbits(x.x), 0x0C0C0703u);  // x.x, x.y top bytes -> bytes 0, 1
+  const uint32_t s23 = __builtin_amdgcn_perm(fbits(x.w), fbits(x.z), 0x07030C0Cu);  // x.z, x.w top bytes -> bytes 2, 3
+  return ((uint32_t)w & 0x7F7F7F7Fu) | ((s01 | s23) & 0x80808080u);
+}
+
+// Saturation of quotients to +-448, NaN kept.  Only a block whose scale is
+// subnormal needs it: a normal s = RN(a / 448) is within 2^-24 of a / 448, so
+// |x / s| <= a / s rounds to at most 448 * (1 + 2^-23), and a power-of-two
+// scale is at least a / 448.  A subnormal s carries an absolute rounding
+// error that can put a / s anywhere above 448.
+__device__ __forceinline__ f4 clamp448(f4 v) {
+  f4 c;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const float t = fminf(fmaxf(v[e], -448.0f), 448.0f);
+    c[e] = v[e] != v[e] ? v[e] : t;
+  }
+  return c;
+}
+
+// Values of 4 packed E4M3 codes (exact; NaN codes give NaN).
+__device__ __forceinline__ f4 e4m3_unpack4(uint32_t w) {
+  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return f4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Elements of a 256-value block owned by a lane: 4 vectors, vector j at
+// element offset (16 j + col) * 4 of the block, so every load or store
+// instruction of a row covers 256 contiguous bytes of fp32 (64 of codes).
+__device__ __forceinline__ size_t lane_elem(size_t block, int j, uint32_t col) {
+  return block * kBlock + (size_t)(16 * j + col) * 4;
+}
+
+// Encodes a lane's 16 values of one block (all 64 lanes must be active):
+// returns the block scale and writes the 4 packed code words to w.
+__device__ __forceinline__ float encode_block16(const f4 (&x)[4], int mode, uint32_t (&w)[4]) {
+  const float s = block_scale(row_max16(lane_absmax16(x)), mode);
+  const double rinv = scale_reciprocal(s);
+  const bool subnormal_scale = s > 0.0f && s < 0x1p-126f;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f4 v = quotient4(x[j], rinv);
+    if (subnormal_scale) v = clamp448(v);
+    w[j] = e4m3_pack4(v, x[j]);
+  }
+  return s;
+}
+
+// Every kernel below runs one of two instantiations of its body per
+// workgroup: FULL when the workgroup's whole range lies below n (all but the
+// last workgroup of a launch), with no bounds test on any access, and the
+// guarded one otherwise.  The choice is uniform across the workgroup.
+constexpr size_t kVecPerGroup = (size_t)kThreads * 4;       // 1024 values: one 4-vector per lane
+constexpr size_t kBlocksPerGroup = kThreads / 16;          // 16 fp8 blocks: one per 16-lane row
+
+__device__ __forceinline__ bool group_full(size_t per_group, size_t n) {
+  return ((size_t)blockIdx.x + 1) * per_group <= n;
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers.
+// ---------------------------------------------------------------------------
+constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
+
+// Dynamic LDS reserved per workgroup by the kernels that keep the most bytes
+// in flight.  No kernel uses LDS: reserving 64 KiB of the 160 KiB a compute
+// unit has caps it at 2 such workgroups.  A fused fp8 pass over k >= 4 ranks
+// keeps 16k bytes of loads in flight per lane; measured on MI355X at 1e9
+// values per rank, 2 workgroups per compute unit move about 4% more bytes
+// per second than the 5 its registers allow (fewer concurrent streams of
+// requests at the memory), while 1 per unit is worse.  Kernels with fewer
+// bytes per lane lose heavily under any cap and get none.
+constexpr unsigned kHeavyLds = 64u << 10;
+__host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kHeavyLds : 0u; }
+
+size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+// Workgroups for one lane per `per_lane` values, or 0 if too many.
+size_t grid_for(size_t n, size_t per_lane) {
+  const size_t g = ceil_div(ceil_div(n, per_lane), (size_t)kThreads);
+  return g > kMaxGrid ? 0 : g;
+}
+
+#define GB_DISPATCH_K(k, CALL) \
+  switch (k) {                 \
+    case 1: CALL(1); break;    \
+    case 2: CALL(2); break;    \
+    case 3: CALL(3); break;    \
+    case 4: CALL(4); break;    \
+    case 5: CALL(5); break;    \
+    case 6: CALL(6); break;    \
+    case 7: CALL(7); break;    \
+    case 8: CALL(8); break;    \
+    default: return hipErrorInvalidValue; \
+  }
+
+// Switch on a codec kernel's element type (return CALL(ET)).
+#define GB_DISPATCH_ET(et, CALL)                      \
+  (void)hipGetLastError();                             \
+  switch (et) {                                        \
+    case GB_DTYPE_F32: return CALL(GB_DTYPE_F32);      \
+    case GB_DTYPE_F16: return CALL(GB_DTYPE_F16);      \
+    case GB_DTYPE_BF16: return CALL(GB_DTYPE_BF16);    \
+    case GB_DTYPE_F64: return CALL(GB_DTYPE_F64);      \
+    default: return hipErrorInvalidValue;              \
+  }
+
+}  // namespace
+}  // namespace gb

@@ -1,5 +1,5 @@
 // gb_internal.h — launchers shared by the C-ABI layer (gb_api.cpp) and the
-// HIP kernels (gb_kernels.hip).  Not installed; the public ABI is
+// HIP kernel sources (gb_*.hip).  Not installed; the public ABI is
 // include/gbreduce.h.
 //
 // Every launcher assumes its arguments were validated by gb_api.cpp: pointers
