@@ -62,17 +62,83 @@ gb_status check_array(const void* p, size_t align, const char* fn, const char* n
   return GB_OK;
 }
 
-gb_status check_table(const void* const* table, int k, size_t align, const char* fn, const char* name,
-                      gb::PtrTable* out) {
+gb_status check_table(const void* const* table, int k, size_t align, const char* fn, const char* name) {
   if (table == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: %s array is NULL", fn, name);
   for (int r = 0; r < k; r++) {
     char label[64];
     std::snprintf(label, sizeof label, "%s[%d]", name, r);
     gb_status s = check_array(table[r], align, fn, label);
     if (s != GB_OK) return s;
-    out->p[r] = table[r];
   }
   return GB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// More ranks than one launch reads (kLaunchRanks).  Every reduction here is a
+// left fold over ranks, so it continues across launches from the stored
+// partial result: a later launch reads the output as its first operand (or
+// accumulates into it) and folds the next ranks in.  Each step of the fold
+// rounds exactly as in one launch (the partial is a value of the output's
+// type), so the bits are the same.  AVG divides only in the last launch.
+// ---------------------------------------------------------------------------
+constexpr int kR = gb::kLaunchRanks;
+
+int group_size(int k, int g) { return k - g < kR ? k - g : kR; }
+
+gb::PtrTable slice(const void* const* table, int first, int count) {
+  gb::PtrTable t = {};
+  for (int r = 0; r < count; r++) t.p[r] = table[first + r];
+  return t;
+}
+
+// dst = [dst +] srcs[0] + ... + srcs[k-1], float32, in rank order.
+hipError_t sum_groups(float* dst, const void* const* srcs, int k, size_t n, bool accumulate, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  for (int g = 0; g < k && e == hipSuccess; g += kR) {
+    const int m = group_size(k, g);
+    e = gb::launch_reduce_sum(dst, slice(srcs, g, m), m, n, accumulate || g > 0, st);
+  }
+  return e;
+}
+
+// SUM / AVG / MAX / MIN over k ranks of element type dtype into dst: the
+// first launch takes kR ranks, each further one dst and up to kR - 1 ranks.
+hipError_t op_groups(void* dst, const void* const* srcs, int k, size_t n, int dtype, int op, int divisor,
+                     hipStream_t st) {
+  auto launch = [&](const gb::PtrTable& t, int m, int o) {
+    return dtype == GB_DTYPE_F32 ? gb::launch_reduce_op(static_cast<float*>(dst), t, m, n, o, divisor, st)
+                                 : gb::launch_reduce_typed(dst, t, m, n, dtype, o, divisor, st);
+  };
+  if (k <= kR) return launch(slice(srcs, 0, k), k, op);
+  const int fold_op = op == GB_OP_AVG ? GB_OP_SUM : op;
+  hipError_t e = launch(slice(srcs, 0, kR), kR, fold_op);
+  for (int g = kR; g < k && e == hipSuccess; g += kR - 1) {
+    const int m = k - g < kR - 1 ? k - g : kR - 1;
+    gb::PtrTable t = {};
+    t.p[0] = dst;
+    for (int r = 0; r < m; r++) t.p[1 + r] = srcs[g + r];
+    e = launch(t, m + 1, g + m == k ? op : fold_op);
+  }
+  return e;
+}
+
+// Decode k payloads and add them in rank order into the float32 acc (or,
+// with k <= kR, into dst of dtype, rounded once).
+hipError_t decode_groups(void* acc, const void* const* codes, const float* const* scales, int k, size_t n,
+                         int codec, bool accumulate, int dtype, hipStream_t st) {
+  if (codec == GB_CODEC_NONE) return sum_groups(static_cast<float*>(acc), codes, k, n, accumulate, st);
+  hipError_t e = hipSuccess;
+  for (int g = 0; g < k && e == hipSuccess; g += kR) {
+    const int m = group_size(k, g);
+    const bool a = accumulate || g > 0;
+    if (codec == GB_CODEC_BF16) {
+      e = gb::launch_decode_bf16(acc, slice(codes, g, m), m, n, a, dtype, st);
+    } else {
+      e = gb::launch_decode_fp8(acc, slice(codes, g, m), slice(reinterpret_cast<const void* const*>(scales), g, m), m,
+                                n, a, dtype, st);
+    }
+  }
+  return e;
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -208,11 +274,9 @@ gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n, v
   if (s != GB_OK) return s;
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  gb::PtrTable t = {};
-  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) {
-    return s;
-  }
-  return from_hip(gb::launch_reduce_sum(dst, t, k, n, false, as_stream(stream)), fn);
+  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+  if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  return from_hip(sum_groups(dst, sp, k, n, false, as_stream(stream)), fn);
 }
 
 gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n, int op, int divisor, void* stream) {
@@ -227,11 +291,9 @@ gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n, int o
   if (s != GB_OK) return s;
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  gb::PtrTable t = {};
-  if ((s = check_table(reinterpret_cast<const void* const*>(srcs), k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) {
-    return s;
-  }
-  return from_hip(gb::launch_reduce_op(dst, t, k, n, op, divisor, as_stream(stream)), fn);
+  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+  if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  return from_hip(op_groups(dst, sp, k, n, GB_DTYPE_F32, op, divisor, as_stream(stream)), fn);
 }
 
 gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, int dtype, int op, int divisor,
@@ -251,13 +313,8 @@ gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, i
   if (s != GB_OK) return s;
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  gb::PtrTable t = {};
-  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs", &t)) != GB_OK) return s;
-  hipStream_t st = as_stream(stream);
-  if (dtype == GB_DTYPE_F32) {
-    return from_hip(gb::launch_reduce_op(static_cast<float*>(dst), t, k, n, op, divisor, st), fn);
-  }
-  return from_hip(gb::launch_reduce_typed(dst, t, k, n, dtype, op, divisor, st), fn);
+  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  return from_hip(op_groups(dst, srcs, k, n, dtype, op, divisor, as_stream(stream)), fn);
 }
 
 gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stream) {
@@ -292,22 +349,13 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float
   }
   if (n == 0) return GB_OK;
   if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
-  gb::PtrTable c = {};
-  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes", &c)) != GB_OK) return s;
-  hipStream_t st = as_stream(stream);
-  switch (codec) {
-    case GB_CODEC_NONE:
-      return from_hip(gb::launch_reduce_sum(acc, c, k, n, accumulate != 0, st), fn);
-    case GB_CODEC_BF16:
-      return from_hip(gb::launch_decode_bf16(acc, c, k, n, accumulate != 0, GB_DTYPE_F32, st), fn);
-    default: {
-      gb::PtrTable sc = {};
-      if ((s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales", &sc)) != GB_OK) {
-        return s;
-      }
-      return from_hip(gb::launch_decode_fp8(acc, c, sc, k, n, accumulate != 0, GB_DTYPE_F32, st), fn);
-    }
+  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if (codec == GB_CODEC_FP8_E4M3_B256 &&
+      (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
+    return s;
   }
+  return from_hip(decode_groups(acc, codes, scales, k, n, codec, accumulate != 0, GB_DTYPE_F32, as_stream(stream)),
+                  fn);
 }
 
 gb_status gb_encode(int codec, int dtype, void* codes, float* scales, const void* src, size_t n, int scale_mode,
@@ -342,24 +390,18 @@ gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes, const fl
   }
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
+  if (k > kR && dtype != GB_DTYPE_F32) {
+    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a %s total is rounded once from float32, which holds up to %d "
+                "payloads per call; sum more into a float32 buffer", fn, k, "non-float32", kR);
+  }
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  gb::PtrTable c = {};
-  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes", &c)) != GB_OK) return s;
-  hipStream_t st = as_stream(stream);
-  switch (codec) {
-    case GB_CODEC_NONE:
-      return from_hip(gb::launch_reduce_sum(static_cast<float*>(dst), c, k, n, false, st), fn);
-    case GB_CODEC_BF16:
-      return from_hip(gb::launch_decode_bf16(dst, c, k, n, false, dtype, st), fn);
-    default: {
-      gb::PtrTable sc = {};
-      if ((s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales", &sc)) != GB_OK) {
-        return s;
-      }
-      return from_hip(gb::launch_decode_fp8(dst, c, sc, k, n, false, dtype, st), fn);
-    }
+  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if (codec == GB_CODEC_FP8_E4M3_B256 &&
+      (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
+    return s;
   }
+  return from_hip(decode_groups(dst, codes, scales, k, n, codec, false, dtype, as_stream(stream)), fn);
 }
 
 gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* scales_dev, void* codes_host,
@@ -469,20 +511,19 @@ gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
   for (size_t o = 0; o < n && e == hipSuccess; o += chunk_elems, chunk++) {
     const size_t l = n - o < chunk_elems ? n - o : chunk_elems;
     const int ci = (int)(chunk % kCopyStreams);
-    gb::PtrTable cp = {}, sp = {};
+    const void* cp[GB_MAX_K];
+    const float* sp[GB_MAX_K];
     for (int r = 0; r < k && e == hipSuccess; r++) {
       char* dst = static_cast<char*>(codes_dev[r]) + cb * o;
       e = hipMemcpyAsync(dst, static_cast<const char*>(codes_host[r]) + cb * o, cb * l, hipMemcpyHostToDevice,
                          c->copy[ci]);
-      cp.p[r] = dst;
-      if (fp8) sp.p[r] = scales_dev[r] + o / GB_BLOCK;
+      cp[r] = dst;
+      sp[r] = fp8 ? scales_dev[r] + o / GB_BLOCK : nullptr;
     }
     if (e == hipSuccess) e = hipEventRecord(c->ev_copy[ci], c->copy[ci]);
     if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[ci], 0);
     if (e != hipSuccess) break;
-    if (codec == GB_CODEC_NONE) e = gb::launch_reduce_sum(acc + o, cp, k, l, accumulate != 0, st);
-    else if (codec == GB_CODEC_BF16) e = gb::launch_decode_bf16(acc + o, cp, k, l, accumulate != 0, GB_DTYPE_F32, st);
-    else e = gb::launch_decode_fp8(acc + o, cp, sp, k, l, accumulate != 0, GB_DTYPE_F32, st);
+    e = decode_groups(acc + o, cp, sp, k, l, codec, accumulate != 0, GB_DTYPE_F32, st);
   }
   return from_hip(e, fn);
 }
@@ -495,7 +536,7 @@ namespace {
 // workspace layout and the source table.
 gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k, size_t n,
                        size_t bucket_elems, int codec, int scale_mode, void* workspace, size_t workspace_bytes,
-                       size_t* cs, size_t* so, size_t* ss, gb::PtrTable* t) {
+                       size_t* cs, size_t* so, size_t* ss) {
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
   if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
     return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
@@ -511,7 +552,7 @@ gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k
   }
   if (n == 0) return GB_OK;
   if ((s = check_array(out, GB_ALIGN, fn, "out")) != GB_OK) return s;
-  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs", t)) != GB_OK) return s;
+  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
   if (codec != GB_CODEC_NONE) {
     if (workspace == nullptr || workspace_bytes < need) {
       return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes,
@@ -524,6 +565,57 @@ gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k
   return GB_OK;
 }
 
+// The bucket stream over the whole buffer (all buckets start on block
+// boundaries, so one launch covers them; rank r's payload lands where a
+// whole-buffer encode would put it).  The first kLaunchRanks ranks go through
+// the fused pass (encode, decode, add; with error feedback when residuals is
+// not NULL); the remaining ranks are encoded one by one into the workspace
+// and their payloads decoded and added in rank order.  Without a codec: the
+// exact SUM of the element type.
+hipError_t bucket_groups(void* out, const void* const* srcs, float* const* residuals, int k, size_t n, int codec,
+                         int mode, int dtype, char* ws, size_t cs, size_t so, size_t ss, hipStream_t st) {
+  if (codec == GB_CODEC_NONE) {
+    return dtype == GB_DTYPE_F32 ? sum_groups(static_cast<float*>(out), srcs, k, n, false, st)
+                                 : op_groups(out, srcs, k, n, dtype, GB_OP_SUM, 1, st);
+  }
+  const bool bf16 = codec == GB_CODEC_BF16;
+  void* code[GB_MAX_K];
+  float* scale[GB_MAX_K];
+  for (int r = 0; r < k; r++) {
+    code[r] = ws + (size_t)r * cs;
+    scale[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
+  }
+  const int m = k < kR ? k : kR;
+  const gb::PtrTable t = slice(srcs, 0, m);
+  hipError_t e;
+  if (residuals != nullptr && bf16) {
+    e = gb::launch_fused_bf16_ef(static_cast<float*>(out), t, residuals, reinterpret_cast<uint16_t* const*>(code), m,
+                                 n, st);
+  } else if (residuals != nullptr) {
+    e = gb::launch_fused_fp8_ef(static_cast<float*>(out), t, residuals, reinterpret_cast<uint8_t* const*>(code),
+                                scale, m, n, mode, st);
+  } else if (bf16) {
+    e = gb::launch_fused_bf16(out, t, reinterpret_cast<uint16_t* const*>(code), m, n, dtype, st);
+  } else {
+    e = gb::launch_fused_fp8(out, t, reinterpret_cast<uint8_t* const*>(code), scale, m, n, mode, dtype, st);
+  }
+  for (int r = kR; r < k && e == hipSuccess; r++) {
+    const float* x = static_cast<const float*>(srcs[r]);
+    if (residuals != nullptr) {
+      e = bf16 ? gb::launch_encode_bf16_ef(static_cast<uint16_t*>(code[r]), residuals[r], x, n, st)
+               : gb::launch_encode_fp8_ef(static_cast<uint8_t*>(code[r]), scale[r], residuals[r], x, n, mode, st);
+    } else {
+      e = bf16 ? gb::launch_encode_bf16(static_cast<uint16_t*>(code[r]), x, n, GB_DTYPE_F32, st)
+               : gb::launch_encode_fp8(static_cast<uint8_t*>(code[r]), scale[r], x, n, mode, GB_DTYPE_F32, st);
+    }
+  }
+  if (k > kR && e == hipSuccess) {
+    e = decode_groups(out, const_cast<const void* const*>(code + kR), const_cast<const float* const*>(scale + kR),
+                      k - kR, n, codec, true, GB_DTYPE_F32, st);
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -533,35 +625,15 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
                                     size_t workspace_bytes, void* stream) {
   const char* fn = "gb_bucket_allreduce_local";
   size_t cs, so, ss;
-  gb::PtrTable t = {};
-  gb_status s = check_bucket(fn, out, reinterpret_cast<const void* const*>(srcs), k, n, bucket_elems, codec,
-                             scale_mode, workspace, workspace_bytes, &cs, &so, &ss, &t);
+  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+  gb_status s = check_bucket(fn, out, sp, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                             &so, &ss);
   if (s != GB_OK || n == 0) return s;
-  hipStream_t st = as_stream(stream);
-  char* ws = static_cast<char*>(workspace);
-  // Every bucket starts on a 256-value boundary, so the blocks of a bucket
-  // are blocks of the whole buffer and the buckets together are exactly one
-  // pass over [0, n): a single launch covers all of them, its workgroups
-  // taking blocks (hence buckets) in order.  The result equals one launch per
-  // bucket bit for bit, without a partly idle GPU at the end of every bucket.
-  // Rank r's payload lands where a whole-buffer encode would put it.
-  hipError_t e;
-  if (codec == GB_CODEC_NONE) {
-    e = gb::launch_reduce_sum(out, t, k, n, false, st);
-  } else if (codec == GB_CODEC_BF16) {
-    uint16_t* c[GB_MAX_K];
-    for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
-    e = gb::launch_fused_bf16(out, t, c, k, n, GB_DTYPE_F32, st);
-  } else {
-    uint8_t* c[GB_MAX_K];
-    float* sc[GB_MAX_K];
-    for (int r = 0; r < k; r++) {
-      c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
-      sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
-    }
-    e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, GB_DTYPE_F32, st);
-  }
-  return from_hip(e, fn);
+  // One launch covers every bucket: a partly idle GPU at the end of each
+  // bucket is avoided, and the result equals one call per bucket bit for bit.
+  return from_hip(bucket_groups(out, sp, nullptr, k, n, codec, scale_mode, GB_DTYPE_F32,
+                                static_cast<char*>(workspace), cs, so, ss, as_stream(stream)),
+                  fn);
 }
 
 gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* const* srcs, int k, size_t n,
@@ -570,32 +642,17 @@ gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* cons
   const char* fn = "gb_bucket_allreduce_local_typed";
   if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
   size_t cs, so, ss;
-  gb::PtrTable t = {};
   gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
-                             &so, &ss, &t);
-  if (s != GB_OK || n == 0) return s;
-  hipStream_t st = as_stream(stream);
-  char* ws = static_cast<char*>(workspace);
-  // One launch over all buckets, as gb_bucket_allreduce_local; without a
-  // codec the exact SUM of the type.
-  hipError_t e;
-  if (codec == GB_CODEC_NONE) {
-    e = dtype == GB_DTYPE_F32 ? gb::launch_reduce_sum(static_cast<float*>(out), t, k, n, false, st)
-                              : gb::launch_reduce_typed(out, t, k, n, dtype, GB_OP_SUM, 1, st);
-  } else if (codec == GB_CODEC_BF16) {
-    uint16_t* c[GB_MAX_K];
-    for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
-    e = gb::launch_fused_bf16(out, t, c, k, n, dtype, st);
-  } else {
-    uint8_t* c[GB_MAX_K];
-    float* sc[GB_MAX_K];
-    for (int r = 0; r < k; r++) {
-      c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
-      sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
-    }
-    e = gb::launch_fused_fp8(out, t, c, sc, k, n, scale_mode, dtype, st);
+                             &so, &ss);
+  if (s != GB_OK) return s;
+  if (k > kR && dtype != GB_DTYPE_F32 && codec != GB_CODEC_NONE) {
+    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
+                "which holds up to %d ranks per call", fn, k, kR);
   }
-  return from_hip(e, fn);
+  if (n == 0) return GB_OK;
+  return from_hip(bucket_groups(out, srcs, nullptr, k, n, codec, scale_mode, dtype, static_cast<char*>(workspace),
+                                cs, so, ss, as_stream(stream)),
+                  fn);
 }
 
 gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n, void* stream) {
@@ -629,34 +686,16 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, flo
     return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
   }
   size_t cs, so, ss;
-  gb::PtrTable t = {};
-  gb_status s = check_bucket(fn, out, reinterpret_cast<const void* const*>(srcs), k, n, bucket_elems, codec,
-                             scale_mode, workspace, workspace_bytes, &cs, &so, &ss, &t);
+  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+  gb_status s = check_bucket(fn, out, sp, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                             &so, &ss);
   if (s != GB_OK || n == 0) return s;
-  gb::PtrTable rt = {};
-  if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals", &rt)) !=
-      GB_OK) {
+  if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
     return s;
   }
-  float* res[GB_MAX_K];
-  for (int r = 0; r < k; r++) res[r] = residuals[r];
-  hipStream_t st = as_stream(stream);
-  char* ws = static_cast<char*>(workspace);
-  hipError_t e;
-  if (codec == GB_CODEC_BF16) {
-    uint16_t* c[GB_MAX_K];
-    for (int r = 0; r < k; r++) c[r] = reinterpret_cast<uint16_t*>(ws + (size_t)r * cs);
-    e = gb::launch_fused_bf16_ef(out, t, res, c, k, n, st);
-  } else {
-    uint8_t* c[GB_MAX_K];
-    float* sc[GB_MAX_K];
-    for (int r = 0; r < k; r++) {
-      c[r] = reinterpret_cast<uint8_t*>(ws + (size_t)r * cs);
-      sc[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
-    }
-    e = gb::launch_fused_fp8_ef(out, t, res, c, sc, k, n, scale_mode, st);
-  }
-  return from_hip(e, fn);
+  return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32,
+                                static_cast<char*>(workspace), cs, so, ss, as_stream(stream)),
+                  fn);
 }
 
 }  // extern "C"

@@ -42,7 +42,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 struct OutTable {
-  void* p[GB_MAX_K];
+  void* p[kLaunchRanks];
 };
 
 constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes

@@ -3,7 +3,7 @@
 // include/gbreduce.h.
 //
 // Every launcher assumes its arguments were validated by gb_api.cpp: pointers
-// non-null and aligned as the ABI requires, 1 <= k <= GB_MAX_K, n > 0.  Each
+// non-null and aligned as the ABI requires, 1 <= k <= kLaunchRanks, n > 0.  Each
 // returns hipSuccess or the launch error.
 #pragma once
 
@@ -15,9 +15,13 @@
 
 namespace gb {
 
-// Up to GB_MAX_K device pointers, passed to kernels by value.
+// Ranks one kernel launch reads (its rank count is a template parameter);
+// calls with more ranks fold the rest in further launches.
+constexpr int kLaunchRanks = 8;
+
+// Up to kLaunchRanks device pointers, passed to kernels by value.
 struct PtrTable {
-  const void* p[GB_MAX_K];
+  const void* p[kLaunchRanks];
 };
 
 // Values per fp8 scale block, and blocks per workgroup in the block kernels

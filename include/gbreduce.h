@@ -52,8 +52,12 @@ extern "C" {
 /* Values per fp8 scale block (README "Bridge compression": one scale per
  * 256 values). */
 #define GB_BLOCK 256
-/* Largest number of contributions (ranks or islands) one call sums. */
-#define GB_MAX_K 8
+/* Largest number of contributions (ranks or islands) one call sums.  A
+ * kernel launch reads up to 8; a call with more folds the rest in further
+ * launches, continuing the same rank-order fold from the stored partial
+ * result (the same bits as one pass), at 8 more bytes of traffic per value
+ * per extra launch. */
+#define GB_MAX_K 16
 /* Required byte alignment of element arrays. */
 #define GB_ALIGN 16
 
@@ -271,7 +275,10 @@ gb_status gb_encode(int codec, int dtype, void* codes, float* scales,
  *   decoded payloads (as gb_decode_accumulate with accumulate 0), rounded once
  *   to dtype.  codes, scales, k and codec as gb_decode_accumulate; codec NONE
  *   (float32 payloads) only with dtype F32 (other types reduce exactly with
- *   gb_reduce_typed).  dst must not overlap any payload.
+ *   gb_reduce_typed).  dst must not overlap any payload.  For a dtype other
+ *   than F32, k is at most 8 (GB_ERR_INVALID_ARG beyond): the total is
+ *   rounded once from float32, and the library keeps no float32 buffer of its
+ *   own; sum more payloads into a float32 buffer with gb_decode_accumulate.
  */
 gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes,
                         const float* const* scales, int k, size_t n, int codec,
@@ -283,7 +290,9 @@ gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes,
  *   encoded as gb_encode does (into the same workspace, of the same size, as
  *   for float32) and out = the float32 total rounded once to dtype; without
  *   one (GB_CODEC_NONE) out is the exact SUM of the type (gb_reduce_typed).
- *   out may equal srcs[0].  Everything else as gb_bucket_allreduce_local.
+ *   out may equal srcs[0].  With a codec and a dtype other than F32, k is at
+ *   most 8, as for gb_decode_sum.  Everything else as
+ *   gb_bucket_allreduce_local.
  */
 gb_status gb_bucket_allreduce_local_typed(int dtype, void* out,
                                           const void* const* srcs, int k,

@@ -106,7 +106,7 @@ def _arr(*addrs):
 
 @pytest.mark.parametrize("call,status,msg", [
     (lambda L: L.gb_reduce_sum(None, _arr(256), 0, 10, None), 1, "k = 0"),
-    (lambda L: L.gb_reduce_sum(None, _arr(256), 9, 10, None), 1, "k = 9"),
+    (lambda L: L.gb_reduce_sum(None, _arr(256), 17, 10, None), 1, "k = 17"),
     (lambda L: L.gb_reduce_sum(None, _arr(256), 1, 10, None), 1, "dst is NULL"),
     (lambda L: L.gb_reduce_sum(ctypes.c_void_p(260), _arr(256), 1, 10, None), 2, "dst"),
     (lambda L: L.gb_reduce_sum(ctypes.c_void_p(256), _arr(256, 0), 2, 10, None), 1, "srcs[1] is NULL"),
@@ -145,7 +145,11 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
     (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 1, 10, 2, 1, 0, None), 1, "divisor"),
     (lambda L: L.gb_reduce_typed(ctypes.c_void_p(264), _arr(256), 1, 10, 4, 0, 1, None), 2, "dst"),
     (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256, 257), 2, 10, 5, 2, 1, None), 2, "srcs[1]"),
-    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 9, 10, 3, 0, 1, None), 1, "k = 9"),
+    (lambda L: L.gb_reduce_typed(ctypes.c_void_p(256), _arr(256), 17, 10, 3, 0, 1, None), 1, "k = 17"),
+    (lambda L: L.gb_decode_sum(1, ctypes.c_void_p(256), _arr(*[256] * 9), None, 9, 10, 1, None), 1,
+     "rounded once from float32"),
+    (lambda L: L.gb_bucket_allreduce_local_typed(2, ctypes.c_void_p(256), _arr(*[256] * 9), 9, 1000, 256, 2, 0,
+                                                 ctypes.c_void_p(512), 1 << 24, None), 1, "rounded once"),
     (lambda L: L.gb_encode(0, 1, None, None, None, 10, 0, None), 3, "not bf16 or fp8"),
     (lambda L: L.gb_encode(1, 6, None, None, None, 10, 0, None), 3, "not a floating-point type"),
     (lambda L: L.gb_encode(2, 2, None, None, None, 10, 3, None), 3, "scale mode"),
@@ -177,8 +181,8 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
      1, "pointer array"),
     (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 1, 10, 0, 1, 0, None),
      1, "chunk_elems"),
-    (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 9, 10, 256, 1, 0, None),
-     1, "k = 9"),
+    (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 17, 10, 256, 1, 0, None),
+     1, "k = 17"),
 ])
 def test_validation_of_the_wider_calls(gb, call, status, msg):
     assert call(gb._lib) == status

@@ -307,7 +307,7 @@ def test_errors_enqueue_nothing(gb):
         gb.gb_reduce_sum(out[1:n + 1], [x[:n], x[:n]])  # misaligned dst
     assert e.value.status == gb.GB_ERR_MISALIGNED
     with pytest.raises(gb.GbError) as e:
-        gb.gb_reduce_sum(out[:n], [x[:n]] * 9)  # k beyond the maximum
+        gb.gb_reduce_sum(out[:n], [x[:n]] * 17)  # k beyond the maximum (16)
     assert e.value.status == gb.GB_ERR_INVALID_ARG
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
     with pytest.raises(gb.GbError) as e:
