@@ -533,7 +533,7 @@ class Gradients64(Workload):
         return self.k * 6 * self.n + self.k * 2 * self.n + 4 * self.n
 
     def timed_kernel(self):
-        return ("encode_bf16_kernel<0>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
+        return ("encode_bf16_kernel<0,2>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
 
     def cpu_units(self):
         """4 bf16 encodes and the decode-and-add on 2^18-value pieces."""

@@ -93,6 +93,22 @@ def test_encode_bf16(gb, n):
     assert_bits_equal(host(codes.view(torch.int16)).view(np.uint16), O.encode_bf16(x), f"bf16 n={n}")
 
 
+@pytest.mark.parametrize("n", [(1 << 23) + 1, (1 << 23) + 1024 + 3, (1 << 23) + 2047, (1 << 23) + 2048,
+                               (1 << 23) - 5])
+def test_encode_bf16_two_vectors_per_lane(gb, n):
+    """From 2^23 values the encoder gives each lane two vectors 1024 values
+    apart: tails that end inside the first vector, inside the second, and on
+    a workgroup boundary, and the size just below the switch."""
+    x = W.gradients(n, 37)
+    codes = torch.empty(n, dtype=torch.uint16, device=DEV)
+    gb.gb_encode_bf16(codes, dev(x))
+    assert_bits_equal(host(codes.view(torch.int16)).view(np.uint16), O.encode_bf16(x), f"bf16 n={n}")
+    half = torch.empty(n, dtype=torch.uint16, device=DEV)
+    gb.gb_encode(gb.GB_CODEC_BF16, half, None, dev(x).half())
+    want = O.encode_typed(dev(x).half().cpu().view(torch.int16).numpy().view(np.uint16), "f16", O.CODEC_BF16)[0]
+    assert_bits_equal(host(half.view(torch.int16)).view(np.uint16), want, f"f16 -> bf16 n={n}")
+
+
 def test_encode_bf16_every_rounding_class(gb):
     hi = np.arange(1 << 16, dtype=np.uint32) << 16
     lows = np.array([0, 1, 0x3FFF, 0x4000, 0x7FFF, 0x8000, 0x8001, 0xC000, 0xFFFF,
