@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--op", default="sum", choices=["sum", "avg", "max", "min"],
                    help="reduction of the two_island_sweep workload (avg divides by the "
                         "world size, 2 here)")
+    p.add_argument("--codec", default="fp8", choices=["fp8", "bf16", "none"],
+                   help="bridge codec of the ddp_1b_buckets stream")
     p.add_argument("--dtype", default="f32", choices=["f32", "f16", "bf16", "f64", "i8", "u8", "i32", "i64"],
                    help="element type of the two_island_sweep workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,9 +153,11 @@ class DdpBuckets(Workload):
         if self.dt not in ("f32", "f16", "bf16", "f64"):
             raise SystemExit("the bucket stream compresses floating-point gradients only")
         self.esize = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}[self.dt]
+        self.codec = {"fp8": gb.GB_CODEC_FP8_E4M3_B256, "bf16": gb.GB_CODEC_BF16, "none": gb.GB_CODEC_NONE}[
+            getattr(args, "codec", "fp8")]
         self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n,
                        "bucket_elems": self.bucket, "buckets": len(W.ddp_buckets()),
-                       "codec": "fp8_e4m3_b256",
+                       "codec": {2: "fp8_e4m3_b256", 1: "bf16", 0: "none"}[self.codec],
                        "scale_mode": ["absmax_div_448", "pow2"][self.mode],
                        "distribution": "N(0, sigma=1e-3)", "element_type": self.dt}
 
@@ -162,31 +166,35 @@ class DdpBuckets(Workload):
         self.x = [self.W.device_gradients_typed(self.n, self.W.BASE_SEED + r, self.dev, self.dt)
                   for r in range(self.k)]
         self.out = torch.empty(self.n, dtype=self.x[0].dtype, device=self.dev)
-        self.lay = gb.gb_bucket_workspace_layout(gb.GB_CODEC_FP8_E4M3_B256, self.k, self.n, self.bucket)
-        self.ws = torch.empty(self.lay["total"], dtype=torch.uint8, device=self.dev)
+        self.lay = gb.gb_bucket_workspace_layout(self.codec, self.k, self.n, self.bucket)
+        self.ws = torch.empty(max(1, self.lay["total"]), dtype=torch.uint8, device=self.dev)
 
     def step(self):
         if self.dt == "f32":
-            self.gb.gb_bucket_allreduce_local(self.out, self.x, self.bucket, self.gb.GB_CODEC_FP8_E4M3_B256,
-                                              self.mode, self.ws)
+            self.gb.gb_bucket_allreduce_local(self.out, self.x, self.bucket, self.codec, self.mode, self.ws)
         else:
-            self.gb.gb_bucket_allreduce_local_typed(self.out, self.x, self.bucket, self.gb.GB_CODEC_FP8_E4M3_B256,
-                                                    self.mode, self.ws)
+            self.gb.gb_bucket_allreduce_local_typed(self.out, self.x, self.bucket, self.codec, self.mode, self.ws)
+
+    def payload_bytes(self, n):
+        return {2: n + 4 * nblocks(n), 1: 2 * n, 0: 0}[self.codec]
 
     def bytes_for(self, n):
         # every rank's gradients read, every payload written, the sum written
-        return self.k * self.esize * n + self.k * (n + 4 * nblocks(n)) + self.esize * n
+        return self.k * self.esize * n + self.k * self.payload_bytes(n) + self.esize * n
 
     def step_bytes(self):
         return sum(self.bytes_for(l) for _, l in self.W.ddp_buckets())
 
     def timed_kernel(self):
-        return (f"fused_fp8_kernel<4,{self.gb.GB_DTYPE_OF[self.dt]}>", self.step_bytes(), 1, self.step)
+        et = self.gb.GB_DTYPE_OF[self.dt]
+        name = {2: f"fused_fp8_kernel<4,{et}>", 1: f"fused_bf16_kernel<4,{et}>",
+                0: "reduce_sum_kernel<4,false>" if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]
+        return (name, self.step_bytes(), 1, self.step)
 
     def per_bucket_step(self):
         gb = self.gb
         for out, xs, ws in self.pb_args:
-            gb.gb_bucket_allreduce_local(out, xs, self.bucket, gb.GB_CODEC_FP8_E4M3_B256, self.mode, ws)
+            gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
 
     def extra(self, time_region, reps):
         """Throughput of the same pass issued as one call per bucket, as a DDP
@@ -203,7 +211,7 @@ class DdpBuckets(Workload):
         self.pb_args = []
         off = 0
         for start, length in self.W.ddp_buckets():
-            need = gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, self.k, length, self.bucket)
+            need = gb.gb_bucket_workspace_bytes(self.codec, self.k, length, self.bucket)
             self.pb_args.append((self.out[start:start + length],
                                  [t[start:start + length] for t in self.x],
                                  self.ws[off:off + need]))
@@ -240,18 +248,21 @@ class DdpBuckets(Workload):
             def factory():
                 xs = [host_values(torch, t[start:start + length]) for t in self.x]
                 if self.dt == "f32":
-                    compute = lambda: O.bucket_allreduce(xs, self.bucket, O.CODEC_FP8, self.mode)
+                    compute = lambda: O.bucket_allreduce(xs, self.bucket, self.codec, self.mode)
                 else:
-                    compute = lambda: O.bucket_allreduce_typed(xs, self.dt, self.bucket, O.CODEC_FP8, self.mode)
+                    compute = lambda: O.bucket_allreduce_typed(xs, self.dt, self.bucket, self.codec, self.mode)
 
                 def check(res):
                     want, codes, scales = res
                     ok = same_bits(host_values(torch, self.out[start:start + length]), want)
-                    for r in range(self.k):
-                        c0 = r * self.lay["codes_stride"] + start
-                        s0 = self.lay["scales_offset"] + r * self.lay["scales_stride"] + 4 * (start // 256)
-                        ok &= same_bits(self.ws[c0:c0 + length].cpu().numpy(), codes[r])
-                        ok &= same_bits(self.ws[s0:s0 + 4 * nblocks(length)].cpu().numpy(), scales[r].view("uint8"))
+                    cb = {2: 1, 1: 2, 0: 0}[self.codec]  # code bytes per value
+                    for r in range(self.k if cb else 0):
+                        c0 = r * self.lay["codes_stride"] + cb * start
+                        ok &= same_bits(self.ws[c0:c0 + cb * length].cpu().numpy(), codes[r].view("uint8"))
+                        if self.codec == 2:
+                            s0 = self.lay["scales_offset"] + r * self.lay["scales_stride"] + 4 * (start // 256)
+                            ok &= same_bits(self.ws[s0:s0 + 4 * nblocks(length)].cpu().numpy(),
+                                            scales[r].view("uint8"))
                     return ok
                 return Unit(self.bytes_for(length), compute, check)
             return factory
@@ -267,6 +278,8 @@ class DdpBucketsEF(DdpBuckets):
 
     def __init__(self, gb, torch, args):
         super().__init__(gb, torch, args)
+        if self.codec == gb.GB_CODEC_NONE or self.dt != "f32":
+            raise SystemExit("error feedback runs on float32 gradients with the bf16 or fp8 codec")
         self.config = dict(self.config, workload=self.name, error_feedback="fp32 residual per rank")
 
     def setup(self):
@@ -274,15 +287,15 @@ class DdpBucketsEF(DdpBuckets):
         self.res = [self.torch.zeros(self.n, dtype=self.torch.float32, device=self.dev) for _ in range(self.k)]
 
     def step(self):
-        self.gb.gb_bucket_allreduce_local_ef(self.out, self.x, self.res, self.bucket,
-                                             self.gb.GB_CODEC_FP8_E4M3_B256, self.mode, self.ws)
+        self.gb.gb_bucket_allreduce_local_ef(self.out, self.x, self.res, self.bucket, self.codec, self.mode, self.ws)
 
     def bytes_for(self, n):
         # sources and residuals read; payload, residuals and sum written
-        return self.k * 8 * n + self.k * (n + 4 * nblocks(n)) + self.k * 4 * n + 4 * n
+        return self.k * 8 * n + self.k * self.payload_bytes(n) + self.k * 4 * n + 4 * n
 
     def timed_kernel(self):
-        return ("fused_fp8_ef_kernel<4>", self.step_bytes(), 1, self.step)
+        name = "fused_fp8_ef_kernel<4>" if self.codec == self.gb.GB_CODEC_FP8_E4M3_B256 else "fused_bf16_ef_kernel<4>"
+        return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):
         return {}
@@ -307,15 +320,16 @@ class DdpBucketsEF(DdpBuckets):
 
             def factory():
                 xs = [t[start:start + length].cpu().numpy() for t in self.x]
-                compute = lambda: O.bucket_allreduce_ef(xs, before[i], self.bucket, O.CODEC_FP8, self.mode)
+                compute = lambda: O.bucket_allreduce_ef(xs, before[i], self.bucket, self.codec, self.mode)
 
                 def check(res):
                     want, codes, scales, res1 = res
                     ok = same_bits(self.out[start:start + length].cpu().numpy(), want)
+                    cb = 1 if self.codec == self.gb.GB_CODEC_FP8_E4M3_B256 else 2  # code bytes per value
                     for r in range(self.k):
                         ok &= same_bits(self.res[r][start:start + length].cpu().numpy(), res1[r])
-                        c0 = r * self.lay["codes_stride"] + start
-                        ok &= same_bits(self.ws[c0:c0 + length].cpu().numpy(), codes[r])
+                        c0 = r * self.lay["codes_stride"] + cb * start
+                        ok &= same_bits(self.ws[c0:c0 + cb * length].cpu().numpy(), codes[r].view("uint8"))
                     return ok
                 return Unit(self.bytes_for(length), compute, check)
             return factory
