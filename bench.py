@@ -31,7 +31,9 @@ Workloads (inputs from workloads.py):
                    gb_reduce; --dtype f16|bf16|f64|i8|u8|i32|i64 runs the
                    sweep in that element type through gb_reduce_typed.
   two_rank_4mib    k=2 x 2^20 fp32; gb_reduce_sum, gb_encode_bf16 of the sum,
-                   gb_decode_accumulate(bf16, k=1).
+                   gb_decode_accumulate(bf16, k=1).  The same outputs from
+                   gb_reduce_encode (sum and codes in one pass) + the decode
+                   are reported too.
   staged_fp8_256mib the leader's staged (pipelined) bridge step on one GPU:
                    its 2^26-value fp32 island sum encoded to fp8 and copied to
                    pinned host memory in 4 MiB chunks (gb_encode_staged), then
@@ -710,6 +712,32 @@ class TwoRank(Workload):
 
     def timed_kernel(self):
         return ("reduce_sum_kernel<2,false>", 12 * self.n, 1, lambda: self.gb.gb_reduce_sum(self.sum, self.x))
+
+    def fused_step(self):
+        gb = self.gb
+        gb.gb_reduce_encode(gb.GB_CODEC_BF16, self.codes2, None, self.x, self.sum2)
+        gb.gb_decode_accumulate(self.dec2, [self.codes2], None, gb.GB_CODEC_BF16)
+
+    def extra(self, time_region, reps):
+        """The same outputs (sum, bf16 codes of the sum, its decode) from two
+        launches: gb_reduce_encode writes the sum and its codes in one pass
+        (reads 8n, writes 4n + 2n), then the decode.  Checked bit for bit
+        against the three-call path."""
+        torch = self.torch
+        self.sum2 = torch.empty_like(self.sum)
+        self.codes2 = torch.empty_like(self.codes)
+        self.dec2 = torch.empty_like(self.dec)
+        reps = max(reps, 50)
+        self.fused_step()
+        torch.cuda.synchronize()
+        same = (torch.equal(self.sum2.view(torch.int32), self.sum.view(torch.int32))
+                and torch.equal(self.codes2.view(torch.int16), self.codes.view(torch.int16))
+                and torch.equal(self.dec2.view(torch.int32), self.dec.view(torch.int32)))
+        ms = time_region(self.fused_step, reps) / reps
+        base = time_region(self.step, reps) / reps
+        return {"fused_sum_encode_step_ms": round(ms, 4), "three_call_step_ms": round(base, 4),
+                "fused_sum_encode_gbs": round(20 * self.n / (ms * 1e-3) / 1e9, 2),
+                "fused_outputs_match": bool(same)}
 
     def cpu_units(self):
         """Sum, bf16 encode of the sum and its decode, on 2^18-value pieces."""

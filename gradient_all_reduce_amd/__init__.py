@@ -26,7 +26,7 @@ __all__ = [
     "gb_encode_bf16_ef", "gb_encode_fp8_e4m3_blockscaled_ef", "gb_bucket_allreduce_local_ef",
     "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
     "gb_encode_staged", "gb_decode_accumulate_staged", "gb_reduce_typed", "GB_DTYPE", "GB_DTYPE_OF",
-    "gb_encode", "gb_decode_sum", "gb_bucket_allreduce_local_typed",
+    "gb_encode", "gb_decode_sum", "gb_bucket_allreduce_local_typed", "gb_reduce_encode",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -58,6 +58,7 @@ _SIGNATURES = {
     "gb_reduce": (_I, [_P, _PP, _I, _S, _I, _I, _P]),
     "gb_reduce_typed": (_I, [_P, _PP, _I, _S, _I, _I, _I, _P]),
     "gb_encode": (_I, [_I, _I, _P, _P, _P, _S, _I, _P]),
+    "gb_reduce_encode": (_I, [_P, _P, _P, _PP, _I, _S, _I, _I, _P]),
     "gb_decode_sum": (_I, [_I, _P, _PP, _PP, _I, _S, _I, _P]),
     "gb_bucket_allreduce_local_typed": (_I, [_I, _P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
     "gb_encode_bf16": (_I, [_P, _P, _S, _P]),
@@ -163,6 +164,27 @@ def gb_reduce_typed(dst, srcs, op, divisor=1, stream=None):
     _same_numel(srcs, dst.numel(), "srcs")
     _check(_lib.gb_reduce_typed(_ptr(dst), _ptr_array(srcs), len(srcs), dst.numel(), GB_DTYPE[dst.dtype],
                                 int(op), int(divisor), _stream(stream, dst.device)))
+
+
+def gb_reduce_encode(codec, codes, scales, srcs, sum=None, scale_mode=GB_SCALE_ABSMAX_DIV_448, stream=None):
+    """The rank-order float32 sum of srcs encoded in one pass: codes (uint16
+    for bf16, uint8 for fp8) and, for fp8, scales; the sum itself is stored in
+    `sum` when given (required for more than 8 sources)."""
+    for i, s in enumerate(srcs):
+        _device_tensor(s, torch.float32, f"srcs[{i}]")
+    n = srcs[0].numel() if srcs else 0
+    _same_numel(srcs, n, "srcs")
+    _device_tensor(codes, _CODE_DTYPE[int(codec)] if int(codec) in _CODE_DTYPE else torch.uint8, "codes")
+    _same_numel([codes], n, "codes")
+    if scales is not None:
+        _device_tensor(scales, torch.float32, "scales")
+        _same_numel([scales], (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    if sum is not None:
+        _device_tensor(sum, torch.float32, "sum")
+        _same_numel([sum], n, "sum")
+    dev = srcs[0].device if srcs else codes.device
+    _check(_lib.gb_reduce_encode(_ptr(sum), _ptr(codes), _ptr(scales), _ptr_array(srcs), len(srcs), n, int(codec),
+                                 int(scale_mode), _stream(stream, dev)))
 
 
 def gb_encode_bf16(codes, src, stream=None):

@@ -404,6 +404,43 @@ gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes, const fl
   return from_hip(decode_groups(dst, codes, scales, k, n, codec, false, dtype, as_stream(stream)), fn);
 }
 
+gb_status gb_reduce_encode(float* sum, void* codes, float* scales, const float* const* srcs, int k, size_t n,
+                           int codec, int scale_mode, void* stream) {
+  const char* fn = "gb_reduce_encode";
+  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+  }
+  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  if (k > kR && sum == nullptr) {
+    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: more than %d sources are summed into sum first, which is NULL", fn,
+                k, kR);
+  }
+  if (n == 0) return GB_OK;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+  if (sum != nullptr && (s = check_array(sum, GB_ALIGN, fn, "sum")) != GB_OK) return s;
+  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+  if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  hipError_t e;
+  if (k <= kR) {
+    const gb::PtrTable t = slice(sp, 0, k);
+    e = fp8 ? gb::launch_reduce_encode_fp8(sum, static_cast<uint8_t*>(codes), scales, t, k, n, scale_mode, st)
+            : gb::launch_reduce_encode_bf16(sum, static_cast<uint16_t*>(codes), t, k, n, st);
+  } else {
+    // the rank-order sum first (further launches continue the fold), then its payload
+    e = sum_groups(sum, sp, k, n, false, st);
+    if (e == hipSuccess) {
+      e = fp8 ? gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, sum, n, scale_mode, GB_DTYPE_F32, st)
+              : gb::launch_encode_bf16(static_cast<uint16_t*>(codes), sum, n, GB_DTYPE_F32, st);
+    }
+  }
+  return from_hip(e, fn);
+}
+
 gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* scales_dev, void* codes_host,
                            float* scales_host, const float* src, size_t n, size_t chunk_elems, void* stream) {
   const char* fn = "gb_encode_staged";

@@ -36,6 +36,31 @@ __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, 
   else encode_bf16_body<ET, V, false>(codes, src, n);
 }
 
+// Island sum then bf16 encode in one pass: the rank-order float32 sum of K
+// sources, encoded as above and stored too when SUM (all sources are loaded
+// before anything is stored, so the sum may overwrite the first source).
+template <int K, bool SUM, bool FULL>
+__device__ __forceinline__ void reduce_encode_bf16_body(float* sum, uint16_t* codes, const PtrTable& src,
+                                                        size_t n) {
+  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (!FULL && i >= n) return;
+  f4 x[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) x[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), i, n);
+  f4 a = x[0];
+#pragma unroll
+  for (int r = 1; r < K; r++) a = a + x[r];
+  store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(a));
+  if (SUM) store4_at<FULL>(sum, i, n, a);
+}
+
+template <int K, bool SUM>
+__global__ __launch_bounds__(kThreads) void reduce_encode_bf16_kernel(float* sum, uint16_t* codes, PtrTable src,
+                                                                       size_t n) {
+  if (group_full(kVecPerGroup, n)) reduce_encode_bf16_body<K, SUM, true>(sum, codes, src, n);
+  else reduce_encode_bf16_body<K, SUM, false>(sum, codes, src, n);
+}
+
 template <int K, bool ACC, int ET, bool FULL>
 __device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n) {
   const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -150,6 +175,19 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 #define GB_CALL(ET) fused_bf16_t<ET>(out, srcs, c, k, n, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
+}
+
+hipError_t launch_reduce_encode_bf16(float* sum, uint16_t* codes, const PtrTable& srcs, int k, size_t n,
+                                    hipStream_t stream) {
+  const size_t grid = grid_for(n, 4);
+  if (grid == 0) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+#define GB_CALL(K)                                                                                     \
+  if (sum != nullptr) reduce_encode_bf16_kernel<K, true><<<grid, kThreads, 0, stream>>>(sum, codes, srcs, n); \
+  else reduce_encode_bf16_kernel<K, false><<<grid, kThreads, 0, stream>>>(sum, codes, srcs, n);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
 }
 
 }  // namespace gb

@@ -34,6 +34,48 @@ __global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, fl
 }
 
 // ===========================================================================
+// Island sum then fp8 encode in one pass: the rank-order float32 sum of K
+// sources, encoded exactly as the encoder above encodes a float32 array, and
+// stored too when SUM.  Every source is loaded before anything is stored, so
+// the sum may overwrite the first source.
+// ===========================================================================
+template <int K, bool SUM, bool FULL>
+__device__ __forceinline__ void reduce_encode_fp8_body(float* sum, uint8_t* codes, float* scales,
+                                                       const PtrTable& src, size_t n, int mode) {
+  const uint32_t col = threadIdx.x & 15u;
+  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  f4 x[K][4];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) x[r][j] = load4_at<FULL>(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n);
+  }
+  f4 a[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    a[j] = x[0][j];
+#pragma unroll
+    for (int r = 1; r < K; r++) a[j] = a[j] + x[r][j];
+  }
+  uint32_t w[4];
+  const float s = encode_block16(a, mode, w);  // all 64 lanes take part
+  if (!FULL && block * kBlock >= n) return;
+  if (col == 0u) scales[block] = s;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    store_codes4_at<FULL>(codes, lane_elem(block, j, col), n, w[j]);
+    if (SUM) store4_at<FULL>(sum, lane_elem(block, j, col), n, a[j]);
+  }
+}
+
+template <int K, bool SUM>
+__global__ __launch_bounds__(kThreads) void reduce_encode_fp8_kernel(float* sum, uint8_t* codes, float* scales,
+                                                                      PtrTable src, size_t n, int mode) {
+  if (group_full(kBlocksPerGroup * kBlock, n)) reduce_encode_fp8_body<K, SUM, true>(sum, codes, scales, src, n, mode);
+  else reduce_encode_fp8_body<K, SUM, false>(sum, codes, scales, src, n, mode);
+}
+
+// ===========================================================================
 // fp8 decode-accumulate over K payloads: one DPP row per block, each rank's
 // block scale read once per lane.
 // ===========================================================================
@@ -187,6 +229,23 @@ hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* cod
 #define GB_CALL(ET) fused_fp8_t<ET>(out, srcs, c, s, k, n, scale_mode, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
+}
+
+hipError_t launch_reduce_encode_fp8(float* sum, uint8_t* codes, float* scales, const PtrTable& srcs, int k,
+                                   size_t n, int scale_mode, hipStream_t stream) {
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+#define GB_CALL(K)                                                                                              \
+  if (sum != nullptr)                                                                                           \
+    reduce_encode_fp8_kernel<K, true><<<grid, kThreads, heavy_lds(K), stream>>>(sum, codes, scales, srcs, n,     \
+                                                                                scale_mode);                    \
+  else                                                                                                          \
+    reduce_encode_fp8_kernel<K, false><<<grid, kThreads, heavy_lds(K), stream>>>(sum, codes, scales, srcs, n,    \
+                                                                                 scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
 }
 
 }  // namespace gb

@@ -53,6 +53,13 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales, int k,
                             size_t n, int scale_mode, int dtype, hipStream_t stream);
 
+// The rank-order float32 sum of k sources encoded in one pass (sum stored too
+// when not NULL).
+hipError_t launch_reduce_encode_bf16(float* sum, uint16_t* codes, const PtrTable& srcs, int k, size_t n,
+                                    hipStream_t stream);
+hipError_t launch_reduce_encode_fp8(float* sum, uint8_t* codes, float* scales, const PtrTable& srcs, int k,
+                                   size_t n, int scale_mode, hipStream_t stream);
+
 // Error-feedback variants: residual (or residuals[r]) is read and rewritten.
 hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n,
                                  hipStream_t stream);

@@ -252,6 +252,29 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
                                     void* stream);
 
 /*
+ * gb_reduce_encode — the leader's island sum and its bridge payload in one
+ * pass (README "How it works": each island reduces onto its leader;
+ * "Bridge compression": leaders quantize their island's sum before the
+ * bridge step).  With the island's k contributions resident here:
+ *   sum[i]   = the rank-order fold of srcs[r][i], exactly as gb_reduce_sum;
+ *   payload  = codes (and, for fp8, scales) of that sum, exactly as
+ *              gb_encode_bf16 / gb_encode_fp8_e4m3_blockscaled encode it.
+ * Reads each source once and writes the payload (and the sum) once, instead
+ * of writing the sum and reading it back.
+ *   sum     device fp32[n], written; may be NULL to skip storing it when
+ *           k <= 8 (a larger k sums into it first, so it is then required:
+ *           GB_ERR_INVALID_ARG); may equal srcs[0].
+ *   codes   device uint16[n] (GB_CODEC_BF16) or uint8[n]
+ *           (GB_CODEC_FP8_E4M3_B256), written; must not overlap a source.
+ *   scales  device fp32[ceil(n/256)] for fp8 (ignored for bf16).
+ *   srcs    host array of k device fp32[n] pointers;  k 1 .. GB_MAX_K.
+ * GB_ERR_UNSUPPORTED for codec NONE or an unknown scale mode.
+ */
+gb_status gb_reduce_encode(float* sum, void* codes, float* scales,
+                           const float* const* srcs, int k, size_t n,
+                           int codec, int scale_mode, void* stream);
+
+/*
  * Bridge compression of float16, bfloat16 and float64 tensors (README
  * "Bridge compression": the bridged policies compress floating-point SUM and
  * AVG, and the dequantized payloads are added in float32).  The island sum,

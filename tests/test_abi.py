@@ -150,6 +150,15 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
      "rounded once from float32"),
     (lambda L: L.gb_bucket_allreduce_local_typed(2, ctypes.c_void_p(256), _arr(*[256] * 9), 9, 1000, 256, 2, 0,
                                                  ctypes.c_void_p(512), 1 << 24, None), 1, "rounded once"),
+    (lambda L: L.gb_reduce_encode(None, ctypes.c_void_p(256), None, _arr(256), 1, 10, 0, 0, None), 3,
+     "not bf16 or fp8"),
+    (lambda L: L.gb_reduce_encode(None, ctypes.c_void_p(256), None, _arr(256), 1, 10, 2, 5, None), 3, "scale mode"),
+    (lambda L: L.gb_reduce_encode(None, ctypes.c_void_p(256), None, _arr(*[256] * 9), 9, 10, 1, 0, None), 1,
+     "sum first"),
+    (lambda L: L.gb_reduce_encode(ctypes.c_void_p(264), ctypes.c_void_p(256), None, _arr(256), 1, 10, 1, 0, None), 2,
+     "sum"),
+    (lambda L: L.gb_reduce_encode(None, ctypes.c_void_p(256), ctypes.c_void_p(258), _arr(256), 1, 10, 2, 0, None), 2,
+     "scales"),
     (lambda L: L.gb_encode(0, 1, None, None, None, 10, 0, None), 3, "not bf16 or fp8"),
     (lambda L: L.gb_encode(1, 6, None, None, None, 10, 0, None), 3, "not a floating-point type"),
     (lambda L: L.gb_encode(2, 2, None, None, None, 10, 3, None), 3, "scale mode"),
@@ -194,6 +203,7 @@ def test_zero_length_returns_ok_without_pointers(gb):
     assert L.gb_reduce_sum(None, None, 2, 0, None) == 0
     assert L.gb_reduce_typed(None, None, 2, 0, 7, 2, 1, None) == 0
     assert L.gb_encode(2, 1, None, None, None, 0, 0, None) == 0
+    assert L.gb_reduce_encode(None, None, None, None, 3, 0, 2, 0, None) == 0
     assert L.gb_decode_sum(3, None, None, None, 2, 0, 2, None) == 0
     assert L.gb_bucket_allreduce_local_typed(2, None, None, 2, 0, 256, 2, 0, None, 0, None) == 0
     assert L.gb_encode_bf16(None, None, 0, None) == 0
