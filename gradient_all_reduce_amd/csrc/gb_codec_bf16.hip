@@ -16,7 +16,7 @@ namespace {
 // workgroups for the same bytes in flight); below that one vector is faster.
 template <int ET, int V, bool FULL>
 __device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const void* src, size_t n) {
-  const size_t base = (size_t)blockIdx.x * kVecPerGroup * V + (size_t)threadIdx.x * 4;
+  const size_t base = group_index<VecOrder>() * kVecPerGroup * V + (size_t)threadIdx.x * 4;
   f4 x[V];
 #pragma unroll
   for (int v = 0; v < V; v++) {
@@ -32,7 +32,7 @@ __device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const void* sr
 
 template <int ET, int V>
 __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, const void* src, size_t n) {
-  if (group_full(kVecPerGroup * V, n)) encode_bf16_body<ET, V, true>(codes, src, n);
+  if (group_full<VecOrder>(kVecPerGroup * V, n)) encode_bf16_body<ET, V, true>(codes, src, n);
   else encode_bf16_body<ET, V, false>(codes, src, n);
 }
 
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(uint16_t* codes, 
 template <int K, bool SUM, bool FULL>
 __device__ __forceinline__ void reduce_encode_bf16_body(float* sum, uint16_t* codes, const PtrTable& src,
                                                         size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   f4 x[K];
 #pragma unroll
@@ -57,13 +57,13 @@ __device__ __forceinline__ void reduce_encode_bf16_body(float* sum, uint16_t* co
 template <int K, bool SUM>
 __global__ __launch_bounds__(kThreads) void reduce_encode_bf16_kernel(float* sum, uint16_t* codes, PtrTable src,
                                                                        size_t n) {
-  if (group_full(kVecPerGroup, n)) reduce_encode_bf16_body<K, SUM, true>(sum, codes, src, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) reduce_encode_bf16_body<K, SUM, true>(sum, codes, src, n);
   else reduce_encode_bf16_body<K, SUM, false>(sum, codes, src, n);
 }
 
 template <int K, bool ACC, int ET, bool FULL>
 __device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   u2 w[K];
 #pragma unroll
@@ -80,7 +80,7 @@ __device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& code
 
 template <int K, bool ACC, int ET>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTable codes, size_t n) {
-  if (group_full(kVecPerGroup, n)) decode_bf16_body<K, ACC, ET, true>(acc, codes, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) decode_bf16_body<K, ACC, ET, true>(acc, codes, n);
   else decode_bf16_body<K, ACC, ET, false>(acc, codes, n);
 }
 
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTab
 // ===========================================================================
 template <int K, int ET, bool FULL>
 __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   f4 x[K];
 #pragma unroll
@@ -107,7 +107,7 @@ __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, 
 
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTable src, OutTable codes, size_t n) {
-  if (group_full(kVecPerGroup, n)) fused_bf16_body<K, ET, true>(out, src, codes, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) fused_bf16_body<K, ET, true>(out, src, codes, n);
   else fused_bf16_body<K, ET, false>(out, src, codes, n);
 }
 

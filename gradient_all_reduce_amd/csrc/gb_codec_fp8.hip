@@ -14,7 +14,7 @@ __device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, c
                                                 int mode) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
-  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) x[j] = load_vals4_at<ET, FULL>(src, lane_elem(block, j, col), n);
@@ -29,7 +29,7 @@ __device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, c
 template <int ET>
 __global__ __launch_bounds__(kThreads) void encode_fp8_kernel(uint8_t* codes, float* scales, const void* src,
                                                                size_t n, int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) encode_fp8_body<ET, true>(codes, scales, src, n, mode);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) encode_fp8_body<ET, true>(codes, scales, src, n, mode);
   else encode_fp8_body<ET, false>(codes, scales, src, n, mode);
 }
 
@@ -43,7 +43,7 @@ template <int K, bool SUM, bool FULL>
 __device__ __forceinline__ void reduce_encode_fp8_body(float* sum, uint8_t* codes, float* scales,
                                                        const PtrTable& src, size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[K][4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -71,7 +71,7 @@ __device__ __forceinline__ void reduce_encode_fp8_body(float* sum, uint8_t* code
 template <int K, bool SUM>
 __global__ __launch_bounds__(kThreads) void reduce_encode_fp8_kernel(float* sum, uint8_t* codes, float* scales,
                                                                       PtrTable src, size_t n, int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) reduce_encode_fp8_body<K, SUM, true>(sum, codes, scales, src, n, mode);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) reduce_encode_fp8_body<K, SUM, true>(sum, codes, scales, src, n, mode);
   else reduce_encode_fp8_body<K, SUM, false>(sum, codes, scales, src, n, mode);
 }
 
@@ -83,7 +83,7 @@ template <int K, bool ACC, int ET, bool FULL>
 __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes, const PtrTable& scales,
                                                 size_t n) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   if (!FULL && block * kBlock >= n) return;
   uint32_t w[K][4];
   float s[K];
@@ -114,7 +114,7 @@ __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes
 template <int K, bool ACC, int ET>
 __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTable codes, PtrTable scales,
                                                                size_t n) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) decode_fp8_body<K, ACC, ET, true>(acc, codes, scales, n);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) decode_fp8_body<K, ACC, ET, true>(acc, codes, scales, n);
   else decode_fp8_body<K, ACC, ET, false>(acc, codes, scales, n);
 }
 
@@ -126,7 +126,7 @@ template <int K, int ET, bool FULL>
 __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, const OutTable& codes,
                                                const OutTable& scales, size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[K][4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -159,7 +159,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable src, OutTable codes,
                                                               OutTable scales, size_t n, int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode);
   else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode);
 }
 

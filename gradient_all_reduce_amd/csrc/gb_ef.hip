@@ -13,7 +13,7 @@ namespace {
 // ===========================================================================
 template <bool FULL>
 __device__ __forceinline__ void encode_bf16_ef_body(uint16_t* codes, float* res, const float* src, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   const f4 y = load4_at<FULL>(src, i, n) + load4_at<FULL>(res, i, n);
   const u2 w = bf16_pack4(y);
@@ -23,7 +23,7 @@ __device__ __forceinline__ void encode_bf16_ef_body(uint16_t* codes, float* res,
 
 __global__ __launch_bounds__(kThreads) void encode_bf16_ef_kernel(uint16_t* codes, float* res, const float* src,
                                                                    size_t n) {
-  if (group_full(kVecPerGroup, n)) encode_bf16_ef_body<true>(codes, res, src, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) encode_bf16_ef_body<true>(codes, res, src, n);
   else encode_bf16_ef_body<false>(codes, res, src, n);
 }
 
@@ -31,7 +31,7 @@ template <bool FULL>
 __device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales, float* res, const float* src,
                                                    size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[4], r[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
@@ -53,7 +53,7 @@ __device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales
 
 __global__ __launch_bounds__(kThreads) void encode_fp8_ef_kernel(uint8_t* codes, float* scales, float* res,
                                                                   const float* src, size_t n, int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) encode_fp8_ef_body<true>(codes, scales, res, src, n, mode);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) encode_fp8_ef_body<true>(codes, scales, res, src, n, mode);
   else encode_fp8_ef_body<false>(codes, scales, res, src, n, mode);
 }
 
@@ -62,7 +62,7 @@ __device__ __forceinline__ void fused_fp8_ef_body(float* out, const PtrTable& sr
                                                   const OutTable& codes, const OutTable& scales, size_t n,
                                                   int mode) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = (size_t)blockIdx.x * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 y[K][4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -100,14 +100,14 @@ template <int K>
 __global__ __launch_bounds__(kThreads) void fused_fp8_ef_kernel(float* out, PtrTable src, OutTable resid,
                                                                  OutTable codes, OutTable scales, size_t n,
                                                                  int mode) {
-  if (group_full(kBlocksPerGroup * kBlock, n)) fused_fp8_ef_body<K, true>(out, src, resid, codes, scales, n, mode);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) fused_fp8_ef_body<K, true>(out, src, resid, codes, scales, n, mode);
   else fused_fp8_ef_body<K, false>(out, src, resid, codes, scales, n, mode);
 }
 
 template <int K, bool FULL>
 __device__ __forceinline__ void fused_bf16_ef_body(float* out, const PtrTable& src, const OutTable& resid,
                                                    const OutTable& codes, size_t n) {
-  const size_t i = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   f4 y[K];
 #pragma unroll
@@ -130,7 +130,7 @@ __device__ __forceinline__ void fused_bf16_ef_body(float* out, const PtrTable& s
 template <int K>
 __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(float* out, PtrTable src, OutTable resid,
                                                                   OutTable codes, size_t n) {
-  if (group_full(kVecPerGroup, n)) fused_bf16_ef_body<K, true>(out, src, resid, codes, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) fused_bf16_ef_body<K, true>(out, src, resid, codes, n);
   else fused_bf16_ef_body<K, false>(out, src, resid, codes, n);
 }
 

@@ -1,0 +1,191 @@
+"""Launches large enough to take their groups out of index order (the
+permuted workgroup order of the streaming kernels, used from about 3.4e7
+values for the kernels over 1024-value vector groups and from about 4e8 for
+the kernels over 4096-value fp8 groups) give, bit for bit, what the same call
+gives over slices of the stream small enough to keep the index order.
+
+Every result is elementwise (per value, or per 256-value fp8 block), so a
+call over a slice that starts on a bucket boundary computes exactly that
+slice of the whole call; the small-launch path is checked against the oracle
+by the other GPU tests, and the 1e9-value fp8 bucket stream against the
+oracle on sampled blocks.  Outputs start filled with a sentinel, so a group
+that no workgroup took shows as a difference.  Sizes end in a ragged tail
+that is not a whole number of runs of the permutation."""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W  # noqa: E402
+
+DEV = "cuda:0"
+B = W.DDP_BUCKET  # 6,553,600 values: a multiple of 4096
+N_VEC = 72_000_000 + 1234  # > 16 runs of 2048 groups of 2048 values
+N_BLK = 410_000_000 + 4096 * 7 + 99  # > 96 runs of 1024 groups of 4096 values
+STEP_VEC = 5 * B  # 32,768,000 values: fewer than 16 runs of 1024-value groups
+STEP_BLK = 50 * B  # 327,680,000 values: fewer than 96 runs of 4096-value groups
+SENTINEL = 0x7FBADBAD  # a float32 NaN no kernel writes
+
+
+@pytest.fixture(scope="module")
+def gb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gradient_all_reduce_amd as lib
+    return lib
+
+
+def slices(n, step):
+    return [(s, min(s + step, n)) for s in range(0, n, step)]
+
+
+def filled(n, dtype=torch.float32):
+    t = torch.empty(n, dtype=dtype, device=DEV)
+    if t.element_size() == 4:
+        t.view(torch.int32).fill_(SENTINEL)
+    else:
+        t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def bits(t):
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()])
+
+
+def same(a, b, what):
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a), bits(b)), what
+
+
+def test_vector_group_kernels(gb):
+    n = N_VEC
+    x = [W.device_gradients(n, 900 + r, DEV) for r in range(3)]
+    parts = slices(n, STEP_VEC)
+
+    # fixed-order sum and AVG
+    for op, div in ((None, 1), (gb.GB_OP_AVG, 3)):
+        whole, ref = filled(n), filled(n)
+        call = (lambda o, s: gb.gb_reduce_sum(o, s)) if op is None else (lambda o, s: gb.gb_reduce(o, s, op, div))
+        call(whole, x)
+        for s, e in parts:
+            call(ref[s:e], [t[s:e] for t in x])
+        same(whole, ref, f"reduce op={op}")
+
+    # bf16 encode (two vectors per lane at this size) and decode-accumulate
+    cw, cr = filled(n, torch.uint16), filled(n, torch.uint16)
+    gb.gb_encode_bf16(cw, x[0])
+    for s, e in parts:
+        gb.gb_encode_bf16(cr[s:e], x[0][s:e])
+    same(cw, cr, "encode bf16")
+    c2 = torch.empty(n, dtype=torch.uint16, device=DEV)
+    gb.gb_encode_bf16(c2, x[1])
+    whole, ref = filled(n), filled(n)
+    gb.gb_decode_accumulate(whole, [cw, c2], None, gb.GB_CODEC_BF16)
+    for s, e in parts:
+        gb.gb_decode_accumulate(ref[s:e], [cw[s:e], c2[s:e]], None, gb.GB_CODEC_BF16)
+    same(whole, ref, "decode bf16")
+
+    # the bf16 bucket stream, plain and with error feedback
+    ws = torch.empty(gb.gb_bucket_workspace_bytes(gb.GB_CODEC_BF16, 3, n, B), dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local(whole, x, B, gb.GB_CODEC_BF16, 0, ws)
+    for s, e in parts:
+        gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, gb.GB_CODEC_BF16, 0, ws)
+    same(whole, ref, "bf16 bucket stream")
+    rw = [torch.full((n,), 1e-5, device=DEV) for _ in range(3)]
+    rr = [t.clone() for t in rw]
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local_ef(whole, x, rw, B, gb.GB_CODEC_BF16, 0, ws)
+    for s, e in parts:
+        gb.gb_bucket_allreduce_local_ef(ref[s:e], [t[s:e] for t in x], [t[s:e] for t in rr], B,
+                                        gb.GB_CODEC_BF16, 0, ws)
+    same(whole, ref, "bf16 bucket stream with error feedback")
+    for r in range(3):
+        same(rw[r], rr[r], f"bf16 residual {r}")
+    del rw, rr
+
+    # island sum with its bf16 payload
+    sw, sr = filled(n), filled(n)
+    cw.view(torch.uint8).fill_(0xFF)
+    cr.view(torch.uint8).fill_(0xFF)
+    gb.gb_reduce_encode(gb.GB_CODEC_BF16, cw, None, x, sum=sw)
+    for s, e in parts:
+        gb.gb_reduce_encode(gb.GB_CODEC_BF16, cr[s:e], None, [t[s:e] for t in x], sum=sr[s:e])
+    same(sw, sr, "reduce_encode bf16 sum")
+    same(cw, cr, "reduce_encode bf16 codes")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
+def test_typed_reduce(gb, dt):
+    n = N_VEC
+    x = [W.device_gradients_typed(n, 950 + r, DEV, dt) for r in range(2)]
+    whole = filled(n, x[0].dtype)
+    ref = filled(n, x[0].dtype)
+    gb.gb_reduce_typed(whole, x, gb.GB_OP_AVG, 2)
+    for s, e in slices(n, STEP_VEC):
+        gb.gb_reduce_typed(ref[s:e], [t[s:e] for t in x], gb.GB_OP_AVG, 2)
+    same(whole, ref, f"typed AVG {dt}")
+
+
+def test_fp8_group_kernels(gb):
+    n = N_BLK
+    k = 4
+    x = [W.device_gradients(n, 970 + r, DEV) for r in range(k)]
+    parts = slices(n, STEP_BLK)
+    nb = (n + 255) // 256
+
+    # encode, then decode-accumulate of two ranks' payloads
+    codes = [filled(n, torch.uint8) for _ in range(2)]
+    scales = [filled(nb) for _ in range(2)]
+    cr, sr = filled(n, torch.uint8), filled(nb)
+    for r in range(2):
+        gb.gb_encode_fp8_e4m3_blockscaled(codes[r], scales[r], x[r], 0)
+    for s, e in parts:
+        gb.gb_encode_fp8_e4m3_blockscaled(cr[s:e], sr[s // 256:(e + 255) // 256], x[0][s:e], 0)
+    same(codes[0], cr, "encode fp8 codes")
+    same(scales[0], sr, "encode fp8 scales")
+    del cr, sr
+    whole, ref = filled(n), filled(n)
+    gb.gb_decode_accumulate(whole, codes, scales, gb.GB_CODEC_FP8_E4M3_B256)
+    for s, e in parts:
+        gb.gb_decode_accumulate(ref[s:e], [c[s:e] for c in codes], [t[s // 256:(e + 255) // 256] for t in scales],
+                                gb.GB_CODEC_FP8_E4M3_B256)
+    same(whole, ref, "decode fp8")
+
+    # island sum with its fp8 payload, the sum written over the first source
+    x0 = x[0].clone()
+    cw, sw = codes[0], scales[0]
+    cr, sr = filled(n, torch.uint8), filled(nb)
+    cw.fill_(0xFF)
+    sw.view(torch.int32).fill_(SENTINEL)
+    srcs = [x0] + x[1:2]
+    ref = filled(n)
+    for s, e in parts:
+        gb.gb_reduce_encode(gb.GB_CODEC_FP8_E4M3_B256, cr[s:e], sr[s // 256:(e + 255) // 256],
+                            [t[s:e] for t in srcs], sum=ref[s:e], scale_mode=1)
+    gb.gb_reduce_encode(gb.GB_CODEC_FP8_E4M3_B256, cw, sw, srcs, sum=x0, scale_mode=1)
+    same(x0, ref, "reduce_encode fp8 sum in place")
+    same(cw, cr, "reduce_encode fp8 codes")
+    same(sw, sr, "reduce_encode fp8 scales")
+    del x0, cr, sr, codes, scales, cw, sw, ref
+
+    # the fp8 bucket stream over 4 ranks, and with error feedback over 2
+    ws = torch.empty(gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, k, n, B), dtype=torch.uint8,
+                     device=DEV)
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local(whole, x, B, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
+    for s, e in parts:
+        gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
+    same(whole, ref, "fp8 bucket stream")
+    rw = [torch.full((n,), -2e-5, device=DEV) for _ in range(2)]
+    rr = [t.clone() for t in rw]
+    whole.view(torch.int32).fill_(SENTINEL)
+    ref.view(torch.int32).fill_(SENTINEL)
+    gb.gb_bucket_allreduce_local_ef(whole, x[:2], rw, B, gb.GB_CODEC_FP8_E4M3_B256, 1, ws)
+    for s, e in parts:
+        gb.gb_bucket_allreduce_local_ef(ref[s:e], [t[s:e] for t in x[:2]], [t[s:e] for t in rr], B,
+                                        gb.GB_CODEC_FP8_E4M3_B256, 1, ws)
+    same(whole, ref, "fp8 bucket stream with error feedback")
+    for r in range(2):
+        same(rw[r], rr[r], f"fp8 residual {r}")
