@@ -198,14 +198,27 @@ class DdpBuckets(Workload):
         for out, xs, ws in self.pb_args:
             gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
 
+    def per_bucket_step_two_streams(self):
+        """The per-bucket calls alternating between the current stream and a
+        second one (both at the default priority), forked from and joined
+        back into the current stream, so two buckets are in flight at once."""
+        torch, gb = self.torch, self.gb
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)
+        for i, (out, xs, ws) in enumerate(self.pb_args):
+            with torch.cuda.stream(main if i % 2 == 0 else self.side):
+                gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
+        main.wait_stream(self.side)
+
     def extra(self, time_region, reps):
         """Throughput of the same pass issued as one call per bucket, as a DDP
         hook would issue it, each bucket's payloads in its own slice of the
         workspace.  The 153 calls are captured once in a HIP graph and the
         graph is replayed, so the figure is the GPU's, not the Python
         binding's per-call cost; every replay's output is checked against the
-        single-launch result.  Leaves the workspace in the per-bucket layout.
-        Measured on float32 gradients only."""
+        single-launch result.  The same calls are also timed alternating over
+        two streams inside one graph.  Leaves the workspace in the per-bucket
+        layout.  Measured on float32 gradients only."""
         torch, gb = self.torch, self.gb
         if self.dt != "f32":
             return {}
@@ -232,8 +245,25 @@ class DdpBuckets(Workload):
         replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
         eager_ms = time_region(self.per_bucket_step, reps) / reps
         del graph
+        # the same calls over two streams: the buckets' workspace slices and
+        # output slices are disjoint, so two calls may run at once
+        self.side = torch.cuda.Stream()
+        self.per_bucket_step_two_streams()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.per_bucket_step_two_streams()
+        self.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        ms2 = time_region(graph.replay, reps) / reps
+        replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        del graph
         return {"per_bucket_calls_graph_gbs": round(self.step_bytes() / (ms * 1e-3) / 1e9, 2),
                 "per_bucket_calls_graph_ms": round(ms, 4),
+                "per_bucket_calls_two_streams_graph_gbs": round(self.step_bytes() / (ms2 * 1e-3) / 1e9, 2),
+                "per_bucket_calls_two_streams_graph_ms": round(ms2, 4),
                 "per_bucket_calls_eager_ms": round(eager_ms, 4),
                 "per_bucket_outputs_match": eager_ok and replay_ok}
 
