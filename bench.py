@@ -79,6 +79,11 @@ def parse():
                    help="bridge codec of the ddp_1b_buckets stream")
     p.add_argument("--dtype", default="f32", choices=["f32", "f16", "bf16", "f64", "i8", "u8", "i32", "i64"],
                    help="element type of the two_island_sweep workload")
+    p.add_argument("--shard", type=int, default=1,
+                   help="run one GPU's share of the workload when it is split over G GPUs: every "
+                        "bucket (or buffer) cut into G contiguous ranges aligned to 256 values, "
+                        "GPU 0's range kept (ddp_1b_buckets, ddp_1b_buckets_ef, gradients_256mib, "
+                        "gradients_64mib)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="rough budget of oracle CPU time for the baseline sample")
@@ -110,6 +115,19 @@ class Workload:
 
 def nblocks(n):
     return (n + 255) // 256
+
+
+def shard_len(length, g):
+    """Values of GPU 0's range when `length` values are cut into g contiguous
+    ranges aligned to 256 values (so no fp8 block straddles two GPUs)."""
+    return min(length, -(-length // (256 * g)) * 256)
+
+
+SHARDED = ("ddp_1b_buckets", "ddp_1b_buckets_ef", "gradients_256mib", "gradients_64mib")
+
+
+def shard_note(g):
+    return f"GPU 0 of {g}: each buffer cut into {g} contiguous ranges aligned to 256 values"
 
 
 class Unit:
@@ -150,6 +168,12 @@ class DdpBuckets(Workload):
         import workloads as W
         self.W = W
         self.k, self.n, self.bucket = 4, W.DDP_N, W.DDP_BUCKET
+        if args.shard > 1:
+            # each bucket is reduced across the GPUs on its own, so each is cut
+            pieces = [shard_len(l, args.shard) for _, l in W.ddp_buckets()]
+            self.bucket = shard_len(W.DDP_BUCKET, args.shard)
+            assert all(p == self.bucket for p in pieces[:-1])
+            self.n = sum(pieces)
         self.mode = args.scale_mode
         self.dt = args.dtype
         if self.dt not in ("f32", "f16", "bf16", "f64"):
@@ -158,10 +182,15 @@ class DdpBuckets(Workload):
         self.codec = {"fp8": gb.GB_CODEC_FP8_E4M3_B256, "bf16": gb.GB_CODEC_BF16, "none": gb.GB_CODEC_NONE}[
             getattr(args, "codec", "fp8")]
         self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n,
-                       "bucket_elems": self.bucket, "buckets": len(W.ddp_buckets()),
+                       "bucket_elems": self.bucket, "buckets": len(self.buckets()),
                        "codec": {2: "fp8_e4m3_b256", 1: "bf16", 0: "none"}[self.codec],
                        "scale_mode": ["absmax_div_448", "pow2"][self.mode],
                        "distribution": "N(0, sigma=1e-3)", "element_type": self.dt}
+        if args.shard > 1:
+            self.config["shard"] = shard_note(args.shard)
+
+    def buckets(self):
+        return self.W.ddp_buckets(self.n, self.bucket)
 
     def setup(self):
         torch, gb = self.torch, self.gb
@@ -185,7 +214,7 @@ class DdpBuckets(Workload):
         return self.k * self.esize * n + self.k * self.payload_bytes(n) + self.esize * n
 
     def step_bytes(self):
-        return sum(self.bytes_for(l) for _, l in self.W.ddp_buckets())
+        return sum(self.bytes_for(l) for _, l in self.buckets())
 
     def timed_kernel(self):
         et = self.gb.GB_DTYPE_OF[self.dt]
@@ -198,17 +227,20 @@ class DdpBuckets(Workload):
         for out, xs, ws in self.pb_args:
             gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
 
-    def per_bucket_step_two_streams(self):
-        """The per-bucket calls alternating between the current stream and a
-        second one (both at the default priority), forked from and joined
-        back into the current stream, so two buckets are in flight at once."""
+    def per_bucket_step_streams(self, m):
+        """The per-bucket calls dealt round-robin over the current stream and
+        m - 1 more (all at the default priority), forked from and joined back
+        into the current stream, so m buckets are in flight at once."""
         torch, gb = self.torch, self.gb
         main = torch.cuda.current_stream()
-        self.side.wait_stream(main)
+        streams = [main] + self.side[:m - 1]
+        for st in streams[1:]:
+            st.wait_stream(main)
         for i, (out, xs, ws) in enumerate(self.pb_args):
-            with torch.cuda.stream(main if i % 2 == 0 else self.side):
+            with torch.cuda.stream(streams[i % m]):
                 gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
-        main.wait_stream(self.side)
+        for st in streams[1:]:
+            main.wait_stream(st)
 
     def extra(self, time_region, reps):
         """Throughput of the same pass issued as one call per bucket, as a DDP
@@ -216,8 +248,8 @@ class DdpBuckets(Workload):
         workspace.  The 153 calls are captured once in a HIP graph and the
         graph is replayed, so the figure is the GPU's, not the Python
         binding's per-call cost; every replay's output is checked against the
-        single-launch result.  The same calls are also timed alternating over
-        two streams inside one graph.  Leaves the workspace in the per-bucket
+        single-launch result.  The same calls are also timed dealt over two and
+        over four streams inside one graph.  Leaves the workspace in the per-bucket
         layout.  Measured on float32 gradients only."""
         torch, gb = self.torch, self.gb
         if self.dt != "f32":
@@ -225,7 +257,7 @@ class DdpBuckets(Workload):
         want = self.out.clone()
         self.pb_args = []
         off = 0
-        for start, length in self.W.ddp_buckets():
+        for start, length in self.buckets():
             need = gb.gb_bucket_workspace_bytes(self.codec, self.k, length, self.bucket)
             self.pb_args.append((self.out[start:start + length],
                                  [t[start:start + length] for t in self.x],
@@ -245,25 +277,30 @@ class DdpBuckets(Workload):
         replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
         eager_ms = time_region(self.per_bucket_step, reps) / reps
         del graph
-        # the same calls over two streams: the buckets' workspace slices and
-        # output slices are disjoint, so two calls may run at once
-        self.side = torch.cuda.Stream()
-        self.per_bucket_step_two_streams()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            self.per_bucket_step_two_streams()
-        self.out.zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
-        ms2 = time_region(graph.replay, reps) / reps
-        replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
-        del graph
-        return {"per_bucket_calls_graph_gbs": round(self.step_bytes() / (ms * 1e-3) / 1e9, 2),
+        # the same calls over 2 and 4 streams: the buckets' workspace slices
+        # and output slices are disjoint, so several calls may run at once
+        self.side = [torch.cuda.Stream() for _ in range(3)]
+        by_streams = {}
+        for m in (2, 4):
+            self.per_bucket_step_streams(m)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                self.per_bucket_step_streams(m)
+            self.out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+            ms_m = time_region(graph.replay, reps) / reps
+            replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+            del graph
+            by_streams[m] = ms_m
+        gbs = lambda t: round(self.step_bytes() / (t * 1e-3) / 1e9, 2)
+        return {"per_bucket_calls_graph_gbs": gbs(ms),
                 "per_bucket_calls_graph_ms": round(ms, 4),
-                "per_bucket_calls_two_streams_graph_gbs": round(self.step_bytes() / (ms2 * 1e-3) / 1e9, 2),
-                "per_bucket_calls_two_streams_graph_ms": round(ms2, 4),
+                "per_bucket_calls_two_streams_graph_gbs": gbs(by_streams[2]),
+                "per_bucket_calls_four_streams_graph_gbs": gbs(by_streams[4]),
+                "per_bucket_calls_four_streams_graph_ms": round(by_streams[4], 4),
                 "per_bucket_calls_eager_ms": round(eager_ms, 4),
                 "per_bucket_outputs_match": eager_ok and replay_ok}
 
@@ -300,7 +337,7 @@ class DdpBuckets(Workload):
             return factory
 
         factories = [make(s + o, min(self.CPU_CHUNK, l - o))
-                     for s, l in self.W.ddp_buckets() for o in range(0, l, self.CPU_CHUNK)]
+                     for s, l in self.buckets() for o in range(0, l, self.CPU_CHUNK)]
         return factories, lambda m: (f"first {m} quarter-buckets ({m * self.CPU_CHUNK:,} values x {self.k} ranks) "
                                      f"of {len(factories)}")
 
@@ -339,7 +376,7 @@ class DdpBucketsEF(DdpBuckets):
         from oracle import oracle as O
         torch = self.torch
         pieces = []
-        for s, l in self.W.ddp_buckets():
+        for s, l in self.buckets():
             for o in range(0, l, self.CPU_CHUNK):
                 pieces.append((s + o, min(self.CPU_CHUNK, l - o)))
         pieces = pieces[:24]  # about 0.55 s of oracle work each
@@ -489,12 +526,14 @@ class Gradients256(Workload):
         super().__init__(gb, torch, args)
         import workloads as W
         self.W = W
-        self.k, self.n = 4, W.GRAD256_N
+        self.k, self.n = 4, shard_len(W.GRAD256_N, args.shard)
         self.mode = args.scale_mode
         self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n,
                        "codec": "fp8_e4m3_b256", "scale_mode": ["absmax_div_448", "pow2"][self.mode],
                        "distribution": "N(0, sigma=1e-3), 1% outliers x100",
                        "path": "4 x encode_fp8 + decode_accumulate"}
+        if args.shard > 1:
+            self.config["shard"] = shard_note(args.shard)
 
     def setup(self):
         torch = self.torch
@@ -555,10 +594,12 @@ class Gradients64(Workload):
         super().__init__(gb, torch, args)
         import workloads as W
         self.W = W
-        self.k, self.n = 4, W.GRAD64_N
+        self.k, self.n = 4, shard_len(W.GRAD64_N, args.shard)
         self.config = {"workload": self.name, "k": self.k, "n_per_rank": self.n, "codec": "bf16",
                        "distribution": "N(0, sigma=1e-3), 1% outliers x100",
                        "path": "4 x encode_bf16 + decode_accumulate"}
+        if args.shard > 1:
+            self.config["shard"] = shard_note(args.shard)
 
     def setup(self):
         torch = self.torch
@@ -916,6 +957,11 @@ def main():
               file=sys.stderr, flush=True)
         sys.exit(2)
 
+    if args.shard < 1 or (args.shard > 1 and args.workload not in SHARDED):
+        print(f"--shard G (G >= 1) applies to {', '.join(SHARDED)}; the sweep already spans the "
+              f"smaller sizes", file=sys.stderr, flush=True)
+        sys.exit(2)
+
     import torch
     import gradient_all_reduce_amd as gb
 
@@ -989,7 +1035,7 @@ def main():
         "data": "synthetic",
         "config": dict(wl.config, **extra),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(kname, wl.name),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(kname, wl.name if args.shard == 1 else f"{wl.name}_shard{args.shard}"),
                      "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3),
                      "frac_of_copy_ceiling": round(achieved / max(ceiling["library_copy_gbs"],
                                                                   ceiling["hipMemcpyDtoD_gbs"]), 4)},
