@@ -428,10 +428,21 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 // keeps 16k bytes of loads in flight per lane; measured on MI355X at 1e9
 // values per rank, 2 workgroups per compute unit move about 4% more bytes
 // per second than the 5 its registers allow (fewer concurrent streams of
-// requests at the memory), while 1 per unit is worse.  Kernels with fewer
-// bytes per lane lose heavily under any cap and get none.
+// requests at the memory), while 1 per unit is worse.  The fused bf16 pass
+// with error feedback (17 streams at k = 4) gains 6-11% from 6.7e7 values
+// per rank up under the same cap, and the plain fused bf16 pass nothing
+// that holds at bucket sizes.  Kernels with fewer bytes per lane lose
+// heavily under any cap and get none.
 constexpr unsigned kHeavyLds = 64u << 10;
 __host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kHeavyLds : 0u; }
+
+// The fused fp8 pass with error feedback keeps 21 memory streams open at
+// k = 4 (sources and residuals read; codes, scales, residuals and the sum
+// written).  With the workgroup order above it moves 2% more bytes per
+// second at one workgroup per compute unit (81 KiB reserved) than at two,
+// from 6.7e7 to 1e9 values per rank, and the same below and at k = 8.
+constexpr unsigned kEfLds = 81u << 10;
+__host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kEfLds : 0u; }
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 

@@ -164,7 +164,7 @@ hipError_t launch_fused_bf16_ef(float* out, const PtrTable& srcs, float* const* 
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-#define GB_CALL(K) fused_bf16_ef_kernel<K><<<grid, kThreads, 0, stream>>>(out, srcs, rs, c, n);
+#define GB_CALL(K) fused_bf16_ef_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, rs, c, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
@@ -181,7 +181,7 @@ hipError_t launch_fused_fp8_ef(float* out, const PtrTable& srcs, float* const* r
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
   (void)hipGetLastError();
-#define GB_CALL(K) fused_fp8_ef_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, rs, c, s, n, scale_mode);
+#define GB_CALL(K) fused_fp8_ef_kernel<K><<<grid, kThreads, ef_lds(K), stream>>>(out, srcs, rs, c, s, n, scale_mode);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
