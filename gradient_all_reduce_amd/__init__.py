@@ -36,6 +36,7 @@ GB_SCALE_ABSMAX_DIV_448, GB_SCALE_POW2 = 0, 1
 GB_OP_SUM, GB_OP_AVG, GB_OP_MAX, GB_OP_MIN = 0, 1, 2, 3
 GB_BLOCK = 256
 GB_MAX_K = 16
+GB_MAX_N = 1 << 39  # largest element count a call accepts
 # gb_dtype of each torch element type gb_reduce_typed takes
 GB_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3,
             torch.int8: 4, torch.uint8: 5, torch.int32: 6, torch.int64: 7}

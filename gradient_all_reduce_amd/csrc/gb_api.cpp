@@ -54,6 +54,11 @@ gb_status check_k(int k, const char* fn) {
   return GB_OK;
 }
 
+gb_status check_n(size_t n, const char* fn) {
+  if (n > GB_MAX_N) return fail(GB_ERR_INVALID_ARG, "%s: n = %zu exceeds GB_MAX_N = %zu", fn, n, GB_MAX_N);
+  return GB_OK;
+}
+
 gb_status check_array(const void* p, size_t align, const char* fn, const char* name) {
   if (p == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
   if (!aligned(p, align)) {
@@ -228,7 +233,7 @@ const char* gb_status_string(int status) {
 const char* gb_last_error(void) { return g_last_error; }
 
 size_t gb_payload_bytes(int codec, size_t n) {
-  if (!known_codec(codec)) return 0;
+  if (!known_codec(codec) || n > GB_MAX_N) return 0;
   return code_bytes(codec, n) + (codec == GB_CODEC_FP8_E4M3_B256 ? 4 * nblocks(n) : 0);
 }
 
@@ -239,6 +244,7 @@ gb_status gb_bucket_workspace_layout(int codec, int k, size_t n, size_t bucket_e
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
+  if ((s = check_n(n, fn)) != GB_OK) return s;
   if (bucket_elems == 0 || bucket_elems % GB_BLOCK != 0) {
     return fail(GB_ERR_INVALID_ARG, "%s: bucket_elems = %zu is not a positive multiple of %d", fn,
                 bucket_elems, GB_BLOCK);
@@ -272,6 +278,7 @@ gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n, v
   const char* fn = "gb_reduce_sum";
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   const void* const* sp = reinterpret_cast<const void* const*>(srcs);
@@ -289,6 +296,7 @@ gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n, int o
   }
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   const void* const* sp = reinterpret_cast<const void* const*>(srcs);
@@ -311,6 +319,7 @@ gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, i
   }
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
@@ -319,6 +328,7 @@ gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, i
 
 gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stream) {
   const char* fn = "gb_encode_bf16";
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
@@ -330,6 +340,7 @@ gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales, const fl
                                          int scale_mode, void* stream) {
   const char* fn = "gb_encode_fp8_e4m3_blockscaled";
   if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
@@ -347,6 +358,7 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float
   if (accumulate != 0 && accumulate != 1) {
     return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
   }
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
   if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
@@ -367,6 +379,7 @@ gb_status gb_encode(int codec, int dtype, void* codes, float* scales, const void
   if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
   const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
   if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
@@ -394,6 +407,7 @@ gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes, const fl
     return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a %s total is rounded once from float32, which holds up to %d "
                 "payloads per call; sum more into a float32 buffer", fn, k, "non-float32", kR);
   }
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
@@ -418,6 +432,7 @@ gb_status gb_reduce_encode(float* sum, void* codes, float* scales, const float* 
     return fail(GB_ERR_INVALID_ARG, "%s: k = %d: more than %d sources are summed into sum first, which is NULL", fn,
                 k, kR);
   }
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
@@ -453,6 +468,7 @@ gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* sc
     return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
                 GB_BLOCK);
   }
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   gb_status s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
@@ -472,8 +488,8 @@ gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* sc
   char* ch = static_cast<char*>(codes_host);
   hipError_t e = hipSuccess;
   size_t chunk = 0;
-  for (size_t o = 0; o < n && e == hipSuccess; o += chunk_elems, chunk++) {
-    const size_t l = n - o < chunk_elems ? n - o : chunk_elems;
+  for (size_t o = 0, l = 0; o < n && e == hipSuccess; o += l, chunk++) {
+    l = n - o < chunk_elems ? n - o : chunk_elems;
     hipStream_t cs = c->copy[chunk % kCopyStreams];
     e = fp8 ? gb::launch_encode_fp8(reinterpret_cast<uint8_t*>(cd + o), scales_dev + o / GB_BLOCK, src + o, l,
                                     scale_mode, GB_DTYPE_F32, st)
@@ -509,6 +525,7 @@ gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
     return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
                 GB_BLOCK);
   }
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
   if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
@@ -545,8 +562,8 @@ gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
                        c->copy[0]);
   }
   size_t chunk = 0;
-  for (size_t o = 0; o < n && e == hipSuccess; o += chunk_elems, chunk++) {
-    const size_t l = n - o < chunk_elems ? n - o : chunk_elems;
+  for (size_t o = 0, l = 0; o < n && e == hipSuccess; o += l, chunk++) {
+    l = n - o < chunk_elems ? n - o : chunk_elems;
     const int ci = (int)(chunk % kCopyStreams);
     const void* cp[GB_MAX_K];
     const float* sp[GB_MAX_K];
@@ -694,6 +711,7 @@ gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* cons
 
 gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n, void* stream) {
   const char* fn = "gb_encode_bf16_ef";
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
@@ -706,6 +724,7 @@ gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales, float
                                             size_t n, int scale_mode, void* stream) {
   const char* fn = "gb_encode_fp8_e4m3_blockscaled_ef";
   if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n > GB_MAX_N) return check_n(n, fn);
   if (n == 0) return GB_OK;
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;

@@ -35,8 +35,10 @@
  *    and no fused multiply-add: every sum is a left fold over ranks
  *    0, 1, ..., k-1 starting from rank 0's value, so a result does not depend
  *    on the launch configuration and is bit-reproducible.
- *  - Only fp32 SUM is supported, as the README's compression applies to
- *    floating-point SUM; the codecs never apply to other reductions.
+ *  - The codecs apply to floating-point SUM (and to AVG as a decode followed
+ *    by the division), as the README's compression does; MAX, MIN and the
+ *    integer types are reduced exactly, never compressed.
+ *  - n is at most GB_MAX_N; a larger n is GB_ERR_INVALID_ARG.
  */
 #ifndef GBREDUCE_H
 #define GBREDUCE_H
@@ -60,10 +62,14 @@ extern "C" {
 #define GB_MAX_K 16
 /* Required byte alignment of element arrays. */
 #define GB_ALIGN 16
+/* Largest element count any call accepts: 2^39 values (2 TiB of fp32 per
+ * buffer, beyond the memory of any one GPU), so that no size or offset the
+ * library computes from n can wrap. */
+#define GB_MAX_N ((size_t)1 << 39)
 
 typedef enum gb_status {
   GB_OK = 0,
-  GB_ERR_INVALID_ARG = 1, /* null pointer with n > 0, k out of range, bad flag, bad bucket size */
+  GB_ERR_INVALID_ARG = 1, /* null pointer with n > 0, n > GB_MAX_N, k out of range, bad flag, bad bucket size */
   GB_ERR_MISALIGNED = 2,  /* an element array is not 16-byte aligned, or a scale array not 4-byte */
   GB_ERR_UNSUPPORTED = 3, /* unknown codec or scale mode */
   GB_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than required */

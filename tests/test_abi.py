@@ -67,6 +67,50 @@ def test_constants_match_header(gb):
         assert gb.GB_DTYPE[dt] == v == O.DTYPES[name.lower()], name
 
 
+def test_max_n_matches_header(gb):
+    text = open(HEADER).read()
+    shift = int(re.search(r"#define GB_MAX_N \(\(size_t\)1 << (\d+)\)", text).group(1))
+    assert gb.GB_MAX_N == 1 << shift
+
+
+def test_oversized_n_is_rejected_before_anything_else(gb):
+    """n above GB_MAX_N fails as an invalid argument on every call that takes
+    n, before any pointer is looked at, so no size computed from it can wrap."""
+    L, big = gb._lib, gb.GB_MAX_N + 1
+    calls = {
+        "gb_reduce_sum": lambda: L.gb_reduce_sum(None, None, 2, big, None),
+        "gb_reduce": lambda: L.gb_reduce(None, None, 2, big, 1, 2, None),
+        "gb_reduce_typed": lambda: L.gb_reduce_typed(None, None, 2, big, 2, 0, 1, None),
+        "gb_encode_bf16": lambda: L.gb_encode_bf16(None, None, big, None),
+        "gb_encode_fp8_e4m3_blockscaled": lambda: L.gb_encode_fp8_e4m3_blockscaled(None, None, None, big, 0, None),
+        "gb_decode_accumulate": lambda: L.gb_decode_accumulate(None, None, None, 2, big, 2, 0, None),
+        "gb_encode": lambda: L.gb_encode(2, 0, None, None, None, big, 0, None),
+        "gb_decode_sum": lambda: L.gb_decode_sum(0, None, None, None, 2, big, 2, None),
+        "gb_reduce_encode": lambda: L.gb_reduce_encode(None, None, None, None, 2, big, 2, 0, None),
+        "gb_encode_staged": lambda: L.gb_encode_staged(2, 0, None, None, None, None, None, big, 1 << 20, None),
+        "gb_decode_accumulate_staged": lambda: L.gb_decode_accumulate_staged(None, None, None, None, None, 2, big,
+                                                                             1 << 20, 2, 0, None),
+        "gb_bucket_allreduce_local": lambda: L.gb_bucket_allreduce_local(None, None, 2, big, 256, 2, 0, None, 0,
+                                                                         None),
+        "gb_bucket_allreduce_local_typed": lambda: L.gb_bucket_allreduce_local_typed(0, None, None, 2, big, 256, 2,
+                                                                                     0, None, 0, None),
+        "gb_bucket_allreduce_local_ef": lambda: L.gb_bucket_allreduce_local_ef(None, None, None, 2, big, 256, 2, 0,
+                                                                               None, 0, None),
+        "gb_encode_bf16_ef": lambda: L.gb_encode_bf16_ef(None, None, None, big, None),
+        "gb_encode_fp8_e4m3_blockscaled_ef": lambda: L.gb_encode_fp8_e4m3_blockscaled_ef(None, None, None, None, big,
+                                                                                         0, None),
+    }
+    for name, call in calls.items():
+        assert call() == gb.GB_ERR_INVALID_ARG, name
+        assert gb.gb_last_error().startswith(name + ":") and "exceeds GB_MAX_N" in gb.gb_last_error(), name
+    for codec in (0, 1, 2):
+        assert gb.gb_payload_bytes(codec, big) == 0
+        assert gb.gb_payload_bytes(codec, gb.GB_MAX_N) > 0
+        assert gb.gb_bucket_workspace_bytes(codec, 2, big, 256) == 0
+    # the largest accepted n still sizes a workspace without wrapping
+    assert gb.gb_bucket_workspace_bytes(2, 16, gb.GB_MAX_N, 256) == 16 * (gb.GB_MAX_N + 4 * gb.GB_MAX_N // 256)
+
+
 def test_status_strings(gb):
     assert gb.gb_status_string(0) == "GB_OK"
     assert gb.gb_status_string(4) == "GB_ERR_WORKSPACE"
