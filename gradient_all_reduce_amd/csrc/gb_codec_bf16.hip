@@ -16,17 +16,16 @@ namespace {
 // workgroups for the same bytes in flight); below that one vector is faster.
 template <int ET, int V, bool FULL>
 __device__ __forceinline__ void encode_bf16_body(uint16_t* codes, const void* src, size_t n) {
-  const size_t base = group_index<VecOrder>() * kVecPerGroup * V + (size_t)threadIdx.x * 4;
+  const size_t sg0 = group_index<VecOrder>() * V;  // the workgroup's first 1024-value vector group
+  const uint32_t t = threadIdx.x;
   f4 x[V];
 #pragma unroll
   for (int v = 0; v < V; v++) {
-    const size_t i = base + (size_t)v * kVecPerGroup;
-    if (FULL || i < n) x[v] = load_vals4_at<ET, FULL>(src, i, n);
+    if (FULL || group_first<ET>(sg0 + v, t) < n) x[v] = load_group_vec<ET, FULL>(src, sg0 + v, t, n);
   }
 #pragma unroll
   for (int v = 0; v < V; v++) {
-    const size_t i = base + (size_t)v * kVecPerGroup;
-    if (FULL || i < n) store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(x[v]));
+    if (FULL || group_first<ET>(sg0 + v, t) < n) store_group_bf16<ET, FULL>(codes, sg0 + v, t, n, bf16_pack4(x[v]));
   }
 }
 
@@ -63,19 +62,20 @@ __global__ __launch_bounds__(kThreads) void reduce_encode_bf16_kernel(float* sum
 
 template <int K, bool ACC, int ET, bool FULL>
 __device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n) {
-  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
-  if (!FULL && i >= n) return;
+  const size_t sg = group_index<VecOrder>();
+  const uint32_t t = threadIdx.x;
+  if (!FULL && group_first<ET>(sg, t) >= n) return;
   u2 w[K];
 #pragma unroll
-  for (int r = 0; r < K; r++) w[r] = load_bf16_4_at<FULL>(static_cast<const uint16_t*>(codes.p[r]), i, n);
+  for (int r = 0; r < K; r++) w[r] = load_group_bf16<ET, FULL>(static_cast<const uint16_t*>(codes.p[r]), sg, t, n);
   f4 a;
-  if (ACC) a = load_vals4_at<ET, FULL>(acc, i, n);
+  if (ACC) a = load_group_vec<ET, FULL>(acc, sg, t, n);
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const f4 v = bf16_unpack4(w[r]);
     a = (!ACC && r == 0) ? v : a + v;
   }
-  store_vals4_at<ET, FULL>(acc, i, n, a);
+  store_group_vec<ET, FULL>(acc, sg, t, n, a);
 }
 
 template <int K, bool ACC, int ET>
@@ -89,20 +89,21 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTab
 // ===========================================================================
 template <int K, int ET, bool FULL>
 __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n) {
-  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
-  if (!FULL && i >= n) return;
+  const size_t sg = group_index<VecOrder>();
+  const uint32_t t = threadIdx.x;
+  if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 x[K];
 #pragma unroll
-  for (int r = 0; r < K; r++) x[r] = load_vals4_at<ET, FULL>(src.p[r], i, n);
+  for (int r = 0; r < K; r++) x[r] = load_group_vec<ET, FULL>(src.p[r], sg, t, n);
   f4 a;
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const u2 w = bf16_pack4(x[r]);
-    store_bf16_4_at<FULL>(static_cast<uint16_t*>(codes.p[r]), i, n, w);
+    store_group_bf16<ET, FULL>(static_cast<uint16_t*>(codes.p[r]), sg, t, n, w);
     const f4 v = bf16_unpack4(w);
     a = r == 0 ? v : a + v;
   }
-  store_vals4_at<ET, FULL>(out, i, n, a);
+  store_group_vec<ET, FULL>(out, sg, t, n, a);
 }
 
 template <int K, int ET>

@@ -17,13 +17,13 @@ __device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, c
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++) x[j] = load_vals4_at<ET, FULL>(src, lane_elem(block, j, col), n);
+  for (int j = 0; j < 4; j++) x[j] = load_block_vec<ET, FULL>(src, block, j, col, n);
   uint32_t w[4];
   const float s = encode_block16(x, mode, w);  // all 64 lanes take part
   if (!FULL && block * kBlock >= n) return;
   if (col == 0u) scales[block] = s;
 #pragma unroll
-  for (int j = 0; j < 4; j++) store_codes4_at<FULL>(codes, lane_elem(block, j, col), n, w[j]);
+  for (int j = 0; j < 4; j++) store_block_codes<ET, FULL>(codes, block, j, col, n, w[j]);
 }
 
 template <int ET>
@@ -91,13 +91,13 @@ __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes
   for (int r = 0; r < K; r++) {
     const uint8_t* c = static_cast<const uint8_t*>(codes.p[r]);
 #pragma unroll
-    for (int j = 0; j < 4; j++) w[r][j] = load_codes4_at<FULL>(c, lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) w[r][j] = load_block_codes<ET, FULL>(c, block, j, col, n);
     s[r] = static_cast<const float*>(scales.p[r])[block];
   }
   f4 a[4];
   if (ACC) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) a[j] = load_vals4_at<ET, FULL>(acc, lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) a[j] = load_block_vec<ET, FULL>(acc, block, j, col, n);
   }
 #pragma unroll
   for (int r = 0; r < K; r++) {
@@ -108,7 +108,7 @@ __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(acc, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store_block_vec<ET, FULL>(acc, block, j, col, n, a[j]);
 }
 
 template <int K, bool ACC, int ET>
@@ -131,7 +131,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
 #pragma unroll
   for (int r = 0; r < K; r++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) x[r][j] = load_vals4_at<ET, FULL>(src.p[r], lane_elem(block, j, col), n);
+    for (int j = 0; j < 4; j++) x[r][j] = load_block_vec<ET, FULL>(src.p[r], block, j, col, n);
   }
   const bool live = FULL || block * kBlock < n;
   f4 a[4];
@@ -143,7 +143,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
     if (live) {
       if (col == 0u) static_cast<float*>(scales.p[r])[block] = s;
 #pragma unroll
-      for (int j = 0; j < 4; j++) store_codes4_at<FULL>(c, lane_elem(block, j, col), n, w[j]);
+      for (int j = 0; j < 4; j++) store_block_codes<ET, FULL>(c, block, j, col, n, w[j]);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -153,7 +153,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
   }
   if (!live) return;
 #pragma unroll
-  for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(out, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store_block_vec<ET, FULL>(out, block, j, col, n, a[j]);
 }
 
 template <int K, int ET>

@@ -233,6 +233,29 @@ __device__ __forceinline__ void store_vals4_at(void* p, size_t i, size_t n, f4 v
   }
 }
 
+// float64 pairs and pairs of fp8 codes: 16 and 2 bytes per lane, clipped to n.
+template <bool FULL>
+__device__ __forceinline__ d2v load_f64x2_at(const double* d, size_t e, size_t n) {
+  if (FULL || e + 2 <= n) return __builtin_nontemporal_load(reinterpret_cast<const d2v*>(d + e));
+  return d2v{e < n ? d[e] : 0.0, 0.0};
+}
+template <bool FULL>
+__device__ __forceinline__ void store_f64x2_at(double* d, size_t e, size_t n, d2v v) {
+  if (FULL || e + 2 <= n) __builtin_nontemporal_store(v, reinterpret_cast<d2v*>(d + e));
+  else if (e < n) d[e] = v.x;
+}
+// Codes of elements [e, e + 2), the low byte first.
+template <bool FULL>
+__device__ __forceinline__ uint32_t load_codes2_at(const uint8_t* c, size_t e, size_t n) {
+  if (FULL || e + 2 <= n) return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(c + e));
+  return e < n ? (uint32_t)c[e] : 0u;
+}
+template <bool FULL>
+__device__ __forceinline__ void store_codes2_at(uint8_t* c, size_t e, size_t n, uint32_t h) {
+  if (FULL || e + 2 <= n) __builtin_nontemporal_store((uint16_t)h, reinterpret_cast<uint16_t*>(c + e));
+  else if (e < n) c[e] = (uint8_t)h;
+}
+
 // ---------------------------------------------------------------------------
 // fp8: OCP E4M3 (bias 7, largest finite 448 = 0x7E, S.1111.111 = NaN), one
 // fp32 scale per 256-value block.
@@ -356,6 +379,64 @@ __device__ __forceinline__ size_t lane_elem(size_t block, int j, uint32_t col) {
   return block * kBlock + (size_t)(16 * j + col) * 4;
 }
 
+// float64 values are 8 bytes: 4 consecutive ones are 32 bytes per lane, and a
+// row's 16-byte accesses would cover 512 bytes at half density.  For float64
+// a lane's vector j is instead two pairs 32 values apart, at
+// pair_elem(block, j, col) and 32 values further: each 16-byte access of a
+// row instruction then covers 256 contiguous bytes, and each 2-byte code
+// access of the row 32 contiguous bytes.  Which lane holds which values of a
+// block changes no result: the block maximum is taken over the whole row,
+// and every value and code keeps its own position in memory.
+__device__ __forceinline__ size_t pair_elem(size_t block, int j, uint32_t col) {
+  return block * kBlock + (size_t)(64 * j + 2 * col);
+}
+
+// A lane's vector j of a block (4 values as binary32, converted as
+// load_vals4_at converts), its store, and its 4 codes packed in one word
+// (value 0 in the low byte), placed by lane_elem or, for float64, pair_elem.
+template <int ET, bool FULL>
+__device__ __forceinline__ f4 load_block_vec(const void* p, size_t block, int j, uint32_t col, size_t n) {
+  if constexpr (ET != GB_DTYPE_F64) {
+    return load_vals4_at<ET, FULL>(p, lane_elem(block, j, col), n);
+  } else {
+    const double* d = static_cast<const double*>(p);
+    const size_t e = pair_elem(block, j, col);
+    const d2v lo = load_f64x2_at<FULL>(d, e, n), hi = load_f64x2_at<FULL>(d, e + 32, n);
+    return f4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+  }
+}
+template <int ET, bool FULL>
+__device__ __forceinline__ void store_block_vec(void* p, size_t block, int j, uint32_t col, size_t n, f4 v) {
+  if constexpr (ET != GB_DTYPE_F64) {
+    store_vals4_at<ET, FULL>(p, lane_elem(block, j, col), n, v);
+  } else {
+    double* d = static_cast<double*>(p);
+    const size_t e = pair_elem(block, j, col);
+    store_f64x2_at<FULL>(d, e, n, d2v{(double)v.x, (double)v.y});
+    store_f64x2_at<FULL>(d, e + 32, n, d2v{(double)v.z, (double)v.w});
+  }
+}
+template <int ET, bool FULL>
+__device__ __forceinline__ uint32_t load_block_codes(const uint8_t* c, size_t block, int j, uint32_t col, size_t n) {
+  if constexpr (ET != GB_DTYPE_F64) {
+    return load_codes4_at<FULL>(c, lane_elem(block, j, col), n);
+  } else {
+    const size_t e = pair_elem(block, j, col);
+    return load_codes2_at<FULL>(c, e, n) | (load_codes2_at<FULL>(c, e + 32, n) << 16);
+  }
+}
+template <int ET, bool FULL>
+__device__ __forceinline__ void store_block_codes(uint8_t* c, size_t block, int j, uint32_t col, size_t n,
+                                                  uint32_t w) {
+  if constexpr (ET != GB_DTYPE_F64) {
+    store_codes4_at<FULL>(c, lane_elem(block, j, col), n, w);
+  } else {
+    const size_t e = pair_elem(block, j, col);
+    store_codes2_at<FULL>(c, e, n, w & 0xFFFFu);
+    store_codes2_at<FULL>(c, e + 32, n, w >> 16);
+  }
+}
+
 // Encodes a lane's 16 values of one block (all 64 lanes must be active):
 // returns the block scale and writes the 4 packed code words to w.
 __device__ __forceinline__ float encode_block16(const f4 (&x)[4], int mode, uint32_t (&w)[4]) {
@@ -415,6 +496,66 @@ __device__ __forceinline__ size_t group_index() {
 template <class Order>
 __device__ __forceinline__ bool group_full(size_t per_group, size_t n) {
   return (group_index<Order>() + 1) * per_group <= n;
+}
+
+// A lane's 4 values of a 1024-value vector group sg (the bf16 codec's unit):
+// 4 consecutive values at 4 t for a 1-, 2- or 4-byte type; for float64 two
+// pairs, at 2 t and 512 values further, so that each 16-byte access of a
+// wavefront covers 1 KiB contiguous (4 consecutive doubles would be 32 bytes
+// per lane at half density) and each 4-byte code access 256 bytes.  Which
+// lane holds which values changes no result.
+template <int ET>
+__device__ __forceinline__ size_t group_first(size_t sg, uint32_t t) {
+  return sg * kVecPerGroup + (size_t)t * (ET == GB_DTYPE_F64 ? 2 : 4);
+}
+template <bool FULL>
+__device__ __forceinline__ uint32_t load_bf16_2_at(const uint16_t* c, size_t e, size_t n) {
+  if (FULL || e + 2 <= n) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c + e));
+  return e < n ? (uint32_t)c[e] : 0u;
+}
+template <bool FULL>
+__device__ __forceinline__ void store_bf16_2_at(uint16_t* c, size_t e, size_t n, uint32_t w) {
+  if (FULL || e + 2 <= n) __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(c + e));
+  else if (e < n) c[e] = (uint16_t)w;
+}
+template <int ET, bool FULL>
+__device__ __forceinline__ f4 load_group_vec(const void* p, size_t sg, uint32_t t, size_t n) {
+  const size_t e = group_first<ET>(sg, t);
+  if constexpr (ET != GB_DTYPE_F64) {
+    return load_vals4_at<ET, FULL>(p, e, n);
+  } else {
+    const double* d = static_cast<const double*>(p);
+    const d2v lo = load_f64x2_at<FULL>(d, e, n), hi = load_f64x2_at<FULL>(d, e + 512, n);
+    return f4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+  }
+}
+template <int ET, bool FULL>
+__device__ __forceinline__ void store_group_vec(void* p, size_t sg, uint32_t t, size_t n, f4 v) {
+  const size_t e = group_first<ET>(sg, t);
+  if constexpr (ET != GB_DTYPE_F64) {
+    store_vals4_at<ET, FULL>(p, e, n, v);
+  } else {
+    double* d = static_cast<double*>(p);
+    store_f64x2_at<FULL>(d, e, n, d2v{(double)v.x, (double)v.y});
+    store_f64x2_at<FULL>(d, e + 512, n, d2v{(double)v.z, (double)v.w});
+  }
+}
+// The 4 bf16 codes of those values, value 0 in the low half of word 0.
+template <int ET, bool FULL>
+__device__ __forceinline__ u2 load_group_bf16(const uint16_t* c, size_t sg, uint32_t t, size_t n) {
+  const size_t e = group_first<ET>(sg, t);
+  if constexpr (ET != GB_DTYPE_F64) return load_bf16_4_at<FULL>(c, e, n);
+  else return u2{load_bf16_2_at<FULL>(c, e, n), load_bf16_2_at<FULL>(c, e + 512, n)};
+}
+template <int ET, bool FULL>
+__device__ __forceinline__ void store_group_bf16(uint16_t* c, size_t sg, uint32_t t, size_t n, u2 w) {
+  const size_t e = group_first<ET>(sg, t);
+  if constexpr (ET != GB_DTYPE_F64) {
+    store_bf16_4_at<FULL>(c, e, n, w);
+  } else {
+    store_bf16_2_at<FULL>(c, e, n, w.x);
+    store_bf16_2_at<FULL>(c, e + 512, n, w.y);
+  }
 }
 
 // ---------------------------------------------------------------------------
