@@ -565,25 +565,31 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 
 // Dynamic LDS reserved per workgroup by the kernels that keep the most bytes
 // in flight.  No kernel uses LDS: reserving 64 KiB of the 160 KiB a compute
-// unit has caps it at 2 such workgroups.  A fused fp8 pass over k >= 4 ranks
-// keeps 16k bytes of loads in flight per lane; measured on MI355X at 1e9
-// values per rank, 2 workgroups per compute unit move about 4% more bytes
-// per second than the 5 its registers allow (fewer concurrent streams of
-// requests at the memory), while 1 per unit is worse.  The fused bf16 pass
-// with error feedback (17 streams at k = 4) gains 6-11% from 6.7e7 values
-// per rank up under the same cap, and the plain fused bf16 pass nothing
-// that holds at bucket sizes.  Kernels with fewer bytes per lane lose
-// heavily under any cap and get none.
-constexpr unsigned kHeavyLds = 64u << 10;
-__host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kHeavyLds : 0u; }
-
-// The fused fp8 pass with error feedback keeps 21 memory streams open at
-// k = 4 (sources and residuals read; codes, scales, residuals and the sum
-// written).  With the workgroup order above it moves 2% more bytes per
-// second at one workgroup per compute unit (81 KiB reserved) than at two,
-// from 6.7e7 to 1e9 values per rank, and the same below and at k = 8.
-constexpr unsigned kEfLds = 81u << 10;
-__host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kEfLds : 0u; }
+// unit has caps it at 2 such workgroups, 81 KiB at 1.
+//
+// Two per unit: a fused fp8 pass over k >= 4 ranks keeps 16k bytes of loads
+// in flight per lane; measured on MI355X at 1e9 values per rank, 2
+// workgroups per compute unit move about 4% more bytes per second than the 5
+// its registers allow (fewer concurrent streams of requests at the memory).
+// The fused bf16 pass with error feedback (17 streams at k = 4) gains 6-11%
+// from 6.7e7 values per rank up under the same cap, and the plain fused bf16
+// pass nothing that holds at bucket sizes.  Kernels with fewer bytes per
+// lane lose heavily under any cap and get none.
+//
+// One per unit: the fused fp8 pass with error feedback (21 streams at k = 4:
+// sources and residuals read; codes, scales, residuals and the sum written)
+// moves 2% more bytes per second than at two, from 6.7e7 to 1e9 values per
+// rank, and the same below and at k = 8; the fused fp8 pass over float64
+// gradients (32k bytes of loads per lane) 5% more at 5e8 values per rank
+// and the same at 6.7e7.
+constexpr unsigned kTwoPerCuLds = 64u << 10;
+constexpr unsigned kOnePerCuLds = 81u << 10;
+__host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kTwoPerCuLds : 0u; }
+__host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kOnePerCuLds : 0u; }
+template <int ET>
+__host__ __device__ constexpr unsigned fused_fp8_lds(int k) {
+  return ET == GB_DTYPE_F64 ? (k >= 4 ? kOnePerCuLds : 0u) : heavy_lds(k);
+}
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 
