@@ -696,3 +696,30 @@ void or_bucket_allreduce_typed(void* out, void* const* codes, float* const* scal
   free(sum);
   for (int r = 0; r < k; r++) free(f[r]);
 }
+
+/* Error feedback over the other floating types (reading: the error-feedback
+ * step of the README's "Bridge compression" runs in binary32 whatever the
+ * gradient's type, as the codecs do; the residual is binary32; only the
+ * conversion of the gradient on the way in and of the total on the way out
+ * depend on the type). */
+void or_encode_ef_typed(int codec, int dtype, void* codes, float* scales, float* residual,
+                        const void* x, size_t n, int mode) {
+  float* f = typed_array_to_f32(x, n, dtype);
+  if (codec == OR_CODEC_BF16) or_encode_bf16_ef((uint16_t*)codes, residual, f, n);
+  else or_encode_fp8_ef((uint8_t*)codes, scales, residual, f, n, mode);
+  free(f);
+}
+
+void or_bucket_allreduce_ef_typed(void* out, void* const* codes, float* const* scales,
+                                  float* const* residuals, const void* const* x, int k,
+                                  size_t n, size_t bucket_elems, int codec, int mode,
+                                  int dtype) {
+  float* f[64];
+  for (int r = 0; r < k; r++) f[r] = typed_array_to_f32(x[r], n, dtype);
+  float* sum = (float*)malloc((n ? n : 1) * sizeof(float));
+  or_bucket_allreduce_ef(sum, codes, scales, residuals, (const float* const*)f, k, n, bucket_elems,
+                         codec, mode);
+  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, sum[i]);
+  free(sum);
+  for (int r = 0; r < k; r++) free(f[r]);
+}

@@ -110,6 +110,17 @@ void or_bucket_allreduce_typed(void* out, void* const* codes, float* const* scal
                                const void* const* x, int k, size_t n, size_t bucket_elems,
                                int codec, int mode, int dtype);
 
+/* Error feedback over float16 / bfloat16 / float64 (or float32) arrays: the
+ * values go to binary32 as above, the binary32 error-feedback step runs on
+ * them with the binary32 residual, and the decoded binary32 total is rounded
+ * once to the type. */
+void or_encode_ef_typed(int codec, int dtype, void* codes, float* scales, float* residual,
+                        const void* x, size_t n, int mode);
+void or_bucket_allreduce_ef_typed(void* out, void* const* codes, float* const* scales,
+                                  float* const* residuals, const void* const* x, int k,
+                                  size_t n, size_t bucket_elems, int codec, int mode,
+                                  int dtype);
+
 #ifdef __cplusplus
 }
 #endif

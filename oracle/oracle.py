@@ -60,6 +60,8 @@ def _load():
         "or_encode_typed": (None, [_I, _I, _P, _P, _P, _S, _I]),
         "or_decode_sum_typed": (None, [_P, _I, _P, _P, _I, _S, _I]),
         "or_bucket_allreduce_typed": (None, [_P, _P, _P, _P, _I, _S, _S, _I, _I, _I]),
+        "or_encode_ef_typed": (None, [_I, _I, _P, _P, _P, _P, _S, _I]),
+        "or_bucket_allreduce_ef_typed": (None, [_P, _P, _P, _P, _P, _I, _S, _S, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -284,6 +286,41 @@ def decode_sum_typed(codes, scales, codec, dtype):
     out = np.empty(n, dtype=NP_DTYPES[dtype])
     _load().or_decode_sum_typed(_ptr(out), DTYPES[dtype], _ptr_array(codes), sp, len(codes), n, int(codec))
     return out
+
+
+def encode_ef_typed(x, residual, dtype, codec, mode=SCALE_ABSMAX_DIV_448):
+    """Error-feedback encode of a float16 / bfloat16 / float64 (or float32)
+    array with a binary32 residual: returns (codes, scales or None, new
+    residual)."""
+    x = _typed(x, dtype)
+    res = _f32(residual).copy()
+    n = x.size
+    if codec == CODEC_BF16:
+        codes, scales = np.empty(n, dtype=np.uint16), None
+    else:
+        codes, scales = np.empty(n, dtype=np.uint8), np.empty(nblocks(n), dtype=np.float32)
+    _load().or_encode_ef_typed(int(codec), DTYPES[dtype], _ptr(codes),
+                               _ptr(scales) if scales is not None else None, _ptr(res), _ptr(x), n, int(mode))
+    return codes, scales, res
+
+
+def bucket_allreduce_ef_typed(xs, residuals, dtype, bucket_elems, codec, mode=SCALE_ABSMAX_DIV_448):
+    """Bucket stream with error feedback over arrays of dtype, binary32
+    residuals.  Returns (out, codes, scales or None, new residuals)."""
+    xs = [_typed(x, dtype) for x in xs]
+    res = [_f32(r).copy() for r in residuals]
+    k, n = len(xs), xs[0].size
+    out = np.empty(n, dtype=NP_DTYPES[dtype])
+    if codec == CODEC_BF16:
+        codes, scales = [np.empty(n, dtype=np.uint16) for _ in range(k)], None
+    else:
+        codes = [np.empty(n, dtype=np.uint8) for _ in range(k)]
+        nb = sum(nblocks(min(bucket_elems, n - s)) for s in range(0, n, bucket_elems))
+        scales = [np.empty(nb, dtype=np.float32) for _ in range(k)]
+    _load().or_bucket_allreduce_ef_typed(
+        _ptr(out), _ptr_array(codes), _ptr_array(scales) if scales else None, _ptr_array(res),
+        _ptr_array(xs), k, n, int(bucket_elems), int(codec), int(mode), DTYPES[dtype])
+    return out, codes, scales, res
 
 
 def bucket_allreduce_typed(xs, dtype, bucket_elems, codec, mode=SCALE_ABSMAX_DIV_448):
