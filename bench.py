@@ -347,8 +347,8 @@ class DdpBucketsEF(DdpBuckets):
 
     def __init__(self, gb, torch, args):
         super().__init__(gb, torch, args)
-        if self.codec == gb.GB_CODEC_NONE or self.dt != "f32":
-            raise SystemExit("error feedback runs on float32 gradients with the bf16 or fp8 codec")
+        if self.codec == gb.GB_CODEC_NONE:
+            raise SystemExit("error feedback runs with the bf16 or fp8 codec")
         self.config = dict(self.config, workload=self.name, error_feedback="fp32 residual per rank")
 
     def setup(self):
@@ -356,14 +356,21 @@ class DdpBucketsEF(DdpBuckets):
         self.res = [self.torch.zeros(self.n, dtype=self.torch.float32, device=self.dev) for _ in range(self.k)]
 
     def step(self):
-        self.gb.gb_bucket_allreduce_local_ef(self.out, self.x, self.res, self.bucket, self.codec, self.mode, self.ws)
+        if self.dt == "f32":
+            self.gb.gb_bucket_allreduce_local_ef(self.out, self.x, self.res, self.bucket, self.codec, self.mode,
+                                                 self.ws)
+        else:
+            self.gb.gb_bucket_allreduce_local_ef_typed(self.out, self.x, self.res, self.bucket, self.codec, self.mode,
+                                                       self.ws)
 
     def bytes_for(self, n):
-        # sources and residuals read; payload, residuals and sum written
-        return self.k * 8 * n + self.k * self.payload_bytes(n) + self.k * 4 * n + 4 * n
+        # sources and (fp32) residuals read; payload, residuals and sum written
+        return self.k * (self.esize + 4) * n + self.k * self.payload_bytes(n) + self.k * 4 * n + self.esize * n
 
     def timed_kernel(self):
-        name = "fused_fp8_ef_kernel<4>" if self.codec == self.gb.GB_CODEC_FP8_E4M3_B256 else "fused_bf16_ef_kernel<4>"
+        et = self.gb.GB_DTYPE_OF[self.dt]
+        fp8 = self.codec == self.gb.GB_CODEC_FP8_E4M3_B256
+        name = f"fused_fp8_ef_kernel<4,{et}>" if fp8 else f"fused_bf16_ef_kernel<4,{et}>"
         return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):
@@ -388,12 +395,13 @@ class DdpBucketsEF(DdpBuckets):
             start, length = pieces[i]
 
             def factory():
-                xs = [t[start:start + length].cpu().numpy() for t in self.x]
-                compute = lambda: O.bucket_allreduce_ef(xs, before[i], self.bucket, self.codec, self.mode)
+                xs = [host_values(torch, t[start:start + length]) for t in self.x]
+                compute = lambda: O.bucket_allreduce_ef_typed(xs, before[i], self.dt, self.bucket, self.codec,
+                                                              self.mode)
 
                 def check(res):
                     want, codes, scales, res1 = res
-                    ok = same_bits(self.out[start:start + length].cpu().numpy(), want)
+                    ok = same_bits(host_values(torch, self.out[start:start + length]), want)
                     cb = 1 if self.codec == self.gb.GB_CODEC_FP8_E4M3_B256 else 2  # code bytes per value
                     for r in range(self.k):
                         ok &= same_bits(self.res[r][start:start + length].cpu().numpy(), res1[r])

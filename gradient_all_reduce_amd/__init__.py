@@ -69,6 +69,8 @@ _SIGNATURES = {
     "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
     "gb_bucket_allreduce_local_ef": (_I, [_P, _PP, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
+    "gb_encode_ef": (_I, [_I, _I, _P, _P, _P, _P, _S, _I, _P]),
+    "gb_bucket_allreduce_local_ef_typed": (_I, [_I, _P, _PP, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
     "gb_encode_staged": (_I, [_I, _I, _P, _P, _P, _P, _P, _S, _S, _P]),
     "gb_decode_accumulate_staged": (_I, [_P, _PP, _PP, _PP, _PP, _I, _S, _S, _I, _I, _P]),
     "gb_payload_bytes": (_S, [_I, _S]),
@@ -346,6 +348,46 @@ def gb_bucket_allreduce_local_ef(out, srcs, residuals, bucket_elems, codec,
                                              int(bucket_elems), int(codec), int(scale_mode), _ptr(workspace),
                                              ws_bytes, _stream(stream, out.device)))
 
+
+
+def gb_encode_ef(codec, codes, scales, residual, src, scale_mode=GB_SCALE_ABSMAX_DIV_448, stream=None):
+    """Error-feedback encode of src (float32, float16, bfloat16 or float64)
+    with a float32 residual: encodes binary32(src) + residual into codes (and,
+    for fp8, scales), updates residual."""
+    _float_tensor(src, "src")
+    n = src.numel()
+    _device_tensor(codes, _CODE_DTYPE[int(codec)] if int(codec) in _CODE_DTYPE else torch.uint8, "codes")
+    _device_tensor(residual, torch.float32, "residual")
+    _same_numel([codes, residual], n, "codes/residual")
+    if scales is not None:
+        _device_tensor(scales, torch.float32, "scales")
+        _same_numel([scales], (n + GB_BLOCK - 1) // GB_BLOCK, "scales")
+    _check(_lib.gb_encode_ef(int(codec), GB_DTYPE[src.dtype], _ptr(codes), _ptr(scales), _ptr(residual), _ptr(src),
+                             n, int(scale_mode), _stream(stream, src.device)))
+
+
+def gb_bucket_allreduce_local_ef_typed(out, srcs, residuals, bucket_elems, codec,
+                                       scale_mode=GB_SCALE_ABSMAX_DIV_448, workspace=None, stream=None):
+    """gb_bucket_allreduce_local_ef over float32, float16, bfloat16 or float64
+    gradients (out's type; srcs share it), float32 residuals."""
+    _float_tensor(out, "out")
+    n = out.numel()
+    for i, t in enumerate(srcs):
+        _device_tensor(t, out.dtype, f"srcs[{i}]")
+    for i, t in enumerate(residuals):
+        _device_tensor(t, torch.float32, f"residuals[{i}]")
+    _same_numel(srcs, n, "srcs")
+    _same_numel(residuals, n, "residuals")
+    if len(residuals) != len(srcs):
+        raise ValueError("one residual per source is needed")
+    ws_bytes = 0
+    if workspace is not None:
+        _device_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(_lib.gb_bucket_allreduce_local_ef_typed(GB_DTYPE[out.dtype], _ptr(out), _ptr_array(srcs),
+                                                   _ptr_array(residuals), len(srcs), n, int(bucket_elems),
+                                                   int(codec), int(scale_mode), _ptr(workspace), ws_bytes,
+                                                   _stream(stream, out.device)))
 
 def _host_pinned(t, name):
     if not isinstance(t, torch.Tensor):

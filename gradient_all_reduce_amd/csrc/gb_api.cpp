@@ -643,21 +643,22 @@ hipError_t bucket_groups(void* out, const void* const* srcs, float* const* resid
   const gb::PtrTable t = slice(srcs, 0, m);
   hipError_t e;
   if (residuals != nullptr && bf16) {
-    e = gb::launch_fused_bf16_ef(static_cast<float*>(out), t, residuals, reinterpret_cast<uint16_t* const*>(code), m,
-                                 n, st);
+    e = gb::launch_fused_bf16_ef(out, t, residuals, reinterpret_cast<uint16_t* const*>(code), m, n, dtype, st);
   } else if (residuals != nullptr) {
-    e = gb::launch_fused_fp8_ef(static_cast<float*>(out), t, residuals, reinterpret_cast<uint8_t* const*>(code),
-                                scale, m, n, mode, st);
+    e = gb::launch_fused_fp8_ef(out, t, residuals, reinterpret_cast<uint8_t* const*>(code), scale, m, n, mode, dtype,
+                                st);
   } else if (bf16) {
     e = gb::launch_fused_bf16(out, t, reinterpret_cast<uint16_t* const*>(code), m, n, dtype, st);
   } else {
     e = gb::launch_fused_fp8(out, t, reinterpret_cast<uint8_t* const*>(code), scale, m, n, mode, dtype, st);
   }
+  // more than kR ranks: float32 gradients only (checked by the callers)
   for (int r = kR; r < k && e == hipSuccess; r++) {
-    const float* x = static_cast<const float*>(srcs[r]);
+    const void* x = srcs[r];
     if (residuals != nullptr) {
-      e = bf16 ? gb::launch_encode_bf16_ef(static_cast<uint16_t*>(code[r]), residuals[r], x, n, st)
-               : gb::launch_encode_fp8_ef(static_cast<uint8_t*>(code[r]), scale[r], residuals[r], x, n, mode, st);
+      e = bf16 ? gb::launch_encode_bf16_ef(static_cast<uint16_t*>(code[r]), residuals[r], x, n, GB_DTYPE_F32, st)
+               : gb::launch_encode_fp8_ef(static_cast<uint8_t*>(code[r]), scale[r], residuals[r], x, n, mode,
+                                          GB_DTYPE_F32, st);
     } else {
       e = bf16 ? gb::launch_encode_bf16(static_cast<uint16_t*>(code[r]), x, n, GB_DTYPE_F32, st)
                : gb::launch_encode_fp8(static_cast<uint8_t*>(code[r]), scale[r], x, n, mode, GB_DTYPE_F32, st);
@@ -717,7 +718,7 @@ gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, 
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  return from_hip(gb::launch_encode_bf16_ef(codes, residual, src, n, as_stream(stream)), fn);
+  return from_hip(gb::launch_encode_bf16_ef(codes, residual, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
 }
 
 gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales, float* residual, const float* src,
@@ -731,7 +732,9 @@ gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales, float
   if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
   if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  return from_hip(gb::launch_encode_fp8_ef(codes, scales, residual, src, n, scale_mode, as_stream(stream)), fn);
+  return from_hip(gb::launch_encode_fp8_ef(codes, scales, residual, src, n, scale_mode, GB_DTYPE_F32,
+                                           as_stream(stream)),
+                  fn);
 }
 
 gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, float* const* residuals, int k,
@@ -751,6 +754,56 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, flo
   }
   return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32,
                                 static_cast<char*>(workspace), cs, so, ss, as_stream(stream)),
+                  fn);
+}
+
+gb_status gb_encode_ef(int codec, int dtype, void* codes, float* scales, float* residual, const void* src, size_t n,
+                       int scale_mode, void* stream) {
+  const char* fn = "gb_encode_ef";
+  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+  }
+  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  if (n > GB_MAX_N) return check_n(n, fn);
+  if (n == 0) return GB_OK;
+  gb_status s;
+  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+  if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+  if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
+  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  hipStream_t st = as_stream(stream);
+  if (fp8) {
+    return from_hip(gb::launch_encode_fp8_ef(static_cast<uint8_t*>(codes), scales, residual, src, n, scale_mode,
+                                             dtype, st),
+                    fn);
+  }
+  return from_hip(gb::launch_encode_bf16_ef(static_cast<uint16_t*>(codes), residual, src, n, dtype, st), fn);
+}
+
+gb_status gb_bucket_allreduce_local_ef_typed(int dtype, void* out, const void* const* srcs, float* const* residuals,
+                                             int k, size_t n, size_t bucket_elems, int codec, int scale_mode,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gb_bucket_allreduce_local_ef_typed";
+  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+  if (codec == GB_CODEC_NONE) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
+  }
+  size_t cs, so, ss;
+  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                             &so, &ss);
+  if (s != GB_OK) return s;
+  if (k > kR && dtype != GB_DTYPE_F32) {
+    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
+                "which holds up to %d ranks per call", fn, k, kR);
+  }
+  if (n == 0) return GB_OK;
+  if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
+    return s;
+  }
+  return from_hip(bucket_groups(out, srcs, residuals, k, n, codec, scale_mode, dtype, static_cast<char*>(workspace),
+                                cs, so, ss, as_stream(stream)),
                   fn);
 }
 

@@ -244,6 +244,18 @@ __device__ __forceinline__ void store_f64x2_at(double* d, size_t e, size_t n, d2
   if (FULL || e + 2 <= n) __builtin_nontemporal_store(v, reinterpret_cast<d2v*>(d + e));
   else if (e < n) d[e] = v.x;
 }
+// float32 pairs: the binary32 residual of a float64 gradient follows the
+// gradient's lane map.
+template <bool FULL>
+__device__ __forceinline__ f2 load_f32x2_at(const float* p, size_t e, size_t n) {
+  if (FULL || e + 2 <= n) return __builtin_nontemporal_load(reinterpret_cast<const f2*>(p + e));
+  return f2{e < n ? p[e] : 0.0f, 0.0f};
+}
+template <bool FULL>
+__device__ __forceinline__ void store_f32x2_at(float* p, size_t e, size_t n, f2 v) {
+  if (FULL || e + 2 <= n) __builtin_nontemporal_store(v, reinterpret_cast<f2*>(p + e));
+  else if (e < n) p[e] = v.x;
+}
 // Codes of elements [e, e + 2), the low byte first.
 template <bool FULL>
 __device__ __forceinline__ uint32_t load_codes2_at(const uint8_t* c, size_t e, size_t n) {
@@ -437,6 +449,28 @@ __device__ __forceinline__ void store_block_codes(uint8_t* c, size_t block, int 
   }
 }
 
+// A float32 array (a residual) placed by the lane map of element type MAP.
+template <int MAP, bool FULL>
+__device__ __forceinline__ f4 load_block_f32(const float* p, size_t block, int j, uint32_t col, size_t n) {
+  if constexpr (MAP != GB_DTYPE_F64) {
+    return load4_at<FULL>(p, lane_elem(block, j, col), n);
+  } else {
+    const size_t e = pair_elem(block, j, col);
+    const f2 lo = load_f32x2_at<FULL>(p, e, n), hi = load_f32x2_at<FULL>(p, e + 32, n);
+    return f4{lo.x, lo.y, hi.x, hi.y};
+  }
+}
+template <int MAP, bool FULL>
+__device__ __forceinline__ void store_block_f32(float* p, size_t block, int j, uint32_t col, size_t n, f4 v) {
+  if constexpr (MAP != GB_DTYPE_F64) {
+    store4_at<FULL>(p, lane_elem(block, j, col), n, v);
+  } else {
+    const size_t e = pair_elem(block, j, col);
+    store_f32x2_at<FULL>(p, e, n, f2{v.x, v.y});
+    store_f32x2_at<FULL>(p, e + 32, n, f2{v.z, v.w});
+  }
+}
+
 // Encodes a lane's 16 values of one block (all 64 lanes must be active):
 // returns the block scale and writes the 4 packed code words to w.
 __device__ __forceinline__ float encode_block16(const f4 (&x)[4], int mode, uint32_t (&w)[4]) {
@@ -555,6 +589,26 @@ __device__ __forceinline__ void store_group_bf16(uint16_t* c, size_t sg, uint32_
   } else {
     store_bf16_2_at<FULL>(c, e, n, w.x);
     store_bf16_2_at<FULL>(c, e + 512, n, w.y);
+  }
+}
+template <int MAP, bool FULL>
+__device__ __forceinline__ f4 load_group_f32(const float* p, size_t sg, uint32_t t, size_t n) {
+  const size_t e = group_first<MAP>(sg, t);
+  if constexpr (MAP != GB_DTYPE_F64) {
+    return load4_at<FULL>(p, e, n);
+  } else {
+    const f2 lo = load_f32x2_at<FULL>(p, e, n), hi = load_f32x2_at<FULL>(p, e + 512, n);
+    return f4{lo.x, lo.y, hi.x, hi.y};
+  }
+}
+template <int MAP, bool FULL>
+__device__ __forceinline__ void store_group_f32(float* p, size_t sg, uint32_t t, size_t n, f4 v) {
+  const size_t e = group_first<MAP>(sg, t);
+  if constexpr (MAP != GB_DTYPE_F64) {
+    store4_at<FULL>(p, e, n, v);
+  } else {
+    store_f32x2_at<FULL>(p, e, n, f2{v.x, v.y});
+    store_f32x2_at<FULL>(p, e + 512, n, f2{v.z, v.w});
   }
 }
 

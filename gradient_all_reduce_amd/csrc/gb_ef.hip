@@ -8,35 +8,40 @@ namespace {
 // Error feedback (README "Bridge compression": each bridge member keeps a
 // residual per buffer).  y = x + residual is encoded exactly as above, and
 // the residual becomes y minus the value the payload decodes to (rounded
-// binary32 subtraction; exact for bf16).  The residual is read and written
-// in place by the lane that owns the value.
+// binary32 subtraction; exact for bf16).  The residual is binary32 whatever
+// the gradient's element type ET: x is converted to binary32 as the codecs
+// convert it, and the decoded total is rounded once to ET.  The residual is
+// read and written in place by the lane that owns the value, through the
+// gradient's lane map.
 // ===========================================================================
-template <bool FULL>
-__device__ __forceinline__ void encode_bf16_ef_body(uint16_t* codes, float* res, const float* src, size_t n) {
-  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
-  if (!FULL && i >= n) return;
-  const f4 y = load4_at<FULL>(src, i, n) + load4_at<FULL>(res, i, n);
+template <int ET, bool FULL>
+__device__ __forceinline__ void encode_bf16_ef_body(uint16_t* codes, float* res, const void* src, size_t n) {
+  const size_t sg = group_index<VecOrder>();
+  const uint32_t t = threadIdx.x;
+  if (!FULL && group_first<ET>(sg, t) >= n) return;
+  const f4 y = load_group_vec<ET, FULL>(src, sg, t, n) + load_group_f32<ET, FULL>(res, sg, t, n);
   const u2 w = bf16_pack4(y);
-  store_bf16_4_at<FULL>(codes, i, n, w);
-  store4_at<FULL>(res, i, n, y - bf16_unpack4(w));
+  store_group_bf16<ET, FULL>(codes, sg, t, n, w);
+  store_group_f32<ET, FULL>(res, sg, t, n, y - bf16_unpack4(w));
 }
 
-__global__ __launch_bounds__(kThreads) void encode_bf16_ef_kernel(uint16_t* codes, float* res, const float* src,
+template <int ET>
+__global__ __launch_bounds__(kThreads) void encode_bf16_ef_kernel(uint16_t* codes, float* res, const void* src,
                                                                    size_t n) {
-  if (group_full<VecOrder>(kVecPerGroup, n)) encode_bf16_ef_body<true>(codes, res, src, n);
-  else encode_bf16_ef_body<false>(codes, res, src, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) encode_bf16_ef_body<ET, true>(codes, res, src, n);
+  else encode_bf16_ef_body<ET, false>(codes, res, src, n);
 }
 
-template <bool FULL>
-__device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales, float* res, const float* src,
+template <int ET, bool FULL>
+__device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales, float* res, const void* src,
                                                    size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
   f4 x[4], r[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    x[j] = load4_at<FULL>(src, lane_elem(block, j, col), n);
-    r[j] = load4_at<FULL>(res, lane_elem(block, j, col), n);
+    x[j] = load_block_vec<ET, FULL>(src, block, j, col, n);
+    r[j] = load_block_f32<ET, FULL>(res, block, j, col, n);
   }
 #pragma unroll
   for (int j = 0; j < 4; j++) x[j] = x[j] + r[j];  // y
@@ -46,19 +51,20 @@ __device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales
   if (col == 0u) scales[block] = s;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    store_codes4_at<FULL>(codes, lane_elem(block, j, col), n, w[j]);
-    store4_at<FULL>(res, lane_elem(block, j, col), n, x[j] - e4m3_unpack4(w[j]) * s);
+    store_block_codes<ET, FULL>(codes, block, j, col, n, w[j]);
+    store_block_f32<ET, FULL>(res, block, j, col, n, x[j] - e4m3_unpack4(w[j]) * s);
   }
 }
 
+template <int ET>
 __global__ __launch_bounds__(kThreads) void encode_fp8_ef_kernel(uint8_t* codes, float* scales, float* res,
-                                                                  const float* src, size_t n, int mode) {
-  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) encode_fp8_ef_body<true>(codes, scales, res, src, n, mode);
-  else encode_fp8_ef_body<false>(codes, scales, res, src, n, mode);
+                                                                  const void* src, size_t n, int mode) {
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) encode_fp8_ef_body<ET, true>(codes, scales, res, src, n, mode);
+  else encode_fp8_ef_body<ET, false>(codes, scales, res, src, n, mode);
 }
 
-template <int K, bool FULL>
-__device__ __forceinline__ void fused_fp8_ef_body(float* out, const PtrTable& src, const OutTable& resid,
+template <int K, int ET, bool FULL>
+__device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src, const OutTable& resid,
                                                   const OutTable& codes, const OutTable& scales, size_t n,
                                                   int mode) {
   const uint32_t col = threadIdx.x & 15u;
@@ -68,8 +74,8 @@ __device__ __forceinline__ void fused_fp8_ef_body(float* out, const PtrTable& sr
   for (int r = 0; r < K; r++) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      y[r][j] = load4_at<FULL>(static_cast<const float*>(src.p[r]), lane_elem(block, j, col), n) +
-                load4_at<FULL>(static_cast<const float*>(resid.p[r]), lane_elem(block, j, col), n);
+      y[r][j] = load_block_vec<ET, FULL>(src.p[r], block, j, col, n) +
+                load_block_f32<ET, FULL>(static_cast<const float*>(resid.p[r]), block, j, col, n);
     }
   }
   const bool live = FULL || block * kBlock < n;
@@ -85,106 +91,134 @@ __device__ __forceinline__ void fused_fp8_ef_body(float* out, const PtrTable& sr
     for (int j = 0; j < 4; j++) {
       const f4 v = e4m3_unpack4(w[j]) * s;
       if (live) {
-        store_codes4_at<FULL>(c, lane_elem(block, j, col), n, w[j]);
-        store4_at<FULL>(rp, lane_elem(block, j, col), n, y[r][j] - v);
+        store_block_codes<ET, FULL>(c, block, j, col, n, w[j]);
+        store_block_f32<ET, FULL>(rp, block, j, col, n, y[r][j] - v);
       }
       a[j] = r == 0 ? v : a[j] + v;
     }
   }
   if (!live) return;
 #pragma unroll
-  for (int j = 0; j < 4; j++) store4_at<FULL>(out, lane_elem(block, j, col), n, a[j]);
+  for (int j = 0; j < 4; j++) store_block_vec<ET, FULL>(out, block, j, col, n, a[j]);
 }
 
-template <int K>
-__global__ __launch_bounds__(kThreads) void fused_fp8_ef_kernel(float* out, PtrTable src, OutTable resid,
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_fp8_ef_kernel(void* out, PtrTable src, OutTable resid,
                                                                  OutTable codes, OutTable scales, size_t n,
                                                                  int mode) {
-  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) fused_fp8_ef_body<K, true>(out, src, resid, codes, scales, n, mode);
-  else fused_fp8_ef_body<K, false>(out, src, resid, codes, scales, n, mode);
+  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) fused_fp8_ef_body<K, ET, true>(out, src, resid, codes, scales, n, mode);
+  else fused_fp8_ef_body<K, ET, false>(out, src, resid, codes, scales, n, mode);
 }
 
-template <int K, bool FULL>
-__device__ __forceinline__ void fused_bf16_ef_body(float* out, const PtrTable& src, const OutTable& resid,
+template <int K, int ET, bool FULL>
+__device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& src, const OutTable& resid,
                                                    const OutTable& codes, size_t n) {
-  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
-  if (!FULL && i >= n) return;
+  const size_t sg = group_index<VecOrder>();
+  const uint32_t t = threadIdx.x;
+  if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 y[K];
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    y[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), i, n) +
-           load4_at<FULL>(static_cast<const float*>(resid.p[r]), i, n);
+    y[r] = load_group_vec<ET, FULL>(src.p[r], sg, t, n) +
+           load_group_f32<ET, FULL>(static_cast<const float*>(resid.p[r]), sg, t, n);
   }
   f4 a;
 #pragma unroll
   for (int r = 0; r < K; r++) {
     const u2 w = bf16_pack4(y[r]);
     const f4 v = bf16_unpack4(w);
-    store_bf16_4_at<FULL>(static_cast<uint16_t*>(codes.p[r]), i, n, w);
-    store4_at<FULL>(static_cast<float*>(resid.p[r]), i, n, y[r] - v);
+    store_group_bf16<ET, FULL>(static_cast<uint16_t*>(codes.p[r]), sg, t, n, w);
+    store_group_f32<ET, FULL>(static_cast<float*>(resid.p[r]), sg, t, n, y[r] - v);
     a = r == 0 ? v : a + v;
   }
-  store4_at<FULL>(out, i, n, a);
+  store_group_vec<ET, FULL>(out, sg, t, n, a);
 }
 
-template <int K>
-__global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(float* out, PtrTable src, OutTable resid,
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrTable src, OutTable resid,
                                                                   OutTable codes, size_t n) {
-  if (group_full<VecOrder>(kVecPerGroup, n)) fused_bf16_ef_body<K, true>(out, src, resid, codes, n);
-  else fused_bf16_ef_body<K, false>(out, src, resid, codes, n);
+  if (group_full<VecOrder>(kVecPerGroup, n)) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n);
+  else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n);
 }
 
-}  // namespace
-
-hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n,
-                                 hipStream_t stream) {
+template <int ET>
+hipError_t encode_bf16_ef_t(uint16_t* codes, float* residual, const void* src, size_t n, hipStream_t stream) {
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-  encode_bf16_ef_kernel<<<grid, kThreads, 0, stream>>>(codes, residual, src, n);
+  encode_bf16_ef_kernel<ET><<<grid, kThreads, 0, stream>>>(codes, residual, src, n);
   return hipGetLastError();
 }
 
-hipError_t launch_encode_fp8_ef(uint8_t* codes, float* scales, float* residual, const float* src, size_t n,
-                                int scale_mode, hipStream_t stream) {
+template <int ET>
+hipError_t encode_fp8_ef_t(uint8_t* codes, float* scales, float* residual, const void* src, size_t n,
+                           int scale_mode, hipStream_t stream) {
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-  encode_fp8_ef_kernel<<<grid, kThreads, 0, stream>>>(codes, scales, residual, src, n, scale_mode);
+  encode_fp8_ef_kernel<ET><<<grid, kThreads, 0, stream>>>(codes, scales, residual, src, n, scale_mode);
   return hipGetLastError();
 }
 
-hipError_t launch_fused_bf16_ef(float* out, const PtrTable& srcs, float* const* residuals,
-                                uint16_t* const* codes, int k, size_t n, hipStream_t stream) {
-  OutTable c = {}, rs = {};
-  for (int r = 0; r < k; r++) {
-    c.p[r] = codes[r];
-    rs.p[r] = residuals[r];
-  }
+template <int ET>
+hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, int k, size_t n,
+                           hipStream_t stream) {
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-#define GB_CALL(K) fused_bf16_ef_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, rs, c, n);
+#define GB_CALL(K) fused_bf16_ef_kernel<K, ET><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, rs, c, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
 }
 
-hipError_t launch_fused_fp8_ef(float* out, const PtrTable& srcs, float* const* residuals, uint8_t* const* codes,
-                               float* const* scales, int k, size_t n, int scale_mode, hipStream_t stream) {
+template <int ET>
+hipError_t fused_fp8_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, const OutTable& s,
+                          int k, size_t n, int scale_mode, hipStream_t stream) {
+  const size_t grid = grid_for(n, 16);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_fp8_ef_kernel<K, ET><<<grid, kThreads, ef_lds(K), stream>>>(out, srcs, rs, c, s, n, scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const void* src, size_t n, int dtype,
+                                 hipStream_t stream) {
+#define GB_CALL(ET) encode_bf16_ef_t<ET>(codes, residual, src, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_encode_fp8_ef(uint8_t* codes, float* scales, float* residual, const void* src, size_t n,
+                                int scale_mode, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) encode_fp8_ef_t<ET>(codes, scales, residual, src, n, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_bf16_ef(void* out, const PtrTable& srcs, float* const* residuals, uint16_t* const* codes,
+                                int k, size_t n, int dtype, hipStream_t stream) {
+  OutTable c = {}, rs = {};
+  for (int r = 0; r < k; r++) {
+    c.p[r] = codes[r];
+    rs.p[r] = residuals[r];
+  }
+#define GB_CALL(ET) fused_bf16_ef_t<ET>(out, srcs, rs, c, k, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_fp8_ef(void* out, const PtrTable& srcs, float* const* residuals, uint8_t* const* codes,
+                               float* const* scales, int k, size_t n, int scale_mode, int dtype, hipStream_t stream) {
   OutTable c = {}, s = {}, rs = {};
   for (int r = 0; r < k; r++) {
     c.p[r] = codes[r];
     s.p[r] = scales[r];
     rs.p[r] = residuals[r];
   }
-  const size_t grid = grid_for(n, 16);
-  if (grid == 0) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-#define GB_CALL(K) fused_fp8_ef_kernel<K><<<grid, kThreads, ef_lds(K), stream>>>(out, srcs, rs, c, s, n, scale_mode);
-  GB_DISPATCH_K(k, GB_CALL)
+#define GB_CALL(ET) fused_fp8_ef_t<ET>(out, srcs, rs, c, s, k, n, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
-  return hipGetLastError();
 }
 
 }  // namespace gb

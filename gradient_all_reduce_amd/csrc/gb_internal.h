@@ -60,14 +60,15 @@ hipError_t launch_reduce_encode_bf16(float* sum, uint16_t* codes, const PtrTable
 hipError_t launch_reduce_encode_fp8(float* sum, uint8_t* codes, float* scales, const PtrTable& srcs, int k,
                                    size_t n, int scale_mode, hipStream_t stream);
 
-// Error-feedback variants: residual (or residuals[r]) is read and rewritten.
-hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n,
+// Error-feedback variants over gradients of element type dtype (binary32
+// residuals): residual (or residuals[r]) is read and rewritten.
+hipError_t launch_encode_bf16_ef(uint16_t* codes, float* residual, const void* src, size_t n, int dtype,
                                  hipStream_t stream);
-hipError_t launch_encode_fp8_ef(uint8_t* codes, float* scales, float* residual, const float* src, size_t n,
-                                int scale_mode, hipStream_t stream);
-hipError_t launch_fused_bf16_ef(float* out, const PtrTable& srcs, float* const* residuals,
-                                uint16_t* const* codes, int k, size_t n, hipStream_t stream);
-hipError_t launch_fused_fp8_ef(float* out, const PtrTable& srcs, float* const* residuals, uint8_t* const* codes,
-                               float* const* scales, int k, size_t n, int scale_mode, hipStream_t stream);
+hipError_t launch_encode_fp8_ef(uint8_t* codes, float* scales, float* residual, const void* src, size_t n,
+                                int scale_mode, int dtype, hipStream_t stream);
+hipError_t launch_fused_bf16_ef(void* out, const PtrTable& srcs, float* const* residuals, uint16_t* const* codes,
+                                int k, size_t n, int dtype, hipStream_t stream);
+hipError_t launch_fused_fp8_ef(void* out, const PtrTable& srcs, float* const* residuals, uint8_t* const* codes,
+                               float* const* scales, int k, size_t n, int scale_mode, int dtype, hipStream_t stream);
 
 }  // namespace gb

@@ -365,6 +365,38 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs,
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * Error feedback over float16, bfloat16 and float64 gradients (the same
+ * README paragraph, over the floating types of the typed calls above).  The
+ * residual stays binary32, and the step is the binary32 one above applied to
+ * the gradient taken to binary32 as gb_encode takes it (exactly from float16
+ * and bfloat16; rounded once from float64, that rounding not being fed
+ * back):
+ *   y[i]        = RN(binary32(src[i]) + residual[i])
+ *   residual[i] = RN(y[i] - decoded payload value[i])
+ *
+ * gb_encode_ef — codes (and, for fp8, scales) of y for src of dtype[n],
+ *   residual updated; codec, dtype, scales and scale_mode as gb_encode.
+ *
+ * gb_bucket_allreduce_local_ef_typed — gb_bucket_allreduce_local_ef over
+ *   arrays of dtype: out and srcs[r] hold dtype[n], residuals[r] fp32[n];
+ *   out = the float32 rank-order total of the decoded payloads rounded once
+ *   to dtype (out may equal srcs[0]).  For a dtype other than F32, k is at
+ *   most 8, as for gb_bucket_allreduce_local_typed.  Everything else as
+ *   gb_bucket_allreduce_local_ef.
+ */
+gb_status gb_encode_ef(int codec, int dtype, void* codes, float* scales,
+                       float* residual, const void* src, size_t n,
+                       int scale_mode, void* stream);
+gb_status gb_bucket_allreduce_local_ef_typed(int dtype, void* out,
+                                             const void* const* srcs,
+                                             float* const* residuals, int k,
+                                             size_t n, size_t bucket_elems,
+                                             int codec, int scale_mode,
+                                             void* workspace,
+                                             size_t workspace_bytes,
+                                             void* stream);
+
+/*
  * Staged (pipelined) leader steps: the README's pipelined policy cuts the
  * bridge step into chunks so that the copy of one chunk to pinned host memory
  * overlaps the work on the next ("Collective policies": pipelined

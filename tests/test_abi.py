@@ -99,6 +99,9 @@ def test_oversized_n_is_rejected_before_anything_else(gb):
         "gb_encode_bf16_ef": lambda: L.gb_encode_bf16_ef(None, None, None, big, None),
         "gb_encode_fp8_e4m3_blockscaled_ef": lambda: L.gb_encode_fp8_e4m3_blockscaled_ef(None, None, None, None, big,
                                                                                          0, None),
+        "gb_encode_ef": lambda: L.gb_encode_ef(2, 2, None, None, None, None, big, 0, None),
+        "gb_bucket_allreduce_local_ef_typed": lambda: L.gb_bucket_allreduce_local_ef_typed(2, None, None, None, 2, big,
+                                                                                           256, 2, 0, None, 0, None),
     }
     for name, call in calls.items():
         assert call() == gb.GB_ERR_INVALID_ARG, name
@@ -236,6 +239,22 @@ def test_validation_rejects_before_launch(gb, call, status, msg):
      1, "chunk_elems"),
     (lambda L: L.gb_decode_accumulate_staged(ctypes.c_void_p(256), None, None, None, None, 17, 10, 256, 1, 0, None),
      1, "k = 17"),
+    (lambda L: L.gb_encode_ef(0, 2, None, None, None, None, 10, 0, None), 3, "not bf16 or fp8"),
+    (lambda L: L.gb_encode_ef(2, 5, None, None, None, None, 10, 0, None), 3, "not a floating-point type"),
+    (lambda L: L.gb_encode_ef(2, 2, None, None, None, None, 10, 7, None), 3, "scale mode"),
+    (lambda L: L.gb_encode_ef(1, 1, ctypes.c_void_p(256), None, ctypes.c_void_p(264), ctypes.c_void_p(256), 10, 0,
+                              None), 2, "residual"),
+    (lambda L: L.gb_encode_ef(2, 3, ctypes.c_void_p(256), None, ctypes.c_void_p(256), ctypes.c_void_p(256), 10, 0,
+                              None), 1, "scales is NULL"),
+    (lambda L: L.gb_bucket_allreduce_local_ef_typed(6, ctypes.c_void_p(256), _arr(256), _arr(512), 1, 1000, 256, 2,
+                                                    0, ctypes.c_void_p(512), 1 << 20, None), 3, "floating-point"),
+    (lambda L: L.gb_bucket_allreduce_local_ef_typed(2, ctypes.c_void_p(256), _arr(256), _arr(512), 1, 1000, 256, 0,
+                                                    0, None, 0, None), 3, "lossy codec"),
+    (lambda L: L.gb_bucket_allreduce_local_ef_typed(2, ctypes.c_void_p(256), _arr(*[256] * 9), _arr(*[512] * 9), 9,
+                                                    1000, 256, 2, 0, ctypes.c_void_p(512), 1 << 24, None), 1,
+     "k = 9"),
+    (lambda L: L.gb_bucket_allreduce_local_ef_typed(1, ctypes.c_void_p(256), _arr(256), _arr(516), 1, 1000, 256, 1,
+                                                    0, ctypes.c_void_p(512), 1 << 20, None), 2, "residuals[0]"),
 ])
 def test_validation_of_the_wider_calls(gb, call, status, msg):
     assert call(gb._lib) == status
@@ -254,3 +273,5 @@ def test_zero_length_returns_ok_without_pointers(gb):
     assert L.gb_encode_fp8_e4m3_blockscaled(None, None, None, 0, 0, None) == 0
     assert L.gb_decode_accumulate(None, None, None, 3, 0, 2, 0, None) == 0
     assert L.gb_bucket_allreduce_local(None, None, 2, 0, 256, 2, 0, None, 0, None) == 0
+    assert L.gb_encode_ef(2, 2, None, None, None, None, 0, 0, None) == 0
+    assert L.gb_bucket_allreduce_local_ef_typed(2, None, None, None, 2, 0, 256, 2, 0, None, 0, None) == 0

@@ -189,3 +189,21 @@ def test_fp8_group_kernels(gb):
     same(whole, ref, "fp8 bucket stream with error feedback")
     for r in range(2):
         same(rw[r], rr[r], f"fp8 residual {r}")
+
+
+@pytest.mark.parametrize("dt,codec,n,step", [("bf16", 2, N_BLK, STEP_BLK), ("f64", 1, N_VEC, STEP_VEC)])
+def test_typed_error_feedback(gb, dt, codec, n, step):
+    """Error feedback over bfloat16 gradients with the fp8 codec, and over
+    float64 gradients (their own lane map) with the bf16 codec, above the
+    thresholds."""
+    x = [W.device_gradients_typed(n, 990 + r, DEV, dt) for r in range(2)]
+    rw = [torch.full((n,), 1.5e-5, device=DEV) for _ in range(2)]
+    rr = [t.clone() for t in rw]
+    whole, ref = filled(n, x[0].dtype), filled(n, x[0].dtype)
+    ws = torch.empty(gb.gb_bucket_workspace_bytes(codec, 2, n, B), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_ef_typed(whole, x, rw, B, codec, 0, ws)
+    for s, e in slices(n, step):
+        gb.gb_bucket_allreduce_local_ef_typed(ref[s:e], [t[s:e] for t in x], [t[s:e] for t in rr], B, codec, 0, ws)
+    same(whole, ref, f"{dt} error-feedback stream")
+    for r in range(2):
+        same(rw[r], rr[r], f"{dt} residual {r}")

@@ -1,7 +1,7 @@
 """Randomised parity: many drawn configurations of every bucket-stream and
 reduction call (rank count 1..16, odd sizes and bucket lengths, each codec and
 scale mode, every element type, in place or not, with or without error
-feedback), each checked bit for bit against the oracle.  The draws are seeded,
+feedback over every floating type), each checked bit for bit against the oracle.  The draws are seeded,
 so a failure names a reproducible case."""
 import numpy as np
 import pytest
@@ -81,7 +81,7 @@ def test_bucket_stream(gb, seed):
     dt = str(rng.choice(["f32", "f32", "f16", "bf16", "f64"]))
     if codec != 0 and dt != "f32" and k > 8:
         k = int(rng.integers(1, 9))
-    ef = dt == "f32" and codec != 0 and rng.random() < 0.3
+    ef = codec != 0 and rng.random() < 0.3
     in_place = rng.random() < 0.3
     what = f"seed={seed} k={k} n={n} bucket={bucket} codec={codec} mode={mode} dt={dt} ef={ef} in_place={in_place}"
     xs = [draw_values(rng, dt, n) for _ in range(k)]
@@ -92,9 +92,12 @@ def test_bucket_stream(gb, seed):
     if ef:
         res0 = [(rng.standard_normal(n) * 1e-4).astype(np.float32) for _ in range(k)]
         res = [to_dev(r, "f32") for r in res0]
-        gb.gb_bucket_allreduce_local_ef(out, d, res, bucket, codec, mode, ws)
+        if dt == "f32":
+            gb.gb_bucket_allreduce_local_ef(out, d, res, bucket, codec, mode, ws)
+        else:
+            gb.gb_bucket_allreduce_local_ef_typed(out, d, res, bucket, codec, mode, ws)
         torch.cuda.synchronize()
-        want, _, _, res1 = O.bucket_allreduce_ef(xs, res0, bucket, codec, mode)
+        want, _, _, res1 = O.bucket_allreduce_ef_typed(xs, res0, dt, bucket, codec, mode)
         for r in range(k):
             same(res[r].cpu().numpy(), res1[r], "f32", what + f" residual {r}")
     else:

@@ -75,13 +75,15 @@ def device_gradients(n, seed, device):
 
 
 def typed(n, dtype, seed):
-    """n values of element type `dtype` ("f16", "bf16", "f64", "i8", "u8",
+    """n values of element type `dtype` ("f32", "f16", "bf16", "f64", "i8", "u8",
     "i32", "i64") from the given seed.  Floating types carry the N(0,1) draw:
     float16 by numpy's conversion, bfloat16 as the top 16 bits of the float32
     draw (uint16 codes, truncated: a draw, not a rounding under test), float64
     by widening.  Integer types are uniform over the type's whole range."""
-    if dtype in ("f16", "bf16", "f64"):
+    if dtype in ("f32", "f16", "bf16", "f64"):
         x = normal(n, seed)
+        if dtype == "f32":
+            return x
         if dtype == "f16":
             return x.astype(np.float16).view(np.uint16)
         if dtype == "bf16":
