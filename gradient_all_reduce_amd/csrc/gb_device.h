@@ -7,9 +7,10 @@
 // All of this work streams HBM: a few integer and float operations per 4-byte
 // element, no reuse, no contraction (so no MFMA).  The kernels are shaped for
 // that:
-//   * every lane moves 16-byte vectors (4-byte words for fp8 codes), and each
-//     load or store instruction of a 16-lane row covers 256 contiguous bytes,
-//     so requests coalesce into whole cache lines;
+//   * every lane moves 16-byte vectors of 4-byte values (8 bytes of 2-byte
+//     values, 4-byte words of fp8 codes), and each load or store instruction
+//     of a 16-lane row covers one contiguous run, so requests coalesce into
+//     whole cache lines; float64 has lane maps of its own that keep this;
 //   * loads and stores carry the non-temporal hint: each byte is touched once,
 //     so nothing is worth keeping in L2 or the last-level cache;
 //   * a lane issues all of its loads (every rank) before it computes, and the
@@ -20,7 +21,10 @@
 //     16 lanes holding 16 values each, a wavefront works on 4 blocks and a
 //     256-lane workgroup on 16;
 //   * E4M3 conversion uses gfx950's packed converters (v_cvt_pk_fp8_f32 to
-//     encode two values per instruction, v_cvt_pk_f32_fp8 to decode two).
+//     encode two values per instruction, v_cvt_pk_f32_fp8 to decode two);
+//   * large launches take their groups in a permuted order (group_index) that
+//     spreads the workgroups in flight over several regions of the stream,
+//     one contiguous chunk per XCD for the vector kernels.
 //
 // Arithmetic follows the gpubridge README, "How it works" (sum of island sums)
 // and "Bridge compression" (bf16; OCP E4M3 with one scale per 256 values;
