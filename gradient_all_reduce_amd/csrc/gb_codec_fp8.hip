@@ -15,15 +15,14 @@ __device__ __forceinline__ void encode_fp8_body(uint8_t* codes, float* scales, c
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t col = lane & 15u;
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  constexpr int MAP = codec_map<ET>();
   f4 x[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) x[j] = load_block_vec<ET, FULL>(src, block, j, col, n);
+  load_block<ET, MAP, FULL>(src, block, col, n, x);
   uint32_t w[4];
   const float s = encode_block16(x, mode, w);  // all 64 lanes take part
   if (!FULL && block * kBlock >= n) return;
   if (col == 0u) scales[block] = s;
-#pragma unroll
-  for (int j = 0; j < 4; j++) store_block_codes<ET, FULL>(codes, block, j, col, n, w[j]);
+  store_block_codes<MAP, FULL>(codes, block, col, n, w);
 }
 
 template <int ET>
@@ -84,21 +83,17 @@ __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes
                                                 size_t n) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  constexpr int MAP = codec_map<ET>();
   if (!FULL && block * kBlock >= n) return;
   uint32_t w[K][4];
   float s[K];
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    const uint8_t* c = static_cast<const uint8_t*>(codes.p[r]);
-#pragma unroll
-    for (int j = 0; j < 4; j++) w[r][j] = load_block_codes<ET, FULL>(c, block, j, col, n);
+    load_block_codes<MAP, FULL>(static_cast<const uint8_t*>(codes.p[r]), block, col, n, w[r]);
     s[r] = static_cast<const float*>(scales.p[r])[block];
   }
   f4 a[4];
-  if (ACC) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) a[j] = load_block_vec<ET, FULL>(acc, block, j, col, n);
-  }
+  if (ACC) load_block<ET, MAP, FULL>(acc, block, col, n, a);
 #pragma unroll
   for (int r = 0; r < K; r++) {
 #pragma unroll
@@ -107,8 +102,7 @@ __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes
       a[j] = (!ACC && r == 0) ? v : a[j] + v;
     }
   }
-#pragma unroll
-  for (int j = 0; j < 4; j++) store_block_vec<ET, FULL>(acc, block, j, col, n, a[j]);
+  store_block<ET, MAP, FULL>(acc, block, col, n, a);
 }
 
 template <int K, bool ACC, int ET>
@@ -127,12 +121,10 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
                                                const OutTable& scales, size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  constexpr int MAP = codec_map<ET>();
   f4 x[K][4];
 #pragma unroll
-  for (int r = 0; r < K; r++) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) x[r][j] = load_block_vec<ET, FULL>(src.p[r], block, j, col, n);
-  }
+  for (int r = 0; r < K; r++) load_block<ET, MAP, FULL>(src.p[r], block, col, n, x[r]);
   const bool live = FULL || block * kBlock < n;
   f4 a[4];
 #pragma unroll
@@ -142,8 +134,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
     uint8_t* c = static_cast<uint8_t*>(codes.p[r]);
     if (live) {
       if (col == 0u) static_cast<float*>(scales.p[r])[block] = s;
-#pragma unroll
-      for (int j = 0; j < 4; j++) store_block_codes<ET, FULL>(c, block, j, col, n, w[j]);
+      store_block_codes<MAP, FULL>(c, block, col, n, w);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -152,8 +143,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
     }
   }
   if (!live) return;
-#pragma unroll
-  for (int j = 0; j < 4; j++) store_block_vec<ET, FULL>(out, block, j, col, n, a[j]);
+  store_block<ET, MAP, FULL>(out, block, col, n, a);
 }
 
 template <int K, int ET>

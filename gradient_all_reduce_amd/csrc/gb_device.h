@@ -395,83 +395,184 @@ __device__ __forceinline__ size_t lane_elem(size_t block, int j, uint32_t col) {
   return block * kBlock + (size_t)(16 * j + col) * 4;
 }
 
-// float64 values are 8 bytes: 4 consecutive ones are 32 bytes per lane, and a
-// row's 16-byte accesses would cover 512 bytes at half density.  For float64
-// a lane's vector j is instead two pairs 32 values apart, at
-// pair_elem(block, j, col) and 32 values further: each 16-byte access of a
-// row instruction then covers 256 contiguous bytes, and each 2-byte code
-// access of the row 32 contiguous bytes.  Which lane holds which values of a
-// block changes no result: the block maximum is taken over the whole row,
-// and every value and code keeps its own position in memory.
+// Lane maps of a block's 256 values.  A lane of row col holds 16 values of
+// the block as 4 vectors of 4; the map says which, chosen per element type
+// so that every access of a row instruction is one contiguous run:
+//   kMapNarrow: vector j is the 4 consecutive values at lane_elem(block, j,
+//     col) (16 bytes of 4-byte values per access);
+//   kMapWide (2-byte types): vectors 2m and 2m + 1 are the 8 consecutive
+//     values at wide_elem(block, 2m, col), moved by one 16-byte access (and
+//     their codes by one 8-byte access) instead of two 8-byte ones;
+//   kMapPair (float64): vector j is two pairs of values 32 apart, at
+//     pair_elem(block, j, col) and 32 further, each pair one 16-byte access
+//     (4 consecutive doubles would be 32 bytes per lane at half density).
+// Which lane holds which values of a block changes no result: the block
+// maximum is taken over the whole row, and every value and code keeps its own
+// position in memory.
+enum : int { kMapNarrow = 0, kMapWide = 1, kMapPair = 2 };
+template <int ET>
+__host__ __device__ constexpr int codec_map() {
+  return ET == GB_DTYPE_F64 ? kMapPair : (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) ? kMapWide : kMapNarrow;
+}
+// The error-feedback kernels keep the float32 residual on the gradient's map;
+// the wide map would read it at half density, so 2-byte gradients stay narrow.
+template <int ET>
+__host__ __device__ constexpr int ef_map() {
+  return ET == GB_DTYPE_F64 ? kMapPair : kMapNarrow;
+}
+
+__device__ __forceinline__ size_t wide_elem(size_t block, int j, uint32_t col) {
+  return block * kBlock + (size_t)(128 * (j >> 1) + 8 * col + 4 * (j & 1));
+}
 __device__ __forceinline__ size_t pair_elem(size_t block, int j, uint32_t col) {
   return block * kBlock + (size_t)(64 * j + 2 * col);
 }
+template <int MAP>
+__device__ __forceinline__ size_t vec_elem(size_t block, int j, uint32_t col) {
+  return MAP == kMapWide ? wide_elem(block, j, col) : lane_elem(block, j, col);
+}
 
-// A lane's vector j of a block (4 values as binary32, converted as
-// load_vals4_at converts), its store, and its 4 codes packed in one word
-// (value 0 in the low byte), placed by lane_elem or, for float64, pair_elem.
-template <int ET, bool FULL>
-__device__ __forceinline__ f4 load_block_vec(const void* p, size_t block, int j, uint32_t col, size_t n) {
-  if constexpr (ET != GB_DTYPE_F64) {
-    return load_vals4_at<ET, FULL>(p, lane_elem(block, j, col), n);
+typedef uint32_t u4w __attribute__((ext_vector_type(4)));
+
+// 8 consecutive 2-byte values at element e as two binary32 vectors, and back.
+template <int ET>
+__device__ __forceinline__ void load8_half(const void* p, size_t e, f4& a, f4& b) {
+  const u4w w = __builtin_nontemporal_load(reinterpret_cast<const u4w*>(static_cast<const uint16_t*>(p) + e));
+  if constexpr (ET == GB_DTYPE_BF16) {
+    a = bf16_unpack4(u2{w.x, w.y});
+    b = bf16_unpack4(u2{w.z, w.w});
   } else {
+    const h4 ha = __builtin_bit_cast(h4, u2{w.x, w.y}), hb = __builtin_bit_cast(h4, u2{w.z, w.w});
+    a = f4{(float)ha.x, (float)ha.y, (float)ha.z, (float)ha.w};
+    b = f4{(float)hb.x, (float)hb.y, (float)hb.z, (float)hb.w};
+  }
+}
+template <int ET>
+__device__ __forceinline__ void store8_half(void* p, size_t e, f4 a, f4 b) {
+  u2 wa, wb;
+  if constexpr (ET == GB_DTYPE_BF16) {
+    wa = bf16_pack4(a);
+    wb = bf16_pack4(b);
+  } else {
+    // as in store_vals4_at: the binary32 values must exist before rounding
+    asm volatile("" : "+v"(a));
+    asm volatile("" : "+v"(b));
+    const h4 ha = {(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w};
+    const h4 hb = {(_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+    wa = __builtin_bit_cast(u2, ha);
+    wb = __builtin_bit_cast(u2, hb);
+  }
+  __builtin_nontemporal_store(u4w{wa.x, wa.y, wb.x, wb.y}, reinterpret_cast<u4w*>(static_cast<uint16_t*>(p) + e));
+}
+
+// A lane's 4 vectors of a block as binary32 (converted as load_vals4_at
+// converts), their store, and their codes (4 per word, value 0 in the low
+// byte), placed by map MAP.
+template <int ET, int MAP, bool FULL>
+__device__ __forceinline__ void load_block(const void* p, size_t block, uint32_t col, size_t n, f4 (&x)[4]) {
+  if constexpr (MAP == kMapPair) {
     const double* d = static_cast<const double*>(p);
-    const size_t e = pair_elem(block, j, col);
-    const d2v lo = load_f64x2_at<FULL>(d, e, n), hi = load_f64x2_at<FULL>(d, e + 32, n);
-    return f4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const size_t e = pair_elem(block, j, col);
+      const d2v lo = load_f64x2_at<FULL>(d, e, n), hi = load_f64x2_at<FULL>(d, e + 32, n);
+      x[j] = f4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+    }
+  } else if constexpr (MAP == kMapWide && FULL) {
+#pragma unroll
+    for (int m = 0; m < 2; m++) load8_half<ET>(p, wide_elem(block, 2 * m, col), x[2 * m], x[2 * m + 1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) x[j] = load_vals4_at<ET, FULL>(p, vec_elem<MAP>(block, j, col), n);
   }
 }
-template <int ET, bool FULL>
-__device__ __forceinline__ void store_block_vec(void* p, size_t block, int j, uint32_t col, size_t n, f4 v) {
-  if constexpr (ET != GB_DTYPE_F64) {
-    store_vals4_at<ET, FULL>(p, lane_elem(block, j, col), n, v);
-  } else {
+template <int ET, int MAP, bool FULL>
+__device__ __forceinline__ void store_block(void* p, size_t block, uint32_t col, size_t n, const f4 (&v)[4]) {
+  if constexpr (MAP == kMapPair) {
     double* d = static_cast<double*>(p);
-    const size_t e = pair_elem(block, j, col);
-    store_f64x2_at<FULL>(d, e, n, d2v{(double)v.x, (double)v.y});
-    store_f64x2_at<FULL>(d, e + 32, n, d2v{(double)v.z, (double)v.w});
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const size_t e = pair_elem(block, j, col);
+      store_f64x2_at<FULL>(d, e, n, d2v{(double)v[j].x, (double)v[j].y});
+      store_f64x2_at<FULL>(d, e + 32, n, d2v{(double)v[j].z, (double)v[j].w});
+    }
+  } else if constexpr (MAP == kMapWide && FULL) {
+#pragma unroll
+    for (int m = 0; m < 2; m++) store8_half<ET>(p, wide_elem(block, 2 * m, col), v[2 * m], v[2 * m + 1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) store_vals4_at<ET, FULL>(p, vec_elem<MAP>(block, j, col), n, v[j]);
   }
 }
-template <int ET, bool FULL>
-__device__ __forceinline__ uint32_t load_block_codes(const uint8_t* c, size_t block, int j, uint32_t col, size_t n) {
-  if constexpr (ET != GB_DTYPE_F64) {
-    return load_codes4_at<FULL>(c, lane_elem(block, j, col), n);
+template <int MAP, bool FULL>
+__device__ __forceinline__ void load_block_codes(const uint8_t* c, size_t block, uint32_t col, size_t n,
+                                                 uint32_t (&w)[4]) {
+  if constexpr (MAP == kMapPair) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const size_t e = pair_elem(block, j, col);
+      w[j] = load_codes2_at<FULL>(c, e, n) | (load_codes2_at<FULL>(c, e + 32, n) << 16);
+    }
+  } else if constexpr (MAP == kMapWide && FULL) {
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const u2 v = __builtin_nontemporal_load(reinterpret_cast<const u2*>(c + wide_elem(block, 2 * m, col)));
+      w[2 * m] = v.x;
+      w[2 * m + 1] = v.y;
+    }
   } else {
-    const size_t e = pair_elem(block, j, col);
-    return load_codes2_at<FULL>(c, e, n) | (load_codes2_at<FULL>(c, e + 32, n) << 16);
+#pragma unroll
+    for (int j = 0; j < 4; j++) w[j] = load_codes4_at<FULL>(c, vec_elem<MAP>(block, j, col), n);
   }
 }
-template <int ET, bool FULL>
-__device__ __forceinline__ void store_block_codes(uint8_t* c, size_t block, int j, uint32_t col, size_t n,
-                                                  uint32_t w) {
-  if constexpr (ET != GB_DTYPE_F64) {
-    store_codes4_at<FULL>(c, lane_elem(block, j, col), n, w);
+template <int MAP, bool FULL>
+__device__ __forceinline__ void store_block_codes(uint8_t* c, size_t block, uint32_t col, size_t n,
+                                                  const uint32_t (&w)[4]) {
+  if constexpr (MAP == kMapPair) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const size_t e = pair_elem(block, j, col);
+      store_codes2_at<FULL>(c, e, n, w[j] & 0xFFFFu);
+      store_codes2_at<FULL>(c, e + 32, n, w[j] >> 16);
+    }
+  } else if constexpr (MAP == kMapWide && FULL) {
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      __builtin_nontemporal_store(u2{w[2 * m], w[2 * m + 1]}, reinterpret_cast<u2*>(c + wide_elem(block, 2 * m, col)));
+    }
   } else {
-    const size_t e = pair_elem(block, j, col);
-    store_codes2_at<FULL>(c, e, n, w & 0xFFFFu);
-    store_codes2_at<FULL>(c, e + 32, n, w >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; j++) store_codes4_at<FULL>(c, vec_elem<MAP>(block, j, col), n, w[j]);
   }
 }
 
-// A float32 array (a residual) placed by the lane map of element type MAP.
+// A float32 array (an error-feedback residual) on the narrow or pair map.
 template <int MAP, bool FULL>
-__device__ __forceinline__ f4 load_block_f32(const float* p, size_t block, int j, uint32_t col, size_t n) {
-  if constexpr (MAP != GB_DTYPE_F64) {
-    return load4_at<FULL>(p, lane_elem(block, j, col), n);
-  } else {
-    const size_t e = pair_elem(block, j, col);
-    const f2 lo = load_f32x2_at<FULL>(p, e, n), hi = load_f32x2_at<FULL>(p, e + 32, n);
-    return f4{lo.x, lo.y, hi.x, hi.y};
+__device__ __forceinline__ void load_block_f32(const float* p, size_t block, uint32_t col, size_t n, f4 (&x)[4]) {
+  static_assert(MAP != kMapWide, "residuals use the narrow or the pair map");
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if constexpr (MAP == kMapPair) {
+      const size_t e = pair_elem(block, j, col);
+      const f2 lo = load_f32x2_at<FULL>(p, e, n), hi = load_f32x2_at<FULL>(p, e + 32, n);
+      x[j] = f4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      x[j] = load4_at<FULL>(p, lane_elem(block, j, col), n);
+    }
   }
 }
 template <int MAP, bool FULL>
-__device__ __forceinline__ void store_block_f32(float* p, size_t block, int j, uint32_t col, size_t n, f4 v) {
-  if constexpr (MAP != GB_DTYPE_F64) {
-    store4_at<FULL>(p, lane_elem(block, j, col), n, v);
-  } else {
-    const size_t e = pair_elem(block, j, col);
-    store_f32x2_at<FULL>(p, e, n, f2{v.x, v.y});
-    store_f32x2_at<FULL>(p, e + 32, n, f2{v.z, v.w});
+__device__ __forceinline__ void store_block_f32(float* p, size_t block, uint32_t col, size_t n, const f4 (&v)[4]) {
+  static_assert(MAP != kMapWide, "residuals use the narrow or the pair map");
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if constexpr (MAP == kMapPair) {
+      const size_t e = pair_elem(block, j, col);
+      store_f32x2_at<FULL>(p, e, n, f2{v[j].x, v[j].y});
+      store_f32x2_at<FULL>(p, e + 32, n, f2{v[j].z, v[j].w});
+    } else {
+      store4_at<FULL>(p, lane_elem(block, j, col), n, v[j]);
+    }
   }
 }
 

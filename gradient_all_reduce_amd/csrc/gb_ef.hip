@@ -37,12 +37,10 @@ __device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales
                                                    size_t n, int mode) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  constexpr int MAP = ef_map<ET>();
   f4 x[4], r[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    x[j] = load_block_vec<ET, FULL>(src, block, j, col, n);
-    r[j] = load_block_f32<ET, FULL>(res, block, j, col, n);
-  }
+  load_block<ET, MAP, FULL>(src, block, col, n, x);
+  load_block_f32<MAP, FULL>(res, block, col, n, r);
 #pragma unroll
   for (int j = 0; j < 4; j++) x[j] = x[j] + r[j];  // y
   uint32_t w[4];
@@ -50,10 +48,9 @@ __device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales
   if (!FULL && block * kBlock >= n) return;
   if (col == 0u) scales[block] = s;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    store_block_codes<ET, FULL>(codes, block, j, col, n, w[j]);
-    store_block_f32<ET, FULL>(res, block, j, col, n, x[j] - e4m3_unpack4(w[j]) * s);
-  }
+  for (int j = 0; j < 4; j++) r[j] = x[j] - e4m3_unpack4(w[j]) * s;
+  store_block_codes<MAP, FULL>(codes, block, col, n, w);
+  store_block_f32<MAP, FULL>(res, block, col, n, r);
 }
 
 template <int ET>
@@ -69,14 +66,15 @@ __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src
                                                   int mode) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  constexpr int MAP = ef_map<ET>();
   f4 y[K][4];
 #pragma unroll
   for (int r = 0; r < K; r++) {
+    f4 q[4];
+    load_block<ET, MAP, FULL>(src.p[r], block, col, n, y[r]);
+    load_block_f32<MAP, FULL>(static_cast<const float*>(resid.p[r]), block, col, n, q);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      y[r][j] = load_block_vec<ET, FULL>(src.p[r], block, j, col, n) +
-                load_block_f32<ET, FULL>(static_cast<const float*>(resid.p[r]), block, j, col, n);
-    }
+    for (int j = 0; j < 4; j++) y[r][j] = y[r][j] + q[j];
   }
   const bool live = FULL || block * kBlock < n;
   f4 a[4];
@@ -87,19 +85,20 @@ __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src
     uint8_t* c = static_cast<uint8_t*>(codes.p[r]);
     float* rp = static_cast<float*>(resid.p[r]);
     if (live && col == 0u) static_cast<float*>(scales.p[r])[block] = s;
+    f4 d[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const f4 v = e4m3_unpack4(w[j]) * s;
-      if (live) {
-        store_block_codes<ET, FULL>(c, block, j, col, n, w[j]);
-        store_block_f32<ET, FULL>(rp, block, j, col, n, y[r][j] - v);
-      }
+      d[j] = y[r][j] - v;
       a[j] = r == 0 ? v : a[j] + v;
+    }
+    if (live) {
+      store_block_codes<MAP, FULL>(c, block, col, n, w);
+      store_block_f32<MAP, FULL>(rp, block, col, n, d);
     }
   }
   if (!live) return;
-#pragma unroll
-  for (int j = 0; j < 4; j++) store_block_vec<ET, FULL>(out, block, j, col, n, a[j]);
+  store_block<ET, MAP, FULL>(out, block, col, n, a);
 }
 
 template <int K, int ET>
