@@ -148,6 +148,45 @@ def test_ddp_1b_buckets_fp8_sampled(gb):
     assert bool(torch.isfinite(out).all())
 
 
+def raw(t):
+    """A device tensor's bits as an integer view (16-bit floats as their codes)."""
+    return t.view({2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()]) if t.is_floating_point() else t
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
+def test_ddp_1b_buckets_fp8_typed_sampled(gb, dt):
+    """The benchmark's --dtype runs: 4 x 1e9 gradients of the type (float64
+    at 5e8, as large in bytes), the same buckets and one
+    gb_bucket_allreduce_local_typed call, checked against the oracle on
+    random blocks and on the first and last block of every bucket: the total
+    rounded to the type, every code and every scale."""
+    k, bucket = 4, W.DDP_BUCKET
+    n = W.DDP_N if dt != "f64" else W.DDP_N // 2
+    x = [W.device_gradients_typed(n, W.BASE_SEED + r, DEV, dt) for r in range(k)]
+    out = torch.empty(n, dtype=x[0].dtype, device=DEV)
+    lay = gb.gb_bucket_workspace_layout(gb.GB_CODEC_FP8_E4M3_B256, k, n, bucket)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_typed(out, x, bucket, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
+    torch.cuda.synchronize()
+    nb = n // 256
+    edges = [e for s, l in W.ddp_buckets(n, bucket) for e in (s // 256, (s + l) // 256 - 1)]
+    blocks = sample_blocks(nb, 2000, 4, must=edges)
+    # the gathered bits, reinterpreted as the oracle's arrays of the type
+    as_type = (lambda a: a.view(np.uint16)) if dt in ("bf16", "f16") else (lambda a: a.view(np.float64))
+    xs = [as_type(gather_blocks(raw(t), blocks)) for t in x]
+    want, codes, scales = O.bucket_allreduce_typed(xs, dt, 256, O.CODEC_FP8, O.SCALE_ABSMAX_DIV_448)
+    got = gather_blocks(raw(out), blocks)
+    bad = int((got != np.ascontiguousarray(want).view(got.dtype)).sum())
+    assert bad == 0, f"{bad} of {got.size} sampled values differ from the oracle"
+
+    bt = torch.as_tensor(blocks, device=DEV)
+    for r in range(k):
+        c = ws[r * lay["codes_stride"]:r * lay["codes_stride"] + n]
+        s = ws[lay["scales_offset"] + r * lay["scales_stride"]:][:4 * nb].view(torch.float32)
+        assert int((gather_blocks(c, blocks) != codes[r]).sum()) == 0, f"codes of rank {r}"
+        assert int((u32(s[bt].cpu().numpy()) != u32(scales[r])).sum()) == 0, f"scales of rank {r}"
+
+
 def test_ddp_per_bucket_calls_in_a_replayed_graph(gb):
     """One call per bucket (as a DDP hook issues them), captured in a HIP graph
     and replayed several times with eager work in between: every replay gives
