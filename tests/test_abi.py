@@ -275,3 +275,35 @@ def test_zero_length_returns_ok_without_pointers(gb):
     assert L.gb_bucket_allreduce_local(None, None, 2, 0, 256, 2, 0, None, 0, None) == 0
     assert L.gb_encode_ef(2, 2, None, None, None, None, 0, 0, None) == 0
     assert L.gb_bucket_allreduce_local_ef_typed(2, None, None, None, 2, 0, 256, 2, 0, None, 0, None) == 0
+
+
+def test_header_compiles_and_links_from_plain_c(gb, tmp_path):
+    """The header is plain C (C11, no C++), and a C program linked against the
+    library calls its host-only functions."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use_gbreduce.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "gbreduce.h"
+int main(void) {
+  size_t cs = 0, so = 0, ss = 0, total = 0;
+  gb_status s = gb_bucket_workspace_layout(GB_CODEC_FP8_E4M3_B256, 4, 1000, 256, &cs, &so, &ss, &total);
+  printf("%d %d %zu %zu %zu %zu %zu %s\n", gb_version(), (int)s, cs, so, ss, total,
+         gb_payload_bytes(GB_CODEC_FP8_E4M3_B256, 1000), gb_status_string(GB_ERR_WORKSPACE));
+  return gb_reduce_sum(NULL, NULL, 0, 10, NULL) == GB_ERR_INVALID_ARG ? 0 : 1;
+}
+''')
+    exe = tmp_path / "use_gbreduce"
+    libdir = os.path.dirname(gb.library_path)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-l:libgbreduce.so", f"-Wl,-rpath,{libdir}"],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    v, s, cs, so, ss, total, pb, name = r.stdout.split()
+    assert int(v) == gb.gb_version() and int(s) == 0
+    assert (int(cs), int(ss), int(total)) == (1024, 256, 4 * (1024 + 256)) and int(so) == 4 * 1024
+    assert int(pb) == 1000 + 4 * 4 and name == "GB_ERR_WORKSPACE"
