@@ -12,7 +12,12 @@
  *   - the elementwise fp32 SUM of k contributions in fixed rank order;
  *   - the opt-in bf16 bridge compression (encode; decode and add in fp32);
  *   - the opt-in fp8 bridge compression: OCP E4M3 codes with one fp32 scale
- *     per 256 values (encode; decode and add in fp32).
+ *     per 256 values (encode; decode and add in fp32);
+ *   - the DDP bucket stream of all three in one pass.
+ *
+ * and, around them: AVG, MAX and MIN; the README's other element types,
+ * reduced exactly or through the codecs; an error-feedback residual per
+ * buffer; and the staged (pipelined) steps through pinned host memory.
  *
  * Conventions shared by every call
  * --------------------------------
