@@ -113,3 +113,91 @@ def test_ef_rejects_without_a_lossy_codec(gb):
         big = torch.zeros(1028, device=DEV)
         gb.gb_encode_bf16_ef(codes, big[1:1025], x)  # misaligned residual
     assert e.value.status == gb.GB_ERR_MISALIGNED
+
+
+def same_codes(got, want, codec, what):
+    """Codes equal, except that NaN codes compare as NaN: a NaN an invalid
+    operation creates (0 * Inf in the decode of an Inf-scaled block, Inf - Inf
+    in a residual) is +NaN on the GPU and -NaN on the host, whose sign IEEE
+    754-2019 leaves uninterpreted, and a code carries its value's sign."""
+    if codec == O.CODEC_FP8:
+        gn, wn = (got & 0x7F) == 0x7F, (want & 0x7F) == 0x7F
+    else:
+        gn, wn = (got & 0x7FFF) > 0x7F80, (want & 0x7FFF) > 0x7F80
+    assert (gn == wn).all(), what + ": NaN codes at different places"
+    bad = np.flatnonzero(got[~gn] != want[~wn])
+    assert bad.size == 0, f"{what}: {bad.size} mismatches"
+
+
+def planted(n, seed):
+    """Gradient-like float32 values with the special values planted: one whole
+    block of them (tiled) and 40 more at random places."""
+    rng = np.random.default_rng(seed)
+    sv = W.special_values()
+    x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    if n >= 512:
+        x[256:512] = np.resize(sv, 256)
+    idx = rng.choice(n, min(40, n), replace=False)
+    x[idx] = rng.choice(sv, idx.size)
+    return x
+
+
+@pytest.mark.parametrize("codec,mode", [(O.CODEC_BF16, 0), (O.CODEC_FP8, 0), (O.CODEC_FP8, 1)])
+def test_special_values_in_gradients_and_residuals(gb, codec, mode):
+    """NaN, Inf, subnormals and the format edges in both the gradient and the
+    residual: codes, scales and the new residual as the oracle gives them,
+    over two steps (NaN compared as NaN)."""
+    n = 256 * 6 + 19
+    x = planted(n, 60)
+    rng = np.random.default_rng(61)
+    r0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    idx = rng.choice(n, 20, replace=False)
+    r0[idx] = rng.choice(W.special_values(), idx.size)
+    res = dev(r0)
+    wres = r0
+    for step in range(2):
+        if codec == O.CODEC_BF16:
+            codes = torch.empty(n, dtype=torch.uint16, device=DEV)
+            gb.gb_encode_bf16_ef(codes, res, dev(x))
+            wc, wres = O.encode_bf16_ef(x, wres)
+        else:
+            codes = torch.empty(n, dtype=torch.uint8, device=DEV)
+            scales = torch.empty(O.nblocks(n), device=DEV)
+            gb.gb_encode_fp8_e4m3_blockscaled_ef(codes, scales, res, dev(x), mode)
+            wc, ws, wres = O.encode_fp8_ef(x, wres, mode)
+            same(bits(scales), ws, f"scales step {step}")
+        same_codes(bits(codes), wc, codec, f"codes step {step}")
+        same(bits(res), wres, f"residual step {step}")
+
+
+@pytest.mark.parametrize("codec", [O.CODEC_BF16, O.CODEC_FP8])
+def test_special_values_through_the_bucket_stream(gb, codec):
+    k, bucket, n = 3, 512, 512 * 5 + 300
+    xs = [planted(n, 70 + r) for r in range(k)]
+    res = [dev(np.zeros(n, np.float32)) for _ in range(k)]
+    out = torch.empty(n, device=DEV)
+    ws = torch.empty(gb.gb_bucket_workspace_bytes(codec, k, n, bucket), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_ef(out, [dev(x) for x in xs], res, bucket, codec, 0, ws)
+    want, _, _, wres = O.bucket_allreduce_ef(xs, [np.zeros(n, np.float32)] * k, bucket, codec, 0)
+    same(bits(out), want, "out")
+    for r in range(k):
+        same(bits(res[r]), wres[r], f"residual {r}")
+
+
+@pytest.mark.parametrize("codec,mode", [(O.CODEC_BF16, 0), (O.CODEC_FP8, 0), (O.CODEC_FP8, 1)])
+def test_every_float16_code_through_error_feedback(gb, codec, mode):
+    """All 2^16 float16 codes (NaN payloads, Inf, subnormals) as a gradient with
+    a small residual, through the typed error-feedback encoder."""
+    x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    n = x.size
+    r0 = (np.random.default_rng(80).standard_normal(n) * 1e-5).astype(np.float32)
+    codes = torch.empty(n, dtype=torch.uint16 if codec == O.CODEC_BF16 else torch.uint8, device=DEV)
+    scales = torch.empty(O.nblocks(n), device=DEV) if codec == O.CODEC_FP8 else None
+    res = dev(r0)
+    src = torch.from_numpy(x.view(np.int16).copy()).to(DEV).view(torch.float16)
+    gb.gb_encode_ef(codec, codes, scales, res, src, mode)
+    wc, ws, wres = O.encode_ef_typed(x, r0, "f16", codec, mode)
+    same_codes(bits(codes), wc, codec, "codes")
+    if codec == O.CODEC_FP8:
+        same(bits(scales), ws, "scales")
+    same(bits(res), wres, "residual")
