@@ -27,7 +27,8 @@ def gb():
 
 def draw_values(rng, dt, n):
     """Gradient-like values with outliers, zeros of both signs and, now and
-    then, a whole block of tiny values or one huge value."""
+    then, a whole block of tiny values or special values (Inf, NaN, the
+    extremes of the type)."""
     v = rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 1)
     v[rng.random(n) < 0.01] *= 300.0
     v[rng.random(n) < 0.003] = 0.0
@@ -35,6 +36,12 @@ def draw_values(rng, dt, n):
     if n > 600 and rng.random() < 0.3:
         s = int(rng.integers(0, n - 256))
         v[s:s + 256] *= 1e-30
+    if rng.random() < 0.15:
+        # special values now and then: infinities, NaNs of both signs, the
+        # float32 extremes, a float32 subnormal, -0 and float16's edge
+        specials = np.array([np.inf, -np.inf, np.nan, -np.nan, 3.4e38, -3.4e38, 1e-45, -0.0, 65504.0, 1e5])
+        where = rng.choice(n, max(1, n // 500), replace=False)
+        v[where] = rng.choice(specials, where.size)
     if dt == "f64":
         return v
     if dt == "f32":
