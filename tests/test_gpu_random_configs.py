@@ -77,7 +77,7 @@ def same(got, want, dt, what):
     assert got[~gn].tobytes() == want[~wn].tobytes(), f"{what}: values differ"
 
 
-@pytest.mark.parametrize("seed", range(200))
+@pytest.mark.parametrize("seed", range(400))
 def test_bucket_stream(gb, seed):
     rng = np.random.default_rng(7000 + seed)
     k = int(rng.integers(1, 17))
@@ -117,7 +117,7 @@ def test_bucket_stream(gb, seed):
     same(to_host(out), want, dt, what)
 
 
-@pytest.mark.parametrize("seed", range(200))
+@pytest.mark.parametrize("seed", range(400))
 def test_reduction(gb, seed):
     rng = np.random.default_rng(8000 + seed)
     k = int(rng.integers(1, 17))
@@ -136,7 +136,7 @@ def test_reduction(gb, seed):
     same(to_host(out), O.reduce_typed(xs, dt, op, divisor), dt, what)
 
 
-@pytest.mark.parametrize("seed", range(80))
+@pytest.mark.parametrize("seed", range(160))
 def test_encode_decode(gb, seed):
     rng = np.random.default_rng(9000 + seed)
     k = int(rng.integers(1, 9))
