@@ -132,3 +132,40 @@ def test_typed_calls_in_a_replayed_graph(gb):
         assert (np.isnan(gh.view(np.float16)) == nan).all() and (gh[~nan] == wh[~nan]).all(), rep
         gb.gb_reduce_sum(torch.empty(16, device=DEV), [torch.ones(16, device=DEV)])  # eager work between
         torch.cuda.synchronize()
+
+
+def test_error_feedback_in_a_replayed_graph(gb):
+    """One error-feedback bucket stream captured once and replayed three times:
+    each replay reads the residuals the previous one wrote, exactly as three
+    eager calls do, for float32 and bfloat16 gradients."""
+    k, n, bucket = 3, 4096 * 5 + 256 * 3 + 17, 4096
+    for dt in ("f32", "bf16"):
+        xs = W.typed_ranks(k, n, dt, 6700) if dt != "f32" else W.gradient_ranks(k, n, 6700)
+        dx = ([torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16) for x in xs] if dt == "bf16"
+              else [torch.from_numpy(x).to(DEV) for x in xs])
+        res = [torch.zeros(n, device=DEV) for _ in range(k)]
+        out = torch.empty(n, dtype=dx[0].dtype, device=DEV)
+        ws = torch.empty(gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, k, n, bucket), dtype=torch.uint8,
+                         device=DEV)
+        step = lambda: gb.gb_bucket_allreduce_local_ef_typed(out, dx, res, bucket, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
+        # warm up on scratch residuals, then capture
+        saved = [r.clone() for r in res]
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for r, s in zip(res, saved):
+            r.copy_(s)
+        torch.cuda.synchronize()
+        wres = [np.zeros(n, np.float32) for _ in range(k)]
+        for rep in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            want, _, _, wres = O.bucket_allreduce_ef_typed(xs, wres, dt, bucket, O.CODEC_FP8)
+            got = out.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16" else out.cpu().numpy()
+            assert got.tobytes() == np.ascontiguousarray(want).tobytes(), (dt, rep)
+            for r in range(k):
+                assert (u32(res[r].cpu().numpy()) == u32(wres[r])).all(), (dt, rep, r)
+            gb.gb_reduce_sum(torch.empty(16, device=DEV), [torch.ones(16, device=DEV)])  # eager work between
+            torch.cuda.synchronize()
