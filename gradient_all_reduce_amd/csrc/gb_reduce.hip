@@ -228,13 +228,19 @@ template <bool P2>
 __device__ __forceinline__ float div_round_odd(float a, float d, float inv) {
   // a power-of-two d: a * (1/d) is the exact quotient rounded once, as a / d
   const float q = P2 ? a * inv : a / d;
-  const float r = __builtin_fmaf(q, d, -a);
-  uint32_t b = fbits(q);
-  if ((r < 0.0f || r > 0.0f) && !(b & 1u)) {
-    const bool grow = (r > 0.0f) == (a < 0.0f);  // |q| below |a / d|
-    b = grow ? b + 1u : b - 1u;
+  // With a power-of-two d the product is exact unless it is a binary32
+  // subnormal, so only those lanes need the residual; the block is skipped
+  // when no lane of the wavefront does.
+  if (!P2 || __builtin_fabsf(q) < 0x1p-126f) {
+    const float r = __builtin_fmaf(q, d, -a);
+    uint32_t b = fbits(q);
+    if ((r < 0.0f || r > 0.0f) && !(b & 1u)) {
+      const bool grow = (r > 0.0f) == (a < 0.0f);  // |q| below |a / d|
+      b = grow ? b + 1u : b - 1u;
+    }
+    return bitsf(b);
   }
-  return bitsf(b);
+  return q;
 }
 
 // Divisor of an AVG: d in binary32 and binary64, and for a power of two its
