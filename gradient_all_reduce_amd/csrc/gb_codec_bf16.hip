@@ -148,7 +148,7 @@ template <int ET>
 hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_bf16_kernel<K, ET><<<grid, kThreads, 0, stream>>>(out, srcs, c, n);
+#define GB_CALL(K) fused_bf16_kernel<K, ET><<<grid, kThreads, fused_bf16_lds<ET>(K, n), stream>>>(out, srcs, c, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();

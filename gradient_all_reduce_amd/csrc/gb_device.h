@@ -731,9 +731,15 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 // workgroups per compute unit move about 4% more bytes per second than the 5
 // its registers allow (fewer concurrent streams of requests at the memory).
 // The fused bf16 pass with error feedback (17 streams at k = 4) gains 6-11%
-// from 6.7e7 values per rank up under the same cap, and the plain fused bf16
-// pass nothing that holds at bucket sizes.  Kernels with fewer bytes per
-// lane lose heavily under any cap and get none.
+// from 6.7e7 values per rank up under the same cap.  Kernels with fewer bytes
+// per lane lose heavily under any cap and get none.
+//
+// The plain fused bf16 pass depends on the size and the gradient's type.
+// From 2^25 values per rank up, float32 gradients move 2-4% more bytes per
+// second at 3 workgroups per unit (48 KiB) and float64 gradients 4-5% more at
+// 2.  Both lose about 3% at bucket sizes (6.55e6 values), which stay
+// uncapped.  Half-precision gradients lose under 2 per unit and gain nothing
+// that holds below 2.5e8 values under 3, so they are never capped.
 //
 // One per unit: the fused fp8 pass with error feedback (21 streams at k = 4:
 // sources and residuals read; codes, scales, residuals and the sum written)
@@ -741,6 +747,7 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 // rank, and the same below and at k = 8; the fused fp8 pass over float64
 // gradients (32k bytes of loads per lane) 5% more at 5e8 values per rank
 // and the same at 6.7e7.
+constexpr unsigned kThreePerCuLds = 48u << 10;
 constexpr unsigned kTwoPerCuLds = 64u << 10;
 constexpr unsigned kOnePerCuLds = 81u << 10;
 __host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kTwoPerCuLds : 0u; }
@@ -748,6 +755,11 @@ __host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kOnePerCu
 template <int ET>
 __host__ __device__ constexpr unsigned fused_fp8_lds(int k) {
   return ET == GB_DTYPE_F64 ? (k >= 4 ? kOnePerCuLds : 0u) : heavy_lds(k);
+}
+template <int ET>
+__host__ __device__ constexpr unsigned fused_bf16_lds(int k, size_t n) {
+  if (k < 4 || n < ((size_t)1 << 25)) return 0u;
+  return ET == GB_DTYPE_F32 ? kThreePerCuLds : (ET == GB_DTYPE_F64 ? kTwoPerCuLds : 0u);
 }
 
 size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
