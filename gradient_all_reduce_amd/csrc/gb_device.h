@@ -730,9 +730,9 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 // in flight per lane; measured on MI355X at 1e9 values per rank, 2
 // workgroups per compute unit move about 4% more bytes per second than the 5
 // its registers allow (fewer concurrent streams of requests at the memory).
-// The fused bf16 pass with error feedback (17 streams at k = 4) gains 6-11%
-// from 6.7e7 values per rank up under the same cap.  Kernels with fewer bytes
-// per lane lose heavily under any cap and get none.
+// The fused bf16 pass with error feedback (17 streams at k = 4) over float16
+// gradients gains up to 2% from 3.3e7 values per rank up under the same cap.
+// Kernels with fewer bytes per lane lose heavily under any cap and get none.
 //
 // The plain fused bf16 pass depends on the size and the gradient's type.
 // From 2^25 values per rank up, float32 gradients move 2-4% more bytes per
@@ -746,7 +746,10 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 // moves 2% more bytes per second than at two, from 6.7e7 to 1e9 values per
 // rank, and the same below and at k = 8; the fused fp8 pass over float64
 // gradients (32k bytes of loads per lane) 5% more at 5e8 values per rank
-// and the same at 6.7e7.
+// and the same at 6.7e7; the fused bf16 pass with error feedback over
+// float32 gradients 2-4% more than at two, at every size from one bucket to
+// 1e9 values per rank, over float64 and bfloat16 gradients up to 1.5% and 2%
+// more from 6.7e7 values up (over float16 gradients 3% less at 1e9).
 constexpr unsigned kThreePerCuLds = 48u << 10;
 constexpr unsigned kTwoPerCuLds = 64u << 10;
 constexpr unsigned kOnePerCuLds = 81u << 10;
@@ -755,6 +758,10 @@ __host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kOnePerCu
 template <int ET>
 __host__ __device__ constexpr unsigned fused_fp8_lds(int k) {
   return ET == GB_DTYPE_F64 ? (k >= 4 ? kOnePerCuLds : 0u) : heavy_lds(k);
+}
+template <int ET>
+__host__ __device__ constexpr unsigned fused_bf16_ef_lds(int k) {
+  return ET == GB_DTYPE_F16 ? heavy_lds(k) : ef_lds(k);
 }
 template <int ET>
 __host__ __device__ constexpr unsigned fused_bf16_lds(int k, size_t n) {

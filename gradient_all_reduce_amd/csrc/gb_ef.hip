@@ -162,7 +162,7 @@ hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, 
                            hipStream_t stream) {
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_bf16_ef_kernel<K, ET><<<grid, kThreads, heavy_lds(K), stream>>>(out, srcs, rs, c, n);
+#define GB_CALL(K) fused_bf16_ef_kernel<K, ET><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(out, srcs, rs, c, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
