@@ -187,7 +187,7 @@ hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const
                        int scale_mode, hipStream_t stream) {
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_fp8_kernel<K, ET><<<grid, kThreads, fused_fp8_lds<ET>(K), stream>>>(out, srcs, c, s, n, scale_mode);
+#define GB_CALL(K) fused_fp8_kernel<K, ET><<<grid, kThreads, fused_fp8_lds<ET>(K, n), stream>>>(out, srcs, c, s, n, scale_mode);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();

@@ -755,9 +755,15 @@ constexpr unsigned kTwoPerCuLds = 64u << 10;
 constexpr unsigned kOnePerCuLds = 81u << 10;
 __host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kTwoPerCuLds : 0u; }
 __host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kOnePerCuLds : 0u; }
+// The fused fp8 pass over half-precision gradients keeps half the bytes per
+// lane of the float32 pass in flight: below 2^26 values per rank it moves
+// 1-6% more bytes per second uncapped (float16 5.8% and bfloat16 2.3% more at
+// one bucket), and from there up it gains under the cap as float32 does.
 template <int ET>
-__host__ __device__ constexpr unsigned fused_fp8_lds(int k) {
-  return ET == GB_DTYPE_F64 ? (k >= 4 ? kOnePerCuLds : 0u) : heavy_lds(k);
+__host__ __device__ constexpr unsigned fused_fp8_lds(int k, size_t n) {
+  if (ET == GB_DTYPE_F64) return k >= 4 ? kOnePerCuLds : 0u;
+  if ((ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) && n < ((size_t)1 << 26)) return 0u;
+  return heavy_lds(k);
 }
 template <int ET>
 __host__ __device__ constexpr unsigned fused_bf16_ef_lds(int k) {
