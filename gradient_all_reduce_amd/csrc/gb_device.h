@@ -743,8 +743,8 @@ constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 //
 // One per unit: the fused fp8 pass with error feedback (21 streams at k = 4:
 // sources and residuals read; codes, scales, residuals and the sum written)
-// moves 2% more bytes per second than at two, from 6.7e7 to 1e9 values per
-// rank, and the same below and at k = 8; the fused fp8 pass over float64
+// moves 2-4% more bytes per second than at two or uncapped at 5e8 and 1e9
+// values per rank, over every gradient type; the fused fp8 pass over float64
 // gradients (32k bytes of loads per lane) 5% more at 5e8 values per rank
 // and the same at 6.7e7; the fused bf16 pass with error feedback over
 // float32 gradients 2-4% more than at two, at every size from one bucket to
@@ -755,6 +755,12 @@ constexpr unsigned kTwoPerCuLds = 64u << 10;
 constexpr unsigned kOnePerCuLds = 81u << 10;
 __host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kTwoPerCuLds : 0u; }
 __host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kOnePerCuLds : 0u; }
+// The fused fp8 pass with error feedback takes the one-per-unit cap from 2^28
+// values per rank up: below, it moves 1-8% more bytes per second uncapped,
+// over every gradient type, at one bucket too.
+__host__ __device__ constexpr unsigned fused_fp8_ef_lds(int k, size_t n) {
+  return n >= ((size_t)1 << 28) ? ef_lds(k) : 0u;
+}
 // The fused fp8 pass over half-precision gradients keeps half the bytes per
 // lane of the float32 pass in flight: below 2^26 values per rank it moves
 // 1-6% more bytes per second uncapped (float16 5.8% and bfloat16 2.3% more at

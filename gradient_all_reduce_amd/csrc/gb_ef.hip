@@ -173,7 +173,7 @@ hipError_t fused_fp8_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, c
                           int k, size_t n, int scale_mode, hipStream_t stream) {
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_fp8_ef_kernel<K, ET><<<grid, kThreads, ef_lds(K), stream>>>(out, srcs, rs, c, s, n, scale_mode);
+#define GB_CALL(K) fused_fp8_ef_kernel<K, ET><<<grid, kThreads, fused_fp8_ef_lds(K, n), stream>>>(out, srcs, rs, c, s, n, scale_mode);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
