@@ -172,10 +172,10 @@ hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales
   if (accumulate && ET != GB_DTYPE_F32) return hipErrorInvalidValue;
 #define GB_CALL(K)                                                                                               \
   if constexpr (ET == GB_DTYPE_F32) {                                                                            \
-    if (accumulate) decode_fp8_kernel<K, true, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n); \
-    else decode_fp8_kernel<K, false, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);          \
+    if (accumulate) decode_fp8_kernel<K, true, ET><<<grid, kThreads, decode_fp8_lds<ET>(K), stream>>>(acc, codes, scales, n); \
+    else decode_fp8_kernel<K, false, ET><<<grid, kThreads, decode_fp8_lds<ET>(K), stream>>>(acc, codes, scales, n);          \
   } else {                                                                                                       \
-    decode_fp8_kernel<K, false, ET><<<grid, kThreads, heavy_lds(K), stream>>>(acc, codes, scales, n);             \
+    decode_fp8_kernel<K, false, ET><<<grid, kThreads, decode_fp8_lds<ET>(K), stream>>>(acc, codes, scales, n);             \
   }
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL

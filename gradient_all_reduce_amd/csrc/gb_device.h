@@ -722,59 +722,66 @@ __device__ __forceinline__ void store_group_f32(float* p, size_t sg, uint32_t t,
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 
-// Dynamic LDS reserved per workgroup by the kernels that keep the most bytes
-// in flight.  No kernel uses LDS: reserving 64 KiB of the 160 KiB a compute
-// unit has caps it at 2 such workgroups, 81 KiB at 1.
-//
-// Two per unit: a fused fp8 pass over k >= 4 ranks keeps 16k bytes of loads
-// in flight per lane; measured on MI355X at 1e9 values per rank, 2
-// workgroups per compute unit move about 4% more bytes per second than the 5
-// its registers allow (fewer concurrent streams of requests at the memory).
-// The fused bf16 pass with error feedback (17 streams at k = 4) over float16
-// gradients gains up to 2% from 3.3e7 values per rank up under the same cap.
-// Kernels with fewer bytes per lane lose heavily under any cap and get none.
-//
-// The plain fused bf16 pass depends on the size and the gradient's type.
-// From 2^25 values per rank up, float32 gradients move 2-4% more bytes per
-// second at 3 workgroups per unit (48 KiB) and float64 gradients 4-5% more at
-// 2.  Both lose about 3% at bucket sizes (6.55e6 values), which stay
-// uncapped.  Half-precision gradients lose under 2 per unit and gain nothing
-// that holds below 2.5e8 values under 3, so they are never capped.
-//
-// One per unit: the fused fp8 pass with error feedback (21 streams at k = 4:
-// sources and residuals read; codes, scales, residuals and the sum written)
-// moves 2-4% more bytes per second than at two or uncapped at 5e8 and 1e9
-// values per rank, over every gradient type; the fused fp8 pass over float64
-// gradients (32k bytes of loads per lane) 5% more at 5e8 values per rank
-// and the same at 6.7e7; the fused bf16 pass with error feedback over
-// float32 gradients 2-4% more than at two, at every size from one bucket to
-// 1e9 values per rank, over float64 and bfloat16 gradients up to 1.5% and 2%
-// more from 6.7e7 values up (over float16 gradients 3% less at 1e9).
+// Dynamic LDS reserved per workgroup: an occupancy cap.  No kernel uses LDS;
+// reserving 48, 64 or 81 KiB of the 160 KiB a compute unit has caps it at 3,
+// 2 or 1 such workgroups.  A kernel that keeps many bytes of loads in flight
+// per lane moves more bytes per second with fewer workgroups at once (fewer
+// concurrent streams of requests at the memory); one with few bytes per lane
+// loses under any cap.  Each rule below was measured on MI355X against the
+// other caps in one process, with the same bits; sizes are values per rank.
 constexpr unsigned kThreePerCuLds = 48u << 10;
 constexpr unsigned kTwoPerCuLds = 64u << 10;
 constexpr unsigned kOnePerCuLds = 81u << 10;
+// Two per unit over k >= 4 ranks (also the fused sum-and-encode fp8 pass).
 __host__ __device__ constexpr unsigned heavy_lds(int k) { return k >= 4 ? kTwoPerCuLds : 0u; }
+// One per unit over k >= 4 ranks.
 __host__ __device__ constexpr unsigned ef_lds(int k) { return k >= 4 ? kOnePerCuLds : 0u; }
-// The fused fp8 pass with error feedback takes the one-per-unit cap from 2^28
-// values per rank up: below, it moves 1-8% more bytes per second uncapped,
-// over every gradient type, at one bucket too.
-__host__ __device__ constexpr unsigned fused_fp8_ef_lds(int k, size_t n) {
-  return n >= ((size_t)1 << 28) ? ef_lds(k) : 0u;
-}
-// The fused fp8 pass over half-precision gradients keeps half the bytes per
-// lane of the float32 pass in flight: below 2^26 values per rank it moves
-// 1-6% more bytes per second uncapped (float16 5.8% and bfloat16 2.3% more at
-// one bucket), and from there up it gains under the cap as float32 does.
+
+// Fused fp8 pass (16k bytes of loads per lane for float32 gradients): 2 per
+// unit, about 4% ahead of the 5 its registers allow at 1e9 values.  Float64
+// gradients (32k bytes per lane) at 1: 5% ahead at 5e8, level at 6.7e7.
+// Half-precision gradients keep half the float32 bytes in flight: uncapped
+// below 2^26 values (float16 5.8% and bfloat16 2.3% ahead at one bucket),
+// and at 2 from there up, as float32.
 template <int ET>
 __host__ __device__ constexpr unsigned fused_fp8_lds(int k, size_t n) {
-  if (ET == GB_DTYPE_F64) return k >= 4 ? kOnePerCuLds : 0u;
+  if (ET == GB_DTYPE_F64) return ef_lds(k);
   if ((ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) && n < ((size_t)1 << 26)) return 0u;
   return heavy_lds(k);
 }
+
+// Fused fp8 pass with error feedback (21 streams at k = 4: sources and
+// residuals read; codes, scales, residuals and the sum written): 1 per unit
+// from 2^28 values up, 2-4% ahead of 2 or uncapped at 5e8 and 1e9 over every
+// gradient type; uncapped below, 1-8% ahead, at one bucket too.
+__host__ __device__ constexpr unsigned fused_fp8_ef_lds(int k, size_t n) {
+  return n >= ((size_t)1 << 28) ? ef_lds(k) : 0u;
+}
+
+// fp8 decode-accumulate over k >= 4 payloads, by the type it writes: a
+// float32 total at 3 per unit, 5% ahead of 2 from 6.55e6 to 2.5e8 values and
+// level at 1e9; a half-precision total uncapped, 21-26% ahead of 2; a
+// float64 total at 2.
+template <int ET>
+__host__ __device__ constexpr unsigned decode_fp8_lds(int k) {
+  if (k < 4) return 0u;
+  return ET == GB_DTYPE_F32 ? kThreePerCuLds : (ET == GB_DTYPE_F64 ? kTwoPerCuLds : 0u);
+}
+
+// Fused bf16 pass with error feedback (17 streams at k = 4): 1 per unit,
+// for float32 gradients 2-4% ahead of 2 at every size from one bucket to 1e9
+// values, for float64 and bfloat16 gradients up to 1.5% and 2% from 6.7e7
+// up; float16 gradients at 2, 3% ahead of 1 at 1e9 and up to 2% ahead of
+// uncapped from 3.3e7 up.
 template <int ET>
 __host__ __device__ constexpr unsigned fused_bf16_ef_lds(int k) {
   return ET == GB_DTYPE_F16 ? heavy_lds(k) : ef_lds(k);
 }
+
+// Plain fused bf16 pass: from 2^25 values up, float32 gradients at 3 per
+// unit (2-4% ahead) and float64 gradients at 2 (1-5% ahead); both lose about
+// 3% at bucket sizes, which stay uncapped.  Half-precision gradients are
+// never capped: 22% behind at 2, and at 3 nothing that holds below 2.5e8.
 template <int ET>
 __host__ __device__ constexpr unsigned fused_bf16_lds(int k, size_t n) {
   if (k < 4 || n < ((size_t)1 << 25)) return 0u;
