@@ -18,7 +18,9 @@ Workloads (inputs from workloads.py):
                    order, fp32 sum written out.  One gb_bucket_allreduce_local
                    call over the whole stream per step (one launch; buckets
                    start on block boundaries).  The same pass made as one call
-                   per bucket, as a DDP hook would issue it, is reported too.
+                   per bucket, as a DDP hook would issue it, is reported too,
+                   and the buckets as separate buffers through
+                   gb_bucket_allreduce_local_batch (16 per launch).
                    --dtype f16|bf16|f64 runs the same stream over gradients
                    of that type (gb_bucket_allreduce_local_typed): values
                    taken to float32, encoded, the float32 total rounded once
@@ -295,8 +297,31 @@ class DdpBuckets(Workload):
             replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
             del graph
             by_streams[m] = ms_m
+        # the same buckets through gb_bucket_allreduce_local_batch: up to 16
+        # buckets, each its own buffer for the library, per launch
+        outs = [a[0] for a in self.pb_args]
+        srcs = [a[1] for a in self.pb_args]
+        sizes = [o.numel() for o in outs]
+        need = gb.gb_bucket_batch_workspace_bytes(self.codec, self.k, sizes)
+        wsb = self.ws if need <= self.ws.numel() else torch.empty(need, dtype=torch.uint8, device=self.dev)
+        batch = lambda: gb.gb_bucket_allreduce_local_batch(outs, srcs, self.codec, self.mode, wsb if need else None)
+        batch()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            batch()
+        self.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        batch_ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        ms_batch = time_region(graph.replay, reps) / reps
+        batch_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        del graph
         gbs = lambda t: round(self.step_bytes() / (t * 1e-3) / 1e9, 2)
-        return {"per_bucket_calls_graph_gbs": gbs(ms),
+        return {"per_bucket_batched_graph_gbs": gbs(ms_batch),
+                "per_bucket_batched_graph_ms": round(ms_batch, 4),
+                "per_bucket_batched_outputs_match": batch_ok,
+                "per_bucket_calls_graph_gbs": gbs(ms),
                 "per_bucket_calls_graph_ms": round(ms, 4),
                 "per_bucket_calls_two_streams_graph_gbs": gbs(by_streams[2]),
                 "per_bucket_calls_four_streams_graph_gbs": gbs(by_streams[4]),

@@ -27,6 +27,7 @@ __all__ = [
     "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
     "gb_encode_staged", "gb_decode_accumulate_staged", "gb_reduce_typed", "GB_DTYPE", "GB_DTYPE_OF",
     "gb_encode", "gb_decode_sum", "gb_bucket_allreduce_local_typed", "gb_reduce_encode",
+    "gb_bucket_allreduce_local_batch", "gb_bucket_batch_workspace_bytes", "GB_MAX_BATCH",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -37,6 +38,7 @@ GB_OP_SUM, GB_OP_AVG, GB_OP_MAX, GB_OP_MIN = 0, 1, 2, 3
 GB_BLOCK = 256
 GB_MAX_K = 16
 GB_MAX_N = 1 << 39  # largest element count a call accepts
+GB_MAX_BATCH = 4096  # largest bucket count of gb_bucket_allreduce_local_batch
 # gb_dtype of each torch element type gb_reduce_typed takes
 GB_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3,
             torch.int8: 4, torch.uint8: 5, torch.int32: 6, torch.int64: 7}
@@ -66,6 +68,8 @@ _SIGNATURES = {
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
+    "gb_bucket_allreduce_local_batch": (_I, [_PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
+    "gb_bucket_batch_workspace_bytes": (_S, [_I, _I, _SP, _I]),
     "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
     "gb_bucket_allreduce_local_ef": (_I, [_P, _PP, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
@@ -244,6 +248,40 @@ def gb_bucket_allreduce_local(out, srcs, bucket_elems, codec, scale_mode=GB_SCAL
     _check(_lib.gb_bucket_allreduce_local(_ptr(out), _ptr_array(srcs), len(srcs), n,
                                           int(bucket_elems), int(codec), int(scale_mode),
                                           _ptr(workspace), ws_bytes, _stream(stream, out.device)))
+
+
+def _size_array(ns):
+    arr = (ctypes.c_size_t * max(1, len(ns)))(*[int(v) for v in ns])
+    return ctypes.cast(arr, _SP)
+
+
+def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                    workspace=None, stream=None):
+    """The bucket stream over separately allocated buckets: outs[b] (float32)
+    receives bucket b's result from the k float32 tensors srcs[b], as
+    gb_bucket_allreduce_local on that bucket alone; up to 16 buckets per
+    launch."""
+    if len(outs) != len(srcs):
+        raise ValueError(f"{len(outs)} outputs for {len(srcs)} buckets of sources")
+    k = len(srcs[0]) if srcs else 0
+    ns, flat = [], []
+    for b, (o, ss) in enumerate(zip(outs, srcs)):
+        _device_tensor(o, torch.float32, f"outs[{b}]")
+        if len(ss) != k:
+            raise ValueError(f"bucket {b} has {len(ss)} sources, bucket 0 has {k}")
+        for r, t in enumerate(ss):
+            _device_tensor(t, torch.float32, f"srcs[{b}][{r}]")
+        _same_numel(ss, o.numel(), f"srcs[{b}]")
+        ns.append(o.numel())
+        flat.extend(ss)
+    ws_bytes = 0
+    if workspace is not None:
+        _device_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    device = outs[0].device if outs else torch.device("cuda", torch.cuda.current_device())
+    _check(_lib.gb_bucket_allreduce_local_batch(_ptr_array(outs), _ptr_array(flat), _size_array(ns), len(outs),
+                                                k, int(codec), int(scale_mode), _ptr(workspace), ws_bytes,
+                                                _stream(stream, device)))
 
 
 _CODEC_TYPES = (torch.float32, torch.float16, torch.bfloat16, torch.float64)
@@ -457,6 +495,11 @@ def gb_bucket_workspace_layout(codec, k, n, bucket_elems):
 
 def gb_bucket_workspace_bytes(codec, k, n, bucket_elems):
     return int(_lib.gb_bucket_workspace_bytes(int(codec), int(k), int(n), int(bucket_elems)))
+
+
+def gb_bucket_batch_workspace_bytes(codec, k, ns):
+    """Workspace bytes of gb_bucket_allreduce_local_batch over buckets of ns values."""
+    return int(_lib.gb_bucket_batch_workspace_bytes(int(codec), int(k), _size_array(ns), len(ns)))
 
 
 def gb_status_string(status):

@@ -627,7 +627,7 @@ gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k
 // and their payloads decoded and added in rank order.  Without a codec: the
 // exact SUM of the element type.
 hipError_t bucket_groups(void* out, const void* const* srcs, float* const* residuals, int k, size_t n, int codec,
-                         int mode, int dtype, char* ws, size_t cs, size_t so, size_t ss, hipStream_t st) {
+                         int mode, int dtype, char* codes0, size_t cs, char* scales0, size_t ss, hipStream_t st) {
   if (codec == GB_CODEC_NONE) {
     return dtype == GB_DTYPE_F32 ? sum_groups(static_cast<float*>(out), srcs, k, n, false, st)
                                  : op_groups(out, srcs, k, n, dtype, GB_OP_SUM, 1, st);
@@ -636,8 +636,8 @@ hipError_t bucket_groups(void* out, const void* const* srcs, float* const* resid
   void* code[GB_MAX_K];
   float* scale[GB_MAX_K];
   for (int r = 0; r < k; r++) {
-    code[r] = ws + (size_t)r * cs;
-    scale[r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss);
+    code[r] = codes0 + (size_t)r * cs;
+    scale[r] = reinterpret_cast<float*>(scales0 + (size_t)r * ss);
   }
   const int m = k < kR ? k : kR;
   const gb::PtrTable t = slice(srcs, 0, m);
@@ -686,8 +686,9 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
   if (s != GB_OK || n == 0) return s;
   // One launch covers every bucket: a partly idle GPU at the end of each
   // bucket is avoided, and the result equals one call per bucket bit for bit.
-  return from_hip(bucket_groups(out, sp, nullptr, k, n, codec, scale_mode, GB_DTYPE_F32,
-                                static_cast<char*>(workspace), cs, so, ss, as_stream(stream)),
+  char* ws = static_cast<char*>(workspace);
+  return from_hip(bucket_groups(out, sp, nullptr, k, n, codec, scale_mode, GB_DTYPE_F32, ws, cs, ws + so, ss,
+                                as_stream(stream)),
                   fn);
 }
 
@@ -705,9 +706,131 @@ gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* cons
                 "which holds up to %d ranks per call", fn, k, kR);
   }
   if (n == 0) return GB_OK;
-  return from_hip(bucket_groups(out, srcs, nullptr, k, n, codec, scale_mode, dtype, static_cast<char*>(workspace),
-                                cs, so, ss, as_stream(stream)),
+  char* ws = static_cast<char*>(workspace);
+  return from_hip(bucket_groups(out, srcs, nullptr, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
+                                as_stream(stream)),
                   fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The sizes of a batch: 1..GB_MAX_BATCH buckets of at most GB_MAX_N values
+// whose sizes, each rounded up to a multiple of GB_BLOCK, add up to at most
+// GB_MAX_N (the workspace's virtual buffer); *total receives that sum.
+gb_status check_batch_sizes(const char* fn, const size_t* ns, int nbuckets, size_t* total) {
+  if (nbuckets < 1 || nbuckets > GB_MAX_BATCH) {
+    return fail(GB_ERR_INVALID_ARG, "%s: nbuckets = %d is outside 1..%d", fn, nbuckets, GB_MAX_BATCH);
+  }
+  if (ns == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: ns is NULL", fn);
+  size_t t = 0;
+  for (int b = 0; b < nbuckets; b++) {
+    if (ns[b] > GB_MAX_N) {
+      return fail(GB_ERR_INVALID_ARG, "%s: ns[%d] = %zu exceeds GB_MAX_N = %zu", fn, b, ns[b], GB_MAX_N);
+    }
+    t += round_up(ns[b], GB_BLOCK);
+    if (t > GB_MAX_N) {
+      return fail(GB_ERR_INVALID_ARG, "%s: the bucket sizes, each rounded up to a multiple of %d, exceed GB_MAX_N",
+                  fn, GB_BLOCK);
+    }
+  }
+  *total = t;
+  return GB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gb_bucket_batch_workspace_bytes(int codec, int k, const size_t* ns, int nbuckets) {
+  char saved[sizeof g_last_error];
+  std::memcpy(saved, g_last_error, sizeof saved);
+  size_t total = 0, cs, so, ss, bytes = 0;
+  gb_status s = check_batch_sizes("gb_bucket_batch_workspace_bytes", ns, nbuckets, &total);
+  if (s == GB_OK) s = gb_bucket_workspace_layout(codec, k, total, GB_BLOCK, &cs, &so, &ss, &bytes);
+  std::memcpy(g_last_error, saved, sizeof saved);  // a size query reports no failure
+  return s == GB_OK ? bytes : 0;
+}
+
+gb_status gb_bucket_allreduce_local_batch(float* const* outs, const float* const* srcs, const size_t* ns,
+                                          int nbuckets, int k, int codec, int scale_mode, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  const char* fn = "gb_bucket_allreduce_local_batch";
+  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  }
+  gb_status s = check_k(k, fn);
+  if (s != GB_OK) return s;
+  size_t total;
+  if ((s = check_batch_sizes(fn, ns, nbuckets, &total)) != GB_OK) return s;
+  if (total == 0) return GB_OK;
+  if (outs == nullptr || srcs == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: outs or srcs is NULL", fn);
+  for (int b = 0; b < nbuckets; b++) {
+    if (ns[b] == 0) continue;
+    char name[48];
+    std::snprintf(name, sizeof name, "outs[%d]", b);
+    if ((s = check_array(outs[b], GB_ALIGN, fn, name)) != GB_OK) return s;
+    std::snprintf(name, sizeof name, "srcs[%d * k + r]", b);
+    const void* const* sp = reinterpret_cast<const void* const*>(srcs + (size_t)b * k);
+    if ((s = check_table(sp, k, GB_ALIGN, fn, name)) != GB_OK) return s;
+  }
+  size_t cs = 0, so = 0, ss = 0, need = 0;
+  if ((s = gb_bucket_workspace_layout(codec, k, total, GB_BLOCK, &cs, &so, &ss, &need)) != GB_OK) return s;
+  if (codec != GB_CODEC_NONE) {
+    if (workspace == nullptr || workspace_bytes < need) {
+      return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes,
+                  need);
+    }
+    if (!aligned(workspace, 256)) {
+      return fail(GB_ERR_MISALIGNED, "%s: workspace = %p is not 256-byte aligned", fn, workspace);
+    }
+  }
+  hipStream_t st = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t csz = code_size(codec);
+  hipError_t e = hipSuccess;
+  size_t o = 0;  // the bucket's first value in the workspace's virtual buffer
+  if (codec == GB_CODEC_NONE || k > kR) {
+    // one bucket at a time, exactly as gb_bucket_allreduce_local
+    for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
+      if (ns[b] == 0) continue;
+      const void* const* sp = reinterpret_cast<const void* const*>(srcs + (size_t)b * k);
+      e = bucket_groups(outs[b], sp, nullptr, k, ns[b], codec, scale_mode, GB_DTYPE_F32,
+                        ws == nullptr ? nullptr : ws + o * csz, cs,
+                        ws == nullptr ? nullptr : ws + so + 4 * (o / GB_BLOCK), ss, st);
+      o += round_up(ns[b], GB_BLOCK);
+    }
+    return from_hip(e, fn);
+  }
+  // up to kBatchBuckets buckets per launch, as many as one grid holds
+  gb::BucketBatch t = {};
+  size_t groups = 0;
+  auto flush = [&]() {
+    if (t.count == 0 || e != hipSuccess) return;
+    e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, st)
+                               : gb::launch_fused_fp8_batch(t, k, scale_mode, st);
+    t = gb::BucketBatch{};
+    groups = 0;
+  };
+  for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
+    if (ns[b] == 0) continue;
+    const size_t g = gb::batch_groups(codec, ns[b]);
+    if (t.count == (uint32_t)gb::kBatchBuckets || groups + g > gb::kMaxGrid) flush();
+    const uint32_t i = t.count++;
+    t.n[i] = ns[b];
+    t.out[i] = outs[b];
+    for (int r = 0; r < k; r++) {
+      t.src[i][r] = srcs[(size_t)b * k + r];
+      t.codes[i][r] = ws + (size_t)r * cs + o * csz;
+      t.scales[i][r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss + 4 * (o / GB_BLOCK));
+    }
+    groups += g;
+    o += round_up(ns[b], GB_BLOCK);
+  }
+  flush();
+  return from_hip(e, fn);
 }
 
 gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n, void* stream) {
@@ -752,8 +875,9 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, flo
   if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
     return s;
   }
-  return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32,
-                                static_cast<char*>(workspace), cs, so, ss, as_stream(stream)),
+  char* ws = static_cast<char*>(workspace);
+  return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32, ws, cs, ws + so, ss,
+                                as_stream(stream)),
                   fn);
 }
 
@@ -802,8 +926,9 @@ gb_status gb_bucket_allreduce_local_ef_typed(int dtype, void* out, const void* c
   if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
     return s;
   }
-  return from_hip(bucket_groups(out, srcs, residuals, k, n, codec, scale_mode, dtype, static_cast<char*>(workspace),
-                                cs, so, ss, as_stream(stream)),
+  char* ws = static_cast<char*>(workspace);
+  return from_hip(bucket_groups(out, srcs, residuals, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
+                                as_stream(stream)),
                   fn);
 }
 

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTab
 // Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
 template <int K, int ET, bool FULL>
-__device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n) {
-  const size_t sg = group_index<VecOrder>();
+__device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n,
+                                                size_t sg) {
   const uint32_t t = threadIdx.x;
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 x[K];
@@ -108,8 +108,28 @@ __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, 
 
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTable src, OutTable codes, size_t n) {
-  if (group_full<VecOrder>(kVecPerGroup, n)) fused_bf16_body<K, ET, true>(out, src, codes, n);
-  else fused_bf16_body<K, ET, false>(out, src, codes, n);
+  const size_t sg = group_index<VecOrder>();
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true>(out, src, codes, n, sg);
+  else fused_bf16_body<K, ET, false>(out, src, codes, n, sg);
+}
+
+// Several buckets in one launch (float32 gradients), as the fp8 batch: each
+// workgroup finds its bucket, then takes that bucket's vector group.
+template <int K>
+__global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch t) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  PtrTable src;
+  OutTable codes;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    codes.p[r] = t.codes[b][r];
+  }
+  const size_t sg = w - t.first[b], n = t.n[b];
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, GB_DTYPE_F32, true>(t.out[b], src, codes, n, sg);
+  else fused_bf16_body<K, GB_DTYPE_F32, false>(t.out[b], src, codes, n, sg);
 }
 
 // Launcher bodies, one per element type ET.
@@ -176,6 +196,21 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 #define GB_CALL(ET) fused_bf16_t<ET>(out, srcs, c, k, n, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
+}
+
+hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, hipStream_t stream) {
+  if (t.count == 0 || t.count > (uint32_t)kBatchBuckets) return hipErrorInvalidValue;
+  size_t grid = 0;
+  for (uint32_t b = 0; b < t.count; b++) {
+    t.first[b] = grid;
+    grid += batch_groups(GB_CODEC_BF16, t.n[b]);
+  }
+  for (int b = (int)t.count; b <= kBatchBuckets; b++) t.first[b] = grid;
+  if (grid == 0 || grid > kMaxGrid) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_bf16_batch_kernel<K><<<grid, kThreads, 0, stream>>>(t);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_encode_bf16(float* sum, uint16_t* codes, const PtrTable& srcs, int k, size_t n,

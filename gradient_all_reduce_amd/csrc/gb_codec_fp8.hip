@@ -118,9 +118,9 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTabl
 // ===========================================================================
 template <int K, int ET, bool FULL>
 __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, const OutTable& codes,
-                                               const OutTable& scales, size_t n, int mode) {
+                                               const OutTable& scales, size_t n, int mode, size_t g) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = g * kBlocksPerGroup + (threadIdx.x >> 4);
   constexpr int MAP = codec_map<ET>();
   f4 x[K][4];
 #pragma unroll
@@ -149,8 +149,30 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable src, OutTable codes,
                                                               OutTable scales, size_t n, int mode) {
-  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode);
-  else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode);
+  const size_t g = group_index<BlockOrder>();
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode, g);
+  else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode, g);
+}
+
+// Several buckets in one launch (float32 gradients): each workgroup finds its
+// bucket from the table of first workgroups, then runs the fused pass over
+// that bucket's group, in index order.
+template <int K>
+__global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t, int mode) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  PtrTable src;
+  OutTable codes, scales;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    codes.p[r] = t.codes[b][r];
+    scales.p[r] = t.scales[b][r];
+  }
+  const size_t g = w - t.first[b], n = t.n[b];
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, GB_DTYPE_F32, true>(t.out[b], src, codes, scales, n, mode, g);
+  else fused_fp8_body<K, GB_DTYPE_F32, false>(t.out[b], src, codes, scales, n, mode, g);
 }
 
 // Launcher bodies, one per element type ET.  Accumulation into the output
@@ -219,6 +241,25 @@ hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* cod
 #define GB_CALL(ET) fused_fp8_t<ET>(out, srcs, c, s, k, n, scale_mode, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
+}
+
+size_t batch_groups(int codec, size_t n) {
+  return codec == GB_CODEC_BF16 ? ceil_div(n, kVecPerGroup) : ceil_div(n, kBlocksPerGroup * kBlock);
+}
+
+hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, hipStream_t stream) {
+  if (t.count == 0 || t.count > (uint32_t)kBatchBuckets) return hipErrorInvalidValue;
+  size_t grid = 0;
+  for (uint32_t b = 0; b < t.count; b++) {
+    t.first[b] = grid;
+    grid += batch_groups(GB_CODEC_FP8_E4M3_B256, t.n[b]);
+  }
+  for (int b = (int)t.count; b <= kBatchBuckets; b++) t.first[b] = grid;
+  if (grid == 0 || grid > kMaxGrid) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_fp8_batch_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(t, scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_encode_fp8(float* sum, uint8_t* codes, float* scales, const PtrTable& srcs, int k,

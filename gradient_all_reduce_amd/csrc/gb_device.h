@@ -720,7 +720,6 @@ __device__ __forceinline__ void store_group_f32(float* p, size_t sg, uint32_t t,
 // ---------------------------------------------------------------------------
 // Launch helpers.
 // ---------------------------------------------------------------------------
-constexpr size_t kMaxGrid = ((size_t)1 << 31) - 1;
 
 // Dynamic LDS reserved per workgroup: an occupancy cap.  No kernel uses LDS;
 // reserving 48, 64 or 81 KiB of the 160 KiB a compute unit has caps it at 3,

@@ -71,6 +71,10 @@ extern "C" {
  * buffer, beyond the memory of any one GPU), so that no size or offset the
  * library computes from n can wrap. */
 #define GB_MAX_N ((size_t)1 << 39)
+/* Largest number of buckets one gb_bucket_allreduce_local_batch call takes;
+ * their sizes, each rounded up to a multiple of 256, add up to at most
+ * GB_MAX_N. */
+#define GB_MAX_BATCH 4096
 
 typedef enum gb_status {
   GB_OK = 0,
@@ -261,6 +265,45 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
                                     int codec, int scale_mode,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * gb_bucket_allreduce_local_batch — the bucket stream over nbuckets buckets
+ * that live in separate buffers, as a DDP hook holds them (README "How it
+ * works": one all_reduce per gradient bucket).  Bucket b of ns[b] values has
+ * its own k float32 sources srcs[b * k + r] and its own output outs[b], and
+ * gives, bit for bit, what gb_bucket_allreduce_local gives for it alone with
+ * bucket_elems >= ns[b]: fp8 blocks restart at each bucket.  With k <= 8 and
+ * a bf16 or fp8 codec, up to 16 buckets run in one launch, so buckets that
+ * are ready together keep the GPU full where one small bucket per launch
+ * cannot; otherwise the buckets run one after another.
+ *   outs       host array of nbuckets device fp32[ns[b]] pointers, written;
+ *              outs[b] may equal srcs[b * k]; no other overlap between any
+ *              output, source or the workspace.
+ *   srcs       host array of nbuckets * k device fp32 pointers, bucket-major.
+ *   ns         host array of nbuckets sizes, each 0 .. GB_MAX_N (a bucket
+ *              of 0 values is skipped, its pointers unread).
+ *   nbuckets   1 .. GB_MAX_BATCH; the sizes, each rounded up to a
+ *              multiple of 256, add up to at most GB_MAX_N.
+ *   workspace  device buffer of at least gb_bucket_batch_workspace_bytes();
+ *              rank r's payload of bucket b sits where the payload of values
+ *              [o_b, o_b + ns[b]) of one buffer would, in the layout
+ *              gb_bucket_workspace_layout() reports for that buffer, with
+ *              o_b the sum of ns[i] rounded up to a multiple of 256 over
+ *              i < b (unused for NONE, may then be NULL).
+ * Errors as gb_bucket_allreduce_local, checked for every bucket before
+ * anything is enqueued; the host arrays may be freed on return.
+ */
+gb_status gb_bucket_allreduce_local_batch(float* const* outs,
+                                          const float* const* srcs,
+                                          const size_t* ns, int nbuckets, int k,
+                                          int codec, int scale_mode,
+                                          void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of gb_bucket_allreduce_local_batch (0 on invalid
+ * arguments, or for codec NONE). */
+size_t gb_bucket_batch_workspace_bytes(int codec, int k, const size_t* ns,
+                                       int nbuckets);
 
 /*
  * gb_reduce_encode — the leader's island sum and its bridge payload in one

@@ -1,0 +1,164 @@
+"""GPU parity of gb_bucket_allreduce_local_batch: buckets in separate
+buffers, each with its own sources and output, against the oracle's bucket
+stream of that bucket alone (fp8 blocks restart at each bucket), bit for
+bit, with every rank's payload checked where the workspace layout puts it.
+Up to 16 buckets share a launch; lists of more buckets, empty buckets, ragged
+sizes, 9..16 ranks (one bucket at a time), the uncompressed codec, outputs
+over the first source, and a replayed HIP graph are covered too."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from oracle import oracle as O  # noqa: E402
+import workloads as W  # noqa: E402
+
+DEV = "cuda:0"
+SIZES = [1000, 0, 1, 255, 256, 257, 4096 * 2 + 100, 513, 12_345, 4096, 77, 20_000,
+         300, 1024, 5, 700, 4096 * 4, 999, 256 * 3 + 1, 64]  # 20 buckets, 19 of them in two launches
+CODECS = [(O.CODEC_BF16, 0), (O.CODEC_FP8, O.SCALE_ABSMAX_DIV_448), (O.CODEC_FP8, O.SCALE_POW2)]
+
+
+@pytest.fixture(scope="module")
+def gb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gradient_all_reduce_amd as lib
+    return lib
+
+
+def host_buckets(sizes, k, seed):
+    out = []
+    for b, n in enumerate(sizes):
+        xs = [W.gradients(n, seed + 100 * b + r) if n else np.empty(0, np.float32) for r in range(k)]
+        out.append(xs)
+    return out
+
+
+def to_dev(buckets):
+    return [[torch.from_numpy(x.copy()).to(DEV) for x in xs] for xs in buckets]
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def offsets(sizes):
+    o, offs = 0, []
+    for n in sizes:
+        offs.append(o)
+        o += (n + 255) // 256 * 256
+    return offs, o
+
+
+def check(gb, sizes, k, codec, mode, seed, in_place=False):
+    hb = host_buckets(sizes, k, seed)
+    db = to_dev(hb)
+    outs = [xs[0] if in_place else torch.full((n,), float("nan"), device=DEV) for xs, n in zip(db, sizes)]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, sizes)
+    ws = torch.full((max(need, 1),), 0xEE, dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch(outs, db, codec, mode, ws if need else None)
+    torch.cuda.synchronize()
+    offs, total = offsets(sizes)
+    lay = gb.gb_bucket_workspace_layout(codec, k, total, 256) if codec != O.CODEC_NONE else None
+    wsh = ws.cpu().numpy()
+    for b, (xs, n) in enumerate(zip(hb, sizes)):
+        if n == 0:
+            continue
+        bucket = (n + 255) // 256 * 256
+        want, wc, wsc = O.bucket_allreduce(xs, bucket, codec, mode)
+        what = f"sizes={sizes} k={k} codec={codec} mode={mode} bucket {b} (n={n})"
+        assert (bits(outs[b].cpu().numpy()) == bits(want)).all(), what
+        if lay is None:
+            continue
+        for r in range(k):
+            if codec == O.CODEC_BF16:
+                c0 = r * lay["codes_stride"] + 2 * offs[b]
+                assert (wsh[c0:c0 + 2 * n].view(np.uint16) == wc[r]).all(), what + f" codes {r}"
+            else:
+                c0 = r * lay["codes_stride"] + offs[b]
+                assert (wsh[c0:c0 + n] == wc[r]).all(), what + f" codes {r}"
+                s0 = lay["scales_offset"] + r * lay["scales_stride"] + 4 * (offs[b] // 256)
+                assert (wsh[s0:s0 + 4 * wsc[r].size].view(np.uint32) == bits(wsc[r])).all(), what + f" scales {r}"
+
+
+@pytest.mark.parametrize("codec,mode", CODECS)
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+def test_matches_the_oracle_bucket_by_bucket(gb, codec, mode, k):
+    check(gb, SIZES, k, codec, mode, 3000 + 10 * k + codec + mode)
+
+
+@pytest.mark.parametrize("codec,mode", CODECS + [(O.CODEC_NONE, 0)])
+def test_more_ranks_than_one_launch_reads(gb, codec, mode):
+    check(gb, [300, 0, 4096 + 5, 256], 11, codec, mode, 3100 + codec + mode)
+
+
+def test_uncompressed_codec_is_the_plain_sum(gb):
+    check(gb, SIZES[:5], 3, O.CODEC_NONE, 0, 3200)
+
+
+@pytest.mark.parametrize("codec", [O.CODEC_BF16, O.CODEC_FP8])
+def test_outputs_over_the_first_sources(gb, codec):
+    check(gb, [1000, 4096 * 3 + 1, 256], 4, codec, 0, 3300, in_place=True)
+
+
+@pytest.mark.parametrize("codec", [O.CODEC_BF16, O.CODEC_FP8])
+def test_equals_one_call_per_bucket_at_bucket_sizes(gb, codec):
+    """Buckets of one GPU's 1/8 share of a 25 MiB bucket (819,200 values) and
+    a ragged last one, 21 of them (two launches), four ranks: the same bits
+    and payloads as gb_bucket_allreduce_local called once per bucket."""
+    sizes = [819_200] * 20 + [481_600 + 37]
+    k = 4
+    x = [[W.device_gradients(n, 3400 + 10 * b + r, DEV) for r in range(k)] for b, n in enumerate(sizes)]
+    outs = [torch.empty(n, device=DEV) for n in sizes]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, sizes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch(outs, x, codec, 0, ws)
+    offs, total = offsets(sizes)
+    lay = gb.gb_bucket_workspace_layout(codec, k, total, 256)
+    csz = 2 if codec == O.CODEC_BF16 else 1
+    for b, n in enumerate(sizes):
+        ref = torch.empty(n, device=DEV)
+        w1 = torch.zeros(gb.gb_bucket_workspace_bytes(codec, k, n, 819_200), dtype=torch.uint8, device=DEV)
+        gb.gb_bucket_allreduce_local(ref, x[b], 819_200, codec, 0, w1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[b].view(torch.int32), ref.view(torch.int32)), f"bucket {b}"
+        l1 = gb.gb_bucket_workspace_layout(codec, k, n, 819_200)
+        for r in range(k):
+            a = ws[r * lay["codes_stride"] + csz * offs[b]:][:csz * n]
+            assert torch.equal(a, w1[r * l1["codes_stride"]:][:csz * n]), f"bucket {b} codes {r}"
+            if codec == O.CODEC_FP8:
+                nb = (n + 255) // 256
+                a = ws[lay["scales_offset"] + r * lay["scales_stride"] + 4 * (offs[b] // 256):][:4 * nb]
+                assert torch.equal(a, w1[l1["scales_offset"] + r * l1["scales_stride"]:][:4 * nb]), f"scales {r}"
+
+
+def test_replayed_graph_matches_eager(gb):
+    """The call captured in a HIP graph (kernel launches only) and replayed
+    three times with new inputs and eager work in between."""
+    sizes, k = [5000, 819_200, 256, 70_000], 4
+    x = [[torch.empty(n, device=DEV) for _ in range(k)] for n in sizes]
+    outs = [torch.empty(n, device=DEV) for n in sizes]
+    ws = torch.empty(gb.gb_bucket_batch_workspace_bytes(O.CODEC_FP8, k, sizes), dtype=torch.uint8, device=DEV)
+    for b in range(len(sizes)):
+        for r in range(k):
+            x[b][r].copy_(W.device_gradients(sizes[b], 3500 + 10 * b + r, DEV))
+    gb.gb_bucket_allreduce_local_batch(outs, x, O.CODEC_FP8, 0, ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gb.gb_bucket_allreduce_local_batch(outs, x, O.CODEC_FP8, 0, ws)
+    for rep in range(3):
+        for b in range(len(sizes)):
+            for r in range(k):
+                x[b][r].copy_(W.device_gradients(sizes[b], 3600 + 100 * rep + 10 * b + r, DEV))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        ref = [torch.empty_like(o) for o in outs]
+        gb.gb_bucket_allreduce_local_batch(ref, x, O.CODEC_FP8, 0, ws)
+        torch.cuda.synchronize()
+        for b in range(len(sizes)):
+            assert torch.equal(got[b].view(torch.int32), ref[b].view(torch.int32)), f"replay {rep} bucket {b}"
