@@ -68,7 +68,7 @@ _SIGNATURES = {
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
-    "gb_bucket_allreduce_local_batch": (_I, [_PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
+    "gb_bucket_allreduce_local_batch": (_I, [_I, _PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
     "gb_bucket_batch_workspace_bytes": (_S, [_I, _I, _SP, _I]),
     "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
@@ -257,20 +257,23 @@ def _size_array(ns):
 
 def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
                                     workspace=None, stream=None):
-    """The bucket stream over separately allocated buckets: outs[b] (float32)
-    receives bucket b's result from the k float32 tensors srcs[b], as
-    gb_bucket_allreduce_local on that bucket alone; up to 16 buckets per
-    launch."""
+    """The bucket stream over separately allocated buckets: outs[b] receives
+    bucket b's result from the k tensors srcs[b] (all float32, float16,
+    bfloat16 or float64, of one type), as gb_bucket_allreduce_local_typed on
+    that bucket alone; up to 16 buckets per launch."""
     if len(outs) != len(srcs):
         raise ValueError(f"{len(outs)} outputs for {len(srcs)} buckets of sources")
     k = len(srcs[0]) if srcs else 0
+    dtype = outs[0].dtype if outs else torch.float32
+    if dtype not in _CODEC_TYPES:
+        raise TypeError(f"outs must be tensors of one of {list(_CODEC_TYPES)}")
     ns, flat = [], []
     for b, (o, ss) in enumerate(zip(outs, srcs)):
-        _device_tensor(o, torch.float32, f"outs[{b}]")
+        _device_tensor(o, dtype, f"outs[{b}]")
         if len(ss) != k:
             raise ValueError(f"bucket {b} has {len(ss)} sources, bucket 0 has {k}")
         for r, t in enumerate(ss):
-            _device_tensor(t, torch.float32, f"srcs[{b}][{r}]")
+            _device_tensor(t, dtype, f"srcs[{b}][{r}]")
         _same_numel(ss, o.numel(), f"srcs[{b}]")
         ns.append(o.numel())
         flat.extend(ss)
@@ -279,7 +282,8 @@ def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMA
         _device_tensor(workspace, torch.uint8, "workspace")
         ws_bytes = workspace.numel()
     device = outs[0].device if outs else torch.device("cuda", torch.cuda.current_device())
-    _check(_lib.gb_bucket_allreduce_local_batch(_ptr_array(outs), _ptr_array(flat), _size_array(ns), len(outs),
+    _check(_lib.gb_bucket_allreduce_local_batch(GB_DTYPE[dtype], _ptr_array(outs), _ptr_array(flat),
+                                                _size_array(ns), len(outs),
                                                 k, int(codec), int(scale_mode), _ptr(workspace), ws_bytes,
                                                 _stream(stream, device)))
 

@@ -753,16 +753,21 @@ size_t gb_bucket_batch_workspace_bytes(int codec, int k, const size_t* ns, int n
   return s == GB_OK ? bytes : 0;
 }
 
-gb_status gb_bucket_allreduce_local_batch(float* const* outs, const float* const* srcs, const size_t* ns,
+gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const void* const* srcs, const size_t* ns,
                                           int nbuckets, int k, int codec, int scale_mode, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   const char* fn = "gb_bucket_allreduce_local_batch";
+  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
   if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
     return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
   }
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
+  if (k > kR && dtype != GB_DTYPE_F32 && codec != GB_CODEC_NONE) {
+    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
+                "which holds up to %d ranks per call", fn, k, kR);
+  }
   size_t total;
   if ((s = check_batch_sizes(fn, ns, nbuckets, &total)) != GB_OK) return s;
   if (total == 0) return GB_OK;
@@ -773,8 +778,7 @@ gb_status gb_bucket_allreduce_local_batch(float* const* outs, const float* const
     std::snprintf(name, sizeof name, "outs[%d]", b);
     if ((s = check_array(outs[b], GB_ALIGN, fn, name)) != GB_OK) return s;
     std::snprintf(name, sizeof name, "srcs[%d * k + r]", b);
-    const void* const* sp = reinterpret_cast<const void* const*>(srcs + (size_t)b * k);
-    if ((s = check_table(sp, k, GB_ALIGN, fn, name)) != GB_OK) return s;
+    if ((s = check_table(srcs + (size_t)b * k, k, GB_ALIGN, fn, name)) != GB_OK) return s;
   }
   size_t cs = 0, so = 0, ss = 0, need = 0;
   if ((s = gb_bucket_workspace_layout(codec, k, total, GB_BLOCK, &cs, &so, &ss, &need)) != GB_OK) return s;
@@ -796,8 +800,7 @@ gb_status gb_bucket_allreduce_local_batch(float* const* outs, const float* const
     // one bucket at a time, exactly as gb_bucket_allreduce_local
     for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
       if (ns[b] == 0) continue;
-      const void* const* sp = reinterpret_cast<const void* const*>(srcs + (size_t)b * k);
-      e = bucket_groups(outs[b], sp, nullptr, k, ns[b], codec, scale_mode, GB_DTYPE_F32,
+      e = bucket_groups(outs[b], srcs + (size_t)b * k, nullptr, k, ns[b], codec, scale_mode, dtype,
                         ws == nullptr ? nullptr : ws + o * csz, cs,
                         ws == nullptr ? nullptr : ws + so + 4 * (o / GB_BLOCK), ss, st);
       o += round_up(ns[b], GB_BLOCK);
@@ -809,8 +812,8 @@ gb_status gb_bucket_allreduce_local_batch(float* const* outs, const float* const
   size_t groups = 0;
   auto flush = [&]() {
     if (t.count == 0 || e != hipSuccess) return;
-    e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, st)
-                               : gb::launch_fused_fp8_batch(t, k, scale_mode, st);
+    e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, dtype, st)
+                               : gb::launch_fused_fp8_batch(t, k, scale_mode, dtype, st);
     t = gb::BucketBatch{};
     groups = 0;
   };

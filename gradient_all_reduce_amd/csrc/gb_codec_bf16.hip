@@ -113,9 +113,10 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTabl
   else fused_bf16_body<K, ET, false>(out, src, codes, n, sg);
 }
 
-// Several buckets in one launch (float32 gradients), as the fp8 batch: each
-// workgroup finds its bucket, then takes that bucket's vector group.
-template <int K>
+// Several buckets in one launch (gradients of element type ET), as the fp8
+// batch: each workgroup finds its bucket, then takes that bucket's vector
+// group.
+template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch t) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
@@ -128,8 +129,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch 
     codes.p[r] = t.codes[b][r];
   }
   const size_t sg = w - t.first[b], n = t.n[b];
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, GB_DTYPE_F32, true>(t.out[b], src, codes, n, sg);
-  else fused_bf16_body<K, GB_DTYPE_F32, false>(t.out[b], src, codes, n, sg);
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true>(t.out[b], src, codes, n, sg);
+  else fused_bf16_body<K, ET, false>(t.out[b], src, codes, n, sg);
 }
 
 // Launcher bodies, one per element type ET.
@@ -198,7 +199,17 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 #undef GB_CALL
 }
 
-hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, hipStream_t stream) {
+namespace {
+template <int ET>
+hipError_t fused_bf16_batch_t(BucketBatch& t, size_t grid, int k, hipStream_t stream) {
+#define GB_CALL(K) fused_bf16_batch_kernel<K, ET><<<grid, kThreads, 0, stream>>>(t);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, int dtype, hipStream_t stream) {
   if (t.count == 0 || t.count > (uint32_t)kBatchBuckets) return hipErrorInvalidValue;
   size_t grid = 0;
   for (uint32_t b = 0; b < t.count; b++) {
@@ -207,10 +218,9 @@ hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, hipStream_t stream) {
   }
   for (int b = (int)t.count; b <= kBatchBuckets; b++) t.first[b] = grid;
   if (grid == 0 || grid > kMaxGrid) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_bf16_batch_kernel<K><<<grid, kThreads, 0, stream>>>(t);
-  GB_DISPATCH_K(k, GB_CALL)
+#define GB_CALL(ET) fused_bf16_batch_t<ET>(t, grid, k, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
-  return hipGetLastError();
 }
 
 hipError_t launch_reduce_encode_bf16(float* sum, uint16_t* codes, const PtrTable& srcs, int k, size_t n,

@@ -154,10 +154,10 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable
   else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode, g);
 }
 
-// Several buckets in one launch (float32 gradients): each workgroup finds its
-// bucket from the table of first workgroups, then runs the fused pass over
-// that bucket's group, in index order.
-template <int K>
+// Several buckets in one launch (gradients of element type ET): each
+// workgroup finds its bucket from the table of first workgroups, then runs
+// the fused pass over that bucket's group, in index order.
+template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t, int mode) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t
     scales.p[r] = t.scales[b][r];
   }
   const size_t g = w - t.first[b], n = t.n[b];
-  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, GB_DTYPE_F32, true>(t.out[b], src, codes, scales, n, mode, g);
-  else fused_fp8_body<K, GB_DTYPE_F32, false>(t.out[b], src, codes, scales, n, mode, g);
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, ET, true>(t.out[b], src, codes, scales, n, mode, g);
+  else fused_fp8_body<K, ET, false>(t.out[b], src, codes, scales, n, mode, g);
 }
 
 // Launcher bodies, one per element type ET.  Accumulation into the output
@@ -247,7 +247,19 @@ size_t batch_groups(int codec, size_t n) {
   return codec == GB_CODEC_BF16 ? ceil_div(n, kVecPerGroup) : ceil_div(n, kBlocksPerGroup * kBlock);
 }
 
-hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, hipStream_t stream) {
+namespace {
+// Batched launches are bucket-sized pieces: they take the fused pass's cap
+// for launches below every size threshold.
+template <int ET>
+hipError_t fused_fp8_batch_t(BucketBatch& t, size_t grid, int k, int scale_mode, hipStream_t stream) {
+#define GB_CALL(K) fused_fp8_batch_kernel<K, ET><<<grid, kThreads, fused_fp8_lds<ET>(K, 0), stream>>>(t, scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, int dtype, hipStream_t stream) {
   if (t.count == 0 || t.count > (uint32_t)kBatchBuckets) return hipErrorInvalidValue;
   size_t grid = 0;
   for (uint32_t b = 0; b < t.count; b++) {
@@ -256,10 +268,9 @@ hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, hipStre
   }
   for (int b = (int)t.count; b <= kBatchBuckets; b++) t.first[b] = grid;
   if (grid == 0 || grid > kMaxGrid) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_fp8_batch_kernel<K><<<grid, kThreads, heavy_lds(K), stream>>>(t, scale_mode);
-  GB_DISPATCH_K(k, GB_CALL)
+#define GB_CALL(ET) fused_fp8_batch_t<ET>(t, grid, k, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
-  return hipGetLastError();
 }
 
 hipError_t launch_reduce_encode_fp8(float* sum, uint8_t* codes, float* scales, const PtrTable& srcs, int k,

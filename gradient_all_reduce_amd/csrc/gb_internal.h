@@ -56,9 +56,9 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 hipError_t launch_fused_fp8(void* out, const PtrTable& srcs, uint8_t* const* codes, float* const* scales, int k,
                             size_t n, int scale_mode, int dtype, hipStream_t stream);
 
-// Up to kBatchBuckets separately allocated buckets in one fused launch over
-// float32 gradients, each with its own sources, output and payloads, passed
-// to the kernel by value (about 3.5 KiB of kernel arguments).  The caller
+// Up to kBatchBuckets separately allocated buckets in one fused launch, each
+// with its own sources, output and payloads, passed to the kernel by value
+// (about 3.5 KiB of kernel arguments).  The caller
 // fills count, n, out, src, codes and scales (scales for fp8 only); the
 // launcher fills first: bucket b takes workgroups [first[b], first[b + 1]).
 // 16 buckets per launch move 4-6% more bytes per second than 8 for buckets of
@@ -79,8 +79,8 @@ static_assert(sizeof(BucketBatch) <= 4000, "a batch must fit the 4 KiB of kernel
 // (GB_CODEC_BF16 or GB_CODEC_FP8_E4M3_B256).
 size_t batch_groups(int codec, size_t n);
 // Every bucket has 0 < n, and the workgroups of all buckets fit one grid.
-hipError_t launch_fused_fp8_batch(BucketBatch& batch, int k, int scale_mode, hipStream_t stream);
-hipError_t launch_fused_bf16_batch(BucketBatch& batch, int k, hipStream_t stream);
+hipError_t launch_fused_fp8_batch(BucketBatch& batch, int k, int scale_mode, int dtype, hipStream_t stream);
+hipError_t launch_fused_bf16_batch(BucketBatch& batch, int k, int dtype, hipStream_t stream);
 
 // The rank-order float32 sum of k sources encoded in one pass (sum stored too
 // when not NULL).

@@ -270,16 +270,19 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
  * gb_bucket_allreduce_local_batch — the bucket stream over nbuckets buckets
  * that live in separate buffers, as a DDP hook holds them (README "How it
  * works": one all_reduce per gradient bucket).  Bucket b of ns[b] values has
- * its own k float32 sources srcs[b * k + r] and its own output outs[b], and
- * gives, bit for bit, what gb_bucket_allreduce_local gives for it alone with
- * bucket_elems >= ns[b]: fp8 blocks restart at each bucket.  With k <= 8 and
+ * its own k sources srcs[b * k + r] and its own output outs[b], of element
+ * type dtype (GB_DTYPE_F32, F16, BF16 or F64), and gives, bit for bit, what
+ * gb_bucket_allreduce_local_typed gives for it alone with bucket_elems >=
+ * ns[b]: fp8 blocks restart at each bucket.  A compressed total of another
+ * type than float32 holds up to 8 ranks, as there.  With k <= 8 and
  * a bf16 or fp8 codec, up to 16 buckets run in one launch, so buckets that
  * are ready together keep the GPU full where one small bucket per launch
  * cannot; otherwise the buckets run one after another.
- *   outs       host array of nbuckets device fp32[ns[b]] pointers, written;
- *              outs[b] may equal srcs[b * k]; no other overlap between any
- *              output, source or the workspace.
- *   srcs       host array of nbuckets * k device fp32 pointers, bucket-major.
+ *   outs       host array of nbuckets device dtype[ns[b]] pointers,
+ *              written; outs[b] may equal srcs[b * k]; no other overlap
+ *              between any output, source or the workspace.
+ *   srcs       host array of nbuckets * k device dtype pointers,
+ *              bucket-major.
  *   ns         host array of nbuckets sizes, each 0 .. GB_MAX_N (a bucket
  *              of 0 values is skipped, its pointers unread).
  *   nbuckets   1 .. GB_MAX_BATCH; the sizes, each rounded up to a
@@ -293,8 +296,8 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
  * Errors as gb_bucket_allreduce_local, checked for every bucket before
  * anything is enqueued; the host arrays may be freed on return.
  */
-gb_status gb_bucket_allreduce_local_batch(float* const* outs,
-                                          const float* const* srcs,
+gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs,
+                                          const void* const* srcs,
                                           const size_t* ns, int nbuckets, int k,
                                           int codec, int scale_mode,
                                           void* workspace,

@@ -270,35 +270,35 @@ _BIG_WS = (ctypes.c_void_p(1 << 20), 1 << 30)
 
 
 @pytest.mark.parametrize("call,status,msg", [
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(10), 1, 1, 5, 0, *_BIG_WS, None), 3,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 1, 1, 5, 0, *_BIG_WS, None), 3,
      "unknown codec"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(10), 1, 1, 2, 4, *_BIG_WS, None), 3,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 4, *_BIG_WS, None), 3,
      "scale mode"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(10), 1, 0, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 1, 0, 2, 0, *_BIG_WS, None), 1,
      "k = 0"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(10), 0, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 0, 1, 2, 0, *_BIG_WS, None), 1,
      "nbuckets = 0"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(10), 4097, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 4097, 1, 2, 0, *_BIG_WS, None), 1,
      "nbuckets = 4097"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), None, 1, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), None, 1, 1, 2, 0, *_BIG_WS, None), 1,
      "ns is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256, 512), _arr(256, 512), _sizes(10, (1 << 39) + 1), 2, 1,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 512), _arr(256, 512), _sizes(10, (1 << 39) + 1), 2, 1,
                                                  2, 0, *_BIG_WS, None), 1, "ns[1]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256, 512), _arr(256, 512), _sizes(1 << 39, 1), 2, 1, 2, 0,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 512), _arr(256, 512), _sizes(1 << 39, 1), 2, 1, 2, 0,
                                                  *_BIG_WS, None), 1, "exceed GB_MAX_N"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(None, _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, None, _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 1,
      "outs or srcs is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256, 264), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 264), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
                                                  *_BIG_WS, None), 2, "outs[1]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256, 0), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 0), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
                                                  *_BIG_WS, None), 1, "outs[1] is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256, 512), _arr(256, 512, 768, 1032), _sizes(10, 10), 2, 2,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 512), _arr(256, 512, 768, 1032), _sizes(10, 10), 2, 2,
                                                  2, 0, *_BIG_WS, None), 2, "srcs[1 * k + r][1]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
                                                  ctypes.c_void_p(1 << 20), 100, None), 4, "needed"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(1000), 1, 1, 1, 0, None, 0, None), 4,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(1000), 1, 1, 1, 0, None, 0, None), 4,
      "needed"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(_arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
+    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
                                                  ctypes.c_void_p((1 << 20) + 16), 1 << 30, None), 2, "workspace"),
 ])
 def test_validation_of_the_batched_bucket_call(gb, call, status, msg):
@@ -306,12 +306,25 @@ def test_validation_of_the_batched_bucket_call(gb, call, status, msg):
     assert msg in gb.gb_last_error()
 
 
+@pytest.mark.parametrize("call,status,msg", [
+    (lambda L: L.gb_bucket_allreduce_local_batch(4, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 3,
+     "floating-point"),
+    (lambda L: L.gb_bucket_allreduce_local_batch(2, _arr(256), _arr(*[256] * 9), _sizes(10), 1, 9, 2, 0, *_BIG_WS,
+                                                 None), 1, "rounded once"),
+    (lambda L: L.gb_bucket_allreduce_local_batch(3, _arr(256), _arr(256, 264), _sizes(10), 1, 2, 1, 0, *_BIG_WS,
+                                                 None), 2, "srcs[0 * k + r][1]"),
+])
+def test_validation_of_the_typed_batched_bucket_call(gb, call, status, msg):
+    assert call(gb._lib) == status
+    assert msg in gb.gb_last_error()
+
+
 def test_batched_bucket_call_skips_empty_buckets_and_sizes_its_workspace(gb):
     L = gb._lib
     # every bucket empty: nothing to do, no pointer read
-    assert L.gb_bucket_allreduce_local_batch(None, None, _sizes(0, 0, 0), 3, 4, 2, 0, None, 0, None) == 0
+    assert L.gb_bucket_allreduce_local_batch(0, None, None, _sizes(0, 0, 0), 3, 4, 2, 0, None, 0, None) == 0
     # an empty bucket's pointers are not read: only bucket 1's are checked (and misaligned here)
-    assert L.gb_bucket_allreduce_local_batch(_arr(0, 264), _arr(0, 256), _sizes(0, 10), 2, 1, 2, 0,
+    assert L.gb_bucket_allreduce_local_batch(0, _arr(0, 264), _arr(0, 256), _sizes(0, 10), 2, 1, 2, 0,
                                              *_BIG_WS, None) == 2
     assert "outs[1]" in gb.gb_last_error()
     # the workspace is that of one buffer of the sizes rounded up to 256 values each

@@ -4,7 +4,8 @@ stream of that bucket alone (fp8 blocks restart at each bucket), bit for
 bit, with every rank's payload checked where the workspace layout puts it.
 Up to 16 buckets share a launch; lists of more buckets, empty buckets, ragged
 sizes, 9..16 ranks (one bucket at a time), the uncompressed codec, outputs
-over the first source, and a replayed HIP graph are covered too."""
+over the first source, float16, bfloat16 and float64 gradients, and a
+replayed HIP graph are covered too."""
 import numpy as np
 import pytest
 
@@ -162,3 +163,55 @@ def test_replayed_graph_matches_eager(gb):
         torch.cuda.synchronize()
         for b in range(len(sizes)):
             assert torch.equal(got[b].view(torch.int32), ref[b].view(torch.int32)), f"replay {rep} bucket {b}"
+
+
+TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}
+
+
+def typed_to_dev(a, dt):
+    if dt in ("f16", "bf16"):
+        return torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(TORCH[dt])
+    return torch.from_numpy(a.copy()).to(DEV)
+
+
+def typed_to_host(t):
+    if t.element_size() == 2:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint64)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f64"])
+@pytest.mark.parametrize("codec,mode", CODECS + [(O.CODEC_NONE, 0)])
+@pytest.mark.parametrize("k", [1, 4, 8])
+def test_typed_gradients_match_the_oracle(gb, dt, codec, mode, k):
+    """Buckets of float16, bfloat16 or float64 gradients: each total equals
+    the oracle's typed bucket stream of that bucket alone, and each payload
+    sits where the workspace layout puts it."""
+    sizes = [300, 0, 4096 * 3 + 17, 256, 1, 20_000, 513] + [700] * 12  # 18 buckets: two launches
+    hb = [[W.typed(n, dt, 3700 + 50 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+    db = [[typed_to_dev(x, dt) for x in xs] for xs in hb]
+    outs = [torch.empty(n, dtype=TORCH[dt], device=DEV) for n in sizes]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, sizes)
+    ws = torch.full((max(need, 1),), 0xEE, dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch(outs, db, codec, mode, ws if need else None)
+    torch.cuda.synchronize()
+    offs, total = offsets(sizes)
+    lay = gb.gb_bucket_workspace_layout(codec, k, total, 256) if codec != O.CODEC_NONE else None
+    wsh = ws.cpu().numpy()
+    for b, n in enumerate(sizes):
+        if n == 0:
+            continue
+        want, wc, wsc = O.bucket_allreduce_typed(hb[b], dt, (n + 255) // 256 * 256, codec, mode)
+        what = f"dt={dt} k={k} codec={codec} mode={mode} bucket {b} (n={n})"
+        assert typed_to_host(outs[b]).tobytes() == np.ascontiguousarray(want).tobytes(), what
+        if lay is None:
+            continue
+        for r in range(k):
+            if codec == O.CODEC_BF16:
+                c0 = r * lay["codes_stride"] + 2 * offs[b]
+                assert (wsh[c0:c0 + 2 * n].view(np.uint16) == wc[r]).all(), what + f" codes {r}"
+            else:
+                c0 = r * lay["codes_stride"] + offs[b]
+                assert (wsh[c0:c0 + n] == wc[r]).all(), what + f" codes {r}"
+                s0 = lay["scales_offset"] + r * lay["scales_stride"] + 4 * (offs[b] // 256)
+                assert (wsh[s0:s0 + 4 * wsc[r].size].view(np.uint32) == bits(wsc[r])).all(), what + f" scales {r}"
