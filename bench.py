@@ -399,7 +399,54 @@ class DdpBucketsEF(DdpBuckets):
         return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):
-        return {}
+        """The same step as one gb_bucket_allreduce_local_ef call per bucket
+        and through gb_bucket_allreduce_local_batch_ef (8 buckets per launch),
+        each captured in a HIP graph; the two give the same bits from the
+        same residuals."""
+        if self.dt != "f32":
+            return {}
+        torch, gb = self.torch, self.gb
+        buckets = list(self.buckets())
+        outs = [self.out[s:s + n] for s, n in buckets]
+        srcs = [[t[s:s + n] for t in self.x] for s, n in buckets]
+        ress = [[t[s:s + n] for t in self.res] for s, n in buckets]
+        wsl, off = [], 0
+        for _, n in buckets:
+            need = gb.gb_bucket_workspace_bytes(self.codec, self.k, n, self.bucket)
+            wsl.append(self.ws[off:off + need])
+            off += need
+
+        def per_bucket():
+            for o, xs, rs, w in zip(outs, srcs, ress, wsl):
+                gb.gb_bucket_allreduce_local_ef(o, xs, rs, self.bucket, self.codec, self.mode, w)
+
+        need = gb.gb_bucket_batch_workspace_bytes(self.codec, self.k, [n for _, n in buckets])
+        wsb = self.ws if need <= self.ws.numel() else torch.empty(need, dtype=torch.uint8, device=self.dev)
+        batch = lambda: gb.gb_bucket_allreduce_local_batch_ef(outs, srcs, ress, self.codec, self.mode, wsb)
+        saved = [t.clone() for t in self.res]
+        per_bucket()
+        torch.cuda.synchronize()
+        want, want_res = self.out.clone(), [t.clone() for t in self.res]
+        for t, s0 in zip(self.res, saved):
+            t.copy_(s0)
+        batch()
+        torch.cuda.synchronize()
+        ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        ok &= all(bool(torch.equal(a.view(torch.int32), b.view(torch.int32))) for a, b in zip(self.res, want_res))
+        del saved, want, want_res
+        ms = {}
+        for name, fn in (("calls", per_bucket), ("batched", batch)):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            ms[name] = time_region(graph.replay, reps) / reps
+            del graph
+        gbs = lambda t: round(self.step_bytes() / (t * 1e-3) / 1e9, 2)
+        return {"per_bucket_calls_graph_gbs": gbs(ms["calls"]),
+                "per_bucket_calls_graph_ms": round(ms["calls"], 4),
+                "per_bucket_batched_graph_gbs": gbs(ms["batched"]),
+                "per_bucket_batched_graph_ms": round(ms["batched"], 4),
+                "per_bucket_batched_matches_calls": ok}
 
     def cpu_units(self):
         """One more step of the stream, checked against the oracle from the

@@ -27,7 +27,8 @@ __all__ = [
     "gb_reduce", "GB_OP_SUM", "GB_OP_AVG", "GB_OP_MAX", "GB_OP_MIN",
     "gb_encode_staged", "gb_decode_accumulate_staged", "gb_reduce_typed", "GB_DTYPE", "GB_DTYPE_OF",
     "gb_encode", "gb_decode_sum", "gb_bucket_allreduce_local_typed", "gb_reduce_encode",
-    "gb_bucket_allreduce_local_batch", "gb_bucket_batch_workspace_bytes", "GB_MAX_BATCH",
+    "gb_bucket_allreduce_local_batch", "gb_bucket_allreduce_local_batch_ef", "gb_bucket_batch_workspace_bytes",
+    "GB_MAX_BATCH",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -49,7 +50,7 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgbre
 if not os.path.exists(library_path):
     raise ImportError(
         f"libgbreduce is not built ({library_path} is missing); build it with "
-        "`python -m gradient_all_reduce_amd.build` or __graft_entry__.build()")
+        "`python gradient_all_reduce_amd/build.py` or __graft_entry__.build()")
 
 _lib = ctypes.CDLL(library_path)
 
@@ -69,6 +70,7 @@ _SIGNATURES = {
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
     "gb_bucket_allreduce_local_batch": (_I, [_I, _PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
+    "gb_bucket_allreduce_local_batch_ef": (_I, [_I, _PP, _PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
     "gb_bucket_batch_workspace_bytes": (_S, [_I, _I, _SP, _I]),
     "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
@@ -255,19 +257,16 @@ def _size_array(ns):
     return ctypes.cast(arr, _SP)
 
 
-def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
-                                    workspace=None, stream=None):
-    """The bucket stream over separately allocated buckets: outs[b] receives
-    bucket b's result from the k tensors srcs[b] (all float32, float16,
-    bfloat16 or float64, of one type), as gb_bucket_allreduce_local_typed on
-    that bucket alone; up to 16 buckets per launch."""
+def _batch_args(outs, srcs, residuals):
     if len(outs) != len(srcs):
         raise ValueError(f"{len(outs)} outputs for {len(srcs)} buckets of sources")
+    if residuals is not None and len(residuals) != len(srcs):
+        raise ValueError(f"{len(residuals)} buckets of residuals for {len(srcs)} buckets of sources")
     k = len(srcs[0]) if srcs else 0
     dtype = outs[0].dtype if outs else torch.float32
     if dtype not in _CODEC_TYPES:
         raise TypeError(f"outs must be tensors of one of {list(_CODEC_TYPES)}")
-    ns, flat = [], []
+    ns, flat, flat_res = [], [], []
     for b, (o, ss) in enumerate(zip(outs, srcs)):
         _device_tensor(o, dtype, f"outs[{b}]")
         if len(ss) != k:
@@ -275,17 +274,50 @@ def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMA
         for r, t in enumerate(ss):
             _device_tensor(t, dtype, f"srcs[{b}][{r}]")
         _same_numel(ss, o.numel(), f"srcs[{b}]")
+        if residuals is not None:
+            if len(residuals[b]) != k:
+                raise ValueError(f"bucket {b} has {len(residuals[b])} residuals for {k} sources")
+            for r, t in enumerate(residuals[b]):
+                _device_tensor(t, torch.float32, f"residuals[{b}][{r}]")
+            _same_numel(residuals[b], o.numel(), f"residuals[{b}]")
+            flat_res.extend(residuals[b])
         ns.append(o.numel())
         flat.extend(ss)
-    ws_bytes = 0
-    if workspace is not None:
-        _device_tensor(workspace, torch.uint8, "workspace")
-        ws_bytes = workspace.numel()
+    return k, dtype, ns, flat, flat_res
+
+
+def _workspace_args(workspace):
+    if workspace is None:
+        return _ptr(None), 0
+    _device_tensor(workspace, torch.uint8, "workspace")
+    return _ptr(workspace), workspace.numel()
+
+
+def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                    workspace=None, stream=None):
+    """The bucket stream over separately allocated buckets: outs[b] receives
+    bucket b's result from the k tensors srcs[b] (all float32, float16,
+    bfloat16 or float64, of one type), as gb_bucket_allreduce_local_typed on
+    that bucket alone; up to 16 buckets per launch."""
+    k, dtype, ns, flat, _ = _batch_args(outs, srcs, None)
     device = outs[0].device if outs else torch.device("cuda", torch.cuda.current_device())
     _check(_lib.gb_bucket_allreduce_local_batch(GB_DTYPE[dtype], _ptr_array(outs), _ptr_array(flat),
-                                                _size_array(ns), len(outs),
-                                                k, int(codec), int(scale_mode), _ptr(workspace), ws_bytes,
-                                                _stream(stream, device)))
+                                                _size_array(ns), len(outs), k, int(codec), int(scale_mode),
+                                                *_workspace_args(workspace), _stream(stream, device)))
+
+
+def gb_bucket_allreduce_local_batch_ef(outs, srcs, residuals, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                       workspace=None, stream=None):
+    """gb_bucket_allreduce_local_batch with error feedback: residuals[b][r]
+    (float32, one per source) is read and rewritten, as
+    gb_bucket_allreduce_local_ef_typed on each bucket alone; up to 8 buckets
+    per launch."""
+    k, dtype, ns, flat, flat_res = _batch_args(outs, srcs, residuals)
+    device = outs[0].device if outs else torch.device("cuda", torch.cuda.current_device())
+    _check(_lib.gb_bucket_allreduce_local_batch_ef(GB_DTYPE[dtype], _ptr_array(outs), _ptr_array(flat),
+                                                   _ptr_array(flat_res), _size_array(ns), len(outs), k,
+                                                   int(codec), int(scale_mode), *_workspace_args(workspace),
+                                                   _stream(stream, device)))
 
 
 _CODEC_TYPES = (torch.float32, torch.float16, torch.bfloat16, torch.float64)

@@ -753,12 +753,21 @@ size_t gb_bucket_batch_workspace_bytes(int codec, int k, const size_t* ns, int n
   return s == GB_OK ? bytes : 0;
 }
 
-gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const void* const* srcs, const size_t* ns,
-                                          int nbuckets, int k, int codec, int scale_mode, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local_batch";
+}  // extern "C"
+
+namespace {
+
+// The batched bucket stream, with error feedback when residuals is not NULL
+// (a host array of nbuckets * k residual pointers, bucket-major).
+gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void* const* srcs,
+                       float* const* residuals, const size_t* ns, int nbuckets, int k, int codec, int scale_mode,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const bool ef = residuals != nullptr;
   if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+  if (ef && codec == GB_CODEC_NONE) {
+    return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
+  }
   if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
     return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
   }
@@ -779,6 +788,11 @@ gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const vo
     if ((s = check_array(outs[b], GB_ALIGN, fn, name)) != GB_OK) return s;
     std::snprintf(name, sizeof name, "srcs[%d * k + r]", b);
     if ((s = check_table(srcs + (size_t)b * k, k, GB_ALIGN, fn, name)) != GB_OK) return s;
+    if (ef) {
+      std::snprintf(name, sizeof name, "residuals[%d * k + r]", b);
+      const void* const* rp = reinterpret_cast<const void* const*>(residuals + (size_t)b * k);
+      if ((s = check_table(rp, k, GB_ALIGN, fn, name)) != GB_OK) return s;
+    }
   }
   size_t cs = 0, so = 0, ss = 0, need = 0;
   if ((s = gb_bucket_workspace_layout(codec, k, total, GB_BLOCK, &cs, &so, &ss, &need)) != GB_OK) return s;
@@ -797,43 +811,91 @@ gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const vo
   hipError_t e = hipSuccess;
   size_t o = 0;  // the bucket's first value in the workspace's virtual buffer
   if (codec == GB_CODEC_NONE || k > kR) {
-    // one bucket at a time, exactly as gb_bucket_allreduce_local
+    // one bucket at a time, exactly as the single-buffer calls
     for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
       if (ns[b] == 0) continue;
-      e = bucket_groups(outs[b], srcs + (size_t)b * k, nullptr, k, ns[b], codec, scale_mode, dtype,
-                        ws == nullptr ? nullptr : ws + o * csz, cs,
+      e = bucket_groups(outs[b], srcs + (size_t)b * k, ef ? residuals + (size_t)b * k : nullptr, k, ns[b], codec,
+                        scale_mode, dtype, ws == nullptr ? nullptr : ws + o * csz, cs,
                         ws == nullptr ? nullptr : ws + so + 4 * (o / GB_BLOCK), ss, st);
       o += round_up(ns[b], GB_BLOCK);
     }
     return from_hip(e, fn);
   }
-  // up to kBatchBuckets buckets per launch, as many as one grid holds
+  // several buckets per launch, as many as the table and one grid hold
   gb::BucketBatch t = {};
+  gb::BucketBatchEf te = {};
+  const uint32_t cap = (uint32_t)(ef ? gb::kBatchBucketsEf : gb::kBatchBuckets);
+  uint32_t count = 0;
   size_t groups = 0;
   auto flush = [&]() {
-    if (t.count == 0 || e != hipSuccess) return;
-    e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, dtype, st)
-                               : gb::launch_fused_fp8_batch(t, k, scale_mode, dtype, st);
-    t = gb::BucketBatch{};
+    if (count == 0 || e != hipSuccess) return;
+    if (ef) {
+      te.count = count;
+      e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_ef_batch(te, k, dtype, st)
+                                 : gb::launch_fused_fp8_ef_batch(te, k, scale_mode, dtype, st);
+      te = gb::BucketBatchEf{};
+    } else {
+      t.count = count;
+      e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, dtype, st)
+                                 : gb::launch_fused_fp8_batch(t, k, scale_mode, dtype, st);
+      t = gb::BucketBatch{};
+    }
+    count = 0;
     groups = 0;
   };
   for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
     if (ns[b] == 0) continue;
     const size_t g = gb::batch_groups(codec, ns[b]);
-    if (t.count == (uint32_t)gb::kBatchBuckets || groups + g > gb::kMaxGrid) flush();
-    const uint32_t i = t.count++;
-    t.n[i] = ns[b];
-    t.out[i] = outs[b];
+    if (count == cap || groups + g > gb::kMaxGrid) flush();
+    const uint32_t i = count++;
     for (int r = 0; r < k; r++) {
-      t.src[i][r] = srcs[(size_t)b * k + r];
-      t.codes[i][r] = ws + (size_t)r * cs + o * csz;
-      t.scales[i][r] = reinterpret_cast<float*>(ws + so + (size_t)r * ss + 4 * (o / GB_BLOCK));
+      const void* x = srcs[(size_t)b * k + r];
+      void* c = ws + (size_t)r * cs + o * csz;
+      float* sc = reinterpret_cast<float*>(ws + so + (size_t)r * ss + 4 * (o / GB_BLOCK));
+      if (ef) {
+        te.src[i][r] = x;
+        te.codes[i][r] = c;
+        te.scales[i][r] = sc;
+        te.resid[i][r] = residuals[(size_t)b * k + r];
+      } else {
+        t.src[i][r] = x;
+        t.codes[i][r] = c;
+        t.scales[i][r] = sc;
+      }
+    }
+    if (ef) {
+      te.n[i] = ns[b];
+      te.out[i] = outs[b];
+    } else {
+      t.n[i] = ns[b];
+      t.out[i] = outs[b];
     }
     groups += g;
     o += round_up(ns[b], GB_BLOCK);
   }
   flush();
   return from_hip(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const void* const* srcs, const size_t* ns,
+                                          int nbuckets, int k, int codec, int scale_mode, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return bucket_batch("gb_bucket_allreduce_local_batch", dtype, outs, srcs, nullptr, ns, nbuckets, k, codec,
+                      scale_mode, workspace, workspace_bytes, stream);
+}
+
+gb_status gb_bucket_allreduce_local_batch_ef(int dtype, void* const* outs, const void* const* srcs,
+                                             float* const* residuals, const size_t* ns, int nbuckets, int k,
+                                             int codec, int scale_mode, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  const char* fn = "gb_bucket_allreduce_local_batch_ef";
+  if (residuals == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: residuals is NULL", fn);
+  return bucket_batch(fn, dtype, outs, srcs, residuals, ns, nbuckets, k, codec, scale_mode, workspace,
+                      workspace_bytes, stream);
 }
 
 gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n, void* stream) {

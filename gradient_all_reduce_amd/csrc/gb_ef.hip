@@ -63,9 +63,9 @@ __global__ __launch_bounds__(kThreads) void encode_fp8_ef_kernel(uint8_t* codes,
 template <int K, int ET, bool FULL>
 __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src, const OutTable& resid,
                                                   const OutTable& codes, const OutTable& scales, size_t n,
-                                                  int mode) {
+                                                  int mode, size_t g) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = group_index<BlockOrder>() * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = g * kBlocksPerGroup + (threadIdx.x >> 4);
   constexpr int MAP = ef_map<ET>();
   f4 y[K][4];
 #pragma unroll
@@ -105,14 +105,14 @@ template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_fp8_ef_kernel(void* out, PtrTable src, OutTable resid,
                                                                  OutTable codes, OutTable scales, size_t n,
                                                                  int mode) {
-  if (group_full<BlockOrder>(kBlocksPerGroup * kBlock, n)) fused_fp8_ef_body<K, ET, true>(out, src, resid, codes, scales, n, mode);
-  else fused_fp8_ef_body<K, ET, false>(out, src, resid, codes, scales, n, mode);
+  const size_t g = group_index<BlockOrder>();
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_ef_body<K, ET, true>(out, src, resid, codes, scales, n, mode, g);
+  else fused_fp8_ef_body<K, ET, false>(out, src, resid, codes, scales, n, mode, g);
 }
 
 template <int K, int ET, bool FULL>
 __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& src, const OutTable& resid,
-                                                   const OutTable& codes, size_t n) {
-  const size_t sg = group_index<VecOrder>();
+                                                   const OutTable& codes, size_t n, size_t sg) {
   const uint32_t t = threadIdx.x;
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 y[K];
@@ -136,8 +136,83 @@ __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& sr
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrTable src, OutTable resid,
                                                                   OutTable codes, size_t n) {
-  if (group_full<VecOrder>(kVecPerGroup, n)) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n);
-  else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n);
+  const size_t sg = group_index<VecOrder>();
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n, sg);
+  else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, sg);
+}
+
+// Several buckets in one launch, with their residuals: each workgroup finds
+// its bucket from the table of first workgroups and takes that bucket's
+// group, in index order.
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_fp8_ef_batch_kernel(BucketBatchEf t, int mode) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  PtrTable src;
+  OutTable resid, codes, scales;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    resid.p[r] = t.resid[b][r];
+    codes.p[r] = t.codes[b][r];
+    scales.p[r] = t.scales[b][r];
+  }
+  const size_t g = w - t.first[b], n = t.n[b];
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_ef_body<K, ET, true>(t.out[b], src, resid, codes, scales, n, mode, g);
+  else fused_fp8_ef_body<K, ET, false>(t.out[b], src, resid, codes, scales, n, mode, g);
+}
+
+template <int K, int ET>
+__global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBatchEf t) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  PtrTable src;
+  OutTable resid, codes;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    resid.p[r] = t.resid[b][r];
+    codes.p[r] = t.codes[b][r];
+  }
+  const size_t sg = w - t.first[b], n = t.n[b];
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(t.out[b], src, resid, codes, n, sg);
+  else fused_bf16_ef_body<K, ET, false>(t.out[b], src, resid, codes, n, sg);
+}
+
+// The table's first workgroups and the grid; 0 if the table is empty or too large.
+size_t batch_grid(BucketBatchEf& t, int codec) {
+  if (t.count == 0 || t.count > (uint32_t)kBatchBucketsEf) return 0;
+  size_t grid = 0;
+  for (uint32_t b = 0; b < t.count; b++) {
+    t.first[b] = grid;
+    grid += batch_groups(codec, t.n[b]);
+  }
+  for (int b = (int)t.count; b <= kBatchBucketsEf; b++) t.first[b] = grid;
+  return grid > kMaxGrid ? 0 : grid;
+}
+
+// Batched launches are bucket-sized pieces: they take each pass's cap for
+// launches below every size threshold.
+template <int ET>
+hipError_t fused_fp8_ef_batch_t(BucketBatchEf& t, int k, int scale_mode, hipStream_t stream) {
+  const size_t grid = batch_grid(t, GB_CODEC_FP8_E4M3_B256);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_fp8_ef_batch_kernel<K, ET><<<grid, kThreads, fused_fp8_ef_lds(K, 0), stream>>>(t, scale_mode);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t fused_bf16_ef_batch_t(BucketBatchEf& t, int k, hipStream_t stream) {
+  const size_t grid = batch_grid(t, GB_CODEC_BF16);
+  if (grid == 0) return hipErrorInvalidValue;
+#define GB_CALL(K) fused_bf16_ef_batch_kernel<K, ET><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(t);
+  GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+  return hipGetLastError();
 }
 
 template <int ET>
@@ -203,6 +278,18 @@ hipError_t launch_fused_bf16_ef(void* out, const PtrTable& srcs, float* const* r
     rs.p[r] = residuals[r];
   }
 #define GB_CALL(ET) fused_bf16_ef_t<ET>(out, srcs, rs, c, k, n, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_fp8_ef_batch(BucketBatchEf& t, int k, int scale_mode, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) fused_fp8_ef_batch_t<ET>(t, k, scale_mode, stream)
+  GB_DISPATCH_ET(dtype, GB_CALL)
+#undef GB_CALL
+}
+
+hipError_t launch_fused_bf16_ef_batch(BucketBatchEf& t, int k, int dtype, hipStream_t stream) {
+#define GB_CALL(ET) fused_bf16_ef_batch_t<ET>(t, k, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
 }

@@ -75,12 +75,29 @@ struct BucketBatch {
   float* scales[kBatchBuckets][kLaunchRanks];
 };
 static_assert(sizeof(BucketBatch) <= 4000, "a batch must fit the 4 KiB of kernel arguments");
+// The error-feedback form also carries each rank's residual, so it takes 8
+// buckets per launch to stay within the kernel arguments.
+constexpr int kBatchBucketsEf = 8;
+struct BucketBatchEf {
+  uint32_t count;
+  size_t first[kBatchBucketsEf + 1];
+  size_t n[kBatchBucketsEf];
+  void* out[kBatchBucketsEf];
+  const void* src[kBatchBucketsEf][kLaunchRanks];
+  void* codes[kBatchBucketsEf][kLaunchRanks];
+  float* scales[kBatchBucketsEf][kLaunchRanks];
+  float* resid[kBatchBucketsEf][kLaunchRanks];
+};
+static_assert(sizeof(BucketBatchEf) <= 4000, "a batch must fit the 4 KiB of kernel arguments");
+
 // Workgroups of one bucket of n values in a batched launch of codec
 // (GB_CODEC_BF16 or GB_CODEC_FP8_E4M3_B256).
 size_t batch_groups(int codec, size_t n);
 // Every bucket has 0 < n, and the workgroups of all buckets fit one grid.
 hipError_t launch_fused_fp8_batch(BucketBatch& batch, int k, int scale_mode, int dtype, hipStream_t stream);
 hipError_t launch_fused_bf16_batch(BucketBatch& batch, int k, int dtype, hipStream_t stream);
+hipError_t launch_fused_fp8_ef_batch(BucketBatchEf& batch, int k, int scale_mode, int dtype, hipStream_t stream);
+hipError_t launch_fused_bf16_ef_batch(BucketBatchEf& batch, int k, int dtype, hipStream_t stream);
 
 // The rank-order float32 sum of k sources encoded in one pass (sum stored too
 // when not NULL).

@@ -303,8 +303,29 @@ gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs,
                                           void* workspace,
                                           size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of gb_bucket_allreduce_local_batch (0 on invalid
- * arguments, or for codec NONE). */
+/*
+ * gb_bucket_allreduce_local_batch_ef — the batched bucket stream with error
+ * feedback (README "Bridge compression": a residual per buffer carries each
+ * step's rounding error into the next).  Bucket b gives, bit for bit, what
+ * gb_bucket_allreduce_local_ef_typed gives for it alone, reading and
+ * rewriting the binary32 residuals residuals[b * k + r] (device
+ * float[ns[b]] each, bucket-major, 16-byte aligned, overlapping nothing
+ * else).  Up to 8 buckets per launch.  GB_ERR_UNSUPPORTED for codec NONE;
+ * everything else as gb_bucket_allreduce_local_batch, whose workspace size
+ * applies.
+ */
+gb_status gb_bucket_allreduce_local_batch_ef(int dtype, void* const* outs,
+                                             const void* const* srcs,
+                                             float* const* residuals,
+                                             const size_t* ns, int nbuckets,
+                                             int k, int codec, int scale_mode,
+                                             void* workspace,
+                                             size_t workspace_bytes,
+                                             void* stream);
+
+/* Workspace bytes of gb_bucket_allreduce_local_batch and
+ * gb_bucket_allreduce_local_batch_ef (0 on invalid arguments, or for codec
+ * NONE). */
 size_t gb_bucket_batch_workspace_bytes(int codec, int k, const size_t* ns,
                                        int nbuckets);
 

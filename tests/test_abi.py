@@ -319,6 +319,24 @@ def test_validation_of_the_typed_batched_bucket_call(gb, call, status, msg):
     assert msg in gb.gb_last_error()
 
 
+@pytest.mark.parametrize("call,status,msg", [
+    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256), _arr(256), None, _sizes(10), 1, 1, 2, 0,
+                                                    *_BIG_WS, None), 1, "residuals is NULL"),
+    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256), _arr(256), _arr(512), _sizes(10), 1, 1, 0, 0,
+                                                    *_BIG_WS, None), 3, "lossy codec"),
+    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256, 768), _arr(256, 1024), _arr(512, 1288),
+                                                    _sizes(10, 10), 2, 1, 2, 0, *_BIG_WS, None), 2,
+     "residuals[1 * k + r][0]"),
+    (lambda L: L.gb_bucket_allreduce_local_batch_ef(2, _arr(256), _arr(*[256] * 9), _arr(*[512] * 9), _sizes(10), 1,
+                                                    9, 1, 0, *_BIG_WS, None), 1, "rounded once"),
+    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256), _arr(256), _arr(512), _sizes(1000), 1, 1, 2, 0,
+                                                    ctypes.c_void_p(1 << 20), 100, None), 4, "needed"),
+])
+def test_validation_of_the_batched_error_feedback_call(gb, call, status, msg):
+    assert call(gb._lib) == status
+    assert msg in gb.gb_last_error()
+
+
 def test_batched_bucket_call_skips_empty_buckets_and_sizes_its_workspace(gb):
     L = gb._lib
     # every bucket empty: nothing to do, no pointer read

@@ -215,3 +215,71 @@ def test_typed_gradients_match_the_oracle(gb, dt, codec, mode, k):
                 assert (wsh[c0:c0 + n] == wc[r]).all(), what + f" codes {r}"
                 s0 = lay["scales_offset"] + r * lay["scales_stride"] + 4 * (offs[b] // 256)
                 assert (wsh[s0:s0 + 4 * wsc[r].size].view(np.uint32) == bits(wsc[r])).all(), what + f" scales {r}"
+
+
+def dev_typed(x, dt):
+    return torch.from_numpy(x.copy()).to(DEV) if dt == "f32" else typed_to_dev(x, dt)
+
+
+def host_typed(t, dt):
+    return t.cpu().numpy().view(np.uint32) if dt == "f32" else typed_to_host(t)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f64"])
+@pytest.mark.parametrize("codec,mode", CODECS)
+@pytest.mark.parametrize("k", [1, 4, 8])
+def test_error_feedback_matches_the_oracle_over_steps(gb, dt, codec, mode, k):
+    """gb_bucket_allreduce_local_batch_ef over three steps, residuals carried:
+    each bucket's total, payloads and residuals equal the oracle's typed
+    error-feedback stream of that bucket alone.  11 non-empty buckets: two
+    launches of at most 8."""
+    sizes = [300, 0, 4096 * 3 + 17, 256, 1, 20_000, 513] + [700] * 5
+    res = [[(np.random.default_rng(3800 + 50 * b + r).standard_normal(n) * 1e-4).astype(np.float32)
+            for r in range(k)] for b, n in enumerate(sizes)]
+    dres = [[torch.from_numpy(a.copy()).to(DEV) for a in rb] for rb in res]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, sizes)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    offs, total = offsets(sizes)
+    lay = gb.gb_bucket_workspace_layout(codec, k, total, 256)
+    for step in range(3):
+        hb = [[W.typed(n, dt, 3900 + 100 * step + 10 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+        db = [[dev_typed(x, dt) for x in xs] for xs in hb]
+        outs = [torch.empty(n, dtype=db[b][0].dtype, device=DEV) for b, n in enumerate(sizes)]
+        gb.gb_bucket_allreduce_local_batch_ef(outs, db, dres, codec, mode, ws)
+        torch.cuda.synchronize()
+        wsh = ws.cpu().numpy()
+        for b, n in enumerate(sizes):
+            if n == 0:
+                continue
+            want, wc, wsc, res[b] = O.bucket_allreduce_ef_typed(hb[b], res[b], dt, (n + 255) // 256 * 256, codec, mode)
+            what = f"dt={dt} k={k} codec={codec} mode={mode} step={step} bucket {b} (n={n})"
+            assert host_typed(outs[b], dt).tobytes() == np.ascontiguousarray(want).tobytes(), what
+            for r in range(k):
+                assert (dres[b][r].cpu().numpy().view(np.uint32) == bits(res[b][r])).all(), what + f" residual {r}"
+                if codec == O.CODEC_BF16:
+                    c0 = r * lay["codes_stride"] + 2 * offs[b]
+                    assert (wsh[c0:c0 + 2 * n].view(np.uint16) == wc[r]).all(), what + f" codes {r}"
+                else:
+                    c0 = r * lay["codes_stride"] + offs[b]
+                    assert (wsh[c0:c0 + n] == wc[r]).all(), what + f" codes {r}"
+                    s0 = lay["scales_offset"] + r * lay["scales_stride"] + 4 * (offs[b] // 256)
+                    assert (wsh[s0:s0 + 4 * wsc[r].size].view(np.uint32) == bits(wsc[r])).all(), what + f" scales {r}"
+
+
+def test_error_feedback_with_more_ranks_than_one_launch_reads(gb):
+    """11 ranks of float32 gradients: one bucket at a time, as the
+    single-buffer error-feedback call, against the oracle."""
+    sizes, k = [1000, 4096 + 3, 256], 11
+    res = [[np.full(n, 2e-5, np.float32) for _ in range(k)] for n in sizes]
+    dres = [[torch.from_numpy(a.copy()).to(DEV) for a in rb] for rb in res]
+    hb = [[W.gradients(n, 4000 + 20 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+    db = [[torch.from_numpy(x.copy()).to(DEV) for x in xs] for xs in hb]
+    outs = [torch.empty(n, device=DEV) for n in sizes]
+    ws = torch.empty(gb.gb_bucket_batch_workspace_bytes(O.CODEC_FP8, k, sizes), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch_ef(outs, db, dres, O.CODEC_FP8, 0, ws)
+    torch.cuda.synchronize()
+    for b, n in enumerate(sizes):
+        want, _, _, wres = O.bucket_allreduce_ef(hb[b], res[b], (n + 255) // 256 * 256, O.CODEC_FP8, 0)
+        assert (bits(outs[b].cpu().numpy()) == bits(want)).all(), f"bucket {b}"
+        for r in range(k):
+            assert (dres[b][r].cpu().numpy().view(np.uint32) == bits(wres[r])).all(), f"bucket {b} residual {r}"
