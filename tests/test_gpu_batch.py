@@ -283,3 +283,26 @@ def test_error_feedback_with_more_ranks_than_one_launch_reads(gb):
         assert (bits(outs[b].cpu().numpy()) == bits(want)).all(), f"bucket {b}"
         for r in range(k):
             assert (dres[b][r].cpu().numpy().view(np.uint32) == bits(wres[r])).all(), f"bucket {b} residual {r}"
+
+
+def test_the_largest_batch(gb):
+    """GB_MAX_BATCH buckets of 0..700 values (256 launches of 16), two ranks,
+    fp8 with power-of-two scales: every bucket equals gb_bucket_allreduce_local
+    on that bucket alone."""
+    rng = np.random.default_rng(4100)
+    sizes = [int(v) for v in rng.integers(0, 701, gb.GB_MAX_BATCH)]
+    k = 2
+    big = [W.device_gradients(sum(sizes), 4101 + r, DEV) for r in range(k)]
+    starts = np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
+    # each bucket in its own 16-byte-aligned buffer
+    x = [[big[r][s:s + n].clone() for r in range(k)] for s, n in zip(starts, sizes)]
+    outs = [torch.empty(n, device=DEV) for n in sizes]
+    ws = torch.empty(gb.gb_bucket_batch_workspace_bytes(O.CODEC_FP8, k, sizes), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch(outs, x, O.CODEC_FP8, O.SCALE_POW2, ws)
+    w1 = torch.empty(gb.gb_bucket_workspace_bytes(O.CODEC_FP8, k, 768, 768), dtype=torch.uint8, device=DEV)
+    ref = [torch.empty(n, device=DEV) for n in sizes]
+    for r_out, n, xs in zip(ref, sizes, x):
+        if n:
+            gb.gb_bucket_allreduce_local(r_out, xs, 768, O.CODEC_FP8, O.SCALE_POW2, w1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs).view(torch.int32), torch.cat(ref).view(torch.int32))
