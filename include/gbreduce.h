@@ -17,7 +17,8 @@
  *
  * and, around them: AVG, MAX and MIN; the README's other element types,
  * reduced exactly or through the codecs; an error-feedback residual per
- * buffer; and the staged (pipelined) steps through pinned host memory.
+ * buffer; the bucket stream over buckets held in separate buffers, several
+ * per launch; and the staged (pipelined) steps through pinned host memory.
  *
  * Conventions shared by every call
  * --------------------------------
