@@ -1,8 +1,9 @@
 """Randomised parity: many drawn configurations of every bucket-stream and
-reduction call (rank count 1..16, odd sizes and bucket lengths, each codec and
-scale mode, every element type, in place or not, with or without error
-feedback over every floating type), each checked bit for bit against the oracle.  The draws are seeded,
-so a failure names a reproducible case."""
+reduction call, the batched bucket calls among them (rank count 1..16, odd
+sizes and bucket lengths, each codec and scale mode, every element type, in
+place or not, with or without error feedback over every floating type), each
+checked bit for bit against the oracle.  The draws are seeded, so a failure
+names a reproducible case."""
 import numpy as np
 import pytest
 
@@ -115,6 +116,46 @@ def test_bucket_stream(gb, seed):
         torch.cuda.synchronize()
         want, _, _ = O.bucket_allreduce_typed(xs, dt, bucket, codec, mode)
     same(to_host(out), want, dt, what)
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_batched_bucket_stream(gb, seed):
+    """gb_bucket_allreduce_local_batch (and _batch_ef): a drawn list of 1..40
+    buckets of 0..5000 values, each checked against the oracle's bucket
+    stream of that bucket alone."""
+    rng = np.random.default_rng(9000 + seed)
+    nb = int(rng.integers(1, 41))
+    sizes = [int(v) for v in rng.integers(0, 5001, nb)]
+    codec = int(rng.integers(0, 3))
+    mode = int(rng.integers(0, 2))
+    dt = str(rng.choice(["f32", "f32", "f16", "bf16", "f64"]))
+    k = int(rng.integers(1, 17)) if dt == "f32" or codec == 0 else int(rng.integers(1, 9))
+    ef = codec != 0 and rng.random() < 0.4
+    what = f"seed={seed} nb={nb} k={k} codec={codec} mode={mode} dt={dt} ef={ef}"
+    empty = np.empty(0, {"f32": np.float32, "f64": np.float64}.get(dt, np.uint16))
+    xs = [[draw_values(rng, dt, n) if n else empty for _ in range(k)] for n in sizes]
+    d = [[to_dev(x, dt) for x in xb] for xb in xs]
+    outs = [torch.empty(n, dtype=TORCH[dt], device=DEV) for n in sizes]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, sizes)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV) if codec else None
+    if ef:
+        res0 = [[(rng.standard_normal(n) * 1e-4).astype(np.float32) for _ in range(k)] for n in sizes]
+        res = [[to_dev(r, "f32") for r in rb] for rb in res0]
+        gb.gb_bucket_allreduce_local_batch_ef(outs, d, res, codec, mode, ws)
+    else:
+        gb.gb_bucket_allreduce_local_batch(outs, d, codec, mode, ws)
+    torch.cuda.synchronize()
+    for b, n in enumerate(sizes):
+        if n == 0:
+            continue
+        bucket = (n + 255) // 256 * 256
+        if ef:
+            want, _, _, res1 = O.bucket_allreduce_ef_typed(xs[b], res0[b], dt, bucket, codec, mode)
+            for r in range(k):
+                same(res[b][r].cpu().numpy(), res1[r], "f32", what + f" bucket {b} residual {r}")
+        else:
+            want, _, _ = O.bucket_allreduce_typed(xs[b], dt, bucket, codec, mode)
+        same(to_host(outs[b]), want, dt, what + f" bucket {b}")
 
 
 @pytest.mark.parametrize("seed", range(400))
