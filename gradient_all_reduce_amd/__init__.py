@@ -69,8 +69,8 @@ _SIGNATURES = {
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
-    "gb_bucket_allreduce_local_batch": (_I, [_I, _PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
-    "gb_bucket_allreduce_local_batch_ef": (_I, [_I, _PP, _PP, _PP, _SP, _I, _I, _I, _I, _P, _S, _P]),
+    "gb_bucket_allreduce_local_batch": (_I, [_I, _PP, _PP, _SP, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "gb_bucket_allreduce_local_batch_ef": (_I, [_I, _PP, _PP, _PP, _SP, _I, _I, _I, _I, _I, _P, _S, _P]),
     "gb_bucket_batch_workspace_bytes": (_S, [_I, _I, _SP, _I]),
     "gb_encode_bf16_ef": (_I, [_P, _P, _P, _S, _P]),
     "gb_encode_fp8_e4m3_blockscaled_ef": (_I, [_P, _P, _P, _P, _S, _I, _P]),
@@ -294,20 +294,22 @@ def _workspace_args(workspace):
 
 
 def gb_bucket_allreduce_local_batch(outs, srcs, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
-                                    workspace=None, stream=None):
+                                    workspace=None, stream=None, divisor=1):
     """The bucket stream over separately allocated buckets: outs[b] receives
     bucket b's result from the k tensors srcs[b] (all float32, float16,
     bfloat16 or float64, of one type), as gb_bucket_allreduce_local_typed on
-    that bucket alone; up to 16 buckets per launch."""
+    that bucket alone; up to 16 buckets per launch.  divisor > 1 gives the
+    AVG over that world size instead of the SUM."""
     k, dtype, ns, flat, _ = _batch_args(outs, srcs, None)
     device = outs[0].device if outs else torch.device("cuda", torch.cuda.current_device())
     _check(_lib.gb_bucket_allreduce_local_batch(GB_DTYPE[dtype], _ptr_array(outs), _ptr_array(flat),
                                                 _size_array(ns), len(outs), k, int(codec), int(scale_mode),
-                                                *_workspace_args(workspace), _stream(stream, device)))
+                                                int(divisor), *_workspace_args(workspace),
+                                                _stream(stream, device)))
 
 
 def gb_bucket_allreduce_local_batch_ef(outs, srcs, residuals, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
-                                       workspace=None, stream=None):
+                                       workspace=None, stream=None, divisor=1):
     """gb_bucket_allreduce_local_batch with error feedback: residuals[b][r]
     (float32, one per source) is read and rewritten, as
     gb_bucket_allreduce_local_ef_typed on each bucket alone; up to 8 buckets
@@ -316,8 +318,8 @@ def gb_bucket_allreduce_local_batch_ef(outs, srcs, residuals, codec, scale_mode=
     device = outs[0].device if outs else torch.device("cuda", torch.cuda.current_device())
     _check(_lib.gb_bucket_allreduce_local_batch_ef(GB_DTYPE[dtype], _ptr_array(outs), _ptr_array(flat),
                                                    _ptr_array(flat_res), _size_array(ns), len(outs), k,
-                                                   int(codec), int(scale_mode), *_workspace_args(workspace),
-                                                   _stream(stream, device)))
+                                                   int(codec), int(scale_mode), int(divisor),
+                                                   *_workspace_args(workspace), _stream(stream, device)))
 
 
 _CODEC_TYPES = (torch.float32, torch.float16, torch.bfloat16, torch.float64)

@@ -761,7 +761,7 @@ namespace {
 // (a host array of nbuckets * k residual pointers, bucket-major).
 gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void* const* srcs,
                        float* const* residuals, const size_t* ns, int nbuckets, int k, int codec, int scale_mode,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       int divisor, void* workspace, size_t workspace_bytes, void* stream) {
   const bool ef = residuals != nullptr;
   if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
   if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
@@ -770,6 +770,9 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
   }
   if (codec == GB_CODEC_FP8_E4M3_B256 && !known_mode(scale_mode)) {
     return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+  }
+  if (divisor < 1 || divisor > (1 << 24)) {
+    return fail(GB_ERR_INVALID_ARG, "%s: divisor %d is outside 1..2^24", fn, divisor);
   }
   gb_status s = check_k(k, fn);
   if (s != GB_OK) return s;
@@ -809,18 +812,34 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
   char* ws = static_cast<char*>(workspace);
   const size_t csz = code_size(codec);
   hipError_t e = hipSuccess;
+  // AVG of a compressed total: the decode-and-add, then the division, fused
+  // for float32 totals; other types divide their total in a second pass
+  auto divide = [&](void* out, size_t n) {
+    const void* one[1] = {out};
+    return op_groups(out, one, 1, n, dtype, GB_OP_AVG, divisor, st);
+  };
   size_t o = 0;  // the bucket's first value in the workspace's virtual buffer
-  if (codec == GB_CODEC_NONE || k > kR) {
-    // one bucket at a time, exactly as the single-buffer calls
+  if (codec == GB_CODEC_NONE) {
+    // the exact SUM (or AVG) of the type, one bucket at a time
+    for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
+      if (ns[b] == 0) continue;
+      e = op_groups(outs[b], srcs + (size_t)b * k, k, ns[b], dtype, divisor == 1 ? GB_OP_SUM : GB_OP_AVG, divisor,
+                    st);
+    }
+    return from_hip(e, fn);
+  }
+  if (k > kR) {
+    // one bucket at a time, exactly as the single-buffer calls (float32 only)
     for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
       if (ns[b] == 0) continue;
       e = bucket_groups(outs[b], srcs + (size_t)b * k, ef ? residuals + (size_t)b * k : nullptr, k, ns[b], codec,
-                        scale_mode, dtype, ws == nullptr ? nullptr : ws + o * csz, cs,
-                        ws == nullptr ? nullptr : ws + so + 4 * (o / GB_BLOCK), ss, st);
+                        scale_mode, dtype, ws + o * csz, cs, ws + so + 4 * (o / GB_BLOCK), ss, st);
+      if (e == hipSuccess && divisor != 1) e = divide(outs[b], ns[b]);
       o += round_up(ns[b], GB_BLOCK);
     }
     return from_hip(e, fn);
   }
+  const int fused_divisor = dtype == GB_DTYPE_F32 ? divisor : 1;
   // several buckets per launch, as many as the table and one grid hold
   gb::BucketBatch t = {};
   gb::BucketBatchEf te = {};
@@ -831,13 +850,13 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
     if (count == 0 || e != hipSuccess) return;
     if (ef) {
       te.count = count;
-      e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_ef_batch(te, k, dtype, st)
-                                 : gb::launch_fused_fp8_ef_batch(te, k, scale_mode, dtype, st);
+      e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_ef_batch(te, k, dtype, fused_divisor, st)
+                                 : gb::launch_fused_fp8_ef_batch(te, k, scale_mode, dtype, fused_divisor, st);
       te = gb::BucketBatchEf{};
     } else {
       t.count = count;
-      e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, dtype, st)
-                                 : gb::launch_fused_fp8_batch(t, k, scale_mode, dtype, st);
+      e = codec == GB_CODEC_BF16 ? gb::launch_fused_bf16_batch(t, k, dtype, fused_divisor, st)
+                                 : gb::launch_fused_fp8_batch(t, k, scale_mode, dtype, fused_divisor, st);
       t = gb::BucketBatch{};
     }
     count = 0;
@@ -874,6 +893,11 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
     o += round_up(ns[b], GB_BLOCK);
   }
   flush();
+  if (fused_divisor != divisor) {
+    for (int b = 0; b < nbuckets && e == hipSuccess; b++) {
+      if (ns[b] != 0) e = divide(outs[b], ns[b]);
+    }
+  }
   return from_hip(e, fn);
 }
 
@@ -882,19 +906,19 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
 extern "C" {
 
 gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const void* const* srcs, const size_t* ns,
-                                          int nbuckets, int k, int codec, int scale_mode, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
+                                          int nbuckets, int k, int codec, int scale_mode, int divisor,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
   return bucket_batch("gb_bucket_allreduce_local_batch", dtype, outs, srcs, nullptr, ns, nbuckets, k, codec,
-                      scale_mode, workspace, workspace_bytes, stream);
+                      scale_mode, divisor, workspace, workspace_bytes, stream);
 }
 
 gb_status gb_bucket_allreduce_local_batch_ef(int dtype, void* const* outs, const void* const* srcs,
                                              float* const* residuals, const size_t* ns, int nbuckets, int k,
-                                             int codec, int scale_mode, void* workspace, size_t workspace_bytes,
-                                             void* stream) {
+                                             int codec, int scale_mode, int divisor, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
   const char* fn = "gb_bucket_allreduce_local_batch_ef";
   if (residuals == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: residuals is NULL", fn);
-  return bucket_batch(fn, dtype, outs, srcs, residuals, ns, nbuckets, k, codec, scale_mode, workspace,
+  return bucket_batch(fn, dtype, outs, srcs, residuals, ns, nbuckets, k, codec, scale_mode, divisor, workspace,
                       workspace_bytes, stream);
 }
 

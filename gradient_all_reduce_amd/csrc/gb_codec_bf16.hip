@@ -87,9 +87,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTab
 // ===========================================================================
 // Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
-template <int K, int ET, bool FULL>
+template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n,
-                                                size_t sg) {
+                                                size_t sg, float d = 1.0f, float inv = 0.0f) {
   const uint32_t t = threadIdx.x;
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 x[K];
@@ -103,7 +103,9 @@ __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, 
     const f4 v = bf16_unpack4(w);
     a = r == 0 ? v : a + v;
   }
-  store_group_vec<ET, FULL>(out, sg, t, n, a);
+  f4 q[1] = {a};
+  avg_total<DIV>(q, d, inv);
+  store_group_vec<ET, FULL>(out, sg, t, n, q[0]);
 }
 
 template <int K, int ET>
@@ -116,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTabl
 // Several buckets in one launch (gradients of element type ET), as the fp8
 // batch: each workgroup finds its bucket, then takes that bucket's vector
 // group.
-template <int K, int ET>
-__global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch t) {
+template <int K, int ET, int DIV>
+__global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch t, float d, float inv) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
   for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
@@ -129,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch 
     codes.p[r] = t.codes[b][r];
   }
   const size_t sg = w - t.first[b], n = t.n[b];
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true>(t.out[b], src, codes, n, sg);
-  else fused_bf16_body<K, ET, false>(t.out[b], src, codes, n, sg);
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true, DIV>(t.out[b], src, codes, n, sg, d, inv);
+  else fused_bf16_body<K, ET, false, DIV>(t.out[b], src, codes, n, sg, d, inv);
 }
 
 // Launcher bodies, one per element type ET.
@@ -200,16 +202,16 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 }
 
 namespace {
-template <int ET>
-hipError_t fused_bf16_batch_t(BucketBatch& t, size_t grid, int k, hipStream_t stream) {
-#define GB_CALL(K) fused_bf16_batch_kernel<K, ET><<<grid, kThreads, 0, stream>>>(t);
+template <int ET, int DIV>
+hipError_t fused_bf16_batch_t(BucketBatch& t, size_t grid, int k, float d, float inv, hipStream_t stream) {
+#define GB_CALL(K) fused_bf16_batch_kernel<K, ET, DIV><<<grid, kThreads, 0, stream>>>(t, d, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, int dtype, hipStream_t stream) {
+hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, int dtype, int divisor, hipStream_t stream) {
   if (t.count == 0 || t.count > (uint32_t)kBatchBuckets) return hipErrorInvalidValue;
   size_t grid = 0;
   for (uint32_t b = 0; b < t.count; b++) {
@@ -218,7 +220,14 @@ hipError_t launch_fused_bf16_batch(BucketBatch& t, int k, int dtype, hipStream_t
   }
   for (int b = (int)t.count; b <= kBatchBuckets; b++) t.first[b] = grid;
   if (grid == 0 || grid > kMaxGrid) return hipErrorInvalidValue;
-#define GB_CALL(ET) fused_bf16_batch_t<ET>(t, grid, k, stream)
+  if (divisor != 1) {  // float32 totals only
+    if (dtype != GB_DTYPE_F32) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    const float d = (float)divisor, inv = (divisor & (divisor - 1)) == 0 ? 1.0f / d : 0.0f;
+    return inv != 0.0f ? fused_bf16_batch_t<GB_DTYPE_F32, 1>(t, grid, k, d, inv, stream)
+                       : fused_bf16_batch_t<GB_DTYPE_F32, 2>(t, grid, k, d, inv, stream);
+  }
+#define GB_CALL(ET) fused_bf16_batch_t<ET, 0>(t, grid, k, 1.0f, 0.0f, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
 }

@@ -116,9 +116,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTabl
 // Fused fp8 bucket pass: read each rank's block once, write its payload
 // (codes, scale), decode those codes and add them in rank order.
 // ===========================================================================
-template <int K, int ET, bool FULL>
+template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, const OutTable& codes,
-                                               const OutTable& scales, size_t n, int mode, size_t g) {
+                                               const OutTable& scales, size_t n, int mode, size_t g,
+                                               float d = 1.0f, float inv = 0.0f) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = g * kBlocksPerGroup + (threadIdx.x >> 4);
   constexpr int MAP = codec_map<ET>();
@@ -143,6 +144,7 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
     }
   }
   if (!live) return;
+  avg_total<DIV>(a, d, inv);
   store_block<ET, MAP, FULL>(out, block, col, n, a);
 }
 
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable
 // Several buckets in one launch (gradients of element type ET): each
 // workgroup finds its bucket from the table of first workgroups, then runs
 // the fused pass over that bucket's group, in index order.
-template <int K, int ET>
-__global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t, int mode) {
+template <int K, int ET, int DIV>
+__global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t, int mode, float d, float inv) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
   for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
@@ -171,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t
     scales.p[r] = t.scales[b][r];
   }
   const size_t g = w - t.first[b], n = t.n[b];
-  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, ET, true>(t.out[b], src, codes, scales, n, mode, g);
-  else fused_fp8_body<K, ET, false>(t.out[b], src, codes, scales, n, mode, g);
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, ET, true, DIV>(t.out[b], src, codes, scales, n, mode, g, d, inv);
+  else fused_fp8_body<K, ET, false, DIV>(t.out[b], src, codes, scales, n, mode, g, d, inv);
 }
 
 // Launcher bodies, one per element type ET.  Accumulation into the output
@@ -250,16 +252,19 @@ size_t batch_groups(int codec, size_t n) {
 namespace {
 // Batched launches are bucket-sized pieces: they take the fused pass's cap
 // for launches below every size threshold.
-template <int ET>
-hipError_t fused_fp8_batch_t(BucketBatch& t, size_t grid, int k, int scale_mode, hipStream_t stream) {
-#define GB_CALL(K) fused_fp8_batch_kernel<K, ET><<<grid, kThreads, fused_fp8_lds<ET>(K, 0), stream>>>(t, scale_mode);
+template <int ET, int DIV>
+hipError_t fused_fp8_batch_t(BucketBatch& t, size_t grid, int k, int scale_mode, float d, float inv,
+                             hipStream_t stream) {
+#define GB_CALL(K) \
+  fused_fp8_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_lds<ET>(K, 0), stream>>>(t, scale_mode, d, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, int dtype, hipStream_t stream) {
+hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, int dtype, int divisor,
+                                  hipStream_t stream) {
   if (t.count == 0 || t.count > (uint32_t)kBatchBuckets) return hipErrorInvalidValue;
   size_t grid = 0;
   for (uint32_t b = 0; b < t.count; b++) {
@@ -268,7 +273,14 @@ hipError_t launch_fused_fp8_batch(BucketBatch& t, int k, int scale_mode, int dty
   }
   for (int b = (int)t.count; b <= kBatchBuckets; b++) t.first[b] = grid;
   if (grid == 0 || grid > kMaxGrid) return hipErrorInvalidValue;
-#define GB_CALL(ET) fused_fp8_batch_t<ET>(t, grid, k, scale_mode, stream)
+  if (divisor != 1) {  // float32 totals only
+    if (dtype != GB_DTYPE_F32) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    const float d = (float)divisor, inv = (divisor & (divisor - 1)) == 0 ? 1.0f / d : 0.0f;
+    return inv != 0.0f ? fused_fp8_batch_t<GB_DTYPE_F32, 1>(t, grid, k, scale_mode, d, inv, stream)
+                       : fused_fp8_batch_t<GB_DTYPE_F32, 2>(t, grid, k, scale_mode, d, inv, stream);
+  }
+#define GB_CALL(ET) fused_fp8_batch_t<ET, 0>(t, grid, k, scale_mode, 1.0f, 0.0f, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
 }

@@ -721,6 +721,21 @@ __device__ __forceinline__ void store_group_f32(float* p, size_t sg, uint32_t t,
 // Launch helpers.
 // ---------------------------------------------------------------------------
 
+// AVG of a float32 total fused into a bucket pass (README "API": AVG is the
+// SUM divided by the world size; a compressed AVG is the decode-and-add,
+// then the division): DIV 0 leaves the total, 1 multiplies it by the exact
+// reciprocal of a power-of-two divisor (the quotient rounded once, as a
+// divide), 2 divides it (IEEE binary32 division, correctly rounded).
+template <int DIV, int NV>
+__device__ __forceinline__ void avg_total(f4 (&a)[NV], float d, float inv) {
+  if (DIV == 0) return;
+#pragma unroll
+  for (int j = 0; j < NV; j++) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) a[j][e] = DIV == 1 ? a[j][e] * inv : a[j][e] / d;
+  }
+}
+
 // Dynamic LDS reserved per workgroup: an occupancy cap.  No kernel uses LDS;
 // reserving 48, 64 or 81 KiB of the 160 KiB a compute unit has caps it at 3,
 // 2 or 1 such workgroups.  A kernel that keeps many bytes of loads in flight

@@ -60,10 +60,10 @@ __global__ __launch_bounds__(kThreads) void encode_fp8_ef_kernel(uint8_t* codes,
   else encode_fp8_ef_body<ET, false>(codes, scales, res, src, n, mode);
 }
 
-template <int K, int ET, bool FULL>
+template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src, const OutTable& resid,
                                                   const OutTable& codes, const OutTable& scales, size_t n,
-                                                  int mode, size_t g) {
+                                                  int mode, size_t g, float dv = 1.0f, float inv = 0.0f) {
   const uint32_t col = threadIdx.x & 15u;
   const size_t block = g * kBlocksPerGroup + (threadIdx.x >> 4);
   constexpr int MAP = ef_map<ET>();
@@ -98,6 +98,7 @@ __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src
     }
   }
   if (!live) return;
+  avg_total<DIV>(a, dv, inv);
   store_block<ET, MAP, FULL>(out, block, col, n, a);
 }
 
@@ -110,9 +111,10 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_ef_kernel(void* out, PtrTa
   else fused_fp8_ef_body<K, ET, false>(out, src, resid, codes, scales, n, mode, g);
 }
 
-template <int K, int ET, bool FULL>
+template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& src, const OutTable& resid,
-                                                   const OutTable& codes, size_t n, size_t sg) {
+                                                   const OutTable& codes, size_t n, size_t sg, float dv = 1.0f,
+                                                   float inv = 0.0f) {
   const uint32_t t = threadIdx.x;
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 y[K];
@@ -130,7 +132,9 @@ __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& sr
     store_group_f32<ET, FULL>(static_cast<float*>(resid.p[r]), sg, t, n, y[r] - v);
     a = r == 0 ? v : a + v;
   }
-  store_group_vec<ET, FULL>(out, sg, t, n, a);
+  f4 q[1] = {a};
+  avg_total<DIV>(q, dv, inv);
+  store_group_vec<ET, FULL>(out, sg, t, n, q[0]);
 }
 
 template <int K, int ET>
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrT
 // Several buckets in one launch, with their residuals: each workgroup finds
 // its bucket from the table of first workgroups and takes that bucket's
 // group, in index order.
-template <int K, int ET>
-__global__ __launch_bounds__(kThreads) void fused_fp8_ef_batch_kernel(BucketBatchEf t, int mode) {
+template <int K, int ET, int DIV>
+__global__ __launch_bounds__(kThreads) void fused_fp8_ef_batch_kernel(BucketBatchEf t, int mode, float dv, float inv) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
   for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
@@ -159,12 +163,13 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_ef_batch_kernel(BucketBatc
     scales.p[r] = t.scales[b][r];
   }
   const size_t g = w - t.first[b], n = t.n[b];
-  if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_ef_body<K, ET, true>(t.out[b], src, resid, codes, scales, n, mode, g);
-  else fused_fp8_ef_body<K, ET, false>(t.out[b], src, resid, codes, scales, n, mode, g);
+  if ((g + 1) * kBlocksPerGroup * kBlock <= n)
+    fused_fp8_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, scales, n, mode, g, dv, inv);
+  else fused_fp8_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, scales, n, mode, g, dv, inv);
 }
 
-template <int K, int ET>
-__global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBatchEf t) {
+template <int K, int ET, int DIV>
+__global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBatchEf t, float dv, float inv) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
   for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
@@ -177,8 +182,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBat
     codes.p[r] = t.codes[b][r];
   }
   const size_t sg = w - t.first[b], n = t.n[b];
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(t.out[b], src, resid, codes, n, sg);
-  else fused_bf16_ef_body<K, ET, false>(t.out[b], src, resid, codes, n, sg);
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
+  else fused_bf16_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
 }
 
 // The table's first workgroups and the grid; 0 if the table is empty or too large.
@@ -195,21 +200,23 @@ size_t batch_grid(BucketBatchEf& t, int codec) {
 
 // Batched launches are bucket-sized pieces: they take each pass's cap for
 // launches below every size threshold.
-template <int ET>
-hipError_t fused_fp8_ef_batch_t(BucketBatchEf& t, int k, int scale_mode, hipStream_t stream) {
+template <int ET, int DIV>
+hipError_t fused_fp8_ef_batch_t(BucketBatchEf& t, int k, int scale_mode, float dv, float inv, hipStream_t stream) {
   const size_t grid = batch_grid(t, GB_CODEC_FP8_E4M3_B256);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_fp8_ef_batch_kernel<K, ET><<<grid, kThreads, fused_fp8_ef_lds(K, 0), stream>>>(t, scale_mode);
+#define GB_CALL(K) \
+  fused_fp8_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_ef_lds(K, 0), stream>>>(t, scale_mode, dv, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
 }
 
-template <int ET>
-hipError_t fused_bf16_ef_batch_t(BucketBatchEf& t, int k, hipStream_t stream) {
+template <int ET, int DIV>
+hipError_t fused_bf16_ef_batch_t(BucketBatchEf& t, int k, float dv, float inv, hipStream_t stream) {
   const size_t grid = batch_grid(t, GB_CODEC_BF16);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_bf16_ef_batch_kernel<K, ET><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(t);
+#define GB_CALL(K) \
+  fused_bf16_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(t, dv, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
@@ -282,14 +289,29 @@ hipError_t launch_fused_bf16_ef(void* out, const PtrTable& srcs, float* const* r
 #undef GB_CALL
 }
 
-hipError_t launch_fused_fp8_ef_batch(BucketBatchEf& t, int k, int scale_mode, int dtype, hipStream_t stream) {
-#define GB_CALL(ET) fused_fp8_ef_batch_t<ET>(t, k, scale_mode, stream)
+hipError_t launch_fused_fp8_ef_batch(BucketBatchEf& t, int k, int scale_mode, int dtype, int divisor,
+                                     hipStream_t stream) {
+  if (divisor != 1) {  // float32 totals only
+    if (dtype != GB_DTYPE_F32) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    const float dv = (float)divisor, inv = (divisor & (divisor - 1)) == 0 ? 1.0f / dv : 0.0f;
+    return inv != 0.0f ? fused_fp8_ef_batch_t<GB_DTYPE_F32, 1>(t, k, scale_mode, dv, inv, stream)
+                       : fused_fp8_ef_batch_t<GB_DTYPE_F32, 2>(t, k, scale_mode, dv, inv, stream);
+  }
+#define GB_CALL(ET) fused_fp8_ef_batch_t<ET, 0>(t, k, scale_mode, 1.0f, 0.0f, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
 }
 
-hipError_t launch_fused_bf16_ef_batch(BucketBatchEf& t, int k, int dtype, hipStream_t stream) {
-#define GB_CALL(ET) fused_bf16_ef_batch_t<ET>(t, k, stream)
+hipError_t launch_fused_bf16_ef_batch(BucketBatchEf& t, int k, int dtype, int divisor, hipStream_t stream) {
+  if (divisor != 1) {  // float32 totals only
+    if (dtype != GB_DTYPE_F32) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    const float dv = (float)divisor, inv = (divisor & (divisor - 1)) == 0 ? 1.0f / dv : 0.0f;
+    return inv != 0.0f ? fused_bf16_ef_batch_t<GB_DTYPE_F32, 1>(t, k, dv, inv, stream)
+                       : fused_bf16_ef_batch_t<GB_DTYPE_F32, 2>(t, k, dv, inv, stream);
+  }
+#define GB_CALL(ET) fused_bf16_ef_batch_t<ET, 0>(t, k, 1.0f, 0.0f, stream)
   GB_DISPATCH_ET(dtype, GB_CALL)
 #undef GB_CALL
 }

@@ -94,10 +94,14 @@ static_assert(sizeof(BucketBatchEf) <= 4000, "a batch must fit the 4 KiB of kern
 // (GB_CODEC_BF16 or GB_CODEC_FP8_E4M3_B256).
 size_t batch_groups(int codec, size_t n);
 // Every bucket has 0 < n, and the workgroups of all buckets fit one grid.
-hipError_t launch_fused_fp8_batch(BucketBatch& batch, int k, int scale_mode, int dtype, hipStream_t stream);
-hipError_t launch_fused_bf16_batch(BucketBatch& batch, int k, int dtype, hipStream_t stream);
-hipError_t launch_fused_fp8_ef_batch(BucketBatchEf& batch, int k, int scale_mode, int dtype, hipStream_t stream);
-hipError_t launch_fused_bf16_ef_batch(BucketBatchEf& batch, int k, int dtype, hipStream_t stream);
+// divisor 1 leaves each total; any other divisor (1 .. 2^24, float32
+// totals only) stores RN(total / divisor), the AVG of the job's world size.
+hipError_t launch_fused_fp8_batch(BucketBatch& batch, int k, int scale_mode, int dtype, int divisor,
+                                  hipStream_t stream);
+hipError_t launch_fused_bf16_batch(BucketBatch& batch, int k, int dtype, int divisor, hipStream_t stream);
+hipError_t launch_fused_fp8_ef_batch(BucketBatchEf& batch, int k, int scale_mode, int dtype, int divisor,
+                                     hipStream_t stream);
+hipError_t launch_fused_bf16_ef_batch(BucketBatchEf& batch, int k, int dtype, int divisor, hipStream_t stream);
 
 // The rank-order float32 sum of k sources encoded in one pass (sum stored too
 // when not NULL).

@@ -288,6 +288,13 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
  *              of 0 values is skipped, its pointers unread).
  *   nbuckets   1 .. GB_MAX_BATCH; the sizes, each rounded up to a
  *              multiple of 256, add up to at most GB_MAX_N.
+ *   divisor    1 for SUM; the job's world size (up to 2^24) for AVG, which
+ *              the README compresses as the decode-and-add followed by the
+ *              division: a float32 total becomes RN(total / divisor) in the
+ *              same pass; a total of another type is divided as
+ *              gb_reduce_typed divides it, in a second pass over the output;
+ *              with codec NONE each bucket is the exact AVG of gb_reduce_typed.
+ *              GB_ERR_INVALID_ARG outside 1 .. 2^24.
  *   workspace  device buffer of at least gb_bucket_batch_workspace_bytes();
  *              rank r's payload of bucket b sits where the payload of values
  *              [o_b, o_b + ns[b]) of one buffer would, in the layout
@@ -301,7 +308,7 @@ gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs,
                                           const void* const* srcs,
                                           const size_t* ns, int nbuckets, int k,
                                           int codec, int scale_mode,
-                                          void* workspace,
+                                          int divisor, void* workspace,
                                           size_t workspace_bytes, void* stream);
 
 /*
@@ -320,7 +327,7 @@ gb_status gb_bucket_allreduce_local_batch_ef(int dtype, void* const* outs,
                                              float* const* residuals,
                                              const size_t* ns, int nbuckets,
                                              int k, int codec, int scale_mode,
-                                             void* workspace,
+                                             int divisor, void* workspace,
                                              size_t workspace_bytes,
                                              void* stream);
 

@@ -269,36 +269,47 @@ def _sizes(*ns):
 _BIG_WS = (ctypes.c_void_p(1 << 20), 1 << 30)
 
 
+def _batch(L, *a, divisor=1):
+    """gb_bucket_allreduce_local_batch(dtype, outs, srcs, ns, nbuckets, k, codec, scale_mode, divisor, ...)."""
+    return L.gb_bucket_allreduce_local_batch(*a[:8], divisor, *a[8:])
+
+
+def _batch_ef(L, *a, divisor=1):
+    """gb_bucket_allreduce_local_batch_ef(dtype, outs, srcs, residuals, ns, nbuckets, k, codec, scale_mode,
+    divisor, ...)."""
+    return L.gb_bucket_allreduce_local_batch_ef(*a[:9], divisor, *a[9:])
+
+
 @pytest.mark.parametrize("call,status,msg", [
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 1, 1, 5, 0, *_BIG_WS, None), 3,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 1, 1, 5, 0, *_BIG_WS, None), 3,
      "unknown codec"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 4, *_BIG_WS, None), 3,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 4, *_BIG_WS, None), 3,
      "scale mode"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 1, 0, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 1, 0, 2, 0, *_BIG_WS, None), 1,
      "k = 0"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 0, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 0, 1, 2, 0, *_BIG_WS, None), 1,
      "nbuckets = 0"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(10), 4097, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 4097, 1, 2, 0, *_BIG_WS, None), 1,
      "nbuckets = 4097"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), None, 1, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), None, 1, 1, 2, 0, *_BIG_WS, None), 1,
      "ns is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 512), _arr(256, 512), _sizes(10, (1 << 39) + 1), 2, 1,
+    (lambda L: _batch(L, 0, _arr(256, 512), _arr(256, 512), _sizes(10, (1 << 39) + 1), 2, 1,
                                                  2, 0, *_BIG_WS, None), 1, "ns[1]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 512), _arr(256, 512), _sizes(1 << 39, 1), 2, 1, 2, 0,
+    (lambda L: _batch(L, 0, _arr(256, 512), _arr(256, 512), _sizes(1 << 39, 1), 2, 1, 2, 0,
                                                  *_BIG_WS, None), 1, "exceed GB_MAX_N"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, None, _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 1,
+    (lambda L: _batch(L, 0, None, _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 1,
      "outs or srcs is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 264), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
+    (lambda L: _batch(L, 0, _arr(256, 264), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
                                                  *_BIG_WS, None), 2, "outs[1]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 0), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
+    (lambda L: _batch(L, 0, _arr(256, 0), _arr(256, 512), _sizes(10, 10), 2, 1, 2, 0,
                                                  *_BIG_WS, None), 1, "outs[1] is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256, 512), _arr(256, 512, 768, 1032), _sizes(10, 10), 2, 2,
+    (lambda L: _batch(L, 0, _arr(256, 512), _arr(256, 512, 768, 1032), _sizes(10, 10), 2, 2,
                                                  2, 0, *_BIG_WS, None), 2, "srcs[1 * k + r][1]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
                                                  ctypes.c_void_p(1 << 20), 100, None), 4, "needed"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(1000), 1, 1, 1, 0, None, 0, None), 4,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(1000), 1, 1, 1, 0, None, 0, None), 4,
      "needed"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(0, _arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(1000), 1, 1, 2, 0,
                                                  ctypes.c_void_p((1 << 20) + 16), 1 << 30, None), 2, "workspace"),
 ])
 def test_validation_of_the_batched_bucket_call(gb, call, status, msg):
@@ -307,11 +318,11 @@ def test_validation_of_the_batched_bucket_call(gb, call, status, msg):
 
 
 @pytest.mark.parametrize("call,status,msg", [
-    (lambda L: L.gb_bucket_allreduce_local_batch(4, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 3,
+    (lambda L: _batch(L, 4, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None), 3,
      "floating-point"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(2, _arr(256), _arr(*[256] * 9), _sizes(10), 1, 9, 2, 0, *_BIG_WS,
+    (lambda L: _batch(L, 2, _arr(256), _arr(*[256] * 9), _sizes(10), 1, 9, 2, 0, *_BIG_WS,
                                                  None), 1, "rounded once"),
-    (lambda L: L.gb_bucket_allreduce_local_batch(3, _arr(256), _arr(256, 264), _sizes(10), 1, 2, 1, 0, *_BIG_WS,
+    (lambda L: _batch(L, 3, _arr(256), _arr(256, 264), _sizes(10), 1, 2, 1, 0, *_BIG_WS,
                                                  None), 2, "srcs[0 * k + r][1]"),
 ])
 def test_validation_of_the_typed_batched_bucket_call(gb, call, status, msg):
@@ -320,16 +331,28 @@ def test_validation_of_the_typed_batched_bucket_call(gb, call, status, msg):
 
 
 @pytest.mark.parametrize("call,status,msg", [
-    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256), _arr(256), None, _sizes(10), 1, 1, 2, 0,
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None, divisor=0), 1, "divisor 0"),
+    (lambda L: _batch(L, 0, _arr(256), _arr(256), _sizes(10), 1, 1, 2, 0, *_BIG_WS, None, divisor=(1 << 24) + 1), 1,
+     "divisor"),
+    (lambda L: _batch_ef(L, 0, _arr(256), _arr(256), _arr(512), _sizes(10), 1, 1, 1, 0, *_BIG_WS, None,
+                         divisor=-3), 1, "divisor -3"),
+])
+def test_validation_of_the_batched_divisor(gb, call, status, msg):
+    assert call(gb._lib) == status
+    assert msg in gb.gb_last_error()
+
+
+@pytest.mark.parametrize("call,status,msg", [
+    (lambda L: _batch_ef(L, 0, _arr(256), _arr(256), None, _sizes(10), 1, 1, 2, 0,
                                                     *_BIG_WS, None), 1, "residuals is NULL"),
-    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256), _arr(256), _arr(512), _sizes(10), 1, 1, 0, 0,
+    (lambda L: _batch_ef(L, 0, _arr(256), _arr(256), _arr(512), _sizes(10), 1, 1, 0, 0,
                                                     *_BIG_WS, None), 3, "lossy codec"),
-    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256, 768), _arr(256, 1024), _arr(512, 1288),
+    (lambda L: _batch_ef(L, 0, _arr(256, 768), _arr(256, 1024), _arr(512, 1288),
                                                     _sizes(10, 10), 2, 1, 2, 0, *_BIG_WS, None), 2,
      "residuals[1 * k + r][0]"),
-    (lambda L: L.gb_bucket_allreduce_local_batch_ef(2, _arr(256), _arr(*[256] * 9), _arr(*[512] * 9), _sizes(10), 1,
+    (lambda L: _batch_ef(L, 2, _arr(256), _arr(*[256] * 9), _arr(*[512] * 9), _sizes(10), 1,
                                                     9, 1, 0, *_BIG_WS, None), 1, "rounded once"),
-    (lambda L: L.gb_bucket_allreduce_local_batch_ef(0, _arr(256), _arr(256), _arr(512), _sizes(1000), 1, 1, 2, 0,
+    (lambda L: _batch_ef(L, 0, _arr(256), _arr(256), _arr(512), _sizes(1000), 1, 1, 2, 0,
                                                     ctypes.c_void_p(1 << 20), 100, None), 4, "needed"),
 ])
 def test_validation_of_the_batched_error_feedback_call(gb, call, status, msg):
@@ -340,9 +363,9 @@ def test_validation_of_the_batched_error_feedback_call(gb, call, status, msg):
 def test_batched_bucket_call_skips_empty_buckets_and_sizes_its_workspace(gb):
     L = gb._lib
     # every bucket empty: nothing to do, no pointer read
-    assert L.gb_bucket_allreduce_local_batch(0, None, None, _sizes(0, 0, 0), 3, 4, 2, 0, None, 0, None) == 0
+    assert _batch(L, 0, None, None, _sizes(0, 0, 0), 3, 4, 2, 0, None, 0, None) == 0
     # an empty bucket's pointers are not read: only bucket 1's are checked (and misaligned here)
-    assert L.gb_bucket_allreduce_local_batch(0, _arr(0, 264), _arr(0, 256), _sizes(0, 10), 2, 1, 2, 0,
+    assert _batch(L, 0, _arr(0, 264), _arr(0, 256), _sizes(0, 10), 2, 1, 2, 0,
                                              *_BIG_WS, None) == 2
     assert "outs[1]" in gb.gb_last_error()
     # the workspace is that of one buffer of the sizes rounded up to 256 values each

@@ -306,3 +306,78 @@ def test_the_largest_batch(gb):
             gb.gb_bucket_allreduce_local(r_out, xs, 768, O.CODEC_FP8, O.SCALE_POW2, w1)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(outs).view(torch.int32), torch.cat(ref).view(torch.int32))
+
+
+def avg_of(total, dt, d):
+    """The oracle's AVG of a bucket's total: its SUM divided as the README's
+    AVG divides it (float32: O.reduce; other types: O.reduce_typed)."""
+    if dt == "f32":
+        return O.reduce([total], O.OP_AVG, d)
+    return O.reduce_typed([total], dt, O.OP_AVG, d)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16", "f64"])
+@pytest.mark.parametrize("codec,mode", CODECS + [(O.CODEC_NONE, 0)])
+@pytest.mark.parametrize("d", [2, 3, 8, (1 << 24) - 1, 1 << 24])
+def test_avg_matches_the_oracle(gb, dt, codec, mode, d):
+    """AVG over world size d: each bucket's compressed SUM from the oracle,
+    divided by the oracle's AVG (fused into the pass for float32 totals); with
+    codec NONE the oracle's exact AVG of the type."""
+    k = 4
+    sizes = [1000, 0, 4096 * 3 + 17, 256, 1, 20_000] + [513] * 12  # 17 non-empty: two launches
+    hb = [[W.typed(n, dt, 4200 + 50 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+    db = [[dev_typed(x, dt) for x in xs] for xs in hb]
+    outs = [torch.empty(n, dtype=db[b][0].dtype, device=DEV) for b, n in enumerate(sizes)]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, sizes)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV) if need else None
+    gb.gb_bucket_allreduce_local_batch(outs, db, codec, mode, ws, divisor=d)
+    torch.cuda.synchronize()
+    for b, n in enumerate(sizes):
+        if n == 0:
+            continue
+        if codec == O.CODEC_NONE:
+            want = O.reduce(hb[b], O.OP_AVG, d) if dt == "f32" else O.reduce_typed(hb[b], dt, O.OP_AVG, d)
+        else:
+            want = avg_of(O.bucket_allreduce_typed(hb[b], dt, (n + 255) // 256 * 256, codec, mode)[0], dt, d)
+        what = f"dt={dt} codec={codec} mode={mode} d={d} bucket {b} (n={n})"
+        assert host_typed(outs[b], dt).tobytes() == np.ascontiguousarray(want).tobytes(), what
+
+
+@pytest.mark.parametrize("dt,codec", [("f32", O.CODEC_FP8), ("f32", O.CODEC_BF16), ("bf16", O.CODEC_FP8),
+                                      ("f64", O.CODEC_BF16)])
+@pytest.mark.parametrize("d", [4, 6])
+def test_avg_with_error_feedback(gb, dt, codec, d):
+    """The error-feedback batch with AVG: residuals as for SUM, each total
+    divided as above, over two steps."""
+    k, sizes = 3, [700, 4096 + 9, 0, 256]
+    res = [[np.zeros(n, np.float32) for _ in range(k)] for n in sizes]
+    dres = [[torch.zeros(n, device=DEV) for _ in range(k)] for n in sizes]
+    ws = torch.empty(gb.gb_bucket_batch_workspace_bytes(codec, k, sizes), dtype=torch.uint8, device=DEV)
+    for step in range(2):
+        hb = [[W.typed(n, dt, 4300 + 100 * step + 10 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+        db = [[dev_typed(x, dt) for x in xs] for xs in hb]
+        outs = [torch.empty(n, dtype=db[b][0].dtype, device=DEV) for b, n in enumerate(sizes)]
+        gb.gb_bucket_allreduce_local_batch_ef(outs, db, dres, codec, 0, ws, divisor=d)
+        torch.cuda.synchronize()
+        for b, n in enumerate(sizes):
+            if n == 0:
+                continue
+            total, _, _, res[b] = O.bucket_allreduce_ef_typed(hb[b], res[b], dt, (n + 255) // 256 * 256, codec, 0)
+            what = f"dt={dt} codec={codec} d={d} step={step} bucket {b}"
+            assert host_typed(outs[b], dt).tobytes() == np.ascontiguousarray(avg_of(total, dt, d)).tobytes(), what
+            for r in range(k):
+                assert (dres[b][r].cpu().numpy().view(np.uint32) == bits(res[b][r])).all(), what + f" residual {r}"
+
+
+def test_avg_with_more_ranks_than_one_launch_reads(gb):
+    """11 ranks (one bucket at a time, then the division in a second pass)."""
+    k, sizes, d = 11, [1000, 4096 + 3], 11
+    hb = [[W.gradients(n, 4400 + 20 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+    db = [[torch.from_numpy(x.copy()).to(DEV) for x in xs] for xs in hb]
+    outs = [torch.empty(n, device=DEV) for n in sizes]
+    ws = torch.empty(gb.gb_bucket_batch_workspace_bytes(O.CODEC_FP8, k, sizes), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch(outs, db, O.CODEC_FP8, 0, ws, divisor=d)
+    torch.cuda.synchronize()
+    for b, n in enumerate(sizes):
+        total = O.bucket_allreduce(hb[b], (n + 255) // 256 * 256, O.CODEC_FP8, 0)[0]
+        assert (bits(outs[b].cpu().numpy()) == bits(avg_of(total, "f32", d))).all(), f"bucket {b}"
