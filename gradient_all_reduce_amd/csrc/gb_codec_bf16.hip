@@ -110,7 +110,10 @@ __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, 
 
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTable src, OutTable codes, size_t n) {
-  const size_t sg = group_index<VecOrder>();
+  // float32 gradients in the permuted order; the others move more bytes
+  // per second in index order (1-7%, up to 21% with error feedback over
+  // bfloat16), measured on three machines
+  const size_t sg = ET == GB_DTYPE_F32 ? group_index<VecOrder>() : (size_t)blockIdx.x;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true>(out, src, codes, n, sg);
   else fused_bf16_body<K, ET, false>(out, src, codes, n, sg);
 }
