@@ -133,7 +133,10 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch 
     src.p[r] = t.src[b][r];
     codes.p[r] = t.codes[b][r];
   }
-  const size_t sg = w - t.first[b], n = t.n[b];
+  // a large bucket of float32 gradients takes the permuted order of a
+  // whole-buffer launch, as there
+  const size_t wl = w - t.first[b], n = t.n[b];
+  const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<VecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true, DIV>(t.out[b], src, codes, n, sg, d, inv);
   else fused_bf16_body<K, ET, false, DIV>(t.out[b], src, codes, n, sg, d, inv);
 }
@@ -205,9 +208,12 @@ hipError_t launch_fused_bf16(void* out, const PtrTable& srcs, uint16_t* const* c
 }
 
 namespace {
+// A batched launch takes the fused pass's cap for its largest bucket.
 template <int ET, int DIV>
 hipError_t fused_bf16_batch_t(BucketBatch& t, size_t grid, int k, float d, float inv, hipStream_t stream) {
-#define GB_CALL(K) fused_bf16_batch_kernel<K, ET, DIV><<<grid, kThreads, 0, stream>>>(t, d, inv);
+  size_t largest = 0;
+  for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
+#define GB_CALL(K) fused_bf16_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_bf16_lds<ET>(K, largest), stream>>>(t, d, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();

@@ -172,7 +172,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t
     codes.p[r] = t.codes[b][r];
     scales.p[r] = t.scales[b][r];
   }
-  const size_t g = w - t.first[b], n = t.n[b];
+  // a bucket large enough takes the permuted order of a whole-buffer launch
+  const size_t g = group_index_in<BlockOrder>(w - t.first[b], t.first[b + 1] - t.first[b]), n = t.n[b];
   if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, ET, true, DIV>(t.out[b], src, codes, scales, n, mode, g, d, inv);
   else fused_fp8_body<K, ET, false, DIV>(t.out[b], src, codes, scales, n, mode, g, d, inv);
 }
@@ -250,13 +251,14 @@ size_t batch_groups(int codec, size_t n) {
 }
 
 namespace {
-// Batched launches are bucket-sized pieces: they take the fused pass's cap
-// for launches below every size threshold.
+// A batched launch takes the fused pass's cap for its largest bucket.
 template <int ET, int DIV>
 hipError_t fused_fp8_batch_t(BucketBatch& t, size_t grid, int k, int scale_mode, float d, float inv,
                              hipStream_t stream) {
+  size_t largest = 0;
+  for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
 #define GB_CALL(K) \
-  fused_fp8_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_lds<ET>(K, 0), stream>>>(t, scale_mode, d, inv);
+  fused_fp8_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_lds<ET>(K, largest), stream>>>(t, scale_mode, d, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();

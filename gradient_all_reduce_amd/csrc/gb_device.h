@@ -624,12 +624,18 @@ struct GroupOrder {
 using VecOrder = GroupOrder<8, 256, 16>;
 using BlockOrder = GroupOrder<4, 256, 96>;
 
+// The group of workgroup w of a grid of `grid` workgroups (also a bucket's
+// share of a batched launch, w counted from the bucket's first workgroup).
 template <class Order>
-__device__ __forceinline__ size_t group_index() {
+__device__ __forceinline__ size_t group_index_in(size_t w, size_t grid) {
   constexpr size_t F = Order::fronts, D = Order::spacing, run = F * D;
-  const size_t w = blockIdx.x, grid = gridDim.x;
   if (grid < Order::min_runs * run || w >= grid / run * run) return w;
   return w / run * run + (w % F) * D + (w % run) / F;
+}
+
+template <class Order>
+__device__ __forceinline__ size_t group_index() {
+  return group_index_in<Order>(blockIdx.x, gridDim.x);
 }
 
 template <class Order>

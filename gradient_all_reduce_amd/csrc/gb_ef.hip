@@ -165,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_ef_batch_kernel(BucketBatc
     codes.p[r] = t.codes[b][r];
     scales.p[r] = t.scales[b][r];
   }
-  const size_t g = w - t.first[b], n = t.n[b];
+  // a bucket large enough takes the permuted order of a whole-buffer launch
+  const size_t g = group_index_in<BlockOrder>(w - t.first[b], t.first[b + 1] - t.first[b]), n = t.n[b];
   if ((g + 1) * kBlocksPerGroup * kBlock <= n)
     fused_fp8_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, scales, n, mode, g, dv, inv);
   else fused_fp8_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, scales, n, mode, g, dv, inv);
@@ -184,7 +185,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBat
     resid.p[r] = t.resid[b][r];
     codes.p[r] = t.codes[b][r];
   }
-  const size_t sg = w - t.first[b], n = t.n[b];
+  const size_t wl = w - t.first[b], n = t.n[b];
+  const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<VecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
   else fused_bf16_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
 }
@@ -201,14 +203,15 @@ size_t batch_grid(BucketBatchEf& t, int codec) {
   return grid > kMaxGrid ? 0 : grid;
 }
 
-// Batched launches are bucket-sized pieces: they take each pass's cap for
-// launches below every size threshold.
+// A batched launch takes each pass's cap for its largest bucket.
 template <int ET, int DIV>
 hipError_t fused_fp8_ef_batch_t(BucketBatchEf& t, int k, int scale_mode, float dv, float inv, hipStream_t stream) {
   const size_t grid = batch_grid(t, GB_CODEC_FP8_E4M3_B256);
   if (grid == 0) return hipErrorInvalidValue;
+  size_t largest = 0;
+  for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
 #define GB_CALL(K) \
-  fused_fp8_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_ef_lds(K, 0), stream>>>(t, scale_mode, dv, inv);
+  fused_fp8_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_ef_lds(K, largest), stream>>>(t, scale_mode, dv, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();

@@ -381,3 +381,36 @@ def test_avg_with_more_ranks_than_one_launch_reads(gb):
     for b, n in enumerate(sizes):
         total = O.bucket_allreduce(hb[b], (n + 255) // 256 * 256, O.CODEC_FP8, 0)[0]
         assert (bits(outs[b].cpu().numpy()) == bits(avg_of(total, "f32", d))).all(), f"bucket {b}"
+
+
+@pytest.mark.parametrize("codec,n,ef", [
+    (O.CODEC_FP8, 410_000_000 + 4096 * 7 + 99, False),  # above the fp8 passes' permuted-order size
+    (O.CODEC_FP8, 410_000_000 + 4096 * 7 + 99, True),
+    (O.CODEC_BF16, 72_000_000 + 1234, False),            # above the vector passes' permuted-order size
+    (O.CODEC_BF16, 72_000_000 + 1234, True),
+])
+def test_one_large_bucket_equals_the_single_buffer_call(gb, codec, n, ef):
+    """A batch of one bucket large enough to take the permuted workgroup
+    order and the large launches' occupancy cap gives the single-buffer
+    call's bits: output, payloads and residuals."""
+    k = 2
+    x = [W.device_gradients(n, 4500 + r, DEV) for r in range(k)]
+    need = gb.gb_bucket_batch_workspace_bytes(codec, k, [n])
+    assert need == gb.gb_bucket_workspace_bytes(codec, k, n, 256)
+    w1 = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    w2 = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    o1, o2 = torch.empty(n, device=DEV), torch.empty(n, device=DEV)
+    if ef:
+        r1 = [torch.full((n,), 3e-5, device=DEV) for _ in range(k)]
+        r2 = [t.clone() for t in r1]
+        gb.gb_bucket_allreduce_local_ef(o1, x, r1, 256 * 25_600, codec, 0, w1)
+        gb.gb_bucket_allreduce_local_batch_ef([o2], [x], [r2], codec, 0, w2)
+    else:
+        gb.gb_bucket_allreduce_local(o1, x, 256 * 25_600, codec, 0, w1)
+        gb.gb_bucket_allreduce_local_batch([o2], [x], codec, 0, w2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(w1, w2)
+    if ef:
+        for a, b in zip(r1, r2):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
