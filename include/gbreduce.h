@@ -278,7 +278,10 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
  * type than float32 holds up to 8 ranks, as there.  With k <= 8 and
  * a bf16 or fp8 codec, up to 16 buckets run in one launch, so buckets that
  * are ready together keep the GPU full where one small bucket per launch
- * cannot; otherwise the buckets run one after another.
+ * cannot; otherwise the buckets run one after another.  A large bucket takes
+ * the workgroup order and occupancy of a whole-buffer launch, so a batch of
+ * one bucket runs as the single-buffer call does, and with a divisor gives
+ * that stream's AVG.
  *   outs       host array of nbuckets device dtype[ns[b]] pointers,
  *              written; outs[b] may equal srcs[b * k]; no other overlap
  *              between any output, source or the workspace.
