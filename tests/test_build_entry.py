@@ -26,3 +26,23 @@ def test_build_scripts_load_with_the_package_unimportable():
     )
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+def test_the_binding_fails_loudly_without_the_library(tmp_path):
+    """With libgbreduce.so absent the package refuses to import, naming the
+    build step: there is no fallback to any other implementation."""
+    import shutil
+    pkg = tmp_path / "gradient_all_reduce_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "gradient_all_reduce_amd", "__init__.py"), pkg / "__init__.py")
+    code = ("import sys\n"
+            f"sys.path.insert(0, {str(tmp_path)!r})\n"
+            "try:\n"
+            "    import gradient_all_reduce_amd\n"
+            "except ImportError as e:\n"
+            "    assert 'not built' in str(e) and 'build.py' in str(e), e\n"
+            "    print('refused')\n"
+            "else:\n"
+            "    raise SystemExit('imported without the library')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=str(tmp_path), capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "refused" in r.stdout, r.stderr
