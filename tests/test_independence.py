@@ -73,10 +73,9 @@ def enclosing_function(tree, node):
 
 def test_only_the_allowed_callers_reach_the_oracle():
     allowed = {"__graft_entry__.py": {"smoke"}, "bench.py": {"cpu_units", "factory", "make", "compute", "check"}}
-    for p in list(files(ROOT, (".py",))):
+    product = [os.path.join(ROOT, n) for n in os.listdir(ROOT) if n.endswith(".py")] + list(files(PKG, (".py",)))
+    for p in product:
         rel = os.path.relpath(p, ROOT)
-        if rel.startswith(("tests", "oracle", "_work", "gpurun_out")) or "/." in rel:
-            continue
         hits = list(imports_oracle(p))
         if not hits:
             continue
