@@ -177,7 +177,9 @@ gb_status staging_context(const char* fn, StagingContext** out) {
   return GB_OK;
 }
 
-// Creates the context's streams and events; call with c->mu held.
+// Creates the context's streams and events; call with c->mu held.  On a
+// failure whatever was created is destroyed again, so a later call starts
+// from nothing.
 gb_status staging_ready(const char* fn, StagingContext* c) {
   if (c->ready) return GB_OK;
   hipError_t e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming);
@@ -185,7 +187,17 @@ gb_status staging_ready(const char* fn, StagingContext* c) {
     e = hipStreamCreateWithFlags(&c->copy[i], hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy[i], hipEventDisableTiming);
   }
-  if (e != hipSuccess) return fail(GB_ERR_HIP, "%s: creating the copy streams: %s", fn, hipGetErrorString(e));
+  if (e != hipSuccess) {
+    for (int i = 0; i < kCopyStreams; i++) {
+      if (c->ev_copy[i] != nullptr) (void)hipEventDestroy(c->ev_copy[i]);
+      if (c->copy[i] != nullptr) (void)hipStreamDestroy(c->copy[i]);
+      c->ev_copy[i] = nullptr;
+      c->copy[i] = nullptr;
+    }
+    if (c->ev_compute != nullptr) (void)hipEventDestroy(c->ev_compute);
+    c->ev_compute = nullptr;
+    return fail(GB_ERR_HIP, "%s: creating the copy streams: %s", fn, hipGetErrorString(e));
+  }
   c->ready = true;
   return GB_OK;
 }
@@ -586,6 +598,19 @@ gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
 
 namespace {
 
+// The workspace of a bucket-stream call: at least `need` bytes, 256-byte
+// aligned (unused, and may be NULL, for codec NONE).
+gb_status check_workspace(const char* fn, int codec, const void* workspace, size_t workspace_bytes, size_t need) {
+  if (codec == GB_CODEC_NONE) return GB_OK;
+  if (workspace == nullptr || workspace_bytes < need) {
+    return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes, need);
+  }
+  if (!aligned(workspace, 256)) {
+    return fail(GB_ERR_MISALIGNED, "%s: workspace = %p is not 256-byte aligned", fn, workspace);
+  }
+  return GB_OK;
+}
+
 // Validation shared by the two bucket-stream calls; on success fills the
 // workspace layout and the source table.
 gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k, size_t n,
@@ -607,16 +632,7 @@ gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k
   if (n == 0) return GB_OK;
   if ((s = check_array(out, GB_ALIGN, fn, "out")) != GB_OK) return s;
   if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
-  if (codec != GB_CODEC_NONE) {
-    if (workspace == nullptr || workspace_bytes < need) {
-      return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes,
-                  need);
-    }
-    if (!aligned(workspace, 256)) {
-      return fail(GB_ERR_MISALIGNED, "%s: workspace = %p is not 256-byte aligned", fn, workspace);
-    }
-  }
-  return GB_OK;
+  return check_workspace(fn, codec, workspace, workspace_bytes, need);
 }
 
 // The bucket stream over the whole buffer (all buckets start on block
@@ -799,15 +815,7 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
   }
   size_t cs = 0, so = 0, ss = 0, need = 0;
   if ((s = gb_bucket_workspace_layout(codec, k, total, GB_BLOCK, &cs, &so, &ss, &need)) != GB_OK) return s;
-  if (codec != GB_CODEC_NONE) {
-    if (workspace == nullptr || workspace_bytes < need) {
-      return fail(GB_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace, workspace_bytes,
-                  need);
-    }
-    if (!aligned(workspace, 256)) {
-      return fail(GB_ERR_MISALIGNED, "%s: workspace = %p is not 256-byte aligned", fn, workspace);
-    }
-  }
+  if ((s = check_workspace(fn, codec, workspace, workspace_bytes, need)) != GB_OK) return s;
   hipStream_t st = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   const size_t csz = code_size(codec);
