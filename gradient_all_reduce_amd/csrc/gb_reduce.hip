@@ -263,7 +263,7 @@ __device__ __forceinline__ void divide_half8(float a[8], const Divisor& dv) {
 
 template <int DT, int K, int OP, bool FULL, bool P2>
 __device__ __forceinline__ void reduce_typed_body(void* dst, const PtrTable& src, size_t nbytes, const Divisor& dv) {
-  const size_t byte = (group_index<VecOrder>() * kThreads + threadIdx.x) * 16;
+  const size_t byte = (group_index<TypedOrder>() * kThreads + threadIdx.x) * 16;
   if (!FULL && byte >= nbytes) return;
   // Loads: all K at once in a full workgroup; rank by rank in the one ragged
   // workgroup, so that its byte-wise loads keep few registers live (the
@@ -308,7 +308,7 @@ __device__ __forceinline__ void reduce_typed_body(void* dst, const PtrTable& src
 template <int DT, int K, int OP>
 __global__ __launch_bounds__(kThreads) void reduce_typed_kernel(void* dst, PtrTable src, size_t nbytes, Divisor dv,
                                                                  int pow2) {
-  const bool full = group_full<VecOrder>((size_t)kThreads * 16, nbytes);
+  const bool full = group_full<TypedOrder>((size_t)kThreads * 16, nbytes);
   if (OP == GB_OP_AVG && pow2) {
     if (full) reduce_typed_body<DT, K, OP, true, true>(dst, src, nbytes, dv);
     else reduce_typed_body<DT, K, OP, false, true>(dst, src, nbytes, dv);
