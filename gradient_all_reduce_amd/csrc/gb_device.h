@@ -622,10 +622,11 @@ struct GroupOrder {
   static constexpr size_t fronts = Fronts, spacing = Spacing, min_runs = MinRuns;
 };
 using VecOrder = GroupOrder<8, 256, 16>;
-// The typed reductions (4 KiB per workgroup whatever the element type) take
-// the same order from 8 runs, 64 MiB per rank: from 8 to 16 runs it moves
-// 2.4-5.2% more bytes per second than index order for every element type.
-using TypedOrder = GroupOrder<8, 256, 8>;
+// The reductions (the float32 sums and ops, and the typed reductions: 4 KiB
+// of each source per workgroup) take the same order from 8 runs, 64 MiB per
+// rank: from 8 to 16 runs it moves 1.3-5.2% more bytes per second than index
+// order, for every element type and for 2 and 4 ranks.
+using ReduceOrder = GroupOrder<8, 256, 8>;
 using BlockOrder = GroupOrder<4, 256, 96>;
 
 // The group of workgroup w of a grid of `grid` workgroups (also a bucket's

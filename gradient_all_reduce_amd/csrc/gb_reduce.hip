@@ -11,7 +11,7 @@ namespace {
 // ===========================================================================
 template <int K, bool ACC, bool FULL>
 __device__ __forceinline__ void reduce_sum_body(float* dst, const PtrTable& src, size_t n) {
-  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<ReduceOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   f4 x[K];
   f4 a;
@@ -26,7 +26,7 @@ __device__ __forceinline__ void reduce_sum_body(float* dst, const PtrTable& src,
 
 template <int K, bool ACC>
 __global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTable src, size_t n) {
-  if (group_full<VecOrder>(kVecPerGroup, n)) reduce_sum_body<K, ACC, true>(dst, src, n);
+  if (group_full<ReduceOrder>(kVecPerGroup, n)) reduce_sum_body<K, ACC, true>(dst, src, n);
   else reduce_sum_body<K, ACC, false>(dst, src, n);
 }
 
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void reduce_sum_kernel(float* dst, PtrTab
 // ===========================================================================
 template <int K, int OP, bool FULL, bool P2>
 __device__ __forceinline__ void reduce_op_body(float* dst, const PtrTable& src, size_t n, float d, float inv) {
-  const size_t i = (group_index<VecOrder>() * kThreads + threadIdx.x) * 4;
+  const size_t i = (group_index<ReduceOrder>() * kThreads + threadIdx.x) * 4;
   if (!FULL && i >= n) return;
   f4 x[K];
 #pragma unroll
@@ -58,7 +58,7 @@ __device__ __forceinline__ void reduce_op_body(float* dst, const PtrTable& src, 
 
 template <int K, int OP>
 __global__ __launch_bounds__(kThreads) void reduce_op_kernel(float* dst, PtrTable src, size_t n, float d, float inv) {
-  const bool full = group_full<VecOrder>(kVecPerGroup, n);
+  const bool full = group_full<ReduceOrder>(kVecPerGroup, n);
   if (OP == GB_OP_AVG && inv != 0.0f) {
     if (full) reduce_op_body<K, OP, true, true>(dst, src, n, d, inv);
     else reduce_op_body<K, OP, false, true>(dst, src, n, d, inv);
@@ -263,7 +263,7 @@ __device__ __forceinline__ void divide_half8(float a[8], const Divisor& dv) {
 
 template <int DT, int K, int OP, bool FULL, bool P2>
 __device__ __forceinline__ void reduce_typed_body(void* dst, const PtrTable& src, size_t nbytes, const Divisor& dv) {
-  const size_t byte = (group_index<TypedOrder>() * kThreads + threadIdx.x) * 16;
+  const size_t byte = (group_index<ReduceOrder>() * kThreads + threadIdx.x) * 16;
   if (!FULL && byte >= nbytes) return;
   // Loads: all K at once in a full workgroup; rank by rank in the one ragged
   // workgroup, so that its byte-wise loads keep few registers live (the
@@ -308,7 +308,7 @@ __device__ __forceinline__ void reduce_typed_body(void* dst, const PtrTable& src
 template <int DT, int K, int OP>
 __global__ __launch_bounds__(kThreads) void reduce_typed_kernel(void* dst, PtrTable src, size_t nbytes, Divisor dv,
                                                                  int pow2) {
-  const bool full = group_full<TypedOrder>((size_t)kThreads * 16, nbytes);
+  const bool full = group_full<ReduceOrder>((size_t)kThreads * 16, nbytes);
   if (OP == GB_OP_AVG && pow2) {
     if (full) reduce_typed_body<DT, K, OP, true, true>(dst, src, nbytes, dv);
     else reduce_typed_body<DT, K, OP, false, true>(dst, src, nbytes, dv);
