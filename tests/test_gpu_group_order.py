@@ -1,8 +1,9 @@
 """Launches large enough to take their groups out of index order (the
 permuted workgroup order of the streaming kernels, used from about 3.4e7
-values for the kernels over 1024-value vector groups and from about 4e8 for
-the kernels over 4096-value fp8 groups) give, bit for bit, what the same call
-gives over slices of the stream small enough to keep the index order.
+values for the kernels over 1024-value vector groups, from 64 MiB per rank
+for the reductions and from about 4e8 values for the kernels over
+4096-value fp8 groups) give, bit for bit, what the same call gives over
+slices of the stream small enough to keep the index order.
 
 Every result is elementwise (per value, or per 256-value fp8 block), so a
 call over a slice that starts on a bucket boundary computes exactly that
@@ -24,6 +25,7 @@ B = W.DDP_BUCKET  # 6,553,600 values: a multiple of 4096
 N_VEC = 72_000_000 + 1234  # > 16 runs of 2048 groups of 2048 values
 N_BLK = 410_000_000 + 4096 * 7 + 99  # > 96 runs of 1024 groups of 4096 values
 STEP_VEC = 5 * B  # 32,768,000 values: fewer than 16 runs of 1024-value groups
+STEP_RED = 2 * B  # 13,107,200 values: fewer than 8 runs of the reductions' 4 KiB groups (float32)
 STEP_BLK = 50 * B  # 327,680,000 values: fewer than 96 runs of 4096-value groups
 SENTINEL = 0x7FBADBAD  # a float32 NaN no kernel writes
 
@@ -68,7 +70,7 @@ def test_vector_group_kernels(gb):
         whole, ref = filled(n), filled(n)
         call = (lambda o, s: gb.gb_reduce_sum(o, s)) if op is None else (lambda o, s: gb.gb_reduce(o, s, op, div))
         call(whole, x)
-        for s, e in parts:
+        for s, e in slices(n, STEP_RED):
             call(ref[s:e], [t[s:e] for t in x])
         same(whole, ref, f"reduce op={op}")
 
@@ -123,7 +125,8 @@ def test_typed_reduce(gb, dt):
     whole = filled(n, x[0].dtype)
     ref = filled(n, x[0].dtype)
     gb.gb_reduce_typed(whole, x, gb.GB_OP_AVG, 2)
-    for s, e in slices(n, STEP_VEC):
+    step = STEP_RED * 4 // x[0].element_size() // 2  # below 8 runs of 4 KiB groups for the type
+    for s, e in slices(n, step):
         gb.gb_reduce_typed(ref[s:e], [t[s:e] for t in x], gb.GB_OP_AVG, 2)
     same(whole, ref, f"typed AVG {dt}")
 
