@@ -627,6 +627,9 @@ using VecOrder = GroupOrder<8, 256, 16>;
 // rank: from 8 to 16 runs it moves 1.3-5.2% more bytes per second than index
 // order, for every element type and for 2 and 4 ranks.
 using ReduceOrder = GroupOrder<8, 256, 8>;
+// The fused bf16-codec passes over float32 gradients take it from 8 runs too
+// (+3-7.5% between 8 and 16 runs; the plain bf16 decode loses there).
+using FusedVecOrder = GroupOrder<8, 256, 8>;
 using BlockOrder = GroupOrder<4, 256, 96>;
 
 // The group of workgroup w of a grid of `grid` workgroups (also a bucket's

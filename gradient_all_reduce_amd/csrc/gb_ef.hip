@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrT
   // float32 gradients in the permuted order; the others move more bytes
   // per second in index order (1-7%, up to 21% with error feedback over
   // bfloat16), measured on three machines
-  const size_t sg = ET == GB_DTYPE_F32 ? group_index<VecOrder>() : (size_t)blockIdx.x;
+  const size_t sg = ET == GB_DTYPE_F32 ? group_index<FusedVecOrder>() : (size_t)blockIdx.x;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n, sg);
   else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, sg);
 }
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBat
     codes.p[r] = t.codes[b][r];
   }
   const size_t wl = w - t.first[b], n = t.n[b];
-  const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<VecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
+  const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<FusedVecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
   else fused_bf16_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
 }
