@@ -49,6 +49,7 @@ __device__ __forceinline__ void reduce_encode_bf16_body(float* sum, uint16_t* co
   f4 a = x[0];
 #pragma unroll
   for (int r = 1; r < K; r++) a = a + x[r];
+  if (K > 1) a = canon4(a);
   store_bf16_4_at<FULL>(codes, i, n, bf16_pack4(a));
   if (SUM) store4_at<FULL>(sum, i, n, a);
 }
@@ -75,6 +76,9 @@ __device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& code
     const f4 v = bf16_unpack4(w[r]);
     a = (!ACC && r == 0) ? v : a + v;
   }
+  // one payload alone into float32 is an exact widening; a total of another
+  // type is rounded from the canonical NaN, so no NaN payload is narrowed
+  if (K > 1 || ACC || ET != GB_DTYPE_F32) a = canon4(a);
   store_group_vec<ET, FULL>(acc, sg, t, n, a);
 }
 
@@ -105,6 +109,7 @@ __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, 
   }
   f4 q[1] = {a};
   avg_total<DIV>(q, d, inv);
+  if (K > 1 || DIV != 0 || ET != GB_DTYPE_F32) q[0] = canon4(q[0]);
   store_group_vec<ET, FULL>(out, sg, t, n, q[0]);
 }
 

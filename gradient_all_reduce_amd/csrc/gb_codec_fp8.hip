@@ -55,6 +55,7 @@ __device__ __forceinline__ void reduce_encode_fp8_body(float* sum, uint8_t* code
     a[j] = x[0][j];
 #pragma unroll
     for (int r = 1; r < K; r++) a[j] = a[j] + x[r][j];
+    if (K > 1) a[j] = canon4(a[j]);
   }
   uint32_t w[4];
   const float s = encode_block16(a, mode, w);  // all 64 lanes take part
@@ -102,6 +103,8 @@ __device__ __forceinline__ void decode_fp8_body(void* acc, const PtrTable& codes
       a[j] = (!ACC && r == 0) ? v : a[j] + v;
     }
   }
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = canon4(a[j]);
   store_block<ET, MAP, FULL>(acc, block, col, n, a);
 }
 
@@ -145,6 +148,8 @@ __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, c
   }
   if (!live) return;
   avg_total<DIV>(a, d, inv);
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = canon4(a[j]);
   store_block<ET, MAP, FULL>(out, block, col, n, a);
 }
 

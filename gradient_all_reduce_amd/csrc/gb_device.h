@@ -54,6 +54,21 @@ constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
 
+// Canonical NaN (README "Bridge compression": every rank ends with the same
+// bits, whichever vendor's GPU ran the kernels).  The sign and payload of
+// the NaN an operation delivers are the platform's (an invalid operation
+// gives +NaN here and -NaN on x86 hosts; which input NaN an add passes on
+// may follow the compiler's operand order), so every NaN that the float32
+// arithmetic of the method delivers -- a sum of two or more terms, an AVG
+// quotient, a MAX or MIN over two or more ranks, a decoded fp8 value and
+// every decoded-and-added total, the error-feedback value and residual -- is
+// stored as the quiet NaN 0x7FC00000.  A copy (one source, or the decode of
+// one bf16 payload with nothing added) keeps its bits.  One compare and
+// select per stored value.
+constexpr uint32_t kCanonicalNan = 0x7FC00000u;
+__device__ __forceinline__ float canon(float v) { return v != v ? bitsf(kCanonicalNan) : v; }
+__device__ __forceinline__ f4 canon4(f4 v) { return f4{canon(v.x), canon(v.y), canon(v.z), canon(v.w)}; }
+
 // ---------------------------------------------------------------------------
 // Streaming memory access (non-temporal) with guarded variants for the ragged
 // end of a buffer.

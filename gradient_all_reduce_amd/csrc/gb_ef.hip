@@ -19,10 +19,10 @@ __device__ __forceinline__ void encode_bf16_ef_body(uint16_t* codes, float* res,
   const size_t sg = group_index<VecOrder>();
   const uint32_t t = threadIdx.x;
   if (!FULL && group_first<ET>(sg, t) >= n) return;
-  const f4 y = load_group_vec<ET, FULL>(src, sg, t, n) + load_group_f32<ET, FULL>(res, sg, t, n);
+  const f4 y = canon4(load_group_vec<ET, FULL>(src, sg, t, n) + load_group_f32<ET, FULL>(res, sg, t, n));
   const u2 w = bf16_pack4(y);
   store_group_bf16<ET, FULL>(codes, sg, t, n, w);
-  store_group_f32<ET, FULL>(res, sg, t, n, y - bf16_unpack4(w));
+  store_group_f32<ET, FULL>(res, sg, t, n, canon4(y - bf16_unpack4(w)));
 }
 
 template <int ET>
@@ -42,13 +42,13 @@ __device__ __forceinline__ void encode_fp8_ef_body(uint8_t* codes, float* scales
   load_block<ET, MAP, FULL>(src, block, col, n, x);
   load_block_f32<MAP, FULL>(res, block, col, n, r);
 #pragma unroll
-  for (int j = 0; j < 4; j++) x[j] = x[j] + r[j];  // y
+  for (int j = 0; j < 4; j++) x[j] = canon4(x[j] + r[j]);  // y
   uint32_t w[4];
   const float s = encode_block16(x, mode, w);  // all 64 lanes take part
   if (!FULL && block * kBlock >= n) return;
   if (col == 0u) scales[block] = s;
 #pragma unroll
-  for (int j = 0; j < 4; j++) r[j] = x[j] - e4m3_unpack4(w[j]) * s;
+  for (int j = 0; j < 4; j++) r[j] = canon4(x[j] - e4m3_unpack4(w[j]) * s);
   store_block_codes<MAP, FULL>(codes, block, col, n, w);
   store_block_f32<MAP, FULL>(res, block, col, n, r);
 }
@@ -74,7 +74,7 @@ __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src
     load_block<ET, MAP, FULL>(src.p[r], block, col, n, y[r]);
     load_block_f32<MAP, FULL>(static_cast<const float*>(resid.p[r]), block, col, n, q);
 #pragma unroll
-    for (int j = 0; j < 4; j++) y[r][j] = y[r][j] + q[j];
+    for (int j = 0; j < 4; j++) y[r][j] = canon4(y[r][j] + q[j]);
   }
   const bool live = FULL || block * kBlock < n;
   f4 a[4];
@@ -89,7 +89,7 @@ __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const f4 v = e4m3_unpack4(w[j]) * s;
-      d[j] = y[r][j] - v;
+      d[j] = canon4(y[r][j] - v);
       a[j] = r == 0 ? v : a[j] + v;
     }
     if (live) {
@@ -99,6 +99,8 @@ __device__ __forceinline__ void fused_fp8_ef_body(void* out, const PtrTable& src
   }
   if (!live) return;
   avg_total<DIV>(a, dv, inv);
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = canon4(a[j]);
   store_block<ET, MAP, FULL>(out, block, col, n, a);
 }
 
@@ -120,8 +122,8 @@ __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& sr
   f4 y[K];
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    y[r] = load_group_vec<ET, FULL>(src.p[r], sg, t, n) +
-           load_group_f32<ET, FULL>(static_cast<const float*>(resid.p[r]), sg, t, n);
+    y[r] = canon4(load_group_vec<ET, FULL>(src.p[r], sg, t, n) +
+                  load_group_f32<ET, FULL>(static_cast<const float*>(resid.p[r]), sg, t, n));
   }
   f4 a;
 #pragma unroll
@@ -129,11 +131,12 @@ __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& sr
     const u2 w = bf16_pack4(y[r]);
     const f4 v = bf16_unpack4(w);
     store_group_bf16<ET, FULL>(static_cast<uint16_t*>(codes.p[r]), sg, t, n, w);
-    store_group_f32<ET, FULL>(static_cast<float*>(resid.p[r]), sg, t, n, y[r] - v);
+    store_group_f32<ET, FULL>(static_cast<float*>(resid.p[r]), sg, t, n, canon4(y[r] - v));
     a = r == 0 ? v : a + v;
   }
   f4 q[1] = {a};
   avg_total<DIV>(q, dv, inv);
+  if (K > 1 || DIV != 0 || ET != GB_DTYPE_F32) q[0] = canon4(q[0]);
   store_group_vec<ET, FULL>(out, sg, t, n, q[0]);
 }
 

@@ -21,6 +21,7 @@ __device__ __forceinline__ void reduce_sum_body(float* dst, const PtrTable& src,
   f4 s = ACC ? a + x[0] : x[0];
 #pragma unroll
   for (int r = 1; r < K; r++) s = s + x[r];
+  if (K > 1 || ACC) s = canon4(s);  // one source alone is a copy
   store4_at<FULL>(dst, i, n, s);
 }
 
@@ -53,6 +54,7 @@ __device__ __forceinline__ void reduce_op_body(float* dst, const PtrTable& src, 
   }
   // a power-of-two d: s * (1/d) is the exact quotient rounded once, as s / d
   if (OP == GB_OP_AVG) s = P2 ? s * inv : s / d;
+  if (OP == GB_OP_AVG || K > 1) s = canon4(s);
   store4_at<FULL>(dst, i, n, s);
 }
 

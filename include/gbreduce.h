@@ -41,6 +41,18 @@
  *    and no fused multiply-add: every sum is a left fold over ranks
  *    0, 1, ..., k-1 starting from rank 0's value, so a result does not depend
  *    on the launch configuration and is bit-reproducible.
+ *  - NaN (README "Bridge compression": every rank ends with the same bits,
+ *    whichever vendor's GPU ran the kernels).  Every NaN that the float32
+ *    arithmetic delivers -- a sum of two or more terms, an AVG quotient, a
+ *    MAX or MIN over two or more values, a decoded-and-added total, the
+ *    error-feedback value and residual -- is stored as the quiet NaN
+ *    0x7FC00000, whatever the operands' NaN signs and payloads, and a NaN
+ *    total of another element type as that NaN's rounding (float16 0x7E00,
+ *    bfloat16 0x7FC0, float64 0x7FF8000000000000).  A copy keeps its bits:
+ *    k = 1 sums, MAX and MIN, and the decode of one bf16 payload into
+ *    float32.  An encoder's code for a NaN input keeps the input's sign.
+ *    The exact reductions of gb_reduce_typed over float16, bfloat16 and
+ *    float64 are excepted: their NaN results are some quiet NaN.
  *  - The codecs apply to floating-point SUM (and to AVG as a decode followed
  *    by the division), as the README's compression does; MAX, MIN and the
  *    integer types are reduced exactly, never compressed.

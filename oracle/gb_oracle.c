@@ -56,9 +56,16 @@
  *                         running mean of the decoded values converges to the
  *                         input, which fails for a wrong sign or a dropped
  *                         feedback term [test_oracle_ef.py].
+ *   canonical NaN         every NaN the float32 arithmetic delivers is
+ *                         0x7FC00000 whatever the host's default NaN: cases
+ *                         built from invalid operations (negative default
+ *                         NaN on x86) and from NaNs of both signs with
+ *                         payloads, copies keeping their bits
+ *                         [test_oracle_nan.py].
  * The pages fix none of the NaN and Inf conventions (NaN sign and payload,
- * Inf scale); they are readings taken here, stated at each function: parity
- * unpinned for non-finite inputs.
+ * Inf scale); they are readings taken here, stated at each function and
+ * pinned to their own definitions: parity with the pages unpinned for
+ * non-finite inputs.
  */
 #include "gb_oracle.h"
 
@@ -81,6 +88,28 @@ static float bits_float(uint32_t u) {
 }
 
 /* ------------------------------------------------------------------------
+ * Canonical NaN (reading taken).  README "Bridge compression": every rank
+ * ends with the same bits, whichever vendor's GPU ran the kernels.  IEEE
+ * 754-2019 fixes neither the sign nor the payload of the NaN an operation
+ * delivers: an invalid operation (0 * Inf, Inf - Inf) gives the platform's
+ * default NaN, positive on AMD GPUs and negative on x86, and which input
+ * NaN an operation passes on is only a recommendation (6.2.3), so those
+ * bits would depend on the machine.  Every NaN that the float32 arithmetic
+ * of this method delivers -- a rank-order sum, an AVG quotient, a MAX or
+ * MIN, a decoded-and-added total, the error-feedback value y = x + residual
+ * and the new residual -- is therefore stored as the one quiet NaN
+ * 0x7FC00000 (sign 0, only the quiet bit of the fraction set).  A result
+ * that no arithmetic produced keeps its bits: a sum or MAX / MIN of one rank
+ * is a copy, and the decode of one bf16 payload (no accumulation) is the
+ * exact widening of its codes; so do the conversions, an encoder's code for
+ * a NaN input keeping the NaN's own sign and payload bits as stated where
+ * it is defined.
+ * --------------------------------------------------------------------- */
+#define OR_CANONICAL_NAN 0x7FC00000u
+
+static float canonical(float v) { return isnan(v) ? bits_float(OR_CANONICAL_NAN) : v; }
+
+/* ------------------------------------------------------------------------
  * Fixed-order sum.  README "How it works": the leaders all-reduce the island
  * sums, so the leader holds the SUM of the k contributions; "API": all_reduce
  * with SUM.  The pages leave the order open (the Rust bridges add in ring
@@ -93,7 +122,7 @@ void or_reduce_sum(float* out, const float* const* x, int k, size_t n) {
     for (int r = 1; r < k; r++) {
       acc = acc + x[r][i];
     }
-    out[i] = acc;
+    out[i] = k == 1 ? acc : canonical(acc);
   }
 }
 
@@ -292,7 +321,9 @@ void or_decode_accumulate(float* acc, const void* const* codes,
       float v = decoded_value(codes[r], sc, i, codec);
       a = a + v;
     }
-    acc[i] = a;
+    /* one bf16 or uncompressed payload, nothing added: a widening or a copy */
+    int copied = k == 1 && !accumulate && codec != OR_CODEC_FP8;
+    acc[i] = copied ? a : canonical(a);
   }
 }
 
@@ -344,9 +375,9 @@ void or_bucket_allreduce(float* out, void* const* codes, float* const* scales,
  * --------------------------------------------------------------------- */
 void or_encode_bf16_ef(uint16_t* codes, float* residual, const float* x, size_t n) {
   for (size_t i = 0; i < n; i++) {
-    float y = x[i] + residual[i];
+    float y = canonical(x[i] + residual[i]);
     codes[i] = or_bf16_encode_one(y);
-    residual[i] = y - or_bf16_decode_one(codes[i]);
+    residual[i] = canonical(y - or_bf16_decode_one(codes[i]));
   }
 }
 
@@ -357,14 +388,14 @@ void or_encode_fp8_ef(uint8_t* codes, float* scales, float* residual,
   for (size_t b = 0; b < nblocks; b++) {
     size_t start = b * 256;
     size_t len = (n - start < 256) ? n - start : 256;
-    for (size_t i = 0; i < len; i++) y[i] = x[start + i] + residual[start + i];
+    for (size_t i = 0; i < len; i++) y[i] = canonical(x[start + i] + residual[start + i]);
     float s = or_block_scale(or_block_absmax(y, len), mode);
     scales[b] = s;
     for (size_t i = 0; i < len; i++) {
       uint8_t c = or_fp8_quantize_one(y[i], s);
       codes[start + i] = c;
       float decoded = or_e4m3_decode_one(c) * s;
-      residual[start + i] = y[i] - decoded;
+      residual[start + i] = canonical(y[i] - decoded);
     }
   }
 }
@@ -430,7 +461,7 @@ void or_reduce(float* out, const float* const* x, int k, size_t n, int op,
     or_reduce_sum(out, x, k, n);
     if (op == OR_OP_AVG) {
       float d = (float)divisor;
-      for (size_t i = 0; i < n; i++) out[i] = out[i] / d;
+      for (size_t i = 0; i < n; i++) out[i] = canonical(out[i] / d);
     }
     return;
   }
@@ -439,7 +470,7 @@ void or_reduce(float* out, const float* const* x, int k, size_t n, int op,
     for (int r = 1; r < k; r++) {
       acc = (op == OR_OP_MAX) ? max2019(acc, x[r][i]) : min2019(acc, x[r][i]);
     }
-    out[i] = acc;
+    out[i] = k == 1 ? acc : canonical(acc);
   }
 }
 
@@ -659,6 +690,12 @@ static void f32_to_typed(void* a, size_t i, int t, float v) {
   }
 }
 
+/* The binary32 total that a total of type t is rounded from: a NaN total of
+ * another type is always the canonical NaN's rounding (0x7E00, 0x7FC0,
+ * 0x7FF8000000000000), the decode of one bf16 payload included, so that no
+ * NaN payload is narrowed (reading taken, with the canonical NaN above). */
+static float typed_total(float v, int t) { return t == OR_T_F32 ? v : canonical(v); }
+
 static float* typed_array_to_f32(const void* x, size_t n, int t) {
   float* f = (float*)malloc((n ? n : 1) * sizeof(float));
   for (size_t i = 0; i < n; i++) f[i] = typed_to_f32(x, i, t);
@@ -677,7 +714,7 @@ void or_decode_sum_typed(void* out, int dtype, const void* const* codes,
                          const float* const* scales, int k, size_t n, int codec) {
   float* f = (float*)malloc((n ? n : 1) * sizeof(float));
   or_decode_accumulate(f, codes, scales, k, n, codec, 0);
-  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, f[i]);
+  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, typed_total(f[i], dtype));
   free(f);
 }
 
@@ -692,7 +729,7 @@ void or_bucket_allreduce_typed(void* out, void* const* codes, float* const* scal
   for (int r = 0; r < k; r++) f[r] = typed_array_to_f32(x[r], n, dtype);
   float* sum = (float*)malloc((n ? n : 1) * sizeof(float));
   or_bucket_allreduce(sum, codes, scales, (const float* const*)f, k, n, bucket_elems, codec, mode);
-  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, sum[i]);
+  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, typed_total(sum[i], dtype));
   free(sum);
   for (int r = 0; r < k; r++) free(f[r]);
 }
@@ -719,7 +756,7 @@ void or_bucket_allreduce_ef_typed(void* out, void* const* codes, float* const* s
   float* sum = (float*)malloc((n ? n : 1) * sizeof(float));
   or_bucket_allreduce_ef(sum, codes, scales, residuals, (const float* const*)f, k, n, bucket_elems,
                          codec, mode);
-  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, sum[i]);
+  for (size_t i = 0; i < n; i++) f32_to_typed(out, i, dtype, typed_total(sum[i], dtype));
   free(sum);
   for (int r = 0; r < k; r++) free(f[r]);
 }

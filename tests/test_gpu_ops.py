@@ -26,10 +26,9 @@ def dev(a):
 
 
 def same(got, want, what):
-    gn, wn = np.isnan(got), np.isnan(want)
-    assert (gn == wn).all(), f"{what}: NaN positions differ"
-    bad = np.flatnonzero(got.view(np.uint32)[~gn] != want.view(np.uint32)[~wn])
-    assert bad.size == 0, f"{what}: {bad.size} mismatches"
+    """Every bit, NaN included (the canonical NaN on both sides)."""
+    bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, f"{what}: {bad.size} mismatches at {bad[:5]}"
 
 
 def inputs(k, n, seed):

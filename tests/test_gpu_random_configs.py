@@ -66,7 +66,14 @@ def to_host(t):
     return t.cpu().numpy()
 
 
-def same(got, want, dt, what):
+def same(got, want, dt, what, nan_as_nan=False):
+    """Every byte equal, NaN included: every NaN the float arithmetic delivers
+    is the canonical one on both sides.  The exact reductions of the other
+    element types (nan_as_nan) compare NaN as NaN: their payloads are the
+    reading on format conversions, not pinned."""
+    if not nan_as_nan:
+        assert got.tobytes() == want.tobytes(), f"{what}: values differ"
+        return
     if dt in ("f32", "f64"):
         gn, wn = np.isnan(got), np.isnan(want)
     elif dt in ("f16", "bf16"):
@@ -115,7 +122,7 @@ def test_bucket_stream(gb, seed):
             gb.gb_bucket_allreduce_local_typed(out, d, bucket, codec, mode, ws)
         torch.cuda.synchronize()
         want, _, _ = O.bucket_allreduce_typed(xs, dt, bucket, codec, mode)
-    same(to_host(out), want, dt, what)
+    same(to_host(out), want, dt, what, nan_as_nan=codec == 0 and dt != "f32")
 
 
 @pytest.mark.parametrize("seed", range(120))
@@ -155,7 +162,7 @@ def test_batched_bucket_stream(gb, seed):
                 same(res[b][r].cpu().numpy(), res1[r], "f32", what + f" bucket {b} residual {r}")
         else:
             want, _, _ = O.bucket_allreduce_typed(xs[b], dt, bucket, codec, mode)
-        same(to_host(outs[b]), want, dt, what + f" bucket {b}")
+        same(to_host(outs[b]), want, dt, what + f" bucket {b}", nan_as_nan=codec == 0 and dt != "f32")
 
 
 @pytest.mark.parametrize("seed", range(400))
@@ -174,7 +181,7 @@ def test_reduction(gb, seed):
     out = d[0] if in_place else torch.empty(n, dtype=TORCH[dt], device=DEV)
     gb.gb_reduce_typed(out, d, op, divisor)
     torch.cuda.synchronize()
-    same(to_host(out), O.reduce_typed(xs, dt, op, divisor), dt, what)
+    same(to_host(out), O.reduce_typed(xs, dt, op, divisor), dt, what, nan_as_nan=dt != "f32")
 
 
 @pytest.mark.parametrize("seed", range(160))

@@ -1,6 +1,6 @@
 """GPU parity of the bridge codecs over float16, bfloat16 and float64 (and
 float32) arrays — gb_encode, gb_decode_sum, gb_bucket_allreduce_local_typed —
-against the CPU oracle, bit for bit (NaN compares as NaN): ragged sizes,
+against the CPU oracle, bit for bit (NaNs included): ragged sizes,
 every 16-bit code, float64 values at binary32 rounding boundaries and beyond
 its range, every rank count, and the bucket stream at full size on sampled
 blocks."""
@@ -57,9 +57,8 @@ def values(a, dt):
 
 
 def same_typed(got, want, dt, what):
-    gn, wn = np.isnan(values(got, dt)), np.isnan(values(want, dt))
-    assert (gn == wn).all(), f"{what}: NaN positions differ"
-    g, w = got[~gn], want[~wn]
+    """Every bit: a NaN total of any type is the canonical NaN's rounding."""
+    g, w = got, want
     if dt == "f32":
         g, w = g.view(np.uint32), w.view(np.uint32)
     elif dt == "f64":
