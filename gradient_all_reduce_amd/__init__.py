@@ -28,7 +28,7 @@ __all__ = [
     "gb_encode_staged", "gb_decode_accumulate_staged", "gb_reduce_typed", "GB_DTYPE", "GB_DTYPE_OF",
     "gb_encode", "gb_decode_sum", "gb_bucket_allreduce_local_typed", "gb_reduce_encode",
     "gb_bucket_allreduce_local_batch", "gb_bucket_allreduce_local_batch_ef", "gb_bucket_batch_workspace_bytes",
-    "GB_MAX_BATCH",
+    "GB_MAX_BATCH", "gb_bucket_allreduce_local_noalloc", "GB_NOALLOC_SCRATCH_BYTES",
 ]
 
 GB_OK, GB_ERR_INVALID_ARG, GB_ERR_MISALIGNED = 0, 1, 2
@@ -40,6 +40,7 @@ GB_BLOCK = 256
 GB_MAX_K = 16
 GB_MAX_N = 1 << 39  # largest element count a call accepts
 GB_MAX_BATCH = 4096  # largest bucket count of gb_bucket_allreduce_local_batch
+GB_NOALLOC_SCRATCH_BYTES = 64 << 20  # static payload scratch of gb_bucket_allreduce_local_noalloc
 # gb_dtype of each torch element type gb_reduce_typed takes
 GB_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3,
             torch.int8: 4, torch.uint8: 5, torch.int32: 6, torch.int64: 7}
@@ -69,6 +70,7 @@ _SIGNATURES = {
     "gb_encode_fp8_e4m3_blockscaled": (_I, [_P, _P, _P, _S, _I, _P]),
     "gb_decode_accumulate": (_I, [_P, _PP, _PP, _I, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P, _S, _P]),
+    "gb_bucket_allreduce_local_noalloc": (_I, [_P, _PP, _I, _S, _S, _I, _I, _P]),
     "gb_bucket_allreduce_local_batch": (_I, [_I, _PP, _PP, _SP, _I, _I, _I, _I, _I, _P, _S, _P]),
     "gb_bucket_allreduce_local_batch_ef": (_I, [_I, _PP, _PP, _PP, _SP, _I, _I, _I, _I, _I, _P, _S, _P]),
     "gb_bucket_batch_workspace_bytes": (_S, [_I, _I, _SP, _I]),
@@ -250,6 +252,19 @@ def gb_bucket_allreduce_local(out, srcs, bucket_elems, codec, scale_mode=GB_SCAL
     _check(_lib.gb_bucket_allreduce_local(_ptr(out), _ptr_array(srcs), len(srcs), n,
                                           int(bucket_elems), int(codec), int(scale_mode),
                                           _ptr(workspace), ws_bytes, _stream(stream, out.device)))
+
+
+def gb_bucket_allreduce_local_noalloc(out, srcs, bucket_elems, codec, scale_mode=GB_SCALE_ABSMAX_DIV_448,
+                                      stream=None):
+    """gb_bucket_allreduce_local with the payloads in the library's static
+    scratch (no workspace; at most GB_NOALLOC_SCRATCH_BYTES of payloads)."""
+    _device_tensor(out, torch.float32, "out")
+    for i, s in enumerate(srcs):
+        _device_tensor(s, torch.float32, f"srcs[{i}]")
+    n = out.numel()
+    _same_numel(srcs, n, "srcs")
+    _check(_lib.gb_bucket_allreduce_local_noalloc(_ptr(out), _ptr_array(srcs), len(srcs), n, int(bucket_elems),
+                                                  int(codec), int(scale_mode), _stream(stream, out.device)))
 
 
 def _size_array(ns):

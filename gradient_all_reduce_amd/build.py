@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgbreduce.so")
 # The kernels are split over several sources so that they compile in parallel.
-SOURCES = ["gb_reduce.hip", "gb_codec_fp8.hip", "gb_codec_bf16.hip", "gb_ef.hip", "gb_api.cpp"]
+SOURCES = ["gb_reduce.hip", "gb_codec_fp8.hip", "gb_codec_bf16.hip", "gb_ef.hip", "gb_noalloc.hip",
+           "gb_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: no multiply-add fusion, so decode (multiply) and add

@@ -689,12 +689,13 @@ hipError_t bucket_groups(void* out, const void* const* srcs, float* const* resid
 
 }  // namespace
 
-extern "C" {
+namespace gb {
 
-gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k, size_t n,
-                                    size_t bucket_elems, int codec, int scale_mode, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local";
+gb_status fail_status(gb_status s, const char* msg) { return fail(s, "%s", msg); }
+
+gb_status bucket_allreduce_local(const char* fn, float* out, const float* const* srcs, int k, size_t n,
+                                 size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   size_t cs, so, ss;
   const void* const* sp = reinterpret_cast<const void* const*>(srcs);
   gb_status s = check_bucket(fn, out, sp, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
@@ -706,6 +707,17 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k,
   return from_hip(bucket_groups(out, sp, nullptr, k, n, codec, scale_mode, GB_DTYPE_F32, ws, cs, ws + so, ss,
                                 as_stream(stream)),
                   fn);
+}
+
+}  // namespace gb
+
+extern "C" {
+
+gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k, size_t n,
+                                    size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return gb::bucket_allreduce_local("gb_bucket_allreduce_local", out, srcs, k, n, bucket_elems, codec, scale_mode,
+                                    workspace, workspace_bytes, stream);
 }
 
 gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* const* srcs, int k, size_t n,

@@ -121,4 +121,12 @@ hipError_t launch_fused_bf16_ef(void* out, const PtrTable& srcs, float* const* r
 hipError_t launch_fused_fp8_ef(void* out, const PtrTable& srcs, float* const* residuals, uint8_t* const* codes,
                                float* const* scales, int k, size_t n, int scale_mode, int dtype, hipStream_t stream);
 
+// gb_bucket_allreduce_local with its failures reported under the name fn:
+// validation (workspace included), then the launches.
+gb_status bucket_allreduce_local(const char* fn, float* out, const float* const* srcs, int k, size_t n,
+                                 size_t bucket_elems, int codec, int scale_mode, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+// Records a failure for gb_last_error() and returns s.
+gb_status fail_status(gb_status s, const char* msg);
+
 }  // namespace gb

@@ -279,6 +279,35 @@ gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* Size of the static device scratch of gb_bucket_allreduce_local_noalloc:
+ * 64 MiB per GPU, enough for the payloads of a 25 MiB DDP bucket
+ * (6,553,600 float32 values) from up to 10 ranks with the fp8 codec or 5
+ * with bf16. */
+#define GB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gb_bucket_allreduce_local_noalloc — gb_bucket_allreduce_local for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, result
+ * and errors, without the workspace: the payloads go to a static device
+ * array of GB_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends.  The call allocates nothing, device or
+ * host; its first call on a device looks up that device's array address
+ * once.
+ *   - GB_ERR_WORKSPACE, with nothing enqueued, when
+ *     gb_bucket_workspace_bytes(codec, k, n, bucket_elems) exceeds
+ *     GB_NOALLOC_SCRATCH_BYTES (codec NONE needs no scratch).
+ *   - The payloads are not returned: the array keeps the last call's
+ *     contents and every call on one GPU shares it, so calls that overlap on
+ *     one GPU (on different streams, or concurrently from several threads)
+ *     race.  Nothing in the array needs to start at zero: a call writes every
+ *     payload byte it reads.
+ */
+gb_status gb_bucket_allreduce_local_noalloc(float* out, const float* const* srcs,
+                                            int k, size_t n, size_t bucket_elems,
+                                            int codec, int scale_mode,
+                                            void* stream);
+
 /*
  * gb_bucket_allreduce_local_batch — the bucket stream over nbuckets buckets
  * that live in separate buffers, as a DDP hook holds them (README "How it
