@@ -62,8 +62,7 @@ __global__ __launch_bounds__(kThreads) void reduce_encode_bf16_kernel(float* sum
 }
 
 template <int K, bool ACC, int ET, bool FULL>
-__device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n) {
-  const size_t sg = group_index<VecOrder>();
+__device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& codes, size_t n, size_t sg) {
   const uint32_t t = threadIdx.x;
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   u2 w[K];
@@ -84,8 +83,9 @@ __device__ __forceinline__ void decode_bf16_body(void* acc, const PtrTable& code
 
 template <int K, bool ACC, int ET>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTable codes, size_t n) {
-  if (group_full<VecOrder>(kVecPerGroup, n)) decode_bf16_body<K, ACC, ET, true>(acc, codes, n);
-  else decode_bf16_body<K, ACC, ET, false>(acc, codes, n);
+  const size_t sg = ET == GB_DTYPE_F32 ? group_index<DecodeBf16Order>() : group_index<VecOrder>();
+  if ((sg + 1) * kVecPerGroup <= n) decode_bf16_body<K, ACC, ET, true>(acc, codes, n, sg);
+  else decode_bf16_body<K, ACC, ET, false>(acc, codes, n, sg);
 }
 
 // ===========================================================================

@@ -163,7 +163,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable
 
 // Several buckets in one launch (gradients of element type ET): each
 // workgroup finds its bucket from the table of first workgroups, then runs
-// the fused pass over that bucket's group, in index order.
+// the fused pass over that bucket's group: in index order within a bucket,
+// or in BlockOrder for a bucket large enough, as a whole-buffer launch.
 template <int K, int ET, int DIV>
 __global__ __launch_bounds__(kThreads) void fused_fp8_batch_kernel(BucketBatch t, int mode, float d, float inv) {
   const size_t w = blockIdx.x;

@@ -630,8 +630,11 @@ constexpr size_t kBlocksPerGroup = kThreads / 16;          // 16 fp8 blocks: one
 // bytes per second with 8 fronts 256 groups (1 MiB of float32) apart, and
 // the kernels over 4096-value fp8 groups 2-5% more with 4 fronts 256 groups
 // (4 MiB of float32) apart; neighbouring spacings gain less or lose.  Below
-// the MinRuns sizes (about 3.4e7 and 4e8 values) the gain is not there and
-// bucket-sized launches of a few million values lose up to 8%.
+// each order's MinRuns (16 runs, about 3.4e7 values, for the vector kernels;
+// 8 runs, 1.7e7, for the reductions and the fused bf16 passes over float32;
+// 4 runs, 8.4e6, for the bf16 decode into float32; 96 runs, about 4e8, for
+// the fp8 kernels) the gain is not there and bucket-sized launches of a few
+// million values lose up to 8%.
 template <size_t Fronts, size_t Spacing, size_t MinRuns>
 struct GroupOrder {
   static constexpr size_t fronts = Fronts, spacing = Spacing, min_runs = MinRuns;
@@ -646,6 +649,15 @@ using ReduceOrder = GroupOrder<8, 256, 8>;
 // (+3-7.5% between 8 and 16 runs; the plain bf16 decode loses there).
 using FusedVecOrder = GroupOrder<8, 256, 8>;
 using BlockOrder = GroupOrder<4, 256, 96>;
+// The bf16 decode into float32 takes the vector order from 4 runs (2^23
+// values of each payload): 4-rank decodes of 2^23 and 2^24 values moved
+// 19-20% more bytes per second than in index order, and nothing changed
+// from 2^26 up, where it was already permuted.
+using DecodeBf16Order = GroupOrder<8, 256, 4>;
+// The wide 4-rank sum (4 vectors per lane, 4096-value groups): 8 fronts 64
+// groups apart, so each front still starts 1 MiB of float32 after the
+// previous one, in every launch it is used for.
+using WideSumOrder = GroupOrder<8, 64, 1>;
 
 // The group of workgroup w of a grid of `grid` workgroups (also a bucket's
 // share of a batched launch, w counted from the bucket's first workgroup).

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrT
 
 // Several buckets in one launch, with their residuals: each workgroup finds
 // its bucket from the table of first workgroups and takes that bucket's
-// group, in index order.
+// group: in index order within a bucket, or in the whole-buffer launch's
+// order for a bucket large enough.
 template <int K, int ET, int DIV>
 __global__ __launch_bounds__(kThreads) void fused_fp8_ef_batch_kernel(BucketBatchEf t, int mode, float dv, float inv) {
   const size_t w = blockIdx.x;

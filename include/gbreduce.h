@@ -310,8 +310,9 @@ gb_status gb_bucket_allreduce_local_noalloc(float* out, const float* const* srcs
 
 /*
  * gb_bucket_allreduce_local_batch — the bucket stream over nbuckets buckets
- * that live in separate buffers, as a DDP hook holds them (README "How it
- * works": one all_reduce per gradient bucket).  Bucket b of ns[b] values has
+ * that live in separate buffers, as a DDP hook holds them (README "API",
+ * the ddp_comm_hook entry, and its "DistributedDataParallel" section: each
+ * gradient bucket is averaged by one async all_reduce).  Bucket b of ns[b] values has
  * its own k sources srcs[b * k + r] and its own output outs[b], of element
  * type dtype (GB_DTYPE_F32, F16, BF16 or F64), and gives, bit for bit, what
  * gb_bucket_allreduce_local_typed gives for it alone with bucket_elems >=

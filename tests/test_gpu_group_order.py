@@ -1,9 +1,12 @@
 """Launches large enough to take their groups out of index order (the
-permuted workgroup order of the streaming kernels, used from about 3.4e7
-values for the kernels over 1024-value vector groups, from 64 MiB per rank
-for the reductions and from about 4e8 values for the kernels over
-4096-value fp8 groups) give, bit for bit, what the same call gives over
-slices of the stream small enough to keep the index order.
+permuted workgroup order of the streaming kernels, used from 16 runs of
+2048 groups, about 3.4e7 values, for the kernels over 1024-value vector
+groups; from 8 runs, about 1.7e7 values, for the fused bf16-codec passes
+over float32 gradients; from 4 runs, 2^23 values, for the bf16 decode into
+float32; from 64 MiB per rank for the reductions; from about 4e8 values for
+the kernels over 4096-value fp8 groups) and the wide four-rank sum (from
+2^28 values) give, bit for bit, what the same call gives over slices of the
+stream small enough to keep the index order and the narrow shape.
 
 Every result is elementwise (per value, or per 256-value fp8 block), so a
 call over a slice that starts on a bucket boundary computes exactly that
@@ -25,6 +28,7 @@ B = W.DDP_BUCKET  # 6,553,600 values: a multiple of 4096
 N_VEC = 72_000_000 + 1234  # > 16 runs of 2048 groups of 2048 values
 N_BLK = 410_000_000 + 4096 * 7 + 99  # > 96 runs of 1024 groups of 4096 values
 STEP_VEC = 5 * B  # 32,768,000 values: fewer than 16 runs of 1024-value groups
+STEP_DEC = B  # 6,553,600 values: fewer than the bf16 decode's 4 runs (2^23 values)
 STEP_RED = 2 * B  # 13,107,200 values: fewer than 8 runs of the reductions' 4 KiB groups (float32)
 STEP_BLK = 50 * B  # 327,680,000 values: fewer than 96 runs of 4096-value groups
 SENTINEL = 0x7FBADBAD  # a float32 NaN no kernel writes
@@ -84,22 +88,23 @@ def test_vector_group_kernels(gb):
     gb.gb_encode_bf16(c2, x[1])
     whole, ref = filled(n), filled(n)
     gb.gb_decode_accumulate(whole, [cw, c2], None, gb.GB_CODEC_BF16)
-    for s, e in parts:
+    for s, e in slices(n, STEP_DEC):
         gb.gb_decode_accumulate(ref[s:e], [cw[s:e], c2[s:e]], None, gb.GB_CODEC_BF16)
     same(whole, ref, "decode bf16")
 
-    # the bf16 bucket stream, plain and with error feedback
+    # the bf16 bucket stream, plain and with error feedback (float32
+    # gradients: permuted from 8 runs, so the reference slices stay below)
     ws = torch.empty(gb.gb_bucket_workspace_bytes(gb.GB_CODEC_BF16, 3, n, B), dtype=torch.uint8, device=DEV)
     whole, ref = filled(n), filled(n)
     gb.gb_bucket_allreduce_local(whole, x, B, gb.GB_CODEC_BF16, 0, ws)
-    for s, e in parts:
+    for s, e in slices(n, STEP_RED):
         gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, gb.GB_CODEC_BF16, 0, ws)
     same(whole, ref, "bf16 bucket stream")
     rw = [torch.full((n,), 1e-5, device=DEV) for _ in range(3)]
     rr = [t.clone() for t in rw]
     whole, ref = filled(n), filled(n)
     gb.gb_bucket_allreduce_local_ef(whole, x, rw, B, gb.GB_CODEC_BF16, 0, ws)
-    for s, e in parts:
+    for s, e in slices(n, STEP_RED):
         gb.gb_bucket_allreduce_local_ef(ref[s:e], [t[s:e] for t in x], [t[s:e] for t in rr], B,
                                         gb.GB_CODEC_BF16, 0, ws)
     same(whole, ref, "bf16 bucket stream with error feedback")
@@ -116,6 +121,30 @@ def test_vector_group_kernels(gb):
         gb.gb_reduce_encode(gb.GB_CODEC_BF16, cr[s:e], None, [t[s:e] for t in x], sum=sr[s:e])
     same(sw, sr, "reduce_encode bf16 sum")
     same(cw, cr, "reduce_encode bf16 codes")
+
+
+def test_wide_four_rank_sum(gb):
+    """The four-rank float32 sum from 2^28 values (4 vectors per lane, one
+    workgroup per compute unit, its own order), with a ragged last group and
+    in place, against the narrow kernel over slices below 2^28 and against
+    the oracle on sampled windows (the first and last values included)."""
+    import numpy as np
+    from oracle import oracle as O
+    n = (1 << 28) + 4096 * 3 + 77
+    x = [W.device_gradients(n, 1100 + r, DEV) for r in range(4)]
+    whole, ref = filled(n), filled(n)
+    gb.gb_reduce_sum(whole, x)
+    for s, e in slices(n, STEP_BLK // 4):
+        gb.gb_reduce_sum(ref[s:e], [t[s:e] for t in x])
+    same(whole, ref, "wide four-rank sum")
+    rng = np.random.default_rng(5)
+    for s in [0, n - 100_000] + [int(v) for v in rng.integers(0, n - 100_000, 6)]:
+        got = whole[s:s + 100_000].cpu().numpy()
+        want = O.reduce_sum([t[s:s + 100_000].cpu().numpy() for t in x])
+        assert (got.view(np.uint32) == want.view(np.uint32)).all(), f"oracle window at {s}"
+    x0 = x[0].clone()
+    gb.gb_reduce_sum(x0, [x0] + x[1:])
+    same(x0, ref, "wide four-rank sum in place")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
