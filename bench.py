@@ -87,6 +87,9 @@ def parse():
                         "GPU 0's range kept (ddp_1b_buckets, ddp_1b_buckets_ef, gradients_256mib, "
                         "gradients_64mib)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="with the default workload, skip the summary of the four other workloads "
+                        "(two_rank_4mib, two_island_sweep, gradients_64mib, gradients_256mib)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="rough budget of oracle CPU time for the baseline sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -152,13 +155,8 @@ def host_values(torch, t):
 
 
 def same_bits(got, want):
-    """Bit-identical arrays, NaN compared as NaN."""
-    import numpy as np
-    if got.dtype.kind == "f" or want.dtype.kind == "f":
-        gn, wn = np.isnan(got), np.isnan(want)
-        if not (gn == wn).all():
-            return False
-        got, want = got[~gn], want[~wn]
+    """Bit-identical arrays, NaN included (every NaN the arithmetic delivers
+    is the canonical one on both sides)."""
     return got.tobytes() == want.tobytes()
 
 
@@ -599,6 +597,45 @@ class Staged(Workload):
         return [make(o) for o in range(0, 1 << 22, piece)], lambda m: f"first {m * piece:,} values of each rank"
 
 
+def codec_extra(wl, time_region, reps, dec_name, dec_bytes):
+    """Extras of the two gradient workloads (4 encodes, then the decode): the
+    decode kernel timed alone, and the same arithmetic as one fused launch,
+    gb_bucket_allreduce_local over the whole buffer (each rank's values read
+    once, its payload written, decoded and added in rank order), whose
+    output, codes and scales are checked bit for bit against the separate
+    calls'."""
+    torch, gb = wl.torch, wl.gb
+    fp8 = hasattr(wl, "scales")
+    codec = gb.GB_CODEC_FP8_E4M3_B256 if fp8 else gb.GB_CODEC_BF16
+    wl.step()
+    torch.cuda.synchronize()
+    dec_ms = time_region(wl.decode, reps) / reps
+    lay = gb.gb_bucket_workspace_layout(codec, wl.k, wl.n, wl.n)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=wl.dev)
+    out = torch.empty_like(wl.out)
+    fused = lambda: gb.gb_bucket_allreduce_local(out, wl.x, wl.n, codec, getattr(wl, "mode", 0), ws)
+    fused()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int32), wl.out.view(torch.int32)))
+    cb = 1 if fp8 else 2
+    for r in range(wl.k):
+        c0 = r * lay["codes_stride"]
+        same &= bool(torch.equal(ws[c0:c0 + cb * wl.n], wl.codes[r].view(torch.uint8)))
+        if fp8:
+            s0 = lay["scales_offset"] + r * lay["scales_stride"]
+            same &= bool(torch.equal(ws[s0:s0 + 4 * nblocks(wl.n)], wl.scales[r].view(torch.uint8)))
+    fused_ms = time_region(fused, reps) / reps
+    del ws, out
+    gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1)
+    return {"decode_kernel": dec_name, "decode_kernel_gbs": gbs(dec_bytes, dec_ms),
+            "decode_kernel_frac": round(gbs(dec_bytes, dec_ms) / HBM_PEAK_GBS, 4),
+            "fused_pass_kernel": "fused_fp8_kernel<4,0>" if fp8 else "fused_bf16_kernel<4,0>",
+            "fused_pass_bytes": wl.fused_bytes(), "fused_pass_us": round(fused_ms * 1e3, 2),
+            "fused_pass_gbs": gbs(wl.fused_bytes(), fused_ms),
+            "fused_pass_frac": round(gbs(wl.fused_bytes(), fused_ms) / HBM_PEAK_GBS, 4),
+            "fused_pass_same_bits_as_the_calls": same}
+
+
 class Gradients256(Workload):
     name = "gradients_256mib"
 
@@ -638,6 +675,16 @@ class Gradients256(Workload):
     def timed_kernel(self):
         per = 4 * self.n + self.n + 4 * nblocks(self.n)
         return ("encode_fp8_kernel<0>", per, self.k, lambda: [self.encode(r) for r in range(self.k)])
+
+    def decode(self):
+        self.gb.gb_decode_accumulate(self.out, self.codes, self.scales, self.gb.GB_CODEC_FP8_E4M3_B256)
+
+    def fused_bytes(self):
+        return self.k * (4 * self.n + self.n + 4 * nblocks(self.n)) + 4 * self.n
+
+    def extra(self, time_region, reps):
+        return codec_extra(self, time_region, reps, "decode_fp8_kernel<4,false,0>",
+                           self.k * (self.n + 4 * nblocks(self.n)) + 4 * self.n)
 
     def cpu_units(self):
         """4 fp8 encodes and the decode-and-add on 2^18-value pieces of every
@@ -701,6 +748,15 @@ class Gradients64(Workload):
 
     def timed_kernel(self):
         return ("encode_bf16_kernel<0,2>", 6 * self.n, self.k, lambda: [self.encode(r) for r in range(self.k)])
+
+    def decode(self):
+        self.gb.gb_decode_accumulate(self.out, self.codes, None, self.gb.GB_CODEC_BF16)
+
+    def fused_bytes(self):
+        return self.k * (4 * self.n + 2 * self.n) + 4 * self.n
+
+    def extra(self, time_region, reps):
+        return codec_extra(self, time_region, reps, "decode_bf16_kernel<4,false,0>", self.k * 2 * self.n + 4 * self.n)
 
     def cpu_units(self):
         """4 bf16 encodes and the decode-and-add on 2^18-value pieces."""
@@ -810,7 +866,46 @@ class Sweep(Workload):
             us[str(n)] = round(med * 1e3, 2)
             gbs[str(n)] = round(3 * self.esize * n / (med * 1e-3) / 1e9, 1)
         del scratch
-        return {"per_size_us_cache_flushed": us, "per_size_gbs_cache_flushed": gbs}
+        res = {"per_size_us_cache_flushed": us, "per_size_gbs_cache_flushed": gbs}
+        if self.dt == "f32" and self.op == 0:
+            res.update(self.copy_contrast(time_region, reps))
+        return res
+
+    def copy_contrast(self, time_region, reps):
+        """The leader's total written once, straight into the output (the sum
+        kernel's 12 bytes per value), against the unfused form: the sum made
+        in place into the first island buffer, then a device-to-device copy
+        (torch copy_, hipMemcpyAsync) into the output, 20 bytes per value.
+        Back to back at the three largest sizes; both give the same bits."""
+        torch, gb = self.torch, self.gb
+        res = {}
+        for n in self.sizes[-3:]:
+            x0 = self.x[n][0].clone()
+            fused = lambda: gb.gb_reduce_sum(self.out[n], self.x[n])
+            tmp = torch.empty_like(x0)
+            reset = lambda: tmp.copy_(x0)  # restores the first operand, untimed
+
+            def pair():
+                gb.gb_reduce_sum(tmp, [tmp, self.x[n][1]])
+                self.out[n].copy_(tmp)
+            fused()
+            want = self.out[n].clone()
+            reset()
+            pair()
+            torch.cuda.synchronize()
+            same = bool(torch.equal(self.out[n].view(torch.int32), want.view(torch.int32)))
+            f_ms = time_region(fused, reps) / reps
+            tot = 0.0
+            for _ in range(reps):
+                reset()
+                tot += time_region(pair, 1)
+            u_ms = tot / reps
+            res[str(n)] = {"fused_12n_us": round(f_ms * 1e3, 2), "inplace_plus_d2d_20n_us": round(u_ms * 1e3, 2),
+                           "fused_gbs": round(12 * n / (f_ms * 1e-3) / 1e9, 1),
+                           "inplace_plus_d2d_gbs_of_20n": round(20 * n / (u_ms * 1e-3) / 1e9, 1),
+                           "speedup": round(u_ms / f_ms, 3), "same_bits": same}
+            del x0, tmp, want
+        return {"sum_written_once_vs_inplace_plus_copy": res}
 
     def cpu_units(self):
         """Every size of the sweep, the larger ones in 2^20-value pieces."""
@@ -942,13 +1037,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def kernel_sources_sha256():
-    """sha256 over the kernel sources (gb_device.h and every .hip file, by name
-    in sorted order: each name, a NUL, its bytes, a NUL)."""
+    """sha256 over the library's kernel sources (gb_device.h and every .hip
+    file but the ceiling program's, by name in sorted order: each name, a NUL,
+    its bytes, a NUL)."""
     import glob
     import hashlib
     csrc = os.path.join(ROOT, "gradient_all_reduce_amd", "csrc")
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + [os.path.join(csrc, "gb_device.h")]):
+    srcs = [p for p in glob.glob(os.path.join(csrc, "*.hip")) if os.path.basename(p) != "gb_ceiling.hip"]
+    for path in sorted(srcs + [os.path.join(csrc, "gb_device.h")]):
         h.update(os.path.basename(path).encode() + b"\0" + open(path, "rb").read() + b"\0")
     return h.hexdigest()
 
@@ -1012,16 +1109,60 @@ def cpu_baseline(wl, budget):
         if t_one >= budget:
             break
     ok = all(bool(u.check(u.result)) for u in units)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    affinity = len(os.sched_getaffinity(0))
+    # every core this process may run on, up to the 16 a one-GPU share of the
+    # benchmark host holds
+    cores = max(1, min(affinity, 16))
     with cf.ThreadPoolExecutor(cores) as ex:
         t0 = time.perf_counter()
         list(ex.map(lambda u: u.compute(), units))
         t_all = time.perf_counter() - t0
     nbytes = sum(u.nbytes for u in units)
-    return {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": cores, "affinity_cores": affinity,
+            "kind": "oracle",
             "sample": describe(len(units)), "seconds": round(t_all, 3),
             "single_core": {"value": round(nbytes / t_one / 1e9, 4), "seconds": round(t_one, 3)},
             "cpu_model": cpu_model(), "gpu_matches_oracle_on_sample": ok}
+
+
+OTHER_WORKLOADS = ("two_rank_4mib", "two_island_sweep", "gradients_64mib", "gradients_256mib")
+
+
+def workload_summary(gb, torch, args, name, reps):
+    """One of the smaller workloads, timed as its own --workload run times it
+    but with fewer repetitions: the step's GB/s, its dominant kernel's GB/s
+    and fraction of the HBM peak, the p10/p50/p90 of single steps with the
+    last-level cache flushed, the workload's extras, and the oracle on the
+    first pieces of its CPU sample (compared with the GPU's outputs)."""
+    a = argparse.Namespace(**vars(args))
+    a.workload, a.shard, a.dtype, a.op, a.codec, a.scale_mode = name, 1, "f32", "sum", "fp8", 0
+    wl = WORKLOADS[name](gb, torch, a)
+    wl.setup()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        wl.step()
+    ms = time_region(torch, wl.stream, wl.step, reps) / reps
+    kname, kbytes, klaunches, kfn = wl.timed_kernel()
+    kms = time_region(torch, wl.stream, kfn, reps) / (reps * klaunches)
+    dist = step_distribution(torch, wl.stream, wl.step, reps)
+    extra = wl.extra(lambda fn, r: time_region(torch, wl.stream, fn, r), reps) if hasattr(wl, "extra") else {}
+    torch.cuda.synchronize()
+    factories, describe = wl.cpu_units()
+    units = [f() for f in factories[:2]]
+    ok = all(bool(u.check(u.compute())) for u in units)
+    sb = wl.step_bytes()
+    res = {"workload": wl.config, "step_ms": round(ms, 4), "step_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
+           "dominant_kernel": kname, "kernel_us_per_launch": round(kms * 1e3, 3),
+           "kernel_gbs": round(kbytes / (kms * 1e-3) / 1e9, 1),
+           "kernel_frac": round(kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "step_p50_ms_cache_flushed": dist["p50_ms"],
+           "step_gbs_cache_flushed_p50": round(sb / (dist["p50_ms"] * 1e-3) / 1e9, 1),
+           "step_distribution": dist, "oracle_sample": describe(len(units)),
+           "gpu_matches_oracle_on_sample": ok}
+    res.update(extra)
+    del wl, units
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_ceiling(torch, gb, stream, reps=5):
@@ -1038,6 +1179,38 @@ def copy_ceiling(torch, gb, stream, reps=5):
     del src, dst
     return {"library_copy_gbs": round(2 * 4 * n / (lib_ms * 1e-3) / 1e9, 1),
             "hipMemcpyDtoD_gbs": round(2 * 4 * n / (rt_ms * 1e-3) / 1e9, 1), "bytes_each_way": 4 * n}
+
+
+def memory_ceiling(gib=4, reps=10):
+    """The memory-ceiling program (gradient_all_reduce_amd/gb_ceiling, built
+    with the library) run as a child process: median GB/s of plain copies
+    (1, 2 and 4 vectors per lane; index order or 8 fronts; through LDS with
+    global_load_lds_dwordx4), read-only and write-only streams, and a
+    memory-only replica of the fused fp8 pass, on `gib`-GiB buffers."""
+    import subprocess
+    prog = os.path.join(ROOT, "gradient_all_reduce_amd", "gb_ceiling")
+    if not os.path.exists(prog):
+        return {"error": "gb_ceiling is not built"}
+    try:
+        r = subprocess.run([prog, str(gib), str(reps)], capture_output=True, text=True, timeout=180)
+    except subprocess.TimeoutExpired:
+        return {"error": "gb_ceiling timed out"}
+    if r.returncode != 0:
+        return {"error": f"gb_ceiling exited with {r.returncode}: {r.stderr.strip()[-300:]}"}
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    copies = {k: v for k, v in res.items() if k.startswith("copy")}
+    best = max(copies, key=copies.get)
+    return {"command": f"gradient_all_reduce_amd/gb_ceiling {gib} {reps}", "median_gbs": res,
+            "best_copy": best, "best_copy_gbs": copies[best]}
+
+
+def replica_frac(achieved, mem_ceiling, wl):
+    """For the float32 fp8 bucket stream: the fused pass against the
+    memory-only replica of its own access pattern, in the same run."""
+    rep = mem_ceiling.get("median_gbs", {}).get("fused_fp8_replica_4GiB")
+    if rep and type(wl) is DdpBuckets and wl.dt == "f32" and wl.codec == 2:
+        return {"frac_of_own_memory_pattern": round(achieved / rep, 4)}
+    return {}
 
 
 def step_distribution(torch, stream, fn, reps):
@@ -1122,11 +1295,33 @@ def main():
 
     ceiling = copy_ceiling(torch, gb, wl.stream)
     log(f"[bench] copy ceiling: {ceiling}")
+    mem_ceiling = memory_ceiling()
+    log(f"[bench] memory ceiling: {mem_ceiling}")
 
     extra = {}
     if hasattr(wl, "extra"):
         extra = wl.extra(lambda fn, reps: time_region(torch, wl.stream, fn, reps), max(3, args.steps // 2))
         log(f"[bench] extra: {extra}")
+    if isinstance(wl, DdpBuckets) and not isinstance(wl, DdpBucketsEF):
+        extra["headline"] = (f"value = one gb_bucket_allreduce_local call over the whole {wl.n:,}-value buffer of "
+                             f"each rank: a single launch covering all {len(wl.buckets())} buckets (each starts on a "
+                             f"256-value block boundary, so the result equals one call per bucket, bit for bit); "
+                             f"one call per bucket, as a DDP hook issues them, is per_bucket_calls_*")
+
+    if (args.workload == "ddp_1b_buckets" and args.shard == 1 and args.dtype == "f32" and args.codec == "fp8"
+            and args.scale_mode == 0 and not args.no_other_workloads):
+        for attr in ("pb_args", "x", "out", "ws"):  # the headline's 24 GB
+            if hasattr(wl, attr):
+                delattr(wl, attr)
+        torch.cuda.empty_cache()
+        others = {}
+        for name in OTHER_WORKLOADS:
+            log(f"[bench] other workload {name}")
+            others[name] = workload_summary(gb, torch, args, name, max(5, min(args.steps, 20)))
+            log(f"[bench] {name}: step {others[name]['step_gbs']} GB/s, {others[name]['dominant_kernel']} "
+                f"{others[name]['kernel_gbs']} GB/s (frac {others[name]['kernel_frac']}), oracle sample "
+                f"{others[name]['gpu_matches_oracle_on_sample']}")
+        extra["other_workloads"] = others
 
     line = {
         "metric": METRIC,
@@ -1146,8 +1341,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(kname, wl.name if args.shard == 1 else f"{wl.name}_shard{args.shard}"),
                      "kernel": kname, "bytes_per_launch": int(kbytes), "us_per_launch": round(kms * 1e3, 3),
                      "frac_of_copy_ceiling": round(achieved / max(ceiling["library_copy_gbs"],
-                                                                  ceiling["hipMemcpyDtoD_gbs"]), 4)},
+                                                                  ceiling["hipMemcpyDtoD_gbs"],
+                                                                  mem_ceiling.get("best_copy_gbs", 0.0)), 4),
+                     **replica_frac(achieved, mem_ceiling, wl)},
         "copy_ceiling": ceiling,
+        "memory_ceiling": mem_ceiling,
         "step_distribution": dist,
         "cpu_baseline": cpu,
     }

@@ -18,6 +18,9 @@ LIB = os.path.join(HERE, "libgbreduce.so")
 SOURCES = ["gb_reduce.hip", "gb_codec_fp8.hip", "gb_codec_bf16.hip", "gb_ef.hip", "gb_noalloc.hip",
            "gb_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# The memory-ceiling measurement program bench.py runs (not part of the library).
+CEILING_SRC = "gb_ceiling.hip"
+CEILING = os.path.join(HERE, "gb_ceiling")
 
 # -ffp-contract=off: no multiply-add fusion, so decode (multiply) and add
 #   round separately as the arithmetic requires.
@@ -44,9 +47,19 @@ def build(verbose=False):
         subprocess.run(cmd, check=True)
         return obj
 
-    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    def compile_ceiling():
+        tmp = CEILING + ".tmp"
+        cmd = [HIPCC, *FLAGS, "-Wno-unused-function", "-x", "hip", os.path.join(CSRC, CEILING_SRC), "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, CEILING)
+
+    jobs = max(1, min(len(SOURCES) + 1, os.cpu_count() or 1))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        ceiling = ex.submit(compile_ceiling)
         objs = list(ex.map(compile_one, SOURCES))
+        ceiling.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

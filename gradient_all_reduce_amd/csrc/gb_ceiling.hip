@@ -1,0 +1,225 @@
+// gb_ceiling.hip — the memory ceiling of one MI355X, measured: the program
+// behind bench.py's `memory_ceiling` object and its rocprofv3 summaries.
+// It is not part of libgbreduce.
+//
+// Every kernel here moves 16-byte non-temporal vectors through HBM with no
+// arithmetic worth the name, in one of the shapes the library's kernels
+// could take, so the fastest of them bounds what a streaming kernel of that
+// read/write mix can reach on this chip:
+//   copy      1 GiB or 4 GiB read and written: U vectors per lane (U = 1, 2,
+//             4), index order or the 8-front order of the vector kernels;
+//   copy_lds  the same with the loads going straight into LDS
+//             (global_load_lds_dwordx4, gfx950) and out of it to the stores;
+//   read      read only (the sum of each lane's values is stored only if it
+//             takes an impossible value), 4 vectors per lane, 2 per CU;
+//   write     write only, 1 vector per lane;
+//   replica   the memory pattern of the fused fp8 bucket pass over 4 ranks,
+//             with the encode replaced by taking each value's top byte: 4
+//             float32 sources read, 4 code streams, 4 scale streams and the
+//             float32 total written, in the pass's lane map, workgroup order
+//             and occupancy cap.
+// Each line of output is one variant: its bytes per launch and the median
+// and best GB/s over timed launches (hipEvents); the last line is one JSON
+// object of the medians.  Usage: gb_ceiling [size_gib] [reps].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "gb_device.h"
+
+namespace {
+
+using gb::f4;
+using gb::kThreads;
+
+#define CK(call)                                                                              \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess) {                                                                   \
+      std::fprintf(stderr, "gb_ceiling: %s failed: %s\n", #call, hipGetErrorString(e_));      \
+      std::exit(1);                                                                           \
+    }                                                                                         \
+  } while (0)
+
+// The workgroup's group: index order, or 8 fronts 256 groups apart.
+template <bool FRONTS>
+__device__ __forceinline__ size_t group() {
+  return FRONTS ? gb::group_index_in<gb::GroupOrder<8, 256, 1>>(blockIdx.x, gridDim.x) : (size_t)blockIdx.x;
+}
+
+template <int U, bool FRONTS>
+__global__ __launch_bounds__(kThreads) void copy_kernel(const f4* __restrict__ src, f4* __restrict__ dst) {
+  const size_t base = group<FRONTS>() * kThreads * U + threadIdx.x;
+  f4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(src + base + (size_t)u * kThreads);
+#pragma unroll
+  for (int u = 0; u < U; u++) __builtin_nontemporal_store(v[u], dst + base + (size_t)u * kThreads);
+}
+
+// Loads land in LDS at M0 + 16 * lane: each wave passes its own 1 KiB slice
+// of a vector's 4 KiB row as the base.
+template <int U>
+__global__ __launch_bounds__(kThreads) void copy_lds_kernel(const f4* __restrict__ src, f4* __restrict__ dst) {
+  __shared__ f4 buf[U * kThreads];
+  const size_t base = (size_t)blockIdx.x * kThreads * U + threadIdx.x;
+  const unsigned wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + base + (size_t)u * kThreads),
+                                     (__attribute__((address_space(3))) void*)&buf[u * kThreads + wave * 64],
+                                     16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has landed
+#pragma unroll
+  for (int u = 0; u < U; u++) __builtin_nontemporal_store(buf[u * kThreads + threadIdx.x], dst + base + (size_t)u * kThreads);
+}
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void read_kernel(const f4* __restrict__ src, float* sink) {
+  const size_t base = (size_t)blockIdx.x * kThreads * U + threadIdx.x;
+  f4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(src + base + (size_t)u * kThreads);
+  float a = 0.0f;
+#pragma unroll
+  for (int u = 0; u < U; u++) a += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+  if (a == -1.25f) sink[0] = a;  // never true for the zeros read here
+}
+
+__global__ __launch_bounds__(kThreads) void write_kernel(f4* __restrict__ dst, float value) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  __builtin_nontemporal_store(f4{value, value, value, value}, dst + i);
+}
+
+// The fused fp8 pass's memory pattern (4 ranks, float32): lane map, group
+// order and cap of the library's kernel, the encode replaced by the top byte
+// of each value and the scale by the block's first value.
+__global__ __launch_bounds__(kThreads) void replica_kernel(gb::PtrTable src, gb::OutTable codes, gb::OutTable scales,
+                                                           float* __restrict__ out) {
+  const uint32_t col = threadIdx.x & 15u;
+  const size_t block = gb::group_index<gb::BlockOrder>() * gb::kBlocksPerGroup + (threadIdx.x >> 4);
+  f4 x[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) x[r][j] = gb::load4(static_cast<const float*>(src.p[r]) + gb::lane_elem(block, j, col));
+  }
+  f4 a[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f4 v = x[r][j];
+      const uint32_t w = (gb::fbits(v.x) >> 24) | ((gb::fbits(v.y) >> 24) << 8) | ((gb::fbits(v.z) >> 24) << 16) |
+                         ((gb::fbits(v.w) >> 24) << 24);
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(codes.p[r]) +
+                                                                 gb::lane_elem(block, j, col)));
+      a[j] = r == 0 ? v : a[j] + v;
+    }
+    if (col == 0u) static_cast<float*>(scales.p[r])[block] = x[r][0].x;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) gb::store4(out + gb::lane_elem(block, j, col), a[j]);
+}
+
+struct Result {
+  std::string name;
+  double bytes, med_gbs, best_gbs;
+};
+std::vector<Result> g_results;
+
+template <class F>
+void measure(const std::string& name, double bytes, int reps, F launch) {
+  hipEvent_t a, b;
+  CK(hipEventCreate(&a));
+  CK(hipEventCreate(&b));
+  launch();
+  launch();
+  CK(hipGetLastError());
+  CK(hipDeviceSynchronize());
+  std::vector<float> ms;
+  for (int i = 0; i < reps; i++) {
+    CK(hipEventRecord(a, nullptr));
+    launch();
+    CK(hipEventRecord(b, nullptr));
+    CK(hipEventSynchronize(b));
+    float t = 0.0f;
+    CK(hipEventElapsedTime(&t, a, b));
+    ms.push_back(t);
+  }
+  CK(hipGetLastError());
+  std::sort(ms.begin(), ms.end());
+  const Result r{name, bytes, bytes / (ms[ms.size() / 2] * 1e6), bytes / (ms[0] * 1e6)};
+  g_results.push_back(r);
+  std::printf("%-28s %12.0f bytes  median %7.1f GB/s  best %7.1f GB/s\n", name.c_str(), bytes, r.med_gbs, r.best_gbs);
+  std::fflush(stdout);
+  CK(hipEventDestroy(a));
+  CK(hipEventDestroy(b));
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  const size_t gib = argc > 1 ? std::strtoull(argv[1], nullptr, 10) : 4;
+  const int reps = argc > 2 ? std::atoi(argv[2]) : 10;
+  if (gib < 1 || gib > 16 || reps < 1 || reps > 1000) {
+    std::fprintf(stderr, "usage: gb_ceiling [size_gib 1..16] [reps 1..1000]\n");
+    return 2;
+  }
+  const size_t bytes = gib << 30, nvec = bytes / 16, nval = bytes / 4;
+  // five float32 buffers of `bytes` (4 sources and an output), 4 code
+  // streams of nval bytes, 4 scale streams
+  const size_t nblk = nval / 256;
+  f4 *buf[5];
+  for (auto& p : buf) {
+    CK(hipMalloc(&p, bytes));
+    CK(hipMemset(p, 0, bytes));
+  }
+  uint8_t* codes;
+  float *scales, *sink;
+  CK(hipMalloc(&codes, 4 * nval));
+  CK(hipMalloc(&scales, 4 * nblk * sizeof(float)));
+  CK(hipMalloc(&sink, 256));
+  CK(hipDeviceSynchronize());
+  std::printf("gb_ceiling: buffers of %zu GiB, %d timed launches per variant\n", gib, reps);
+
+  const double copy_bytes = 2.0 * bytes;
+  const std::string sz = std::to_string(gib) + "GiB";
+  // grids: nvec / (256 U) workgroups; nvec is a multiple of 2^26, so every grid divides exactly
+  measure("copy_u1_" + sz, copy_bytes, reps, [&] { copy_kernel<1, false><<<nvec / kThreads, kThreads>>>(buf[0], buf[1]); });
+  measure("copy_u1_fronts_" + sz, copy_bytes, reps, [&] { copy_kernel<1, true><<<nvec / kThreads, kThreads>>>(buf[0], buf[1]); });
+  measure("copy_u2_" + sz, copy_bytes, reps, [&] { copy_kernel<2, false><<<nvec / (2 * kThreads), kThreads>>>(buf[0], buf[1]); });
+  measure("copy_u4_" + sz, copy_bytes, reps, [&] { copy_kernel<4, false><<<nvec / (4 * kThreads), kThreads>>>(buf[0], buf[1]); });
+  measure("copy_u4_fronts_" + sz, copy_bytes, reps, [&] { copy_kernel<4, true><<<nvec / (4 * kThreads), kThreads>>>(buf[0], buf[1]); });
+  measure("copy_lds_u1_" + sz, copy_bytes, reps, [&] { copy_lds_kernel<1><<<nvec / kThreads, kThreads>>>(buf[0], buf[1]); });
+  measure("copy_lds_u4_" + sz, copy_bytes, reps, [&] { copy_lds_kernel<4><<<nvec / (4 * kThreads), kThreads>>>(buf[0], buf[1]); });
+  measure("read_u4_2percu_" + sz, (double)bytes, reps,
+          [&] { read_kernel<4><<<nvec / (4 * kThreads), kThreads, gb::kTwoPerCuLds>>>(buf[0], sink); });
+  measure("write_u1_" + sz, (double)bytes, reps, [&] { write_kernel<<<nvec / kThreads, kThreads>>>(buf[1], 1.0f); });
+  gb::PtrTable st = {};
+  gb::OutTable ct = {}, sct = {};
+  for (int r = 0; r < 4; r++) {
+    st.p[r] = buf[r];
+    ct.p[r] = codes + (size_t)r * nval;
+    sct.p[r] = scales + (size_t)r * nblk;
+  }
+  const double replica_bytes = (double)nval * (16.0 + 4.0 + 16.0 / 256 + 4.0);
+  measure("fused_fp8_replica_" + sz, replica_bytes, reps,
+          [&] { replica_kernel<<<nblk / gb::kBlocksPerGroup, kThreads, gb::kTwoPerCuLds>>>(st, ct, sct, reinterpret_cast<float*>(buf[4])); });
+
+  std::printf("{");
+  for (size_t i = 0; i < g_results.size(); i++) {
+    std::printf("%s\"%s\": %.1f", i ? ", " : "", g_results[i].name.c_str(), g_results[i].med_gbs);
+  }
+  std::printf("}\n");
+  for (auto& p : buf) CK(hipFree(p));
+  CK(hipFree(codes));
+  CK(hipFree(scales));
+  CK(hipFree(sink));
+  return 0;
+}
