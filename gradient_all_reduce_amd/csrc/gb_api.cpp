@@ -3,10 +3,12 @@
 // every argument is valid; no call allocates device memory.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "gb_internal.h"
 
@@ -76,6 +78,142 @@ gb_status check_table(const void* const* table, int k, size_t align, const char*
     if (s != GB_OK) return s;
   }
   return GB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Overlapping buffers.  Every buffer a call writes (outputs, and the buffers
+// it reads and rewrites: residuals, workspaces, staging buffers) must share
+// no byte with any other buffer of the call, except where the ABI lets one
+// output be one input exactly (out == srcs[0]: same address, same length);
+// inputs may overlap one another.  A partial overlap would let one lane's
+// store reach the values another lane has still to read.  The spans are
+// sorted, so a batch of thousands of buckets costs O(N log N); a call with
+// few buffers keeps them in fixed storage and allocates nothing.
+// ---------------------------------------------------------------------------
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // bytes [lo, hi)
+  const char* name = "";
+  long i = -1, j = -1;  // indices shown with the name, -1 if none
+};
+
+class Spans {
+ public:
+  void add(const void* p, size_t bytes, const char* name, long i = -1, long j = -1) {
+    if (p == nullptr || bytes == 0) return;
+    Span s;
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+    s.name = name;
+    s.i = i;
+    s.j = j;
+    if (n_ < kInline) {
+      inline_[n_] = s;
+    } else {
+      if (n_ == kInline) heap_.assign(inline_, inline_ + kInline);
+      heap_.push_back(s);
+    }
+    n_++;
+  }
+  // An input, left out when it is exactly the output `alias` may be.
+  void add_input(const void* p, size_t bytes, const void* alias, const char* name, long i = -1, long j = -1) {
+    if (p != nullptr && p == alias) return;
+    add(p, bytes, name, i, j);
+  }
+  Span* data() { return n_ <= kInline ? inline_ : heap_.data(); }
+  size_t size() const { return n_; }
+
+ private:
+  static constexpr size_t kInline = 48;
+  Span inline_[kInline];
+  std::vector<Span> heap_;
+  size_t n_ = 0;
+};
+
+void span_label(const Span& s, char* buf, size_t size) {
+  if (s.j >= 0) std::snprintf(buf, size, "%s[%ld * k + %ld]", s.name, s.i, s.j);
+  else if (s.i >= 0) std::snprintf(buf, size, "%s[%ld]", s.name, s.i);
+  else std::snprintf(buf, size, "%s", s.name);
+}
+
+gb_status overlap_error(const char* fn, const Span& a, const Span& b) {
+  char la[64], lb[64];
+  span_label(a, la, sizeof la);
+  span_label(b, lb, sizeof lb);
+  return fail(GB_ERR_INVALID_ARG, "%s: %s overlaps %s (bytes %#zx..%#zx and %#zx..%#zx)", fn, la, lb, (size_t)a.lo,
+              (size_t)a.hi, (size_t)b.lo, (size_t)b.hi);
+}
+
+bool by_start(const Span& a, const Span& b) { return a.lo < b.lo; }
+
+// outs: every buffer the call writes; ins: the buffers it only reads, the
+// exactly aliased input already left out.
+gb_status check_disjoint(const char* fn, Spans& outs, Spans& ins) {
+  Span* o = outs.data();
+  Span* in = ins.data();
+  const size_t no = outs.size(), ni = ins.size();
+  std::sort(o, o + no, by_start);
+  size_t far = 0;  // the output reaching furthest so far
+  for (size_t a = 1; a < no; a++) {
+    if (o[a].lo < o[far].hi) return overlap_error(fn, o[far], o[a]);
+    if (o[a].hi > o[far].hi) far = a;
+  }
+  // the outputs are now disjoint and in order, so their ends increase too:
+  // the inputs starting before an output's end only grow from one output to
+  // the next, and the one of them reaching furthest decides
+  std::sort(in, in + ni, by_start);
+  size_t q = 0;
+  long reach = -1;
+  for (size_t a = 0; a < no; a++) {
+    for (; q < ni && in[q].lo < o[a].hi; q++) {
+      if (reach < 0 || in[q].hi > in[reach].hi) reach = (long)q;
+    }
+    if (reach >= 0 && in[reach].hi > o[a].lo) return overlap_error(fn, o[a], in[reach]);
+  }
+  return GB_OK;
+}
+
+// dst against k sources of `bytes` each; dst may be srcs[0].
+gb_status check_sum_overlaps(const char* fn, const void* dst, const void* const* srcs, int k, size_t bytes) {
+  Spans outs, ins;
+  outs.add(dst, bytes, "dst");
+  for (int r = 0; r < k; r++) ins.add_input(srcs[r], bytes, r == 0 ? dst : nullptr, "srcs", r);
+  return check_disjoint(fn, outs, ins);
+}
+
+// An output of out_bytes against k payloads (code arrays of code_bytes, and
+// for fp8 scale arrays of scale_bytes).
+gb_status check_decode_overlaps(const char* fn, const void* out, size_t out_bytes, const void* const* codes,
+                                const float* const* scales, int k, size_t code_bytes, size_t scale_bytes) {
+  Spans outs, ins;
+  outs.add(out, out_bytes, "acc");
+  for (int r = 0; r < k; r++) {
+    ins.add(codes[r], code_bytes, "codes", r);
+    if (scales != nullptr) ins.add(scales[r], scale_bytes, "scales", r);
+  }
+  return check_disjoint(fn, outs, ins);
+}
+
+// An encoder's payload (and error-feedback residual) against its source.
+gb_status check_encode_overlaps(const char* fn, const void* codes, size_t code_bytes, const void* scales,
+                                size_t scale_bytes, const void* residual, size_t n, const void* src, size_t src_bytes) {
+  Spans outs, ins;
+  outs.add(codes, code_bytes, "codes");
+  outs.add(scales, scale_bytes, "scales");
+  outs.add(residual, 4 * n, "residual");
+  ins.add(src, src_bytes, "src");
+  return check_disjoint(fn, outs, ins);
+}
+
+size_t dtype_size(int dtype) {
+  switch (dtype) {
+    case GB_DTYPE_F16:
+    case GB_DTYPE_BF16: return 2;
+    case GB_DTYPE_F64:
+    case GB_DTYPE_I64: return 8;
+    case GB_DTYPE_I8:
+    case GB_DTYPE_U8: return 1;
+    default: return 4;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -295,6 +433,7 @@ gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n, v
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   const void* const* sp = reinterpret_cast<const void* const*>(srcs);
   if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  if ((s = check_sum_overlaps(fn, dst, sp, k, 4 * n)) != GB_OK) return s;
   return from_hip(sum_groups(dst, sp, k, n, false, as_stream(stream)), fn);
 }
 
@@ -313,6 +452,7 @@ gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n, int o
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   const void* const* sp = reinterpret_cast<const void* const*>(srcs);
   if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  if ((s = check_sum_overlaps(fn, dst, sp, k, 4 * n)) != GB_OK) return s;
   return from_hip(op_groups(dst, sp, k, n, GB_DTYPE_F32, op, divisor, as_stream(stream)), fn);
 }
 
@@ -335,6 +475,7 @@ gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, i
   if (n == 0) return GB_OK;
   if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
   if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  if ((s = check_sum_overlaps(fn, dst, srcs, k, dtype_size(dtype) * n)) != GB_OK) return s;
   return from_hip(op_groups(dst, srcs, k, n, dtype, op, divisor, as_stream(stream)), fn);
 }
 
@@ -345,6 +486,7 @@ gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stre
   gb_status s;
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_encode_overlaps(fn, codes, 2 * n, nullptr, 0, nullptr, n, src, 4 * n)) != GB_OK) return s;
   return from_hip(gb::launch_encode_bf16(codes, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
 }
 
@@ -358,6 +500,7 @@ gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales, const fl
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_encode_overlaps(fn, codes, n, scales, 4 * nblocks(n), nullptr, n, src, 4 * n)) != GB_OK) return s;
   return from_hip(gb::launch_encode_fp8(codes, scales, src, n, scale_mode, GB_DTYPE_F32, as_stream(stream)), fn);
 }
 
@@ -376,6 +519,10 @@ gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float
   if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if (codec == GB_CODEC_FP8_E4M3_B256 &&
       (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
+    return s;
+  }
+  if ((s = check_decode_overlaps(fn, acc, 4 * n, codes, codec == GB_CODEC_FP8_E4M3_B256 ? scales : nullptr, k,
+                                 code_bytes(codec, n), 4 * nblocks(n))) != GB_OK) {
     return s;
   }
   return from_hip(decode_groups(acc, codes, scales, k, n, codec, accumulate != 0, GB_DTYPE_F32, as_stream(stream)),
@@ -397,6 +544,10 @@ gb_status gb_encode(int codec, int dtype, void* codes, float* scales, const void
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_encode_overlaps(fn, codes, code_bytes(codec, n), fp8 ? scales : nullptr, 4 * nblocks(n), nullptr, n,
+                                 src, dtype_size(dtype) * n)) != GB_OK) {
+    return s;
+  }
   hipStream_t st = as_stream(stream);
   if (fp8) {
     return from_hip(gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, src, n, scale_mode, dtype, st), fn);
@@ -427,6 +578,11 @@ gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes, const fl
       (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
     return s;
   }
+  if ((s = check_decode_overlaps(fn, dst, dtype_size(dtype) * n, codes,
+                                 codec == GB_CODEC_FP8_E4M3_B256 ? scales : nullptr, k, code_bytes(codec, n),
+                                 4 * nblocks(n))) != GB_OK) {
+    return s;
+  }
   return from_hip(decode_groups(dst, codes, scales, k, n, codec, false, dtype, as_stream(stream)), fn);
 }
 
@@ -451,6 +607,14 @@ gb_status gb_reduce_encode(float* sum, void* codes, float* scales, const float* 
   if (sum != nullptr && (s = check_array(sum, GB_ALIGN, fn, "sum")) != GB_OK) return s;
   const void* const* sp = reinterpret_cast<const void* const*>(srcs);
   if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+  {
+    Spans outs, ins;
+    outs.add(sum, 4 * n, "sum");
+    outs.add(codes, code_bytes(codec, n), "codes");
+    if (fp8) outs.add(scales, 4 * nblocks(n), "scales");
+    for (int r = 0; r < k; r++) ins.add_input(sp[r], 4 * n, r == 0 ? sum : nullptr, "srcs", r);
+    if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
+  }
   hipStream_t st = as_stream(stream);
   hipError_t e;
   if (k <= kR) {
@@ -489,6 +653,16 @@ gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* sc
   if (fp8) {
     if ((s = check_array(scales_dev, 4, fn, "scales_dev")) != GB_OK) return s;
     if ((s = check_pinned(scales_host, 4, fn, "scales_host")) != GB_OK) return s;
+  }
+  {
+    Spans outs, ins;
+    const size_t cbytes = code_bytes(codec, n), sbytes = fp8 ? 4 * nblocks(n) : 0;
+    outs.add(codes_dev, cbytes, "codes_dev");
+    outs.add(codes_host, cbytes, "codes_host");
+    outs.add(fp8 ? scales_dev : nullptr, sbytes, "scales_dev");
+    outs.add(fp8 ? scales_host : nullptr, sbytes, "scales_host");
+    ins.add(src, 4 * n, "src");
+    if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
   }
   StagingContext* c;
   if ((s = staging_context(fn, &c)) != GB_OK) return s;
@@ -556,6 +730,20 @@ gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host,
       std::snprintf(name, sizeof name, "scales_dev[%d]", r);
       if ((s = check_array(scales_dev[r], 4, fn, name)) != GB_OK) return s;
     }
+  }
+  {
+    Spans outs, ins;
+    const size_t cbytes = code_bytes(codec, n), sbytes = 4 * nblocks(n);
+    outs.add(acc, 4 * n, "acc");
+    for (int r = 0; r < k; r++) {
+      outs.add(codes_dev[r], cbytes, "codes_dev", r);
+      ins.add(codes_host[r], cbytes, "codes_host", r);
+      if (fp8) {
+        outs.add(scales_dev[r], sbytes, "scales_dev", r);
+        ins.add(scales_host[r], sbytes, "scales_host", r);
+      }
+    }
+    if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
   }
   StagingContext* c;
   if ((s = staging_context(fn, &c)) != GB_OK) return s;
@@ -635,6 +823,21 @@ gb_status check_bucket(const char* fn, void* out, const void* const* srcs, int k
   return check_workspace(fn, codec, workspace, workspace_bytes, need);
 }
 
+// A single-buffer bucket stream: out (esize bytes per value, may be
+// srcs[0]), the k residuals and the workspace's k payloads (cs + ss bytes
+// each) against the k sources.
+gb_status check_bucket_overlaps(const char* fn, const void* out, const void* const* srcs, float* const* residuals,
+                                int k, size_t n, size_t esize, int codec, const void* workspace, size_t cs, size_t ss) {
+  Spans outs, ins;
+  outs.add(out, esize * n, "out");
+  if (codec != GB_CODEC_NONE) outs.add(workspace, (size_t)k * (cs + ss), "workspace");
+  for (int r = 0; r < k; r++) {
+    if (residuals != nullptr) outs.add(residuals[r], 4 * n, "residuals", r);
+    ins.add_input(srcs[r], esize * n, r == 0 ? out : nullptr, "srcs", r);
+  }
+  return check_disjoint(fn, outs, ins);
+}
+
 // The bucket stream over the whole buffer (all buckets start on block
 // boundaries, so one launch covers them; rank r's payload lands where a
 // whole-buffer encode would put it).  The first kLaunchRanks ranks go through
@@ -701,6 +904,7 @@ gb_status bucket_allreduce_local(const char* fn, float* out, const float* const*
   gb_status s = check_bucket(fn, out, sp, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
                              &so, &ss);
   if (s != GB_OK || n == 0) return s;
+  if ((s = check_bucket_overlaps(fn, out, sp, nullptr, k, n, 4, codec, workspace, cs, ss)) != GB_OK) return s;
   // One launch covers every bucket: a partly idle GPU at the end of each
   // bucket is avoided, and the result equals one call per bucket bit for bit.
   char* ws = static_cast<char*>(workspace);
@@ -734,6 +938,9 @@ gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* cons
                 "which holds up to %d ranks per call", fn, k, kR);
   }
   if (n == 0) return GB_OK;
+  if ((s = check_bucket_overlaps(fn, out, srcs, nullptr, k, n, dtype_size(dtype), codec, workspace, cs, ss)) != GB_OK) {
+    return s;
+  }
   char* ws = static_cast<char*>(workspace);
   return from_hip(bucket_groups(out, srcs, nullptr, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
                                 as_stream(stream)),
@@ -828,6 +1035,23 @@ gb_status bucket_batch(const char* fn, int dtype, void* const* outs, const void*
   size_t cs = 0, so = 0, ss = 0, need = 0;
   if ((s = gb_bucket_workspace_layout(codec, k, total, GB_BLOCK, &cs, &so, &ss, &need)) != GB_OK) return s;
   if ((s = check_workspace(fn, codec, workspace, workspace_bytes, need)) != GB_OK) return s;
+  {
+    // every bucket's output and residuals, and the workspace, against each
+    // other and against every source (outs[b] may be srcs[b * k])
+    const size_t esize = dtype_size(dtype);
+    Spans written, read;
+    if (codec != GB_CODEC_NONE) written.add(workspace, need, "workspace");
+    for (int b = 0; b < nbuckets; b++) {
+      if (ns[b] == 0) continue;
+      written.add(outs[b], esize * ns[b], "outs", b);
+      for (int r = 0; r < k; r++) {
+        const size_t i = (size_t)b * k + r;
+        if (ef) written.add(residuals[i], 4 * ns[b], "residuals", b, r);
+        read.add_input(srcs[i], esize * ns[b], r == 0 ? outs[b] : nullptr, "srcs", b, r);
+      }
+    }
+    if ((s = check_disjoint(fn, written, read)) != GB_OK) return s;
+  }
   hipStream_t st = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   const size_t csz = code_size(codec);
@@ -950,6 +1174,7 @@ gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, 
   if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
   if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_encode_overlaps(fn, codes, 2 * n, nullptr, 0, residual, n, src, 4 * n)) != GB_OK) return s;
   return from_hip(gb::launch_encode_bf16_ef(codes, residual, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
 }
 
@@ -964,6 +1189,7 @@ gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales, float
   if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
   if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_encode_overlaps(fn, codes, n, scales, 4 * nblocks(n), residual, n, src, 4 * n)) != GB_OK) return s;
   return from_hip(gb::launch_encode_fp8_ef(codes, scales, residual, src, n, scale_mode, GB_DTYPE_F32,
                                            as_stream(stream)),
                   fn);
@@ -984,6 +1210,7 @@ gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, flo
   if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
     return s;
   }
+  if ((s = check_bucket_overlaps(fn, out, sp, residuals, k, n, 4, codec, workspace, cs, ss)) != GB_OK) return s;
   char* ws = static_cast<char*>(workspace);
   return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32, ws, cs, ws + so, ss,
                                 as_stream(stream)),
@@ -1006,6 +1233,10 @@ gb_status gb_encode_ef(int codec, int dtype, void* codes, float* scales, float* 
   if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
   if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
   if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+  if ((s = check_encode_overlaps(fn, codes, code_bytes(codec, n), fp8 ? scales : nullptr, 4 * nblocks(n), residual, n,
+                                 src, dtype_size(dtype) * n)) != GB_OK) {
+    return s;
+  }
   hipStream_t st = as_stream(stream);
   if (fp8) {
     return from_hip(gb::launch_encode_fp8_ef(static_cast<uint8_t*>(codes), scales, residual, src, n, scale_mode,
@@ -1033,6 +1264,10 @@ gb_status gb_bucket_allreduce_local_ef_typed(int dtype, void* out, const void* c
   }
   if (n == 0) return GB_OK;
   if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
+    return s;
+  }
+  if ((s = check_bucket_overlaps(fn, out, srcs, residuals, k, n, dtype_size(dtype), codec, workspace, cs, ss)) !=
+      GB_OK) {
     return s;
   }
   char* ws = static_cast<char*>(workspace);

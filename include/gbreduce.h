@@ -33,7 +33,12 @@
  *    and untouched until the stream has passed the work (the duty the
  *    README's "Async collectives" section places on tensors in flight).
  *  - Validation happens before anything is enqueued: a call that returns an
- *    error enqueued nothing and wrote nothing.  n == 0 is GB_OK and enqueues
+ *    error enqueued nothing and wrote nothing.
+ *  - Overlap: every buffer a call writes (outputs, payloads, workspaces,
+ *    residuals, staging buffers) shares no byte with any other buffer of the
+ *    call, except the in-place aliases each call documents (out == srcs[0]:
+ *    the same address and length); inputs may overlap one another.  Any
+ *    other overlap is GB_ERR_INVALID_ARG, naming the two buffers.  n == 0 is GB_OK and enqueues
  *    nothing.  The calls never abort or exit the process.
  *  - Failures return a gb_status; gb_last_error() then holds a one-line
  *    detail for the calling thread.
@@ -91,7 +96,8 @@ extern "C" {
 
 typedef enum gb_status {
   GB_OK = 0,
-  GB_ERR_INVALID_ARG = 1, /* null pointer with n > 0, n > GB_MAX_N, k out of range, bad flag, bad bucket size */
+  GB_ERR_INVALID_ARG = 1, /* null pointer with n > 0, n > GB_MAX_N, k out of range, bad flag, bad bucket size,
+                             overlapping buffers */
   GB_ERR_MISALIGNED = 2,  /* an element array is not 16-byte aligned, or a scale array not 4-byte */
   GB_ERR_UNSUPPORTED = 3, /* unknown codec or scale mode */
   GB_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than required */

@@ -255,7 +255,9 @@ float or_block_absmax(const float* x, size_t len) {
 
 float or_block_scale(float a, int mode) {
   if (mode == OR_SCALE_ABSMAX_DIV_448) return a / 448.0f;
-  /* OR_SCALE_POW2 */
+  /* OR_SCALE_POW2.  No block's absmax is NaN (NaN elements are skipped); a
+   * NaN argument gives NaN rather than a search that never ends. */
+  if (isnan(a)) return a;
   if (a == 0.0f) return 1.0f;
   if (isinf(a)) return INFINITY;
   for (int e = -149;; e++) {

@@ -1,0 +1,54 @@
+"""The host code under AddressSanitizer and UndefinedBehaviorSanitizer, on the
+CPU: the C ABI layer of libgbreduce (gb_api.cpp, built with g++ against the
+host stand-ins of tests/sanitize/stub_hip.cpp, driven by
+tests/sanitize/api_driver.c: validation, the refusal of overlapping buffers,
+the launches a call plans, and a launch failure injected at every launch of
+several multi-launch calls), and the CPU oracle (gb_oracle.c, driven by
+tests/sanitize/oracle_driver.c over ragged sizes and special values).  The
+two are built and run apart.  Any sanitizer report aborts the program."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.join(ROOT, "tests", "sanitize")
+SAN = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+HIP_INCLUDE = "/opt/rocm/include"
+
+pytestmark = pytest.mark.skipif(shutil.which("g++") is None or shutil.which("gcc") is None,
+                                reason="needs gcc and g++")
+
+
+def run(cmd, **kw):
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, **kw)
+    assert r.returncode == 0, f"{' '.join(cmd)}\n{r.stdout}\n{r.stderr}"
+    return r
+
+
+def test_abi_layer_under_sanitizers(tmp_path):
+    if not os.path.exists(os.path.join(HIP_INCLUDE, "hip", "hip_runtime_api.h")):
+        pytest.skip("HIP headers not installed")
+    cxx = ["g++", "-std=c++17", *SAN, "-D__HIP_PLATFORM_AMD__", "-I", HIP_INCLUDE, "-I", os.path.join(ROOT, "include")]
+    api = tmp_path / "gb_api.o"
+    stub = tmp_path / "stub_hip.o"
+    drv = tmp_path / "api_driver.o"
+    exe = tmp_path / "api_driver"
+    run([*cxx, "-c", os.path.join(ROOT, "gradient_all_reduce_amd", "csrc", "gb_api.cpp"), "-o", str(api)])
+    run([*cxx, "-c", os.path.join(HERE, "stub_hip.cpp"), "-o", str(stub)])
+    run(["gcc", "-std=c11", *SAN, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(HERE, "api_driver.c"),
+         "-o", str(drv)])
+    run(["g++", *SAN, str(api), str(stub), str(drv), "-o", str(exe)])
+    out = run([str(exe)], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    assert "0 failed" in out.stdout, out.stdout + out.stderr
+    assert "runtime error" not in out.stderr
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    exe = tmp_path / "oracle_driver"
+    run(["gcc", "-std=c11", *SAN, "-ffp-contract=off", "-fno-fast-math", "-I", os.path.join(ROOT, "oracle"),
+         os.path.join(HERE, "oracle_driver.c"), os.path.join(ROOT, "oracle", "gb_oracle.c"), "-lm", "-o", str(exe)])
+    out = run([str(exe)], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    assert "0 failed" in out.stdout, out.stdout + out.stderr
+    assert "runtime error" not in out.stderr
