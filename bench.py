@@ -87,6 +87,8 @@ def parse():
                         "GPU 0's range kept (ddp_1b_buckets, ddp_1b_buckets_ef, gradients_256mib, "
                         "gradients_64mib)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-memory-ceiling", action="store_true",
+                   help="skip the memory-ceiling program (gradient_all_reduce_amd/gb_ceiling)")
     p.add_argument("--no-other-workloads", action="store_true",
                    help="with the default workload, skip the summary of the four other workloads "
                         "(two_rank_4mib, two_island_sweep, gradients_64mib, gradients_256mib)")
@@ -218,8 +220,10 @@ class DdpBuckets(Workload):
 
     def timed_kernel(self):
         et = self.gb.GB_DTYPE_OF[self.dt]
+        # the four-rank float32 sum takes its wide kernel from 2^28 values per rank
+        f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
         name = {2: f"fused_fp8_kernel<4,{et}>", 1: f"fused_bf16_kernel<4,{et}>",
-                0: "reduce_sum_kernel<4,false>" if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]
+                0: f32_sum if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]
         return (name, self.step_bytes(), 1, self.step)
 
     def per_bucket_step(self):
@@ -1295,7 +1299,7 @@ def main():
 
     ceiling = copy_ceiling(torch, gb, wl.stream)
     log(f"[bench] copy ceiling: {ceiling}")
-    mem_ceiling = memory_ceiling()
+    mem_ceiling = {} if args.no_memory_ceiling else memory_ceiling()
     log(f"[bench] memory ceiling: {mem_ceiling}")
 
     extra = {}
