@@ -1132,12 +1132,33 @@ def cpu_baseline(wl, budget):
 OTHER_WORKLOADS = ("two_rank_4mib", "two_island_sweep", "gradients_64mib", "gradients_256mib")
 
 
+def graph_kernel_ms(torch, stream, fn, launches, calls=16, reps=5):
+    """Milliseconds per launch of the dominant kernel with the host out of
+    the way: `calls` calls of fn captured in one HIP graph, the graph
+    replayed `reps` times back to back.  Each launch still pays the GPU's
+    own boundary between kernels on one stream (about 1.6 us)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = time_region(torch, stream, g.replay, reps) / (reps * calls * launches)
+    del g
+    return ms
+
+
 def workload_summary(gb, torch, args, name, reps):
     """One of the smaller workloads, timed as its own --workload run times it
     but with fewer repetitions: the step's GB/s, its dominant kernel's GB/s
     and fraction of the HBM peak, the p10/p50/p90 of single steps with the
     last-level cache flushed, the workload's extras, and the oracle on the
-    first pieces of its CPU sample (compared with the GPU's outputs)."""
+    first pieces of its CPU sample (compared with the GPU's outputs).  The
+    dominant kernel is timed twice: called from Python back to back (a short
+    kernel is then bound by the host's launch rate) and replayed from a HIP
+    graph."""
     a = argparse.Namespace(**vars(args))
     a.workload, a.shard, a.dtype, a.op, a.codec, a.scale_mode = name, 1, "f32", "sum", "fp8", 0
     wl = WORKLOADS[name](gb, torch, a)
@@ -1148,6 +1169,7 @@ def workload_summary(gb, torch, args, name, reps):
     ms = time_region(torch, wl.stream, wl.step, reps) / reps
     kname, kbytes, klaunches, kfn = wl.timed_kernel()
     kms = time_region(torch, wl.stream, kfn, reps) / (reps * klaunches)
+    gms = graph_kernel_ms(torch, wl.stream, kfn, klaunches)
     dist = step_distribution(torch, wl.stream, wl.step, reps)
     extra = wl.extra(lambda fn, r: time_region(torch, wl.stream, fn, r), reps) if hasattr(wl, "extra") else {}
     torch.cuda.synchronize()
@@ -1159,6 +1181,9 @@ def workload_summary(gb, torch, args, name, reps):
            "dominant_kernel": kname, "kernel_us_per_launch": round(kms * 1e3, 3),
            "kernel_gbs": round(kbytes / (kms * 1e-3) / 1e9, 1),
            "kernel_frac": round(kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernel_us_per_launch_graph": round(gms * 1e3, 3),
+           "kernel_graph_gbs": round(kbytes / (gms * 1e-3) / 1e9, 1),
+           "kernel_graph_frac": round(kbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "step_p50_ms_cache_flushed": dist["p50_ms"],
            "step_gbs_cache_flushed_p50": round(sb / (dist["p50_ms"] * 1e-3) / 1e9, 1),
            "step_distribution": dist, "oracle_sample": describe(len(units)),
@@ -1190,7 +1215,9 @@ def memory_ceiling(gib=4, reps=10):
     with the library) run as a child process: median GB/s of plain copies
     (1, 2 and 4 vectors per lane; index order or 8 fronts; through LDS with
     global_load_lds_dwordx4), read-only and write-only streams, and a
-    memory-only replica of the fused fp8 pass, on `gib`-GiB buffers."""
+    memory-only replica of the fused fp8 pass, on `gib`-GiB buffers; and the
+    median microseconds per launch of an empty kernel (1, 1,600 and 25,600
+    workgroups) launched back to back from a stream and from a graph."""
     import subprocess
     prog = os.path.join(ROOT, "gradient_all_reduce_amd", "gb_ceiling")
     if not os.path.exists(prog):
@@ -1201,11 +1228,12 @@ def memory_ceiling(gib=4, reps=10):
         return {"error": "gb_ceiling timed out"}
     if r.returncode != 0:
         return {"error": f"gb_ceiling exited with {r.returncode}: {r.stderr.strip()[-300:]}"}
-    res = json.loads(r.stdout.strip().splitlines()[-1])
+    last = json.loads(r.stdout.strip().splitlines()[-1])
+    res = last["median_gbs"]
     copies = {k: v for k, v in res.items() if k.startswith("copy")}
     best = max(copies, key=copies.get)
     return {"command": f"gradient_all_reduce_amd/gb_ceiling {gib} {reps}", "median_gbs": res,
-            "best_copy": best, "best_copy_gbs": copies[best]}
+            "best_copy": best, "best_copy_gbs": copies[best], "empty_launch_us": last["launch_us"]}
 
 
 def replica_frac(achieved, mem_ceiling, wl):

@@ -18,15 +18,21 @@
 //             float32 sources read, 4 code streams, 4 scale streams and the
 //             float32 total written, in the pass's lane map, workgroup order
 //             and occupancy cap.
+// Then the fixed cost of a launch itself: 153 launches, back to back on one
+// stream, of a kernel whose body does nothing, from the stream and replayed
+// from a HIP graph, for grids of 1 workgroup, of the 1,600 of one 6,553,600-
+// value bucket, and of 25,600.
 // Each line of output is one variant: its bytes per launch and the median
-// and best GB/s over timed launches (hipEvents); the last line is one JSON
-// object of the medians.  Usage: gb_ceiling [size_gib] [reps].
+// and best GB/s over timed launches (hipEvents), or the median microseconds
+// per launch; the last line is one JSON object: {"median_gbs": {...},
+// "launch_us": {...}}.  Usage: gb_ceiling [size_gib] [reps].
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "gb_device.h"
@@ -89,6 +95,11 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const f4* __restrict__ s
 #pragma unroll
   for (int u = 0; u < U; u++) a += (v[u].x + v[u].y) + (v[u].z + v[u].w);
   if (a == -1.25f) sink[0] = a;  // never true for the zeros read here
+}
+
+// Stores only if the grid has more lanes than it can (never).
+__global__ __launch_bounds__(kThreads) void empty_kernel(float* sink) {
+  if (threadIdx.x >= kThreads) sink[0] = 1.0f;
 }
 
 __global__ __launch_bounds__(kThreads) void write_kernel(f4* __restrict__ dst, float value) {
@@ -162,6 +173,56 @@ void measure(const std::string& name, double bytes, int reps, F launch) {
   CK(hipEventDestroy(b));
 }
 
+std::vector<std::pair<std::string, double>> g_launch_us;
+
+// Median microseconds per launch of `count` empty launches of `grid`
+// workgroups on `s`, issued one by one (graph = false) or replayed from one
+// captured graph.
+void launch_cost(hipStream_t s, float* sink, unsigned grid, bool graph, int reps) {
+  constexpr int count = 153;
+  hipGraphExec_t exec = nullptr;
+  if (graph) {
+    hipGraph_t g;
+    CK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    for (int i = 0; i < count; i++) empty_kernel<<<grid, kThreads, 0, s>>>(sink);
+    CK(hipStreamEndCapture(s, &g));
+    CK(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0));
+    CK(hipGraphDestroy(g));
+  }
+  auto launch = [&] {
+    if (graph) CK(hipGraphLaunch(exec, s));
+    else
+      for (int i = 0; i < count; i++) empty_kernel<<<grid, kThreads, 0, s>>>(sink);
+  };
+  hipEvent_t a, b;
+  CK(hipEventCreate(&a));
+  CK(hipEventCreate(&b));
+  launch();
+  launch();
+  CK(hipGetLastError());
+  CK(hipStreamSynchronize(s));
+  std::vector<float> ms;
+  for (int i = 0; i < reps; i++) {
+    CK(hipEventRecord(a, s));
+    launch();
+    CK(hipEventRecord(b, s));
+    CK(hipEventSynchronize(b));
+    float t = 0.0f;
+    CK(hipEventElapsedTime(&t, a, b));
+    ms.push_back(t);
+  }
+  CK(hipGetLastError());
+  std::sort(ms.begin(), ms.end());
+  const double us = ms[ms.size() / 2] * 1e3 / count;
+  const std::string name = std::string(graph ? "graph_" : "stream_") + std::to_string(grid) + "wg";
+  g_launch_us.emplace_back(name, us);
+  std::printf("launch %-21s %8.2f us per launch (median of %d x %d)\n", name.c_str(), us, reps, count);
+  std::fflush(stdout);
+  CK(hipEventDestroy(a));
+  CK(hipEventDestroy(b));
+  if (exec) CK(hipGraphExecDestroy(exec));
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -212,11 +273,23 @@ int main(int argc, char** argv) {
   measure("fused_fp8_replica_" + sz, replica_bytes, reps,
           [&] { replica_kernel<<<nblk / gb::kBlocksPerGroup, kThreads, gb::kTwoPerCuLds>>>(st, ct, sct, reinterpret_cast<float*>(buf[4])); });
 
-  std::printf("{");
+  hipStream_t s;
+  CK(hipStreamCreate(&s));
+  for (unsigned grid : {1u, 1600u, 25600u}) {
+    launch_cost(s, sink, grid, false, reps);
+    launch_cost(s, sink, grid, true, reps);
+  }
+  CK(hipStreamDestroy(s));
+
+  std::printf("{\"median_gbs\": {");
   for (size_t i = 0; i < g_results.size(); i++) {
     std::printf("%s\"%s\": %.1f", i ? ", " : "", g_results[i].name.c_str(), g_results[i].med_gbs);
   }
-  std::printf("}\n");
+  std::printf("}, \"launch_us\": {");
+  for (size_t i = 0; i < g_launch_us.size(); i++) {
+    std::printf("%s\"%s\": %.2f", i ? ", " : "", g_launch_us[i].first.c_str(), g_launch_us[i].second);
+  }
+  std::printf("}}\n");
   for (auto& p : buf) CK(hipFree(p));
   CK(hipFree(codes));
   CK(hipFree(scales));
