@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -425,361 +426,374 @@ size_t gb_bucket_workspace_bytes(int codec, int k, size_t n, size_t bucket_elems
 }
 
 gb_status gb_reduce_sum(float* dst, const float* const* srcs, int k, size_t n, void* stream) {
-  const char* fn = "gb_reduce_sum";
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
-  if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
-  if ((s = check_sum_overlaps(fn, dst, sp, k, 4 * n)) != GB_OK) return s;
-  return from_hip(sum_groups(dst, sp, k, n, false, as_stream(stream)), fn);
+  return gb::traced_call("gb_reduce_sum", stream, k, n, -1, [&](const char* fn) -> gb_status {
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+    const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+    if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+    if ((s = check_sum_overlaps(fn, dst, sp, k, 4 * n)) != GB_OK) return s;
+    return from_hip(sum_groups(dst, sp, k, n, false, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_reduce(float* dst, const float* const* srcs, int k, size_t n, int op, int divisor, void* stream) {
-  const char* fn = "gb_reduce";
-  if (op != GB_OP_SUM && op != GB_OP_AVG && op != GB_OP_MAX && op != GB_OP_MIN) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: unknown op %d", fn, op);
-  }
-  if (op == GB_OP_AVG && (divisor < 1 || divisor > (1 << 24))) {
-    return fail(GB_ERR_INVALID_ARG, "%s: AVG divisor %d is outside 1..2^24", fn, divisor);
-  }
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
-  if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
-  if ((s = check_sum_overlaps(fn, dst, sp, k, 4 * n)) != GB_OK) return s;
-  return from_hip(op_groups(dst, sp, k, n, GB_DTYPE_F32, op, divisor, as_stream(stream)), fn);
+  return gb::traced_call("gb_reduce", stream, k, n, -1, [&](const char* fn) -> gb_status {
+    if (op != GB_OP_SUM && op != GB_OP_AVG && op != GB_OP_MAX && op != GB_OP_MIN) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: unknown op %d", fn, op);
+    }
+    if (op == GB_OP_AVG && (divisor < 1 || divisor > (1 << 24))) {
+      return fail(GB_ERR_INVALID_ARG, "%s: AVG divisor %d is outside 1..2^24", fn, divisor);
+    }
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+    const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+    if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+    if ((s = check_sum_overlaps(fn, dst, sp, k, 4 * n)) != GB_OK) return s;
+    return from_hip(op_groups(dst, sp, k, n, GB_DTYPE_F32, op, divisor, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_reduce_typed(void* dst, const void* const* srcs, int k, size_t n, int dtype, int op, int divisor,
                           void* stream) {
-  const char* fn = "gb_reduce_typed";
-  if (dtype < GB_DTYPE_F32 || dtype > GB_DTYPE_I64) return fail(GB_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
-  if (op != GB_OP_SUM && op != GB_OP_AVG && op != GB_OP_MAX && op != GB_OP_MIN) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: unknown op %d", fn, op);
-  }
-  if (op == GB_OP_AVG && dtype >= GB_DTYPE_I8) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: AVG needs a floating-point dtype", fn);
-  }
-  if (op == GB_OP_AVG && (divisor < 1 || divisor > (1 << 24))) {
-    return fail(GB_ERR_INVALID_ARG, "%s: AVG divisor %d is outside 1..2^24", fn, divisor);
-  }
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
-  if ((s = check_sum_overlaps(fn, dst, srcs, k, dtype_size(dtype) * n)) != GB_OK) return s;
-  return from_hip(op_groups(dst, srcs, k, n, dtype, op, divisor, as_stream(stream)), fn);
+  return gb::traced_call("gb_reduce_typed", stream, k, n, -1, [&](const char* fn) -> gb_status {
+    if (dtype < GB_DTYPE_F32 || dtype > GB_DTYPE_I64) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    }
+    if (op != GB_OP_SUM && op != GB_OP_AVG && op != GB_OP_MAX && op != GB_OP_MIN) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: unknown op %d", fn, op);
+    }
+    if (op == GB_OP_AVG && dtype >= GB_DTYPE_I8) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: AVG needs a floating-point dtype", fn);
+    }
+    if (op == GB_OP_AVG && (divisor < 1 || divisor > (1 << 24))) {
+      return fail(GB_ERR_INVALID_ARG, "%s: AVG divisor %d is outside 1..2^24", fn, divisor);
+    }
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+    if ((s = check_table(srcs, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+    if ((s = check_sum_overlaps(fn, dst, srcs, k, dtype_size(dtype) * n)) != GB_OK) return s;
+    return from_hip(op_groups(dst, srcs, k, n, dtype, op, divisor, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_encode_bf16(uint16_t* codes, const float* src, size_t n, void* stream) {
-  const char* fn = "gb_encode_bf16";
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_encode_overlaps(fn, codes, 2 * n, nullptr, 0, nullptr, n, src, 4 * n)) != GB_OK) return s;
-  return from_hip(gb::launch_encode_bf16(codes, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
+  return gb::traced_call("gb_encode_bf16", stream, -1, n, -1, [&](const char* fn) -> gb_status {
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_encode_overlaps(fn, codes, 2 * n, nullptr, 0, nullptr, n, src, 4 * n)) != GB_OK) return s;
+    return from_hip(gb::launch_encode_bf16(codes, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_encode_fp8_e4m3_blockscaled(uint8_t* codes, float* scales, const float* src, size_t n,
                                          int scale_mode, void* stream) {
-  const char* fn = "gb_encode_fp8_e4m3_blockscaled";
-  if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_encode_overlaps(fn, codes, n, scales, 4 * nblocks(n), nullptr, n, src, 4 * n)) != GB_OK) return s;
-  return from_hip(gb::launch_encode_fp8(codes, scales, src, n, scale_mode, GB_DTYPE_F32, as_stream(stream)), fn);
+  return gb::traced_call("gb_encode_fp8_e4m3_blockscaled", stream, -1, n, -1, [&](const char* fn) -> gb_status {
+    if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_encode_overlaps(fn, codes, n, scales, 4 * nblocks(n), nullptr, n, src, 4 * n)) != GB_OK) return s;
+    return from_hip(gb::launch_encode_fp8(codes, scales, src, n, scale_mode, GB_DTYPE_F32, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_decode_accumulate(float* acc, const void* const* codes, const float* const* scales, int k,
                                size_t n, int codec, int accumulate, void* stream) {
-  const char* fn = "gb_decode_accumulate";
-  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (accumulate != 0 && accumulate != 1) {
-    return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
-  }
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
-  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if (codec == GB_CODEC_FP8_E4M3_B256 &&
-      (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
-    return s;
-  }
-  if ((s = check_decode_overlaps(fn, acc, 4 * n, codes, codec == GB_CODEC_FP8_E4M3_B256 ? scales : nullptr, k,
-                                 code_bytes(codec, n), 4 * nblocks(n))) != GB_OK) {
-    return s;
-  }
-  return from_hip(decode_groups(acc, codes, scales, k, n, codec, accumulate != 0, GB_DTYPE_F32, as_stream(stream)),
-                  fn);
+  return gb::traced_call("gb_decode_accumulate", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (accumulate != 0 && accumulate != 1) {
+      return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
+    }
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
+    if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if (codec == GB_CODEC_FP8_E4M3_B256 &&
+        (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
+      return s;
+    }
+    if ((s = check_decode_overlaps(fn, acc, 4 * n, codes, codec == GB_CODEC_FP8_E4M3_B256 ? scales : nullptr, k,
+                                   code_bytes(codec, n), 4 * nblocks(n))) != GB_OK) {
+      return s;
+    }
+    return from_hip(decode_groups(acc, codes, scales, k, n, codec, accumulate != 0, GB_DTYPE_F32, as_stream(stream)),
+                    fn);
+  });
 }
 
 gb_status gb_encode(int codec, int dtype, void* codes, float* scales, const void* src, size_t n, int scale_mode,
                     void* stream) {
-  const char* fn = "gb_encode";
-  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
-  }
-  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
-  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
-  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_encode_overlaps(fn, codes, code_bytes(codec, n), fp8 ? scales : nullptr, 4 * nblocks(n), nullptr, n,
-                                 src, dtype_size(dtype) * n)) != GB_OK) {
-    return s;
-  }
-  hipStream_t st = as_stream(stream);
-  if (fp8) {
-    return from_hip(gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, src, n, scale_mode, dtype, st), fn);
-  }
-  return from_hip(gb::launch_encode_bf16(static_cast<uint16_t*>(codes), src, n, dtype, st), fn);
+  return gb::traced_call("gb_encode", stream, -1, n, codec, [&](const char* fn) -> gb_status {
+    if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+    }
+    if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+    const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+    if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_encode_overlaps(fn, codes, code_bytes(codec, n), fp8 ? scales : nullptr, 4 * nblocks(n), nullptr, n,
+                                   src, dtype_size(dtype) * n)) != GB_OK) {
+      return s;
+    }
+    hipStream_t st = as_stream(stream);
+    if (fp8) {
+      return from_hip(gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, src, n, scale_mode, dtype, st), fn);
+    }
+    return from_hip(gb::launch_encode_bf16(static_cast<uint16_t*>(codes), src, n, dtype, st), fn);
+  });
 }
 
 gb_status gb_decode_sum(int dtype, void* dst, const void* const* codes, const float* const* scales, int k,
                         size_t n, int codec, void* stream) {
-  const char* fn = "gb_decode_sum";
-  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
-  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
-  if (codec == GB_CODEC_NONE && dtype != GB_DTYPE_F32) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: uncompressed payloads are float32; reduce other types exactly with "
-                "gb_reduce_typed", fn);
-  }
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (k > kR && dtype != GB_DTYPE_F32) {
-    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a %s total is rounded once from float32, which holds up to %d "
-                "payloads per call; sum more into a float32 buffer", fn, k, "non-float32", kR);
-  }
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
-  if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if (codec == GB_CODEC_FP8_E4M3_B256 &&
-      (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
-    return s;
-  }
-  if ((s = check_decode_overlaps(fn, dst, dtype_size(dtype) * n, codes,
-                                 codec == GB_CODEC_FP8_E4M3_B256 ? scales : nullptr, k, code_bytes(codec, n),
-                                 4 * nblocks(n))) != GB_OK) {
-    return s;
-  }
-  return from_hip(decode_groups(dst, codes, scales, k, n, codec, false, dtype, as_stream(stream)), fn);
+  return gb::traced_call("gb_decode_sum", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+    if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+    if (codec == GB_CODEC_NONE && dtype != GB_DTYPE_F32) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: uncompressed payloads are float32; reduce other types exactly with "
+                  "gb_reduce_typed", fn);
+    }
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (k > kR && dtype != GB_DTYPE_F32) {
+      return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a %s total is rounded once from float32, which holds up to %d "
+                  "payloads per call; sum more into a float32 buffer", fn, k, "non-float32", kR);
+    }
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    if ((s = check_array(dst, GB_ALIGN, fn, "dst")) != GB_OK) return s;
+    if ((s = check_table(codes, k, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if (codec == GB_CODEC_FP8_E4M3_B256 &&
+        (s = check_table(reinterpret_cast<const void* const*>(scales), k, 4, fn, "scales")) != GB_OK) {
+      return s;
+    }
+    if ((s = check_decode_overlaps(fn, dst, dtype_size(dtype) * n, codes,
+                                   codec == GB_CODEC_FP8_E4M3_B256 ? scales : nullptr, k, code_bytes(codec, n),
+                                   4 * nblocks(n))) != GB_OK) {
+      return s;
+    }
+    return from_hip(decode_groups(dst, codes, scales, k, n, codec, false, dtype, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_reduce_encode(float* sum, void* codes, float* scales, const float* const* srcs, int k, size_t n,
                            int codec, int scale_mode, void* stream) {
-  const char* fn = "gb_reduce_encode";
-  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
-  }
-  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
-  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (k > kR && sum == nullptr) {
-    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: more than %d sources are summed into sum first, which is NULL", fn,
-                k, kR);
-  }
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
-  if (sum != nullptr && (s = check_array(sum, GB_ALIGN, fn, "sum")) != GB_OK) return s;
-  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
-  if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
-  {
-    Spans outs, ins;
-    outs.add(sum, 4 * n, "sum");
-    outs.add(codes, code_bytes(codec, n), "codes");
-    if (fp8) outs.add(scales, 4 * nblocks(n), "scales");
-    for (int r = 0; r < k; r++) ins.add_input(sp[r], 4 * n, r == 0 ? sum : nullptr, "srcs", r);
-    if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
-  }
-  hipStream_t st = as_stream(stream);
-  hipError_t e;
-  if (k <= kR) {
-    const gb::PtrTable t = slice(sp, 0, k);
-    e = fp8 ? gb::launch_reduce_encode_fp8(sum, static_cast<uint8_t*>(codes), scales, t, k, n, scale_mode, st)
-            : gb::launch_reduce_encode_bf16(sum, static_cast<uint16_t*>(codes), t, k, n, st);
-  } else {
-    // the rank-order sum first (further launches continue the fold), then its payload
-    e = sum_groups(sum, sp, k, n, false, st);
-    if (e == hipSuccess) {
-      e = fp8 ? gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, sum, n, scale_mode, GB_DTYPE_F32, st)
-              : gb::launch_encode_bf16(static_cast<uint16_t*>(codes), sum, n, GB_DTYPE_F32, st);
+  return gb::traced_call("gb_reduce_encode", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
     }
-  }
-  return from_hip(e, fn);
+    const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+    if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (k > kR && sum == nullptr) {
+      return fail(GB_ERR_INVALID_ARG, "%s: k = %d: more than %d sources are summed into sum first, which is NULL", fn,
+                  k, kR);
+    }
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+    if (sum != nullptr && (s = check_array(sum, GB_ALIGN, fn, "sum")) != GB_OK) return s;
+    const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+    if ((s = check_table(sp, k, GB_ALIGN, fn, "srcs")) != GB_OK) return s;
+    {
+      Spans outs, ins;
+      outs.add(sum, 4 * n, "sum");
+      outs.add(codes, code_bytes(codec, n), "codes");
+      if (fp8) outs.add(scales, 4 * nblocks(n), "scales");
+      for (int r = 0; r < k; r++) ins.add_input(sp[r], 4 * n, r == 0 ? sum : nullptr, "srcs", r);
+      if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
+    }
+    hipStream_t st = as_stream(stream);
+    hipError_t e;
+    if (k <= kR) {
+      const gb::PtrTable t = slice(sp, 0, k);
+      e = fp8 ? gb::launch_reduce_encode_fp8(sum, static_cast<uint8_t*>(codes), scales, t, k, n, scale_mode, st)
+              : gb::launch_reduce_encode_bf16(sum, static_cast<uint16_t*>(codes), t, k, n, st);
+    } else {
+      // the rank-order sum first (further launches continue the fold), then its payload
+      e = sum_groups(sum, sp, k, n, false, st);
+      if (e == hipSuccess) {
+        e = fp8 ? gb::launch_encode_fp8(static_cast<uint8_t*>(codes), scales, sum, n, scale_mode, GB_DTYPE_F32, st)
+                : gb::launch_encode_bf16(static_cast<uint16_t*>(codes), sum, n, GB_DTYPE_F32, st);
+      }
+    }
+    return from_hip(e, fn);
+  });
 }
 
 gb_status gb_encode_staged(int codec, int scale_mode, void* codes_dev, float* scales_dev, void* codes_host,
                            float* scales_host, const float* src, size_t n, size_t chunk_elems, void* stream) {
-  const char* fn = "gb_encode_staged";
-  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
-  }
-  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
-  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
-  if (chunk_elems == 0 || chunk_elems % GB_BLOCK != 0) {
-    return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
-                GB_BLOCK);
-  }
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_array(codes_dev, GB_ALIGN, fn, "codes_dev")) != GB_OK) return s;
-  if ((s = check_pinned(codes_host, 4, fn, "codes_host")) != GB_OK) return s;
-  if (fp8) {
-    if ((s = check_array(scales_dev, 4, fn, "scales_dev")) != GB_OK) return s;
-    if ((s = check_pinned(scales_host, 4, fn, "scales_host")) != GB_OK) return s;
-  }
-  {
-    Spans outs, ins;
-    const size_t cbytes = code_bytes(codec, n), sbytes = fp8 ? 4 * nblocks(n) : 0;
-    outs.add(codes_dev, cbytes, "codes_dev");
-    outs.add(codes_host, cbytes, "codes_host");
-    outs.add(fp8 ? scales_dev : nullptr, sbytes, "scales_dev");
-    outs.add(fp8 ? scales_host : nullptr, sbytes, "scales_host");
-    ins.add(src, 4 * n, "src");
-    if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
-  }
-  StagingContext* c;
-  if ((s = staging_context(fn, &c)) != GB_OK) return s;
-  std::lock_guard<std::mutex> lock(c->mu);
-  if ((s = staging_ready(fn, c)) != GB_OK) return s;
-  hipStream_t st = as_stream(stream);
-  const size_t cb = code_size(codec);
-  char* cd = static_cast<char*>(codes_dev);
-  char* ch = static_cast<char*>(codes_host);
-  hipError_t e = hipSuccess;
-  size_t chunk = 0;
-  for (size_t o = 0, l = 0; o < n && e == hipSuccess; o += l, chunk++) {
-    l = n - o < chunk_elems ? n - o : chunk_elems;
-    hipStream_t cs = c->copy[chunk % kCopyStreams];
-    e = fp8 ? gb::launch_encode_fp8(reinterpret_cast<uint8_t*>(cd + o), scales_dev + o / GB_BLOCK, src + o, l,
-                                    scale_mode, GB_DTYPE_F32, st)
-            : gb::launch_encode_bf16(reinterpret_cast<uint16_t*>(cd + 2 * o), src + o, l, GB_DTYPE_F32, st);
-    if (e == hipSuccess) e = hipEventRecord(c->ev_compute, st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(cs, c->ev_compute, 0);
-    if (e == hipSuccess) e = hipMemcpyAsync(ch + cb * o, cd + cb * o, cb * l, hipMemcpyDeviceToHost, cs);
-  }
-  // the scales (4 bytes per 256 values) go in one copy once all are written
-  if (e == hipSuccess && fp8) {
-    const size_t cs_last = (chunk - 1) % kCopyStreams;
-    e = hipMemcpyAsync(scales_host, scales_dev, 4 * ((n + GB_BLOCK - 1) / GB_BLOCK), hipMemcpyDeviceToHost,
-                       c->copy[cs_last]);
-  }
-  for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) {
-    e = hipEventRecord(c->ev_copy[i], c->copy[i]);
-    if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[i], 0);
-  }
-  return from_hip(e, fn);
+  return gb::traced_call("gb_encode_staged", stream, -1, n, codec, [&](const char* fn) -> gb_status {
+    if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+    }
+    const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+    if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+    if (chunk_elems == 0 || chunk_elems % GB_BLOCK != 0) {
+      return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
+                  GB_BLOCK);
+    }
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_array(codes_dev, GB_ALIGN, fn, "codes_dev")) != GB_OK) return s;
+    if ((s = check_pinned(codes_host, 4, fn, "codes_host")) != GB_OK) return s;
+    if (fp8) {
+      if ((s = check_array(scales_dev, 4, fn, "scales_dev")) != GB_OK) return s;
+      if ((s = check_pinned(scales_host, 4, fn, "scales_host")) != GB_OK) return s;
+    }
+    {
+      Spans outs, ins;
+      const size_t cbytes = code_bytes(codec, n), sbytes = fp8 ? 4 * nblocks(n) : 0;
+      outs.add(codes_dev, cbytes, "codes_dev");
+      outs.add(codes_host, cbytes, "codes_host");
+      outs.add(fp8 ? scales_dev : nullptr, sbytes, "scales_dev");
+      outs.add(fp8 ? scales_host : nullptr, sbytes, "scales_host");
+      ins.add(src, 4 * n, "src");
+      if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
+    }
+    StagingContext* c;
+    if ((s = staging_context(fn, &c)) != GB_OK) return s;
+    std::lock_guard<std::mutex> lock(c->mu);
+    if ((s = staging_ready(fn, c)) != GB_OK) return s;
+    hipStream_t st = as_stream(stream);
+    const size_t cb = code_size(codec);
+    char* cd = static_cast<char*>(codes_dev);
+    char* ch = static_cast<char*>(codes_host);
+    hipError_t e = hipSuccess;
+    size_t chunk = 0;
+    for (size_t o = 0, l = 0; o < n && e == hipSuccess; o += l, chunk++) {
+      l = n - o < chunk_elems ? n - o : chunk_elems;
+      hipStream_t cs = c->copy[chunk % kCopyStreams];
+      e = fp8 ? gb::launch_encode_fp8(reinterpret_cast<uint8_t*>(cd + o), scales_dev + o / GB_BLOCK, src + o, l,
+                                      scale_mode, GB_DTYPE_F32, st)
+              : gb::launch_encode_bf16(reinterpret_cast<uint16_t*>(cd + 2 * o), src + o, l, GB_DTYPE_F32, st);
+      if (e == hipSuccess) e = hipEventRecord(c->ev_compute, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(cs, c->ev_compute, 0);
+      if (e == hipSuccess) e = hipMemcpyAsync(ch + cb * o, cd + cb * o, cb * l, hipMemcpyDeviceToHost, cs);
+    }
+    // the scales (4 bytes per 256 values) go in one copy once all are written
+    if (e == hipSuccess && fp8) {
+      const size_t cs_last = (chunk - 1) % kCopyStreams;
+      e = hipMemcpyAsync(scales_host, scales_dev, 4 * ((n + GB_BLOCK - 1) / GB_BLOCK), hipMemcpyDeviceToHost,
+                         c->copy[cs_last]);
+    }
+    for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) {
+      e = hipEventRecord(c->ev_copy[i], c->copy[i]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[i], 0);
+    }
+    return from_hip(e, fn);
+  });
 }
 
 gb_status gb_decode_accumulate_staged(float* acc, const void* const* codes_host, const float* const* scales_host,
                                       void* const* codes_dev, float* const* scales_dev, int k, size_t n,
                                       size_t chunk_elems, int codec, int accumulate, void* stream) {
-  const char* fn = "gb_decode_accumulate_staged";
-  if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
-  gb_status s = check_k(k, fn);
-  if (s != GB_OK) return s;
-  if (accumulate != 0 && accumulate != 1) {
-    return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
-  }
-  if (chunk_elems == 0 || chunk_elems % GB_BLOCK != 0) {
-    return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
-                GB_BLOCK);
-  }
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
-  if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
-  if (codes_host == nullptr || codes_dev == nullptr || (fp8 && (scales_host == nullptr || scales_dev == nullptr))) {
-    return fail(GB_ERR_INVALID_ARG, "%s: a pointer array is NULL", fn);
-  }
-  for (int r = 0; r < k; r++) {
-    char name[32];
-    std::snprintf(name, sizeof name, "codes_host[%d]", r);
-    if ((s = check_pinned(codes_host[r], 4, fn, name)) != GB_OK) return s;
-    std::snprintf(name, sizeof name, "codes_dev[%d]", r);
-    if ((s = check_array(codes_dev[r], GB_ALIGN, fn, name)) != GB_OK) return s;
-    if (fp8) {
-      std::snprintf(name, sizeof name, "scales_host[%d]", r);
-      if ((s = check_pinned(scales_host[r], 4, fn, name)) != GB_OK) return s;
-      std::snprintf(name, sizeof name, "scales_dev[%d]", r);
-      if ((s = check_array(scales_dev[r], 4, fn, name)) != GB_OK) return s;
+  return gb::traced_call("gb_decode_accumulate_staged", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (!known_codec(codec)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown codec %d", fn, codec);
+    gb_status s = check_k(k, fn);
+    if (s != GB_OK) return s;
+    if (accumulate != 0 && accumulate != 1) {
+      return fail(GB_ERR_INVALID_ARG, "%s: accumulate = %d is not 0 or 1", fn, accumulate);
     }
-  }
-  {
-    Spans outs, ins;
-    const size_t cbytes = code_bytes(codec, n), sbytes = 4 * nblocks(n);
-    outs.add(acc, 4 * n, "acc");
+    if (chunk_elems == 0 || chunk_elems % GB_BLOCK != 0) {
+      return fail(GB_ERR_INVALID_ARG, "%s: chunk_elems = %zu is not a positive multiple of %d", fn, chunk_elems,
+                  GB_BLOCK);
+    }
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+    if ((s = check_array(acc, GB_ALIGN, fn, "acc")) != GB_OK) return s;
+    if (codes_host == nullptr || codes_dev == nullptr || (fp8 && (scales_host == nullptr || scales_dev == nullptr))) {
+      return fail(GB_ERR_INVALID_ARG, "%s: a pointer array is NULL", fn);
+    }
     for (int r = 0; r < k; r++) {
-      outs.add(codes_dev[r], cbytes, "codes_dev", r);
-      ins.add(codes_host[r], cbytes, "codes_host", r);
+      char name[32];
+      std::snprintf(name, sizeof name, "codes_host[%d]", r);
+      if ((s = check_pinned(codes_host[r], 4, fn, name)) != GB_OK) return s;
+      std::snprintf(name, sizeof name, "codes_dev[%d]", r);
+      if ((s = check_array(codes_dev[r], GB_ALIGN, fn, name)) != GB_OK) return s;
       if (fp8) {
-        outs.add(scales_dev[r], sbytes, "scales_dev", r);
-        ins.add(scales_host[r], sbytes, "scales_host", r);
+        std::snprintf(name, sizeof name, "scales_host[%d]", r);
+        if ((s = check_pinned(scales_host[r], 4, fn, name)) != GB_OK) return s;
+        std::snprintf(name, sizeof name, "scales_dev[%d]", r);
+        if ((s = check_array(scales_dev[r], 4, fn, name)) != GB_OK) return s;
       }
     }
-    if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
-  }
-  StagingContext* c;
-  if ((s = staging_context(fn, &c)) != GB_OK) return s;
-  std::lock_guard<std::mutex> lock(c->mu);
-  if ((s = staging_ready(fn, c)) != GB_OK) return s;
-  hipStream_t st = as_stream(stream);
-  const size_t cb = code_size(codec);
-  // copies into the device staging buffers start after the caller's earlier
-  // work on `stream`, which may still read them
-  hipError_t e = hipEventRecord(c->ev_compute, st);
-  for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) e = hipStreamWaitEvent(c->copy[i], c->ev_compute, 0);
-  // every rank's scales (4 bytes per 256 values) first, in one copy each on
-  // the first copy stream, ahead of chunk 0, which the compute stream waits for
-  for (int r = 0; r < k && e == hipSuccess && fp8; r++) {
-    e = hipMemcpyAsync(scales_dev[r], scales_host[r], 4 * ((n + GB_BLOCK - 1) / GB_BLOCK), hipMemcpyHostToDevice,
-                       c->copy[0]);
-  }
-  size_t chunk = 0;
-  for (size_t o = 0, l = 0; o < n && e == hipSuccess; o += l, chunk++) {
-    l = n - o < chunk_elems ? n - o : chunk_elems;
-    const int ci = (int)(chunk % kCopyStreams);
-    const void* cp[GB_MAX_K];
-    const float* sp[GB_MAX_K];
-    for (int r = 0; r < k && e == hipSuccess; r++) {
-      char* dst = static_cast<char*>(codes_dev[r]) + cb * o;
-      e = hipMemcpyAsync(dst, static_cast<const char*>(codes_host[r]) + cb * o, cb * l, hipMemcpyHostToDevice,
-                         c->copy[ci]);
-      cp[r] = dst;
-      sp[r] = fp8 ? scales_dev[r] + o / GB_BLOCK : nullptr;
+    {
+      Spans outs, ins;
+      const size_t cbytes = code_bytes(codec, n), sbytes = 4 * nblocks(n);
+      outs.add(acc, 4 * n, "acc");
+      for (int r = 0; r < k; r++) {
+        outs.add(codes_dev[r], cbytes, "codes_dev", r);
+        ins.add(codes_host[r], cbytes, "codes_host", r);
+        if (fp8) {
+          outs.add(scales_dev[r], sbytes, "scales_dev", r);
+          ins.add(scales_host[r], sbytes, "scales_host", r);
+        }
+      }
+      if ((s = check_disjoint(fn, outs, ins)) != GB_OK) return s;
     }
-    if (e == hipSuccess) e = hipEventRecord(c->ev_copy[ci], c->copy[ci]);
-    if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[ci], 0);
-    if (e != hipSuccess) break;
-    e = decode_groups(acc + o, cp, sp, k, l, codec, accumulate != 0, GB_DTYPE_F32, st);
-  }
-  return from_hip(e, fn);
+    StagingContext* c;
+    if ((s = staging_context(fn, &c)) != GB_OK) return s;
+    std::lock_guard<std::mutex> lock(c->mu);
+    if ((s = staging_ready(fn, c)) != GB_OK) return s;
+    hipStream_t st = as_stream(stream);
+    const size_t cb = code_size(codec);
+    // copies into the device staging buffers start after the caller's earlier
+    // work on `stream`, which may still read them
+    hipError_t e = hipEventRecord(c->ev_compute, st);
+    for (int i = 0; i < kCopyStreams && e == hipSuccess; i++) e = hipStreamWaitEvent(c->copy[i], c->ev_compute, 0);
+    // every rank's scales (4 bytes per 256 values) first, in one copy each on
+    // the first copy stream, ahead of chunk 0, which the compute stream waits for
+    for (int r = 0; r < k && e == hipSuccess && fp8; r++) {
+      e = hipMemcpyAsync(scales_dev[r], scales_host[r], 4 * ((n + GB_BLOCK - 1) / GB_BLOCK), hipMemcpyHostToDevice,
+                         c->copy[0]);
+    }
+    size_t chunk = 0;
+    for (size_t o = 0, l = 0; o < n && e == hipSuccess; o += l, chunk++) {
+      l = n - o < chunk_elems ? n - o : chunk_elems;
+      const int ci = (int)(chunk % kCopyStreams);
+      const void* cp[GB_MAX_K];
+      const float* sp[GB_MAX_K];
+      for (int r = 0; r < k && e == hipSuccess; r++) {
+        char* dst = static_cast<char*>(codes_dev[r]) + cb * o;
+        e = hipMemcpyAsync(dst, static_cast<const char*>(codes_host[r]) + cb * o, cb * l, hipMemcpyHostToDevice,
+                           c->copy[ci]);
+        cp[r] = dst;
+        sp[r] = fp8 ? scales_dev[r] + o / GB_BLOCK : nullptr;
+      }
+      if (e == hipSuccess) e = hipEventRecord(c->ev_copy[ci], c->copy[ci]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, c->ev_copy[ci], 0);
+      if (e != hipSuccess) break;
+      e = decode_groups(acc + o, cp, sp, k, l, codec, accumulate != 0, GB_DTYPE_F32, st);
+    }
+    return from_hip(e, fn);
+  });
 }
 
 }  // extern "C"
@@ -896,6 +910,59 @@ namespace gb {
 
 gb_status fail_status(gb_status s, const char* msg) { return fail(s, "%s", msg); }
 
+namespace {
+
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && *v != '\0' && std::strcmp(v, "0") != 0;
+}
+
+struct Hooks {
+  bool trace, debug;
+};
+
+const Hooks& hooks() {
+  static const Hooks h{env_on("GB_TRACE"), env_on("GB_DEBUG")};
+  return h;
+}
+
+}  // namespace
+
+bool call_hooks_on() {
+  const Hooks& h = hooks();
+  return h.trace || h.debug;
+}
+
+gb_status finish_call(const char* fn, void* stream, int k, size_t n, int codec, gb_status s, double host_us) {
+  const Hooks& h = hooks();
+  const char* note = "";
+  if (h.debug && s == GB_OK) {
+    const hipStream_t st = as_stream(stream);
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &capture);
+    if (e == hipSuccess && capture != hipStreamCaptureStatusNone) {
+      note = " (stream under capture: not waited for)";
+    } else {
+      if (e == hipSuccess) e = hipStreamSynchronize(st);
+      if (e != hipSuccess) {
+        s = fail(GB_ERR_HIP, "%s: GB_DEBUG: the stream reported HIP error %d (%s) after the call", fn, (int)e,
+                 hipGetErrorString(e));
+      }
+    }
+  }
+  if (h.trace) {
+    char args[96] = "";
+    int used = 0;
+    if (k >= 0) used += std::snprintf(args + used, sizeof args - used, " k=%d", k);
+    if (n != kNoSize) used += std::snprintf(args + used, sizeof args - used, " n=%zu", n);
+    if (codec >= 0) std::snprintf(args + used, sizeof args - used, " codec=%d", codec);
+    std::fprintf(stderr, "gbreduce: %s%s stream=%p -> %s%s%s%s (%.1f us on the host)\n", fn, args, stream,
+                 gb_status_string(s), s != GB_OK ? ": " : "", s != GB_OK ? g_last_error : "", note, host_us);
+    std::fflush(stderr);
+  }
+  return s;
+}
+
 gb_status bucket_allreduce_local(const char* fn, float* out, const float* const* srcs, int k, size_t n,
                                  size_t bucket_elems, int codec, int scale_mode, void* workspace,
                                  size_t workspace_bytes, void* stream) {
@@ -920,31 +987,35 @@ extern "C" {
 gb_status gb_bucket_allreduce_local(float* out, const float* const* srcs, int k, size_t n,
                                     size_t bucket_elems, int codec, int scale_mode, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  return gb::bucket_allreduce_local("gb_bucket_allreduce_local", out, srcs, k, n, bucket_elems, codec, scale_mode,
-                                    workspace, workspace_bytes, stream);
+  return gb::traced_call("gb_bucket_allreduce_local", stream, k, n, codec, [&](const char* fn) {
+    return gb::bucket_allreduce_local(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace,
+                                      workspace_bytes, stream);
+  });
 }
 
 gb_status gb_bucket_allreduce_local_typed(int dtype, void* out, const void* const* srcs, int k, size_t n,
                                           size_t bucket_elems, int codec, int scale_mode, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local_typed";
-  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
-  size_t cs, so, ss;
-  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
-                             &so, &ss);
-  if (s != GB_OK) return s;
-  if (k > kR && dtype != GB_DTYPE_F32 && codec != GB_CODEC_NONE) {
-    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
-                "which holds up to %d ranks per call", fn, k, kR);
-  }
-  if (n == 0) return GB_OK;
-  if ((s = check_bucket_overlaps(fn, out, srcs, nullptr, k, n, dtype_size(dtype), codec, workspace, cs, ss)) != GB_OK) {
-    return s;
-  }
-  char* ws = static_cast<char*>(workspace);
-  return from_hip(bucket_groups(out, srcs, nullptr, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
-                                as_stream(stream)),
-                  fn);
+  return gb::traced_call("gb_bucket_allreduce_local_typed", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+    size_t cs, so, ss;
+    gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                               &so, &ss);
+    if (s != GB_OK) return s;
+    if (k > kR && dtype != GB_DTYPE_F32 && codec != GB_CODEC_NONE) {
+      return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
+                  "which holds up to %d ranks per call", fn, k, kR);
+    }
+    if (n == 0) return GB_OK;
+    s = check_bucket_overlaps(fn, out, srcs, nullptr, k, n, dtype_size(dtype), codec, workspace, cs, ss);
+    if (s != GB_OK) {
+      return s;
+    }
+    char* ws = static_cast<char*>(workspace);
+    return from_hip(bucket_groups(out, srcs, nullptr, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
+                                  as_stream(stream)),
+                    fn);
+  });
 }
 
 }  // extern "C"
@@ -1152,128 +1223,136 @@ extern "C" {
 gb_status gb_bucket_allreduce_local_batch(int dtype, void* const* outs, const void* const* srcs, const size_t* ns,
                                           int nbuckets, int k, int codec, int scale_mode, int divisor,
                                           void* workspace, size_t workspace_bytes, void* stream) {
-  return bucket_batch("gb_bucket_allreduce_local_batch", dtype, outs, srcs, nullptr, ns, nbuckets, k, codec,
-                      scale_mode, divisor, workspace, workspace_bytes, stream);
+  return gb::traced_call("gb_bucket_allreduce_local_batch", stream, k, gb::kNoSize, codec, [&](const char* fn) {
+    return bucket_batch(fn, dtype, outs, srcs, nullptr, ns, nbuckets, k, codec, scale_mode, divisor, workspace,
+                        workspace_bytes, stream);
+  });
 }
 
 gb_status gb_bucket_allreduce_local_batch_ef(int dtype, void* const* outs, const void* const* srcs,
                                              float* const* residuals, const size_t* ns, int nbuckets, int k,
                                              int codec, int scale_mode, int divisor, void* workspace,
                                              size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local_batch_ef";
-  if (residuals == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: residuals is NULL", fn);
-  return bucket_batch(fn, dtype, outs, srcs, residuals, ns, nbuckets, k, codec, scale_mode, divisor, workspace,
-                      workspace_bytes, stream);
+  return gb::traced_call("gb_bucket_allreduce_local_batch_ef", stream, k, gb::kNoSize, codec, [&](const char* fn) {
+    if (residuals == nullptr) return fail(GB_ERR_INVALID_ARG, "%s: residuals is NULL", fn);
+    return bucket_batch(fn, dtype, outs, srcs, residuals, ns, nbuckets, k, codec, scale_mode, divisor, workspace,
+                        workspace_bytes, stream);
+  });
 }
 
 gb_status gb_encode_bf16_ef(uint16_t* codes, float* residual, const float* src, size_t n, void* stream) {
-  const char* fn = "gb_encode_bf16_ef";
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_encode_overlaps(fn, codes, 2 * n, nullptr, 0, residual, n, src, 4 * n)) != GB_OK) return s;
-  return from_hip(gb::launch_encode_bf16_ef(codes, residual, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
+  return gb::traced_call("gb_encode_bf16_ef", stream, -1, n, -1, [&](const char* fn) -> gb_status {
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_encode_overlaps(fn, codes, 2 * n, nullptr, 0, residual, n, src, 4 * n)) != GB_OK) return s;
+    return from_hip(gb::launch_encode_bf16_ef(codes, residual, src, n, GB_DTYPE_F32, as_stream(stream)), fn);
+  });
 }
 
 gb_status gb_encode_fp8_e4m3_blockscaled_ef(uint8_t* codes, float* scales, float* residual, const float* src,
                                             size_t n, int scale_mode, void* stream) {
-  const char* fn = "gb_encode_fp8_e4m3_blockscaled_ef";
-  if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
-  if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_encode_overlaps(fn, codes, n, scales, 4 * nblocks(n), residual, n, src, 4 * n)) != GB_OK) return s;
-  return from_hip(gb::launch_encode_fp8_ef(codes, scales, residual, src, n, scale_mode, GB_DTYPE_F32,
-                                           as_stream(stream)),
-                  fn);
+  return gb::traced_call("gb_encode_fp8_e4m3_blockscaled_ef", stream, -1, n, -1, [&](const char* fn) -> gb_status {
+    if (!known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if ((s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+    if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_encode_overlaps(fn, codes, n, scales, 4 * nblocks(n), residual, n, src, 4 * n)) != GB_OK) return s;
+    return from_hip(gb::launch_encode_fp8_ef(codes, scales, residual, src, n, scale_mode, GB_DTYPE_F32,
+                                             as_stream(stream)),
+                    fn);
+  });
 }
 
 gb_status gb_bucket_allreduce_local_ef(float* out, const float* const* srcs, float* const* residuals, int k,
                                        size_t n, size_t bucket_elems, int codec, int scale_mode, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local_ef";
-  if (codec == GB_CODEC_NONE) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
-  }
-  size_t cs, so, ss;
-  const void* const* sp = reinterpret_cast<const void* const*>(srcs);
-  gb_status s = check_bucket(fn, out, sp, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
-                             &so, &ss);
-  if (s != GB_OK || n == 0) return s;
-  if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
-    return s;
-  }
-  if ((s = check_bucket_overlaps(fn, out, sp, residuals, k, n, 4, codec, workspace, cs, ss)) != GB_OK) return s;
-  char* ws = static_cast<char*>(workspace);
-  return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32, ws, cs, ws + so, ss,
-                                as_stream(stream)),
-                  fn);
+  return gb::traced_call("gb_bucket_allreduce_local_ef", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (codec == GB_CODEC_NONE) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
+    }
+    size_t cs, so, ss;
+    const void* const* sp = reinterpret_cast<const void* const*>(srcs);
+    gb_status s = check_bucket(fn, out, sp, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                               &so, &ss);
+    if (s != GB_OK || n == 0) return s;
+    if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
+      return s;
+    }
+    if ((s = check_bucket_overlaps(fn, out, sp, residuals, k, n, 4, codec, workspace, cs, ss)) != GB_OK) return s;
+    char* ws = static_cast<char*>(workspace);
+    return from_hip(bucket_groups(out, sp, residuals, k, n, codec, scale_mode, GB_DTYPE_F32, ws, cs, ws + so, ss,
+                                  as_stream(stream)),
+                    fn);
+  });
 }
 
 gb_status gb_encode_ef(int codec, int dtype, void* codes, float* scales, float* residual, const void* src, size_t n,
                        int scale_mode, void* stream) {
-  const char* fn = "gb_encode_ef";
-  if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
-  }
-  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
-  const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
-  if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
-  if (n > GB_MAX_N) return check_n(n, fn);
-  if (n == 0) return GB_OK;
-  gb_status s;
-  if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
-  if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
-  if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
-  if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
-  if ((s = check_encode_overlaps(fn, codes, code_bytes(codec, n), fp8 ? scales : nullptr, 4 * nblocks(n), residual, n,
-                                 src, dtype_size(dtype) * n)) != GB_OK) {
-    return s;
-  }
-  hipStream_t st = as_stream(stream);
-  if (fp8) {
-    return from_hip(gb::launch_encode_fp8_ef(static_cast<uint8_t*>(codes), scales, residual, src, n, scale_mode,
-                                             dtype, st),
-                    fn);
-  }
-  return from_hip(gb::launch_encode_bf16_ef(static_cast<uint16_t*>(codes), residual, src, n, dtype, st), fn);
+  return gb::traced_call("gb_encode_ef", stream, -1, n, codec, [&](const char* fn) -> gb_status {
+    if (codec != GB_CODEC_BF16 && codec != GB_CODEC_FP8_E4M3_B256) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: codec %d is not bf16 or fp8", fn, codec);
+    }
+    if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+    const bool fp8 = codec == GB_CODEC_FP8_E4M3_B256;
+    if (fp8 && !known_mode(scale_mode)) return fail(GB_ERR_UNSUPPORTED, "%s: unknown scale mode %d", fn, scale_mode);
+    if (n > GB_MAX_N) return check_n(n, fn);
+    if (n == 0) return GB_OK;
+    gb_status s;
+    if ((s = check_array(codes, GB_ALIGN, fn, "codes")) != GB_OK) return s;
+    if (fp8 && (s = check_array(scales, 4, fn, "scales")) != GB_OK) return s;
+    if ((s = check_array(residual, GB_ALIGN, fn, "residual")) != GB_OK) return s;
+    if ((s = check_array(src, GB_ALIGN, fn, "src")) != GB_OK) return s;
+    if ((s = check_encode_overlaps(fn, codes, code_bytes(codec, n), fp8 ? scales : nullptr, 4 * nblocks(n), residual, n,
+                                   src, dtype_size(dtype) * n)) != GB_OK) {
+      return s;
+    }
+    hipStream_t st = as_stream(stream);
+    if (fp8) {
+      return from_hip(gb::launch_encode_fp8_ef(static_cast<uint8_t*>(codes), scales, residual, src, n, scale_mode,
+                                               dtype, st),
+                      fn);
+    }
+    return from_hip(gb::launch_encode_bf16_ef(static_cast<uint16_t*>(codes), residual, src, n, dtype, st), fn);
+  });
 }
 
 gb_status gb_bucket_allreduce_local_ef_typed(int dtype, void* out, const void* const* srcs, float* const* residuals,
                                              int k, size_t n, size_t bucket_elems, int codec, int scale_mode,
                                              void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "gb_bucket_allreduce_local_ef_typed";
-  if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
-  if (codec == GB_CODEC_NONE) {
-    return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
-  }
-  size_t cs, so, ss;
-  gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
-                             &so, &ss);
-  if (s != GB_OK) return s;
-  if (k > kR && dtype != GB_DTYPE_F32) {
-    return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
-                "which holds up to %d ranks per call", fn, k, kR);
-  }
-  if (n == 0) return GB_OK;
-  if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
-    return s;
-  }
-  if ((s = check_bucket_overlaps(fn, out, srcs, residuals, k, n, dtype_size(dtype), codec, workspace, cs, ss)) !=
-      GB_OK) {
-    return s;
-  }
-  char* ws = static_cast<char*>(workspace);
-  return from_hip(bucket_groups(out, srcs, residuals, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
-                                as_stream(stream)),
-                  fn);
+  return gb::traced_call("gb_bucket_allreduce_local_ef_typed", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    if (!codec_dtype(dtype)) return fail(GB_ERR_UNSUPPORTED, "%s: dtype %d is not a floating-point type", fn, dtype);
+    if (codec == GB_CODEC_NONE) {
+      return fail(GB_ERR_UNSUPPORTED, "%s: error feedback needs a lossy codec (bf16 or fp8)", fn);
+    }
+    size_t cs, so, ss;
+    gb_status s = check_bucket(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, workspace, workspace_bytes, &cs,
+                               &so, &ss);
+    if (s != GB_OK) return s;
+    if (k > kR && dtype != GB_DTYPE_F32) {
+      return fail(GB_ERR_INVALID_ARG, "%s: k = %d: a compressed non-float32 total is rounded once from float32, "
+                  "which holds up to %d ranks per call", fn, k, kR);
+    }
+    if (n == 0) return GB_OK;
+    if ((s = check_table(reinterpret_cast<const void* const*>(residuals), k, GB_ALIGN, fn, "residuals")) != GB_OK) {
+      return s;
+    }
+    if ((s = check_bucket_overlaps(fn, out, srcs, residuals, k, n, dtype_size(dtype), codec, workspace, cs, ss)) !=
+        GB_OK) {
+      return s;
+    }
+    char* ws = static_cast<char*>(workspace);
+    return from_hip(bucket_groups(out, srcs, residuals, k, n, codec, scale_mode, dtype, ws, cs, ws + so, ss,
+                                  as_stream(stream)),
+                    fn);
+  });
 }
 
 }  // extern "C"

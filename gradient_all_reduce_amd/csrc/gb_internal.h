@@ -11,6 +11,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <chrono>
+
 #include "gbreduce.h"
 
 namespace gb {
@@ -128,5 +130,29 @@ gb_status bucket_allreduce_local(const char* fn, float* out, const float* const*
                                  size_t workspace_bytes, void* stream);
 // Records a failure for gb_last_error() and returns s.
 gb_status fail_status(gb_status s, const char* msg);
+
+// Per-call hooks, switched on by two environment variables read once, at
+// the first call of the process (set and not "0" means on):
+//   GB_TRACE  one line per call on stderr: the entry point, k, n and the
+//             codec where it takes them, the stream, the status (with the
+//             message of a failure) and the host time the call took;
+//   GB_DEBUG  after a call that returned GB_OK, wait for its stream; an error
+//             the stream reports (a kernel of the call, or earlier work on
+//             the stream, failed) turns the status into GB_ERR_HIP.  A stream
+//             under graph capture is not waited for.
+// Off (the default), a call pays one test of a cached flag.
+constexpr size_t kNoSize = ~(size_t)0;  // no n to report
+bool call_hooks_on();
+gb_status finish_call(const char* fn, void* stream, int k, size_t n, int codec, gb_status s, double host_us);
+
+// Runs an entry point's body under the hooks; fn is the entry point's name.
+template <class Body>
+gb_status traced_call(const char* fn, void* stream, int k, size_t n, int codec, Body&& body) {
+  if (!call_hooks_on()) return body(fn);
+  const auto t0 = std::chrono::steady_clock::now();
+  const gb_status s = body(fn);
+  const double us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  return finish_call(fn, stream, k, n, codec, s, us);
+}
 
 }  // namespace gb

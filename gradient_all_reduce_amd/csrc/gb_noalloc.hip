@@ -56,22 +56,23 @@ gb_status scratch_address(const char* fn, void** out) {
 extern "C" gb_status gb_bucket_allreduce_local_noalloc(float* out, const float* const* srcs, int k, size_t n,
                                                        size_t bucket_elems, int codec, int scale_mode,
                                                        void* stream) {
-  const char* fn = "gb_bucket_allreduce_local_noalloc";
-  // 0 for arguments the layout rejects: the shared validation reports those
-  const size_t need = gb_bucket_workspace_bytes(codec, k, n, bucket_elems);
-  if (need > GB_NOALLOC_SCRATCH_BYTES) {
-    char msg[256];
-    std::snprintf(msg, sizeof msg,
-                  "%s: the payloads of k = %d ranks of n = %zu values need %zu bytes, more than the %zu-byte "
-                  "static scratch; pass a workspace to gb_bucket_allreduce_local instead",
-                  fn, k, n, need, (size_t)GB_NOALLOC_SCRATCH_BYTES);
-    return gb::fail_status(GB_ERR_WORKSPACE, msg);
-  }
-  void* ws = nullptr;
-  if (need > 0) {
-    gb_status s = scratch_address(fn, &ws);
-    if (s != GB_OK) return s;
-  }
-  return gb::bucket_allreduce_local(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, ws,
-                                    need > 0 ? (size_t)GB_NOALLOC_SCRATCH_BYTES : 0, stream);
+  return gb::traced_call("gb_bucket_allreduce_local_noalloc", stream, k, n, codec, [&](const char* fn) -> gb_status {
+    // 0 for arguments the layout rejects: the shared validation reports those
+    const size_t need = gb_bucket_workspace_bytes(codec, k, n, bucket_elems);
+    if (need > GB_NOALLOC_SCRATCH_BYTES) {
+      char msg[256];
+      std::snprintf(msg, sizeof msg,
+                    "%s: the payloads of k = %d ranks of n = %zu values need %zu bytes, more than the %zu-byte "
+                    "static scratch; pass a workspace to gb_bucket_allreduce_local instead",
+                    fn, k, n, need, (size_t)GB_NOALLOC_SCRATCH_BYTES);
+      return gb::fail_status(GB_ERR_WORKSPACE, msg);
+    }
+    void* ws = nullptr;
+    if (need > 0) {
+      gb_status s = scratch_address(fn, &ws);
+      if (s != GB_OK) return s;
+    }
+    return gb::bucket_allreduce_local(fn, out, srcs, k, n, bucket_elems, codec, scale_mode, ws,
+                                      need > 0 ? (size_t)GB_NOALLOC_SCRATCH_BYTES : 0, stream);
+  });
 }

@@ -42,6 +42,15 @@
  *    nothing.  The calls never abort or exit the process.
  *  - Failures return a gb_status; gb_last_error() then holds a one-line
  *    detail for the calling thread.
+ *  - Two environment variables, read once at the first call of the process
+ *    (set and not "0" means on), add per-call hooks to every call that takes
+ *    a stream:  GB_TRACE prints one line per call on stderr (entry point,
+ *    k, n and codec where the call takes them, stream, status and the
+ *    failure's detail, host time);  GB_DEBUG waits for the stream after a
+ *    call that returned GB_OK and returns GB_ERR_HIP if the stream reports
+ *    an error (from the call's kernels, or from earlier work on the stream),
+ *    except on a stream under graph capture, which is not waited for.  Both
+ *    are off by default.
  *  - Arithmetic is IEEE binary32 with round-to-nearest-even, subnormals kept
  *    and no fused multiply-add: every sum is a left fold over ranks
  *    0, 1, ..., k-1 starting from rank 0's value, so a result does not depend

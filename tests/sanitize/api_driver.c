@@ -22,6 +22,9 @@ void stub_fail_at(long nth);
 long stub_launches(void);
 long stub_copies(void);
 unsigned long long stub_pinned_base(void);
+void stub_sync_fails(int on);
+void stub_capturing(int capturing);
+long stub_syncs(void);
 
 static int failures, checks;
 
@@ -258,13 +261,59 @@ static void staged(void) {
          GB_ERR_INVALID_ARG, "not pinned", 8, "pageable host payload");
 }
 
-int main(void) {
-  validation();
-  overlaps();
-  allowed_aliases();
-  largest_batch();
-  launch_failures();
-  staged();
+static void expect_syncs(long before, long want, const char* what) {
+  checks++;
+  if (stub_syncs() - before != want) {
+    fprintf(stderr, "FAIL %s: %ld stream waits (want %ld)\n", what, stub_syncs() - before, want);
+    failures++;
+  }
+}
+
+/* Run with GB_DEBUG=1 and GB_TRACE=1 in the environment: a call that
+ * enqueued work waits for its stream once; an error the stream reports
+ * becomes GB_ERR_HIP; a stream under capture and a refused call are not
+ * waited for.  The trace lines go to stderr for the caller to check. */
+static void hooks(void) {
+  const void* one[1] = {P(dev(1))};
+  long before = stub_syncs();
+  stub_reset();
+  expect(gb_reduce_sum(F(dev(0)), (const float* const*)one, 1, 10, NULL), GB_OK, NULL, 1, "debug: a sum");
+  expect_syncs(before, 1, "debug: a sum");
+  before = stub_syncs();
+  expect(gb_bucket_allreduce_local(F(dev(0)), (const float* const*)one, 1, 1000, 256, GB_CODEC_FP8_E4M3_B256, 0,
+                                   P(dev(2)), MB, NULL),
+         GB_OK, NULL, 2, "debug: a bucket call");
+  expect_syncs(before, 1, "debug: a bucket call");
+  stub_sync_fails(1);
+  before = stub_syncs();
+  expect(gb_reduce_sum(F(dev(0)), (const float* const*)one, 1, 10, NULL), GB_ERR_HIP, "GB_DEBUG", 3,
+         "debug: the stream reports an error");
+  expect_syncs(before, 1, "debug: the stream reports an error");
+  stub_sync_fails(0);
+  stub_capturing(1);
+  before = stub_syncs();
+  expect(gb_reduce_sum(F(dev(0)), (const float* const*)one, 1, 10, NULL), GB_OK, NULL, 4, "debug: under capture");
+  expect_syncs(before, 0, "debug: under capture");
+  stub_capturing(0);
+  before = stub_syncs();
+  expect(gb_reduce_sum(F(dev(0)), (const float* const*)one, 0, 10, NULL), GB_ERR_INVALID_ARG, "k = 0", 4,
+         "debug: a refused call");
+  expect_syncs(before, 0, "debug: a refused call");
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && strcmp(argv[1], "hooks") == 0) {
+    hooks();
+  } else {
+    const long before = stub_syncs();
+    validation();
+    overlaps();
+    allowed_aliases();
+    largest_batch();
+    launch_failures();
+    staged();
+    expect_syncs(before, 0, "no GB_DEBUG: no call waits for its stream");
+  }
   printf("api_driver: %d checks, %d failed\n", checks, failures);
   return failures == 0 ? 0 : 1;
 }

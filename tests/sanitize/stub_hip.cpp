@@ -9,7 +9,9 @@
 // each with values), counts the launch and returns hipSuccess, or the
 // injected error on the chosen launch.  Pointers are never dereferenced: the
 // drivers pass fabricated addresses.  hipPointerGetAttributes reports the
-// addresses from kPinnedBase up as pinned host memory.
+// addresses from kPinnedBase up as pinned host memory.  hipStreamSynchronize
+// and hipStreamIsCapturing count waits and report what the driver sets, for
+// the GB_DEBUG hook.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdio>
@@ -19,7 +21,8 @@
 
 namespace {
 
-long g_launches = 0, g_copies = 0, g_fail_at = 0;
+long g_launches = 0, g_copies = 0, g_fail_at = 0, g_syncs = 0;
+int g_sync_fails = 0, g_capturing = 0;
 hipError_t g_fail_error = hipErrorLaunchFailure;
 constexpr uintptr_t kPinnedBase = (uintptr_t)0x700000000000ull;
 
@@ -64,6 +67,11 @@ void stub_fail_at(long nth) { g_fail_at = nth; }
 long stub_launches(void) { return g_launches; }
 long stub_copies(void) { return g_copies; }
 unsigned long long stub_pinned_base(void) { return (unsigned long long)kPinnedBase; }
+// hipStreamSynchronize reports an error while on != 0; the stream reads as
+// under graph capture while capturing != 0.
+void stub_sync_fails(int on) { g_sync_fails = on; }
+void stub_capturing(int capturing) { g_capturing = capturing; }
+long stub_syncs(void) { return g_syncs; }
 }
 
 namespace gb {
@@ -209,6 +217,14 @@ hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned) { return hipSuc
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind, hipStream_t) {
   if (dst == nullptr || src == nullptr || bytes == 0) broken("hipMemcpyAsync", "empty or NULL copy");
   ++g_copies;
+  return hipSuccess;
+}
+hipError_t hipStreamSynchronize(hipStream_t) {
+  ++g_syncs;
+  return g_sync_fails ? hipErrorIllegalAddress : hipSuccess;
+}
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
+  *status = g_capturing ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
   return hipSuccess;
 }
 hipError_t hipPointerGetAttributes(hipPointerAttribute_t* attributes, const void* ptr) {

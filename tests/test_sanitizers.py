@@ -3,7 +3,8 @@ CPU: the C ABI layer of libgbreduce (gb_api.cpp, built with g++ against the
 host stand-ins of tests/sanitize/stub_hip.cpp, driven by
 tests/sanitize/api_driver.c: validation, the refusal of overlapping buffers,
 the launches a call plans, and a launch failure injected at every launch of
-several multi-launch calls), and the CPU oracle (gb_oracle.c, driven by
+several multi-launch calls; then the GB_DEBUG and GB_TRACE hooks), and the
+CPU oracle (gb_oracle.c, driven by
 tests/sanitize/oracle_driver.c over ragged sizes and special values).  The
 two are built and run apart.  Any sanitizer report aborts the program."""
 import os
@@ -40,9 +41,24 @@ def test_abi_layer_under_sanitizers(tmp_path):
     run(["gcc", "-std=c11", *SAN, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(HERE, "api_driver.c"),
          "-o", str(drv)])
     run(["g++", *SAN, str(api), str(stub), str(drv), "-o", str(exe)])
-    out = run([str(exe)], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    env = {k: v for k, v in os.environ.items() if k not in ("GB_TRACE", "GB_DEBUG")}
+    out = run([str(exe)], env=dict(env, ASAN_OPTIONS="detect_leaks=1"))
     assert "0 failed" in out.stdout, out.stdout + out.stderr
     assert "runtime error" not in out.stderr
+    assert "gbreduce:" not in out.stderr  # no trace unless GB_TRACE is set
+
+    # the per-call hooks: GB_DEBUG waits for the stream after each call that
+    # enqueued work, GB_TRACE prints one line per call
+    out = run([str(exe), "hooks"], env=dict(env, ASAN_OPTIONS="detect_leaks=1", GB_TRACE="1", GB_DEBUG="1"))
+    assert "0 failed" in out.stdout, out.stdout + out.stderr
+    assert "runtime error" not in out.stderr
+    trace = [line for line in out.stderr.splitlines() if line.startswith("gbreduce: ")]
+    assert len(trace) == 5, out.stderr
+    assert trace[0].startswith("gbreduce: gb_reduce_sum k=1 n=10 stream=") and "-> GB_OK" in trace[0]
+    assert "gb_bucket_allreduce_local k=1 n=1000 codec=2" in trace[1] and "-> GB_OK" in trace[1]
+    assert "-> GB_ERR_HIP: gb_reduce_sum: GB_DEBUG: the stream reported HIP error" in trace[2]
+    assert "-> GB_OK (stream under capture: not waited for)" in trace[3]
+    assert "-> GB_ERR_INVALID_ARG: gb_reduce_sum: k = 0 is outside 1..16" in trace[4]
 
 
 def test_oracle_under_sanitizers(tmp_path):
