@@ -1042,13 +1042,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 def kernel_sources_sha256():
     """sha256 over the library's kernel sources (gb_device.h and every .hip
-    file but the ceiling program's, by name in sorted order: each name, a NUL,
-    its bytes, a NUL)."""
+    file of the library that defines a kernel, by name in sorted order: each
+    name, a NUL, its bytes, a NUL).  Host-only sources (the C ABI layer, the
+    no-allocation entry point) and the ceiling program are left out: a
+    change there leaves the kernels and their counters as they were."""
     import glob
     import hashlib
     csrc = os.path.join(ROOT, "gradient_all_reduce_amd", "csrc")
     h = hashlib.sha256()
-    srcs = [p for p in glob.glob(os.path.join(csrc, "*.hip")) if os.path.basename(p) != "gb_ceiling.hip"]
+    srcs = [p for p in glob.glob(os.path.join(csrc, "*.hip"))
+            if os.path.basename(p) != "gb_ceiling.hip" and "__global__" in open(p).read()]
     for path in sorted(srcs + [os.path.join(csrc, "gb_device.h")]):
         h.update(os.path.basename(path).encode() + b"\0" + open(path, "rb").read() + b"\0")
     return h.hexdigest()
