@@ -3,8 +3,8 @@ its payloads in the library's static device scratch gives the same output as
 gb_bucket_allreduce_local with a workspace, bit for bit, on consecutive calls
 whose sizes shrink (the scratch keeps the previous call's bytes), for both
 codecs, both scale rules, more than 8 ranks (whose payloads the pass reads
-back from the scratch) and in place; sizes beyond the scratch are refused
-with nothing written."""
+back from the scratch) and in place, and captured in a HIP graph and
+replayed; sizes beyond the scratch are refused with nothing written."""
 import numpy as np
 import pytest
 
@@ -79,6 +79,30 @@ def test_in_place(gb):
     gb.gb_bucket_allreduce_local(a[0], a, bucket, 2, 0, ws)
     gb.gb_bucket_allreduce_local_noalloc(b[0], b, bucket, 2, 0)
     assert (bits(a[0]) == bits(b[0])).all()
+
+
+@pytest.mark.parametrize("codec,k", [(2, 4), (1, 4), (2, 11)])
+def test_captured_in_a_graph_and_replayed(gb, codec, k):
+    """The call captured once in a HIP graph (no allocation, no memset node)
+    and replayed four times, new inputs copied in eagerly before each replay:
+    every replay equals the eager workspace call on those inputs."""
+    bucket = 256 * 40
+    n = bucket * 3 + 1001
+    xs = ranks(k, n, 101 + k)
+    out = torch.full((n,), float("nan"), device=DEV)
+    gb.gb_bucket_allreduce_local_noalloc(out, xs, bucket, codec, 0)  # the scratch's address looked up eagerly
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gb.gb_bucket_allreduce_local_noalloc(out, xs, bucket, codec, 0)
+    for rep in range(4):
+        for x, fresh in zip(xs, ranks(k, n, 200 + 10 * rep + k)):
+            x.copy_(fresh)
+        want = bits(with_workspace(gb, xs, bucket, codec, 0))
+        out.fill_(float("nan"))
+        graph.replay()
+        assert (bits(out) == want).all(), f"replay {rep}"
+    del graph
 
 
 def test_sizes_beyond_the_scratch_are_refused(gb):
