@@ -222,7 +222,9 @@ class DdpBuckets(Workload):
         et = self.gb.GB_DTYPE_OF[self.dt]
         # the four-rank float32 sum takes its wide kernel from 2^28 values per rank
         f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
-        name = {2: f"fused_fp8_kernel<4,{et}>", 1: f"fused_bf16_kernel<4,{et}>",
+        # the float32 fp8 pass takes its 128-lane workgroups from 2^27 values per rank
+        fp8 = "fused_fp8_half_kernel<4>" if et == 0 and self.n >= (1 << 27) else f"fused_fp8_kernel<4,{et}>"
+        name = {2: fp8, 1: f"fused_bf16_kernel<4,{et}>",
                 0: f32_sum if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]
         return (name, self.step_bytes(), 1, self.step)
 

@@ -16,8 +16,9 @@
 //   replica   the memory pattern of the fused fp8 bucket pass over 4 ranks,
 //             with the encode replaced by taking each value's top byte: 4
 //             float32 sources read, 4 code streams, 4 scale streams and the
-//             float32 total written, in the pass's lane map, workgroup order
-//             and occupancy cap.
+//             float32 total written, in the pass's lane map and in the shape
+//             it takes at this size (128-lane workgroups in index order, 2
+//             per compute unit).
 // Then the fixed cost of a launch itself: 153 launches, back to back on one
 // stream, of a kernel whose body does nothing, from the stream and replayed
 // from a HIP graph, for grids of 1 workgroup, of the 1,600 of one 6,553,600-
@@ -107,13 +108,14 @@ __global__ __launch_bounds__(kThreads) void write_kernel(f4* __restrict__ dst, f
   __builtin_nontemporal_store(f4{value, value, value, value}, dst + i);
 }
 
-// The fused fp8 pass's memory pattern (4 ranks, float32): lane map, group
-// order and cap of the library's kernel, the encode replaced by the top byte
-// of each value and the scale by the block's first value.
-__global__ __launch_bounds__(kThreads) void replica_kernel(gb::PtrTable src, gb::OutTable codes, gb::OutTable scales,
-                                                           float* __restrict__ out) {
+// The fused fp8 pass's memory pattern (4 ranks, float32): lane map,
+// workgroup size, order and cap of the library's kernel for large buffers,
+// the encode replaced by the top byte of each value and the scale by the
+// block's first value.
+__global__ __launch_bounds__(gb::kHalfThreads) void replica_kernel(gb::PtrTable src, gb::OutTable codes,
+                                                                   gb::OutTable scales, float* __restrict__ out) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = gb::group_index<gb::BlockOrder>() * gb::kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = (size_t)blockIdx.x * (gb::kHalfThreads / 16) + (threadIdx.x >> 4);
   f4 x[4][4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
@@ -270,8 +272,11 @@ int main(int argc, char** argv) {
     sct.p[r] = scales + (size_t)r * nblk;
   }
   const double replica_bytes = (double)nval * (16.0 + 4.0 + 16.0 / 256 + 4.0);
-  measure("fused_fp8_replica_" + sz, replica_bytes, reps,
-          [&] { replica_kernel<<<nblk / gb::kBlocksPerGroup, kThreads, gb::kTwoPerCuLds>>>(st, ct, sct, reinterpret_cast<float*>(buf[4])); });
+  static_assert(gb::fused_fp8_half(4, (size_t)1 << 28), "the replica's shape is the pass's from 2^28 values");
+  measure("fused_fp8_replica_" + sz, replica_bytes, reps, [&] {
+    replica_kernel<<<nblk / (gb::kHalfThreads / 16), gb::kHalfThreads, gb::fused_fp8_half_lds(4)>>>(
+        st, ct, sct, reinterpret_cast<float*>(buf[4]));
+  });
 
   hipStream_t s;
   CK(hipStreamCreate(&s));

@@ -119,12 +119,13 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTabl
 // Fused fp8 bucket pass: read each rank's block once, write its payload
 // (codes, scale), decode those codes and add them in rank order.
 // ===========================================================================
-template <int K, int ET, bool FULL, int DIV = 0>
+// T lanes per workgroup: group g is its T / 16 blocks.
+template <int K, int ET, bool FULL, int DIV = 0, int T = kThreads>
 __device__ __forceinline__ void fused_fp8_body(void* out, const PtrTable& src, const OutTable& codes,
                                                const OutTable& scales, size_t n, int mode, size_t g,
                                                float d = 1.0f, float inv = 0.0f) {
   const uint32_t col = threadIdx.x & 15u;
-  const size_t block = g * kBlocksPerGroup + (threadIdx.x >> 4);
+  const size_t block = g * (T / 16) + (threadIdx.x >> 4);
   constexpr int MAP = codec_map<ET>();
   f4 x[K][4];
 #pragma unroll
@@ -159,6 +160,20 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable
   const size_t g = group_index<BlockOrder>();
   if ((g + 1) * kBlocksPerGroup * kBlock <= n) fused_fp8_body<K, ET, true>(out, src, codes, scales, n, mode, g);
   else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode, g);
+}
+
+// The same pass over float32 gradients in 128-lane workgroups taken in
+// index order: the shape for large buffers (fused_fp8_half).
+template <int K>
+__global__ __launch_bounds__(kHalfThreads) void fused_fp8_half_kernel(void* out, PtrTable src, OutTable codes,
+                                                                      OutTable scales, size_t n, int mode) {
+  constexpr size_t per_group = (kHalfThreads / 16) * kBlock;
+  const size_t g = blockIdx.x;
+  if ((g + 1) * per_group <= n) {
+    fused_fp8_body<K, GB_DTYPE_F32, true, 0, kHalfThreads>(out, src, codes, scales, n, mode, g);
+  } else {
+    fused_fp8_body<K, GB_DTYPE_F32, false, 0, kHalfThreads>(out, src, codes, scales, n, mode, g);
+  }
 }
 
 // Several buckets in one launch (gradients of element type ET): each
@@ -216,6 +231,17 @@ hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales
 template <int ET>
 hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const OutTable& s, int k, size_t n,
                        int scale_mode, hipStream_t stream) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    if (fused_fp8_half(k, n)) {
+      const size_t half_grid = ceil_div(n, (kHalfThreads / 16) * kBlock);
+      if (half_grid > kMaxGrid) return hipErrorInvalidValue;
+#define GB_CALL(K) \
+  fused_fp8_half_kernel<K><<<half_grid, kHalfThreads, fused_fp8_half_lds(K), stream>>>(out, srcs, c, s, n, scale_mode);
+      GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+      return hipGetLastError();
+    }
+  }
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
 #define GB_CALL(K) fused_fp8_kernel<K, ET><<<grid, kThreads, fused_fp8_lds<ET>(K, n), stream>>>(out, srcs, c, s, n, scale_mode);

@@ -805,6 +805,22 @@ __host__ __device__ constexpr unsigned fused_fp8_lds(int k, size_t n) {
   return heavy_lds(k);
 }
 
+// Fused fp8 pass over float32 gradients of large buffers: 128-lane
+// workgroups (8 blocks, two wavefronts each) in index order, from 2^27
+// values per rank over 3 to 8 ranks and from 2^28 over 2, capped at 2 per
+// unit over k >= 4 ranks and at 3 over 2 or 3.  Measured on MI355X against
+// the 256-lane kernel (2 per unit; 4 fronts from about 4e8 values) in one
+// process, same bits: 2-9% more bytes per second at 2^27, 2^28 and 6.3e8
+// values for 3, 4, 6 and 8 ranks, 1-2% at 1e9 over 4, and 4-6% over 2 ranks
+// from 2^28; the 256-lane workgroup at 1 per unit (the same 4 wavefronts per
+// unit) and every permuted order of the 128-lane one did worse, and so did
+// the 128-lane shape at bucket sizes (6,553,600 values) and up to 2^26.
+constexpr int kHalfThreads = 128;
+__host__ __device__ constexpr bool fused_fp8_half(int k, size_t n) {
+  return (k >= 3 && n >= ((size_t)1 << 27)) || (k == 2 && n >= ((size_t)1 << 28));
+}
+__host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) { return k >= 4 ? kTwoPerCuLds : kThreePerCuLds; }
+
 // Fused fp8 pass with error feedback (21 streams at k = 4: sources and
 // residuals read; codes, scales, residuals and the sum written): 1 per unit
 // from 2^28 values up, 2-4% ahead of 2 or uncapped at 5e8 and 1e9 over every

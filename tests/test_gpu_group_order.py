@@ -4,9 +4,11 @@ permuted workgroup order of the streaming kernels, used from 16 runs of
 groups; from 8 runs, about 1.7e7 values, for the fused bf16-codec passes
 over float32 gradients; from 4 runs, 2^23 values, for the bf16 decode into
 float32; from 64 MiB per rank for the reductions; from about 4e8 values for
-the kernels over 4096-value fp8 groups) and the wide four-rank sum (from
-2^28 values) give, bit for bit, what the same call gives over slices of the
-stream small enough to keep the index order and the narrow shape.
+the kernels over 4096-value fp8 groups), the wide four-rank sum (from
+2^28 values) and the fused fp8 pass in 128-lane workgroups (float32
+gradients from 2^27 values, 2^28 over two ranks) give, bit for bit, what
+the same call gives over slices of the stream small enough to keep the
+index order and the narrow shape.
 
 Every result is elementwise (per value, or per 256-value fp8 block), so a
 call over a slice that starts on a bucket boundary computes exactly that
@@ -31,6 +33,7 @@ STEP_VEC = 5 * B  # 32,768,000 values: fewer than 16 runs of 1024-value groups
 STEP_DEC = B  # 6,553,600 values: fewer than the bf16 decode's 4 runs (2^23 values)
 STEP_RED = 2 * B  # 13,107,200 values: fewer than 8 runs of the reductions' 4 KiB groups (float32)
 STEP_BLK = 50 * B  # 327,680,000 values: fewer than 96 runs of 4096-value groups
+STEP_HALF = 20 * B  # 131,072,000 values: below 2^27, where the fused fp8 pass keeps 256-lane workgroups
 SENTINEL = 0x7FBADBAD  # a float32 NaN no kernel writes
 
 
@@ -147,6 +150,45 @@ def test_wide_four_rank_sum(gb):
     same(x0, ref, "wide four-rank sum in place")
 
 
+@pytest.mark.parametrize("k", [2, 3, 4, 8])
+def test_fused_fp8_half_workgroups(gb, k):
+    """The fused fp8 bucket stream over float32 gradients from 2^27 values
+    per rank (2^28 over two ranks) runs in 128-lane workgroups in index
+    order.  With a ragged last workgroup and block it must equal the 256-lane
+    kernel over slices below 2^27, and the oracle on sampled windows (the
+    first and the last values included): totals, codes and scales."""
+    import numpy as np
+    from oracle import oracle as O
+    fp8 = gb.GB_CODEC_FP8_E4M3_B256
+    n = ((1 << 28) if k == 2 else (1 << 27)) + 2048 * 5 + 77
+    x = [W.device_gradients(n, 1200 + 10 * k + r, DEV) for r in range(k)]
+    lay = gb.gb_bucket_workspace_layout(fp8, k, n, B)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local(whole, x, B, fp8, 0, ws)
+    wss = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, STEP_HALF, B), dtype=torch.uint8, device=DEV)
+    for s, e in slices(n, STEP_HALF):
+        gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, fp8, 0, wss)
+    same(whole, ref, f"fused fp8 pass over {k} ranks")
+    del ref, wss
+    nb = (n + 255) // 256
+    codes = [ws[r * lay["codes_stride"]:][:n] for r in range(k)]
+    scales = [ws[lay["scales_offset"] + r * lay["scales_stride"]:][:4 * nb].view(torch.float32) for r in range(k)]
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    length = 65536
+    rng = np.random.default_rng(70 + k)
+    last = (n - length) // 256 * 256
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 4)]:
+        e = n if s == last else s + length
+        want, wc, wsc = O.bucket_allreduce([t[s:e].cpu().numpy() for t in x], B, O.CODEC_FP8,
+                                           O.SCALE_ABSMAX_DIV_448)
+        assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+            got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
+            assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
 def test_typed_reduce(gb, dt):
     n = N_VEC
@@ -207,7 +249,7 @@ def test_fp8_group_kernels(gb):
                      device=DEV)
     whole, ref = filled(n), filled(n)
     gb.gb_bucket_allreduce_local(whole, x, B, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
-    for s, e in parts:
+    for s, e in slices(n, STEP_HALF):  # float32: below 2^27, the 256-lane kernel in index order
         gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
     same(whole, ref, "fp8 bucket stream")
     rw = [torch.full((n,), -2e-5, device=DEV) for _ in range(2)]
