@@ -91,10 +91,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTab
 // ===========================================================================
 // Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
+// Lane t of vector group sg (t in [0, 256)).
 template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n,
-                                                size_t sg, float d = 1.0f, float inv = 0.0f) {
-  const uint32_t t = threadIdx.x;
+                                                size_t sg, uint32_t t, float d = 1.0f, float inv = 0.0f) {
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 x[K];
 #pragma unroll
@@ -119,8 +119,22 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTabl
   // per second in index order (1-7%, up to 21% with error feedback over
   // bfloat16), measured on three machines
   const size_t sg = ET == GB_DTYPE_F32 ? group_index<FusedVecOrder>() : (size_t)blockIdx.x;
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true>(out, src, codes, n, sg);
-  else fused_bf16_body<K, ET, false>(out, src, codes, n, sg);
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true>(out, src, codes, n, sg, threadIdx.x);
+  else fused_bf16_body<K, ET, false>(out, src, codes, n, sg, threadIdx.x);
+}
+
+// The same pass over float32 gradients in 64-lane workgroups of 256 values,
+// taken in index order (fused_bf16_wave): workgroup w holds lanes
+// 64 (w mod 4) .. 64 (w mod 4) + 63 of vector group w / 4, so every value is
+// where the 256-lane kernel puts it.
+template <int K>
+__global__ __launch_bounds__(kWaveThreads) void fused_bf16_wave_kernel(void* out, PtrTable src, OutTable codes,
+                                                                       size_t n) {
+  const size_t w = blockIdx.x;
+  const size_t sg = w >> 2;
+  const uint32_t t = ((uint32_t)(w & 3u) << 6) + threadIdx.x;
+  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_body<K, GB_DTYPE_F32, true>(out, src, codes, n, sg, t);
+  else fused_bf16_body<K, GB_DTYPE_F32, false>(out, src, codes, n, sg, t);
 }
 
 // Several buckets in one launch (gradients of element type ET), as the fp8
@@ -142,8 +156,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch 
   // whole-buffer launch, as there
   const size_t wl = w - t.first[b], n = t.n[b];
   const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<FusedVecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true, DIV>(t.out[b], src, codes, n, sg, d, inv);
-  else fused_bf16_body<K, ET, false, DIV>(t.out[b], src, codes, n, sg, d, inv);
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true, DIV>(t.out[b], src, codes, n, sg, threadIdx.x, d, inv);
+  else fused_bf16_body<K, ET, false, DIV>(t.out[b], src, codes, n, sg, threadIdx.x, d, inv);
 }
 
 // Launcher bodies, one per element type ET.
@@ -180,6 +194,17 @@ hipError_t decode_bf16_t(void* acc, const PtrTable& codes, int k, size_t n, bool
 
 template <int ET>
 hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    if (fused_bf16_wave(k)) {
+      const size_t wave_grid = ceil_div(n, kVecPerGroup / 4);
+      if (wave_grid > kMaxGrid) return hipErrorInvalidValue;
+#define GB_CALL(K) \
+  fused_bf16_wave_kernel<K><<<wave_grid, kWaveThreads, fused_bf16_wave_lds(K, n), stream>>>(out, srcs, c, n);
+      GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+      return hipGetLastError();
+    }
+  }
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
 #define GB_CALL(K) fused_bf16_kernel<K, ET><<<grid, kThreads, fused_bf16_lds<ET>(K, n), stream>>>(out, srcs, c, n);

@@ -849,6 +849,23 @@ __host__ __device__ constexpr unsigned fused_bf16_ef_lds(int k) {
   return ET == GB_DTYPE_F16 ? heavy_lds(k) : ef_lds(k);
 }
 
+// Fused bf16 pass over float32 gradients from 3 ranks: 64-lane workgroups
+// (one wavefront, 256 values) in index order, uncapped below 3 * 2^21 values
+// per rank and from there capped by rank count, at 13 per unit over 3
+// ranks, 10 over 4, 8 over 5 or 6 and 6 over 7 or 8.  Measured on MI355X
+// against the 256-lane kernel (its rules below) in one process, same bits:
+// from one 25 MiB bucket (6,553,600 values) to 1e9 values, 2.5-8.6% more
+// bytes per second over 3 ranks, 3.3-8.8% over 4, 5.8-10.8% over 5 and 6,
+// 5-13% over 7 and 8; uncapped from 2^21 to 2^22 values 1-11%; about level
+// at 2^20 and below.  The caps lose below 3 * 2^21 values, and two ranks
+// gain nothing consistent, so they keep the 256-lane kernel.
+constexpr int kWaveThreads = 64;
+__host__ __device__ constexpr bool fused_bf16_wave(int k) { return k >= 3; }
+__host__ __device__ constexpr unsigned fused_bf16_wave_lds(int k, size_t n) {
+  if (n < ((size_t)3 << 21)) return 0u;
+  return k <= 3 ? (12u << 10) : k == 4 ? (16u << 10) : k <= 6 ? (20u << 10) : (24u << 10);
+}
+
 // Plain fused bf16 pass: from 2^25 values up, float32 gradients at 3 per
 // unit (2-4% ahead) and float64 gradients at 2 (1-5% ahead); both lose about
 // 3% at bucket sizes, which stay uncapped.  Half-precision gradients are

@@ -5,10 +5,12 @@ groups; from 8 runs, about 1.7e7 values, for the fused bf16-codec passes
 over float32 gradients; from 4 runs, 2^23 values, for the bf16 decode into
 float32; from 64 MiB per rank for the reductions; from about 4e8 values for
 the kernels over 4096-value fp8 groups), the wide four-rank sum (from
-2^28 values) and the fused fp8 pass in 128-lane workgroups (float32
-gradients from 2^27 values, 2^28 over two ranks) give, bit for bit, what
-the same call gives over slices of the stream small enough to keep the
-index order and the narrow shape.
+2^28 values), the fused fp8 pass in 128-lane workgroups (float32
+gradients from 2^27 values, 2^28 over two ranks) and the fused bf16 pass in
+64-lane workgroups (float32 gradients from 3 ranks) give, bit for bit, what
+the same arithmetic gives in the other shapes: over slices of the stream
+small enough to keep the index order and the narrow shape, or through the
+batch kernel.
 
 Every result is elementwise (per value, or per 256-value fp8 block), so a
 call over a slice that starts on a bucket boundary computes exactly that
@@ -187,6 +189,41 @@ def test_fused_fp8_half_workgroups(gb, k):
             assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
             got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
             assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+
+
+@pytest.mark.parametrize("k", [3, 4, 6, 8])
+@pytest.mark.parametrize("n", [(3 << 21) + 256 * 5 + 77, (1 << 21) + 3 * 64 + 5])
+def test_fused_bf16_wave_workgroups(gb, k, n):
+    """The fused bf16 bucket stream over float32 gradients from 3 ranks runs
+    in 64-lane workgroups (256 values each) in index order, capped by rank
+    count from 3 * 2^21 values and uncapped below.  With a ragged last
+    workgroup it must equal the 256-lane batch kernel on the same buffers (a
+    batch of one bucket), and the oracle on sampled windows (the first and
+    last values included): totals and codes."""
+    import numpy as np
+    from oracle import oracle as O
+    bf16 = gb.GB_CODEC_BF16
+    x = [W.device_gradients(n, 1300 + 10 * k + r, DEV) for r in range(k)]
+    lay = gb.gb_bucket_workspace_layout(bf16, k, n, B)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local(whole, x, B, bf16, 0, ws)
+    wsb = torch.empty(gb.gb_bucket_batch_workspace_bytes(bf16, k, [n]), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch([ref], [x], bf16, workspace=wsb)
+    same(whole, ref, f"fused bf16 pass over {k} ranks against the batch kernel")
+    del ref, wsb
+    codes = [ws[r * lay["codes_stride"]:][:2 * n].view(torch.int16) for r in range(k)]
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    length = 65536
+    rng = np.random.default_rng(90 + k)
+    last = n - length
+    for s in [0, last] + [int(v) * 4 for v in rng.integers(0, last // 4, 4)]:
+        e = n if s == last else s + length
+        want, wc, _ = O.bucket_allreduce([t[s:e].cpu().numpy() for t in x], B, O.CODEC_BF16)
+        assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            got = codes[r][s:e].cpu().numpy().view(np.uint16)
+            assert (got == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
