@@ -401,7 +401,9 @@ class DdpBucketsEF(DdpBuckets):
     def timed_kernel(self):
         et = self.gb.GB_DTYPE_OF[self.dt]
         fp8 = self.codec == self.gb.GB_CODEC_FP8_E4M3_B256
-        name = f"fused_fp8_ef_kernel<4,{et}>" if fp8 else f"fused_bf16_ef_kernel<4,{et}>"
+        # the float32 bf16 pass takes 64-lane workgroups at every size
+        bf16 = "fused_bf16_ef_wave_kernel<4>" if et == 0 else f"fused_bf16_ef_kernel<4,{et}>"
+        name = f"fused_fp8_ef_kernel<4,{et}>" if fp8 else bf16
         return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):

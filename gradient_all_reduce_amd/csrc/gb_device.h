@@ -866,6 +866,18 @@ __host__ __device__ constexpr unsigned fused_bf16_wave_lds(int k, size_t n) {
   return k <= 3 ? (12u << 10) : k == 4 ? (16u << 10) : k <= 6 ? (20u << 10) : (24u << 10);
 }
 
+// Fused bf16 pass with error feedback over float32 gradients: 64-lane
+// workgroups in index order at every size, capped by rank count (each lane
+// keeps 32 bytes of every rank in flight: gradient and residual), at 13 per
+// unit over 1 rank, 10 over 2, 6 over 3 or 4 and 5 over 5 to 8.  Measured on
+// MI355X against the 256-lane kernel (its rule below) in one process, same
+// bits: 4-24% more bytes per second from one 25 MiB bucket to 1e9 values
+// over every rank count from 1 to 8 (4 ranks: +14.5% at a bucket, +12% at
+// 1e9), and 2-19% at 2^20 and 2^22 values.
+__host__ __device__ constexpr unsigned fused_bf16_ef_wave_lds(int k) {
+  return k <= 1 ? (12u << 10) : k == 2 ? (16u << 10) : k <= 4 ? (24u << 10) : (32u << 10);
+}
+
 // Plain fused bf16 pass: from 2^25 values up, float32 gradients at 3 per
 // unit (2-4% ahead) and float64 gradients at 2 (1-5% ahead); both lose about
 // 3% at bucket sizes, which stay uncapped.  Half-precision gradients are

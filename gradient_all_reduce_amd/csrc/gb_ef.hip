@@ -115,9 +115,8 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_ef_kernel(void* out, PtrTa
 
 template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& src, const OutTable& resid,
-                                                   const OutTable& codes, size_t n, size_t sg, float dv = 1.0f,
-                                                   float inv = 0.0f) {
-  const uint32_t t = threadIdx.x;
+                                                   const OutTable& codes, size_t n, size_t sg, uint32_t t,
+                                                   float dv = 1.0f, float inv = 0.0f) {
   if (!FULL && group_first<ET>(sg, t) >= n) return;
   f4 y[K];
 #pragma unroll
@@ -147,8 +146,22 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrT
   // per second in index order (1-7%, up to 21% with error feedback over
   // bfloat16), measured on three machines
   const size_t sg = ET == GB_DTYPE_F32 ? group_index<FusedVecOrder>() : (size_t)blockIdx.x;
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n, sg);
-  else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, sg);
+  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n, sg, threadIdx.x);
+  else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, sg, threadIdx.x);
+}
+
+// The same pass over float32 gradients in 64-lane workgroups of 256 values,
+// taken in index order: workgroup w holds lanes 64 (w mod 4) ..
+// 64 (w mod 4) + 63 of vector group w / 4, so every value is where the
+// 256-lane kernel puts it.
+template <int K>
+__global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_kernel(void* out, PtrTable src, OutTable resid,
+                                                                          OutTable codes, size_t n) {
+  const size_t w = blockIdx.x;
+  const size_t sg = w >> 2;
+  const uint32_t t = ((uint32_t)(w & 3u) << 6) + threadIdx.x;
+  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_ef_body<K, GB_DTYPE_F32, true>(out, src, resid, codes, n, sg, t);
+  else fused_bf16_ef_body<K, GB_DTYPE_F32, false>(out, src, resid, codes, n, sg, t);
 }
 
 // Several buckets in one launch, with their residuals: each workgroup finds
@@ -191,8 +204,11 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBat
   }
   const size_t wl = w - t.first[b], n = t.n[b];
   const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<FusedVecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
-  if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
-  else fused_bf16_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, n, sg, dv, inv);
+  if ((sg + 1) * kVecPerGroup <= n) {
+    fused_bf16_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, n, sg, threadIdx.x, dv, inv);
+  } else {
+    fused_bf16_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, n, sg, threadIdx.x, dv, inv);
+  }
 }
 
 // The table's first workgroups and the grid; 0 if the table is empty or too large.
@@ -252,6 +268,15 @@ hipError_t encode_fp8_ef_t(uint8_t* codes, float* scales, float* residual, const
 template <int ET>
 hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, int k, size_t n,
                            hipStream_t stream) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    const size_t wave_grid = ceil_div(n, kVecPerGroup / 4);
+    if (wave_grid > kMaxGrid) return hipErrorInvalidValue;
+#define GB_CALL(K) \
+  fused_bf16_ef_wave_kernel<K><<<wave_grid, kWaveThreads, fused_bf16_ef_wave_lds(K), stream>>>(out, srcs, rs, c, n);
+    GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+    return hipGetLastError();
+  }
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
 #define GB_CALL(K) fused_bf16_ef_kernel<K, ET><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(out, srcs, rs, c, n);

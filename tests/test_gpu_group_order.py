@@ -1,22 +1,27 @@
-"""Launches large enough to take their groups out of index order (the
-permuted workgroup order of the streaming kernels, used from 16 runs of
-2048 groups, about 3.4e7 values, for the kernels over 1024-value vector
-groups; from 8 runs, about 1.7e7 values, for the fused bf16-codec passes
-over float32 gradients; from 4 runs, 2^23 values, for the bf16 decode into
-float32; from 64 MiB per rank for the reductions; from about 4e8 values for
-the kernels over 4096-value fp8 groups), the wide four-rank sum (from
-2^28 values), the fused fp8 pass in 128-lane workgroups (float32
-gradients from 2^27 values, 2^28 over two ranks) and the fused bf16 pass in
-64-lane workgroups (float32 gradients from 3 ranks) give, bit for bit, what
-the same arithmetic gives in the other shapes: over slices of the stream
-small enough to keep the index order and the narrow shape, or through the
-batch kernel.
+"""Launches whose workgroups take another shape than the small-launch path:
+- the permuted workgroup order of the streaming kernels, from 16 runs of
+  2048 groups (about 3.4e7 values) for the kernels over 1024-value vector
+  groups, from 8 runs (about 1.7e7 values) for the fused bf16-codec passes
+  over float32 gradients of one or two ranks and the batch kernels, from 4
+  runs (2^23 values) for the bf16 decode into float32, from 64 MiB per rank
+  for the reductions, and from about 4e8 values for the kernels over
+  4096-value fp8 groups;
+- the wide four-rank sum, from 2^28 values;
+- the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
+  values, 2^28 over two ranks);
+- the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
+  ranks; with error feedback, from 1 rank).
+
+Each must give, bit for bit, what the same arithmetic gives in another
+shape: over slices of the stream small enough to keep the index order and
+the narrow shape, or through the batch kernel; the new shapes are also
+checked against the oracle on sampled windows.
 
 Every result is elementwise (per value, or per 256-value fp8 block), so a
 call over a slice that starts on a bucket boundary computes exactly that
 slice of the whole call; the small-launch path is checked against the oracle
 by the other GPU tests, and the 1e9-value fp8 bucket stream against the
-oracle on sampled blocks.  Outputs start filled with a sentinel, so a group
+oracle on every value.  Outputs start filled with a sentinel, so a group
 that no workgroup took shows as a difference.  Sizes end in a ragged tail
 that is not a whole number of runs of the permutation."""
 import pytest
@@ -224,6 +229,46 @@ def test_fused_bf16_wave_workgroups(gb, k, n):
         for r in range(k):
             got = codes[r][s:e].cpu().numpy().view(np.uint16)
             assert (got == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+@pytest.mark.parametrize("n", [(3 << 21) + 256 * 5 + 77, (1 << 20) + 3 * 64 + 5])
+def test_fused_bf16_ef_wave_workgroups(gb, k, n):
+    """The fused bf16 bucket stream with error feedback over float32
+    gradients runs in 64-lane workgroups in index order at every size.  With
+    a ragged last workgroup it must equal the 256-lane batch kernel from the
+    same residuals (a batch of one bucket), and the oracle on sampled windows
+    (the first and last values included): totals, codes and new residuals."""
+    import numpy as np
+    from oracle import oracle as O
+    bf16 = gb.GB_CODEC_BF16
+    x = [W.device_gradients(n, 1400 + 10 * k + r, DEV) for r in range(k)]
+    r0 = [W.device_gradients(n, 1500 + 10 * k + r, DEV) * 1e-3 for r in range(k)]
+    lay = gb.gb_bucket_workspace_layout(bf16, k, n, B)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    res = [t.clone() for t in r0]
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local_ef(whole, x, res, B, bf16, 0, ws)
+    resb = [t.clone() for t in r0]
+    wsb = torch.empty(gb.gb_bucket_batch_workspace_bytes(bf16, k, [n]), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch_ef([ref], [x], [resb], bf16, workspace=wsb)
+    same(whole, ref, f"fused bf16 pass with feedback over {k} ranks against the batch kernel")
+    for r in range(k):
+        same(res[r], resb[r], f"residual {r} against the batch kernel")
+    del ref, wsb, resb
+    codes = [ws[r * lay["codes_stride"]:][:2 * n].view(torch.int16) for r in range(k)]
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    length = 65536
+    rng = np.random.default_rng(110 + k)
+    last = n - length
+    for s in [0, last] + [int(v) * 4 for v in rng.integers(0, last // 4, 3)]:
+        e = n if s == last else s + length
+        want, wc, _, wr = O.bucket_allreduce_ef([t[s:e].cpu().numpy() for t in x],
+                                                [t[s:e].cpu().numpy() for t in r0], B, O.CODEC_BF16)
+        assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy().view(np.uint16) == wc[r]).all(), f"oracle codes {r} at {s}"
+            assert (u32(res[r][s:e].cpu().numpy()) == u32(wr[r])).all(), f"oracle residual {r} at {s}"
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
