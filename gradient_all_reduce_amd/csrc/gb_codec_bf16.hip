@@ -123,18 +123,16 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTabl
   else fused_bf16_body<K, ET, false>(out, src, codes, n, sg, threadIdx.x);
 }
 
-// The same pass over float32 gradients in 64-lane workgroups of 256 values,
-// taken in index order (fused_bf16_wave): workgroup w holds lanes
-// 64 (w mod 4) .. 64 (w mod 4) + 63 of vector group w / 4, so every value is
-// where the 256-lane kernel puts it.
+// The same pass over float32 gradients in 64-lane workgroups of 256 values
+// (wave_lane), taken in index order (fused_bf16_wave).  A buffer's last
+// vector group may leave up to 3 workgroups with no values; they return.
 template <int K>
 __global__ __launch_bounds__(kWaveThreads) void fused_bf16_wave_kernel(void* out, PtrTable src, OutTable codes,
                                                                        size_t n) {
   const size_t w = blockIdx.x;
-  const size_t sg = w >> 2;
-  const uint32_t t = ((uint32_t)(w & 3u) << 6) + threadIdx.x;
-  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_body<K, GB_DTYPE_F32, true>(out, src, codes, n, sg, t);
-  else fused_bf16_body<K, GB_DTYPE_F32, false>(out, src, codes, n, sg, t);
+  const WaveLane l = wave_lane(w);
+  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_body<K, GB_DTYPE_F32, true>(out, src, codes, n, l.sg, l.t);
+  else fused_bf16_body<K, GB_DTYPE_F32, false>(out, src, codes, n, l.sg, l.t);
 }
 
 // Several buckets in one launch (gradients of element type ET), as the fp8
@@ -158,6 +156,29 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_batch_kernel(BucketBatch 
   const size_t sg = ET == GB_DTYPE_F32 ? group_index_in<FusedVecOrder>(wl, t.first[b + 1] - t.first[b]) : wl;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_body<K, ET, true, DIV>(t.out[b], src, codes, n, sg, threadIdx.x, d, inv);
   else fused_bf16_body<K, ET, false, DIV>(t.out[b], src, codes, n, sg, threadIdx.x, d, inv);
+}
+
+// The batch over float32 gradients in 64-lane workgroups (fused_bf16_wave):
+// bucket b takes workgroups [first[b], first[b + 1]), four per vector group.
+template <int K, int DIV>
+__global__ __launch_bounds__(kWaveThreads) void fused_bf16_wave_batch_kernel(BucketBatch t, float d, float inv) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  PtrTable src;
+  OutTable codes;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    codes.p[r] = t.codes[b][r];
+  }
+  const size_t wl = w - t.first[b], n = t.n[b];
+  const WaveLane l = wave_lane(wl);
+  if ((wl + 1) * (kVecPerGroup / 4) <= n) {
+    fused_bf16_body<K, GB_DTYPE_F32, true, DIV>(t.out[b], src, codes, n, l.sg, l.t, d, inv);
+  } else {
+    fused_bf16_body<K, GB_DTYPE_F32, false, DIV>(t.out[b], src, codes, n, l.sg, l.t, d, inv);
+  }
 }
 
 // Launcher bodies, one per element type ET.
@@ -195,9 +216,8 @@ hipError_t decode_bf16_t(void* acc, const PtrTable& codes, int k, size_t n, bool
 template <int ET>
 hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
   if constexpr (ET == GB_DTYPE_F32) {
-    if (fused_bf16_wave(k)) {
-      const size_t wave_grid = ceil_div(n, kVecPerGroup / 4);
-      if (wave_grid > kMaxGrid) return hipErrorInvalidValue;
+    const size_t wave_grid = wave_grid_for(n);
+    if (fused_bf16_wave(k) && wave_grid != 0) {
 #define GB_CALL(K) \
   fused_bf16_wave_kernel<K><<<wave_grid, kWaveThreads, fused_bf16_wave_lds(K, n), stream>>>(out, srcs, c, n);
       GB_DISPATCH_K(k, GB_CALL)
@@ -243,6 +263,19 @@ template <int ET, int DIV>
 hipError_t fused_bf16_batch_t(BucketBatch& t, size_t grid, int k, float d, float inv, hipStream_t stream) {
   size_t largest = 0;
   for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
+  if constexpr (ET == GB_DTYPE_F32) {
+    // four 64-lane workgroups per vector group, uncapped: 16-bucket batches
+    // of whole 25 MiB buckets and of 819,200-value ones over 4 ranks moved
+    // 3% and 1% more bytes per second than the 256-lane batch kernel, and
+    // lost 1-17% under any cap (the whole-buffer kernel's included)
+    if (fused_bf16_wave(k) && grid <= kMaxGrid / 4) {
+      for (int b = 0; b <= kBatchBuckets; b++) t.first[b] *= 4;
+#define GB_CALL(K) fused_bf16_wave_batch_kernel<K, DIV><<<4 * grid, kWaveThreads, 0, stream>>>(t, d, inv);
+      GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+      return hipGetLastError();
+    }
+  }
 #define GB_CALL(K) fused_bf16_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_bf16_lds<ET>(K, largest), stream>>>(t, d, inv);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL

@@ -861,6 +861,22 @@ __host__ __device__ constexpr unsigned fused_bf16_ef_lds(int k) {
 // gain nothing consistent, so they keep the 256-lane kernel.
 constexpr int kWaveThreads = 64;
 __host__ __device__ constexpr bool fused_bf16_wave(int k) { return k >= 3; }
+// Workgroups of a 64-lane launch over n values (4 per 1024-value vector
+// group), or 0 beyond the largest grid, where the 256-lane kernel runs.
+__host__ __device__ constexpr size_t wave_grid_for(size_t n) {
+  return (n + kVecPerGroup - 1) / kVecPerGroup * 4 <= kMaxGrid ? (n + kVecPerGroup - 1) / kVecPerGroup * 4 : 0;
+}
+// A 64-lane workgroup's place in the 256-lane vector groups: workgroup w
+// (counted from its buffer's first) holds lanes 64 (w mod 4) ..
+// 64 (w mod 4) + 63 of vector group w / 4, so every value is where a
+// 256-lane workgroup puts it.
+struct WaveLane {
+  size_t sg;
+  uint32_t t;
+};
+__device__ __forceinline__ WaveLane wave_lane(size_t w) {
+  return WaveLane{w >> 2, ((uint32_t)(w & 3u) << 6) + threadIdx.x};
+}
 __host__ __device__ constexpr unsigned fused_bf16_wave_lds(int k, size_t n) {
   if (n < ((size_t)3 << 21)) return 0u;
   return k <= 3 ? (12u << 10) : k == 4 ? (16u << 10) : k <= 6 ? (20u << 10) : (24u << 10);

@@ -142,26 +142,27 @@ __device__ __forceinline__ void fused_bf16_ef_body(void* out, const PtrTable& sr
 template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrTable src, OutTable resid,
                                                                   OutTable codes, size_t n) {
-  // float32 gradients in the permuted order; the others move more bytes
-  // per second in index order (1-7%, up to 21% with error feedback over
-  // bfloat16), measured on three machines
+  // float32 gradients (here only beyond the largest 64-lane grid) in the
+  // permuted order; the others move more bytes per second in index order
+  // (1-7%, up to 21% with error feedback over bfloat16), measured on three
+  // machines
   const size_t sg = ET == GB_DTYPE_F32 ? group_index<FusedVecOrder>() : (size_t)blockIdx.x;
   if ((sg + 1) * kVecPerGroup <= n) fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n, sg, threadIdx.x);
   else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, sg, threadIdx.x);
 }
 
-// The same pass over float32 gradients in 64-lane workgroups of 256 values,
-// taken in index order: workgroup w holds lanes 64 (w mod 4) ..
-// 64 (w mod 4) + 63 of vector group w / 4, so every value is where the
-// 256-lane kernel puts it.
+// The same pass over float32 gradients in 64-lane workgroups of 256 values
+// (wave_lane), taken in index order.
 template <int K>
 __global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_kernel(void* out, PtrTable src, OutTable resid,
                                                                           OutTable codes, size_t n) {
   const size_t w = blockIdx.x;
-  const size_t sg = w >> 2;
-  const uint32_t t = ((uint32_t)(w & 3u) << 6) + threadIdx.x;
-  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_ef_body<K, GB_DTYPE_F32, true>(out, src, resid, codes, n, sg, t);
-  else fused_bf16_ef_body<K, GB_DTYPE_F32, false>(out, src, resid, codes, n, sg, t);
+  const WaveLane l = wave_lane(w);
+  if ((w + 1) * (kVecPerGroup / 4) <= n) {
+    fused_bf16_ef_body<K, GB_DTYPE_F32, true>(out, src, resid, codes, n, l.sg, l.t);
+  } else {
+    fused_bf16_ef_body<K, GB_DTYPE_F32, false>(out, src, resid, codes, n, l.sg, l.t);
+  }
 }
 
 // Several buckets in one launch, with their residuals: each workgroup finds
@@ -211,6 +212,30 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBat
   }
 }
 
+// The batch over float32 gradients in 64-lane workgroups: bucket b takes
+// workgroups [first[b], first[b + 1]), four per vector group.
+template <int K, int DIV>
+__global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_batch_kernel(BucketBatchEf t, float dv, float inv) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  PtrTable src;
+  OutTable resid, codes;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    resid.p[r] = t.resid[b][r];
+    codes.p[r] = t.codes[b][r];
+  }
+  const size_t wl = w - t.first[b], n = t.n[b];
+  const WaveLane l = wave_lane(wl);
+  if ((wl + 1) * (kVecPerGroup / 4) <= n) {
+    fused_bf16_ef_body<K, GB_DTYPE_F32, true, DIV>(t.out[b], src, resid, codes, n, l.sg, l.t, dv, inv);
+  } else {
+    fused_bf16_ef_body<K, GB_DTYPE_F32, false, DIV>(t.out[b], src, resid, codes, n, l.sg, l.t, dv, inv);
+  }
+}
+
 // The table's first workgroups and the grid; 0 if the table is empty or too large.
 size_t batch_grid(BucketBatchEf& t, int codec) {
   if (t.count == 0 || t.count > (uint32_t)kBatchBucketsEf) return 0;
@@ -241,6 +266,20 @@ template <int ET, int DIV>
 hipError_t fused_bf16_ef_batch_t(BucketBatchEf& t, int k, float dv, float inv, hipStream_t stream) {
   const size_t grid = batch_grid(t, GB_CODEC_BF16);
   if (grid == 0) return hipErrorInvalidValue;
+  if constexpr (ET == GB_DTYPE_F32) {
+    // four 64-lane workgroups per vector group, at the whole-buffer kernel's
+    // cap: 8-bucket batches over 4 ranks moved 21% (whole 25 MiB buckets)
+    // and 19% (819,200-value ones) more bytes per second than the 256-lane
+    // batch kernel at 1 per unit
+    if (grid <= kMaxGrid / 4) {
+      for (int b = 0; b <= kBatchBucketsEf; b++) t.first[b] *= 4;
+#define GB_CALL(K) \
+  fused_bf16_ef_wave_batch_kernel<K, DIV><<<4 * grid, kWaveThreads, fused_bf16_ef_wave_lds(K), stream>>>(t, dv, inv);
+      GB_DISPATCH_K(k, GB_CALL)
+#undef GB_CALL
+      return hipGetLastError();
+    }
+  }
 #define GB_CALL(K) \
   fused_bf16_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(t, dv, inv);
   GB_DISPATCH_K(k, GB_CALL)
@@ -269,17 +308,19 @@ template <int ET>
 hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, int k, size_t n,
                            hipStream_t stream) {
   if constexpr (ET == GB_DTYPE_F32) {
-    const size_t wave_grid = ceil_div(n, kVecPerGroup / 4);
-    if (wave_grid > kMaxGrid) return hipErrorInvalidValue;
+    const size_t wave_grid = wave_grid_for(n);
+    if (wave_grid != 0) {
 #define GB_CALL(K) \
   fused_bf16_ef_wave_kernel<K><<<wave_grid, kWaveThreads, fused_bf16_ef_wave_lds(K), stream>>>(out, srcs, rs, c, n);
-    GB_DISPATCH_K(k, GB_CALL)
+      GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-    return hipGetLastError();
+      return hipGetLastError();
+    }
   }
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;
-#define GB_CALL(K) fused_bf16_ef_kernel<K, ET><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(out, srcs, rs, c, n);
+#define GB_CALL(K) \
+  fused_bf16_ef_kernel<K, ET><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(out, srcs, rs, c, n);
   GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
   return hipGetLastError();
