@@ -866,6 +866,9 @@ __host__ __device__ constexpr bool fused_bf16_wave(int k) { return k >= 3; }
 __host__ __device__ constexpr size_t wave_grid_for(size_t n) {
   return (n + kVecPerGroup - 1) / kVecPerGroup * 4 <= kMaxGrid ? (n + kVecPerGroup - 1) / kVecPerGroup * 4 : 0;
 }
+static_assert(wave_grid_for((size_t)1 << 38) != 0, "a 64-lane grid up to 2^38 values");
+static_assert(wave_grid_for(GB_MAX_N) == 0, "the largest calls fall back to 256-lane workgroups");
+static_assert(GB_MAX_N / kVecPerGroup <= kMaxGrid, "and those fit a 256-lane grid");
 // A 64-lane workgroup's place in the 256-lane vector groups: workgroup w
 // (counted from its buffer's first) holds lanes 64 (w mod 4) ..
 // 64 (w mod 4) + 63 of vector group w / 4, so every value is where a
