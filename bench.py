@@ -224,8 +224,10 @@ class DdpBuckets(Workload):
         f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
         # the float32 fp8 pass takes its 128-lane workgroups from 2^27 values per rank
         fp8 = "fused_fp8_half_kernel<4>" if et == 0 and self.n >= (1 << 27) else f"fused_fp8_kernel<4,{et}>"
-        # and the float32 bf16 pass over 3 or more ranks its 64-lane workgroups
-        bf16 = "fused_bf16_wave_kernel<4>" if et == 0 else f"fused_bf16_kernel<4,{et}>"
+        # and the bf16 pass its 64-lane workgroups: float32 gradients over 3 or
+        # more ranks, float16 and bfloat16 ones over 4 or more from 2^22 values
+        wave = et == 0 or (et in (1, 2) and self.n >= (1 << 22))
+        bf16 = f"fused_bf16_wave_kernel<4,{et}>" if wave else f"fused_bf16_kernel<4,{et}>"
         name = {2: fp8, 1: bf16,
                 0: f32_sum if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]
         return (name, self.step_bytes(), 1, self.step)
@@ -639,7 +641,7 @@ def codec_extra(wl, time_region, reps, dec_name, dec_bytes):
     gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1)
     return {"decode_kernel": dec_name, "decode_kernel_gbs": gbs(dec_bytes, dec_ms),
             "decode_kernel_frac": round(gbs(dec_bytes, dec_ms) / HBM_PEAK_GBS, 4),
-            "fused_pass_kernel": "fused_fp8_kernel<4,0>" if fp8 else "fused_bf16_wave_kernel<4>",
+            "fused_pass_kernel": "fused_fp8_kernel<4,0>" if fp8 else "fused_bf16_wave_kernel<4,0>",
             "fused_pass_bytes": wl.fused_bytes(), "fused_pass_us": round(fused_ms * 1e3, 2),
             "fused_pass_gbs": gbs(wl.fused_bytes(), fused_ms),
             "fused_pass_frac": round(gbs(wl.fused_bytes(), fused_ms) / HBM_PEAK_GBS, 4),

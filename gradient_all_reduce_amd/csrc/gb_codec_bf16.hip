@@ -123,16 +123,19 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTabl
   else fused_bf16_body<K, ET, false>(out, src, codes, n, sg, threadIdx.x);
 }
 
-// The same pass over float32 gradients in 64-lane workgroups of 256 values
-// (wave_lane), taken in index order (fused_bf16_wave).  A buffer's last
-// vector group may leave up to 3 workgroups with no values; they return.
-template <int K>
+// The same pass in 64-lane workgroups of 256 values (wave_lane), taken in
+// index order: float32 gradients from 3 ranks (fused_bf16_wave), float16
+// and bfloat16 ones from 4 ranks and 2^22 values (fused_bf16_half_wave).  A
+// buffer's last vector group may leave up to 3 workgroups with no values;
+// they return.
+template <int K, int ET>
 __global__ __launch_bounds__(kWaveThreads) void fused_bf16_wave_kernel(void* out, PtrTable src, OutTable codes,
                                                                        size_t n) {
+  static_assert(ET == GB_DTYPE_F32 || ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16, "4-byte or 2-byte gradients");
   const size_t w = blockIdx.x;
   const WaveLane l = wave_lane(w);
-  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_body<K, GB_DTYPE_F32, true>(out, src, codes, n, l.sg, l.t);
-  else fused_bf16_body<K, GB_DTYPE_F32, false>(out, src, codes, n, l.sg, l.t);
+  if ((w + 1) * (kVecPerGroup / 4) <= n) fused_bf16_body<K, ET, true>(out, src, codes, n, l.sg, l.t);
+  else fused_bf16_body<K, ET, false>(out, src, codes, n, l.sg, l.t);
 }
 
 // Several buckets in one launch (gradients of element type ET), as the fp8
@@ -215,11 +218,12 @@ hipError_t decode_bf16_t(void* acc, const PtrTable& codes, int k, size_t n, bool
 
 template <int ET>
 hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
-  if constexpr (ET == GB_DTYPE_F32) {
+  if constexpr (ET == GB_DTYPE_F32 || ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) {
     const size_t wave_grid = wave_grid_for(n);
-    if (fused_bf16_wave(k) && wave_grid != 0) {
-#define GB_CALL(K) \
-  fused_bf16_wave_kernel<K><<<wave_grid, kWaveThreads, fused_bf16_wave_lds(K, n), stream>>>(out, srcs, c, n);
+    const bool wave = ET == GB_DTYPE_F32 ? fused_bf16_wave(k) : fused_bf16_half_wave(k, n);
+    if (wave && wave_grid != 0) {
+      const unsigned lds = ET == GB_DTYPE_F32 ? fused_bf16_wave_lds(k, n) : fused_bf16_half_wave_lds(k);
+#define GB_CALL(K) fused_bf16_wave_kernel<K, ET><<<wave_grid, kWaveThreads, lds, stream>>>(out, srcs, c, n);
       GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
       return hipGetLastError();

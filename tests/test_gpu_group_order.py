@@ -10,7 +10,8 @@
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
   values, 2^28 over two ranks);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
-  ranks; with error feedback, from 1 rank).
+  ranks; float16 and bfloat16 gradients from 4 ranks and 2^22 values; with
+  error feedback, from 1 rank).
 
 Each must give, bit for bit, what the same arithmetic gives in another
 shape: over slices of the stream small enough to keep the index order and
@@ -229,6 +230,42 @@ def test_fused_bf16_wave_workgroups(gb, k, n):
         for r in range(k):
             got = codes[r][s:e].cpu().numpy().view(np.uint16)
             assert (got == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("k", [4, 5, 6, 7, 8])
+@pytest.mark.parametrize("n", [(1 << 22) + 256 * 5 + 77, (1 << 22) - 3 * 64 - 5])
+def test_fused_bf16_half_wave_workgroups(gb, dt, k, n):
+    """The fused bf16 bucket stream over float16 and bfloat16 gradients from
+    4 ranks runs in 64-lane workgroups in index order from 2^22 values,
+    capped by rank count, and in 256-lane workgroups below.  With a ragged
+    last workgroup, on either side of the threshold, it must equal the
+    256-lane batch kernel on the same buffers (a batch of one bucket), and the
+    oracle on sampled windows (the first and last values included): totals
+    and codes."""
+    import numpy as np
+    from oracle import oracle as O
+    bf16 = gb.GB_CODEC_BF16
+    x = [W.device_gradients_typed(n, 1600 + 10 * k + r, DEV, dt) for r in range(k)]
+    lay = gb.gb_bucket_workspace_layout(bf16, k, n, B)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n, x[0].dtype), filled(n, x[0].dtype)
+    gb.gb_bucket_allreduce_local_typed(whole, x, B, bf16, 0, ws)
+    wsb = torch.empty(gb.gb_bucket_batch_workspace_bytes(bf16, k, [n]), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch([ref], [x], bf16, workspace=wsb)
+    same(whole, ref, f"fused bf16 pass over {k} ranks of {dt} against the batch kernel")
+    del ref, wsb
+    codes = [ws[r * lay["codes_stride"]:][:2 * n].view(torch.int16) for r in range(k)]
+    u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    length = 65536
+    rng = np.random.default_rng(130 + k)
+    last = n - length
+    for s in [0, last] + [int(v) * 4 for v in rng.integers(0, last // 4, 3)]:
+        e = n if s == last else s + length
+        want, wc, _ = O.bucket_allreduce_typed([u16(t[s:e]) for t in x], dt, B, O.CODEC_BF16)
+        assert (u16(whole[s:e]) == want).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (u16(codes[r][s:e]) == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
 
 
 @pytest.mark.parametrize("k", [1, 2, 4, 8])
