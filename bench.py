@@ -202,11 +202,14 @@ class DdpBuckets(Workload):
         self.lay = gb.gb_bucket_workspace_layout(self.codec, self.k, self.n, self.bucket)
         self.ws = torch.empty(max(1, self.lay["total"]), dtype=torch.uint8, device=self.dev)
 
-    def step(self):
+    def call(self, out, xs, ws):
         if self.dt == "f32":
-            self.gb.gb_bucket_allreduce_local(self.out, self.x, self.bucket, self.codec, self.mode, self.ws)
+            self.gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
         else:
-            self.gb.gb_bucket_allreduce_local_typed(self.out, self.x, self.bucket, self.codec, self.mode, self.ws)
+            self.gb.gb_bucket_allreduce_local_typed(out, xs, self.bucket, self.codec, self.mode, ws)
+
+    def step(self):
+        self.call(self.out, self.x, self.ws)
 
     def payload_bytes(self, n):
         return {2: n + 4 * nblocks(n), 1: 2 * n, 0: 0}[self.codec]
@@ -222,8 +225,12 @@ class DdpBuckets(Workload):
         et = self.gb.GB_DTYPE_OF[self.dt]
         # the four-rank float32 sum takes its wide kernel from 2^28 values per rank
         f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
-        # the float32 fp8 pass takes its 128-lane workgroups from 2^27 values per rank
-        fp8 = "fused_fp8_half_kernel<4>" if et == 0 and self.n >= (1 << 27) else f"fused_fp8_kernel<4,{et}>"
+        # the fp8 pass takes its 128-lane workgroups: float32 gradients from 2^27
+        # values per rank, float64 ones over 4 ranks between 3 * 2^21 and 2^29,
+        # float16 and bfloat16 ones between 2^22 and 2^26
+        n = self.n
+        half = {0: n >= (1 << 27), 3: (3 << 21) <= n < (1 << 29)}.get(et, (1 << 22) <= n < (1 << 26))
+        fp8 = f"fused_fp8_half_kernel<4,{et}>" if half else f"fused_fp8_kernel<4,{et}>"
         # and the bf16 pass its 64-lane workgroups: float32 gradients over 3 or
         # more ranks, float16 and bfloat16 ones over 4 or more from 2^22 values
         wave = et == 0 or (et in (1, 2) and self.n >= (1 << 22))
@@ -233,22 +240,21 @@ class DdpBuckets(Workload):
         return (name, self.step_bytes(), 1, self.step)
 
     def per_bucket_step(self):
-        gb = self.gb
         for out, xs, ws in self.pb_args:
-            gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
+            self.call(out, xs, ws)
 
     def per_bucket_step_streams(self, m):
         """The per-bucket calls dealt round-robin over the current stream and
         m - 1 more (all at the default priority), forked from and joined back
         into the current stream, so m buckets are in flight at once."""
-        torch, gb = self.torch, self.gb
+        torch = self.torch
         main = torch.cuda.current_stream()
         streams = [main] + self.side[:m - 1]
         for st in streams[1:]:
             st.wait_stream(main)
         for i, (out, xs, ws) in enumerate(self.pb_args):
             with torch.cuda.stream(streams[i % m]):
-                gb.gb_bucket_allreduce_local(out, xs, self.bucket, self.codec, self.mode, ws)
+                self.call(out, xs, ws)
         for st in streams[1:]:
             main.wait_stream(st)
 
@@ -260,11 +266,11 @@ class DdpBuckets(Workload):
         binding's per-call cost; every replay's output is checked against the
         single-launch result.  The same calls are also timed dealt over two and
         over four streams inside one graph.  Leaves the workspace in the per-bucket
-        layout.  Measured on float32 gradients only."""
+        layout."""
         torch, gb = self.torch, self.gb
-        if self.dt != "f32":
-            return {}
         want = self.out.clone()
+        ibits = {2: torch.int16, 4: torch.int32, 8: torch.int64}[self.esize]
+        matches = lambda: bool(torch.equal(self.out.view(ibits), want.view(ibits)))
         self.pb_args = []
         off = 0
         for start, length in self.buckets():
@@ -275,16 +281,16 @@ class DdpBuckets(Workload):
             off += need
         self.per_bucket_step()  # eager, also warms up
         torch.cuda.synchronize()
-        eager_ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        eager_ok = matches()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             self.per_bucket_step()
         self.out.zero_()
         graph.replay()
         torch.cuda.synchronize()
-        replay_ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        replay_ok = matches()
         ms = time_region(graph.replay, reps) / reps
-        replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        replay_ok &= matches()
         eager_ms = time_region(self.per_bucket_step, reps) / reps
         del graph
         # the same calls over 2 and 4 streams: the buckets' workspace slices
@@ -300,9 +306,9 @@ class DdpBuckets(Workload):
             self.out.zero_()
             graph.replay()
             torch.cuda.synchronize()
-            replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+            replay_ok &= matches()
             ms_m = time_region(graph.replay, reps) / reps
-            replay_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+            replay_ok &= matches()
             del graph
             by_streams[m] = ms_m
         # the same buckets through gb_bucket_allreduce_local_batch: up to 16
@@ -321,9 +327,9 @@ class DdpBuckets(Workload):
         self.out.zero_()
         graph.replay()
         torch.cuda.synchronize()
-        batch_ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        batch_ok = matches()
         ms_batch = time_region(graph.replay, reps) / reps
-        batch_ok &= bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        batch_ok &= matches()
         del graph
         gbs = lambda t: round(self.step_bytes() / (t * 1e-3) / 1e9, 2)
         return {"per_bucket_batched_graph_gbs": gbs(ms_batch),

@@ -272,9 +272,9 @@ int main(int argc, char** argv) {
     sct.p[r] = scales + (size_t)r * nblk;
   }
   const double replica_bytes = (double)nval * (16.0 + 4.0 + 16.0 / 256 + 4.0);
-  static_assert(gb::fused_fp8_half(4, (size_t)1 << 28), "the replica's shape is the pass's from 2^28 values");
+  static_assert(gb::fused_fp8_half<GB_DTYPE_F32>(4, (size_t)1 << 28), "the replica's shape is the pass's from 2^28 values");
   measure("fused_fp8_replica_" + sz, replica_bytes, reps, [&] {
-    replica_kernel<<<nblk / (gb::kHalfThreads / 16), gb::kHalfThreads, gb::fused_fp8_half_lds(4)>>>(
+    replica_kernel<<<nblk / (gb::kHalfThreads / 16), gb::kHalfThreads, gb::fused_fp8_half_lds<GB_DTYPE_F32>(4)>>>(
         st, ct, sct, reinterpret_cast<float*>(buf[4]));
   });
 

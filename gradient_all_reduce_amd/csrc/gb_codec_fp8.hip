@@ -162,17 +162,19 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable
   else fused_fp8_body<K, ET, false>(out, src, codes, scales, n, mode, g);
 }
 
-// The same pass over float32 gradients in 128-lane workgroups taken in
-// index order: the shape for large buffers (fused_fp8_half).
-template <int K>
+// The same pass in 128-lane workgroups (8 blocks) taken in index order, at
+// the sizes fused_fp8_half names for each gradient type.  Every lane map
+// places a block by its index alone, so the bits are those of the 256-lane
+// kernel.
+template <int K, int ET>
 __global__ __launch_bounds__(kHalfThreads) void fused_fp8_half_kernel(void* out, PtrTable src, OutTable codes,
                                                                       OutTable scales, size_t n, int mode) {
   constexpr size_t per_group = (kHalfThreads / 16) * kBlock;
   const size_t g = blockIdx.x;
   if ((g + 1) * per_group <= n) {
-    fused_fp8_body<K, GB_DTYPE_F32, true, 0, kHalfThreads>(out, src, codes, scales, n, mode, g);
+    fused_fp8_body<K, ET, true, 0, kHalfThreads>(out, src, codes, scales, n, mode, g);
   } else {
-    fused_fp8_body<K, GB_DTYPE_F32, false, 0, kHalfThreads>(out, src, codes, scales, n, mode, g);
+    fused_fp8_body<K, ET, false, 0, kHalfThreads>(out, src, codes, scales, n, mode, g);
   }
 }
 
@@ -231,16 +233,15 @@ hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales
 template <int ET>
 hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const OutTable& s, int k, size_t n,
                        int scale_mode, hipStream_t stream) {
-  if constexpr (ET == GB_DTYPE_F32) {
-    if (fused_fp8_half(k, n)) {
-      const size_t half_grid = ceil_div(n, (kHalfThreads / 16) * kBlock);
-      if (half_grid > kMaxGrid) return hipErrorInvalidValue;
-#define GB_CALL(K) \
-  fused_fp8_half_kernel<K><<<half_grid, kHalfThreads, fused_fp8_half_lds(K), stream>>>(out, srcs, c, s, n, scale_mode);
-      GB_DISPATCH_K(k, GB_CALL)
+  if (fused_fp8_half<ET>(k, n)) {
+    const size_t half_grid = ceil_div(n, (kHalfThreads / 16) * kBlock);
+    if (half_grid > kMaxGrid) return hipErrorInvalidValue;
+#define GB_CALL(K)                                                                                   \
+  fused_fp8_half_kernel<K, ET><<<half_grid, kHalfThreads, fused_fp8_half_lds<ET>(K), stream>>>(out, srcs, c, s, n, \
+                                                                                              scale_mode);
+    GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-      return hipGetLastError();
-    }
+    return hipGetLastError();
   }
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;

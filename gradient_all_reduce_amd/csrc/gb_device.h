@@ -815,11 +815,32 @@ __host__ __device__ constexpr unsigned fused_fp8_lds(int k, size_t n) {
 // from 2^28; the 256-lane workgroup at 1 per unit (the same 4 wavefronts per
 // unit) and every permuted order of the 128-lane one did worse, and so did
 // the 128-lane shape at bucket sizes (6,553,600 values) and up to 2^26.
+//
+// Float64 gradients take the 128-lane shape at 2 per unit from 3 * 2^21
+// values, up to 3 ranks at every size and over more only below 2^29: from
+// one bucket to 2^28 values 1.3-10.9% more bytes per second over 2, 3, 4, 6
+// and 8 ranks; at 1e9 +8% over 2 ranks and +4.7% over 3, level over 4
+// (+0.0% and +1.2% in two runs) and -1.7 to -2.4% over 6 and 8; at 2^20
+// values it lost up to 10%, and at 2^22 4-5% over 2 and 3 ranks.
+// Float16 and bfloat16 gradients take it uncapped from 4 ranks between 2^22
+// and 2^26 values, where the 256-lane kernel runs uncapped too: -0.4 to
+// +9.6% over 4 and 8 ranks (+9% at 2^22 over 8); it lost 1-17% at 2^20,
+// over 2 ranks it was level, and from 2^26, where the 256-lane kernel is
+// capped, it gained nothing consistent.  Measured on MI355X against the
+// library's 256-lane kernel in one process, same bits.
 constexpr int kHalfThreads = 128;
+template <int ET>
 __host__ __device__ constexpr bool fused_fp8_half(int k, size_t n) {
+  if (ET == GB_DTYPE_F64) return n >= ((size_t)3 << 21) && (k <= 3 || n < ((size_t)1 << 29));
+  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return k >= 4 && n >= ((size_t)1 << 22) && n < ((size_t)1 << 26);
   return (k >= 3 && n >= ((size_t)1 << 27)) || (k == 2 && n >= ((size_t)1 << 28));
 }
-__host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) { return k >= 4 ? kTwoPerCuLds : kThreePerCuLds; }
+template <int ET>
+__host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) {
+  if (ET == GB_DTYPE_F64) return kTwoPerCuLds;
+  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return 0u;
+  return k >= 4 ? kTwoPerCuLds : kThreePerCuLds;
+}
 
 // Fused fp8 pass with error feedback (21 streams at k = 4: sources and
 // residuals read; codes, scales, residuals and the sum written): 1 per unit

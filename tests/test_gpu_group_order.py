@@ -8,7 +8,8 @@
   4096-value fp8 groups;
 - the wide four-rank sum, from 2^28 values;
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
-  values, 2^28 over two ranks);
+  values, 2^28 over two ranks; float64 gradients from 3 * 2^21 values;
+  float16 and bfloat16 gradients from 4 ranks between 2^22 and 2^26 values);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
   ranks; float16 and bfloat16 gradients from 4 ranks and 2^22 values; with
   error feedback, from 1 rank).
@@ -191,6 +192,56 @@ def test_fused_fp8_half_workgroups(gb, k):
         want, wc, wsc = O.bucket_allreduce([t[s:e].cpu().numpy() for t in x], B, O.CODEC_FP8,
                                            O.SCALE_ABSMAX_DIV_448)
         assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+            got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
+            assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+
+
+HALF_LO, HALF_HI, F64_LO = 1 << 22, 1 << 26, 3 << 21
+
+
+@pytest.mark.parametrize("dt,k,n", [
+    ("f64", 2, F64_LO + 2048 * 5 + 77), ("f64", 4, F64_LO + 2048 * 5 + 77), ("f64", 8, F64_LO + 2048 * 5 + 77),
+    ("f64", 4, F64_LO - 2048 - 77),
+    ("bf16", 4, HALF_LO + 2048 * 3 + 77), ("bf16", 8, HALF_LO + 2048 * 3 + 77), ("bf16", 4, HALF_HI - 2048 * 3 - 77),
+    ("bf16", 4, HALF_LO - 2048 - 77), ("bf16", 4, HALF_HI + 2048 + 77), ("bf16", 2, HALF_LO + 2048 * 3 + 77),
+    ("f16", 4, HALF_LO + 2048 * 3 + 77), ("f16", 8, HALF_HI - 2048 * 3 - 77)])
+def test_fused_fp8_half_typed_workgroups(gb, dt, k, n):
+    """The fused fp8 bucket stream runs in 128-lane workgroups in index order
+    over float64 gradients from 3 * 2^21 values per rank (2 per CU) and over
+    float16 and bfloat16 gradients from 4 ranks between 2^22 and 2^26 values
+    (uncapped); elsewhere in 256-lane ones.  On either side of each
+    threshold, with a ragged last workgroup and block, it must equal the
+    256-lane batch kernel on the same buffers (a batch of one bucket), and
+    the oracle on sampled windows (the first and the last values included):
+    totals, codes and scales."""
+    import numpy as np
+    from oracle import oracle as O
+    fp8 = gb.GB_CODEC_FP8_E4M3_B256
+    x = [W.device_gradients_typed(n, 1700 + 10 * k + r, DEV, dt) for r in range(k)]
+    lay = gb.gb_bucket_workspace_layout(fp8, k, n, B)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n, x[0].dtype), filled(n, x[0].dtype)
+    gb.gb_bucket_allreduce_local_typed(whole, x, B, fp8, 0, ws)
+    wsb = torch.empty(gb.gb_bucket_batch_workspace_bytes(fp8, k, [n]), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch([ref], [x], fp8, workspace=wsb)
+    same(whole, ref, f"fused fp8 pass over {k} ranks of {dt} against the batch kernel")
+    del ref, wsb
+    nb = (n + 255) // 256
+    codes = [ws[r * lay["codes_stride"]:][:n] for r in range(k)]
+    scales = [ws[lay["scales_offset"] + r * lay["scales_stride"]:][:4 * nb].view(torch.float32) for r in range(k)]
+    host = lambda t: bits(t).cpu().numpy()
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    length = 65536
+    rng = np.random.default_rng(150 + k)
+    last = (n - length) // 256 * 256
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 3)]:
+        e = n if s == last else s + length
+        xs = [host(t[s:e]).view(np.uint16) if dt != "f64" else t[s:e].cpu().numpy() for t in x]
+        want, wc, wsc = O.bucket_allreduce_typed(xs, dt, B, O.CODEC_FP8, O.SCALE_ABSMAX_DIV_448)
+        assert (host(whole[s:e]) == np.ascontiguousarray(want).view(host(whole[:1]).dtype)).all(), \
+            f"oracle total window at {s}"
         for r in range(k):
             assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
             got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
