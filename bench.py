@@ -232,8 +232,8 @@ class DdpBuckets(Workload):
         half = {0: n >= (1 << 27), 3: (3 << 21) <= n < (1 << 29)}.get(et, (1 << 22) <= n < (1 << 26))
         fp8 = f"fused_fp8_half_kernel<4,{et}>" if half else f"fused_fp8_kernel<4,{et}>"
         # and the bf16 pass its 64-lane workgroups: float32 gradients over 3 or
-        # more ranks, float16 and bfloat16 ones over 4 or more from 2^22 values
-        wave = et == 0 or (et in (1, 2) and self.n >= (1 << 22))
+        # more ranks, float16 and bfloat16 ones over 4 from 2^29 values
+        wave = et == 0 or (et in (1, 2) and self.n >= (1 << 29))
         bf16 = f"fused_bf16_wave_kernel<4,{et}>" if wave else f"fused_bf16_kernel<4,{et}>"
         name = {2: fp8, 1: bf16,
                 0: f32_sum if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]

@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(void* out, PtrTabl
 
 // The same pass in 64-lane workgroups of 256 values (wave_lane), taken in
 // index order: float32 gradients from 3 ranks (fused_bf16_wave), float16
-// and bfloat16 ones from 4 ranks and 2^22 values (fused_bf16_half_wave).  A
+// and bfloat16 ones from 5 ranks and 2^22 values or 4 ranks and 2^29
+// (fused_bf16_half_wave).  A
 // buffer's last vector group may leave up to 3 workgroups with no values;
 // they return.
 template <int K, int ET>

@@ -906,16 +906,20 @@ __host__ __device__ constexpr unsigned fused_bf16_wave_lds(int k, size_t n) {
   return k <= 3 ? (12u << 10) : k == 4 ? (16u << 10) : k <= 6 ? (20u << 10) : (24u << 10);
 }
 // The same 64-lane pass over float16 and bfloat16 gradients (half the bytes
-// of a float32 lane in flight per rank) from 4 ranks and 2^22 values per
-// rank, capped at 13 per unit over 4 or 5 ranks, 10 over 6 or 7 and 8 over
-// 8.  Measured on MI355X against the 256-lane kernel in one process, same
-// bits, both types alike, from 2^22 values (and one 25 MiB bucket,
-// 13,107,200 values) to 1e9: 4 ranks -0.2 to +5.5% more bytes per second,
-// 5 ranks +0.5-10%, 6 ranks -2.6 to +11% (the loss at 6,553,600 values,
-// where the 256-lane kernel itself varies by 12% between runs), 7 and 8
-// ranks +3.5-18%.  At 2^20 values every 64-lane shape lost 2-13%, and over
-// 2 or 3 ranks nothing gained at every size.
-__host__ __device__ constexpr bool fused_bf16_half_wave(int k, size_t n) { return k >= 4 && n >= ((size_t)1 << 22); }
+// of a float32 lane in flight per rank): over 5 to 8 ranks from 2^22 values
+// per rank, over 4 from 2^29; capped at 13 per unit over 4 or 5 ranks, 10
+// over 6 or 7 and 8 over 8.  Measured on MI355X against the 256-lane kernel
+// in one process, same bits, both types alike, on two machines.  At 1e9
+// values +0.8-10% more bytes per second over every rank count from 4 to 8
+// (one run -0.4% over 5), and over 4 ranks from 2^29 +0.2-5.3%.  Over 5 to 8
+// ranks at 2^22-2^23 values +1-7%.  Between 6,553,600 values and 2^26 one
+// machine gained 2-18% and the other was level (-4.4 to +6.3%).  Over 4
+// ranks below 2^28 the second machine lost up to 6.8%, at 2^20 values every
+// 64-lane shape lost 2-13%, and over 2 or 3 ranks nothing gained at every
+// size.
+__host__ __device__ constexpr bool fused_bf16_half_wave(int k, size_t n) {
+  return (k == 4 && n >= ((size_t)1 << 29)) || (k >= 5 && n >= ((size_t)1 << 22));
+}
 __host__ __device__ constexpr unsigned fused_bf16_half_wave_lds(int k) {
   return k <= 5 ? (12u << 10) : k <= 7 ? (16u << 10) : (20u << 10);
 }

@@ -11,8 +11,8 @@
   values, 2^28 over two ranks; float64 gradients from 3 * 2^21 values;
   float16 and bfloat16 gradients from 4 ranks between 2^22 and 2^26 values);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
-  ranks; float16 and bfloat16 gradients from 4 ranks and 2^22 values; with
-  error feedback, from 1 rank).
+  ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
+  4 ranks and 2^29; with error feedback, from 1 rank).
 
 Each must give, bit for bit, what the same arithmetic gives in another
 shape: over slices of the stream small enough to keep the index order and
@@ -284,16 +284,16 @@ def test_fused_bf16_wave_workgroups(gb, k, n):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-@pytest.mark.parametrize("k", [4, 5, 6, 7, 8])
-@pytest.mark.parametrize("n", [(1 << 22) + 256 * 5 + 77, (1 << 22) - 3 * 64 - 5])
+@pytest.mark.parametrize("k,n", [(k, (1 << 22) + 256 * 5 + 77) for k in (5, 6, 7, 8)]
+                         + [(5, (1 << 22) - 3 * 64 - 5), (4, (1 << 29) + 256 * 5 + 77), (4, (1 << 29) - 3 * 64 - 5)])
 def test_fused_bf16_half_wave_workgroups(gb, dt, k, n):
-    """The fused bf16 bucket stream over float16 and bfloat16 gradients from
-    4 ranks runs in 64-lane workgroups in index order from 2^22 values,
-    capped by rank count, and in 256-lane workgroups below.  With a ragged
-    last workgroup, on either side of the threshold, it must equal the
-    256-lane batch kernel on the same buffers (a batch of one bucket), and the
-    oracle on sampled windows (the first and last values included): totals
-    and codes."""
+    """The fused bf16 bucket stream over float16 and bfloat16 gradients runs
+    in 64-lane workgroups in index order, capped by rank count, over 5 to 8
+    ranks from 2^22 values and over 4 from 2^29; in 256-lane workgroups
+    below.  With a ragged last workgroup, on either side of each threshold,
+    it must equal the 256-lane batch kernel on the same buffers (a batch of
+    one bucket), and the oracle on sampled windows (the first and last values
+    included): totals and codes."""
     import numpy as np
     from oracle import oracle as O
     bf16 = gb.GB_CODEC_BF16
