@@ -226,10 +226,9 @@ class DdpBuckets(Workload):
         # the four-rank float32 sum takes its wide kernel from 2^28 values per rank
         f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
         # the fp8 pass takes its 128-lane workgroups: float32 gradients from 2^27
-        # values per rank, float64 ones over 4 ranks between 3 * 2^21 and 2^29,
-        # float16 and bfloat16 ones between 2^22 and 2^26
+        # values per rank, float64 ones over 4 ranks between 3 * 2^21 and 2^29
         n = self.n
-        half = {0: n >= (1 << 27), 3: (3 << 21) <= n < (1 << 29)}.get(et, (1 << 22) <= n < (1 << 26))
+        half = {0: n >= (1 << 27), 3: (3 << 21) <= n < (1 << 29)}.get(et, False)
         fp8 = f"fused_fp8_half_kernel<4,{et}>" if half else f"fused_fp8_kernel<4,{et}>"
         # and the bf16 pass its 64-lane workgroups: float32 gradients over 3 or
         # more ranks, float16 and bfloat16 ones over 4 from 2^29 values
@@ -409,18 +408,17 @@ class DdpBucketsEF(DdpBuckets):
     def timed_kernel(self):
         et = self.gb.GB_DTYPE_OF[self.dt]
         fp8 = self.codec == self.gb.GB_CODEC_FP8_E4M3_B256
-        # the float32 bf16 pass takes 64-lane workgroups at every size
-        bf16 = "fused_bf16_ef_wave_kernel<4>" if et == 0 else f"fused_bf16_ef_kernel<4,{et}>"
+        # the bf16 pass over four ranks takes 64-lane workgroups at every size,
+        # for every gradient type
+        bf16 = f"fused_bf16_ef_wave_kernel<4,{et}>"
         name = f"fused_fp8_ef_kernel<4,{et}>" if fp8 else bf16
         return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):
-        """The same step as one gb_bucket_allreduce_local_ef call per bucket
-        and through gb_bucket_allreduce_local_batch_ef (8 buckets per launch),
-        each captured in a HIP graph; the two give the same bits from the
-        same residuals."""
-        if self.dt != "f32":
-            return {}
+        """The same step as one gb_bucket_allreduce_local_ef (or _ef_typed)
+        call per bucket and through gb_bucket_allreduce_local_batch_ef (8
+        buckets per launch), each captured in a HIP graph; the two give the
+        same bits from the same residuals."""
         torch, gb = self.torch, self.gb
         buckets = list(self.buckets())
         outs = [self.out[s:s + n] for s, n in buckets]
@@ -432,9 +430,11 @@ class DdpBucketsEF(DdpBuckets):
             wsl.append(self.ws[off:off + need])
             off += need
 
+        call = gb.gb_bucket_allreduce_local_ef if self.dt == "f32" else gb.gb_bucket_allreduce_local_ef_typed
+
         def per_bucket():
             for o, xs, rs, w in zip(outs, srcs, ress, wsl):
-                gb.gb_bucket_allreduce_local_ef(o, xs, rs, self.bucket, self.codec, self.mode, w)
+                call(o, xs, rs, self.bucket, self.codec, self.mode, w)
 
         need = gb.gb_bucket_batch_workspace_bytes(self.codec, self.k, [n for _, n in buckets])
         wsb = self.ws if need <= self.ws.numel() else torch.empty(need, dtype=torch.uint8, device=self.dev)
@@ -447,7 +447,8 @@ class DdpBucketsEF(DdpBuckets):
             t.copy_(s0)
         batch()
         torch.cuda.synchronize()
-        ok = bool(torch.equal(self.out.view(torch.int32), want.view(torch.int32)))
+        ibits = {2: torch.int16, 4: torch.int32, 8: torch.int64}[self.esize]
+        ok = bool(torch.equal(self.out.view(ibits), want.view(ibits)))
         ok &= all(bool(torch.equal(a.view(torch.int32), b.view(torch.int32))) for a, b in zip(self.res, want_res))
         del saved, want, want_res
         ms = {}

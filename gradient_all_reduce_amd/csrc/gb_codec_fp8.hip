@@ -163,9 +163,9 @@ __global__ __launch_bounds__(kThreads) void fused_fp8_kernel(void* out, PtrTable
 }
 
 // The same pass in 128-lane workgroups (8 blocks) taken in index order, at
-// the sizes fused_fp8_half names for each gradient type.  Every lane map
-// places a block by its index alone, so the bits are those of the 256-lane
-// kernel.
+// the sizes fused_fp8_half names for float32 and float64 gradients.  Both
+// lane maps place a block by its index alone, so the bits are those of the
+// 256-lane kernel.
 template <int K, int ET>
 __global__ __launch_bounds__(kHalfThreads) void fused_fp8_half_kernel(void* out, PtrTable src, OutTable codes,
                                                                       OutTable scales, size_t n, int mode) {
@@ -233,15 +233,17 @@ hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales
 template <int ET>
 hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const OutTable& s, int k, size_t n,
                        int scale_mode, hipStream_t stream) {
-  if (fused_fp8_half<ET>(k, n)) {
-    const size_t half_grid = ceil_div(n, (kHalfThreads / 16) * kBlock);
-    if (half_grid > kMaxGrid) return hipErrorInvalidValue;
+  if constexpr (ET == GB_DTYPE_F32 || ET == GB_DTYPE_F64) {
+    if (fused_fp8_half<ET>(k, n)) {
+      const size_t half_grid = ceil_div(n, (kHalfThreads / 16) * kBlock);
+      if (half_grid > kMaxGrid) return hipErrorInvalidValue;
 #define GB_CALL(K)                                                                                   \
   fused_fp8_half_kernel<K, ET><<<half_grid, kHalfThreads, fused_fp8_half_lds<ET>(K), stream>>>(out, srcs, c, s, n, \
                                                                                               scale_mode);
-    GB_DISPATCH_K(k, GB_CALL)
+      GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-    return hipGetLastError();
+      return hipGetLastError();
+    }
   }
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;

@@ -821,25 +821,25 @@ __host__ __device__ constexpr unsigned fused_fp8_lds(int k, size_t n) {
 // one bucket to 2^28 values 1.3-10.9% more bytes per second over 2, 3, 4, 6
 // and 8 ranks; at 1e9 +8% over 2 ranks and +4.7% over 3, level over 4
 // (+0.0% and +1.2% in two runs) and -1.7 to -2.4% over 6 and 8; at 2^20
-// values it lost up to 10%, and at 2^22 4-5% over 2 and 3 ranks.
-// Float16 and bfloat16 gradients take it uncapped from 4 ranks between 2^22
-// and 2^26 values, where the 256-lane kernel runs uncapped too: -0.4 to
-// +9.6% over 4 and 8 ranks (+9% at 2^22 over 8); it lost 1-17% at 2^20,
-// over 2 ranks it was level, and from 2^26, where the 256-lane kernel is
-// capped, it gained nothing consistent.  Measured on MI355X against the
-// library's 256-lane kernel in one process, same bits.
+// values it lost up to 10%, and at 2^22 4-5% over 2 and 3 ranks.  Measured
+// on MI355X against the library's 256-lane kernel in one process, same
+// bits; in the benchmark's bucket stream over 4 ranks, against the library
+// without the rule on the same machine: +3.7-4.0% at 1.25e8 values per
+// rank, and one call per 6,553,600-value bucket +6.4% on one stream and
+// +2.7% over two.  Float16 and bfloat16 gradients keep the 256-lane kernel:
+// uncapped 128-lane workgroups gained up to 9.6% between 2^22 and 2^26
+// values in one process, but the benchmark's one call per bucket (6,553,600
+// values) gained 1% on one stream and lost 2-3% over two and four.
 constexpr int kHalfThreads = 128;
 template <int ET>
 __host__ __device__ constexpr bool fused_fp8_half(int k, size_t n) {
   if (ET == GB_DTYPE_F64) return n >= ((size_t)3 << 21) && (k <= 3 || n < ((size_t)1 << 29));
-  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return k >= 4 && n >= ((size_t)1 << 22) && n < ((size_t)1 << 26);
+  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return false;
   return (k >= 3 && n >= ((size_t)1 << 27)) || (k == 2 && n >= ((size_t)1 << 28));
 }
 template <int ET>
 __host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) {
-  if (ET == GB_DTYPE_F64) return kTwoPerCuLds;
-  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return 0u;
-  return k >= 4 ? kTwoPerCuLds : kThreePerCuLds;
+  return ET == GB_DTYPE_F64 ? kTwoPerCuLds : (k >= 4 ? kTwoPerCuLds : kThreePerCuLds);
 }
 
 // Fused fp8 pass with error feedback (21 streams at k = 4: sources and
@@ -932,7 +932,31 @@ __host__ __device__ constexpr unsigned fused_bf16_half_wave_lds(int k) {
 // bits: 4-24% more bytes per second from one 25 MiB bucket to 1e9 values
 // over every rank count from 1 to 8 (4 ranks: +14.5% at a bucket, +12% at
 // 1e9), and 2-19% at 2^20 and 2^22 values.
+//
+// Float16 and bfloat16 gradients (24 bytes of every rank in flight per lane:
+// 8 of gradient, 16 of residual) take the 64-lane shape over 4 to 8 ranks at
+// every size and over 2 or 3 from 2^22 values, capped at 13 per unit over 2
+// ranks, 10 over 3, 8 over 4 and 6 over 5 to 8.  Float64 gradients (48
+// bytes) take it over 2 and 4 to 8 ranks at every size and over 1 or 3 from
+// 2^22 values, at 13 per unit over 1 rank, 10 over 2 and 6 over 3 to 8.
+// Measured on MI355X against the 256-lane kernel (its rule below) in one
+// process, same bits, from 2^20 values to 1e9 (1 to 4 ranks) or 2^26 (5 to 8
+// ranks): bfloat16 +2.3-18.7% (4 to 8 ranks +4-18.7%), float16 +0.6-10.4%,
+// float64 +0.9-12.9%.  Over 1 to 3 ranks at 2^20 values every 64-lane shape
+// lost up to 7%; one rank of a 2-byte type gained only from 2^26 values
+// (1-3%) and keeps the 256-lane kernel.
+template <int ET>
+__host__ __device__ constexpr bool fused_bf16_ef_wave(int k, size_t n) {
+  if (ET == GB_DTYPE_F64) return (k == 1 || k == 3) ? n >= ((size_t)1 << 22) : true;
+  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return k >= 4 || (k >= 2 && n >= ((size_t)1 << 22));
+  return true;
+}
+template <int ET>
 __host__ __device__ constexpr unsigned fused_bf16_ef_wave_lds(int k) {
+  if (ET == GB_DTYPE_F64) return k <= 1 ? (12u << 10) : k == 2 ? (16u << 10) : (24u << 10);
+  if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) {
+    return k <= 2 ? (12u << 10) : k == 3 ? (16u << 10) : k == 4 ? (20u << 10) : (24u << 10);
+  }
   return k <= 1 ? (12u << 10) : k == 2 ? (16u << 10) : k <= 4 ? (24u << 10) : (32u << 10);
 }
 

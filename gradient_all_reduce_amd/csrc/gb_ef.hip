@@ -143,7 +143,8 @@ template <int K, int ET>
 __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrTable src, OutTable resid,
                                                                   OutTable codes, size_t n) {
   // float32 gradients (here only beyond the largest 64-lane grid) in the
-  // permuted order; the others move more bytes per second in index order
+  // permuted order; the others (here below the 64-lane thresholds or beyond
+  // the largest 64-lane grid) move more bytes per second in index order
   // (1-7%, up to 21% with error feedback over bfloat16), measured on three
   // machines
   const size_t sg = ET == GB_DTYPE_F32 ? group_index<FusedVecOrder>() : (size_t)blockIdx.x;
@@ -151,17 +152,20 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_kernel(void* out, PtrT
   else fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, sg, threadIdx.x);
 }
 
-// The same pass over float32 gradients in 64-lane workgroups of 256 values
-// (wave_lane), taken in index order.
-template <int K>
+// The same pass in 64-lane workgroups of 256 values (wave_lane), taken in
+// index order, where fused_bf16_ef_wave says.  A float64 lane holds values
+// 2t, 2t + 1, 2t + 512 and 2t + 513 of its vector group, so its workgroup
+// lies below n only when the whole group does.
+template <int K, int ET>
 __global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_kernel(void* out, PtrTable src, OutTable resid,
                                                                           OutTable codes, size_t n) {
   const size_t w = blockIdx.x;
   const WaveLane l = wave_lane(w);
-  if ((w + 1) * (kVecPerGroup / 4) <= n) {
-    fused_bf16_ef_body<K, GB_DTYPE_F32, true>(out, src, resid, codes, n, l.sg, l.t);
+  const bool full = ET == GB_DTYPE_F64 ? (l.sg + 1) * kVecPerGroup <= n : (w + 1) * (kVecPerGroup / 4) <= n;
+  if (full) {
+    fused_bf16_ef_body<K, ET, true>(out, src, resid, codes, n, l.sg, l.t);
   } else {
-    fused_bf16_ef_body<K, GB_DTYPE_F32, false>(out, src, resid, codes, n, l.sg, l.t);
+    fused_bf16_ef_body<K, ET, false>(out, src, resid, codes, n, l.sg, l.t);
   }
 }
 
@@ -212,9 +216,10 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_ef_batch_kernel(BucketBat
   }
 }
 
-// The batch over float32 gradients in 64-lane workgroups: bucket b takes
-// workgroups [first[b], first[b + 1]), four per vector group.
-template <int K, int DIV>
+// The batch in 64-lane workgroups: bucket b takes workgroups
+// [first[b], first[b + 1]), four per vector group; a float64 workgroup is
+// whole only with its vector group, as in the whole-buffer kernel.
+template <int K, int ET, int DIV>
 __global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_batch_kernel(BucketBatchEf t, float dv, float inv) {
   const size_t w = blockIdx.x;
   uint32_t b = 0;
@@ -229,10 +234,11 @@ __global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_batch_kernel(
   }
   const size_t wl = w - t.first[b], n = t.n[b];
   const WaveLane l = wave_lane(wl);
-  if ((wl + 1) * (kVecPerGroup / 4) <= n) {
-    fused_bf16_ef_body<K, GB_DTYPE_F32, true, DIV>(t.out[b], src, resid, codes, n, l.sg, l.t, dv, inv);
+  const bool full = ET == GB_DTYPE_F64 ? (l.sg + 1) * kVecPerGroup <= n : (wl + 1) * (kVecPerGroup / 4) <= n;
+  if (full) {
+    fused_bf16_ef_body<K, ET, true, DIV>(t.out[b], src, resid, codes, n, l.sg, l.t, dv, inv);
   } else {
-    fused_bf16_ef_body<K, GB_DTYPE_F32, false, DIV>(t.out[b], src, resid, codes, n, l.sg, l.t, dv, inv);
+    fused_bf16_ef_body<K, ET, false, DIV>(t.out[b], src, resid, codes, n, l.sg, l.t, dv, inv);
   }
 }
 
@@ -266,19 +272,22 @@ template <int ET, int DIV>
 hipError_t fused_bf16_ef_batch_t(BucketBatchEf& t, int k, float dv, float inv, hipStream_t stream) {
   const size_t grid = batch_grid(t, GB_CODEC_BF16);
   if (grid == 0) return hipErrorInvalidValue;
-  if constexpr (ET == GB_DTYPE_F32) {
-    // four 64-lane workgroups per vector group, at the whole-buffer kernel's
-    // cap: 8-bucket batches over 4 ranks moved 21% (whole 25 MiB buckets)
-    // and 19% (819,200-value ones) more bytes per second than the 256-lane
-    // batch kernel at 1 per unit
-    if (grid <= kMaxGrid / 4) {
-      for (int b = 0; b <= kBatchBucketsEf; b++) t.first[b] *= 4;
-#define GB_CALL(K) \
-  fused_bf16_ef_wave_batch_kernel<K, DIV><<<4 * grid, kWaveThreads, fused_bf16_ef_wave_lds(K), stream>>>(t, dv, inv);
-      GB_DISPATCH_K(k, GB_CALL)
+  size_t largest = 0;
+  for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
+  // four 64-lane workgroups per vector group, at the whole-buffer kernel's
+  // rule and cap for the largest bucket: 8-bucket batches over 4 ranks
+  // (whole 25 MiB buckets of float32 gradients, 6,553,600-value buckets of
+  // the other types, and buckets of 819,200 values) moved more bytes per
+  // second than the 256-lane batch kernel at its cap: float32 +19-21%,
+  // bfloat16 +27-32%, float64 +13-15%, float16 level (+0.6-0.9%)
+  if (fused_bf16_ef_wave<ET>(k, largest) && grid <= kMaxGrid / 4) {
+    for (int b = 0; b <= kBatchBucketsEf; b++) t.first[b] *= 4;
+#define GB_CALL(K)                                                                                               \
+  fused_bf16_ef_wave_batch_kernel<K, ET, DIV><<<4 * grid, kWaveThreads, fused_bf16_ef_wave_lds<ET>(K), stream>>>(t, dv, \
+                                                                                                              inv);
+    GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-      return hipGetLastError();
-    }
+    return hipGetLastError();
   }
 #define GB_CALL(K) \
   fused_bf16_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_bf16_ef_lds<ET>(K), stream>>>(t, dv, inv);
@@ -307,15 +316,14 @@ hipError_t encode_fp8_ef_t(uint8_t* codes, float* scales, float* residual, const
 template <int ET>
 hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, int k, size_t n,
                            hipStream_t stream) {
-  if constexpr (ET == GB_DTYPE_F32) {
-    const size_t wave_grid = wave_grid_for(n);
-    if (wave_grid != 0) {
-#define GB_CALL(K) \
-  fused_bf16_ef_wave_kernel<K><<<wave_grid, kWaveThreads, fused_bf16_ef_wave_lds(K), stream>>>(out, srcs, rs, c, n);
-      GB_DISPATCH_K(k, GB_CALL)
+  const size_t wave_grid = wave_grid_for(n);
+  if (fused_bf16_ef_wave<ET>(k, n) && wave_grid != 0) {
+#define GB_CALL(K)                                                                                       \
+  fused_bf16_ef_wave_kernel<K, ET><<<wave_grid, kWaveThreads, fused_bf16_ef_wave_lds<ET>(K), stream>>>(out, srcs, rs, \
+                                                                                                      c, n);
+    GB_DISPATCH_K(k, GB_CALL)
 #undef GB_CALL
-      return hipGetLastError();
-    }
+    return hipGetLastError();
   }
   const size_t grid = grid_for(n, 4);
   if (grid == 0) return hipErrorInvalidValue;

@@ -8,11 +8,11 @@
   4096-value fp8 groups;
 - the wide four-rank sum, from 2^28 values;
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
-  values, 2^28 over two ranks; float64 gradients from 3 * 2^21 values;
-  float16 and bfloat16 gradients from 4 ranks between 2^22 and 2^26 values);
+  values, 2^28 over two ranks; float64 gradients from 3 * 2^21 values);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
   ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
-  4 ranks and 2^29; with error feedback, from 1 rank).
+  4 ranks and 2^29; with error feedback, over float32 gradients from 1 rank
+  and over the other types by rank count and size).
 
 Each must give, bit for bit, what the same arithmetic gives in another
 shape: over slices of the stream small enough to keep the index order and
@@ -198,21 +198,17 @@ def test_fused_fp8_half_workgroups(gb, k):
             assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
 
 
-HALF_LO, HALF_HI, F64_LO = 1 << 22, 1 << 26, 3 << 21
+F64_LO = 3 << 21
 
 
 @pytest.mark.parametrize("dt,k,n", [
-    ("f64", 2, F64_LO + 2048 * 5 + 77), ("f64", 4, F64_LO + 2048 * 5 + 77), ("f64", 8, F64_LO + 2048 * 5 + 77),
-    ("f64", 4, F64_LO - 2048 - 77),
-    ("bf16", 4, HALF_LO + 2048 * 3 + 77), ("bf16", 8, HALF_LO + 2048 * 3 + 77), ("bf16", 4, HALF_HI - 2048 * 3 - 77),
-    ("bf16", 4, HALF_LO - 2048 - 77), ("bf16", 4, HALF_HI + 2048 + 77), ("bf16", 2, HALF_LO + 2048 * 3 + 77),
-    ("f16", 4, HALF_LO + 2048 * 3 + 77), ("f16", 8, HALF_HI - 2048 * 3 - 77)])
+    ("f64", 2, F64_LO + 2048 * 5 + 77), ("f64", 3, F64_LO + 2048 * 5 + 77), ("f64", 4, F64_LO + 2048 * 5 + 77),
+    ("f64", 8, F64_LO + 2048 * 5 + 77), ("f64", 4, F64_LO - 2048 - 77)])
 def test_fused_fp8_half_typed_workgroups(gb, dt, k, n):
     """The fused fp8 bucket stream runs in 128-lane workgroups in index order
-    over float64 gradients from 3 * 2^21 values per rank (2 per CU) and over
-    float16 and bfloat16 gradients from 4 ranks between 2^22 and 2^26 values
-    (uncapped); elsewhere in 256-lane ones.  On either side of each
-    threshold, with a ragged last workgroup and block, it must equal the
+    over float64 gradients from 3 * 2^21 values per rank (2 per CU; over 4
+    or more ranks below 2^29), in 256-lane ones below.  On either side of
+    the threshold, with a ragged last workgroup and block, it must equal the
     256-lane batch kernel on the same buffers (a batch of one bucket), and
     the oracle on sampled windows (the first and the last values included):
     totals, codes and scales."""
@@ -356,6 +352,68 @@ def test_fused_bf16_ef_wave_workgroups(gb, k, n):
         assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
         for r in range(k):
             assert (codes[r][s:e].cpu().numpy().view(np.uint16) == wc[r]).all(), f"oracle codes {r} at {s}"
+            assert (u32(res[r][s:e].cpu().numpy()) == u32(wr[r])).all(), f"oracle residual {r} at {s}"
+
+
+@pytest.mark.parametrize("dt,k,n", [
+    ("bf16", 1, (1 << 22) + 256 * 5 + 77), ("bf16", 2, (1 << 22) + 256 * 5 + 77), ("bf16", 2, (1 << 22) - 3 * 64 - 5), ("bf16", 3, (1 << 22) + 256 * 5 + 77), ("bf16", 4, (1 << 20) + 3 * 64 + 5), ("bf16", 8, (1 << 20) + 3 * 64 + 5),
+    ("f16", 2, (1 << 22) + 256 * 5 + 77), ("f16", 5, (1 << 20) + 3 * 64 + 5),
+    ("f64", 1, (1 << 22) + 256 * 5 + 77), ("f64", 1, (1 << 22) - 3 * 64 - 5), ("f64", 2, (1 << 20) + 3 * 64 + 5), ("f64", 3, (1 << 22) + 256 * 5 + 77), ("f64", 4, (1 << 20) + 3 * 64 + 5), ("f64", 8, (1 << 20) + 3 * 64 + 5)])
+def test_fused_bf16_ef_wave_typed_workgroups(gb, dt, k, n):
+    """The fused bf16 bucket stream with error feedback runs in 64-lane
+    workgroups in index order, capped by rank count: over float16 and
+    bfloat16 gradients from 4 ranks at every size and over 2 or 3 from 2^22
+    values (one rank keeps 256 lanes), over float64 gradients over 2 and 4 to
+    8 ranks at every size and over 1 or 3 from 2^22 values (a float64 lane
+    holds values 512 apart, so its workgroup is whole only with its vector
+    group).  On either side of each threshold, with a ragged last vector
+    group, it must equal the same step as separate 256-lane launches (each
+    rank's error-feedback encode, then the decode-and-add) and the batch
+    kernel (a batch of one bucket, which takes the same rule) from the same
+    residuals, and the oracle on sampled windows (the first and last values
+    included): totals, codes and new residuals."""
+    import numpy as np
+    from oracle import oracle as O
+    bf16 = gb.GB_CODEC_BF16
+    x = [W.device_gradients_typed(n, 1800 + 10 * k + r, DEV, dt) for r in range(k)]
+    r0 = [W.device_gradients(n, 1900 + 10 * k + r, DEV) * 1e-3 for r in range(k)]
+    lay = gb.gb_bucket_workspace_layout(bf16, k, n, B)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+    res = [t.clone() for t in r0]
+    whole, ref = filled(n, x[0].dtype), filled(n, x[0].dtype)
+    gb.gb_bucket_allreduce_local_ef_typed(whole, x, res, B, bf16, 0, ws)
+    codes = [ws[r * lay["codes_stride"]:][:2 * n].view(torch.int16) for r in range(k)]
+    ress = [t.clone() for t in r0]
+    codess = [torch.empty(n, dtype=torch.uint16, device=DEV) for _ in range(k)]
+    for r in range(k):
+        gb.gb_encode_ef(bf16, codess[r], None, ress[r], x[r])
+    gb.gb_decode_sum(ref, codess, None, bf16)
+    same(whole, ref, f"fused bf16 pass with feedback over {k} ranks of {dt} against the separate launches")
+    for r in range(k):
+        same(codes[r], codess[r].view(torch.int16), f"codes {r} against the separate encode")
+        same(res[r], ress[r], f"residual {r} against the separate encode")
+    del codess, ress
+    ref.view(torch.uint8).fill_(0xFF)
+    resb = [t.clone() for t in r0]
+    wsb = torch.empty(gb.gb_bucket_batch_workspace_bytes(bf16, k, [n]), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch_ef([ref], [x], [resb], bf16, workspace=wsb)
+    same(whole, ref, f"fused bf16 pass with feedback over {k} ranks of {dt} against the batch kernel")
+    for r in range(k):
+        same(res[r], resb[r], f"residual {r} against the batch kernel")
+    del ref, wsb, resb
+    host = lambda t: bits(t).cpu().numpy()
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    length = 65536
+    rng = np.random.default_rng(170 + k)
+    last = (n - length) // 1024 * 1024
+    for s in [0, last] + [int(v) * 1024 for v in rng.integers(0, last // 1024, 3)]:
+        e = n if s == last else s + length
+        xs = [host(t[s:e]).view(np.uint16) if dt != "f64" else t[s:e].cpu().numpy() for t in x]
+        want, wc, _, wr = O.bucket_allreduce_ef_typed(xs, [t[s:e].cpu().numpy() for t in r0], dt, B, O.CODEC_BF16)
+        assert (host(whole[s:e]) == np.ascontiguousarray(want).view(host(whole[:1]).dtype)).all(), \
+            f"oracle total window at {s}"
+        for r in range(k):
+            assert (host(codes[r][s:e]).view(np.uint16) == wc[r]).all(), f"oracle codes {r} at {s}"
             assert (u32(res[r][s:e].cpu().numpy()) == u32(wr[r])).all(), f"oracle residual {r} at {s}"
 
 
