@@ -1213,11 +1213,13 @@ def workload_summary(gb, torch, args, name, reps):
 
 
 def copy_ceiling(torch, gb, stream, reps=5):
-    """GB/s of plain 1 GiB device copies: the library's own streaming copy
+    """GB/s of plain 1 GiB device copies of gradient-like values (HBM moves
+    constant or zero data faster): the library's own streaming copy
     (gb_reduce_sum with one source) and the runtime's device-to-device copy
     (torch copy_, a hipMemcpyDtoD), each reading and writing 1 GiB."""
+    import workloads as W
     n = (1 << 30) // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    src = W.device_gradients(n, W.BASE_SEED + 99, "cuda:0")
     dst = torch.empty_like(src)
     gb.gb_reduce_sum(dst, [src])
     dst.copy_(src)

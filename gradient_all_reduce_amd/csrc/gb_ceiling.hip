@@ -19,6 +19,12 @@
 //             float32 total written, in the pass's lane map and in the shape
 //             it takes at this size (128-lane workgroups in index order, 2
 //             per compute unit).
+// The buffers hold gradient-like values (every float32 a hash of its index,
+// spread over +-1e-3; the write kernel stores varying bits too), because
+// what the bits are changes how fast HBM moves them: a buffer of zeros
+// copies several percent faster.  One copy of a zero-filled buffer is
+// measured beside the others as that contrast (zeros_copy_u1), and is not a
+// ceiling.
 // Then the fixed cost of a launch itself: 153 launches, back to back on one
 // stream, of a kernel whose body does nothing, from the stream and replayed
 // from a HIP graph, for grids of 1 workgroup, of the 1,600 of one 6,553,600-
@@ -58,7 +64,8 @@ __device__ __forceinline__ size_t group() {
   return FRONTS ? gb::group_index_in<gb::GroupOrder<8, 256, 1>>(blockIdx.x, gridDim.x) : (size_t)blockIdx.x;
 }
 
-template <int U, bool FRONTS>
+// TAG only names a second instantiation (the zero-data contrast) apart.
+template <int U, bool FRONTS, int TAG = 0>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const f4* __restrict__ src, f4* __restrict__ dst) {
   const size_t base = group<FRONTS>() * kThreads * U + threadIdx.x;
   f4 v[U];
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const f4* __restrict__ s
   float a = 0.0f;
 #pragma unroll
   for (int u = 0; u < U; u++) a += (v[u].x + v[u].y) + (v[u].z + v[u].w);
-  if (a == -1.25f) sink[0] = a;  // never true for the zeros read here
+  if (a == -1.25f) sink[0] = a;  // never true: every value read lies within +-1e-3
 }
 
 // Stores only if the grid has more lanes than it can (never).
@@ -103,9 +110,31 @@ __global__ __launch_bounds__(kThreads) void empty_kernel(float* sink) {
   if (threadIdx.x >= kThreads) sink[0] = 1.0f;
 }
 
-__global__ __launch_bounds__(kThreads) void write_kernel(f4* __restrict__ dst, float value) {
+// Small positive floats whose low 23 bits come from a hash of the index.
+__global__ __launch_bounds__(kThreads) void write_kernel(f4* __restrict__ dst, uint32_t seed) {
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  __builtin_nontemporal_store(f4{value, value, value, value}, dst + i);
+  const uint32_t h = (uint32_t)i * 2654435761u ^ seed;
+  const uint32_t e = 0x3A000000u;
+  const f4 v = {gb::bitsf(e | (h >> 9)), gb::bitsf(e | ((h * 3u) >> 9)), gb::bitsf(e | ((h * 5u) >> 9)),
+                gb::bitsf(e | ((h * 7u) >> 9))};
+  __builtin_nontemporal_store(v, dst + i);
+}
+
+// Gradient-like contents for a buffer of nvec vectors (grid-stride, any grid).
+__global__ void fill_gradient_like(f4* p, size_t nvec, uint32_t seed) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (size_t)gridDim.x * blockDim.x) {
+    float x[4];
+    for (int j = 0; j < 4; j++) {
+      uint32_t h = (uint32_t)(4 * i + j) * 2654435761u ^ seed;
+      h ^= h >> 15;
+      h *= 2246822519u;
+      h ^= h >> 13;
+      h *= 3266489917u;
+      h ^= h >> 16;
+      x[j] = ((float)(h & 0xFFFFFFu) / 16777216.0f - 0.5f) * 2e-3f;
+    }
+    p[i] = f4{x[0], x[1], x[2], x[3]};
+  }
 }
 
 // The fused fp8 pass's memory pattern (4 ranks, float32): lane map,
@@ -238,11 +267,15 @@ int main(int argc, char** argv) {
   // five float32 buffers of `bytes` (4 sources and an output), 4 code
   // streams of nval bytes, 4 scale streams
   const size_t nblk = nval / 256;
+  // four gradient-like sources; the fifth buffer (the replica's output)
+  // starts zeroed and is the zero-data contrast's source
   f4 *buf[5];
-  for (auto& p : buf) {
-    CK(hipMalloc(&p, bytes));
-    CK(hipMemset(p, 0, bytes));
+  for (int i = 0; i < 5; i++) {
+    CK(hipMalloc(&buf[i], bytes));
+    if (i < 4) fill_gradient_like<<<4096, kThreads>>>(buf[i], nvec, 0x9E3779B9u * (i + 1));
+    else CK(hipMemset(buf[i], 0, bytes));
   }
+  CK(hipGetLastError());
   uint8_t* codes;
   float *scales, *sink;
   CK(hipMalloc(&codes, 4 * nval));
@@ -263,7 +296,11 @@ int main(int argc, char** argv) {
   measure("copy_lds_u4_" + sz, copy_bytes, reps, [&] { copy_lds_kernel<4><<<nvec / (4 * kThreads), kThreads>>>(buf[0], buf[1]); });
   measure("read_u4_2percu_" + sz, (double)bytes, reps,
           [&] { read_kernel<4><<<nvec / (4 * kThreads), kThreads, gb::kTwoPerCuLds>>>(buf[0], sink); });
-  measure("write_u1_" + sz, (double)bytes, reps, [&] { write_kernel<<<nvec / kThreads, kThreads>>>(buf[1], 1.0f); });
+  measure("write_u1_" + sz, (double)bytes, reps, [&] { write_kernel<<<nvec / kThreads, kThreads>>>(buf[1], 0x85EBCA6Bu); });
+  measure("zeros_copy_u1_" + sz, copy_bytes, reps,
+          [&] { copy_kernel<1, false, 1><<<nvec / kThreads, kThreads>>>(buf[4], buf[1]); });
+  fill_gradient_like<<<4096, kThreads>>>(buf[1], nvec, 0x9E3779B9u * 2);  // rank 1 of the replica again
+  CK(hipGetLastError());
   gb::PtrTable st = {};
   gb::OutTable ct = {}, sct = {};
   for (int r = 0; r < 4; r++) {
