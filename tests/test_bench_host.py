@@ -79,3 +79,23 @@ def test_profiled_traffic_requires_the_current_kernel_sources():
             assert abs(got / float(kv["algorithmic_bytes"]) - 1) < 0.05, ln
         else:
             assert got is None
+
+
+def test_memory_ceiling_never_takes_the_zero_data_contrast(monkeypatch, tmp_path):
+    """The ceiling program reports a copy of a zero-filled buffer beside the
+    copies of gradient-like data, as a contrast (HBM moves zeros faster).
+    bench's best copy, the denominator of frac_of_copy_ceiling, must be one
+    of the gradient-like copies even when the zero-data copy is faster."""
+    res = {"copy_u1_4GiB": 6400.0, "copy_u1_fronts_4GiB": 6600.0, "read_u4_2percu_4GiB": 7500.0,
+           "write_u1_4GiB": 6650.0, "zeros_copy_u1_4GiB": 6900.0, "fused_fp8_replica_4GiB": 5800.0}
+    out = '{"median_gbs": %s, "launch_us": {"stream_1wg": 2.5}}' % str(res).replace("'", '"')
+
+    class Done:
+        returncode, stdout, stderr = 0, "gb_ceiling: buffers of 4 GiB\n" + out + "\n", ""
+
+    exists = os.path.exists
+    monkeypatch.setattr(os.path, "exists", lambda p: p.endswith("gb_ceiling") or exists(p))
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Done())
+    got = bench.memory_ceiling()
+    assert got["best_copy"] == "copy_u1_fronts_4GiB" and got["best_copy_gbs"] == 6600.0
+    assert got["median_gbs"]["zeros_copy_u1_4GiB"] == 6900.0
