@@ -225,7 +225,7 @@ def host_typed(t, dt):
     return t.cpu().numpy().view(np.uint32) if dt == "f32" else typed_to_host(t)
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "f64"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16", "f64"])
 @pytest.mark.parametrize("codec,mode", CODECS)
 @pytest.mark.parametrize("k", [1, 4, 8])
 def test_error_feedback_matches_the_oracle_over_steps(gb, dt, codec, mode, k):
@@ -264,6 +264,41 @@ def test_error_feedback_matches_the_oracle_over_steps(gb, dt, codec, mode, k):
                     assert (wsh[c0:c0 + n] == wc[r]).all(), what + f" codes {r}"
                     s0 = lay["scales_offset"] + r * lay["scales_stride"] + 4 * (offs[b] // 256)
                     assert (wsh[s0:s0 + 4 * wsc[r].size].view(np.uint32) == bits(wsc[r])).all(), what + f" scales {r}"
+
+
+@pytest.mark.parametrize("dt,k", [("bf16", 2), ("f16", 3), ("f64", 1)])
+def test_error_feedback_batch_takes_its_largest_buckets_shape(gb, dt, k):
+    """The bf16 error-feedback batch takes its whole-buffer rule for its
+    largest bucket: here a bucket above 2^22 values puts every bucket of the
+    launch in 64-lane workgroups, the small and ragged ones included, which
+    alone would take 256 lanes.  Each bucket must equal the oracle and the
+    same bucket through gb_bucket_allreduce_local_ef_typed alone, bit for
+    bit: totals, codes and residuals."""
+    codec = O.CODEC_BF16
+    sizes = [(1 << 22) + 77, 300, 1, 5000, 513]
+    hb = [[W.typed(n, dt, 4100 + 10 * b + r) for r in range(k)] for b, n in enumerate(sizes)]
+    res = [[(np.random.default_rng(4200 + 50 * b + r).standard_normal(n) * 1e-4).astype(np.float32)
+            for r in range(k)] for b, n in enumerate(sizes)]
+    db = [[dev_typed(x, dt) for x in xs] for xs in hb]
+    dres = [[torch.from_numpy(a.copy()).to(DEV) for a in rb] for rb in res]
+    outs = [torch.empty(n, dtype=db[b][0].dtype, device=DEV) for b, n in enumerate(sizes)]
+    ws = torch.empty(gb.gb_bucket_batch_workspace_bytes(codec, k, sizes), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch_ef(outs, db, dres, codec, 0, ws)
+    torch.cuda.synchronize()
+    for b, n in enumerate(sizes):
+        want, _, _, wres = O.bucket_allreduce_ef_typed(hb[b], res[b], dt, (n + 255) // 256 * 256, codec)
+        what = f"dt={dt} k={k} bucket {b} (n={n})"
+        assert host_typed(outs[b], dt).tobytes() == np.ascontiguousarray(want).tobytes(), what
+        one = torch.empty_like(outs[b])
+        rone = [torch.from_numpy(a.copy()).to(DEV) for a in res[b]]
+        wso = torch.empty(gb.gb_bucket_workspace_bytes(codec, k, n, (n + 255) // 256 * 256), dtype=torch.uint8,
+                          device=DEV)
+        gb.gb_bucket_allreduce_local_ef_typed(one, db[b], rone, (n + 255) // 256 * 256, codec, 0, wso)
+        torch.cuda.synchronize()
+        assert host_typed(one, dt).tobytes() == host_typed(outs[b], dt).tobytes(), what + " against the call alone"
+        for r in range(k):
+            assert (dres[b][r].cpu().numpy().view(np.uint32) == bits(wres[r])).all(), what + f" residual {r}"
+            assert torch.equal(rone[r].view(torch.int32), dres[b][r].view(torch.int32)), what + f" residual {r} alone"
 
 
 def test_error_feedback_with_more_ranks_than_one_launch_reads(gb):
