@@ -134,20 +134,21 @@ def test_typed_calls_in_a_replayed_graph(gb):
         torch.cuda.synchronize()
 
 
-def test_error_feedback_in_a_replayed_graph(gb):
+@pytest.mark.parametrize("codec,k", [(O.CODEC_FP8, 3), (O.CODEC_BF16, 4)])
+def test_error_feedback_in_a_replayed_graph(gb, codec, k):
     """One error-feedback bucket stream captured once and replayed three times:
     each replay reads the residuals the previous one wrote, exactly as three
-    eager calls do, for float32 and bfloat16 gradients."""
-    k, n, bucket = 3, 4096 * 5 + 256 * 3 + 17, 4096
-    for dt in ("f32", "bf16"):
+    eager calls do, for float32, bfloat16 and float64 gradients; with the
+    bf16 codec over 4 ranks every type runs the 64-lane kernel."""
+    n, bucket = 4096 * 5 + 256 * 3 + 17, 4096
+    for dt in ("f32", "bf16", "f64"):
         xs = W.typed_ranks(k, n, dt, 6700) if dt != "f32" else W.gradient_ranks(k, n, 6700)
         dx = ([torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16) for x in xs] if dt == "bf16"
               else [torch.from_numpy(x).to(DEV) for x in xs])
         res = [torch.zeros(n, device=DEV) for _ in range(k)]
         out = torch.empty(n, dtype=dx[0].dtype, device=DEV)
-        ws = torch.empty(gb.gb_bucket_workspace_bytes(gb.GB_CODEC_FP8_E4M3_B256, k, n, bucket), dtype=torch.uint8,
-                         device=DEV)
-        step = lambda: gb.gb_bucket_allreduce_local_ef_typed(out, dx, res, bucket, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
+        ws = torch.empty(gb.gb_bucket_workspace_bytes(codec, k, n, bucket), dtype=torch.uint8, device=DEV)
+        step = lambda: gb.gb_bucket_allreduce_local_ef_typed(out, dx, res, bucket, codec, 0, ws)
         # warm up on scratch residuals, then capture
         saved = [r.clone() for r in res]
         step()
@@ -162,7 +163,7 @@ def test_error_feedback_in_a_replayed_graph(gb):
         for rep in range(3):
             g.replay()
             torch.cuda.synchronize()
-            want, _, _, wres = O.bucket_allreduce_ef_typed(xs, wres, dt, bucket, O.CODEC_FP8)
+            want, _, _, wres = O.bucket_allreduce_ef_typed(xs, wres, dt, bucket, codec)
             got = out.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16" else out.cpu().numpy()
             assert got.tobytes() == np.ascontiguousarray(want).tobytes(), (dt, rep)
             for r in range(k):
