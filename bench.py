@@ -1235,7 +1235,8 @@ def memory_ceiling(gib=4, reps=10):
     with the library) run as a child process: median GB/s of plain copies
     (1, 2 and 4 vectors per lane; index order or 8 fronts; through LDS with
     global_load_lds_dwordx4), read-only and write-only streams, and a
-    memory-only replica of the fused fp8 pass, on `gib`-GiB buffers; and the
+    memory-only replicas of the fused fp8 pass with and without error
+    feedback, on `gib`-GiB buffers of gradient-like values; and the
     median microseconds per launch of an empty kernel (1, 1,600 and 25,600
     workgroups) launched back to back from a stream and from a graph."""
     import subprocess
@@ -1257,12 +1258,15 @@ def memory_ceiling(gib=4, reps=10):
 
 
 def replica_frac(achieved, mem_ceiling, wl):
-    """For the float32 fp8 bucket stream: the fused pass against the
-    memory-only replica of its own access pattern, in the same run."""
-    rep = mem_ceiling.get("median_gbs", {}).get("fused_fp8_replica_4GiB")
-    if rep and type(wl) is DdpBuckets and wl.dt == "f32" and wl.codec == 2:
-        return {"frac_of_own_memory_pattern": round(achieved / rep, 4)}
-    return {}
+    """For the float32 fp8 bucket stream, plain or with error feedback, over
+    the whole 1e9-value buffer: the fused pass against the memory-only
+    replica of its own access pattern, in the same run."""
+    med = mem_ceiling.get("median_gbs", {})
+    if getattr(wl, "dt", None) != "f32" or getattr(wl, "codec", None) != 2 or "shard" in wl.config:
+        return {}
+    rep = med.get("fused_fp8_ef_replica_4GiB") if type(wl) is DdpBucketsEF else (
+        med.get("fused_fp8_replica_4GiB") if type(wl) is DdpBuckets else None)
+    return {"frac_of_own_memory_pattern": round(achieved / rep, 4)} if rep else {}
 
 
 def step_distribution(torch, stream, fn, reps):
