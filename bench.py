@@ -225,11 +225,16 @@ class DdpBuckets(Workload):
         et = self.gb.GB_DTYPE_OF[self.dt]
         # the four-rank float32 sum takes its wide kernel from 2^28 values per rank
         f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
-        # the fp8 pass takes its 128-lane workgroups: float32 gradients from 2^27
-        # values per rank, float64 ones over 4 ranks between 3 * 2^21 and 2^29
+        # the fp8 pass over 4 ranks takes one block per 64-lane workgroup for
+        # float32 gradients from 2^27 values per rank, and 128-lane workgroups
+        # for float64 ones between 3 * 2^21 and 2^29
         n = self.n
-        half = {0: n >= (1 << 27), 3: (3 << 21) <= n < (1 << 29)}.get(et, False)
-        fp8 = f"fused_fp8_half_kernel<4,{et}>" if half else f"fused_fp8_kernel<4,{et}>"
+        if et == 0 and n >= (1 << 27):
+            fp8 = "fused_fp8_wave_kernel<4>"
+        elif et == 3 and (3 << 21) <= n < (1 << 29):
+            fp8 = "fused_fp8_half_kernel<4,3>"
+        else:
+            fp8 = f"fused_fp8_kernel<4,{et}>"
         # and the bf16 pass its 64-lane workgroups: float32 gradients over 3 or
         # more ranks, float16 and bfloat16 ones over 4 from 2^29 values
         wave = et == 0 or (et in (1, 2) and self.n >= (1 << 29))

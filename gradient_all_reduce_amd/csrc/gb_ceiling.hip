@@ -17,8 +17,8 @@
 //             with the encode replaced by taking each value's top byte: 4
 //             float32 sources read, 4 code streams, 4 scale streams and the
 //             float32 total written, in the pass's lane map and in the shape
-//             it takes at this size (128-lane workgroups in index order, 2
-//             per compute unit);
+//             it takes at this size (one block per 64-lane workgroup, in
+//             index order, 20 per compute unit);
 //   replica_ef the same for the fp8 pass with error feedback: 4 sources and
 //             4 float32 residuals read; codes, scales, the 4 residuals and
 //             the total written (21 streams), in that pass's shape at this
@@ -142,35 +142,27 @@ __global__ void fill_gradient_like(f4* p, size_t nvec, uint32_t seed) {
 }
 
 // The fused fp8 pass's memory pattern (4 ranks, float32): lane map,
-// workgroup size, order and cap of the library's kernel for large buffers,
-// the encode replaced by the top byte of each value and the scale by the
+// workgroup size, order and cap of the library's kernel for large buffers
+// (one 256-value block per 64-lane workgroup, 4 values per lane), the
+// encode replaced by the top byte of each value and the scale by the
 // block's first value.
-__global__ __launch_bounds__(gb::kHalfThreads) void replica_kernel(gb::PtrTable src, gb::OutTable codes,
-                                                                   gb::OutTable scales, float* __restrict__ out) {
-  const uint32_t col = threadIdx.x & 15u;
-  const size_t block = (size_t)blockIdx.x * (gb::kHalfThreads / 16) + (threadIdx.x >> 4);
-  f4 x[4][4];
+__global__ __launch_bounds__(64) void replica_kernel(gb::PtrTable src, gb::OutTable codes, gb::OutTable scales,
+                                                     float* __restrict__ out) {
+  const size_t block = blockIdx.x, e = block * gb::kBlock + 4 * (size_t)threadIdx.x;
+  f4 x[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) x[r] = gb::load4(static_cast<const float*>(src.p[r]) + e);
+  f4 a;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) x[r][j] = gb::load4(static_cast<const float*>(src.p[r]) + gb::lane_elem(block, j, col));
+    const f4 v = x[r];
+    const uint32_t w = (gb::fbits(v.x) >> 24) | ((gb::fbits(v.y) >> 24) << 8) | ((gb::fbits(v.z) >> 24) << 16) |
+                       ((gb::fbits(v.w) >> 24) << 24);
+    if (threadIdx.x == 0u) static_cast<float*>(scales.p[r])[block] = v.x;
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(codes.p[r]) + e));
+    a = r == 0 ? v : a + v;
   }
-  f4 a[4];
-#pragma unroll
-  for (int r = 0; r < 4; r++) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f4 v = x[r][j];
-      const uint32_t w = (gb::fbits(v.x) >> 24) | ((gb::fbits(v.y) >> 24) << 8) | ((gb::fbits(v.z) >> 24) << 16) |
-                         ((gb::fbits(v.w) >> 24) << 24);
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(codes.p[r]) +
-                                                                 gb::lane_elem(block, j, col)));
-      a[j] = r == 0 ? v : a[j] + v;
-    }
-    if (col == 0u) static_cast<float*>(scales.p[r])[block] = x[r][0].x;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) gb::store4(out + gb::lane_elem(block, j, col), a[j]);
+  gb::store4(out + e, a);
 }
 
 // The error-feedback fp8 pass's memory pattern (4 ranks, float32): the
@@ -350,10 +342,9 @@ int main(int argc, char** argv) {
     sct.p[r] = scales + (size_t)r * nblk;
   }
   const double replica_bytes = (double)nval * (16.0 + 4.0 + 16.0 / 256 + 4.0);
-  static_assert(gb::fused_fp8_half<GB_DTYPE_F32>(4, (size_t)1 << 28), "the replica's shape is the pass's from 2^28 values");
+  static_assert(gb::fused_fp8_wave(4, (size_t)1 << 28), "the replica's shape is the pass's from 2^28 values");
   measure("fused_fp8_replica_" + sz, replica_bytes, reps, [&] {
-    replica_kernel<<<nblk / (gb::kHalfThreads / 16), gb::kHalfThreads, gb::fused_fp8_half_lds<GB_DTYPE_F32>(4)>>>(
-        st, ct, sct, reinterpret_cast<float*>(buf[4]));
+    replica_kernel<<<nblk, 64, gb::kFp8WaveLds>>>(st, ct, sct, reinterpret_cast<float*>(buf[4]));
   });
   // the error-feedback pattern: four gradient-like residual buffers more
   f4* res[4];

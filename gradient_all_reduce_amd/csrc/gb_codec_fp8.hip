@@ -178,6 +178,63 @@ __global__ __launch_bounds__(kHalfThreads) void fused_fp8_half_kernel(void* out,
   }
 }
 
+// The pass over float32 gradients with one block per wavefront: workgroup b
+// is block b, lane l its values 4l to 4l + 3, so each load or store of a
+// rank covers 1 KiB (256 bytes of codes) in one piece.  The block maximum
+// and so every bit are those of the 16-lane map.
+template <int K, bool FULL, int DIV = 0>
+__device__ __forceinline__ void fused_fp8_wave_body(float* out, const PtrTable& src, const OutTable& codes,
+                                                    const OutTable& scales, size_t n, int mode, size_t block,
+                                                    float d = 1.0f, float inv = 0.0f) {
+  const size_t e = block * kBlock + 4 * (size_t)threadIdx.x;
+  f4 x[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) x[r] = load4_at<FULL>(static_cast<const float*>(src.p[r]), e, n);
+  f4 a[1];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    uint32_t w;
+    const float s = encode_block4(x[r], mode, w);  // all 64 lanes take part
+    if (threadIdx.x == 0u) static_cast<float*>(scales.p[r])[block] = s;
+    store_codes4_at<FULL>(static_cast<uint8_t*>(codes.p[r]), e, n, w);
+    const f4 v = e4m3_unpack4(w) * s;
+    a[0] = r == 0 ? v : a[0] + v;
+  }
+  avg_total<DIV>(a, d, inv);
+  store4_at<FULL>(out, e, n, canon4(a[0]));
+}
+
+template <int K>
+__global__ __launch_bounds__(64) void fused_fp8_wave_kernel(float* out, PtrTable src, OutTable codes,
+                                                            OutTable scales, size_t n, int mode) {
+  const size_t block = blockIdx.x;  // the grid has one workgroup per block, so block * kBlock < n
+  if ((block + 1) * kBlock <= n) fused_fp8_wave_body<K, true>(out, src, codes, scales, n, mode, block);
+  else fused_fp8_wave_body<K, false>(out, src, codes, scales, n, mode, block);
+}
+
+// The batch over float32 gradients in the same shape: bucket b takes
+// workgroups [first[b], first[b + 1]), 16 per 4096-value group, and those
+// past the bucket's last block return at once (uniformly per workgroup).
+template <int K, int DIV>
+__global__ __launch_bounds__(64) void fused_fp8_wave_batch_kernel(BucketBatch t, int mode, float d, float inv) {
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  const size_t block = w - t.first[b], n = t.n[b];
+  if (block * kBlock >= n) return;
+  PtrTable src;
+  OutTable codes, scales;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    codes.p[r] = t.codes[b][r];
+    scales.p[r] = t.scales[b][r];
+  }
+  float* out = static_cast<float*>(t.out[b]);
+  if ((block + 1) * kBlock <= n) fused_fp8_wave_body<K, true, DIV>(out, src, codes, scales, n, mode, block, d, inv);
+  else fused_fp8_wave_body<K, false, DIV>(out, src, codes, scales, n, mode, block, d, inv);
+}
+
 // Several buckets in one launch (gradients of element type ET): each
 // workgroup finds its bucket from the table of first workgroups, then runs
 // the fused pass over that bucket's group: in index order within a bucket,
@@ -233,6 +290,17 @@ hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales
 template <int ET>
 hipError_t fused_fp8_t(void* out, const PtrTable& srcs, const OutTable& c, const OutTable& s, int k, size_t n,
                        int scale_mode, hipStream_t stream) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    // one workgroup per block; beyond the largest grid (above 2^39 - 2^8
+    // values) the 256-lane kernel runs
+    const size_t wave_grid = ceil_div(n, kBlock);
+    if (fused_fp8_wave(k, n) && wave_grid <= kMaxGrid) {
+      // the rule holds for 4 ranks only, so only that instantiation exists
+      fused_fp8_wave_kernel<4><<<wave_grid, 64, kFp8WaveLds, stream>>>(static_cast<float*>(out), srcs, c, s, n,
+                                                                      scale_mode);
+      return hipGetLastError();
+    }
+  }
   if constexpr (ET == GB_DTYPE_F32 || ET == GB_DTYPE_F64) {
     if (fused_fp8_half<ET>(k, n)) {
       const size_t half_grid = ceil_div(n, (kHalfThreads / 16) * kBlock);
@@ -292,6 +360,15 @@ hipError_t fused_fp8_batch_t(BucketBatch& t, size_t grid, int k, int scale_mode,
                              hipStream_t stream) {
   size_t largest = 0;
   for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
+  if constexpr (ET == GB_DTYPE_F32) {
+    // sixteen 64-lane workgroups per group, as the whole-buffer launch takes
+    // its largest bucket
+    if (fused_fp8_wave(k, largest) && grid <= kMaxGrid / 16) {
+      for (int b = 0; b <= kBatchBuckets; b++) t.first[b] *= 16;
+      fused_fp8_wave_batch_kernel<4, DIV><<<16 * grid, 64, kFp8WaveLds, stream>>>(t, scale_mode, d, inv);
+      return hipGetLastError();
+    }
+  }
 #define GB_CALL(K) \
   fused_fp8_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_lds<ET>(K, largest), stream>>>(t, scale_mode, d, inv);
   GB_DISPATCH_K(k, GB_CALL)

@@ -19,7 +19,9 @@
 //   * the fp8 block maximum is reduced across the 16 lanes of one DPP row (four
 //     row-local DPP steps, no LDS, no barrier): a 256-value block is one row of
 //     16 lanes holding 16 values each, a wavefront works on 4 blocks and a
-//     256-lane workgroup on 16;
+//     256-lane workgroup on 16 (the fused pass over 4 ranks of large float32
+//     buffers instead spreads one block over a wavefront, 4 values per lane,
+//     and takes the row maxima's maximum with 4 lane reads);
 //   * E4M3 conversion uses gfx950's packed converters (v_cvt_pk_fp8_f32 to
 //     encode two values per instruction, v_cvt_pk_f32_fp8 to decode two);
 //   * large launches take their groups in a permuted order (group_index) that
@@ -606,6 +608,39 @@ __device__ __forceinline__ float encode_block16(const f4 (&x)[4], int mode, uint
   return s;
 }
 
+// The same for a block spread over one whole wavefront, 4 values per lane:
+// the lane maximum as lane_absmax16 takes it, the block maximum from the 4
+// row maxima.  Requires all 64 lanes active.
+__device__ __forceinline__ uint32_t lane_absmax4(f4 x) {
+  uint32_t a = max(max(fbits(x.x) & 0x7FFFFFFFu, fbits(x.y) & 0x7FFFFFFFu),
+                   max(fbits(x.z) & 0x7FFFFFFFu, fbits(x.w) & 0x7FFFFFFFu));
+  if (a > 0x7F800000u) {
+    a = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const uint32_t m = fbits(x[e]) & 0x7FFFFFFFu;
+      a = max(a, m > 0x7F800000u ? 0u : m);
+    }
+  }
+  return a;
+}
+__device__ __forceinline__ uint32_t wave_max64(uint32_t v) {
+  v = row_max16(v);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ float encode_block4(f4 x, int mode, uint32_t& w) {
+  const float s = block_scale(wave_max64(lane_absmax4(x)), mode);
+  const double rinv = scale_reciprocal(s);
+  f4 v = quotient4(x, rinv);
+  if (s > 0.0f && s < 0x1p-126f) v = clamp448(v);
+  w = e4m3_pack4(v, x);
+  return s;
+}
+
 // Every kernel below runs one of two instantiations of its body per
 // workgroup: FULL when the workgroup's whole range lies below n (all but the
 // last workgroup of a launch), with no bounds test on any access, and the
@@ -835,12 +870,31 @@ template <int ET>
 __host__ __device__ constexpr bool fused_fp8_half(int k, size_t n) {
   if (ET == GB_DTYPE_F64) return n >= ((size_t)3 << 21) && (k <= 3 || n < ((size_t)1 << 29));
   if (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) return false;
+  if (k == 4) return false;  // fused_fp8_wave below takes 4 ranks
   return (k >= 3 && n >= ((size_t)1 << 27)) || (k == 2 && n >= ((size_t)1 << 28));
 }
 template <int ET>
 __host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) {
   return ET == GB_DTYPE_F64 ? kTwoPerCuLds : (k >= 4 ? kTwoPerCuLds : kThreePerCuLds);
 }
+
+// Fused fp8 pass over float32 gradients of 4 ranks from 2^27 values per
+// rank: one block per 64-lane workgroup (4 values per lane, so each load
+// and store of a rank covers its 1 KiB, or 256 bytes of codes, in one
+// piece) in index order, capped at 20 per unit (8 KiB of LDS each).  The
+// block scale then costs its maximum, exact divide and reciprocal once per
+// 256 values rather than once per 1,024, which at 13 per unit left the pass
+// bound by that chain; at 20 per unit it is not.  Measured in the
+// benchmark's bucket stream over 4 ranks, against the 128-lane kernel on
+// the same machine, two machines, same bits: +2.5% and +4.5-5.5% at 1e9
+// values, +4.8-5.0% at 5e8, +0.6-1.4% at 2.5e8; at 1.25e8 (256-lane
+// kernel) -0.1 to -1.4%.  In one process it gained -0.4% to +4.4% at 1e9
+// values on three machines, lost 4-9% over 2 ranks and was level over 8
+// at 2^28, so the rule is for 4 ranks only.
+__host__ __device__ constexpr bool fused_fp8_wave(int k, size_t n) {
+  return k == 4 && n >= ((size_t)1 << 27);
+}
+constexpr unsigned kFp8WaveLds = 8u << 10;
 
 // Fused fp8 pass with error feedback (21 streams at k = 4: sources and
 // residuals read; codes, scales, residuals and the sum written): 1 per unit

@@ -8,7 +8,9 @@
   4096-value fp8 groups;
 - the wide four-rank sum, from 2^28 values;
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
-  values, 2^28 over two ranks; float64 gradients from 3 * 2^21 values);
+  values, 2^28 over two ranks, but not over 4; float64 gradients from
+  3 * 2^21 values), and one block per 64-lane workgroup (float32 gradients
+  of 4 ranks from 2^27 values, the batch of such a bucket too);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
   ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
   4 ranks and 2^29; with error feedback, over float32 gradients from 1 rank
@@ -159,13 +161,14 @@ def test_wide_four_rank_sum(gb):
     same(x0, ref, "wide four-rank sum in place")
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 8])
+@pytest.mark.parametrize("k", [2, 3, 5, 8])
 def test_fused_fp8_half_workgroups(gb, k):
     """The fused fp8 bucket stream over float32 gradients from 2^27 values
-    per rank (2^28 over two ranks) runs in 128-lane workgroups in index
-    order.  With a ragged last workgroup and block it must equal the 256-lane
-    kernel over slices below 2^27, and the oracle on sampled windows (the
-    first and the last values included): totals, codes and scales."""
+    per rank (2^28 over two ranks; 4 ranks take the 64-lane shape below) runs
+    in 128-lane workgroups in index order.  With a ragged last workgroup and
+    block it must equal the 256-lane kernel over slices below 2^27, and the
+    oracle on sampled windows (the first and the last values included):
+    totals, codes and scales."""
     import numpy as np
     from oracle import oracle as O
     fp8 = gb.GB_CODEC_FP8_E4M3_B256
@@ -242,6 +245,78 @@ def test_fused_fp8_half_typed_workgroups(gb, dt, k, n):
             assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
             got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
             assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+
+
+def plant_specials(x, n, last):
+    """NaN, Inf, a block whose scale is subnormal, a block of negative zeros
+    and the largest finite magnitude, in the first window and the last, and
+    a NaN in the ragged last block."""
+    for base in (0, last):
+        x[0][base + 3 * 256 + 17] = float("nan")
+        x[1][base + 5 * 256 + 200] = float("inf")
+        x[2][base + 5 * 256 + 9] = -float("inf")
+        x[3][base + 7 * 256:base + 8 * 256] = 3e-41  # scale 3e-41 / 448, subnormal
+        x[1][base + 9 * 256:base + 10 * 256] = -0.0
+        x[2][base + 11 * 256 + 63] = -3.4028234663852886e38
+        x[0][base + 11 * 256 + 64] = float("nan")
+    x[3][n - 1] = float("nan")
+
+
+@pytest.mark.parametrize("n", [(1 << 27) + 256 * 5 + 77, (1 << 27) - 77])
+def test_fused_fp8_wave_workgroups(gb, n):
+    """The fused fp8 bucket stream over float32 gradients of 4 ranks runs one
+    256-value block per 64-lane workgroup from 2^27 values per rank, in
+    256-lane workgroups below.  On either side of the threshold, with a
+    ragged last block and special values planted in the first and the last
+    window, it must equal the 256-lane kernel over slices below 2^27, and the
+    oracle on the first, the last and sampled windows: totals, codes and
+    scales.  A batch of that one bucket takes the same shape and must give
+    the same bits, and its AVG the oracle's AVG of that total."""
+    import numpy as np
+    from oracle import oracle as O
+    fp8, k = gb.GB_CODEC_FP8_E4M3_B256, 4
+    x = [W.device_gradients(n, 1900 + r, DEV) for r in range(k)]
+    last = (n - 65536) // 256 * 256
+    plant_specials(x, n, last)
+    lay = gb.gb_bucket_workspace_layout(fp8, k, n, B)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local(whole, x, B, fp8, 0, ws)
+    wss = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, STEP_HALF, B), dtype=torch.uint8, device=DEV)
+    for s, e in slices(n, STEP_HALF):
+        gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, fp8, 0, wss)
+    same(whole, ref, "fused fp8 pass over 4 ranks against 256-lane slices")
+    del wss
+    need = gb.gb_bucket_batch_workspace_bytes(fp8, k, [n])
+    assert need == lay["total"]
+    wsb = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    ref.fill_(0.0)
+    gb.gb_bucket_allreduce_local_batch([ref], [x], fp8, workspace=wsb)
+    same(whole, ref, "a batch of the one bucket")
+    assert torch.equal(ws, wsb), "the batch's payloads"
+    del wsb
+    nb = (n + 255) // 256
+    codes = [ws[r * lay["codes_stride"]:][:n] for r in range(k)]
+    scales = [ws[lay["scales_offset"] + r * lay["scales_stride"]:][:4 * nb].view(torch.float32) for r in range(k)]
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    rng = np.random.default_rng(190)
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 3)]:
+        e = n if s == last else s + 65536
+        want, wc, wsc = O.bucket_allreduce([t[s:e].cpu().numpy() for t in x], B, O.CODEC_FP8,
+                                           O.SCALE_ABSMAX_DIV_448)
+        assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+            got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
+            assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+    total = whole.cpu().numpy()
+    for d in (4, 3):  # the exact reciprocal of a power of two, and a divide
+        wsb = torch.empty(need, dtype=torch.uint8, device=DEV)
+        ref.fill_(0.0)
+        gb.gb_bucket_allreduce_local_batch([ref], [x], fp8, workspace=wsb, divisor=d)
+        want = O.reduce([total], O.OP_AVG, d)
+        assert (u32(ref.cpu().numpy()) == u32(want)).all(), f"AVG over {d}"
+        del wsb
 
 
 @pytest.mark.parametrize("k", [3, 4, 6, 8])
