@@ -416,7 +416,10 @@ class DdpBucketsEF(DdpBuckets):
         # the bf16 pass over four ranks takes 64-lane workgroups at every size,
         # for every gradient type
         bf16 = f"fused_bf16_ef_wave_kernel<4,{et}>"
-        name = f"fused_fp8_ef_kernel<4,{et}>" if fp8 else bf16
+        # the fp8 pass over four ranks of float32 gradients takes one block
+        # per 64-lane workgroup from 2^22 values per rank
+        wave = et == 0 and self.n >= (1 << 22)
+        name = ("fused_fp8_ef_wave_kernel" if wave else f"fused_fp8_ef_kernel<4,{et}>") if fp8 else bf16
         return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):
@@ -570,7 +573,7 @@ class Staged(Workload):
     def timed_kernel(self):
         n = self.n
         per = self.k * self.payload() + 4 * n
-        return ("decode_fp8_kernel<4,false,0>", per, 1,
+        return (decode_fp8_name(n), per, 1,
                 lambda: self.gb.gb_decode_accumulate(self.acc, self.rd, self.rsd, self.gb.GB_CODEC_FP8_E4M3_B256))
 
     def extra(self, time_region, reps):
@@ -619,6 +622,12 @@ class Staged(Workload):
                 return Unit(4 * piece + 2 * p + 2 * self.k * p + 4 * piece, compute, check)
             return factory
         return [make(o) for o in range(0, 1 << 22, piece)], lambda m: f"first {m * piece:,} values of each rank"
+
+
+def decode_fp8_name(n):
+    """The kernel that decodes 4 fp8 payloads of n values into a float32
+    total: one block per 64-lane workgroup from 2^24 values."""
+    return "decode_fp8_wave_kernel<false>" if n >= (1 << 24) else "decode_fp8_kernel<4,false,0>"
 
 
 def codec_extra(wl, time_region, reps, dec_name, dec_bytes):
@@ -707,7 +716,7 @@ class Gradients256(Workload):
         return self.k * (4 * self.n + self.n + 4 * nblocks(self.n)) + 4 * self.n
 
     def extra(self, time_region, reps):
-        return codec_extra(self, time_region, reps, "decode_fp8_kernel<4,false,0>",
+        return codec_extra(self, time_region, reps, decode_fp8_name(self.n),
                            self.k * (self.n + 4 * nblocks(self.n)) + 4 * self.n)
 
     def cpu_units(self):

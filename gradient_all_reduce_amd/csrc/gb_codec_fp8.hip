@@ -115,6 +115,38 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(void* acc, PtrTabl
   else decode_fp8_body<K, ACC, ET, false>(acc, codes, scales, n);
 }
 
+// The decode of 4 payloads into a float32 total with one block per
+// wavefront: workgroup b is block b, lane l its values 4l to 4l + 3; the
+// scales are uniform across the workgroup.
+template <bool ACC, bool FULL>
+__device__ __forceinline__ void decode_fp8_wave_body(float* acc, const PtrTable& codes, const PtrTable& scales,
+                                                     size_t n, size_t block) {
+  constexpr int K = 4;
+  const size_t e = block * kBlock + 4 * (size_t)threadIdx.x;
+  uint32_t w[K];
+  float s[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    w[r] = load_codes4_at<FULL>(static_cast<const uint8_t*>(codes.p[r]), e, n);
+    s[r] = static_cast<const float*>(scales.p[r])[block];
+  }
+  f4 a;
+  if (ACC) a = load4_at<FULL>(acc, e, n);
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    const f4 v = e4m3_unpack4(w[r]) * s[r];
+    a = (!ACC && r == 0) ? v : a + v;
+  }
+  store4_at<FULL>(acc, e, n, canon4(a));
+}
+
+template <bool ACC>
+__global__ __launch_bounds__(64) void decode_fp8_wave_kernel(float* acc, PtrTable codes, PtrTable scales, size_t n) {
+  const size_t block = blockIdx.x;  // the grid has one workgroup per block, so block * kBlock < n
+  if ((block + 1) * kBlock <= n) decode_fp8_wave_body<ACC, true>(acc, codes, scales, n, block);
+  else decode_fp8_wave_body<ACC, false>(acc, codes, scales, n, block);
+}
+
 // ===========================================================================
 // Fused fp8 bucket pass: read each rank's block once, write its payload
 // (codes, scale), decode those codes and add them in rank order.
@@ -275,6 +307,16 @@ hipError_t decode_fp8_t(void* acc, const PtrTable& codes, const PtrTable& scales
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
   if (accumulate && ET != GB_DTYPE_F32) return hipErrorInvalidValue;
+  if constexpr (ET == GB_DTYPE_F32) {
+    // one workgroup per block; beyond the largest grid the 256-lane kernel runs
+    const size_t wave_grid = ceil_div(n, kBlock);
+    if (decode_fp8_wave(k, n) && wave_grid <= kMaxGrid) {
+      float* a = static_cast<float*>(acc);
+      if (accumulate) decode_fp8_wave_kernel<true><<<wave_grid, 64, 0, stream>>>(a, codes, scales, n);
+      else decode_fp8_wave_kernel<false><<<wave_grid, 64, 0, stream>>>(a, codes, scales, n);
+      return hipGetLastError();
+    }
+  }
 #define GB_CALL(K)                                                                                               \
   if constexpr (ET == GB_DTYPE_F32) {                                                                            \
     if (accumulate) decode_fp8_kernel<K, true, ET><<<grid, kThreads, decode_fp8_lds<ET>(K), stream>>>(acc, codes, scales, n); \

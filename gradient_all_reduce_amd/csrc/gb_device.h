@@ -896,6 +896,33 @@ __host__ __device__ constexpr bool fused_fp8_wave(int k, size_t n) {
 }
 constexpr unsigned kFp8WaveLds = 8u << 10;
 
+// The fp8 pass with error feedback over float32 gradients of 4 ranks in the
+// same shape from 2^22 values per rank, at 6 per unit (24 KiB of LDS each;
+// 32 bytes of each rank per lane in flight, source and residual).  In one
+// process at 2^30 values, against the 256-lane kernel, same bits: uncapped
+// and 20 or 13 per unit lost 1-6%, 10 per unit gained 2-3.5%, 8 per unit
+// 5.5-6%, 6 per unit 6.7-7.1%, and 5 per unit lost 16%.  In the benchmark,
+// against the 256-lane kernel on the same machine, two runs each, same
+// bits: +8.9-9.1% at 1e9 values per rank on two machines, +5.5-8.2% at
+// 5e8, +11.7-13.3% at 2.5e8, +11.2-13.0% at 1.25e8, and one call per
+// 6,553,600-value bucket +4.3-5.1% (8 such buckets batched +0.6-2.8%).
+__host__ __device__ constexpr bool fused_fp8_ef_wave(int k, size_t n) {
+  return k == 4 && n >= ((size_t)1 << 22);
+}
+constexpr unsigned kFp8EfWaveLds = 24u << 10;
+
+// The fp8 decode of 4 payloads into a float32 total in the same shape from
+// 2^24 values, uncapped (the scales are uniform across a workgroup, so each
+// is one load per wavefront).  In one process at 2^26 and 2^28 values: +5%
+// and +10% against the 256-lane kernel uncapped or capped up to 6 KiB, and
+// -2% to -28% at 8 and 12 KiB.  In the benchmark, against the 256-lane
+// kernel on the same machine, two runs each, same bits: +8.8-10.8% at 2^26,
+// +5.0-9.5% at 2^25, +8.4-11.7% at 2^24; level at 2^23 (-1.7% and +1.2%,
+// launches of about 9 us).
+__host__ __device__ constexpr bool decode_fp8_wave(int k, size_t n) {
+  return k == 4 && n >= ((size_t)1 << 24);
+}
+
 // Fused fp8 pass with error feedback (21 streams at k = 4: sources and
 // residuals read; codes, scales, residuals and the sum written): 1 per unit
 // from 2^28 values up, 2-4% ahead of 2 or uncapped at 5e8 and 1e9 over every

@@ -169,6 +169,68 @@ __global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_kernel(void* 
   }
 }
 
+// The pass over float32 gradients of 4 ranks with one block per wavefront:
+// workgroup b is block b, lane l its values 4l to 4l + 3 of every source and
+// residual.  The block maximum and so every bit are those of the 16-lane map.
+template <bool FULL, int DIV = 0>
+__device__ __forceinline__ void fused_fp8_ef_wave_body(float* out, const PtrTable& src, const OutTable& resid,
+                                                       const OutTable& codes, const OutTable& scales, size_t n,
+                                                       int mode, size_t block, float dv = 1.0f, float inv = 0.0f) {
+  constexpr int K = 4;
+  const size_t e = block * kBlock + 4 * (size_t)threadIdx.x;
+  f4 y[K];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    y[r] = canon4(load4_at<FULL>(static_cast<const float*>(src.p[r]), e, n) +
+                  load4_at<FULL>(static_cast<const float*>(resid.p[r]), e, n));
+  }
+  f4 a[1];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    uint32_t w;
+    const float s = encode_block4(y[r], mode, w);  // all 64 lanes take part
+    if (threadIdx.x == 0u) static_cast<float*>(scales.p[r])[block] = s;
+    const f4 v = e4m3_unpack4(w) * s;
+    a[0] = r == 0 ? v : a[0] + v;
+    store_codes4_at<FULL>(static_cast<uint8_t*>(codes.p[r]), e, n, w);
+    store4_at<FULL>(static_cast<float*>(resid.p[r]), e, n, canon4(y[r] - v));
+  }
+  avg_total<DIV>(a, dv, inv);
+  store4_at<FULL>(out, e, n, canon4(a[0]));
+}
+
+__global__ __launch_bounds__(64) void fused_fp8_ef_wave_kernel(float* out, PtrTable src, OutTable resid,
+                                                               OutTable codes, OutTable scales, size_t n, int mode) {
+  const size_t block = blockIdx.x;  // the grid has one workgroup per block, so block * kBlock < n
+  if ((block + 1) * kBlock <= n) fused_fp8_ef_wave_body<true>(out, src, resid, codes, scales, n, mode, block);
+  else fused_fp8_ef_wave_body<false>(out, src, resid, codes, scales, n, mode, block);
+}
+
+// The batch in the same shape: bucket b takes workgroups [first[b],
+// first[b + 1]), 16 per 4096-value group, and those past the bucket's last
+// block return at once (uniformly per workgroup).
+template <int DIV>
+__global__ __launch_bounds__(64) void fused_fp8_ef_wave_batch_kernel(BucketBatchEf t, int mode, float dv, float inv) {
+  constexpr int K = 4;
+  const size_t w = blockIdx.x;
+  uint32_t b = 0;
+  for (uint32_t i = 1; i < t.count; i++) b += w >= t.first[i] ? 1u : 0u;
+  const size_t block = w - t.first[b], n = t.n[b];
+  if (block * kBlock >= n) return;
+  PtrTable src;
+  OutTable resid, codes, scales;
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    src.p[r] = t.src[b][r];
+    resid.p[r] = t.resid[b][r];
+    codes.p[r] = t.codes[b][r];
+    scales.p[r] = t.scales[b][r];
+  }
+  float* out = static_cast<float*>(t.out[b]);
+  if ((block + 1) * kBlock <= n) fused_fp8_ef_wave_body<true, DIV>(out, src, resid, codes, scales, n, mode, block, dv, inv);
+  else fused_fp8_ef_wave_body<false, DIV>(out, src, resid, codes, scales, n, mode, block, dv, inv);
+}
+
 // Several buckets in one launch, with their residuals: each workgroup finds
 // its bucket from the table of first workgroups and takes that bucket's
 // group: in index order within a bucket, or in the whole-buffer launch's
@@ -261,6 +323,15 @@ hipError_t fused_fp8_ef_batch_t(BucketBatchEf& t, int k, int scale_mode, float d
   if (grid == 0) return hipErrorInvalidValue;
   size_t largest = 0;
   for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
+  if constexpr (ET == GB_DTYPE_F32) {
+    // sixteen 64-lane workgroups per group, as the whole-buffer launch takes
+    // its largest bucket
+    if (fused_fp8_ef_wave(k, largest) && grid <= kMaxGrid / 16) {
+      for (int b = 0; b <= kBatchBucketsEf; b++) t.first[b] *= 16;
+      fused_fp8_ef_wave_batch_kernel<DIV><<<16 * grid, 64, kFp8EfWaveLds, stream>>>(t, scale_mode, dv, inv);
+      return hipGetLastError();
+    }
+  }
 #define GB_CALL(K) \
   fused_fp8_ef_batch_kernel<K, ET, DIV><<<grid, kThreads, fused_fp8_ef_lds(K, largest), stream>>>(t, scale_mode, dv, inv);
   GB_DISPATCH_K(k, GB_CALL)
@@ -337,6 +408,15 @@ hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, 
 template <int ET>
 hipError_t fused_fp8_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, const OutTable& s,
                           int k, size_t n, int scale_mode, hipStream_t stream) {
+  if constexpr (ET == GB_DTYPE_F32) {
+    // one workgroup per block; beyond the largest grid the 256-lane kernel runs
+    const size_t wave_grid = ceil_div(n, kBlock);
+    if (fused_fp8_ef_wave(k, n) && wave_grid <= kMaxGrid) {
+      fused_fp8_ef_wave_kernel<<<wave_grid, 64, kFp8EfWaveLds, stream>>>(static_cast<float*>(out), srcs, rs, c, s, n,
+                                                                          scale_mode);
+      return hipGetLastError();
+    }
+  }
   const size_t grid = grid_for(n, 16);
   if (grid == 0) return hipErrorInvalidValue;
 #define GB_CALL(K) fused_fp8_ef_kernel<K, ET><<<grid, kThreads, fused_fp8_ef_lds(K, n), stream>>>(out, srcs, rs, c, s, n, scale_mode);

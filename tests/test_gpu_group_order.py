@@ -10,7 +10,8 @@
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
   values, 2^28 over two ranks, but not over 4; float64 gradients from
   3 * 2^21 values), and one block per 64-lane workgroup (float32 gradients
-  of 4 ranks from 2^27 values, the batch of such a bucket too);
+  of 4 ranks from 2^27 values, with error feedback from 2^22, the batch of
+  such a bucket too; the decode of 4 payloads into float32 from 2^24);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
   ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
   4 ranks and 2^29; with error feedback, over float32 gradients from 1 rank
@@ -317,6 +318,119 @@ def test_fused_fp8_wave_workgroups(gb, n):
         want = O.reduce([total], O.OP_AVG, d)
         assert (u32(ref.cpu().numpy()) == u32(want)).all(), f"AVG over {d}"
         del wsb
+
+
+@pytest.mark.parametrize("n", [(1 << 22) + 256 * 5 + 77, (1 << 22) - 77, (1 << 27) + 256 * 5 + 77])
+def test_fused_fp8_ef_wave_workgroups(gb, n):
+    """The fp8 bucket stream with error feedback over float32 gradients of 4
+    ranks runs one 256-value block per 64-lane workgroup from 2^22 values per
+    rank, in 256-lane workgroups below.  On either side of the threshold and
+    at 2^27, with a ragged last block and special values planted in
+    gradients and a residual, it must equal the 256-lane kernel over slices
+    below 2^22 from the same residuals, and the oracle on the first, the last and sampled
+    windows: totals, codes, scales and the new residuals.  A batch of that
+    one bucket takes the same shape and must give the same bits, and its AVG
+    the oracle's AVG of that total."""
+    import numpy as np
+    from oracle import oracle as O
+    fp8, k = gb.GB_CODEC_FP8_E4M3_B256, 4
+    x = [W.device_gradients(n, 2000 + r, DEV) for r in range(k)]
+    last = (n - 65536) // 256 * 256
+    plant_specials(x, n, last)
+    r0 = [W.device_gradients(n, 2100 + r, DEV) * 1e-2 for r in range(k)]
+    for base in (0, last):
+        r0[2][base + 13 * 256 + 5] = float("nan")
+        r0[0][base + 14 * 256:base + 15 * 256] = -3e-41
+    lay = gb.gb_bucket_workspace_layout(fp8, k, n, B)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=DEV)
+    rw = [t.clone() for t in r0]
+    whole, ref = filled(n), filled(n)
+    gb.gb_bucket_allreduce_local_ef(whole, x, rw, B, fp8, 0, ws)
+    rs = [t.clone() for t in r0]
+    step = 3 * (1 << 20)  # below 2^22, a multiple of 256
+    wss = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, step, step), dtype=torch.uint8, device=DEV)
+    for s, e in slices(n, step):
+        gb.gb_bucket_allreduce_local_ef(ref[s:e], [t[s:e] for t in x], [t[s:e] for t in rs], step, fp8, 0, wss)
+    same(whole, ref, "fp8 pass with error feedback against 256-lane slices")
+    for r in range(k):
+        same(rw[r], rs[r], f"residual {r} against 256-lane slices")
+    del wss, rs
+    need = gb.gb_bucket_batch_workspace_bytes(fp8, k, [n])
+    assert need == lay["total"]
+    wsb = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    rb = [t.clone() for t in r0]
+    ref.fill_(0.0)
+    gb.gb_bucket_allreduce_local_batch_ef([ref], [x], [rb], fp8, 0, wsb)
+    same(whole, ref, "a batch of the one bucket")
+    assert torch.equal(ws, wsb), "the batch's payloads"
+    for r in range(k):
+        same(rw[r], rb[r], f"the batch's residual {r}")
+    del wsb, rb
+    nb = (n + 255) // 256
+    codes = [ws[r * lay["codes_stride"]:][:n] for r in range(k)]
+    scales = [ws[lay["scales_offset"] + r * lay["scales_stride"]:][:4 * nb].view(torch.float32) for r in range(k)]
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    rng = np.random.default_rng(200)
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 3)]:
+        e = n if s == last else s + 65536
+        want, wc, wsc, wres = O.bucket_allreduce_ef([t[s:e].cpu().numpy() for t in x],
+                                                    [t[s:e].cpu().numpy() for t in r0], B, O.CODEC_FP8,
+                                                    O.SCALE_ABSMAX_DIV_448)
+        assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+            got = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
+            assert (u32(got) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+            assert (u32(rw[r][s:e].cpu().numpy()) == u32(wres[r])).all(), f"oracle residual {r}, window at {s}"
+    total = whole.cpu().numpy()
+    for d in (4, 3):  # the exact reciprocal of a power of two, and a divide
+        wsb = torch.empty(need, dtype=torch.uint8, device=DEV)
+        rb = [t.clone() for t in r0]
+        ref.fill_(0.0)
+        gb.gb_bucket_allreduce_local_batch_ef([ref], [x], [rb], fp8, 0, wsb, divisor=d)
+        want = O.reduce([total], O.OP_AVG, d)
+        assert (u32(ref.cpu().numpy()) == u32(want)).all(), f"AVG over {d}"
+        del wsb, rb
+
+
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("n", [(1 << 24) + 256 * 3 + 77, (1 << 24) - 77])
+def test_decode_fp8_wave_workgroups(gb, n, acc):
+    """The fp8 decode of 4 payloads into a float32 total runs one 256-value
+    block per 64-lane workgroup from 2^24 values, in 256-lane workgroups
+    below.  On either side of the threshold, with a ragged last block and
+    payloads of special values (NaN and Inf codes, a subnormal scale, zero
+    blocks), with and without accumulation, it must equal the 256-lane
+    kernel over slices below 2^24, and the oracle on the first, the last and
+    sampled windows."""
+    import numpy as np
+    from oracle import oracle as O
+    fp8, k = gb.GB_CODEC_FP8_E4M3_B256, 4
+    x = [W.device_gradients(n, 2200 + r, DEV) for r in range(k)]
+    last = (n - 65536) // 256 * 256
+    plant_specials(x, n, last)
+    nb = (n + 255) // 256
+    codes = [torch.empty(n, dtype=torch.uint8, device=DEV) for _ in range(k)]
+    scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(k)]
+    for r in range(k):
+        gb.gb_encode_fp8_e4m3_blockscaled(codes[r], scales[r], x[r], 0)
+    start = W.device_gradients(n, 2300, DEV)
+    whole = start.clone() if acc else filled(n)
+    ref = start.clone() if acc else filled(n)
+    gb.gb_decode_accumulate(whole, codes, scales, fp8, accumulate=acc)
+    step = 3 * (1 << 22)  # below 2^24, a multiple of 256
+    for s, e in slices(n, step):
+        gb.gb_decode_accumulate(ref[s:e], [c[s:e] for c in codes], [t[s // 256:(e + 255) // 256] for t in scales],
+                                fp8, accumulate=acc)
+    same(whole, ref, f"decode of 4 payloads (accumulate={acc}) against 256-lane slices")
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    rng = np.random.default_rng(210)
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 3)]:
+        e = n if s == last else s + 65536
+        want = O.decode_accumulate([c[s:e].cpu().numpy() for c in codes],
+                                   [t[s // 256:(e + 255) // 256].cpu().numpy() for t in scales], O.CODEC_FP8,
+                                   start[s:e].cpu().numpy() if acc else None)
+        assert (u32(whole[s:e].cpu().numpy()) == u32(want)).all(), f"oracle window at {s}"
 
 
 @pytest.mark.parametrize("k", [3, 4, 6, 8])
