@@ -22,7 +22,7 @@
 //   replica_ef the same for the fp8 pass with error feedback: 4 sources and
 //             4 float32 residuals read; codes, scales, the 4 residuals and
 //             the total written (21 streams), in that pass's shape at this
-//             size (256-lane workgroups in its workgroup order, 1 per CU).
+//             size (one block per 64-lane workgroup, 6 per CU).
 // The buffers hold gradient-like values (every float32 a hash of its index,
 // spread over +-1e-3; the write kernel stores varying bits too), because
 // what the bits are changes how fast HBM moves them: a buffer of zeros
@@ -165,41 +165,31 @@ __global__ __launch_bounds__(64) void replica_kernel(gb::PtrTable src, gb::OutTa
   gb::store4(out + e, a);
 }
 
-// The error-feedback fp8 pass's memory pattern (4 ranks, float32): the
-// value is gradient plus residual, its top bytes stand in for the codes, the
-// block's first value for the scale and half the value for the new residual.
-__global__ __launch_bounds__(kThreads) void replica_ef_kernel(gb::PtrTable src, gb::OutTable resid,
-                                                              gb::OutTable codes, gb::OutTable scales,
-                                                              float* __restrict__ out) {
-  const size_t g = gb::group_index<gb::BlockOrder>();
-  const uint32_t col = threadIdx.x & 15u;
-  const size_t block = g * gb::kBlocksPerGroup + (threadIdx.x >> 4);
-  f4 y[4][4];
+// The error-feedback fp8 pass's memory pattern (4 ranks, float32), in the
+// shape the pass takes for large buffers (one block per 64-lane workgroup,
+// 4 values per lane, 6 per compute unit): the value is gradient plus
+// residual, its top bytes stand in for the codes, the block's first value
+// for the scale and half the value for the new residual.
+__global__ __launch_bounds__(64) void replica_ef_kernel(gb::PtrTable src, gb::OutTable resid, gb::OutTable codes,
+                                                        gb::OutTable scales, float* __restrict__ out) {
+  const size_t block = blockIdx.x, e = block * gb::kBlock + 4 * (size_t)threadIdx.x;
+  f4 y[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const size_t e = gb::lane_elem(block, j, col);
-      y[r][j] = gb::load4(static_cast<const float*>(src.p[r]) + e) + gb::load4(static_cast<const float*>(resid.p[r]) + e);
-    }
+    y[r] = gb::load4(static_cast<const float*>(src.p[r]) + e) + gb::load4(static_cast<const float*>(resid.p[r]) + e);
   }
-  f4 a[4];
+  f4 a;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f4 v = y[r][j];
-      const size_t e = gb::lane_elem(block, j, col);
-      const uint32_t w = (gb::fbits(v.x) >> 24) | ((gb::fbits(v.y) >> 24) << 8) | ((gb::fbits(v.z) >> 24) << 16) |
-                         ((gb::fbits(v.w) >> 24) << 24);
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(codes.p[r]) + e));
-      gb::store4(static_cast<float*>(resid.p[r]) + e, v * 0.5f);
-      a[j] = r == 0 ? v : a[j] + v;
-    }
-    if (col == 0u) static_cast<float*>(scales.p[r])[block] = y[r][0].x;
+    const f4 v = y[r];
+    const uint32_t w = (gb::fbits(v.x) >> 24) | ((gb::fbits(v.y) >> 24) << 8) | ((gb::fbits(v.z) >> 24) << 16) |
+                       ((gb::fbits(v.w) >> 24) << 24);
+    if (threadIdx.x == 0u) static_cast<float*>(scales.p[r])[block] = v.x;
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(codes.p[r]) + e));
+    gb::store4(static_cast<float*>(resid.p[r]) + e, v * 0.5f);
+    a = r == 0 ? v : a + v;
   }
-#pragma unroll
-  for (int j = 0; j < 4; j++) gb::store4(out + gb::lane_elem(block, j, col), a[j]);
+  gb::store4(out + e, a);
 }
 
 struct Result {
@@ -356,10 +346,9 @@ int main(int argc, char** argv) {
   }
   CK(hipGetLastError());
   const double replica_ef_bytes = (double)nval * (16.0 + 16.0 + 4.0 + 16.0 / 256 + 16.0 + 4.0);
-  static_assert(gb::fused_fp8_ef_lds(4, (size_t)1 << 28) == gb::kOnePerCuLds, "the pass's cap at this size");
+  static_assert(gb::fused_fp8_ef_wave(4, (size_t)1 << 28), "the replica's shape is the pass's at this size");
   measure("fused_fp8_ef_replica_" + sz, replica_ef_bytes, reps, [&] {
-    replica_ef_kernel<<<nblk / gb::kBlocksPerGroup, kThreads, gb::kOnePerCuLds>>>(st, rt, ct, sct,
-                                                                                reinterpret_cast<float*>(buf[4]));
+    replica_ef_kernel<<<nblk, 64, gb::kFp8EfWaveLds>>>(st, rt, ct, sct, reinterpret_cast<float*>(buf[4]));
   });
   for (auto& p : res) CK(hipFree(p));
 
