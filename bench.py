@@ -416,10 +416,10 @@ class DdpBucketsEF(DdpBuckets):
         # the bf16 pass over four ranks takes 64-lane workgroups at every size,
         # for every gradient type
         bf16 = f"fused_bf16_ef_wave_kernel<4,{et}>"
-        # the fp8 pass over four ranks of float32 gradients takes one block
-        # per 64-lane workgroup from 2^22 values per rank
-        wave = et == 0 and self.n >= (1 << 22)
-        name = ("fused_fp8_ef_wave_kernel" if wave else f"fused_fp8_ef_kernel<4,{et}>") if fp8 else bf16
+        # the fp8 pass over four ranks of float32, float16 and bfloat16
+        # gradients takes one block per 64-lane workgroup from 2^22 values
+        wave = et in (0, 1, 2) and self.n >= (1 << 22)
+        name = (f"fused_fp8_ef_wave_kernel<{et}>" if wave else f"fused_fp8_ef_kernel<4,{et}>") if fp8 else bf16
         return (name, self.step_bytes(), 1, self.step)
 
     def extra(self, time_region, reps):

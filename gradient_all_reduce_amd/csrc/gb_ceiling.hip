@@ -346,9 +346,10 @@ int main(int argc, char** argv) {
   }
   CK(hipGetLastError());
   const double replica_ef_bytes = (double)nval * (16.0 + 16.0 + 4.0 + 16.0 / 256 + 16.0 + 4.0);
-  static_assert(gb::fused_fp8_ef_wave(4, (size_t)1 << 28), "the replica's shape is the pass's at this size");
+  static_assert(gb::fused_fp8_ef_wave<GB_DTYPE_F32>(4, (size_t)1 << 28), "the replica's shape is the pass's at this size");
   measure("fused_fp8_ef_replica_" + sz, replica_ef_bytes, reps, [&] {
-    replica_ef_kernel<<<nblk, 64, gb::kFp8EfWaveLds>>>(st, rt, ct, sct, reinterpret_cast<float*>(buf[4]));
+    replica_ef_kernel<<<nblk, 64, gb::fused_fp8_ef_wave_lds<GB_DTYPE_F32>()>>>(st, rt, ct, sct,
+                                                                             reinterpret_cast<float*>(buf[4]));
   });
   for (auto& p : res) CK(hipFree(p));
 

@@ -906,10 +906,26 @@ constexpr unsigned kFp8WaveLds = 8u << 10;
 // bits: +8.9-9.1% at 1e9 values per rank on two machines, +5.5-8.2% at
 // 5e8, +11.7-13.3% at 2.5e8, +11.2-13.0% at 1.25e8, and one call per
 // 6,553,600-value bucket +4.3-5.1% (8 such buckets batched +0.6-2.8%).
+//
+// Bfloat16 and float16 gradients (24 bytes of each rank per lane in flight)
+// take it too, at 8 per unit (20 KiB): in one process, same bits, against
+// the 256-lane kernel, bfloat16 +4.5% at 2^30 values (10 per unit the
+// same, 13 per unit +3%, 6 per unit -8.5%) and float16 +18.4% at 2^28 (10
+// per unit +18%, 13 per unit +15.6%, 6 per unit +5%).  In the benchmark,
+// against the 256-lane kernel on the same machine, two runs each, same
+// bits: bfloat16 +4.6-5.6% at 1e9 values, +11.0-12.7% at 1.25e8, one call
+// per 6,553,600-value bucket +4.9-6.3%, 8 such buckets batched +3.3-3.7%;
+// float16 +3.8-6.7% at 1e9 values, +5.2-6.0% per bucket, +3.9-4.2%
+// batched.  Float64 gradients lost 1.5-3.5% at every cap and keep the
+// 256-lane kernel.
+template <int ET>
 __host__ __device__ constexpr bool fused_fp8_ef_wave(int k, size_t n) {
-  return k == 4 && n >= ((size_t)1 << 22);
+  return ET != GB_DTYPE_F64 && k == 4 && n >= ((size_t)1 << 22);
 }
-constexpr unsigned kFp8EfWaveLds = 24u << 10;
+template <int ET>
+__host__ __device__ constexpr unsigned fused_fp8_ef_wave_lds() {
+  return ET == GB_DTYPE_F32 ? 24u << 10 : 20u << 10;
+}
 
 // The fp8 decode of 4 payloads into a float32 total in the same shape from
 // 2^24 values, uncapped (the scales are uniform across a workgroup, so each

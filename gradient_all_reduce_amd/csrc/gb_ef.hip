@@ -169,11 +169,12 @@ __global__ __launch_bounds__(kWaveThreads) void fused_bf16_ef_wave_kernel(void* 
   }
 }
 
-// The pass over float32 gradients of 4 ranks with one block per wavefront:
-// workgroup b is block b, lane l its values 4l to 4l + 3 of every source and
-// residual.  The block maximum and so every bit are those of the 16-lane map.
-template <bool FULL, int DIV = 0>
-__device__ __forceinline__ void fused_fp8_ef_wave_body(float* out, const PtrTable& src, const OutTable& resid,
+// The pass over float32, float16 or bfloat16 gradients of 4 ranks with one
+// block per wavefront: workgroup b is block b, lane l its values 4l to
+// 4l + 3 of every source and residual.  The block maximum and so every bit
+// are those of the 16-lane map.
+template <int ET, bool FULL, int DIV = 0>
+__device__ __forceinline__ void fused_fp8_ef_wave_body(void* out, const PtrTable& src, const OutTable& resid,
                                                        const OutTable& codes, const OutTable& scales, size_t n,
                                                        int mode, size_t block, float dv = 1.0f, float inv = 0.0f) {
   constexpr int K = 4;
@@ -181,7 +182,7 @@ __device__ __forceinline__ void fused_fp8_ef_wave_body(float* out, const PtrTabl
   f4 y[K];
 #pragma unroll
   for (int r = 0; r < K; r++) {
-    y[r] = canon4(load4_at<FULL>(static_cast<const float*>(src.p[r]), e, n) +
+    y[r] = canon4(load_vals4_at<ET, FULL>(src.p[r], e, n) +
                   load4_at<FULL>(static_cast<const float*>(resid.p[r]), e, n));
   }
   f4 a[1];
@@ -196,20 +197,21 @@ __device__ __forceinline__ void fused_fp8_ef_wave_body(float* out, const PtrTabl
     store4_at<FULL>(static_cast<float*>(resid.p[r]), e, n, canon4(y[r] - v));
   }
   avg_total<DIV>(a, dv, inv);
-  store4_at<FULL>(out, e, n, canon4(a[0]));
+  store_vals4_at<ET, FULL>(out, e, n, canon4(a[0]));
 }
 
-__global__ __launch_bounds__(64) void fused_fp8_ef_wave_kernel(float* out, PtrTable src, OutTable resid,
+template <int ET>
+__global__ __launch_bounds__(64) void fused_fp8_ef_wave_kernel(void* out, PtrTable src, OutTable resid,
                                                                OutTable codes, OutTable scales, size_t n, int mode) {
   const size_t block = blockIdx.x;  // the grid has one workgroup per block, so block * kBlock < n
-  if ((block + 1) * kBlock <= n) fused_fp8_ef_wave_body<true>(out, src, resid, codes, scales, n, mode, block);
-  else fused_fp8_ef_wave_body<false>(out, src, resid, codes, scales, n, mode, block);
+  if ((block + 1) * kBlock <= n) fused_fp8_ef_wave_body<ET, true>(out, src, resid, codes, scales, n, mode, block);
+  else fused_fp8_ef_wave_body<ET, false>(out, src, resid, codes, scales, n, mode, block);
 }
 
 // The batch in the same shape: bucket b takes workgroups [first[b],
 // first[b + 1]), 16 per 4096-value group, and those past the bucket's last
 // block return at once (uniformly per workgroup).
-template <int DIV>
+template <int ET, int DIV>
 __global__ __launch_bounds__(64) void fused_fp8_ef_wave_batch_kernel(BucketBatchEf t, int mode, float dv, float inv) {
   constexpr int K = 4;
   const size_t w = blockIdx.x;
@@ -226,9 +228,9 @@ __global__ __launch_bounds__(64) void fused_fp8_ef_wave_batch_kernel(BucketBatch
     codes.p[r] = t.codes[b][r];
     scales.p[r] = t.scales[b][r];
   }
-  float* out = static_cast<float*>(t.out[b]);
-  if ((block + 1) * kBlock <= n) fused_fp8_ef_wave_body<true, DIV>(out, src, resid, codes, scales, n, mode, block, dv, inv);
-  else fused_fp8_ef_wave_body<false, DIV>(out, src, resid, codes, scales, n, mode, block, dv, inv);
+  void* out = t.out[b];
+  if ((block + 1) * kBlock <= n) fused_fp8_ef_wave_body<ET, true, DIV>(out, src, resid, codes, scales, n, mode, block, dv, inv);
+  else fused_fp8_ef_wave_body<ET, false, DIV>(out, src, resid, codes, scales, n, mode, block, dv, inv);
 }
 
 // Several buckets in one launch, with their residuals: each workgroup finds
@@ -323,12 +325,13 @@ hipError_t fused_fp8_ef_batch_t(BucketBatchEf& t, int k, int scale_mode, float d
   if (grid == 0) return hipErrorInvalidValue;
   size_t largest = 0;
   for (uint32_t b = 0; b < t.count; b++) largest = t.n[b] > largest ? t.n[b] : largest;
-  if constexpr (ET == GB_DTYPE_F32) {
+  if constexpr (ET != GB_DTYPE_F64) {
     // sixteen 64-lane workgroups per group, as the whole-buffer launch takes
     // its largest bucket
-    if (fused_fp8_ef_wave(k, largest) && grid <= kMaxGrid / 16) {
+    if (fused_fp8_ef_wave<ET>(k, largest) && grid <= kMaxGrid / 16) {
       for (int b = 0; b <= kBatchBucketsEf; b++) t.first[b] *= 16;
-      fused_fp8_ef_wave_batch_kernel<DIV><<<16 * grid, 64, kFp8EfWaveLds, stream>>>(t, scale_mode, dv, inv);
+      fused_fp8_ef_wave_batch_kernel<ET, DIV><<<16 * grid, 64, fused_fp8_ef_wave_lds<ET>(), stream>>>(t, scale_mode, dv,
+                                                                                                       inv);
       return hipGetLastError();
     }
   }
@@ -408,12 +411,12 @@ hipError_t fused_bf16_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, 
 template <int ET>
 hipError_t fused_fp8_ef_t(void* out, const PtrTable& srcs, const OutTable& rs, const OutTable& c, const OutTable& s,
                           int k, size_t n, int scale_mode, hipStream_t stream) {
-  if constexpr (ET == GB_DTYPE_F32) {
+  if constexpr (ET != GB_DTYPE_F64) {
     // one workgroup per block; beyond the largest grid the 256-lane kernel runs
     const size_t wave_grid = ceil_div(n, kBlock);
-    if (fused_fp8_ef_wave(k, n) && wave_grid <= kMaxGrid) {
-      fused_fp8_ef_wave_kernel<<<wave_grid, 64, kFp8EfWaveLds, stream>>>(static_cast<float*>(out), srcs, rs, c, s, n,
-                                                                          scale_mode);
+    if (fused_fp8_ef_wave<ET>(k, n) && wave_grid <= kMaxGrid) {
+      fused_fp8_ef_wave_kernel<ET><<<wave_grid, 64, fused_fp8_ef_wave_lds<ET>(), stream>>>(out, srcs, rs, c, s, n,
+                                                                                          scale_mode);
       return hipGetLastError();
     }
   }

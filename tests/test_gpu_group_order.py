@@ -10,8 +10,9 @@
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
   values, 2^28 over two ranks, but not over 4; float64 gradients from
   3 * 2^21 values), and one block per 64-lane workgroup (float32 gradients
-  of 4 ranks from 2^27 values, with error feedback from 2^22, the batch of
-  such a bucket too; the decode of 4 payloads into float32 from 2^24);
+  of 4 ranks from 2^27 values, with error feedback from 2^22 and also over
+  float16 and bfloat16 gradients, the batch of such a bucket too; the
+  decode of 4 payloads into float32 from 2^24);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
   ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
   4 ranks and 2^29; with error feedback, over float32 gradients from 1 rank
@@ -391,6 +392,70 @@ def test_fused_fp8_ef_wave_workgroups(gb, n):
         want = O.reduce([total], O.OP_AVG, d)
         assert (u32(ref.cpu().numpy()) == u32(want)).all(), f"AVG over {d}"
         del wsb, rb
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("n", [(1 << 22) + 256 * 5 + 77, (1 << 22) - 77])
+def test_fused_fp8_ef_wave_typed_workgroups(gb, dt, n):
+    """The fp8 bucket stream with error feedback over bfloat16 and float16
+    gradients of 4 ranks runs one 256-value block per 64-lane workgroup from
+    2^22 values per rank, in 256-lane workgroups below.  On either side of
+    the threshold, with a ragged last block and special values planted in a
+    residual, it must equal the 256-lane kernel over slices below 2^22 from
+    the same residuals, a batch of that one bucket, and the oracle on the
+    first, the last and sampled windows: totals, codes, scales and the new
+    residuals."""
+    import numpy as np
+    from oracle import oracle as O
+    fp8, k = gb.GB_CODEC_FP8_E4M3_B256, 4
+    x = [W.device_gradients_typed(n, 2400 + r, DEV, dt) for r in range(k)]
+    last = (n - 65536) // 256 * 256
+    x[1][n - 1] = float("inf")
+    r0 = [W.device_gradients(n, 2500 + r, DEV) * 1e-2 for r in range(k)]
+    for base in (0, last):
+        r0[2][base + 13 * 256 + 5] = float("nan")
+        r0[0][base + 14 * 256:base + 15 * 256] = -3e-41
+        r0[3][base + 15 * 256 + 7] = 3e38
+    lay = gb.gb_bucket_workspace_layout(fp8, k, n, B)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=DEV)
+    rw = [t.clone() for t in r0]
+    whole, ref = filled(n, x[0].dtype), filled(n, x[0].dtype)
+    gb.gb_bucket_allreduce_local_ef_typed(whole, x, rw, B, fp8, 0, ws)
+    rs = [t.clone() for t in r0]
+    step = 3 * (1 << 20)  # below 2^22, a multiple of 256
+    wss = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, step, step), dtype=torch.uint8, device=DEV)
+    for s, e in slices(n, step):
+        gb.gb_bucket_allreduce_local_ef_typed(ref[s:e], [t[s:e] for t in x], [t[s:e] for t in rs], step, fp8, 0, wss)
+    same(whole, ref, f"{dt} error feedback against 256-lane slices")
+    for r in range(k):
+        same(rw[r], rs[r], f"{dt} residual {r} against 256-lane slices")
+    del wss, rs
+    wsb = torch.zeros(gb.gb_bucket_batch_workspace_bytes(fp8, k, [n]), dtype=torch.uint8, device=DEV)
+    rb = [t.clone() for t in r0]
+    ref.view(torch.int16).fill_(0)
+    gb.gb_bucket_allreduce_local_batch_ef([ref], [x], [rb], fp8, 0, wsb)
+    same(whole, ref, f"{dt}: a batch of the one bucket")
+    assert torch.equal(ws, wsb), "the batch's payloads"
+    for r in range(k):
+        same(rw[r], rb[r], f"{dt}: the batch's residual {r}")
+    del wsb, rb
+    nb = (n + 255) // 256
+    codes = [ws[r * lay["codes_stride"]:][:n] for r in range(k)]
+    scales = [ws[lay["scales_offset"] + r * lay["scales_stride"]:][:4 * nb].view(torch.float32) for r in range(k)]
+    u32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    rng = np.random.default_rng(220)
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 3)]:
+        e = n if s == last else s + 65536
+        xs = [bits(t[s:e]).cpu().numpy().view(np.uint16) for t in x]
+        want, wc, wsc, wres = O.bucket_allreduce_ef_typed(xs, [t[s:e].cpu().numpy() for t in r0], dt, B,
+                                                          O.CODEC_FP8, O.SCALE_ABSMAX_DIV_448)
+        got = bits(whole[s:e]).cpu().numpy().view(np.uint16)
+        assert (got == np.ascontiguousarray(want).view(np.uint16)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy() == wc[r]).all(), f"oracle codes, rank {r}, window at {s}"
+            sc = scales[r][s // 256:(e + 255) // 256].cpu().numpy()
+            assert (u32(sc) == u32(wsc[r])).all(), f"oracle scales, rank {r}, window at {s}"
+            assert (u32(rw[r][s:e].cpu().numpy()) == u32(wres[r])).all(), f"oracle residual {r}, window at {s}"
 
 
 @pytest.mark.parametrize("acc", [False, True])
