@@ -226,10 +226,10 @@ class DdpBuckets(Workload):
         # the four-rank float32 sum takes its wide kernel from 2^28 values per rank
         f32_sum = "reduce_sum4_wide_kernel" if self.n >= (1 << 28) else "reduce_sum_kernel<4,false>"
         # the fp8 pass over 4 ranks takes one block per 64-lane workgroup for
-        # float32 gradients from 2^27 values per rank, and 128-lane workgroups
+        # float32 gradients from 2^22 values per rank, and 128-lane workgroups
         # for float64 ones between 3 * 2^21 and 2^29
         n = self.n
-        if et == 0 and n >= (1 << 27):
+        if et == 0 and n >= (1 << 22):
             fp8 = "fused_fp8_wave_kernel<4>"
         elif et == 3 and (3 << 21) <= n < (1 << 29):
             fp8 = "fused_fp8_half_kernel<4,3>"
@@ -662,7 +662,7 @@ def codec_extra(wl, time_region, reps, dec_name, dec_bytes):
     gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1)
     return {"decode_kernel": dec_name, "decode_kernel_gbs": gbs(dec_bytes, dec_ms),
             "decode_kernel_frac": round(gbs(dec_bytes, dec_ms) / HBM_PEAK_GBS, 4),
-            "fused_pass_kernel": "fused_fp8_kernel<4,0>" if fp8 else "fused_bf16_wave_kernel<4,0>",
+            "fused_pass_kernel": "fused_fp8_wave_kernel<4>" if fp8 else "fused_bf16_wave_kernel<4,0>",
             "fused_pass_bytes": wl.fused_bytes(), "fused_pass_us": round(fused_ms * 1e3, 2),
             "fused_pass_gbs": gbs(wl.fused_bytes(), fused_ms),
             "fused_pass_frac": round(gbs(wl.fused_bytes(), fused_ms) / HBM_PEAK_GBS, 4),

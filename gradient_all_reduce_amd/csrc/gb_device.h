@@ -878,7 +878,7 @@ __host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) {
   return ET == GB_DTYPE_F64 ? kTwoPerCuLds : (k >= 4 ? kTwoPerCuLds : kThreePerCuLds);
 }
 
-// Fused fp8 pass over float32 gradients of 4 ranks from 2^27 values per
+// Fused fp8 pass over float32 gradients of 4 ranks from 2^22 values per
 // rank: one block per 64-lane workgroup (4 values per lane, so each load
 // and store of a rank covers its 1 KiB, or 256 bytes of codes, in one
 // piece) in index order, capped at 20 per unit (8 KiB of LDS each).  The
@@ -887,12 +887,15 @@ __host__ __device__ constexpr unsigned fused_fp8_half_lds(int k) {
 // bound by that chain; at 20 per unit it is not.  Measured in the
 // benchmark's bucket stream over 4 ranks, against the 128-lane kernel on
 // the same machine, two machines, same bits: +2.5% and +4.5-5.5% at 1e9
-// values, +4.8-5.0% at 5e8, +0.6-1.4% at 2.5e8; at 1.25e8 (256-lane
-// kernel) -0.1 to -1.4%.  In one process it gained -0.4% to +4.4% at 1e9
-// values on three machines, lost 4-9% over 2 ranks and was level over 8
-// at 2^28, so the rule is for 4 ranks only.
+// values, +4.8-5.0% at 5e8, +0.6-1.4% at 2.5e8.  Against the 256-lane
+// kernel, three runs each on two machines: at 1.25e8 values -0.1 to -1.4%
+// and +0.2 to +2.7%; one call per 6,553,600-value bucket +0.4 to +3.1% on
+// one stream, -0.6 to +2.0% over two and +2.8 to +5.1% over four.  In one
+// process it gained -0.4% to +4.4% at 1e9 values on three machines, lost
+// 4-9% over 2 ranks and was level over 8 at 2^28, so the rule is for 4
+// ranks only.
 __host__ __device__ constexpr bool fused_fp8_wave(int k, size_t n) {
-  return k == 4 && n >= ((size_t)1 << 27);
+  return k == 4 && n >= ((size_t)1 << 22);
 }
 constexpr unsigned kFp8WaveLds = 8u << 10;
 

@@ -10,9 +10,9 @@
 - the fused fp8 pass in 128-lane workgroups (float32 gradients from 2^27
   values, 2^28 over two ranks, but not over 4; float64 gradients from
   3 * 2^21 values), and one block per 64-lane workgroup (float32 gradients
-  of 4 ranks from 2^27 values, with error feedback from 2^22 and also over
-  float16 and bfloat16 gradients, the batch of such a bucket too; the
-  decode of 4 payloads into float32 from 2^24);
+  of 4 ranks from 2^22 values, with error feedback also over float16 and
+  bfloat16 gradients, the batch of such a bucket too; the decode of 4
+  payloads into float32 from 2^24);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
   ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
   4 ranks and 2^29; with error feedback, over float32 gradients from 1 rank
@@ -264,15 +264,15 @@ def plant_specials(x, n, last):
     x[3][n - 1] = float("nan")
 
 
-@pytest.mark.parametrize("n", [(1 << 27) + 256 * 5 + 77, (1 << 27) - 77])
+@pytest.mark.parametrize("n", [(1 << 22) + 256 * 5 + 77, (1 << 22) - 77, (1 << 27) + 256 * 5 + 77])
 def test_fused_fp8_wave_workgroups(gb, n):
     """The fused fp8 bucket stream over float32 gradients of 4 ranks runs one
-    256-value block per 64-lane workgroup from 2^27 values per rank, in
-    256-lane workgroups below.  On either side of the threshold, with a
-    ragged last block and special values planted in the first and the last
-    window, it must equal the 256-lane kernel over slices below 2^27, and the
-    oracle on the first, the last and sampled windows: totals, codes and
-    scales.  A batch of that one bucket takes the same shape and must give
+    256-value block per 64-lane workgroup from 2^22 values per rank, in
+    256-lane workgroups below.  On either side of the threshold and at 2^27,
+    with a ragged last block and special values planted in the first and the
+    last window, it must equal the 256-lane kernel over slices below 2^22,
+    and the oracle on the first, the last and sampled windows: totals, codes
+    and scales.  A batch of that one bucket takes the same shape and must give
     the same bits, and its AVG the oracle's AVG of that total."""
     import numpy as np
     from oracle import oracle as O
@@ -284,9 +284,10 @@ def test_fused_fp8_wave_workgroups(gb, n):
     ws = torch.zeros(lay["total"], dtype=torch.uint8, device=DEV)
     whole, ref = filled(n), filled(n)
     gb.gb_bucket_allreduce_local(whole, x, B, fp8, 0, ws)
-    wss = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, STEP_HALF, B), dtype=torch.uint8, device=DEV)
-    for s, e in slices(n, STEP_HALF):
-        gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, fp8, 0, wss)
+    step = 3 * (1 << 20)  # below 2^22, a multiple of 256
+    wss = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, step, step), dtype=torch.uint8, device=DEV)
+    for s, e in slices(n, step):
+        gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], step, fp8, 0, wss)
     same(whole, ref, "fused fp8 pass over 4 ranks against 256-lane slices")
     del wss
     need = gb.gb_bucket_batch_workspace_bytes(fp8, k, [n])
@@ -731,7 +732,7 @@ def test_fp8_group_kernels(gb):
                      device=DEV)
     whole, ref = filled(n), filled(n)
     gb.gb_bucket_allreduce_local(whole, x, B, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
-    for s, e in slices(n, STEP_HALF):  # float32: below 2^27, the 256-lane kernel in index order
+    for s, e in slices(n, STEP_HALF):  # one block per wavefront here and in the whole launch
         gb.gb_bucket_allreduce_local(ref[s:e], [t[s:e] for t in x], B, gb.GB_CODEC_FP8_E4M3_B256, 0, ws)
     same(whole, ref, "fp8 bucket stream")
     rw = [torch.full((n,), -2e-5, device=DEV) for _ in range(2)]
