@@ -19,9 +19,11 @@
 //   * the fp8 block maximum is reduced across the 16 lanes of one DPP row (four
 //     row-local DPP steps, no LDS, no barrier): a 256-value block is one row of
 //     16 lanes holding 16 values each, a wavefront works on 4 blocks and a
-//     256-lane workgroup on 16 (the fused pass over 4 ranks of large float32
-//     buffers instead spreads one block over a wavefront, 4 values per lane,
-//     and takes the row maxima's maximum with 4 lane reads);
+//     256-lane workgroup on 16 (the fused pass over 4 ranks of float32
+//     gradients, with error feedback also of float16 and bfloat16 ones, and
+//     the decode of 4 payloads into float32 instead spread one block over a
+//     wavefront from a few million values, 4 values per lane, and take the
+//     row maxima's maximum with 4 lane reads);
 //   * E4M3 conversion uses gfx950's packed converters (v_cvt_pk_fp8_f32 to
 //     encode two values per instruction, v_cvt_pk_f32_fp8 to decode two);
 //   * large launches take their groups in a permuted order (group_index) that
