@@ -170,3 +170,72 @@ def test_error_feedback_in_a_replayed_graph(gb, codec, k):
                 assert (u32(res[r].cpu().numpy()) == u32(wres[r])).all(), (dt, rep, r)
             gb.gb_reduce_sum(torch.empty(16, device=DEV), [torch.ones(16, device=DEV)])  # eager work between
             torch.cuda.synchronize()
+
+
+def test_one_block_per_wavefront_kernels_in_a_replayed_graph(gb):
+    """The 4-rank kernels that take one fp8 block per 64-lane workgroup, each
+    captured once and replayed three times with eager work in between: the
+    fused pass over float32 gradients, the pass with error feedback over
+    float32 and bfloat16 gradients (each replay reads the residuals the
+    previous one wrote, as eager calls do) and the decode of 4 payloads.
+    Every replay must equal the same calls made eagerly, bit for bit."""
+    k, fp8 = 4, gb.GB_CODEC_FP8_E4M3_B256
+    n, bucket = (1 << 22) + 256 * 3 + 17, W.DDP_BUCKET
+    between = lambda: gb.gb_reduce_sum(torch.empty(16, device=DEV), [torch.ones(16, device=DEV)])
+
+    def replays_match(step, outs, reset, eager_steps):
+        """Capture step, reset the state, then compare three replays with
+        the eager results of the same three steps."""
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        reset()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            for got, want in zip(outs(), eager_steps[rep]):
+                assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), rep
+            between()
+            torch.cuda.synchronize()
+
+    x = [W.device_gradients(n, 7000 + r, DEV) for r in range(k)]
+    ws = torch.empty(gb.gb_bucket_workspace_bytes(fp8, k, n, bucket), dtype=torch.uint8, device=DEV)
+    out = torch.empty(n, device=DEV)
+    gb.gb_bucket_allreduce_local(out, x, bucket, fp8, 0, ws)
+    torch.cuda.synchronize()
+    want = [(out.clone(), ws.clone())]
+    replays_match(lambda: gb.gb_bucket_allreduce_local(out, x, bucket, fp8, 0, ws), lambda: (out, ws),
+                  lambda: None, want * 3)
+
+    for dt in ("f32", "bf16"):
+        xs = x if dt == "f32" else [W.device_gradients_typed(n, 7100 + r, DEV, dt) for r in range(k)]
+        r0 = [W.device_gradients(n, 7200 + r, DEV) * 1e-2 for r in range(k)]
+        res = [t.clone() for t in r0]
+        o = torch.empty(n, dtype=xs[0].dtype, device=DEV)
+        step = lambda: gb.gb_bucket_allreduce_local_ef_typed(o, xs, res, bucket, fp8, 0, ws)
+        eager = []
+        for _ in range(3):
+            step()
+            torch.cuda.synchronize()
+            eager.append([o.clone(), ws.clone()] + [t.clone() for t in res])
+        for t, s in zip(res, r0):
+            t.copy_(s)
+
+        def reset():
+            for t, s in zip(res, r0):
+                t.copy_(s)
+        replays_match(step, lambda: [o, ws] + res, reset, eager)
+
+    m = (1 << 24) + 77
+    codes = [torch.empty(m, dtype=torch.uint8, device=DEV) for _ in range(k)]
+    scales = [torch.empty((m + 255) // 256, device=DEV) for _ in range(k)]
+    for r in range(k):
+        gb.gb_encode_fp8_e4m3_blockscaled(codes[r], scales[r], W.device_gradients(m, 7300 + r, DEV), 0)
+    acc = torch.empty(m, device=DEV)
+    gb.gb_decode_accumulate(acc, codes, scales, fp8)
+    torch.cuda.synchronize()
+    replays_match(lambda: gb.gb_decode_accumulate(acc, codes, scales, fp8), lambda: (acc,), lambda: acc.zero_(),
+                  [(acc.clone(),)] * 3)
