@@ -239,6 +239,10 @@ class DdpBuckets(Workload):
         # more ranks, float16 and bfloat16 ones over 4 from 2^29 values
         wave = et == 0 or (et in (1, 2) and self.n >= (1 << 29))
         bf16 = f"fused_bf16_wave_kernel<4,{et}>" if wave else f"fused_bf16_kernel<4,{et}>"
+        # (over four ranks the half-precision types take 8 values per lane
+        # from 2^22 values)
+        if et in (1, 2) and self.n >= (1 << 22):
+            bf16 = f"fused_bf16_eight_kernel<{et}>"
         name = {2: fp8, 1: bf16,
                 0: f32_sum if et == 0 else f"reduce_typed_kernel<{et},4,0>"}[self.codec]
         return (name, self.step_bytes(), 1, self.step)

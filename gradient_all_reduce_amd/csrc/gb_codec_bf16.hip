@@ -91,6 +91,53 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(void* acc, PtrTab
 // ===========================================================================
 // Fused bf16 bucket pass, one 4-value vector per lane.
 // ===========================================================================
+// The same pass over 4 ranks of float16 or bfloat16 gradients with 8
+// consecutive values per lane (one 16-byte load of each rank): workgroup w
+// takes values [512 w, 512 w + 512).  Every result is per value, so the
+// bits are those of every other lane map.
+template <int ET, bool FULL>
+__device__ __forceinline__ void fused_bf16_eight_body(void* out, const PtrTable& src, const OutTable& codes,
+                                                      size_t n, size_t e) {
+  constexpr int K = 4;
+  f4 x[K][2];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    if (FULL) {
+      load8_half<ET>(src.p[r], e, x[r][0], x[r][1]);
+    } else {
+      x[r][0] = load_vals4_at<ET, false>(src.p[r], e, n);
+      x[r][1] = load_vals4_at<ET, false>(src.p[r], e + 4, n);
+    }
+  }
+  f4 a[2];
+#pragma unroll
+  for (int r = 0; r < K; r++) {
+    const u2 w0 = bf16_pack4(x[r][0]), w1 = bf16_pack4(x[r][1]);
+    uint16_t* c = static_cast<uint16_t*>(codes.p[r]);
+    if (FULL) {
+      __builtin_nontemporal_store(u4w{w0.x, w0.y, w1.x, w1.y}, reinterpret_cast<u4w*>(c + e));
+    } else {
+      store_bf16_4_at<false>(c, e, n, w0);
+      store_bf16_4_at<false>(c, e + 4, n, w1);
+    }
+    const f4 v0 = bf16_unpack4(w0), v1 = bf16_unpack4(w1);
+    a[0] = r == 0 ? v0 : a[0] + v0;
+    a[1] = r == 0 ? v1 : a[1] + v1;
+  }
+  if (FULL) {
+    store8_half<ET>(out, e, canon4(a[0]), canon4(a[1]));
+  } else {
+    store_vals4_at<ET, false>(out, e, n, canon4(a[0]));
+    store_vals4_at<ET, false>(out, e + 4, n, canon4(a[1]));
+  }
+}
+
+template <int ET>
+__global__ __launch_bounds__(64) void fused_bf16_eight_kernel(void* out, PtrTable src, OutTable codes, size_t n) {
+  const size_t e = ((size_t)blockIdx.x * 64 + threadIdx.x) * 8;
+  if (((size_t)blockIdx.x + 1) * 512 <= n) fused_bf16_eight_body<ET, true>(out, src, codes, n, e);
+  else if (e < n) fused_bf16_eight_body<ET, false>(out, src, codes, n, e);
+}
 // Lane t of vector group sg (t in [0, 256)).
 template <int K, int ET, bool FULL, int DIV = 0>
 __device__ __forceinline__ void fused_bf16_body(void* out, const PtrTable& src, const OutTable& codes, size_t n,
@@ -219,6 +266,14 @@ hipError_t decode_bf16_t(void* acc, const PtrTable& codes, int k, size_t n, bool
 
 template <int ET>
 hipError_t fused_bf16_t(void* out, const PtrTable& srcs, const OutTable& c, int k, size_t n, hipStream_t stream) {
+  if constexpr (ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) {
+    // one workgroup per 512 values; beyond the largest grid the kernels below run
+    const size_t eight_grid = ceil_div(n, 512);
+    if (fused_bf16_eight(k, n) && eight_grid <= kMaxGrid) {
+      fused_bf16_eight_kernel<ET><<<eight_grid, 64, kBf16EightLds, stream>>>(out, srcs, c, n);
+      return hipGetLastError();
+    }
+  }
   if constexpr (ET == GB_DTYPE_F32 || ET == GB_DTYPE_F16 || ET == GB_DTYPE_BF16) {
     const size_t wave_grid = wave_grid_for(n);
     const bool wave = ET == GB_DTYPE_F32 ? fused_bf16_wave(k) : fused_bf16_half_wave(k, n);

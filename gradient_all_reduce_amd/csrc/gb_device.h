@@ -1019,6 +1019,16 @@ __host__ __device__ constexpr unsigned fused_bf16_wave_lds(int k, size_t n) {
 // ranks below 2^28 the second machine lost up to 6.8%, at 2^20 values every
 // 64-lane shape lost 2-13%, and over 2 or 3 ranks nothing gained at every
 // size.
+// Over 4 ranks of float16 and bfloat16 gradients from 2^22 values the
+// pass instead takes 8 values per lane (16-byte loads) in 64-lane
+// workgroups at 10 per unit (16 KiB of LDS each).  In one process at 2^26
+// and 2^30 values, same bits: +3.9-6.1% against the library's kernels at
+// 10 per unit, less at 13 and below (uncapped -3 to -5%).  In the
+// benchmark, against them on the same machine, two runs each: bfloat16
+// +3.0-3.2% at 1e9 values and +5.4-5.6% at 1.25e8, float16 +0.9-1.2% at
+// 1e9; one call per 6,553,600-value bucket +7.1-7.3% for both.
+__host__ __device__ constexpr bool fused_bf16_eight(int k, size_t n) { return k == 4 && n >= ((size_t)1 << 22); }
+constexpr unsigned kBf16EightLds = 16u << 10;
 __host__ __device__ constexpr bool fused_bf16_half_wave(int k, size_t n) {
   return (k == 4 && n >= ((size_t)1 << 29)) || (k >= 5 && n >= ((size_t)1 << 22));
 }

@@ -459,6 +459,46 @@ def test_fused_fp8_ef_wave_typed_workgroups(gb, dt, n):
             assert (u32(rw[r][s:e].cpu().numpy()) == u32(wres[r])).all(), f"oracle residual {r}, window at {s}"
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("n", [(1 << 22) + 256 * 5 + 77, (1 << 22) - 77])
+def test_fused_bf16_eight_per_lane(gb, dt, n):
+    """The bf16-codec bucket stream over bfloat16 and float16 gradients of 4
+    ranks takes 8 values per lane in 64-lane workgroups from 2^22 values per
+    rank.  On either side of the threshold, with a ragged last lane and
+    special values (Inf, NaN, the largest finite magnitude), it must equal
+    the kernels below the threshold over slices, and the oracle on the
+    first, the last and sampled windows: totals and codes."""
+    import numpy as np
+    from oracle import oracle as O
+    bf16, k = gb.GB_CODEC_BF16, 4
+    x = [W.device_gradients_typed(n, 2600 + r, DEV, dt) for r in range(k)]
+    last = (n - 65536) // 256 * 256
+    for base in (0, last):
+        x[0][base + 17] = float("inf")
+        x[1][base + 300] = float("nan")
+        x[2][base + 301] = -65504.0
+    x[3][n - 1] = float("nan")
+    lay = gb.gb_bucket_workspace_layout(bf16, k, n, B)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=DEV)
+    whole, ref = filled(n, x[0].dtype), filled(n, x[0].dtype)
+    gb.gb_bucket_allreduce_local_typed(whole, x, B, bf16, 0, ws)
+    step = 3 * (1 << 20)  # below 2^22
+    wss = torch.empty(gb.gb_bucket_workspace_bytes(bf16, k, step, step), dtype=torch.uint8, device=DEV)
+    for s, e in slices(n, step):
+        gb.gb_bucket_allreduce_local_typed(ref[s:e], [t[s:e] for t in x], step, bf16, 0, wss)
+    same(whole, ref, f"{dt} bf16-codec stream against slices below 2^22")
+    codes = [ws[r * lay["codes_stride"]:][:2 * n].view(torch.int16) for r in range(k)]
+    rng = np.random.default_rng(230)
+    for s in [0, last] + [int(v) * 256 for v in rng.integers(0, last // 256, 3)]:
+        e = n if s == last else s + 65536
+        xs = [bits(t[s:e]).cpu().numpy().view(np.uint16) for t in x]
+        want, wc, _ = O.bucket_allreduce_typed(xs, dt, B, O.CODEC_BF16)
+        got = bits(whole[s:e]).cpu().numpy().view(np.uint16)
+        assert (got == np.ascontiguousarray(want).view(np.uint16)).all(), f"oracle total window at {s}"
+        for r in range(k):
+            assert (codes[r][s:e].cpu().numpy().view(np.uint16) == wc[r]).all(), f"oracle codes {r}, window at {s}"
+
+
 @pytest.mark.parametrize("acc", [False, True])
 @pytest.mark.parametrize("n", [(1 << 24) + 256 * 3 + 77, (1 << 24) - 77])
 def test_decode_fp8_wave_workgroups(gb, n, acc):
