@@ -14,9 +14,10 @@
   bfloat16 gradients, the batch of such a bucket too; the decode of 4
   payloads into float32 from 2^24);
 - the fused bf16 pass in 64-lane workgroups (float32 gradients from 3
-  ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, from
-  4 ranks and 2^29; with error feedback, over float32 gradients from 1 rank
-  and over the other types by rank count and size).
+  ranks; float16 and bfloat16 gradients from 5 ranks and 2^22 values, and
+  over 4 ranks from 2^22 with 8 values per lane; with error feedback, over
+  float32 gradients from 1 rank and over the other types by rank count and
+  size).
 
 Each must give, bit for bit, what the same arithmetic gives in another
 shape: over slices of the stream small enough to keep the index order and
