@@ -449,3 +449,25 @@ def test_one_large_bucket_equals_the_single_buffer_call(gb, codec, n, ef):
     if ef:
         for a, b in zip(r1, r2):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_half_precision_batch_takes_eight_per_lane(gb, dt):
+    """A bf16-codec batch over 4 ranks of float16 or bfloat16 gradients whose
+    largest bucket has 2^22 values or more runs 8 values per lane, as the
+    single-buffer call does on that bucket: every bucket's total and codes
+    must equal the single-buffer call on it, the small buckets included."""
+    k, codec = 4, gb.GB_CODEC_BF16
+    sizes = [(1 << 22) + 77, 300, 1, 5003, 513]
+    xs = [[W.device_gradients_typed(n, 4800 + 10 * b + r, DEV, dt) for r in range(k)] for b, n in enumerate(sizes)]
+    outs = [torch.empty(n, dtype=xs[b][0].dtype, device=DEV) for b, n in enumerate(sizes)]
+    ws = torch.zeros(gb.gb_bucket_batch_workspace_bytes(codec, k, sizes), dtype=torch.uint8, device=DEV)
+    gb.gb_bucket_allreduce_local_batch(outs, xs, codec, workspace=ws)
+    torch.cuda.synchronize()
+    for b, n in enumerate(sizes):
+        ref = torch.empty_like(outs[b])
+        bucket = (n + 255) // 256 * 256  # one bucket
+        w1 = torch.zeros(gb.gb_bucket_workspace_bytes(codec, k, n, bucket), dtype=torch.uint8, device=DEV)
+        gb.gb_bucket_allreduce_local_typed(ref, xs[b], bucket, codec, 0, w1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[b].view(torch.int16), ref.view(torch.int16)), f"bucket {b} (n={n})"
